@@ -1,0 +1,162 @@
+"""Plain float64 CPU oracle for the dynamic short convolution.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute
+this module; only the tests, the package smoke check and the benchmark's CPU-baseline
+leg use it. It shares no code with the HIP library and imports nothing from it.
+
+What it computes, from "Dynamic Short Convolutions Improve Transformers" (reading
+note, section "Parameterization"):
+
+* eq. 1 (static): y_t = sum_{k=0}^{W-1} w_k * x_{t-k}, one filter w in R^{W x D}
+  for every t;
+* eq. 2 (dynamic): the same sum with a per-token filter w^{(t)};
+* eq. 3 (residual placement on Q, K, V): X <- X + dynamicShortConv(X);
+* head-wise parameterisation: one filter of W taps is shared by H consecutive
+  channels, so the per-token filter tensor is B x T x (D/H) x W (section
+  "Efficient training (Triton kernels)");
+* low-rank parameterisation: the generator D -> R -> W*D is affine ("all transforms
+  have a bias"); the fused kernel takes the rank-R activations z (B x T x R) and the
+  second projection U (R x (D*W)) and forms z U + b.
+
+Readings where the page leaves a step open (each also listed in the design notes):
+
+* positions before t = 0 of every sequence hold zeros (the sum simply has no term
+  for t - k < 0);
+* the filter tensor keeps the W taps of one group contiguous: w[b, t, g, k], with
+  channel d using group g = d // H;
+* the low-rank column index of U and b is j = g * W + k, so z U + b reshapes directly
+  to (D/H, W);
+* the filters carry no nonlinearity (affine generator), and the convolution itself
+  has no bias;
+* the generator's input is the normalised block input, not X itself, so x and w are
+  independent inputs and dx has no path through w.
+
+Everything is float64; bfloat16 and float32 inputs are exact in float64. Arrays are
+processed one sequence (one b) at a time; no blocking, fusion or reordering beyond
+the sums written out below.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _filters_for_sequence(w: np.ndarray, b: int, D: int, H: int) -> np.ndarray:
+    """Per-channel filters of sequence b as a (T, D, W) or (D, W) array.
+
+    Head-wise sharing: channel d reads group d // H, i.e. each filter is repeated over H
+    consecutive channels ("Parameterization", head-wise parameterisation).
+    Static filters (eq. 1) have shape (D/H, W) and are the same for every (b, t).
+    """
+    if w.ndim == 2:  # static (D/H, W)
+        return np.repeat(w, H, axis=0)
+    return np.repeat(w[b], H, axis=1)  # (T, D/H, W) -> (T, D, W)
+
+
+def conv_fwd(x, w, H: int = 1) -> np.ndarray:
+    """Forward of eq. 2 + eq. 3: y_t = x_t + sum_{k<W} w_k^{(t)} * x_{t-k}, zero for t-k < 0.
+
+    x: (B, T, D). w: (B, T, D/H, W) per-token filters, or (D/H, W) for a static filter
+    (eq. 1). Returns y: (B, T, D) in float64.
+    """
+    x = _f64(x)
+    w = _f64(w)
+    B, T, D = x.shape
+    W = w.shape[-1]
+    y = x.copy()  # residual, eq. 3
+    for b in range(B):
+        wf = _filters_for_sequence(w, b, D, H)
+        for k in range(W):
+            if k >= T:
+                break
+            # term k reads x_{t-k}; rows t < k have no term (zeros before t = 0)
+            if wf.ndim == 2:
+                y[b, k:, :] += wf[None, :, k] * x[b, : T - k, :]
+            else:
+                y[b, k:, :] += wf[k:, :, k] * x[b, : T - k, :]
+    return y
+
+
+def conv_bwd(x, w, dy, H: int = 1):
+    """Gradients of <dy, y> for y = conv_fwd(x, w, H).
+
+    Since y is bilinear in (x, w):
+      dx_s = dy_s + sum_k w_k^{(s+k)} * dy_{s+k}            (terms with s + k < T),
+      dwfull[t, d, k] = dy_t[d] * x_{t-k}[d]               (zero for t - k < 0),
+      dw[t, g, k] = sum over the H channels d of group g of dwfull[t, d, k];
+    for a static filter, dw[g, k] is additionally summed over every (b, t).
+    Returns (dx, dw) in float64, dw in the layout of w.
+    """
+    x = _f64(x)
+    w = _f64(w)
+    dy = _f64(dy)
+    B, T, D = x.shape
+    W = w.shape[-1]
+    G = D // H
+    dx = dy.copy()  # residual path
+    if w.ndim == 2:
+        dw = np.zeros((G, W))
+    else:
+        dw = np.zeros((B, T, G, W))
+    for b in range(B):
+        wf = _filters_for_sequence(w, b, D, H)
+        dwf = np.zeros((T, D, W))
+        for k in range(W):
+            if k >= T:
+                break
+            if wf.ndim == 2:
+                dx[b, : T - k, :] += wf[None, :, k] * dy[b, k:, :]
+            else:
+                dx[b, : T - k, :] += wf[k:, :, k] * dy[b, k:, :]
+            dwf[k:, :, k] = dy[b, k:, :] * x[b, : T - k, :]
+        dwg = dwf.reshape(T, G, H, W).sum(axis=2)  # sum over the H channels of a group
+        if w.ndim == 2:
+            dw += dwg.sum(axis=0)
+        else:
+            dw[b] = dwg
+    return dx, dw
+
+
+def lowrank_filters(z, U, bias, W: int) -> np.ndarray:
+    """Per-token filters of the low-rank generator's second projection: w = z U + b.
+
+    z: (B, T, R); U: (R, (D/H)*W); bias: ((D/H)*W,) or None. Column j = g*W + k.
+    Returns (B, T, D/H, W) float64.
+    """
+    z = _f64(z)
+    U = _f64(U)
+    B, T, R = z.shape
+    J = U.shape[1]
+    wf = np.matmul(z.reshape(B * T, R), U).reshape(B, T, J)
+    if bias is not None:
+        wf = wf + _f64(bias)[None, None, :]
+    return wf.reshape(B, T, J // W, W)
+
+
+def lowrank_fwd(x, z, U, bias, W: int, H: int = 1) -> np.ndarray:
+    """Low-rank form: filters z U + b (never stored by the kernel), then eq. 2 + eq. 3."""
+    return conv_fwd(x, lowrank_filters(z, U, bias, W), H)
+
+
+def lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1):
+    """Gradients of <dy, y> for y = lowrank_fwd(x, z, U, bias, W, H).
+
+    With g_t = dw_t flattened to (D/H)*W columns (from conv_bwd):
+      dz_t = g_t U^T,   dU = sum_t z_t^T g_t,   db = sum_t g_t.
+    Returns (dx, dz, dU, db) in float64.
+    """
+    z = _f64(z)
+    U = _f64(U)
+    wf = lowrank_filters(z, U, bias, W)
+    dx, dw = conv_bwd(x, wf, dy, H)
+    B, T, R = z.shape
+    J = U.shape[1]
+    g = dw.reshape(B * T, J)
+    zf = z.reshape(B * T, R)
+    dz = np.matmul(g, U.T).reshape(B, T, R)
+    dU = np.matmul(zf.T, g)
+    db = g.sum(axis=0)
+    return dx, dz, dU, db

@@ -1,0 +1,570 @@
+"""Pins of the float64 oracle against facts that do not come from the oracle itself.
+
+Sources of truth used here (all from "Dynamic Short Convolutions Improve Transformers",
+reading note, section "Parameterization", and plain mathematics):
+
+* hand-worked examples of eq. 1-3, the head-wise and the low-rank parameterisation
+  (tests/golden/handworked.json, every value derived by hand with its arithmetic);
+* eq. 1 is an ordinary causal FIR filter, so the static form must agree with
+  numpy.convolve, scipy.signal.lfilter and torch's grouped conv1d (cross-correlation,
+  hence a flipped kernel);
+* the banded-matrix form of eq. 2 + 3, built entry by entry from index arithmetic:
+  y = M x and, since the loss <dy, y> is linear, dx = M^T dy;
+* <dy, y> is affine in every single scalar input (y is linear in x for fixed filters
+  and linear in the filters for fixed x; the low-rank filters are affine in z, U, b),
+  so central differences give every gradient exactly up to rounding;
+* closed forms (zero filters, one-hot taps, constant input), causality, batch
+  independence and the adjoint identities.
+
+The mutation tests at the end plant typical mistakes in copies of the oracle and
+check that these pins reject every one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+import torch
+
+from oracle import conv_bwd, conv_fwd, lowrank_bwd, lowrank_filters, lowrank_fwd
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "handworked.json")
+
+
+def _rng(*seed):
+    return np.random.default_rng(list(seed))
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+# ----------------------------------------------------------------------------------
+# pin helpers, parametrised over the implementation so that mutants can be checked
+# ----------------------------------------------------------------------------------
+
+
+def pin_golden_fwd(fwd) -> bool:
+    ok = True
+    for c in _golden_cases():
+        x = np.array(c["x"], float)[None]
+        H = c["H"]
+        if "w" in c:
+            y = fwd(x, np.array(c["w"], float)[None], H)
+        elif "w_static" in c:
+            y = fwd(x, np.array(c["w_static"], float), H)
+        else:
+            continue
+        ok &= np.array_equal(y[0], np.array(c["y"], float))
+    return bool(ok)
+
+
+def pin_golden_bwd(bwd) -> bool:
+    ok = True
+    for c in _golden_cases():
+        x = np.array(c["x"], float)[None]
+        dy = np.array(c["dy"], float)[None]
+        H = c["H"]
+        if "w" in c:
+            dx, dw = bwd(x, np.array(c["w"], float)[None], dy, H)
+            ok &= np.array_equal(dx[0], c["dx"]) and np.array_equal(dw[0], c["dw"])
+        elif "w_static" in c:
+            dx, dw = bwd(x, np.array(c["w_static"], float), dy, H)
+            ok &= np.array_equal(dx[0], c["dx"]) and np.array_equal(dw, c["dw_static"])
+    return bool(ok)
+
+
+def _banded_matrix(wfull_bd, T, W):
+    """M[t, s] = [t == s] + w^{(t)}_{t-s} for 0 <= t - s < W (eq. 2 + 3 for one channel)."""
+    M = np.zeros((T, T))
+    for t in range(T):
+        M[t, t] += 1.0
+        for s in range(T):
+            k = t - s
+            if 0 <= k < W:
+                M[t, s] += wfull_bd[t][k]
+    return M
+
+
+def _channel_filters(w, b, d, H, T):
+    """Filter taps of channel d of sequence b at every t, by explicit index arithmetic."""
+    g = d // H
+    if w.ndim == 2:
+        return [w[g] for _ in range(T)]
+    return [w[b, t, g] for t in range(T)]
+
+
+def pin_matrix_form(fwd, bwd, B, T, D, W, H, static, seed) -> bool:
+    r = _rng(11, seed)
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    w = r.standard_normal((D // H, W)) if static else r.standard_normal((B, T, D // H, W))
+    y = fwd(x, w, H)
+    dx, _ = bwd(x, w, dy, H)
+    ok = True
+    for b in range(B):
+        for d in range(D):
+            M = _banded_matrix(_channel_filters(w, b, d, H, T), T, W)
+            ok &= np.allclose(y[b, :, d], M @ x[b, :, d], rtol=0, atol=1e-13)
+            ok &= np.allclose(dx[b, :, d], M.T @ dy[b, :, d], rtol=0, atol=1e-13)
+    return bool(ok)
+
+
+def pin_static_library(fwd, B, T, D, W, H, seed) -> bool:
+    r = _rng(12, seed)
+    x = r.standard_normal((B, T, D))
+    w = r.standard_normal((D // H, W))
+    y = fwd(x, w, H)
+    ok = True
+    for b in range(B):
+        for d in range(D):
+            taps = w[d // H]
+            ref = np.convolve(x[b, :, d], taps)[:T]  # true convolution, no flip
+            ok &= np.allclose(y[b, :, d] - x[b, :, d], ref, rtol=0, atol=1e-13)
+            ref2 = scipy.signal.lfilter(taps, [1.0], x[b, :, d])  # causal FIR
+            ok &= np.allclose(y[b, :, d] - x[b, :, d], ref2, rtol=0, atol=1e-12)
+    # torch conv1d is cross-correlation: flip the taps and pad W-1 zeros on the left
+    xt = torch.from_numpy(x).permute(0, 2, 1)  # (B, D, T)
+    wt = torch.from_numpy(np.repeat(w, H, axis=0)[:, ::-1].copy()).unsqueeze(1)  # (D, 1, W)
+    ref3 = torch.nn.functional.conv1d(torch.nn.functional.pad(xt, (W - 1, 0)), wt, groups=D)
+    ok &= np.allclose(y - x, ref3.permute(0, 2, 1).numpy(), rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def _fd_check(loss, arrays, grads, tol=1e-10) -> bool:
+    """Central differences of an affine-per-coordinate loss, every coordinate."""
+    ok = True
+    for a, g in zip(arrays, grads):
+        flat = a.reshape(-1)
+        gf = np.asarray(g).reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + 1.0
+            lp = loss()
+            flat[i] = old - 1.0
+            lm = loss()
+            flat[i] = old
+            fd = (lp - lm) / 2.0
+            ok &= abs(fd - gf[i]) <= tol * max(1.0, abs(fd))
+    return bool(ok)
+
+
+def pin_fd_conv(fwd, bwd, B, T, D, W, H, static, seed) -> bool:
+    r = _rng(13, seed)
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    w = r.standard_normal((D // H, W)) if static else r.standard_normal((B, T, D // H, W))
+    dx, dw = bwd(x, w, dy, H)
+    return _fd_check(lambda: float(np.sum(dy * fwd(x, w, H))), [x, w], [dx, dw])
+
+
+def pin_fd_lowrank(fwd, bwd, B, T, D, W, H, R, seed) -> bool:
+    r = _rng(14, seed)
+    G = D // H
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    z = r.standard_normal((B, T, R))
+    U = r.standard_normal((R, G * W))
+    bias = r.standard_normal(G * W)
+    dx, dz, dU, db = bwd(x, z, U, bias, dy, W, H)
+    loss = lambda: float(np.sum(dy * fwd(x, z, U, bias, W, H)))  # noqa: E731
+    return _fd_check(loss, [x, z, U, bias], [dx, dz, dU, db])
+
+
+# ----------------------------------------------------------------------------------
+# the pins applied to the oracle
+# ----------------------------------------------------------------------------------
+
+
+def test_golden_handworked_fwd_bwd():
+    assert pin_golden_fwd(conv_fwd)
+    assert pin_golden_bwd(conv_bwd)
+
+
+def test_golden_handworked_lowrank():
+    for c in _golden_cases():
+        if "z" not in c:
+            continue
+        x = np.array(c["x"], float)[None]
+        z = np.array(c["z"], float)[None]
+        U = np.array(c["U"], float)
+        bias = np.array(c["b"], float)
+        dy = np.array(c["dy"], float)[None]
+        W = U.shape[1] // x.shape[2] * c["H"]
+        y = lowrank_fwd(x, z, U, bias, W, c["H"])
+        dx, dz, dU, db = lowrank_bwd(x, z, U, bias, dy, W, c["H"])
+        assert np.array_equal(y[0], c["y"])
+        assert np.array_equal(dx[0], c["dx"])
+        assert np.array_equal(dz[0], c["dz"])
+        assert np.array_equal(dU, c["dU"])
+        assert np.array_equal(db, c["db"])
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("H", [1, 2, 4])
+@pytest.mark.parametrize("T", [1, 3, 9])
+@pytest.mark.parametrize("static", [False, True])
+def test_matrix_form(W, H, T, static):
+    assert pin_matrix_form(conv_fwd, conv_bwd, 2, T, 8, W, H, static, seed=W * 100 + H * 10 + T)
+
+
+@pytest.mark.parametrize("W", [1, 3, 4, 5])
+@pytest.mark.parametrize("H", [1, 4])
+def test_static_matches_library_fir(W, H):
+    assert pin_static_library(conv_fwd, 2, 17, 8, W, H, seed=W + 7 * H)
+
+
+def test_constant_in_t_dynamic_equals_static():
+    r = _rng(15)
+    B, T, D, W, H = 2, 13, 8, 4, 2
+    x = r.standard_normal((B, T, D))
+    ws = r.standard_normal((D // H, W))
+    wd = np.broadcast_to(ws, (B, T, D // H, W)).copy()
+    dy = r.standard_normal((B, T, D))
+    assert np.allclose(conv_fwd(x, wd, H), conv_fwd(x, ws, H), rtol=0, atol=1e-14)
+    dxd, dwd = conv_bwd(x, wd, dy, H)
+    dxs, dws = conv_bwd(x, ws, dy, H)
+    assert np.allclose(dxd, dxs, rtol=0, atol=1e-13)
+    assert np.allclose(dwd.sum(axis=(0, 1)), dws, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("static", [False, True])
+@pytest.mark.parametrize("W,H,T", [(1, 1, 4), (3, 2, 5), (4, 1, 6), (5, 4, 3), (4, 2, 7)])
+def test_finite_differences_conv(W, H, T, static):
+    assert pin_fd_conv(conv_fwd, conv_bwd, 2, T, 4 * H if H > 1 else 4, W, H, static, seed=W * 31 + T)
+
+
+@pytest.mark.parametrize("W,H,R,T", [(4, 1, 3, 6), (2, 2, 2, 5), (5, 1, 1, 4), (3, 4, 5, 7)])
+def test_finite_differences_lowrank(W, H, R, T):
+    assert pin_fd_lowrank(lowrank_fwd, lowrank_bwd, 2, T, 8, W, H, R, seed=W * 17 + R)
+
+
+def test_closed_form_zero_filter():
+    r = _rng(16)
+    x = r.standard_normal((2, 11, 8))
+    dy = r.standard_normal((2, 11, 8))
+    w = np.zeros((2, 11, 8, 4))
+    assert np.array_equal(conv_fwd(x, w), x)
+    dx, _ = conv_bwd(x, w, dy)
+    assert np.array_equal(dx, dy)
+
+
+@pytest.mark.parametrize("j", [0, 1, 2, 3, 4])
+def test_closed_form_one_hot_tap(j):
+    r = _rng(17, j)
+    B, T, D, W = 2, 9, 6, 5
+    x = r.standard_normal((B, T, D))
+    w = np.zeros((B, T, D, W))
+    w[..., j] = 1.0
+    expect = x.copy()
+    expect[:, j:, :] += x[:, : T - j, :]  # y_t = x_t + x_{t-j} for t >= j
+    assert np.array_equal(conv_fwd(x, w), expect)
+
+
+def test_closed_form_constant_input():
+    r = _rng(18)
+    B, T, D, W, H = 2, 7, 4, 4, 2
+    c = 1.75
+    x = np.full((B, T, D), c)
+    w = r.standard_normal((B, T, D // H, W))
+    y = conv_fwd(x, w, H)
+    for b in range(B):
+        for t in range(T):
+            for d in range(D):
+                taps = sum(w[b, t, d // H, k] for k in range(min(W - 1, t) + 1))
+                assert abs(y[b, t, d] - c * (1.0 + taps)) < 1e-13
+
+
+def test_causality_band():
+    r = _rng(19)
+    B, T, D, W, H = 2, 12, 4, 4, 2
+    x = r.standard_normal((B, T, D))
+    w = r.standard_normal((B, T, D // H, W))
+    y0 = conv_fwd(x, w, H)
+    for (b, s, d) in [(0, 0, 0), (1, 5, 3), (0, 11, 2), (1, 9, 1)]:
+        xp = x.copy()
+        xp[b, s, d] += 1.0
+        dif = conv_fwd(xp, w, H) - y0
+        expect = np.zeros_like(dif)
+        for t in range(s, min(T, s + W)):
+            expect[b, t, d] = (1.0 if t == s else 0.0) + w[b, t, d // H, t - s]
+        assert np.allclose(dif, expect, rtol=0, atol=1e-13)
+
+
+def test_headwise_equals_broadcast_perchannel():
+    r = _rng(20)
+    B, T, D, W, H = 2, 10, 16, 3, 4
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    w = r.standard_normal((B, T, D // H, W))
+    wb = np.zeros((B, T, D, W))
+    for d in range(D):  # explicit: channel d takes the filter of group d // H
+        wb[:, :, d, :] = w[:, :, d // H, :]
+    assert np.allclose(conv_fwd(x, w, H), conv_fwd(x, wb, 1), rtol=0, atol=1e-14)
+    dxh, dwh = conv_bwd(x, w, dy, H)
+    dxp, dwp = conv_bwd(x, wb, dy, 1)
+    assert np.allclose(dxh, dxp, rtol=0, atol=1e-13)
+    grouped = np.zeros_like(dwh)
+    for d in range(D):
+        grouped[:, :, d // H, :] += dwp[:, :, d, :]
+    assert np.allclose(dwh, grouped, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("zero", ["U", "z"])
+def test_lowrank_reduces_to_static_bias_filter(zero):
+    r = _rng(21)
+    B, T, D, W, H, R = 2, 9, 8, 4, 2, 3
+    x = r.standard_normal((B, T, D))
+    z = r.standard_normal((B, T, R))
+    U = r.standard_normal((R, D // H * W))
+    bias = r.standard_normal(D // H * W)
+    if zero == "U":
+        U[:] = 0
+    else:
+        z[:] = 0
+    y = lowrank_fwd(x, z, U, bias, W, H)
+    taps = bias.reshape(D // H, W)  # column j = g * W + k
+    for b in range(B):
+        for d in range(D):
+            ref = np.convolve(x[b, :, d], taps[d // H])[:T]
+            assert np.allclose(y[b, :, d] - x[b, :, d], ref, rtol=0, atol=1e-13)
+
+
+def test_lowrank_rank_one_closed_form():
+    """R = 1, U = u (one row): w^{(t)} = z_t u + b, so y - x is linear in z_t per tap."""
+    r = _rng(22)
+    B, T, D, W = 1, 8, 4, 3
+    x = r.standard_normal((B, T, D))
+    z = r.standard_normal((B, T, 1))
+    U = r.standard_normal((1, D * W))
+    bias = r.standard_normal(D * W)
+    y = lowrank_fwd(x, z, U, bias, W, 1)
+    for t in range(T):
+        for d in range(D):
+            acc = x[0, t, d]
+            for k in range(W):
+                if t - k >= 0:
+                    acc += (z[0, t, 0] * U[0, d * W + k] + bias[d * W + k]) * x[0, t - k, d]
+            assert abs(acc - y[0, t, d]) < 1e-12
+
+
+@pytest.mark.parametrize("H,static", [(1, False), (4, False), (1, True), (4, True)])
+def test_adjoint_identities(H, static):
+    r = _rng(23, H, int(static))
+    B, T, D, W = 2, 96, 32, 4
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    w = r.standard_normal((D // H, W)) if static else r.standard_normal((B, T, D // H, W))
+    dx, dw = conv_bwd(x, w, dy, H)
+    dlx = r.standard_normal(x.shape)
+    dlw = r.standard_normal(w.shape)
+    lhs = np.sum((dx - dy) * dlx)
+    rhs = np.sum(dy * (conv_fwd(dlx, w, H) - dlx))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(rhs))
+    lhs = np.sum(dw * dlw)
+    rhs = np.sum(dy * (conv_fwd(x, dlw, H) - x))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(rhs))
+
+
+def test_adjoint_identities_lowrank():
+    r = _rng(24)
+    B, T, D, W, H, R = 2, 64, 16, 4, 1, 6
+    G = D // H
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    z = r.standard_normal((B, T, R))
+    U = r.standard_normal((R, G * W))
+    bias = r.standard_normal(G * W)
+    dx, dz, dU, db = lowrank_bwd(x, z, U, bias, dy, W, H)
+
+    def cx(filters):  # the conv part as a linear map of the filters, x fixed
+        return conv_fwd(x, filters, H) - x
+
+    dz_dir = r.standard_normal(z.shape)
+    dU_dir = r.standard_normal(U.shape)
+    db_dir = r.standard_normal(bias.shape)
+    checks = [
+        (np.sum(dz * dz_dir), np.sum(dy * cx(lowrank_filters(dz_dir, U, None, W)))),
+        (np.sum(dU * dU_dir), np.sum(dy * cx(lowrank_filters(z, dU_dir, None, W)))),
+        (np.sum(db * db_dir), np.sum(dy * cx(np.broadcast_to(db_dir.reshape(G, W), (B, T, G, W))))),
+    ]
+    for lhs, rhs in checks:
+        assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(rhs))
+
+
+def test_batch_independence():
+    r = _rng(25)
+    B, T, D, W, H = 3, 10, 8, 4, 2
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    w = r.standard_normal((B, T, D // H, W))
+    perm = [2, 0, 1]
+    y = conv_fwd(x, w, H)
+    assert np.array_equal(conv_fwd(x[perm], w[perm], H), y[perm])
+    dx, dw = conv_bwd(x, w, dy, H)
+    dxp, dwp = conv_bwd(x[perm], w[perm], dy[perm], H)
+    assert np.array_equal(dxp, dx[perm]) and np.array_equal(dwp, dw[perm])
+
+
+# ----------------------------------------------------------------------------------
+# planted mistakes: each mutant of the oracle must be rejected by at least one pin
+# ----------------------------------------------------------------------------------
+
+
+def _mut_fwd_flipped(x, w, H=1):
+    return conv_fwd(x, w[..., ::-1], H)
+
+
+def _mut_fwd_no_residual(x, w, H=1):
+    return conv_fwd(x, w, H) - np.asarray(x, float)
+
+
+def _mut_fwd_off_by_one(x, w, H=1):
+    x = np.asarray(x, float)
+    w = np.asarray(w, float)
+    B, T, D = x.shape
+    W = w.shape[-1]
+    y = x.copy()
+    for b in range(B):
+        wf = np.repeat(w, H, axis=0) if w.ndim == 2 else np.repeat(w[b], H, axis=1)
+        for k in range(W):
+            s = k + 1  # wrong: reads x_{t-k-1}
+            if s >= T:
+                break
+            y[b, s:, :] += (wf[None, :, k] if wf.ndim == 2 else wf[s:, :, k]) * x[b, : T - s, :]
+    return y
+
+
+def _mut_fwd_wraparound(x, w, H=1):
+    x = np.asarray(x, float)
+    w = np.asarray(w, float)
+    B, T, D = x.shape
+    y = x.copy()
+    for b in range(B):
+        wf = np.repeat(w, H, axis=0)[None] if w.ndim == 2 else np.repeat(w[b], H, axis=1)
+        for k in range(w.shape[-1]):
+            y[b] += wf[..., k] * np.roll(x[b], k, axis=0)  # wrong: circular instead of zeros
+    return y
+
+
+def _mut_fwd_group_modulo(x, w, H=1):
+    w = np.asarray(w, float)
+    D = np.asarray(x).shape[2]
+    G = D // H
+    idx = np.arange(D) % G  # wrong: tiles the filters instead of repeating them
+    if w.ndim == 2:
+        return conv_fwd(x, w[idx], 1)
+    return conv_fwd(x, w[:, :, idx, :], 1)
+
+
+def _mut_fwd_filter_of_source(x, w, H=1):
+    """Wrong token index: uses w^{(t-k)} instead of w^{(t)} for the tap reading x_{t-k}."""
+    x = np.asarray(x, float)
+    w = np.asarray(w, float)
+    if w.ndim == 2:
+        return conv_fwd(x, w, H)
+    B, T, D = x.shape
+    y = x.copy()
+    for b in range(B):
+        wf = np.repeat(w[b], H, axis=1)
+        for k in range(w.shape[-1]):
+            if k >= T:
+                break
+            y[b, k:, :] += wf[: T - k, :, k] * x[b, : T - k, :]
+    return y
+
+
+def _mut_bwd_dx_same_token(x, w, dy, H=1):
+    """Wrong: dx uses w^{(s)} instead of w^{(s+k)}."""
+    x = np.asarray(x, float)
+    w = np.asarray(w, float)
+    dy = np.asarray(dy, float)
+    _, dw = conv_bwd(x, w, dy, H)
+    if w.ndim == 2:
+        return conv_bwd(x, w, dy, H)
+    B, T, D = x.shape
+    dx = dy.copy()
+    for b in range(B):
+        wf = np.repeat(w[b], H, axis=1)
+        for k in range(w.shape[-1]):
+            if k >= T:
+                break
+            dx[b, : T - k, :] += wf[: T - k, :, k] * dy[b, k:, :]
+    return dx, dw
+
+
+def _mut_bwd_dw_flipped(x, w, dy, H=1):
+    dx, dw = conv_bwd(x, w, dy, H)
+    return dx, dw[..., ::-1]
+
+
+def _mut_bwd_dw_no_group_sum(x, w, dy, H=1):
+    dx, dw = conv_bwd(x, w, dy, H)
+    return dx, dw / H  # wrong: averages instead of summing the H channels
+
+
+FWD_MUTANTS = [
+    _mut_fwd_flipped,
+    _mut_fwd_no_residual,
+    _mut_fwd_off_by_one,
+    _mut_fwd_wraparound,
+    _mut_fwd_group_modulo,
+    _mut_fwd_filter_of_source,
+]
+BWD_MUTANTS = [_mut_bwd_dx_same_token, _mut_bwd_dw_flipped, _mut_bwd_dw_no_group_sum]
+
+
+@pytest.mark.parametrize("mutant", FWD_MUTANTS, ids=lambda f: f.__name__)
+def test_pins_reject_forward_mutant(mutant):
+    verdicts = [
+        pin_golden_fwd(mutant),
+        pin_matrix_form(mutant, conv_bwd, 1, 7, 8, 3, 2, False, seed=1),
+        pin_static_library(mutant, 1, 9, 8, 3, 2, seed=2),
+    ]
+    assert not all(verdicts)
+
+
+@pytest.mark.parametrize("mutant", BWD_MUTANTS, ids=lambda f: f.__name__)
+def test_pins_reject_backward_mutant(mutant):
+    verdicts = [
+        pin_golden_bwd(mutant),
+        pin_fd_conv(conv_fwd, mutant, 1, 5, 4, 3, 2, False, seed=3),
+    ]
+    assert not all(verdicts)
+
+
+def _mut_lr_dU_transposed_z(x, z, U, bias, dy, W, H=1):
+    dx, dz, dU, db = lowrank_bwd(x, z, U, bias, dy, W, H)
+    return dx, dz, dU[::-1], db  # wrong row order of dU
+
+
+def _mut_lr_dz_no_taps(x, z, U, bias, dy, W, H=1):
+    dx, dz, dU, db = lowrank_bwd(x, z, U, bias, dy, W, H)
+    return dx, dz * 0.5, dU, db
+
+
+def _mut_lr_column_order(x, z, U, bias, W, H=1):
+    """Wrong column order: j = k * G + g instead of g * W + k."""
+    wf = lowrank_filters(z, U, bias, W)
+    B, T, G, _ = wf.shape
+    flat = wf.reshape(B, T, G * W)
+    return conv_fwd(x, flat.reshape(B, T, W, G).transpose(0, 1, 3, 2), H)
+
+
+def test_pins_reject_lowrank_mutants():
+    for mut in (_mut_lr_dU_transposed_z, _mut_lr_dz_no_taps):
+        assert not pin_fd_lowrank(lowrank_fwd, mut, 1, 5, 4, 3, 1, 2, seed=5)
+    # the column-order mutant: the hand-worked case has D/H = 1 so it cannot tell; the
+    # U = 0 reduction to a static filter b reshaped (D/H, W) does
+    r = _rng(26)
+    B, T, D, W, R = 1, 9, 4, 3, 2
+    x = r.standard_normal((B, T, D))
+    z = r.standard_normal((B, T, R))
+    U = np.zeros((R, D * W))
+    bias = r.standard_normal(D * W)
+    y = _mut_lr_column_order(x, z, U, bias, W)
+    taps = bias.reshape(D, W)
+    ref = np.stack([np.convolve(x[0, :, d], taps[d])[:T] for d in range(D)], axis=1)
+    assert not np.allclose(y[0] - x[0], ref, atol=1e-12)
