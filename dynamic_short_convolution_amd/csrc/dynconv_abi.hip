@@ -1,0 +1,378 @@
+// C ABI of libdynconv: argument checks (before any HIP call) and dispatch to the
+// kernel launchers. See include/dynconv.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include "dynconv_internal.hpp"
+
+namespace dynconv {
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int elem_bytes(dynconv_dtype dt) { return dt == DYNCONV_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % uint64_t(a)) == 0; }
+
+// Activation-shaped tensor [B,T,D] with strides s[0..2].
+struct Act {
+  const void* p;
+  const int64_t* s;
+};
+
+dynconv_status check_act(const void* p, const int64_t* s, bool required) {
+  if (p == nullptr) return required ? DYNCONV_ERR_INVALID_ARG : DYNCONV_OK;
+  if (s == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (s[2] != 1) return DYNCONV_ERR_UNSUPPORTED;
+  if (s[0] < 0 || s[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  return DYNCONV_OK;
+}
+
+// Every activation-shaped tensor must allow 4-byte lane vectors; `wide` reports whether
+// all of them also allow 16-byte vectors.
+bool act_align_ok(const Act* a, int n, int eb, int64_t align_bytes) {
+  for (int i = 0; i < n; ++i) {
+    if (a[i].p == nullptr) continue;
+    if (!aligned(a[i].p, align_bytes)) return false;
+    if ((a[i].s[0] * eb) % align_bytes != 0 || (a[i].s[1] * eb) % align_bytes != 0) return false;
+  }
+  return true;
+}
+
+dynconv_status check_common(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dt) {
+  if (dt != DYNCONV_F32 && dt != DYNCONV_BF16) return DYNCONV_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || D < 0) return DYNCONV_ERR_INVALID_ARG;
+  if (W < 1 || H < 1) return DYNCONV_ERR_INVALID_ARG;
+  if (W > 5) return DYNCONV_ERR_UNSUPPORTED;
+  if (D > 0 && D % H != 0) return DYNCONV_ERR_INVALID_ARG;
+  if (H > 1 && !is_pow2(H)) return DYNCONV_ERR_UNSUPPORTED;
+  if (B > INT32_MAX || T > INT32_MAX || D > INT32_MAX) return DYNCONV_ERR_UNSUPPORTED;
+  return DYNCONV_OK;
+}
+
+// The lane layout of the streaming kernels puts VEC channels on a lane and H / VEC lanes
+// on a group; bf16 lanes hold channel pairs, so D must be even.
+dynconv_status check_stream_layout(int64_t D, int32_t H, int eb, bool wide_ok) {
+  const int small = 4 / eb;
+  const int wide = 16 / eb;
+  if (D % small != 0) return DYNCONV_ERR_UNSUPPORTED;
+  const int vec = (H > 1 && wide_ok && H % wide == 0 && D % wide == 0) ? wide : small;
+  if (H > 1 && H / vec > kWaveSize) return DYNCONV_ERR_UNSUPPORTED;
+  return DYNCONV_OK;
+}
+
+struct FilterInfo {
+  bool is_static;
+};
+
+dynconv_status check_filter(const void* w, const int64_t* ws, int32_t W, int32_t H, int eb, bool bwd,
+                            FilterInfo* fi) {
+  if (w == nullptr || ws == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (ws[3] != 1 || ws[2] != W) return DYNCONV_ERR_UNSUPPORTED;
+  if (ws[0] < 0 || ws[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  fi->is_static = ws[0] == 0 && ws[1] == 0;
+  if (bwd && !fi->is_static && (ws[0] == 0 || ws[1] == 0)) return DYNCONV_ERR_UNSUPPORTED;
+  if (H == 1) {
+    if (!aligned(w, 4) || (ws[0] * eb) % 4 != 0 || (ws[1] * eb) % 4 != 0) return DYNCONV_ERR_UNSUPPORTED;
+  } else if (!aligned(w, eb)) {
+    return DYNCONV_ERR_UNSUPPORTED;
+  }
+  return DYNCONV_OK;
+}
+
+}  // namespace
+
+dynconv_status record_hip_error(hipError_t e) {
+  g_last_hip_error = int(e);
+  return DYNCONV_ERR_HIP;
+}
+
+int last_hip_error() { return g_last_hip_error; }
+
+}  // namespace dynconv
+
+using namespace dynconv;
+
+extern "C" {
+
+const char* dynconv_status_string(dynconv_status s) {
+  switch (s) {
+    case DYNCONV_OK: return "DYNCONV_OK";
+    case DYNCONV_ERR_INVALID_ARG: return "DYNCONV_ERR_INVALID_ARG";
+    case DYNCONV_ERR_UNSUPPORTED: return "DYNCONV_ERR_UNSUPPORTED";
+    case DYNCONV_ERR_WORKSPACE: return "DYNCONV_ERR_WORKSPACE";
+    case DYNCONV_ERR_HIP: return "DYNCONV_ERR_HIP";
+  }
+  return "DYNCONV_UNKNOWN_STATUS";
+}
+
+int dynconv_last_hip_error(void) { return dynconv::last_hip_error(); }
+
+dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws, void* y,
+                           const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                           dynconv_dtype dtype, void* stream) {
+  dynconv_status st = check_common(B, T, D, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
+  if ((st = check_act(y, ys, true)) != DYNCONV_OK) return st;
+  const int eb = elem_bytes(dtype);
+  FilterInfo fi{};
+  if ((st = check_filter(w, ws, W, H, eb, false, &fi)) != DYNCONV_OK) return st;
+  if (y == x || y == w) return DYNCONV_ERR_INVALID_ARG;
+  if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
+  const Act acts[2] = {{x, xs}, {y, ys}};
+  if (!act_align_ok(acts, 2, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
+  const bool wide_ok = act_align_ok(acts, 2, eb, 16);
+  if ((st = check_stream_layout(D, H, eb, wide_ok)) != DYNCONV_OK) return st;
+
+  const StreamPlan plan = plan_stream(B, T, D, H, eb, wide_ok, false, fi.is_static);
+  StreamParams p{};
+  p.x = x;
+  p.w = w;
+  p.out = y;
+  p.xs0 = xs[0];
+  p.xs1 = xs[1];
+  p.ws0 = ws[0];
+  p.ws1 = ws[1];
+  p.os0 = ys[0];
+  p.os1 = ys[1];
+  p.B = int32_t(B);
+  p.T = int32_t(T);
+  p.D = int32_t(D);
+  p.H = H;
+  p.G = int32_t(D / H);
+  p.L = plan.L;
+  p.nTw = plan.nTw;
+  p.nDw = plan.nDw;
+  p.WD = plan.WD;
+  p.WT = plan.WT;
+  p.nDb = plan.nDb;
+  p.nTb = plan.nTb;
+  return launch_stream_fwd(p, plan, W, dtype, fi.is_static, static_cast<hipStream_t>(stream));
+}
+
+size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int is_static,
+                                  dynconv_dtype dtype) {
+  if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK) return 0;
+  if (!is_static || B == 0 || T == 0 || D == 0) return 0;
+  const int eb = elem_bytes(dtype);
+  // The chunking does not depend on the vector width for the static partial count
+  // except through nDw; take the larger of the two possible chunk counts.
+  size_t best = 0;
+  for (int wide = 0; wide < 2; ++wide) {
+    const StreamPlan pl = plan_stream(B, T, D, H, eb, wide != 0, true, true);
+    const size_t need = size_t(B) * size_t(pl.nTw) * size_t(D / H) * size_t(W) * sizeof(float);
+    if (need > best) best = need;
+  }
+  return best;
+}
+
+dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const void* dy,
+                           const int64_t* dys, void* dx, const int64_t* dxs, void* dw, const int64_t* dws, int64_t B,
+                           int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  dynconv_status st = check_common(B, T, D, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  if (dx == nullptr && dw == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
+  if ((st = check_act(dy, dys, true)) != DYNCONV_OK) return st;
+  if ((st = check_act(dx, dxs, false)) != DYNCONV_OK) return st;
+  const int eb = elem_bytes(dtype);
+  FilterInfo fi{};
+  if ((st = check_filter(w, ws, W, H, eb, true, &fi)) != DYNCONV_OK) return st;
+  if (dw != nullptr && !fi.is_static) {
+    if (dws == nullptr) return DYNCONV_ERR_INVALID_ARG;
+    if (dws[3] != 1 || dws[2] != W || dws[0] <= 0 || dws[1] <= 0) return DYNCONV_ERR_UNSUPPORTED;
+    if (H == 1) {
+      if (!aligned(dw, 4) || (dws[0] * eb) % 4 != 0 || (dws[1] * eb) % 4 != 0) return DYNCONV_ERR_UNSUPPORTED;
+    } else if (!aligned(dw, eb)) {
+      return DYNCONV_ERR_UNSUPPORTED;
+    }
+  }
+  if (dw != nullptr && fi.is_static && !aligned(dw, 4)) return DYNCONV_ERR_UNSUPPORTED;
+  const void* ins[3] = {x, w, dy};
+  for (const void* in : ins) {
+    if (dx != nullptr && dx == in) return DYNCONV_ERR_INVALID_ARG;
+    if (dw != nullptr && dw == in) return DYNCONV_ERR_INVALID_ARG;
+  }
+  if (dx != nullptr && dx == dw) return DYNCONV_ERR_INVALID_ARG;
+  if (B == 0 || T == 0 || D == 0) {
+    return DYNCONV_OK;
+  }
+  const Act acts[3] = {{x, xs}, {dy, dys}, {dx, dxs}};
+  if (!act_align_ok(acts, 3, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
+  const bool wide_ok = act_align_ok(acts, 3, eb, 16);
+  if ((st = check_stream_layout(D, H, eb, wide_ok)) != DYNCONV_OK) return st;
+
+  const StreamPlan plan = plan_stream(B, T, D, H, eb, wide_ok, true, fi.is_static);
+  float* partial = nullptr;
+  if (fi.is_static && dw != nullptr) {
+    const size_t need = size_t(B) * size_t(plan.nTw) * size_t(D / H) * size_t(W) * sizeof(float);
+    if (workspace == nullptr || workspace_bytes < need) return DYNCONV_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DYNCONV_ERR_UNSUPPORTED;
+    partial = static_cast<float*>(workspace);
+  }
+  StreamParams p{};
+  p.x = x;
+  p.w = w;
+  p.dy = dy;
+  p.out = dx;
+  p.dw = fi.is_static ? nullptr : dw;
+  p.partial = partial;
+  p.xs0 = xs[0];
+  p.xs1 = xs[1];
+  p.ws0 = ws[0];
+  p.ws1 = ws[1];
+  p.dys0 = dys[0];
+  p.dys1 = dys[1];
+  if (dx != nullptr) {
+    p.os0 = dxs[0];
+    p.os1 = dxs[1];
+  }
+  if (dw != nullptr && !fi.is_static) {
+    p.dws0 = dws[0];
+    p.dws1 = dws[1];
+  }
+  p.B = int32_t(B);
+  p.T = int32_t(T);
+  p.D = int32_t(D);
+  p.H = H;
+  p.G = int32_t(D / H);
+  p.L = plan.L;
+  p.nTw = plan.nTw;
+  p.nDw = plan.nDw;
+  p.WD = plan.WD;
+  p.WT = plan.WT;
+  p.nDb = plan.nDb;
+  p.nTb = plan.nTb;
+  return launch_stream_bwd(p, plan, W, dtype, fi.is_static, fi.is_static ? static_cast<float*>(dw) : nullptr,
+                           static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// Low-rank form
+// ---------------------------------------------------------------------------------
+namespace {
+
+dynconv_status check_lowrank(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                             int64_t ldu, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                             dynconv_dtype dtype) {
+  dynconv_status st = check_common(B, T, D, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  if (R < 1) return DYNCONV_ERR_INVALID_ARG;
+  if (R > 128) return DYNCONV_ERR_UNSUPPORTED;
+  if (H != 1) return DYNCONV_ERR_UNSUPPORTED;  // head-wise low-rank generation is not built
+  if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
+  if (z == nullptr || zs == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (zs[2] != 1) return DYNCONV_ERR_UNSUPPORTED;
+  if (zs[0] < 0 || zs[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (U == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (ldu < (D / H) * W) return DYNCONV_ERR_INVALID_ARG;
+  return DYNCONV_OK;
+}
+
+LowRankParams lowrank_params(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                             int64_t ldu, const void* bias, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                             int32_t R, const LowRankPlan& plan) {
+  LowRankParams p{};
+  p.x = x;
+  p.z = z;
+  p.U = U;
+  p.bias = bias;
+  p.xs0 = xs[0];
+  p.xs1 = xs[1];
+  p.zs0 = zs[0];
+  p.zs1 = zs[1];
+  p.ldu = ldu;
+  p.B = int32_t(B);
+  p.T = int32_t(T);
+  p.D = int32_t(D);
+  p.H = H;
+  p.G = int32_t(D / H);
+  p.R = R;
+  p.J = int32_t((D / H) * W);
+  p.nCs = plan.nCs;
+  p.Ltok = plan.Ltok;
+  p.nTr = plan.nTr;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                                   int64_t ldu, const void* bias, void* y, const int64_t* ys, int64_t B, int64_t T,
+                                   int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype, void* stream) {
+  dynconv_status st = check_lowrank(x, xs, z, zs, U, ldu, B, T, D, W, H, R, dtype);
+  if (st != DYNCONV_OK) return st;
+  if ((st = check_act(y, ys, true)) != DYNCONV_OK) return st;
+  if (y == x || y == z || y == U || (bias != nullptr && y == bias)) return DYNCONV_ERR_INVALID_ARG;
+  if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
+  const int eb = elem_bytes(dtype);
+  const Act acts[2] = {{x, xs}, {y, ys}};
+  if (!act_align_ok(acts, 2, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
+  const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, false);
+  LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
+  p.out = y;
+  p.os0 = ys[0];
+  p.os1 = ys[1];
+  return launch_lowrank_fwd(p, plan, W, dtype, static_cast<hipStream_t>(stream));
+}
+
+size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                          dynconv_dtype dtype) {
+  if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK || R < 1 || R > 128 || H != 1) return 0;
+  if (B == 0 || T == 0 || D == 0) return 0;
+  return plan_lowrank(B, T, D, W, H, R, true).ws_total;
+}
+
+dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                                   int64_t ldu, const void* bias, const void* dy, const int64_t* dys, void* dx,
+                                   const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db, int64_t B,
+                                   int64_t T, int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  dynconv_status st = check_lowrank(x, xs, z, zs, U, ldu, B, T, D, W, H, R, dtype);
+  if (st != DYNCONV_OK) return st;
+  if ((st = check_act(dy, dys, true)) != DYNCONV_OK) return st;
+  if ((st = check_act(dx, dxs, true)) != DYNCONV_OK) return st;
+  if (dz == nullptr || dzs == nullptr || dU == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (dzs[2] != 1 || dzs[0] < 0 || dzs[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  const void* ins[5] = {x, z, U, bias, dy};
+  const void* outs[4] = {dx, dz, dU, db};
+  for (const void* o : outs) {
+    if (o == nullptr) continue;
+    for (const void* in : ins)
+      if (in != nullptr && o == in) return DYNCONV_ERR_INVALID_ARG;
+  }
+  if (dx == dz || dx == dU || dz == dU || (db != nullptr && (db == dx || db == dz || db == dU)))
+    return DYNCONV_ERR_INVALID_ARG;
+  if (!aligned(dU, 4) || (db != nullptr && !aligned(db, 4))) return DYNCONV_ERR_UNSUPPORTED;
+  if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
+  const int eb = elem_bytes(dtype);
+  const Act acts[3] = {{x, xs}, {dy, dys}, {dx, dxs}};
+  if (!act_align_ok(acts, 3, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
+  const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, true);
+  if (workspace == nullptr || workspace_bytes < plan.ws_total) return DYNCONV_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return DYNCONV_ERR_UNSUPPORTED;
+  LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
+  p.dy = dy;
+  p.dys0 = dys[0];
+  p.dys1 = dys[1];
+  p.out = dx;
+  p.os0 = dxs[0];
+  p.os1 = dxs[1];
+  p.dz = dz;
+  p.dzs0 = dzs[0];
+  p.dzs1 = dzs[1];
+  char* wsb = static_cast<char*>(workspace);
+  p.part_dU = reinterpret_cast<float*>(wsb + plan.ws_dU);
+  p.part_db = db != nullptr ? reinterpret_cast<float*>(wsb + plan.ws_db) : nullptr;
+  return launch_lowrank_bwd(p, plan, W, dtype, dU, db, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal interface between the C ABI layer (argument checks) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dynconv.h"
+
+namespace dynconv {
+
+constexpr int kWaveSize = 64;
+constexpr int kBlockThreads = 256;  // 4 waves per workgroup
+
+// Lane mapping of the streaming kernels: each lane owns VEC consecutive channels and
+// sweeps a run of tokens, keeping the W-1 token halo in registers.
+enum class StreamMode {
+  PerChannel,  // H == 1: lane loads the VEC*W contiguous taps of its channels
+  Group,       // H > 1, H % VEC == 0: the lane's channels share one filter
+};
+
+// Parameters of the streaming (materialised / static filter) kernels, passed by value.
+struct StreamParams {
+  const void* x;
+  const void* w;
+  const void* dy;
+  void* out;        // y (forward) or dx (backward, may be null)
+  void* dw;         // per-token dw (backward, may be null)
+  float* partial;   // static dw: per (b, time chunk) partial sums [B*nTw][G][W]
+  int64_t xs0, xs1;
+  int64_t ws0, ws1;
+  int64_t dys0, dys1;
+  int64_t os0, os1;
+  int64_t dws0, dws1;
+  int32_t B, T, D, H, G;
+  int32_t L;         // tokens per wave time chunk
+  int32_t nTw;       // time chunks per sequence
+  int32_t nDw;       // channel slices (one wave wide) across D
+  int32_t WD, WT;    // waves per workgroup along D and along T (WD * WT == 4)
+  int32_t nDb, nTb;  // workgroups along D and along T
+};
+
+struct StreamPlan {
+  int vec;      // channels per lane
+  StreamMode mode;
+  int L, nTw, nDw, WD, WT, nDb, nTb;
+  int64_t blocks;
+};
+
+// Chooses the lane vector width and the time chunking. `wide_ok` says whether every
+// activation-shaped tensor allows 16-byte vectors.
+StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, bool wide_ok, bool bwd,
+                       bool is_static);
+
+dynconv_status launch_stream_fwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
+                                 bool is_static, hipStream_t stream);
+dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
+                                 bool is_static, float* dw_static_out, hipStream_t stream);
+
+// Fixed-order sum of [nchunk][n] float32 partials into out[n].
+dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,
+                                      hipStream_t stream);
+
+// ---------------------------------------------------------------------------------
+// Low-rank form
+// ---------------------------------------------------------------------------------
+struct LowRankParams {
+  const void* x;
+  const void* z;
+  const void* U;
+  const void* bias;  // may be null
+  const void* dy;
+  void* out;   // y (forward) or dx (backward)
+  void* dz;
+  float* part_dU;  // [nTr][R][J]   partial dU per token range
+  float* part_db;  // [nTr][J]      partial db per token range
+  float* part_dz;  // [nCs][B*T][R] partial dz per channel slice
+  int64_t xs0, xs1;
+  int64_t zs0, zs1;
+  int64_t ldu;
+  int64_t dys0, dys1;
+  int64_t os0, os1;
+  int64_t dzs0, dzs1;
+  int32_t B, T, D, H, G, R, J;
+  int32_t nCs;     // channel slices
+  int32_t Ltok;    // tokens per token range
+  int32_t nTr;     // token ranges per sequence
+};
+
+struct LowRankPlan {
+  int nCs, Ltok, nTr;
+  int64_t blocks;
+  size_t ws_dU, ws_db, ws_dz;  // byte offsets inside the workspace
+  size_t ws_total;
+};
+
+LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bwd);
+
+dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
+                                  hipStream_t stream);
+dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
+                                  float* dU, float* db, hipStream_t stream);
+
+// Records a HIP failure for dynconv_last_hip_error(); returns DYNCONV_ERR_HIP.
+dynconv_status record_hip_error(hipError_t e);
+
+}  // namespace dynconv

@@ -1,0 +1,138 @@
+"""Python binding of libdynconv over torch tensors (argument marshalling only).
+
+Every function has the name of the C entry point it calls; all compute runs in the HIP
+kernels. Tensors must live on a ROCm device; PyTorch provides device memory and the
+current stream, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DTYPE = {torch.float32: _lib.DYNCONV_F32, torch.bfloat16: _lib.DYNCONV_BF16}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DTYPE[t.dtype]
+
+
+def _require_device(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise RuntimeError("libdynconv runs on the GPU only: got a CPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise RuntimeError("all tensors must be on the same device")
+    return dev
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def filter_strides(w: torch.Tensor):
+    """Strides of a filter tensor: [B,T,G,W] as is; a static [G,W] filter gets zero b,t strides."""
+    if w.dim() == 2:
+        return [0, 0, w.stride(0), w.stride(1)]
+    if w.dim() != 4:
+        raise ValueError("filters are [B, T, D/H, W] or a static [D/H, W]")
+    return list(w.stride())
+
+
+def dynconv_fwd(x: torch.Tensor, w: torch.Tensor, H: int = 1, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x + causal depthwise conv of x with per-token (or static) filters w."""
+    B, T, D = x.shape
+    W = w.shape[-1]
+    y = torch.empty_like(x) if out is None else out
+    dev = _require_device(x, w, y)
+    lib = _lib.load()
+    st = lib.dynconv_fwd(
+        _ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)), _ptr(y), _lib.strides(y.stride()),
+        B, T, D, W, H, _dtype_code(x), _stream(dev),
+    )
+    _lib.check("dynconv_fwd", st)
+    return y
+
+
+def dynconv_bwd_workspace_size(B, T, D, W, H, is_static, dtype) -> int:
+    return int(_lib.load().dynconv_bwd_workspace_size(B, T, D, W, H, int(bool(is_static)), _DTYPE[dtype]))
+
+
+def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True, dx=None, dw=None):
+    """(dx, dw) of <dy, dynconv_fwd(x, w, H)>; dw of a static filter is float32 [D/H, W]."""
+    B, T, D = x.shape
+    W = w.shape[-1]
+    is_static = w.dim() == 2
+    if need_dx and dx is None:
+        dx = torch.empty_like(x)
+    if need_dw and dw is None:
+        dw = (torch.empty((D // H, W), dtype=torch.float32, device=x.device) if is_static
+              else torch.empty((B, T, D // H, W), dtype=x.dtype, device=x.device))
+    dev = _require_device(x, w, dy, dx, dw)
+    lib = _lib.load()
+    ws_bytes = dynconv_bwd_workspace_size(B, T, D, W, H, is_static and need_dw, x.dtype)
+    work = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device) if ws_bytes else None
+    st = lib.dynconv_bwd(
+        _ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)),
+        _ptr(dy), _lib.strides(dy.stride()),
+        _ptr(dx if need_dx else None), _lib.strides(dx.stride()) if need_dx else None,
+        _ptr(dw if need_dw else None), _lib.strides(dw.stride()) if (need_dw and not is_static) else None,
+        B, T, D, W, H, _dtype_code(x), _ptr(work), ws_bytes, _stream(dev),
+    )
+    _lib.check("dynconv_bwd", st)
+    return (dx if need_dx else None), (dw if need_dw else None)
+
+
+def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None):
+    """y = x + conv(x) with filters z U + bias generated on the GPU (never stored)."""
+    B, T, D = x.shape
+    R = z.shape[-1]
+    y = torch.empty_like(x) if out is None else out
+    dev = _require_device(x, z, U, bias, y)
+    lib = _lib.load()
+    st = lib.dynconv_lowrank_fwd(
+        _ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias),
+        _ptr(y), _lib.strides(y.stride()), B, T, D, W, H, R, _dtype_code(x), _stream(dev),
+    )
+    _lib.check("dynconv_lowrank_fwd", st)
+    return y
+
+
+def dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dtype) -> int:
+    return int(_lib.load().dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, _DTYPE[dtype]))
+
+
+def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = True, workspace=None):
+    """(dx, dz, dU, db) of <dy, dynconv_lowrank_fwd(...)>; dU and db are float32."""
+    B, T, D = x.shape
+    R = z.shape[-1]
+    J = (D // H) * W
+    dx = torch.empty_like(x)
+    dz = torch.empty_like(z)
+    dU = torch.empty((R, J), dtype=torch.float32, device=x.device)
+    db = torch.empty((J,), dtype=torch.float32, device=x.device) if need_db else None
+    dev = _require_device(x, z, U, bias, dy)
+    lib = _lib.load()
+    ws_bytes = dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    st = lib.dynconv_lowrank_bwd(
+        _ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias),
+        _ptr(dy), _lib.strides(dy.stride()), _ptr(dx), _lib.strides(dx.stride()), _ptr(dz), _lib.strides(dz.stride()),
+        _ptr(dU), _ptr(db), B, T, D, W, H, R, _dtype_code(x), _ptr(workspace), ws_bytes, _stream(dev),
+    )
+    _lib.check("dynconv_lowrank_bwd", st)
+    return dx, dz, dU, db

@@ -1,0 +1,142 @@
+/*
+ * dynconv.h: C ABI of the dynamic short convolution library (libdynconv.so), gfx950.
+ *
+ * The operation, from "Dynamic Short Convolutions Improve Transformers" (reading note),
+ * section "Parameterization":
+ *
+ *   eq. 2 + eq. 3:   y[b,t,d] = x[b,t,d] + sum_{k=0}^{W-1} w[b,t,g(d),k] * x[b,t-k,d]
+ *
+ * with x[b,t,d] = 0 for t < 0 in every sequence b, g(d) = d / H (one filter shared by H
+ * consecutive channels: H = 1 is the per-channel form, H > 1 the head-wise form), and a
+ * static filter (eq. 1) as the case where w does not depend on (b, t). In the low-rank
+ * form (same section, and "Efficient training (Triton kernels)") the filters are
+ * generated on the GPU from z (B x T x R) and the second projection U (R x (D/H)*W)
+ * plus a bias b: w[b,t,g,k] = sum_r z[b,t,r] U[r, g*W+k] + b[g*W+k], and are never
+ * written to memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers. The caller owns every buffer, including
+ *   the workspace; the library never allocates or frees device memory, never
+ *   synchronises, and keeps no mutable global state (thread-safe).
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *   returns without waiting.
+ * - Strides are in ELEMENTS, int64, in PyTorch .stride() order. Activation-shaped tensors
+ *   (x, y, dy, dx) are [B, T, D] with strides s[0..2], s[2] == 1. Filter-shaped tensors
+ *   (w, dw) are [B, T, D/H, W] with strides s[0..3], s[3] == 1 and s[2] == W (the W taps
+ *   of one group are contiguous). w with s[0] == s[1] == 0 is a static filter [D/H, W].
+ *   z and dz are [B, T, R] with strides s[0..2], s[2] == 1.
+ * - Element types: x, w, z, U, bias, y, dy, dx, dw (per token) and dz all have `dtype`.
+ *   Reduced parameter gradients (static dw, dU, db) are always float32 and contiguous.
+ * - Arithmetic is float32 (products and sums), bf16 results are rounded to nearest even.
+ * - Validation happens before any HIP call; invalid input returns a status, never aborts.
+ *   B == 0 or T == 0 or D == 0 is a no-op returning DYNCONV_OK.
+ * - Supported parameters: 1 <= W <= 5; H == 1 or H a power of two that divides D, with
+ *   H <= 64 * (16 / element size) (512 for bf16, 256 for float32; H <= 64 * (4 / element
+ *   size) when the wide path below is not available); 1 <= R <= 256 for the low-rank form.
+ * - Alignment: base pointers of activation-shaped tensors and their s[0], s[1] (in bytes)
+ *   must be multiples of 4 bytes (bf16: D even); when all of them are multiples of 16 bytes
+ *   and D is a multiple of 16 / element size, a wider vector path is used. w (H == 1):
+ *   base and strides multiples of 4 bytes. Violations return DYNCONV_ERR_UNSUPPORTED.
+ * - An output pointer equal to any input pointer returns DYNCONV_ERR_INVALID_ARG
+ *   (in-place use would corrupt the time halo); partial overlap is undefined behaviour.
+ * - A failed kernel launch returns DYNCONV_ERR_HIP; dynconv_last_hip_error() then gives
+ *   the hipError_t of the calling thread's last failure.
+ */
+#ifndef DYNCONV_H
+#define DYNCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DYNCONV_F32 = 0, DYNCONV_BF16 = 1 } dynconv_dtype;
+
+typedef enum {
+  DYNCONV_OK = 0,
+  DYNCONV_ERR_INVALID_ARG = 1, /* null / negative / inconsistent argument, aliasing */
+  DYNCONV_ERR_UNSUPPORTED = 2, /* valid per the equations but outside this library's limits */
+  DYNCONV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query */
+  DYNCONV_ERR_HIP = 4          /* a HIP launch failed */
+} dynconv_status;
+
+/* Human-readable name of a status code (static storage). */
+const char* dynconv_status_string(dynconv_status s);
+
+/* hipError_t (as int) of the calling thread's last DYNCONV_ERR_HIP, 0 if none. */
+int dynconv_last_hip_error(void);
+
+/*
+ * Forward, eq. 2 + eq. 3 (eq. 1 when w is static).
+ *   x  [B,T,D]      input activations (read once)
+ *   w  [B,T,D/H,W]  per-token filters, or static [D/H,W] given by ws[0] == ws[1] == 0
+ *   y  [B,T,D]      output, y = x + conv(x) (written once)
+ */
+dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                           void* y, const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W,
+                           int32_t H, dynconv_dtype dtype, void* stream);
+
+/*
+ * Backward of dynconv_fwd given dy = dL/dy (the exact adjoint of eq. 2 + eq. 3):
+ *   dx[b,s,d]   = dy[b,s,d] + sum_k w[b,s+k,g(d),k] * dy[b,s+k,d]        (s + k < T)
+ *   dw[b,t,g,k] = sum_{d : g(d) = g} dy[b,t,d] * x[b,t-k,d]              (0 for t < k)
+ * x and w are independent inputs (the filters are generated from another tensor), so dx
+ * has no term through w.
+ *   dx  [B,T,D] or NULL to skip.
+ *   dw  per-token filters: [B,T,D/H,W] with strides dws, dtype `dtype`, or NULL to skip.
+ *       static w: float32 [D/H, W] contiguous, the sum over all (b, t); dws is ignored.
+ * At least one of dx, dw must be non-NULL. A static w needs a workspace of
+ * dynconv_bwd_workspace_size(...) bytes when dw is requested (per-tile partial sums,
+ * reduced in a fixed order, so results are run-to-run deterministic).
+ */
+dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                           const void* dy, const int64_t* dys, void* dx, const int64_t* dxs, void* dw,
+                           const int64_t* dws, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                           dynconv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by dynconv_bwd (0 unless the filter is static). */
+size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int is_static,
+                                  dynconv_dtype dtype);
+
+/*
+ * Low-rank forward: filters w[b,t,g,k] = sum_r z[b,t,r] U[r, g*W+k] + bias[g*W+k] are
+ * formed on the GPU (matrix cores, float32 accumulation) and applied at once; they are
+ * never written to memory. Then y = x + conv(x) as in dynconv_fwd.
+ *   z     [B,T,R] with strides zs
+ *   U     [R, (D/H)*W] with row stride ldu (elements), column j = g*W + k
+ *   bias  [(D/H)*W] or NULL (zero bias)
+ */
+dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                   const void* U, int64_t ldu, const void* bias, void* y, const int64_t* ys,
+                                   int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                   dynconv_dtype dtype, void* stream);
+
+/*
+ * Low-rank backward. With g[b,t,j] = dw[b,t,g,k] (j = g*W + k) the per-token filter
+ * gradient of dynconv_bwd (never written to memory):
+ *   dx = as in dynconv_bwd with the generated filters,
+ *   dz[b,t,r] = sum_j g[b,t,j] U[r,j],
+ *   dU[r,j]   = sum_{b,t} z[b,t,r] g[b,t,j]   (float32 [R, (D/H)*W] contiguous, overwritten),
+ *   db[j]     = sum_{b,t} g[b,t,j]            (float32 [(D/H)*W], overwritten; NULL to skip).
+ * dx, dz and dU are required. Needs dynconv_lowrank_bwd_workspace_size(...) bytes of
+ * workspace for fixed-order partial sums (run-to-run deterministic, no float atomics).
+ */
+dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                   const void* U, int64_t ldu, const void* bias, const void* dy,
+                                   const int64_t* dys, void* dx, const int64_t* dxs, void* dz,
+                                   const int64_t* dzs, float* dU, float* db, int64_t B, int64_t T, int64_t D,
+                                   int32_t W, int32_t H, int32_t R, dynconv_dtype dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by dynconv_lowrank_bwd. */
+size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                          dynconv_dtype dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYNCONV_H */

@@ -1,0 +1,136 @@
+"""The C ABI on the host: every declared symbol is exported, and every validation path
+returns its status before any HIP call (so these run without a GPU).
+
+Pointers below are fake, non-null addresses: the calls must reject the arguments
+before touching them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_short_convolution_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUP, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from dynamic_short_convolution_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "dynconv.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(dynconv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported(lib):
+    declared = _declared_symbols()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS.items():
+        assert lib.dynconv_status_string(code).decode() == name
+    assert lib.dynconv_last_hip_error() == 0
+
+
+P = ctypes.c_void_p  # fake device pointers, never dereferenced
+X, W_, Y, DY, DX, DW, Z, U = (P(0x10000 * (i + 1)) for i in range(8))
+
+
+def S(*v):
+    return _lib.strides(v)
+
+
+def fwd(lib, x=X, xs=(800, 200, 1), w=W_, ws=(800 * 4, 200 * 4, 4, 1), y=Y, ys=(800, 200, 1), B=2, T=4, D=200, W=4,
+        H=1, dt=BF16):
+    return lib.dynconv_fwd(x, S(*xs), w, S(*ws), y, S(*ys), B, T, D, W, H, dt, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(dt=7), INVALID),
+        (dict(B=-1), INVALID),
+        (dict(W=0), INVALID),
+        (dict(W=6), UNSUP),
+        (dict(H=0), INVALID),
+        (dict(D=200, H=3), INVALID),  # 3 does not divide 200
+        (dict(D=198, H=3, xs=(792, 198, 1), ys=(792, 198, 1), ws=(264 * 4, 66 * 4, 4, 1)), UNSUP),  # not a power of 2
+        (dict(x=P(0)), INVALID),
+        (dict(y=P(0)), INVALID),
+        (dict(w=P(0)), INVALID),
+        (dict(y=X), INVALID),  # in place
+        (dict(xs=(800, 200, 2)), UNSUP),
+        (dict(ws=(800 * 4, 200 * 4, 3, 1)), UNSUP),  # taps of a group not contiguous
+        (dict(ws=(800 * 4, 200 * 4, 4, 2)), UNSUP),
+        (dict(x=P(0x10002)), UNSUP),  # bf16 activations need 4-byte alignment
+        (dict(D=199, xs=(796, 199, 1), ys=(796, 199, 1), ws=(796 * 4, 199 * 4, 4, 1)), UNSUP),  # odd D in bf16
+        (dict(B=0), OK),  # empty: no-op
+        (dict(T=0), OK),
+    ],
+)
+def test_fwd_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def bwd(lib, dx=DX, dw=DW, ws=(800 * 4, 200 * 4, 4, 1), dws=(800 * 4, 200 * 4, 4, 1), wsp=None, wsb=0, H=1, D=200,
+        dy=DY):
+    return lib.dynconv_bwd(X, S(800, D, 1), W_, S(*ws), dy, S(800, D, 1), dx, S(800, D, 1), dw, S(*dws) if dws else None,
+                           2, 4, D, 4, H, BF16, wsp, wsb, None)
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, dx=P(0), dw=P(0)) == INVALID
+    assert bwd(lib, dx=DY) == INVALID  # dx aliasing dy
+    assert bwd(lib, dw=W_) == INVALID  # dw aliasing w
+    assert bwd(lib, dx=DW, dw=DW) == INVALID
+    assert bwd(lib, dy=P(0)) == INVALID
+    # batch-shared but per-token filters: dw would need a batch reduction
+    assert bwd(lib, ws=(0, 200 * 4, 4, 1)) == UNSUP
+    assert bwd(lib, dws=None) == INVALID
+    # static filter: needs a workspace for the partial sums
+    need = lib.dynconv_bwd_workspace_size(2, 4, 200, 4, 1, 1, BF16)
+    assert need > 0
+    assert bwd(lib, ws=(0, 0, 4, 1), dws=None, wsp=None, wsb=0) == WORKSPACE
+    assert bwd(lib, ws=(0, 0, 4, 1), dws=None, wsp=P(0x900000), wsb=need - 1) == WORKSPACE
+    assert lib.dynconv_bwd_workspace_size(2, 4, 200, 4, 1, 0, BF16) == 0
+
+
+def test_workspace_queries(lib):
+    assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 3, 1, 1, BF16) % 4 == 0
+    assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 6, 1, 1, BF16) == 0  # invalid W
+    n = lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 64, BF16)
+    assert n >= 64 * 2048 * 4 * 4  # at least one float32 dU partial
+    assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 0, BF16) == 0
+
+
+def lr_fwd(lib, R=64, z=Z, U_=U, ldu=800, H=1, x=X, y=Y, W=4, D=200):
+    return lib.dynconv_lowrank_fwd(x, S(800, D, 1), z, S(4 * R, R, 1), U_, ldu, None, y, S(800, D, 1), 2, 4, D, W, H,
+                                   R, BF16, None)
+
+
+def test_lowrank_validation(lib):
+    assert lr_fwd(lib, R=0) == INVALID
+    assert lr_fwd(lib, R=129) == UNSUP
+    assert lr_fwd(lib, z=P(0)) == INVALID
+    assert lr_fwd(lib, U_=P(0)) == INVALID
+    assert lr_fwd(lib, y=X) == INVALID
+    assert lr_fwd(lib, ldu=100) == INVALID  # row shorter than (D/H)*W
+    assert lr_fwd(lib, H=2) == UNSUP  # head-wise low-rank is not built
+    need = lib.dynconv_lowrank_bwd_workspace_size(2, 4, 200, 4, 1, 64, BF16)
+    st = lib.dynconv_lowrank_bwd(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, DY, S(800, 200, 1), DX,
+                                 S(800, 200, 1), P(0x990000), S(256, 64, 1), P(0x9a0000), None, 2, 4, 200, 4, 1, 64,
+                                 BF16, P(0x9b0000), need - 1, None)
+    assert st == WORKSPACE

@@ -1,0 +1,153 @@
+"""GPU parity of the fused low-rank kernels against the float64 oracle, through the C ABI.
+
+bf16 path: the generated filters stay in float32 (never rounded, never stored), but
+the per-token filter gradient g is rounded to bf16 as an operand of the matrix-core
+products dz = g U^T and dU = z^T g; the elementwise bound of those two outputs
+therefore adds 2^-9 * sum |terms| (half an ulp of bf16 relative to each rounded term).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from dynamic_short_convolution_amd import dynconv_fwd, dynconv_lowrank_bwd, dynconv_lowrank_fwd
+from oracle import conv_bwd, lowrank_bwd, lowrank_filters, lowrank_fwd
+from tests.parity import assert_close, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(B, T, D, W, R, dtype, seed, bias=True):
+    x = synth.draw((B, T, D), 1.0, seed, "x", dtype)
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", dtype)
+    z = synth.draw((B, T, R), 1.0, seed, "z", dtype)
+    U = synth.draw((R, D * W), 0.1 / R**0.5 * 3.0, seed, "U", dtype)
+    b = synth.draw((D * W,), 0.1**0.5, seed, "b", dtype) if bias else None
+    return x, z, U, b, dy
+
+
+def _g_abs(x64, dy64, W):
+    """|g| for every (b, t, j): the magnitudes of the per-token filter-gradient terms."""
+    B, T, D = x64.shape
+    _, dwabs = conv_bwd(np.abs(x64), np.zeros((B, T, D, W)), np.abs(dy64), 1)
+    return dwabs.reshape(B * T, D * W)
+
+
+def _check(B, T, D, W, R, dtype, seed, bias=True, bwd=True):
+    td = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    x, z, U, b, dy = _inputs(B, T, D, W, R, dtype, seed, bias)
+    xg, zg, Ug, dyg = x.cuda(), z.cuda(), U.cuda(), dy.cuda()
+    bg = b.cuda() if b is not None else None
+    x64, z64, U64, dy64 = to64(x), to64(z), to64(U), to64(dy)
+    b64 = to64(b) if b is not None else None
+    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W)
+    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W), td)
+    if not bwd:
+        return
+    dx, dz, dU, db = dynconv_lowrank_bwd(xg, zg, Ug, bg, dyg, W)
+    rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W)
+    assert_close("dx", dx, rdx, td)
+    gabs = _g_abs(x64, dy64, W)
+    half_ulp = 2.0**-9 if td == torch.bfloat16 else 2.0**-22
+    extra_dz = (half_ulp * (gabs @ np.abs(U64).T)).reshape(B, T, R)
+    extra_dU = half_ulp * (np.abs(z64).reshape(B * T, R).T @ gabs)
+    assert_close("dz", dz, rdz, td, extra=extra_dz)
+    # dU and db are float32 outputs of sums over every token
+    assert_close("dU", dU, rdU, torch.float32 if td == torch.float32 else td, rtol=1e-5, atol=1e-5, extra=extra_dU)
+    assert_close("db", db, rdb, torch.float32 if td == torch.float32 else td, rtol=1e-5, atol=1e-5)
+
+
+SMALL = []
+for dtype in ("f32", "bf16"):
+    for W in (1, 2, 3, 4, 5):
+        for R in (1, 20, 33, 64, 128):
+            SMALL.append((dtype, W, R))
+
+
+@pytest.mark.parametrize("dtype,W,R", SMALL)
+def test_small_parity(dtype, W, R):
+    _check(2, 77, 200, W, R, dtype, seed=W * 13 + R)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,D", [(1, 64), (3, 64), (5, 128), (300, 64), (1000, 96)])
+def test_shapes(dtype, T, D):
+    _check(2, T, D, 4, 16, dtype, seed=T + D)
+
+
+def test_no_bias():
+    _check(2, 50, 128, 4, 32, "bf16", seed=3, bias=False)
+
+
+def test_fused_equals_materialised_path():
+    """The fused kernel applied to z, U, b equals the materialised-filter kernel applied to
+    the filters z U + b, up to the filter rounding the materialised path must do."""
+    B, T, D, W, R = 2, 150, 256, 4, 64
+    x, z, U, b, dy = _inputs(B, T, D, W, R, "f32", 21)
+    wmat = torch.from_numpy(lowrank_filters(to64(z), to64(U), to64(b), W)).to(torch.float32)
+    y_fused = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W)
+    y_mat = dynconv_fwd(x.cuda(), wmat.cuda(), 1)
+    assert_close("fused vs materialised", y_fused, to64(y_mat), torch.float32)
+
+
+def test_deterministic():
+    B, T, D, W, R = 2, 400, 256, 4, 64
+    x, z, U, b, dy = (t.cuda() if t is not None else None for t in _inputs(B, T, D, W, R, "bf16", 22))
+    outs = [dynconv_lowrank_bwd(x, z, U, b, dy, W) for _ in range(3)]
+    for o in outs[1:]:
+        for a, c in zip(outs[0], o):
+            assert torch.equal(a, c)
+
+
+def test_full_lowrank_r64_fwd():
+    wl = synth.workloads()["lowrank_r64"]
+    x, z, U, b = wl.x(), wl.z(), wl.U(), wl.b()
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), wl.W)
+    # every token of sampled channel blocks
+    chans = np.concatenate([np.arange(0, 64), np.arange(992, 1056), np.arange(1984, 2048)])
+    ci = torch.as_tensor(chans)
+    cols = torch.as_tensor((chans[:, None] * wl.W + np.arange(wl.W)[None, :]).reshape(-1))
+    ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
+                      to64(b.index_select(0, cols)), wl.W)
+    assert_close("y", y.index_select(2, ci.cuda()).cpu(), ref, torch.bfloat16)
+
+
+def test_full_lowrank_r64_bwd():
+    wl = synth.workloads()["lowrank_r64_bwd"]
+    x, z, U, b, dy = wl.x(), wl.z(), wl.U(), wl.b(), wl.dy()
+    dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), wl.W)
+    # dx, dU, db on sampled channel blocks (all tokens); dz needs every channel, so it is
+    # checked on whole sequences 0 and B-1 over a token window.
+    chans = np.concatenate([np.arange(0, 64), np.arange(992, 1056), np.arange(1984, 2048)])
+    ci = torch.as_tensor(chans)
+    cols_np = (chans[:, None] * wl.W + np.arange(wl.W)[None, :]).reshape(-1)
+    cols = torch.as_tensor(cols_np)
+    x64 = to64(x.index_select(2, ci))
+    dy64 = to64(dy.index_select(2, ci))
+    U64 = to64(U.index_select(1, cols))
+    b64 = to64(b.index_select(0, cols))
+    z64 = to64(z)
+    rdx, _, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, wl.W)
+    assert_close("dx", dx.index_select(2, ci.cuda()).cpu(), rdx, torch.bfloat16)
+    gabs = _g_abs(x64, dy64, wl.W)
+    extra_dU = 2.0**-9 * (np.abs(z64).reshape(-1, wl.R).T @ gabs)
+    assert_close("dU", dU.index_select(1, cols.cuda()).cpu(), rdU, torch.bfloat16, rtol=1e-5, atol=1e-5,
+                 extra=extra_dU)
+    assert_close("db", db.index_select(0, cols.cuda()).cpu(), rdb, torch.bfloat16, rtol=1e-5, atol=1e-5)
+    for bsel in (0, wl.B - 1):
+        t0, t1 = 1000, 1100  # window; dz_t only needs x_{t-3..t} and dy_t
+        xs = to64(x[bsel : bsel + 1, t0 - 4 : t1])
+        dys = to64(dy[bsel : bsel + 1, t0 - 4 : t1])
+        zs = to64(z[bsel : bsel + 1, t0 - 4 : t1])
+        _, rdz, _, _ = lowrank_bwd(xs, zs, to64(U), to64(b), dys, wl.W)
+        got = dz[bsel : bsel + 1, t0:t1].cpu()
+        gab = _g_abs(xs, dys, wl.W)
+        extra = (2.0**-9 * (gab @ np.abs(to64(U)).T)).reshape(1, -1, wl.R)[:, 4:]
+        assert_close("dz", got, rdz[:, 4:], torch.bfloat16, extra=extra)

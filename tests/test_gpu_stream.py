@@ -1,0 +1,282 @@
+"""GPU parity of the streaming kernels (materialised and static filters) against the
+float64 oracle, through the C ABI.
+
+Small cases span several time chunks and channel slices with ragged tails; the full
+workloads (the pages' D = 2048, T = 4096 model shapes) are checked on every token of
+sampled channel blocks, in the launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from dynamic_short_convolution_amd import dynconv_bwd, dynconv_fwd
+from oracle import conv_bwd, conv_fwd
+from tests.parity import assert_close, to64
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    from dynamic_short_convolution_amd import _lib
+
+    _lib.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(B, T, D, W, H, dtype, static, seed):
+    x = synth.draw((B, T, D), 1.0, seed, "x", dtype)
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", dtype)
+    shape = (D // H, W) if static else (B, T, D // H, W)
+    w = synth.draw(shape, (1.0 / W) ** 0.5, seed, "w", dtype)
+    return x, w, dy
+
+
+def _check_case(B, T, D, W, H, dtype, static, seed=0):
+    x, w, dy = _inputs(B, T, D, W, H, dtype, static, seed)
+    xg, wg, dyg = x.cuda(), w.cuda(), dy.cuda()
+    y = dynconv_fwd(xg, wg, H)
+    dx, dw = dynconv_bwd(xg, wg, dyg, H)
+    torch.cuda.synchronize()
+    x64, w64, dy64 = to64(x), to64(w), to64(dy)
+    td = DT[dtype]
+    assert_close("y", y, conv_fwd(x64, w64, H), td)
+    rdx, rdw = conv_bwd(x64, w64, dy64, H)
+    assert_close("dx", dx, rdx, td)
+    if static:
+        # float32 output of a sum over all (b, t): allow the float32 per-chunk sums
+        assert_close("dw_static", dw, rdw, torch.float32, rtol=1e-5, atol=1e-5)
+    else:
+        assert_close("dw", dw, rdw, td)
+
+
+SMALL = []
+for dtype in ("f32", "bf16"):
+    for W in (1, 2, 3, 4, 5):
+        for H in (1, 2, 4, 16):
+            for static in (False, True):
+                D = 200 if H == 1 else 640
+                for T in (3, 100, 333):
+                    SMALL.append((dtype, W, H, static, D, T))
+
+
+@pytest.mark.parametrize("dtype,W,H,static,D,T", SMALL)
+def test_small_parity(dtype, W, H, static, D, T):
+    _check_case(2, T, D, W, H, dtype, static, seed=W * 7 + H + T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H", [8, 32, 64, 128, 256, 512])
+def test_large_head_sizes(dtype, H):
+    if dtype == "f32" and H > 256:
+        pytest.skip("float32 lanes hold 4 channels: at most 64 * 4 channels per group")
+    _check_case(2, 77, 1024, 4, H, dtype, False, seed=H)
+    _check_case(1, 50, 1024, 3, H, dtype, True, seed=H + 1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 2, 4, 5])
+def test_short_sequences(dtype, T):
+    """T < W and T = 1: every tap past the start of the sequence reads zeros."""
+    for W in (4, 5):
+        _check_case(3, T, 64, W, 1, dtype, False, seed=T)
+        _check_case(3, T, 64, W, 1, dtype, True, seed=T)
+
+
+def test_tiny_perchannel_f32_workload():
+    wl = synth.workloads()["tiny_perchannel_f32"]
+    x, w, dy = wl.x(), wl.w(), wl.dy()
+    y = dynconv_fwd(x.cuda(), w.cuda(), wl.H)
+    dx, dw = dynconv_bwd(x.cuda(), w.cuda(), dy.cuda(), wl.H)
+    ry = conv_fwd(to64(x), to64(w), wl.H)
+    rdx, rdw = conv_bwd(to64(x), to64(w), to64(dy), wl.H)
+    assert_close("y", y, ry, torch.float32)
+    assert_close("dx", dx, rdx, torch.float32)
+    assert_close("dw", dw, rdw, torch.float32)
+
+
+@pytest.mark.parametrize("j", [0, 1, 2, 3])
+def test_one_hot_tap_rounds_to_nearest_even(j):
+    """w one-hot at tap j: y_t = x_t + x_{t-j} (exact in float32), stored with RNE."""
+    B, T, D, W = 2, 40, 256, 4
+    x = synth.draw((B, T, D), 1.0, 5, "x", "bf16")
+    w = torch.zeros((B, T, D, W), dtype=torch.bfloat16)
+    w[..., j] = 1.0
+    y = dynconv_fwd(x.cuda(), w.cuda(), 1).cpu()
+    xs = x.float()
+    ref = xs.clone()
+    if j == 0:
+        ref = xs + xs
+    else:
+        ref[:, j:, :] += xs[:, : T - j, :]
+    assert torch.equal(y.view(torch.int16), ref.to(torch.bfloat16).view(torch.int16))
+
+
+def test_zero_filters_identity_bitwise():
+    x = synth.draw((2, 50, 300), 1.0, 6, "x", "bf16").cuda()
+    dy = synth.draw((2, 50, 300), 1.0, 6, "dy", "bf16").cuda()
+    w = torch.zeros((2, 50, 300, 3), dtype=torch.bfloat16, device="cuda")
+    assert torch.equal(dynconv_fwd(x, w, 1), x)
+    dx, dw = dynconv_bwd(x, w, dy, 1)
+    assert torch.equal(dx, dy)
+
+
+@pytest.mark.parametrize("H,static", [(1, False), (16, False), (1, True)])
+def test_every_output_written_and_guards_untouched(H, static):
+    """Outputs start as NaN inside guard bands of rows and columns; afterwards every
+    element is finite and the guards are still NaN (bitwise)."""
+    B, T, D, W = 2, 130, 1024, 4
+    x, w, dy = _inputs(B, T, D, W, H, "bf16", static, 9)
+    xg, wg, dyg = x.cuda(), w.cuda(), dy.cuda()
+    G = 3
+    ybig = torch.full((B, T + 2 * G, D + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = ybig[:, G : G + T, :D]
+    dynconv_fwd(xg, wg, H, out=y)
+    dxbig = torch.full_like(ybig, float("nan"))
+    dx = dxbig[:, G : G + T, :D]
+    dwbig = None
+    dw = None
+    if not static:
+        dwbig = torch.full((B, T + 2 * G, D // H + 8, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dw = dwbig[:, G : G + T, : D // H, :]
+    dynconv_bwd(xg, wg, dyg, H, dx=dx, dw=dw)
+    torch.cuda.synchronize()
+    for big, view in ((ybig, y), (dxbig, dx)):
+        assert not torch.isnan(view).any()
+        mask = torch.ones(big.shape, dtype=torch.bool, device="cuda")
+        mask[:, G : G + T, :D] = False
+        assert torch.isnan(big[mask]).all()
+    if dwbig is not None:
+        assert not torch.isnan(dw).any()
+        mask = torch.ones(dwbig.shape, dtype=torch.bool, device="cuda")
+        mask[:, G : G + T, : D // H, :] = False
+        assert torch.isnan(dwbig[mask]).all()
+    x64, w64, dy64 = to64(x), to64(w), to64(dy)
+    assert_close("y(strided)", y, conv_fwd(x64, w64, H), torch.bfloat16)
+    rdx, rdw = conv_bwd(x64, w64, dy64, H)
+    assert_close("dx(strided)", dx, rdx, torch.bfloat16)
+    if dw is not None:
+        assert_close("dw(strided)", dw, rdw, torch.bfloat16)
+
+
+@pytest.mark.parametrize("H,static", [(1, False), (4, False), (16, False), (1, True), (16, True)])
+def test_run_to_run_deterministic(H, static):
+    x, w, dy = _inputs(2, 300, 1024, 4, H, "bf16", static, 11)
+    xg, wg, dyg = x.cuda(), w.cuda(), dy.cuda()
+    outs = []
+    for _ in range(3):
+        y = dynconv_fwd(xg, wg, H)
+        dx, dw = dynconv_bwd(xg, wg, dyg, H)
+        outs.append((y.clone(), dx.clone(), dw.clone()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_dx_only_and_dw_only():
+    x, w, dy = _inputs(2, 90, 512, 4, 1, "bf16", False, 12)
+    xg, wg, dyg = x.cuda(), w.cuda(), dy.cuda()
+    dx_a, dw_a = dynconv_bwd(xg, wg, dyg, 1)
+    dx_b, none_b = dynconv_bwd(xg, wg, dyg, 1, need_dw=False)
+    none_c, dw_c = dynconv_bwd(xg, wg, dyg, 1, need_dx=False)
+    assert none_b is None and none_c is None
+    assert torch.equal(dx_a, dx_b) and torch.equal(dw_a, dw_c)
+
+
+def test_fused_qkv_launch_equals_separate_launches():
+    """One launch over the concatenated [Q | K | V] channels equals three launches on the
+    channel slices (the convolution is depthwise), and both match the oracle."""
+    B, T, W = 2, 200, 4
+    split = (512, 128, 128)
+    D = sum(split)
+    x, w, dy = _inputs(B, T, D, W, 1, "bf16", False, 13)
+    xg, wg, dyg = x.cuda(), w.cuda(), dy.cuda()
+    y = dynconv_fwd(xg, wg, 1)
+    dx, dw = dynconv_bwd(xg, wg, dyg, 1)
+    c0 = 0
+    for n in split:
+        ys = dynconv_fwd(xg[:, :, c0 : c0 + n], wg[:, :, c0 : c0 + n, :], 1)
+        dxs, dws = dynconv_bwd(xg[:, :, c0 : c0 + n], wg[:, :, c0 : c0 + n, :], dyg[:, :, c0 : c0 + n], 1)
+        assert torch.equal(ys, y[:, :, c0 : c0 + n])
+        assert torch.equal(dxs, dx[:, :, c0 : c0 + n])
+        assert torch.equal(dws, dw[:, :, c0 : c0 + n, :])
+        c0 += n
+    assert_close("y", y, conv_fwd(to64(x), to64(w)), torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------
+# full-size workloads, every token of sampled channel blocks (whole filter groups)
+# ------------------------------------------------------------------------------------
+
+
+def _channel_blocks(D, H, width=64):
+    mid = (D // 2 - width // 2) // H * H
+    starts = sorted({0, mid, D - width})
+    return np.concatenate([np.arange(s, s + width) for s in starts])
+
+
+def _sub(t, chans, H, dim):
+    idx = torch.as_tensor(chans if dim == 2 and H == 1 else np.unique(chans // H), device=t.device)
+    return t.index_select(dim, idx)
+
+
+def _full_check(wl, do_fwd=True, do_bwd=True, extra_blocks=()):
+    x, w, dy = wl.x(), wl.w(), wl.dy() if do_bwd else None
+    xg, wg = x.cuda(), w.cuda()
+    H = wl.H
+    chans = _channel_blocks(wl.D, H)
+    if extra_blocks:
+        chans = np.unique(np.concatenate([chans] + [np.arange(s, s + 64) for s in extra_blocks]))
+    ci = torch.as_tensor(chans)
+    gi = torch.as_tensor(np.unique(chans // H))
+    x64 = to64(x.index_select(2, ci))
+    w64 = to64(w.index_select(0 if wl.static else 2, gi))
+    if do_fwd:
+        y = dynconv_fwd(xg, wg, H)
+        ys = y.index_select(2, ci.cuda()).cpu()
+        del y
+        assert_close(f"{wl.name} y", ys, conv_fwd(x64, w64, H), torch.bfloat16)
+    if do_bwd:
+        dyg = dy.cuda()
+        dx, dw = dynconv_bwd(xg, wg, dyg, H)
+        dxs = dx.index_select(2, ci.cuda()).cpu()
+        dws = (dw.index_select(0, gi.cuda()) if wl.static else dw.index_select(2, gi.cuda())).cpu()
+        del dx, dw, dyg
+        rdx, rdw = conv_bwd(x64, w64, to64(dy.index_select(2, ci)), H)
+        assert_close(f"{wl.name} dx", dxs, rdx, torch.bfloat16)
+        if wl.static:
+            assert_close(f"{wl.name} dw", dws, rdw, torch.float32, rtol=1e-5, atol=1e-5)
+        else:
+            assert_close(f"{wl.name} dw", dws, rdw, torch.bfloat16)
+    del xg, wg
+    torch.cuda.empty_cache()
+
+
+def test_full_headwise_h16_fwd():
+    _full_check(synth.workloads()["headwise_h16"], do_bwd=False)
+
+
+def test_full_static_w3_fwd_bwd():
+    _full_check(synth.workloads()["static_w3"])
+
+
+def test_full_qkv_gqa_fused_fwd_bwd():
+    # blocks straddling the Q|K and K|V boundaries as well
+    _full_check(synth.workloads()["qkv_gqa_fused"], extra_blocks=(2048 - 32, 2560 - 32))
+
+
+def test_full_perchannel_h1_fwd_bwd():
+    _full_check(synth.workloads()["perchannel_h1"])
+
+
+def test_full_headwise_h4_bwd():
+    _full_check(synth.workloads()["headwise_h4"], do_fwd=False)
+
+
+def test_full_headwise_h16_bwd():
+    _full_check(synth.workloads()["headwise_h16_bwd"], do_fwd=False)
