@@ -121,16 +121,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
   ET* yb = static_cast<ET*>(p.out) + wt.b * p.os0 + wt.c0;
   const ET* wb = static_cast<const ET*>(p.w) + (STATIC ? 0 : wt.b * p.ws0) + int64_t(g) * W;
 
-  // xh[k] = x_{t-k}; before each step xh[1..W-1] hold the W-1 previous inputs.
+  // Window of inputs. Before the step at token t, xh[j] holds x_{t-1-j} (j < W-1); the
+  // step shifts it by one and inserts x_t, after which xh[k] = x_{t-k}.
   float xh[W][VEC];
 #pragma unroll
   for (int k = 1; k < W; ++k) {
     const int t = wt.t0 - k;
     if (t >= 0) {
-      Vec<ET, VEC>::load(xb + t * p.xs1, xh[k]);
+      Vec<ET, VEC>::load(xb + t * p.xs1, xh[k - 1]);
     } else {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) xh[k][v] = 0.f;
+      for (int v = 0; v < VEC; ++v) xh[k - 1][v] = 0.f;
     }
   }
   Taps<ET, W, VEC, PERCH> wst;

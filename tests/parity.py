@@ -4,8 +4,8 @@ Gate (per output tensor): normwise relative max error
     max|gpu - ref| / max|ref|  <=  1e-5 (float32 path)  or  2e-2 (bf16 path, fp32 accumulate).
 Diagnostic bound (also asserted): elementwise
     |gpu - ref| <= rtol * |ref| + atol * max|ref|
-with rtol = 2^-8 for bf16 outputs (half an ulp of bfloat16's 8-bit significand, the
-rounding of the stored result) and 1e-6 for float32, plus atol for accumulation error.
+with rtol = 2^-8 for bf16 outputs (the unit roundoff of bfloat16's 8-bit significand,
+the rounding of the stored result) and 1e-6 for float32, plus atol for accumulation error.
 """
 from __future__ import annotations
 
@@ -35,7 +35,7 @@ def assert_close(name, got, ref, dtype, rtol=None, atol=None, extra=None):
     """Asserts the normwise gate and the elementwise bound; returns the normwise error.
 
     `extra` is an optional per-element allowance added to the bound (used where an
-    operand is rounded to bf16 before a matrix-core product: 2^-9 * sum |terms|).
+    operand is rounded to bf16 before a matrix-core product: 2^-8 * sum |terms|).
     """
     got64 = to64(got)
     ref = np.asarray(ref, dtype=np.float64)
