@@ -1,0 +1,424 @@
+#!/usr/bin/env python3
+"""Benchmark of the dynamic short convolution hot path on one MI355X.
+
+A step is one forward + backward pass of the per-channel (H = 1) dynamic short
+convolution over one synthetic batch of the pages' model shape: B = 8 sequences,
+T = 4096 tokens, D = 2048 channels, W = 4 taps, bfloat16 storage, float32 arithmetic.
+The reported value is algorithmic HBM bytes per step divided by the time per step:
+forward reads x and w and writes y (12 B per token-channel), backward reads x, w and dy
+and writes dx and dw (22 B per token-channel).
+
+Also measured in the same run (one JSON object per row under "rows"): the head-wise,
+static, fused-QKV and low-rank forms, each kernel timed on its own with HIP events and
+the Infinity Cache flushed between launches; and the float64 CPU oracle on a bounded
+sample (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+import zlib
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak, published
+METRIC = "dyn-conv fwd+bwd achieved HBM GB/s (% of peak), B8·T4096·D2048·W4"
+HEADLINE = dict(B=8, T=4096, D=2048, W=4, H=1)
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "dynamic_short_convolution_amd", "csrc", f)
+    for f in ("dynconv_stream.hip", "dynconv_common.hpp", "dynconv_internal.hpp")
+]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-form measurements")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--only", default=None,
+                    help="run only this row's kernel in a loop (for profiler runs): one of ROWS, or 'copy'")
+    ap.add_argument("--reps", type=int, default=20, help="timed launches per row")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stream_bytes(B, T, D, W, H, eb=2, static=False, fwd=True, bwd=True):
+    """Algorithmic HBM bytes: every input read once, every output written once."""
+    tc = B * T * D
+    wb = 0 if static else B * T * (D // H) * W * eb
+    total = 0
+    if fwd:
+        total += 2 * tc * eb + wb  # x, y + w
+    if bwd:
+        total += 3 * tc * eb + 2 * wb  # x, dy, dx + w, dw
+        if static:
+            total += (D // H) * W * 4  # float32 dw
+    if static:
+        total += (D // H) * W * eb * (int(fwd) + int(bwd))
+    return total
+
+
+def lowrank_bytes(B, T, D, W, R, eb=2, fwd=True):
+    tc = B * T * D
+    J = D * W
+    if fwd:
+        return 2 * tc * eb + B * T * R * eb + R * J * eb + J * eb
+    # x, dy, dx; z, dz; U, b; dU, db (float32)
+    return 3 * tc * eb + 2 * B * T * R * eb + R * J * eb + J * eb + R * J * 4 + J * 4
+
+
+def lowrank_flops(B, T, D, W, R, fwd=True):
+    per = 2 * B * T * R * D * W
+    return per if fwd else 3 * per
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def gen(shape, std, seed, name, device):
+    """Timing-only inputs for the extra rows: seeded N(0, std^2) drawn on the GPU."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(zlib.crc32(f"{seed}:{name}".encode()))
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+class Flusher:
+    """Writes 512 MiB between timed launches so neither the L2s nor the 256 MB Infinity
+    Cache still hold the previous launch's data."""
+
+    def __init__(self, device):
+        import torch
+
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+
+    def __call__(self):
+        self.buf.fill_(1)
+
+
+def time_launches(fn, reps, flush, warm=3):
+    import torch
+
+    for _ in range(warm):
+        fn()
+    evs = []
+    for _ in range(reps):
+        flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return ms[len(ms) // 2], sum(ms) / len(ms)
+
+
+def headline_inputs(device):
+    import synth
+
+    wl = synth.Workload("perchannel_h1", seed=5, **HEADLINE)
+    return wl, wl.x().to(device), wl.w().to(device), wl.dy().to(device)
+
+
+def run_headline(args, device):
+    import torch
+
+    from dynamic_short_convolution_amd import dynconv_bwd, dynconv_fwd
+
+    wl, x, w, dy = headline_inputs(device)
+    H = wl.H
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+
+    def step():
+        dynconv_fwd(x, w, H, out=y)
+        dynconv_bwd(x, w, dy, H, dx=dx, dw=dw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        dynconv_fwd(x, w, H, out=y)
+        e1.record()
+        dynconv_bwd(x, w, dy, H, dx=dx, dw=dw)
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / len(ev)
+    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / len(ev)
+    step_ms = sum(a.elapsed_time(c) for a, _, c in ev) / len(ev)
+    nbytes = stream_bytes(**HEADLINE)
+    fwd_b = stream_bytes(**HEADLINE, bwd=False)
+    bwd_b = stream_bytes(**HEADLINE, fwd=False)
+    return dict(
+        wall_ms_per_step=wall * 1e3 / args.steps,
+        event_ms_per_step=step_ms,
+        fwd_ms=fwd_ms,
+        bwd_ms=bwd_ms,
+        bytes=nbytes,
+        fwd_bytes=fwd_b,
+        bwd_bytes=bwd_b,
+    )
+
+
+# ----------------------------------------------------------------------------------
+# rows: every form of the hot path, each kernel launch timed on its own
+# ----------------------------------------------------------------------------------
+
+ROWS = (
+    "perchannel_h1_fwd",
+    "perchannel_h1_bwd",
+    "headwise_h4_fwd",
+    "headwise_h4_bwd",
+    "headwise_h16_fwd",
+    "headwise_h16_bwd",
+    "static_w3_fwd",
+    "static_w3_bwd",
+    "qkv_gqa_fused_fwd",
+    "qkv_gqa_fused_bwd",
+    "lowrank_r64_fwd",
+    "lowrank_r64_bwd",
+)
+
+
+def make_row(name, device):
+    """Returns (callable, algorithmic bytes, flops or None, description)."""
+    import torch
+
+    from dynamic_short_convolution_amd import (dynconv_bwd, dynconv_bwd_workspace_size, dynconv_fwd,
+                                               dynconv_lowrank_bwd, dynconv_lowrank_bwd_workspace_size,
+                                               dynconv_lowrank_fwd)
+
+    if name.startswith("lowrank"):
+        B, T, D, W, R = 8, 4096, 2048, 4, 64
+        x = gen((B, T, D), 1.0, 4, "x", device)
+        z = gen((B, T, R), 1.0, 4, "z", device)
+        U = gen((R, D * W), 0.1 / R**0.5, 4, "U", device)
+        b = gen((D * W,), 0.1**0.5, 4, "b", device)
+        desc = f"B{B} T{T} D{D} W{W} R{R} bf16"
+        if name.endswith("fwd"):
+            y = torch.empty_like(x)
+            return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, out=y)), lowrank_bytes(B, T, D, W, R), \
+                lowrank_flops(B, T, D, W, R), desc
+        dy = gen((B, T, D), 1.0, 4, "dy", device)
+        ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, 1, R, torch.bfloat16), dtype=torch.uint8,
+                         device=device)
+        return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, workspace=ws)), \
+            lowrank_bytes(B, T, D, W, R, fwd=False), lowrank_flops(B, T, D, W, R, fwd=False), desc
+    if name.startswith("qkv"):
+        B, T, D, W, H = 4, 8192, 3072, 4, 1
+    else:
+        B, T, D = 8, 4096, 2048
+        W = 3 if name.startswith("static") else 4
+        H = {"perchannel_h1": 1, "headwise_h4": 4, "headwise_h16": 16}.get(name.rsplit("_", 1)[0], 1)
+    static = name.startswith("static")
+    x = gen((B, T, D), 1.0, 2, "x", device)
+    w = gen((D // H, W) if static else (B, T, D // H, W), (1.0 / W) ** 0.5, 2, "w", device)
+    desc = f"B{B} T{T} D{D} W{W} H{H}{' static' if static else ''} bf16"
+    if name.endswith("fwd"):
+        y = torch.empty_like(x)
+        return (lambda: dynconv_fwd(x, w, H, out=y)), stream_bytes(B, T, D, W, H, static=static, bwd=False), None, desc
+    dy = gen((B, T, D), 1.0, 2, "dy", device)
+    dx = torch.empty_like(x)
+    dw = torch.empty((D // H, W), dtype=torch.float32, device=device) if static else torch.empty_like(w)
+    assert dynconv_bwd_workspace_size(B, T, D, W, H, static, torch.bfloat16) >= 0
+    return (lambda: dynconv_bwd(x, w, dy, H, dx=dx, dw=dw)), stream_bytes(B, T, D, W, H, static=static, fwd=False), \
+        None, desc
+
+
+def run_rows(args, device):
+    import torch
+
+    flush = Flusher(device)
+    out = {}
+    for name in ROWS:
+        fn, nbytes, flops, desc = make_row(name, device)
+        med, mean = time_launches(fn, args.reps, flush)
+        r = dict(config=desc, median_us=round(med * 1e3, 2), mean_us=round(mean * 1e3, 2), bytes=nbytes,
+                 gbs=round(nbytes / (med * 1e-3) / 1e9, 1))
+        r["pct_hbm_peak"] = round(100.0 * r["gbs"] / HBM_PEAK_GBS, 1)
+        if flops:
+            tf = flops / (med * 1e-3) / 1e12
+            r["flops"] = flops
+            r["tflops"] = round(tf, 1)
+            r["pct_mfma_bf16_peak"] = round(100.0 * tf / MFMA_BF16_PEAK_TFLOPS, 1)
+        out[name] = r
+        log(f"{name}: {r['median_us']} us, {r['gbs']} GB/s")
+        del fn
+        torch.cuda.empty_cache()
+    # orderings the pages report for their kernels (latency falls with H; low-rank below H=1)
+    out["orderings"] = {
+        "fwd_h16_lt_h4_lt_h1": out["headwise_h16_fwd"]["median_us"] < out["headwise_h4_fwd"]["median_us"]
+        < out["perchannel_h1_fwd"]["median_us"],
+        "bwd_h16_lt_h4_lt_h1": out["headwise_h16_bwd"]["median_us"] < out["headwise_h4_bwd"]["median_us"]
+        < out["perchannel_h1_bwd"]["median_us"],
+        "lowrank_fwd_lt_h1_fwd": out["lowrank_r64_fwd"]["median_us"] < out["perchannel_h1_fwd"]["median_us"],
+        "lowrank_bwd_lt_h1_bwd": out["lowrank_r64_bwd"]["median_us"] < out["perchannel_h1_bwd"]["median_us"],
+    }
+    return out
+
+
+def run_only(args, device):
+    """A plain loop of one row (or a 1 GiB device copy) for profiler runs."""
+    import torch
+
+    if args.only == "copy":
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+        a.fill_(3)
+        b_ = torch.empty_like(a)
+        for _ in range(args.steps):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": args.steps}))
+        return
+    fn, nbytes, flops, desc = make_row(args.only, device)
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "config": desc, "bytes": nbytes, "launches": args.steps}))
+
+
+# ----------------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the headline workload
+# ----------------------------------------------------------------------------------
+
+
+def run_cpu_baseline():
+    import synth
+    from oracle import conv_bwd, conv_fwd
+
+    nseq = 2
+    wl = synth.Workload("perchannel_h1", seed=5, **HEADLINE)
+    # the first `nseq` sequences of the same seeded workload
+    x = synth.to_f64(wl.x()[:nseq])
+    w = synth.to_f64(wl.w()[:nseq])
+    dy = synth.to_f64(wl.dy()[:nseq])
+    t0 = time.perf_counter()
+    conv_fwd(x, w, 1)
+    conv_bwd(x, w, dy, 1)
+    sec = time.perf_counter() - t0
+    nbytes = stream_bytes(nseq, HEADLINE["T"], HEADLINE["D"], HEADLINE["W"], 1)
+    return dict(
+        value=round(nbytes / sec / 1e9, 3),
+        unit="GB/s",
+        cores=1,
+        kind="oracle",
+        sample=f"sequences 0..{nseq - 1} of the B8 T4096 D2048 W4 H1 workload (fwd+bwd, float64 NumPy, "
+               f"one process): {sec:.1f} s for {nbytes} bf16-equivalent algorithmic bytes",
+        seconds=round(sec, 2),
+    )
+
+
+def traffic_from_profiles(kernel_key):
+    """Measured HBM bytes per launch from committed counter runs, if the kernel sources
+    still match the ones the counters were taken on."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_digest") != sources_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every box in this setup has one MI355X, and the path has no "
+              f"multi-GPU component (got --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda", 0)
+    from dynamic_short_convolution_amd import _lib
+
+    _lib.load()
+    if args.only:
+        run_only(args, device)
+        return
+
+    log("headline: generating inputs")
+    hl = run_headline(args, device)
+    log(f"headline: fwd {hl['fwd_ms'] * 1e3:.1f} us, bwd {hl['bwd_ms'] * 1e3:.1f} us")
+    gbs = hl["bytes"] / (hl["event_ms_per_step"] * 1e-3) / 1e9
+    bwd_gbs = hl["bwd_bytes"] / (hl["bwd_ms"] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(hl["event_ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "per-channel dynamic short conv fwd+bwd, B8 T4096 D2048 W4 H1",
+            "B": 8, "T": 4096, "D": 2048, "W": 4, "H": 1,
+            "algorithmic_bytes_per_step": hl["bytes"],
+        },
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "wall_ms_per_step": round(hl["wall_ms_per_step"], 4),
+        "fwd_us": round(hl["fwd_ms"] * 1e3, 1),
+        "bwd_us": round(hl["bwd_ms"] * 1e3, 1),
+        "roofline": {
+            "kernel": "k_stream_bwd<bf16, W=4, VEC=2, per-channel>",
+            "bound": "hbm",
+            "achieved": round(bwd_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bwd_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles("perchannel_h1_bwd"),
+            "algorithmic_bytes_per_launch": hl["bwd_bytes"],
+            "avg_launch_us": round(hl["bwd_ms"] * 1e3, 2),
+        },
+        "sources_digest": sources_digest(),
+    }
+    if not args.no_rows:
+        result["rows"] = run_rows(args, device)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: float64 oracle on a sample")
+        result["cpu_baseline"] = run_cpu_baseline()
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
