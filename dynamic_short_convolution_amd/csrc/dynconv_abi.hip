@@ -52,15 +52,27 @@ dynconv_status check_common(int64_t B, int64_t T, int64_t D, int32_t W, int32_t 
   return DYNCONV_OK;
 }
 
+// Widest lane vector (16, 8 or 4 bytes) that every activation-shaped tensor allows, or 0.
+int act_alignment(const Act* a, int n, int eb) {
+  for (int al : {16, 8, 4})
+    if (act_align_ok(a, n, eb, al)) return al;
+  return 0;
+}
+
 // The lane layout of the streaming kernels puts VEC channels on a lane and H / VEC lanes
-// on a group; bf16 lanes hold channel pairs, so D must be even.
-dynconv_status check_stream_layout(int64_t D, int32_t H, int eb, bool wide_ok) {
-  const int small = 4 / eb;
-  const int wide = 16 / eb;
-  if (D % small != 0) return DYNCONV_ERR_UNSUPPORTED;
-  const int vec = (H > 1 && wide_ok && H % wide == 0 && D % wide == 0) ? wide : small;
-  if (H > 1 && H / vec > kWaveSize) return DYNCONV_ERR_UNSUPPORTED;
+// on a group; bf16 lanes hold at least a channel pair, so D must be even.
+dynconv_status check_stream_layout(int64_t D, int32_t H, int eb, int act_align) {
+  if (act_align == 0 || D % (4 / eb) != 0) return DYNCONV_ERR_UNSUPPORTED;
+  const int vmax = act_align / eb;
+  const int vec = H == 1 ? 4 / eb : (H < vmax ? H : vmax);
+  if (H / vec > kWaveSize) return DYNCONV_ERR_UNSUPPORTED;
   return DYNCONV_OK;
+}
+
+// Filter groups (H > 1) of whole 32-bit words are read as words: 4-byte alignment.
+bool group_words_aligned(const void* w, const int64_t* ws, int32_t W, int eb) {
+  if ((int64_t(W) * eb) % 4 != 0) return true;
+  return aligned(w, 4) && (ws[0] * eb) % 4 == 0 && (ws[1] * eb) % 4 == 0;
 }
 
 struct FilterInfo {
@@ -76,7 +88,7 @@ dynconv_status check_filter(const void* w, const int64_t* ws, int32_t W, int32_t
   if (bwd && !fi->is_static && (ws[0] == 0 || ws[1] == 0)) return DYNCONV_ERR_UNSUPPORTED;
   if (H == 1) {
     if (!aligned(w, 4) || (ws[0] * eb) % 4 != 0 || (ws[1] * eb) % 4 != 0) return DYNCONV_ERR_UNSUPPORTED;
-  } else if (!aligned(w, eb)) {
+  } else if (!aligned(w, eb) || !group_words_aligned(w, ws, W, eb)) {
     return DYNCONV_ERR_UNSUPPORTED;
   }
   return DYNCONV_OK;
@@ -123,11 +135,10 @@ dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, cons
   if (y == x || y == w) return DYNCONV_ERR_INVALID_ARG;
   if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
   const Act acts[2] = {{x, xs}, {y, ys}};
-  if (!act_align_ok(acts, 2, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
-  const bool wide_ok = act_align_ok(acts, 2, eb, 16);
-  if ((st = check_stream_layout(D, H, eb, wide_ok)) != DYNCONV_OK) return st;
+  const int align = act_alignment(acts, 2, eb);
+  if ((st = check_stream_layout(D, H, eb, align)) != DYNCONV_OK) return st;
 
-  const StreamPlan plan = plan_stream(B, T, D, H, eb, wide_ok, false, fi.is_static);
+  const StreamPlan plan = plan_stream(B, T, D, H, eb, align, false, fi.is_static);
   StreamParams p{};
   p.x = x;
   p.w = w;
@@ -161,8 +172,8 @@ size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, in
   // The chunking does not depend on the vector width for the static partial count
   // except through nDw; take the larger of the two possible chunk counts.
   size_t best = 0;
-  for (int wide = 0; wide < 2; ++wide) {
-    const StreamPlan pl = plan_stream(B, T, D, H, eb, wide != 0, true, true);
+  for (int align : {4, 8, 16}) {
+    const StreamPlan pl = plan_stream(B, T, D, H, eb, align, true, true);
     const size_t need = size_t(B) * size_t(pl.nTw) * size_t(D / H) * size_t(W) * sizeof(float);
     if (need > best) best = need;
   }
@@ -187,7 +198,7 @@ dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, cons
     if (dws[3] != 1 || dws[2] != W || dws[0] <= 0 || dws[1] <= 0) return DYNCONV_ERR_UNSUPPORTED;
     if (H == 1) {
       if (!aligned(dw, 4) || (dws[0] * eb) % 4 != 0 || (dws[1] * eb) % 4 != 0) return DYNCONV_ERR_UNSUPPORTED;
-    } else if (!aligned(dw, eb)) {
+    } else if (!aligned(dw, eb) || !group_words_aligned(dw, dws, W, eb)) {
       return DYNCONV_ERR_UNSUPPORTED;
     }
   }
@@ -202,11 +213,10 @@ dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, cons
     return DYNCONV_OK;
   }
   const Act acts[3] = {{x, xs}, {dy, dys}, {dx, dxs}};
-  if (!act_align_ok(acts, 3, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
-  const bool wide_ok = act_align_ok(acts, 3, eb, 16);
-  if ((st = check_stream_layout(D, H, eb, wide_ok)) != DYNCONV_OK) return st;
+  const int align = act_alignment(acts, 3, eb);
+  if ((st = check_stream_layout(D, H, eb, align)) != DYNCONV_OK) return st;
 
-  const StreamPlan plan = plan_stream(B, T, D, H, eb, wide_ok, true, fi.is_static);
+  const StreamPlan plan = plan_stream(B, T, D, H, eb, align, true, fi.is_static);
   float* partial = nullptr;
   if (fi.is_static && dw != nullptr) {
     const size_t need = size_t(B) * size_t(plan.nTw) * size_t(D / H) * size_t(W) * sizeof(float);

@@ -16,7 +16,7 @@ constexpr int kBlockThreads = 256;  // 4 waves per workgroup
 // sweeps a run of tokens, keeping the W-1 token halo in registers.
 enum class StreamMode {
   PerChannel,  // H == 1: lane loads the VEC*W contiguous taps of its channels
-  Group,       // H > 1, H % VEC == 0: the lane's channels share one filter
+  Group,       // H > 1, VEC = min(H, 16 / element size): the lane's channels share one filter
 };
 
 // Parameters of the streaming (materialised / static filter) kernels, passed by value.
@@ -47,9 +47,9 @@ struct StreamPlan {
   int64_t blocks;
 };
 
-// Chooses the lane vector width and the time chunking. `wide_ok` says whether every
-// activation-shaped tensor allows 16-byte vectors.
-StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, bool wide_ok, bool bwd,
+// Chooses the lane vector width and the time chunking. `act_align` (4, 8 or 16) is the
+// widest lane vector, in bytes, that every activation-shaped tensor allows.
+StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, int act_align, bool bwd,
                        bool is_static);
 
 dynconv_status launch_stream_fwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,

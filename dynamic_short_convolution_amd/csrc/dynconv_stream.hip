@@ -13,90 +13,183 @@
 // its pending dx sums (backward) in registers, so the time halo costs no LDS traffic
 // and only W-1 extra rows per chunk. Every global access of a wave is a contiguous,
 // coalesced run: x/y as 4 or 16 bytes per lane, the filter taps of the lane's channels
-// as VEC*W contiguous elements (H = 1) or one broadcast group (H > 1).
+// as VEC*W contiguous elements (H = 1) or one broadcast group (H > 1). Loads of U
+// consecutive tokens are issued before any of them is used, with U sized so that about
+// DYNCONV_{FWD,BWD}_INFLIGHT bytes of loads per lane are in flight; the data is streamed with
+// non-temporal hints.
+#include <cmath>
+#include <type_traits>
+
 #include "dynconv_common.hpp"
 #include "dynconv_internal.hpp"
+
+// Tuning, measured on MI355X at the pages' model shapes (B8 T4096 D2048 and B4 T8192
+// D3072, W = 4): the forward streams best with plain stores and about 128 bytes of loads
+// in flight per lane (unroll 4 for the per-channel form) at 8 waves per CU; the per-channel
+// backward with non-temporal stores, unroll 2 and 16 waves per CU; the head-wise and
+// static backward with plain stores at 12 and 8 waves per CU; the static forms prefer
+// neighbouring workgroups to walk channels rather than time. Each constant can be
+// overridden at build time for a sweep.
+#ifndef DYNCONV_FWD_INFLIGHT
+#define DYNCONV_FWD_INFLIGHT 128
+#endif
+#ifndef DYNCONV_BWD_INFLIGHT
+#define DYNCONV_BWD_INFLIGHT 64
+#endif
+#ifndef DYNCONV_FWD_UNROLL  // > 0 overrides the unroll derived from the bytes in flight
+#define DYNCONV_FWD_UNROLL 0
+#endif
+#ifndef DYNCONV_BWD_UNROLL
+#define DYNCONV_BWD_UNROLL 0
+#endif
+#ifndef DYNCONV_FWD_WAVES_PER_CU
+#define DYNCONV_FWD_WAVES_PER_CU 8
+#endif
+#ifndef DYNCONV_BWD_WAVES_PER_CU
+#define DYNCONV_BWD_WAVES_PER_CU 16
+#endif
+#ifndef DYNCONV_BWD_GROUP_WAVES_PER_CU
+#define DYNCONV_BWD_GROUP_WAVES_PER_CU 12
+#endif
+#ifndef DYNCONV_BWD_STATIC_WAVES_PER_CU
+#define DYNCONV_BWD_STATIC_WAVES_PER_CU 8
+#endif
 
 namespace dynconv {
 
 namespace {
 
+// Every streamed input is read once, so loads carry the non-temporal hint.
+__device__ __forceinline__ uint32_t ld32(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint16_t ld16(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+template <bool NT>
+__device__ __forceinline__ void st32(uint32_t* p, uint32_t v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void st16(uint16_t* p, uint16_t v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+
+// N contiguous elements at a 4-byte aligned address, kept as raw 32-bit words until
+// they are used (the compiler fuses the word loads into dwordx2/x3/x4).
 template <typename ET, int N>
-__device__ __forceinline__ void load_dwords(const ET* p, float (&o)[N]) {
-  // N contiguous elements at a 4-byte aligned address, as N*sizeof/4 dword loads
-  // (the compiler fuses them into dwordx2/x3/x4).
-  if constexpr (sizeof(ET) == 2) {
-    static_assert(N % 2 == 0, "bf16 dword loads need an even element count");
+struct Words {
+  static_assert((N * sizeof(ET)) % 4 == 0, "a word vector holds whole 32-bit words");
+  static constexpr int ND = int(N * sizeof(ET) / 4);
+  uint32_t u[ND];
+  __device__ __forceinline__ void load(const ET* p) {
     const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
 #pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      const uint32_t u = q[i];
-      o[2 * i] = bf16_lo(u);
-      o[2 * i + 1] = bf16_hi(u);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) o[i] = reinterpret_cast<const float*>(p)[i];
-  }
-}
-
-template <typename ET, int N>
-__device__ __forceinline__ void store_dwords(ET* p, const float (&v)[N]) {
-  if constexpr (sizeof(ET) == 2) {
-    uint32_t* q = reinterpret_cast<uint32_t*>(p);
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) q[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) reinterpret_cast<float*>(p)[i] = v[i];
-  }
-}
-
-// Filters held by one lane for one token: NC rows of W taps (NC = VEC per channel when
-// H == 1, a single shared row when H > 1).
-template <typename ET, int W, int VEC, bool PERCH>
-struct Taps {
-  static constexpr int NC = PERCH ? VEC : 1;
-  float f[NC][W];
-
-  __device__ __forceinline__ void load(const ET* p) {
-    if constexpr (PERCH) {
-      float tmp[VEC * W];
-      load_dwords<ET, VEC * W>(p, tmp);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v)
-#pragma unroll
-        for (int k = 0; k < W; ++k) f[v][k] = tmp[v * W + k];
-    } else {
-      float tmp[W];
-      load_unaligned<ET, W>(p, tmp);
-#pragma unroll
-      for (int k = 0; k < W; ++k) f[0][k] = tmp[k];
-    }
+    for (int i = 0; i < ND; ++i) u[i] = ld32(q + i);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int v = 0; v < NC; ++v)
-#pragma unroll
-      for (int k = 0; k < W; ++k) f[v][k] = 0.f;
+    for (int i = 0; i < ND; ++i) u[i] = 0u;
   }
-  __device__ __forceinline__ float tap(int v, int k) const { return f[PERCH ? v : 0][k]; }
+  __device__ __forceinline__ float at(int i) const {
+    if constexpr (sizeof(ET) == 2) {
+      return (i & 1) ? bf16_hi(u[i >> 1]) : bf16_lo(u[i >> 1]);
+    } else {
+      return __uint_as_float(u[i]);
+    }
+  }
 };
+
+// N contiguous elements with only element alignment (bf16 filter groups of odd W).
+template <typename ET, int N>
+struct Halves {
+  uint16_t h[N];
+  __device__ __forceinline__ void load(const ET* p) {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+#pragma unroll
+    for (int i = 0; i < N; ++i) h[i] = ld16(q + i);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) h[i] = 0;
+  }
+  __device__ __forceinline__ float at(int i) const { return __uint_as_float(uint32_t(h[i]) << 16); }
+};
+
+template <bool NT, typename ET, int N>
+__device__ __forceinline__ void store_words(ET* p, const float (&v)[N]) {
+  uint32_t* q = reinterpret_cast<uint32_t*>(p);
+  if constexpr (sizeof(ET) == 2) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) st32<NT>(q + i, pack_bf16x2(v[2 * i], v[2 * i + 1]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) st32<NT>(q + i, __float_as_uint(v[i]));
+  }
+}
+
+// N elements at element alignment; words when N elements fill whole 32-bit words and the
+// caller guarantees 4-byte alignment (WORDS), 16-bit stores otherwise.
+template <bool NT, bool WORDS, typename ET, int N>
+__device__ __forceinline__ void store_elems(ET* p, const float (&v)[N]) {
+  if constexpr (sizeof(ET) == 2 && !WORDS) {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+#pragma unroll
+    for (int i = 0; i < N; ++i) st16<NT>(q + i, to_bf16_bits(v[i]));
+  } else {
+    store_words<NT, ET, N>(p, v);
+  }
+}
+
+// Raw taps of one token for one lane: the VEC*W taps of its channels (H = 1) or the W
+// taps of its group (H > 1). Groups of whole 32-bit words are 4-byte aligned (the C ABI
+// checks it), odd bf16 groups are read as 16-bit halves.
+template <typename ET, int W, int VEC, bool PERCH>
+struct TapsRaw {
+  static constexpr bool group_words = (W * sizeof(ET)) % 4 == 0;
+  using type = typename std::conditional<PERCH, Words<ET, VEC * W>,
+                                         typename std::conditional<group_words, Words<ET, W>,
+                                                                   Halves<ET, W>>::type>::type;
+  static constexpr int bytes = PERCH ? VEC * W * int(sizeof(ET)) : W * int(sizeof(ET));
+};
+
+template <typename T>
+__device__ __forceinline__ float tap_of(const T& r, int v, int k, int W, bool perch) {
+  return r.at(perch ? v * W + k : k);
+}
+
+constexpr int pow2_floor(int v) { return v >= 16 ? 16 : v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
+constexpr int clamp_unroll(int v) { return v < 2 ? 2 : (v > 16 ? 16 : v); }
 
 struct WaveTile {
   int b, c0, t0, t1, chunk;
   bool valid;
 };
 
+// CHANNEL_FASTEST: consecutive workgroups take neighbouring channel blocks of the same
+// tokens (used by the static forms); otherwise consecutive time chunks of a channel block.
+template <bool CHANNEL_FASTEST>
 __device__ __forceinline__ WaveTile wave_tile(const StreamParams& p, int vec) {
   WaveTile wt;
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wv = threadIdx.x / kWaveSize;
   uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int tb = lb % p.nTb;
-  lb /= p.nTb;
-  const int db = lb % p.nDb;
-  wt.b = lb / p.nDb;
+  int tb, db;
+  if constexpr (CHANNEL_FASTEST) {
+    db = lb % p.nDb;
+    lb /= p.nDb;
+    tb = lb % p.nTb;
+    wt.b = lb / p.nTb;
+  } else {
+    tb = lb % p.nTb;
+    lb /= p.nTb;
+    db = lb % p.nDb;
+    wt.b = lb / p.nDb;
+  }
   const int dsl = db * p.WD + (wv % p.WD);
   const int tch = tb * p.WT + (wv / p.WD);
   wt.c0 = (dsl * kWaveSize + lane) * vec;
@@ -107,14 +200,19 @@ __device__ __forceinline__ WaveTile wave_tile(const StreamParams& p, int vec) {
   return wt;
 }
 
-constexpr int kUnroll = 4;
-
 // ---------------------------------------------------------------------------------
 // Forward: y_t = x_t + sum_k w_k^(t) x_{t-k}
 // ---------------------------------------------------------------------------------
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC>
 __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams p) {
-  const WaveTile wt = wave_tile(p, VEC);
+  using XR = Words<ET, VEC>;
+  using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
+  constexpr int NC = PERCH ? VEC : 1;
+  constexpr int LB = VEC * int(sizeof(ET)) + (STATIC ? 0 : TapsRaw<ET, W, VEC, PERCH>::bytes);
+  constexpr int U = DYNCONV_FWD_UNROLL > 0 ? DYNCONV_FWD_UNROLL : clamp_unroll(pow2_floor(DYNCONV_FWD_INFLIGHT / LB));
+  constexpr bool NT = false;
+
+  const WaveTile wt = wave_tile<STATIC>(p, VEC);
   if (!wt.valid) return;
   const int g = PERCH ? wt.c0 : wt.c0 / p.H;
   const ET* xb = static_cast<const ET*>(p.x) + wt.b * p.xs0 + wt.c0;
@@ -127,60 +225,64 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
 #pragma unroll
   for (int k = 1; k < W; ++k) {
     const int t = wt.t0 - k;
+    XR r;
     if (t >= 0) {
-      Vec<ET, VEC>::load(xb + t * p.xs1, xh[k - 1]);
+      r.load(xb + t * p.xs1);
     } else {
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) xh[k - 1][v] = 0.f;
+      r.zero();
     }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) xh[k - 1][v] = r.at(v);
   }
-  Taps<ET, W, VEC, PERCH> wst;
-  if constexpr (STATIC) wst.load(wb);
+  float wst[NC][W];
+  if constexpr (STATIC) {
+    TR r;
+    r.load(wb);
+#pragma unroll
+    for (int v = 0; v < NC; ++v)
+#pragma unroll
+      for (int k = 0; k < W; ++k) wst[v][k] = tap_of(r, v, k, W, PERCH);
+  }
 
-  auto compute_store = [&](int t, const float (&xv)[VEC], const Taps<ET, W, VEC, PERCH>& f) {
+  auto step = [&](int t, const XR& xr, const TR& wr) {
 #pragma unroll
     for (int k = W - 1; k >= 1; --k)
 #pragma unroll
       for (int v = 0; v < VEC; ++v) xh[k][v] = xh[k - 1][v];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) xh[0][v] = xv[v];
+    for (int v = 0; v < VEC; ++v) xh[0][v] = xr.at(v);
     float yv[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
       float acc = xh[0][v];
 #pragma unroll
-      for (int k = 0; k < W; ++k) acc = fmaf(f.tap(v, k), xh[k][v], acc);
+      for (int k = 0; k < W; ++k) {
+        const float f = STATIC ? wst[PERCH ? v : 0][k] : tap_of(wr, v, k, W, PERCH);
+        acc = fmaf(f, xh[k][v], acc);
+      }
       yv[v] = acc;
     }
-    Vec<ET, VEC>::store(yb + t * p.os1, yv);
+    store_words<NT, ET, VEC>(yb + t * p.os1, yv);
   };
 
   int t = wt.t0;
-  for (; t + kUnroll <= wt.t1; t += kUnroll) {
-    float xin[kUnroll][VEC];
-    Taps<ET, W, VEC, PERCH> win[kUnroll];
+  for (; t + U <= wt.t1; t += U) {
+    XR xr[U];
+    TR wr[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      Vec<ET, VEC>::load(xb + (t + u) * p.xs1, xin[u]);
-      if constexpr (STATIC) {
-        win[u] = wst;
-      } else {
-        win[u].load(wb + (t + u) * p.ws1);
-      }
+    for (int u = 0; u < U; ++u) {
+      xr[u].load(xb + (t + u) * p.xs1);
+      if constexpr (!STATIC) wr[u].load(wb + (t + u) * p.ws1);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) compute_store(t + u, xin[u], win[u]);
+    for (int u = 0; u < U; ++u) step(t + u, xr[u], wr[u]);
   }
   for (; t < wt.t1; ++t) {
-    float xin[VEC];
-    Taps<ET, W, VEC, PERCH> win;
-    Vec<ET, VEC>::load(xb + t * p.xs1, xin);
-    if constexpr (STATIC) {
-      win = wst;
-    } else {
-      win.load(wb + t * p.ws1);
-    }
-    compute_store(t, xin, win);
+    XR xr;
+    TR wr;
+    xr.load(xb + t * p.xs1);
+    if constexpr (!STATIC) wr.load(wb + t * p.ws1);
+    step(t, xr, wr);
   }
 }
 
@@ -191,7 +293,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
 //   dx_s = dy_s + sum_k w_k^(s+k) dy_{s+k}
 //   dw_t[g,k] = sum_{d in g} dy_t[d] x_{t-k}[d]
 // ---------------------------------------------------------------------------------
-template <int VEC>
 __device__ __forceinline__ float group_sum(float v, int lanes) {
   for (int m = 1; m < lanes; m <<= 1) v += __shfl_xor(v, m, kWaveSize);
   return v;
@@ -199,12 +300,18 @@ __device__ __forceinline__ float group_sum(float v, int lanes) {
 
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC>
 __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams p) {
-  const WaveTile wt = wave_tile(p, VEC);
+  using XR = Words<ET, VEC>;
+  using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
+  constexpr int WM = W > 1 ? W - 1 : 1;
+  constexpr int NC = PERCH ? VEC : 1;
+  constexpr int LB = 2 * VEC * int(sizeof(ET)) + (STATIC ? 0 : TapsRaw<ET, W, VEC, PERCH>::bytes);
+  constexpr int U = DYNCONV_BWD_UNROLL > 0 ? DYNCONV_BWD_UNROLL : clamp_unroll(pow2_floor(DYNCONV_BWD_INFLIGHT / LB));
+  constexpr bool NT = PERCH && !STATIC;
+
+  const WaveTile wt = wave_tile<STATIC>(p, VEC);
   // Group reductions need every lane of a group; a whole group is either valid or not
   // (H divides D and groups are lane-aligned), so invalid lanes can leave now.
   if (!wt.valid) return;
-  constexpr int WM = W > 1 ? W - 1 : 1;
-  constexpr int NC = PERCH ? VEC : 1;
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int lanes_per_group = PERCH ? 1 : p.H / VEC;
   const bool group_lead = PERCH || (lane % lanes_per_group) == 0;
@@ -231,27 +338,38 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
 #pragma unroll
     for (int k = 1; k < W; ++k) {
       const int t = wt.t0 - k;
-      if (t >= 0) Vec<ET, VEC>::load(xb + t * p.xs1, xh[k - 1]);
+      if (t >= 0) {
+        XR r;
+        r.load(xb + t * p.xs1);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) xh[k - 1][v] = r.at(v);
+      }
     }
   }
-  Taps<ET, W, VEC, PERCH> wst;
+  float wst[NC][W];
   float sdw[NC][W];  // static: per-lane partial sums of dw over the chunk
   if constexpr (STATIC) {
-    wst.load(wb);
+    TR r;
+    r.load(wb);
 #pragma unroll
     for (int v = 0; v < NC; ++v)
 #pragma unroll
-      for (int k = 0; k < W; ++k) sdw[v][k] = 0.f;
+      for (int k = 0; k < W; ++k) {
+        wst[v][k] = tap_of(r, v, k, W, PERCH);
+        sdw[v][k] = 0.f;
+      }
   }
 
-  // One step at token t. MAIN: t inside the chunk (x is read, dw produced).
-  auto step = [&](int t, bool main, const float (&dyv)[VEC], const Taps<ET, W, VEC, PERCH>& f,
-                  const float (&xv)[VEC]) {
+  // One step at token t. MAIN: t inside the chunk (x is read, dw produced); HAVE: t < T.
+  auto step = [&](int t, bool main, bool have, const XR& dyr, const TR& wr, const XR& xr) {
+    float dyv[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) dyv[v] = have ? dyr.at(v) : 0.f;
     if (main && want_dw) {
       float d[W][VEC];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        d[0][v] = dyv[v] * xv[v];
+        d[0][v] = dyv[v] * xr.at(v);
 #pragma unroll
         for (int k = 1; k < W; ++k) d[k][v] = dyv[v] * xh[k - 1][v];
       }
@@ -267,7 +385,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
           for (int v = 0; v < VEC; ++v)
 #pragma unroll
             for (int k = 0; k < W; ++k) o[v * W + k] = d[k][v];
-          store_dwords<ET, VEC * W>(dwb + t * p.dws1, o);
+          store_words<NT, ET, VEC * W>(dwb + t * p.dws1, o);
         }
       } else {
         float s[W];
@@ -283,25 +401,31 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
           for (int k = 0; k < W; ++k) sdw[0][k] += s[k];
         } else {
 #pragma unroll
-          for (int k = 0; k < W; ++k) s[k] = group_sum<VEC>(s[k], lanes_per_group);
-          if (group_lead) store_unaligned<ET, W>(dwb + t * p.dws1, s);
+          for (int k = 0; k < W; ++k) s[k] = group_sum(s[k], lanes_per_group);
+          if (group_lead) store_elems<NT, TapsRaw<ET, W, VEC, PERCH>::group_words, ET, W>(dwb + t * p.dws1, s);
         }
       }
     }
     if (want_dx) {
       float nacc[VEC];
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) nacc[v] = fmaf(f.tap(v, 0), dyv[v], dyv[v]);
+      for (int v = 0; v < VEC; ++v) {
+        const float f0 = STATIC ? wst[PERCH ? v : 0][0] : (have ? tap_of(wr, v, 0, W, PERCH) : 0.f);
+        nacc[v] = fmaf(f0, dyv[v], dyv[v]);
+      }
 #pragma unroll
       for (int j = 1; j < W; ++j)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[j - 1][v] = fmaf(f.tap(v, j), dyv[v], acc[j - 1][v]);
+        for (int v = 0; v < VEC; ++v) {
+          const float fj = STATIC ? wst[PERCH ? v : 0][j] : (have ? tap_of(wr, v, j, W, PERCH) : 0.f);
+          acc[j - 1][v] = fmaf(fj, dyv[v], acc[j - 1][v]);
+        }
       const int s = t - (W - 1);
       if (s >= wt.t0 && s < wt.t1) {
         if constexpr (W == 1) {
-          Vec<ET, VEC>::store(dxb + s * p.os1, nacc);
+          store_words<NT, ET, VEC>(dxb + s * p.os1, nacc);
         } else {
-          Vec<ET, VEC>::store(dxb + s * p.os1, acc[W - 2]);
+          store_words<NT, ET, VEC>(dxb + s * p.os1, acc[W - 2]);
         }
       }
 #pragma unroll
@@ -319,79 +443,71 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
 #pragma unroll
         for (int v = 0; v < VEC; ++v) xh[j][v] = xh[j - 1][v];
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) xh[0][v] = xv[v];
+      for (int v = 0; v < VEC; ++v) xh[0][v] = xr.at(v);
     }
   };
 
   int t = wt.t0;
-  for (; t + kUnroll <= wt.t1; t += kUnroll) {
-    float xin[kUnroll][VEC], dyin[kUnroll][VEC];
-    Taps<ET, W, VEC, PERCH> win[kUnroll];
+  for (; t + U <= wt.t1; t += U) {
+    XR xr[U], dyr[U];
+    TR wr[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      Vec<ET, VEC>::load(dyb + (t + u) * p.dys1, dyin[u]);
+    for (int u = 0; u < U; ++u) {
+      dyr[u].load(dyb + (t + u) * p.dys1);
       if (want_dw) {
-        Vec<ET, VEC>::load(xb + (t + u) * p.xs1, xin[u]);
+        xr[u].load(xb + (t + u) * p.xs1);
       } else {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) xin[u][v] = 0.f;
+        xr[u].zero();
       }
-      if constexpr (STATIC) {
-        win[u] = wst;
-      } else {
+      if constexpr (!STATIC) {
         if (want_dx) {
-          win[u].load(wb + (t + u) * p.ws1);
+          wr[u].load(wb + (t + u) * p.ws1);
         } else {
-          win[u].zero();
+          wr[u].zero();
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) step(t + u, true, dyin[u], win[u], xin[u]);
+    for (int u = 0; u < U; ++u) step(t + u, true, true, dyr[u], wr[u], xr[u]);
   }
   for (; t < wt.t1; ++t) {
-    float xin[VEC], dyin[VEC];
-    Taps<ET, W, VEC, PERCH> win;
-    Vec<ET, VEC>::load(dyb + t * p.dys1, dyin);
+    XR xr, dyr;
+    TR wr;
+    dyr.load(dyb + t * p.dys1);
     if (want_dw) {
-      Vec<ET, VEC>::load(xb + t * p.xs1, xin);
+      xr.load(xb + t * p.xs1);
     } else {
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) xin[v] = 0.f;
+      xr.zero();
     }
-    if constexpr (STATIC) {
-      win = wst;
-    } else {
+    if constexpr (!STATIC) {
       if (want_dx) {
-        win.load(wb + t * p.ws1);
+        wr.load(wb + t * p.ws1);
       } else {
-        win.zero();
+        wr.zero();
       }
     }
-    step(t, true, dyin, win, xin);
+    step(t, true, true, dyr, wr, xr);
   }
   // Future halo: the W-1 tokens after the chunk complete its last dx rows.
   if (want_dx) {
+    XR hx[WM], hdy[WM];
+    TR hw[WM];
 #pragma unroll
     for (int e = 0; e < W - 1; ++e) {
       const int tt = wt.t1 + e;
-      float dyin[VEC], xin[VEC];
-      Taps<ET, W, VEC, PERCH> win;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) xin[v] = 0.f;
+      hx[e].zero();
       if (tt < p.T) {
-        Vec<ET, VEC>::load(dyb + tt * p.dys1, dyin);
-        if constexpr (STATIC) {
-          win = wst;
-        } else {
-          win.load(wb + tt * p.ws1);
-        }
+        hdy[e].load(dyb + tt * p.dys1);
+        if constexpr (!STATIC) hw[e].load(wb + tt * p.ws1);
       } else {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) dyin[v] = 0.f;
-        win.zero();
+        hdy[e].zero();
+        if constexpr (!STATIC) hw[e].zero();
       }
-      step(tt, false, dyin, win, xin);
+    }
+#pragma unroll
+    for (int e = 0; e < W - 1; ++e) {
+      const int tt = wt.t1 + e;
+      step(tt, false, tt < p.T, hdy[e], hw[e], hx[e]);
     }
   }
   if constexpr (STATIC) {
@@ -405,7 +521,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       } else {
         float s[W];
 #pragma unroll
-        for (int k = 0; k < W; ++k) s[k] = group_sum<VEC>(sdw[0][k], lanes_per_group);
+        for (int k = 0; k < W; ++k) s[k] = group_sum(sdw[0][k], lanes_per_group);
         if (group_lead) {
 #pragma unroll
           for (int k = 0; k < W; ++k) part[int64_t(g) * W + k] = s[k];
@@ -415,14 +531,31 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   }
 }
 
-// Fixed-order (chunk 0, 1, 2, ...) sum of partials, accumulated in float64.
+// Fixed-order sum of partials: out[i] = sum_c part[c * n + i]. A workgroup owns 32
+// consecutive columns; its 8 thread groups take chunks c = grp, grp + 8, ... in order
+// (float64), and the 8 group sums are added in order grp = 0..7. The order depends only
+// on (nchunk, n), so results are run-to-run identical.
+constexpr int kRedCols = 32;
+constexpr int kRedGroups = kBlockThreads / kRedCols;
+
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials(const float* __restrict__ part, int64_t nchunk,
                                                                    int64_t n, float* __restrict__ out) {
-  const int64_t i = int64_t(blockIdx.x) * kBlockThreads + threadIdx.x;
-  if (i >= n) return;
+  __shared__ double red[kRedGroups][kRedCols];
+  const int col = threadIdx.x % kRedCols;
+  const int grp = threadIdx.x / kRedCols;
+  const int64_t i = int64_t(blockIdx.x) * kRedCols + col;
   double s = 0.0;
-  for (int64_t c = 0; c < nchunk; ++c) s += double(part[c * n + i]);
-  out[i] = float(s);
+  if (i < n) {
+    for (int64_t c = grp; c < nchunk; c += kRedGroups) s += double(part[c * n + i]);
+  }
+  red[grp][col] = s;
+  __syncthreads();
+  if (grp == 0 && i < n) {
+    double tot = 0.0;
+#pragma unroll
+    for (int r = 0; r < kRedGroups; ++r) tot += red[r][col];
+    out[i] = float(tot);
+  }
 }
 
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC>
@@ -450,11 +583,11 @@ hipError_t dispatch_static(const StreamParams& p, const StreamPlan& plan, bool s
 
 template <bool BWD, typename ET, int W>
 hipError_t dispatch_mode(const StreamParams& p, const StreamPlan& plan, bool st, hipStream_t s) {
-  constexpr int kSmall = 4 / int(sizeof(ET));
-  constexpr int kWide = 16 / int(sizeof(ET));
-  if (plan.mode == StreamMode::PerChannel) return dispatch_static<BWD, ET, W, kSmall, true>(p, plan, st, s);
-  if (plan.vec == kWide) return dispatch_static<BWD, ET, W, kWide, false>(p, plan, st, s);
-  return dispatch_static<BWD, ET, W, kSmall, false>(p, plan, st, s);
+  constexpr int k4 = 4 / int(sizeof(ET));
+  if (plan.mode == StreamMode::PerChannel) return dispatch_static<BWD, ET, W, k4, true>(p, plan, st, s);
+  if (plan.vec == 4 * k4) return dispatch_static<BWD, ET, W, 4 * k4, false>(p, plan, st, s);
+  if (plan.vec == 2 * k4) return dispatch_static<BWD, ET, W, 2 * k4, false>(p, plan, st, s);
+  return dispatch_static<BWD, ET, W, k4, false>(p, plan, st, s);
 }
 
 template <bool BWD, typename ET>
@@ -471,34 +604,57 @@ hipError_t dispatch_w(const StreamParams& p, const StreamPlan& plan, int W, bool
 
 }  // namespace
 
-StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, bool wide_ok, bool bwd,
+StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, int act_align, bool bwd,
                        bool is_static) {
   StreamPlan pl{};
-  const int small = 4 / elem_bytes;
-  const int wide = 16 / elem_bytes;
   if (H == 1) {
     pl.mode = StreamMode::PerChannel;
-    pl.vec = small;
+    pl.vec = 4 / elem_bytes;
   } else {
+    // a lane holds min(H, widest aligned vector) channels of one group
     pl.mode = StreamMode::Group;
-    pl.vec = (wide_ok && H % wide == 0 && D % wide == 0) ? wide : small;
+    const int vmax = act_align / elem_bytes;
+    pl.vec = H < vmax ? H : vmax;
   }
   const int64_t span = int64_t(kWaveSize) * pl.vec;
   pl.nDw = int((D + span - 1) / span);
-  // Aim at about 16 waves per CU over the 256 CUs, with chunks of at least 16 tokens.
-  const int64_t target_waves = 256 * 16;
-  int64_t per_seq = (target_waves + B * pl.nDw - 1) / (B * pl.nDw);
-  const int64_t max_chunks = (T + 15) / 16;
-  if (per_seq > max_chunks) per_seq = max_chunks;
-  if (per_seq < 1) per_seq = 1;
-  int64_t L = (T + per_seq - 1) / per_seq;
-  L = (L + 3) / 4 * 4;
-  if (bwd && is_static && L < 64) L = T < 64 ? L : 64;  // fewer partials to reduce
-  pl.L = int(L);
-  pl.nTw = int((T + L - 1) / L);
   pl.WD = pl.nDw >= 4 ? 4 : (pl.nDw >= 2 ? 2 : 1);
   pl.WT = 4 / pl.WD;
   pl.nDb = (pl.nDw + pl.WD - 1) / pl.WD;
+  // Time chunking: aim at a number of waves per CU, but prefer grids that spread evenly
+  // over the 256 CUs (a grid of 4.03 workgroups per CU runs as long as one of 5). Chunks
+  // hold a multiple of 4 tokens and at least 16 (64 for the static backward, which writes
+  // one partial sum per chunk).
+  const int waves_per_cu = !bwd ? DYNCONV_FWD_WAVES_PER_CU
+                           : is_static ? DYNCONV_BWD_STATIC_WAVES_PER_CU
+                           : H > 1     ? DYNCONV_BWD_GROUP_WAVES_PER_CU
+                                       : DYNCONV_BWD_WAVES_PER_CU;
+  const double target_blocks = 256.0 * waves_per_cu / (kBlockThreads / kWaveSize);
+  const int64_t min_len = (bwd && is_static) ? 64 : 16;
+  const int64_t max_chunks = T <= min_len ? 1 : (T + min_len - 1) / min_len;
+  const double per_seq_target = target_blocks * pl.WT / double(B * pl.nDb);
+  int64_t lo = int64_t(per_seq_target / 4), hi = int64_t(per_seq_target * 4) + 1;
+  if (lo < 1) lo = 1;
+  if (hi > max_chunks) hi = max_chunks;
+  if (lo > hi) lo = hi;
+  double best = -1e30;
+  int64_t bestL = T;
+  for (int64_t c = lo; c <= hi; ++c) {
+    int64_t L = (T + c - 1) / c;
+    L = (L + 3) / 4 * 4;
+    const int64_t nTw = (T + L - 1) / L;
+    const int64_t blocks = B * pl.nDb * ((nTw + pl.WT - 1) / pl.WT);
+    const int64_t per_cu = (blocks + 255) / 256;
+    const double eff = double(blocks) / double(256 * per_cu);
+    const double dist = std::fabs(std::log(double(blocks) / target_blocks));
+    const double score = eff - 0.25 * dist;
+    if (score > best + 1e-12) {
+      best = score;
+      bestL = L;
+    }
+  }
+  pl.L = int(bestL);
+  pl.nTw = int((T + bestL - 1) / bestL);
   pl.nTb = (pl.nTw + pl.WT - 1) / pl.WT;
   pl.blocks = B * int64_t(pl.nDb) * pl.nTb;
   return pl;
@@ -524,7 +680,7 @@ dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, 
 
 dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,
                                       hipStream_t stream) {
-  const int64_t blocks = (n + kBlockThreads - 1) / kBlockThreads;
+  const int64_t blocks = (n + kRedCols - 1) / kRedCols;
   hipLaunchKernelGGL(k_reduce_partials, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk, n,
                      out);
   const hipError_t e = hipGetLastError();

@@ -32,12 +32,15 @@
  * - Validation happens before any HIP call; invalid input returns a status, never aborts.
  *   B == 0 or T == 0 or D == 0 is a no-op returning DYNCONV_OK.
  * - Supported parameters: 1 <= W <= 5; H == 1 or H a power of two that divides D, with
- *   H <= 64 * (16 / element size) (512 for bf16, 256 for float32; H <= 64 * (4 / element
- *   size) when the wide path below is not available); 1 <= R <= 256 for the low-rank form.
+ *   H / VEC <= 64 where VEC = min(H, widest lane vector allowed by the alignment below /
+ *   element size), i.e. H <= 512 (bf16) or 256 (float32) with 16-byte aligned
+ *   activations; low-rank form: H == 1 and 1 <= R <= 128.
  * - Alignment: base pointers of activation-shaped tensors and their s[0], s[1] (in bytes)
- *   must be multiples of 4 bytes (bf16: D even); when all of them are multiples of 16 bytes
- *   and D is a multiple of 16 / element size, a wider vector path is used. w (H == 1):
- *   base and strides multiples of 4 bytes. Violations return DYNCONV_ERR_UNSUPPORTED.
+ *   must be multiples of 4 bytes (bf16: D even); wider lane vectors (8 or 16 bytes) are
+ *   used when every activation-shaped tensor of the call allows them. Filters: base and
+ *   s[0], s[1] multiples of 4 bytes for H == 1, and for H > 1 when the W taps of a group
+ *   fill whole 32-bit words (float32, or bf16 with W even); element alignment otherwise.
+ *   Violations return DYNCONV_ERR_UNSUPPORTED.
  * - An output pointer equal to any input pointer returns DYNCONV_ERR_INVALID_ARG
  *   (in-place use would corrupt the time halo); partial overlap is undefined behaviour.
  * - A failed kernel launch returns DYNCONV_ERR_HIP; dynconv_last_hip_error() then gives
