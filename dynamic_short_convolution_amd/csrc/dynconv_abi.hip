@@ -328,6 +328,8 @@ dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void*
   if (!act_align_ok(acts, 2, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
   const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, false);
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
+  p.act16 = act_align_ok(acts, 2, eb, 16) ? 1 : 0;
+  p.z16 = (aligned(z, 16) && (zs[0] * eb) % 16 == 0 && (zs[1] * eb) % 16 == 0) ? 1 : 0;
   p.out = y;
   p.os0 = ys[0];
   p.os1 = ys[1];
@@ -370,6 +372,8 @@ dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void*
   if (workspace == nullptr || workspace_bytes < plan.ws_total) return DYNCONV_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return DYNCONV_ERR_UNSUPPORTED;
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
+  p.act16 = act_align_ok(acts, 3, eb, 16) ? 1 : 0;
+  p.z16 = (aligned(z, 16) && (zs[0] * eb) % 16 == 0 && (zs[1] * eb) % 16 == 0) ? 1 : 0;
   p.dy = dy;
   p.dys0 = dys[0];
   p.dys1 = dys[1];

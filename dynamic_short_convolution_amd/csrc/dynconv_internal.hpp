@@ -85,7 +85,28 @@ struct LowRankParams {
   int32_t nCs;     // channel slices
   int32_t Ltok;    // tokens per token range
   int32_t nTr;     // token ranges per sequence
+  int32_t act16;   // every activation-shaped tensor allows 16-byte vectors
+  int32_t z16;     // z rows allow 16-byte vectors
 };
+
+// Low-rank forward tiling, shared by the planner and the kernel: each wave generates MT
+// 16-row MFMA tiles of filter columns; a filter of W <= 4 taps takes 4 rows (one lane
+// group), W = 5 takes 8 rows (two lane groups). A workgroup of 4 waves covers
+// 4 * MT * 16 / rows_per_channel channels.
+#ifndef LOWRANK_FWD_MT
+#define LOWRANK_FWD_MT 8
+#endif
+constexpr int lowrank_fwd_mt(int KS) { return KS <= 2 ? LOWRANK_FWD_MT : 4; }
+constexpr int lowrank_rows_per_channel(int W) { return W > 4 ? 8 : 4; }
+constexpr int lowrank_fwd_dc(int W, int KS) { return 4 * lowrank_fwd_mt(KS) * 16 / lowrank_rows_per_channel(W); }
+// Backward: fewer filter tiles per wave (its registers also hold dU accumulators).
+constexpr int lowrank_bwd_mt(int) { return 2; }
+constexpr int lowrank_bwd_dc(int W, int KS) { return 4 * lowrank_bwd_mt(KS) * 16 / lowrank_rows_per_channel(W); }
+// dz kernel: tokens per workgroup and channels per staged chunk of U.
+constexpr int kLowrankDzTokens = 128;
+constexpr int lowrank_dz_chunk(int KS, int elem_bytes, int W) {
+  return (KS <= 2 ? 64 : 32) * 2 / elem_bytes / (lowrank_rows_per_channel(W) / 4);
+}
 
 struct LowRankPlan {
   int nCs, Ltok, nTr;
