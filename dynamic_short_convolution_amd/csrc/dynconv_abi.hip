@@ -374,6 +374,7 @@ dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void*
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
   p.act16 = act_align_ok(acts, 3, eb, 16) ? 1 : 0;
   p.z16 = (aligned(z, 16) && (zs[0] * eb) % 16 == 0 && (zs[1] * eb) % 16 == 0) ? 1 : 0;
+  p.u16 = (aligned(U, 16) && (ldu * eb) % 16 == 0) ? 1 : 0;
   p.dy = dy;
   p.dys0 = dys[0];
   p.dys1 = dys[1];

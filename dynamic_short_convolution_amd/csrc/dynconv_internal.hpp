@@ -74,7 +74,6 @@ struct LowRankParams {
   void* dz;
   float* part_dU;  // [nTr][R][J]   partial dU per token range
   float* part_db;  // [nTr][J]      partial db per token range
-  float* part_dz;  // [nCs][B*T][R] partial dz per channel slice
   int64_t xs0, xs1;
   int64_t zs0, zs1;
   int64_t ldu;
@@ -87,6 +86,7 @@ struct LowRankParams {
   int32_t nTr;     // token ranges per sequence
   int32_t act16;   // every activation-shaped tensor allows 16-byte vectors
   int32_t z16;     // z rows allow 16-byte vectors
+  int32_t u16;     // U rows allow 16-byte vectors
 };
 
 // Low-rank forward tiling, shared by the planner and the kernel: each wave generates MT
@@ -99,19 +99,19 @@ struct LowRankParams {
 constexpr int lowrank_fwd_mt(int KS) { return KS <= 2 ? LOWRANK_FWD_MT : 4; }
 constexpr int lowrank_rows_per_channel(int W) { return W > 4 ? 8 : 4; }
 constexpr int lowrank_fwd_dc(int W, int KS) { return 4 * lowrank_fwd_mt(KS) * 16 / lowrank_rows_per_channel(W); }
-// Backward: fewer filter tiles per wave (its registers also hold dU accumulators).
+// Backward: fewer filter tiles per wave (its registers also hold dU accumulators); the
+// pipeline advances kLowrankBwdStep tokens per step.
 constexpr int lowrank_bwd_mt(int) { return 2; }
 constexpr int lowrank_bwd_dc(int W, int KS) { return 4 * lowrank_bwd_mt(KS) * 16 / lowrank_rows_per_channel(W); }
-// dz kernel: tokens per workgroup and channels per staged chunk of U.
-constexpr int kLowrankDzTokens = 128;
-constexpr int lowrank_dz_chunk(int KS, int elem_bytes, int W) {
-  return (KS <= 2 ? 64 : 32) * 2 / elem_bytes / (lowrank_rows_per_channel(W) / 4);
-}
+constexpr int kLowrankBwdStep = 64;
+// dz kernel: tokens per workgroup (16 per wave) and channels per staged chunk.
+constexpr int kLowrankDzTokens = 64;
+constexpr int kLowrankDzChunk = 32;
 
 struct LowRankPlan {
   int nCs, Ltok, nTr;
   int64_t blocks;
-  size_t ws_dU, ws_db, ws_dz;  // byte offsets inside the workspace
+  size_t ws_dU, ws_db;  // byte offsets inside the workspace
   size_t ws_total;
 };
 

@@ -127,65 +127,6 @@ __device__ __forceinline__ LrBlock lr_block(const LowRankParams& p) {
   return r;
 }
 
-// U^T fragments of this wave's filter-column tiles, loaded once per workgroup, and the
-// bias as the accumulator's initial value. Columns past J and ranks past R read as 0.
-template <typename ET, int KS, int MTW>
-struct GenFrags {
-  typename Mfma<ET>::F32k a[MTW][KS];
-  f32x4_t binit[MTW];
-
-  __device__ __forceinline__ void load(const LowRankParams& p, int j_base, int wv, int mt_total) {
-    using R_ = Raw<ET>;
-    const int lane = threadIdx.x & 63;
-    const int q = lane >> 4;
-    const ET* U = static_cast<const ET*>(p.U);
-    const ET* bias = static_cast<const ET*>(p.bias);
-#pragma unroll
-    for (int i = 0; i < MTW; ++i) {
-      const int mt = wv + 4 * i;
-      const bool mt_ok = mt < mt_total;
-      const int j = j_base + mt * 16 + (lane & 15);
-      const bool j_ok = mt_ok && j < p.J;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 32 * ks + Mfma<ET>::k32(q, e);
-          const auto v = (j_ok && r < p.R) ? R_::from_mem(U, int64_t(r) * p.ldu + j) : R_::zero();
-          a[i][ks].v[e] = v;
-        }
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int jr = j_base + mt * 16 + 4 * q + ii;
-        binit[i][ii] = (mt_ok && bias != nullptr && jr < p.J) ? R_::to_float(R_::from_mem(bias, jr)) : 0.f;
-      }
-    }
-  }
-};
-
-// One 16 x 16 block of generated filters: rows are filter columns (mt*16 ..), columns are
-// the 16 tokens of the tile; z tile row n starts at zl + n * ZP.
-template <typename ET, int KS, int ZP>
-__device__ __forceinline__ f32x4_t gen_tile(const typename Mfma<ET>::F32k (&a)[KS], f32x4_t acc,
-                                            const typename Raw<ET>::type* zl) {
-  const int lane = threadIdx.x & 63;
-  const int q = lane >> 4;
-  const int n = lane & 15;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    typename Mfma<ET>::F32k bfr;
-    if constexpr (sizeof(ET) == 2) {
-      bfr.v = *reinterpret_cast<const u16x8_t*>(zl + n * ZP + 32 * ks + 8 * q);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bfr.v[e] = zl[n * ZP + 32 * ks + Mfma<ET>::k32(q, e)];
-    }
-    acc = Mfma<ET>::mma32(a[ks], bfr, acc);
-  }
-  return acc;
-}
-
 // Slot of token t in the x ring of one workgroup (tokens t_first - HALO .. kept).
 __device__ __forceinline__ int ring_slot(int t, int t_first) { return (t - t_first + HALO) % RING; }
 
@@ -283,105 +224,6 @@ __device__ __forceinline__ void global_store_run(ET* p, const float (&v)[N], boo
       } else {
         reinterpret_cast<float*>(p)[e] = v[e];
       }
-    }
-  }
-}
-
-template <typename ET>
-__device__ __forceinline__ float chunk_elem(const u32x4& v, int e) {
-  if constexpr (sizeof(ET) == 2) {
-    return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-  } else {
-    return __uint_as_float(v[e]);
-  }
-}
-
-// DPP / register-run helpers shared by the kernels below.
-template <typename ET, int N>
-struct RunWords {  // N contiguous elements as raw 32-bit words
-  static constexpr int ND = N * int(sizeof(ET)) / 4;
-  uint32_t u[ND];
-};
-
-template <typename ET, int N>
-__device__ __forceinline__ void load_run(RunWords<ET, N>& r, const ET* p, bool vec, int count) {
-  constexpr int ND = RunWords<ET, N>::ND;
-  if (vec && count >= N) {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    if constexpr (ND % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < ND / 4; ++i) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q) + i);
-        r.u[4 * i] = v[0];
-        r.u[4 * i + 1] = v[1];
-        r.u[4 * i + 2] = v[2];
-        r.u[4 * i + 3] = v[3];
-      }
-    } else if constexpr (ND == 2) {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q));
-      r.u[0] = v[0];
-      r.u[1] = v[1];
-    } else {
-#pragma unroll
-      for (int i = 0; i < ND; ++i) r.u[i] = __builtin_nontemporal_load(q + i);
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < ND; ++i) r.u[i] = 0u;
-#pragma unroll
-  for (int e = 0; e < N; ++e) {
-    if (e < count) {
-      if constexpr (sizeof(ET) == 2) {
-        const uint32_t h = reinterpret_cast<const uint16_t*>(p)[e];
-        r.u[e >> 1] |= (e & 1) ? (h << 16) : h;
-      } else {
-        r.u[e] = __float_as_uint(reinterpret_cast<const float*>(p)[e]);
-      }
-    }
-  }
-}
-
-template <typename ET, int N>
-__device__ __forceinline__ float run_elem(const RunWords<ET, N>& r, int e) {
-  if constexpr (sizeof(ET) == 2) {
-    return (e & 1) ? bf16_hi(r.u[e >> 1]) : bf16_lo(r.u[e >> 1]);
-  } else {
-    return __uint_as_float(r.u[e]);
-  }
-}
-
-// Lane i of each 16-lane row gets cur from lane i - K, or prev from lane i - K + 16.
-template <int K, typename ET, int N>
-__device__ __forceinline__ RunWords<ET, N> shift_rows(const RunWords<ET, N>& cur, const RunWords<ET, N>& prev) {
-  static_assert(K >= 1 && K <= 15, "row shifts are 1..15 lanes");
-  RunWords<ET, N> r;
-#pragma unroll
-  for (int i = 0; i < RunWords<ET, N>::ND; ++i) {
-    const int from_prev = __builtin_amdgcn_mov_dpp(int(prev.u[i]), 0x120 | K, 0xf, 0xf, false);
-    r.u[i] = uint32_t(__builtin_amdgcn_update_dpp(from_prev, int(cur.u[i]), 0x110 | K, 0xf, 0xf, false));
-  }
-  return r;
-}
-
-// z fragment of one K step for lane (token row, group q): z[row][32 ks + k32(q, e)].
-template <typename ET>
-__device__ __forceinline__ void load_zfrag(typename Mfma<ET>::F32k& f, const ET* zrow, int ks, int q, int R,
-                                           bool vec, bool row_ok) {
-  if constexpr (sizeof(ET) == 2) {
-    const int r0 = 32 * ks + 8 * q;
-    if (row_ok && vec && r0 + 8 <= R) {
-      f.v = __builtin_nontemporal_load(reinterpret_cast<const u16x8_t*>(zrow + r0));
-      return;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      f.v[e] = (row_ok && r0 + e < R) ? reinterpret_cast<const uint16_t*>(zrow)[r0 + e] : uint16_t(0);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = 32 * ks + Mfma<ET>::k32(q, e);
-      f.v[e] = (row_ok && r < R) ? reinterpret_cast<const float*>(zrow)[r] : 0.f;
     }
   }
 }
@@ -583,16 +425,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
 // ---------------------------------------------------------------------------------
 // Backward main kernel: dx, and float32 partial sums of dU and db per token range.
 //
-// Same workgroup decomposition and filter regeneration as the forward (with MT tiles
-// per wave, so lane (token n, group q) holds the filter taps of a run of MT contiguous
-// channels for token t0 + n). Per 16-token tile:
+// Same workgroup decomposition and filter regeneration as the forward (MT tiles per
+// wave, so lane (token n, group q) holds the filter taps of a run of MT contiguous
+// channels for one token). The pipeline advances S = 64 tokens (four 16-token tiles)
+// per step, with the loads of the next two steps in flight; a step's x and dy rows sit
+// in a tile that starts HALO tokens early (those rows are copied from the previous
+// tile), so every LDS address is a per-lane base plus a compile-time offset. Per tile:
 //  * P_k = w_k^(t) dy_t for the lane's token; dx_s = dy_s + sum_k P_k(s + k) is formed
-//    for s = t0 + n - (W-1): the terms of later tokens come from the lanes to the right
-//    (DPP row_shr) and, for the first lanes, from the previous tile (DPP row_ror). One
-//    extra tile past the range supplies the last W-1 rows (the future halo).
-//  * g_k(t) = dy_t x_{t-k} for the lane's token and channels (x from the LDS ring); db
-//    is summed per lane; g goes to a wave-private LDS tile, from which the matrix cores
-//    accumulate dU += z^T g (K = the 16 tokens) in registers over the whole range.
+//    for s = t - (W-1): the terms of later tokens come from the lanes to the right
+//    (DPP row_shr) and, for the first lanes, from the previous tile (DPP row_ror). The
+//    tiles past the range supply the last W-1 rows (the future halo).
+//  * g_k(t) = dy_t x_{t-k} for the lane's token and channels; db is summed per lane; g
+//    is written token-contiguous to a wave-private LDS tile.
+// Per step the matrix cores then accumulate dU += z^T g (K = 32 tokens per instruction)
+// in registers over the whole range, reading z from a token-contiguous copy staged next
+// to the row-major one that feeds the regeneration.
 // ---------------------------------------------------------------------------------
 template <int K>
 __device__ __forceinline__ float shift_lanes(float cur, float prev) {
@@ -610,33 +457,115 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// 16 bytes at base + off (elements) for a lane whose chunk is valid (`ok`). FAST: one
+// 16-byte load whatever `ok` (lanes that must not read load `safe`, a valid address),
+// so every thread issues the same number of loads; the value of a !ok lane is dropped
+// later, by keep_if() when it is stored, so that nothing waits for the load here. The
+// caller guarantees 16-byte alignment and whole chunks. Otherwise element loads of the
+// first `limit` elements behind a branch, zero-filled (keep_if() changes nothing).
+template <bool FAST, typename ET>
+__device__ __forceinline__ u32x4 stage16(const ET* base, int off, bool ok, int limit, const ET* safe) {
+  if constexpr (FAST) {
+    const ET* a = ok ? base + off : safe;
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+  } else {
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (ok) r = load_chunk<ET>(base + off, 0, limit, false);
+    return r;
+  }
+}
+
+__device__ __forceinline__ u32x4 keep_if(const u32x4& v, uint32_t okmask, int bit) {
+  return ((okmask >> bit) & 1u) ? v : u32x4{0u, 0u, 0u, 0u};
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// K = 32 MFMA fragment (element e <-> k = 8q + e) of column col0 + (lane % 16) of a
+// row-major 16-bit LDS tile whose row k0 + k holds index k, by two transposing 8-byte
+// reads (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i % 4 of
+// the 4 values loaded by lanes i / 4 + 4 e', e' = 0..3). Lane j of group q loads row
+// k0 + 8q + j / 4 (+ 4 for the second half), columns col0 + 4 (j % 4) .. + 3.
+__device__ __forceinline__ u16x8_t lds_colfrag_tr(const uint16_t* tile, int pitch, int k0, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, j = lane & 15;
+  const uint16_t* a = tile + (k0 + 8 * q + (j >> 2)) * pitch + col0 + 4 * (j & 3);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 4 * pitch));
+  u16x8_t r;
+  r[0] = uint16_t(lo[0]); r[1] = uint16_t(lo[1]); r[2] = uint16_t(lo[2]); r[3] = uint16_t(lo[3]);
+  r[4] = uint16_t(hi[0]); r[5] = uint16_t(hi[1]); r[6] = uint16_t(hi[2]); r[7] = uint16_t(hi[3]);
+  return r;
+}
+
+// The same fragment for float32 tiles (element e <-> k = k32(q, e)), element reads.
+template <typename ET>
+__device__ __forceinline__ void lds_colfrag(typename Mfma<ET>::F32k& f, const typename Raw<ET>::type* tile, int pitch,
+                                            int k0, int col0) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (sizeof(ET) == 2) {
+    f.v = lds_colfrag_tr(tile, pitch, k0, col0);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = tile[(k0 + Mfma<ET>::k32(lane >> 4, e)) * pitch + col0 + (lane & 15)];
+  }
+}
+
+// Tile shape of the backward main kernel (shared by its LDS layout and its code).
 template <typename ET, int W, int KS>
-__global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankParams p) {
+struct LrBwdShape {
+  using RT = typename Raw<ET>::type;
+  static constexpr int EB = int(sizeof(ET));
+  static constexpr int MT = lowrank_bwd_mt(KS);
+  static constexpr int WP = lowrank_rows_per_channel(W);  // padded taps per channel
+  static constexpr int LPC = WP / 4;
+  static constexpr int CPW = MT * 4 / LPC;  // channels per wave
+  static constexpr int DC = 4 * CPW;        // channels per workgroup
+  static constexpr int RP = 32 * KS;
+  static constexpr int CE = 16 / EB;
+  static constexpr int S = kLowrankBwdStep;  // tokens per pipeline step
+  static constexpr int XR = S + HALO;        // rows of a step's x / dy tile
+  static constexpr int ZP = RP + CE;         // z row pitch (elements)
+  static constexpr int XP = DC + CE;
+  static constexpr int GC = CPW * WP;        // padded filter columns of a wave
+  static constexpr int GP = GC + 4;          // g row pitch (8-byte rows, spread banks)
+  // two z buffers (one barrier per step) when they fit next to the rest
+  static constexpr int LDS_REST = 4 * XR * XP * EB + 4 * S * GP * EB;
+  static constexpr int ZB = (2 * S * ZP * EB + LDS_REST) <= 96 * 1024 ? 2 : 1;
+};
+
+template <typename ET, int W, int KS>
+struct LrBwdSmem {
+  using Sh = LrBwdShape<ET, W, KS>;
+  using RT = typename Sh::RT;
+  __align__(16) RT zl[Sh::ZB][Sh::S * Sh::ZP];
+  __align__(16) ET xl[2][Sh::XR * Sh::XP];
+  __align__(16) ET dyl[2][Sh::XR * Sh::XP];
+  __align__(16) RT gl[4][Sh::S * Sh::GP];
+};
+
+template <bool FAST, typename ET, int W, int KS>
+__device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSmem<ET, W, KS>& sm) {
+  using Sh = LrBwdShape<ET, W, KS>;
   using RT = typename Raw<ET>::type;
   using R_ = Raw<ET>;
-  constexpr int EB = int(sizeof(ET));
-  constexpr int MT = lowrank_bwd_mt(KS);
-  constexpr int WP = lowrank_rows_per_channel(W);  // padded taps per channel
-  constexpr int LPC = WP / 4;
-  constexpr int CPW = MT * 4 / LPC;  // channels per wave
-  constexpr int DC = 4 * CPW;        // channels per workgroup
-  constexpr int RP = 32 * KS;
-  constexpr int CE = 16 / EB;
-  constexpr int ZP = RP + CE;
-  constexpr int XP = DC + CE;
-  constexpr int GC = CPW * WP;       // padded filter columns of a wave
-  constexpr int GP = GC + 8 / EB;    // g row pitch
-  constexpr int RTN = RP / 16;       // r tiles of dU
-  constexpr int JTN = GC / 16;       // column tiles of dU
-  constexpr int ZCH = TT * RP / CE;
-  constexpr int XCH = TT * DC / CE;
-  constexpr int NCH = ZCH + 2 * XCH;
-  constexpr int CPT = (NCH + kBlockThreads - 1) / kBlockThreads;
-  static_assert(GC % 16 == 0, "whole column tiles per wave");
-  __shared__ __align__(16) RT zl[TT * ZP];
-  __shared__ __align__(16) ET xl[RING * XP];
-  __shared__ __align__(16) ET dyl[RING * XP];
-  __shared__ __align__(16) RT gl[4][TT * GP];
+  constexpr int EB = Sh::EB, MT = Sh::MT, WP = Sh::WP, LPC = Sh::LPC, CPW = Sh::CPW, DC = Sh::DC;
+  constexpr int RP = Sh::RP, CE = Sh::CE, S = Sh::S, XR = Sh::XR, ZP = Sh::ZP, XP = Sh::XP;
+  constexpr int GC = Sh::GC, GP = Sh::GP, ZB = Sh::ZB;
+  constexpr int NSUB = S / TT;
+  constexpr int RTN = RP / 16;        // r tiles of dU
+  constexpr int JTN = GC / 16;        // column tiles of dU
+  constexpr int ZCH = S * RP / CE;    // 16-byte chunks of a step's z rows
+  constexpr int XCH = S * DC / CE;    // ... of its x (and dy) rows
+  constexpr int ZS = (ZCH + kBlockThreads - 1) / kBlockThreads;
+  constexpr int XS = (XCH + kBlockThreads - 1) / kBlockThreads;
+  constexpr int HCH = HALO * DC / CE;  // chunks of the HALO rows of x (and dy)
+  static_assert(GC % 16 == 0 && S % 32 == 0 && 2 * HCH <= kBlockThreads && XR <= 2 * S, "tiling");
+  auto& zl = sm.zl;
+  auto& xl = sm.xl;
+  auto& dyl = sm.dyl;
+  auto& gl = sm.gl;
 
   const LrBlock blk = lr_block(p);
   const int tid = threadIdx.x;
@@ -647,17 +576,22 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankPara
   const int c_base = blk.cs * DC;
   const int t_first = blk.tr * p.Ltok;
   const int t_end = min(p.T, t_first + p.Ltok);
+  const int t_need = min(p.T, t_end + HALO);  // z and dy rows feed dx up to t_end + W - 2
   const int range = blk.b * p.nTr + blk.tr;
-  const ET* x = static_cast<const ET*>(p.x) + blk.b * p.xs0;
+  const ET* x = static_cast<const ET*>(p.x) + blk.b * p.xs0 + c_base;
   const ET* z = static_cast<const ET*>(p.z) + blk.b * p.zs0;
-  const ET* dy = static_cast<const ET*>(p.dy) + blk.b * p.dys0;
+  const ET* dy = static_cast<const ET*>(p.dy) + blk.b * p.dys0 + c_base;
   ET* dx = static_cast<ET*>(p.out) + blk.b * p.os0;
+  const ET* xsafe = static_cast<const ET*>(p.x);
+  const ET* zsafe = static_cast<const ET*>(p.z);
+  const ET* dysafe = static_cast<const ET*>(p.dy);
   const bool act16 = p.act16 != 0;
-  const bool z16 = p.z16 != 0;
+  const int xlimit = p.D - c_base;
   const int cw0 = c_base + wv * CPW;
   const int lane_c = (q / LPC) * MT;  // first channel of the lane's run, within the wave
   const int cl = cw0 + lane_c;
   const int cl_count = p.D - cl;
+  const int xcol = wv * CPW + lane_c;  // the lane's column in the x / dy tiles
 
   // regeneration operands, as in the forward
   typename Mfma<ET>::F32k afr[MT][KS];
@@ -689,59 +623,82 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankPara
     }
   }
 
-  // staging: z and dy rows of a tile up to T (dy/w of later tokens complete dx), x rows
-  // up to the end of the range
-  u32x4 pre[CPT];
-  auto prefetch = [&](int t0) {
+  // Loads of one step (tokens t0 .. t0 + S - 1): z rows below t_need, x rows below
+  // t_end, dy rows below t_need; zeros elsewhere. Each thread always stages the same
+  // (row, column) slots, so only the uniform base pointers move from step to step.
+  struct Stage {
+    u32x4 z[ZS], x[XS], d[XS];
+    uint32_t ok;  // bit i: z[i]; bit ZS + i: x[i]; bit ZS + XS + i: d[i]
+  };
+  static_assert(ZS + 2 * XS <= 32, "valid bits");
+  auto prefetch = [&](Stage& st, int t0) {
+    const ET* zb = z + int64_t(t0) * p.zs1;
+    const ET* xb = x + int64_t(t0) * p.xs1;
+    const ET* db_ = dy + int64_t(t0) * p.dys1;
+    uint32_t okm = 0;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < ZS; ++i) {
       const int ck = tid + i * kBlockThreads;
-      pre[i] = u32x4{0u, 0u, 0u, 0u};
-      if (ck < ZCH) {
-        const int row = ck / (RP / CE), c = (ck % (RP / CE)) * CE, t = t0 + row;
-        if (t < p.T) pre[i] = load_chunk<ET>(z + int64_t(t) * p.zs1, c, p.R, z16);
-      } else if (ck < ZCH + XCH) {
-        const int k2 = ck - ZCH;
-        const int row = k2 / (DC / CE), c = (k2 % (DC / CE)) * CE, t = t0 + row;
-        if (t < t_end) pre[i] = load_chunk<ET>(x + int64_t(t) * p.xs1 + c_base, c, p.D - c_base, act16);
-      } else if (ck < NCH) {
-        const int k2 = ck - ZCH - XCH;
-        const int row = k2 / (DC / CE), c = (k2 % (DC / CE)) * CE, t = t0 + row;
-        if (t < p.T) pre[i] = load_chunk<ET>(dy + int64_t(t) * p.dys1 + c_base, c, p.D - c_base, act16);
+      const int row = ck / (RP / CE), c = (ck % (RP / CE)) * CE;
+      const bool ok = ck < ZCH && t0 + row < t_need && c < p.R;
+      st.z[i] = stage16<FAST, ET>(zb, row * int(p.zs1) + c, ok, p.R - c, zsafe);
+      okm |= uint32_t(ok) << i;
+    }
+#pragma unroll
+    for (int i = 0; i < XS; ++i) {
+      const int ck = tid + i * kBlockThreads;
+      const int row = ck / (DC / CE), c = (ck % (DC / CE)) * CE;
+      const bool ok = ck < XCH && c < xlimit;
+      const bool okx = ok && t0 + row < t_end, okd = ok && t0 + row < t_need;
+      st.x[i] = stage16<FAST, ET>(xb, row * int(p.xs1) + c, okx, xlimit - c, xsafe);
+      st.d[i] = stage16<FAST, ET>(db_, row * int(p.dys1) + c, okd, xlimit - c, dysafe);
+      okm |= (uint32_t(okx) << (ZS + i)) | (uint32_t(okd) << (ZS + XS + i));
+    }
+    st.ok = okm;
+  };
+  // Writes a step's loads to x / dy buffer `buf` and z buffer `zbuf`; with `halo`, copies
+  // the HALO rows that precede the step from the last rows of the other x / dy buffer.
+  auto commit = [&](const Stage& st, int buf, int zbuf, bool halo) {
+#pragma unroll
+    for (int i = 0; i < ZS; ++i) {
+      const int ck = tid + i * kBlockThreads;
+      if (ck < ZCH)
+        *reinterpret_cast<u32x4*>(&zl[zbuf][(ck / (RP / CE)) * ZP + (ck % (RP / CE)) * CE]) = keep_if(st.z[i], st.ok, i);
+    }
+#pragma unroll
+    for (int i = 0; i < XS; ++i) {
+      const int ck = tid + i * kBlockThreads;
+      if (ck < XCH) {
+        const int o = (HALO + ck / (DC / CE)) * XP + (ck % (DC / CE)) * CE;
+        *reinterpret_cast<u32x4*>(&xl[buf][o]) = keep_if(st.x[i], st.ok, ZS + i);
+        *reinterpret_cast<u32x4*>(&dyl[buf][o]) = keep_if(st.d[i], st.ok, ZS + XS + i);
       }
     }
-  };
-  auto commit = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ck = tid + i * kBlockThreads;
-      if (ck < ZCH) {
-        *reinterpret_cast<u32x4*>(&zl[(ck / (RP / CE)) * ZP + (ck % (RP / CE)) * CE]) = pre[i];
-      } else if (ck < ZCH + XCH) {
-        const int k2 = ck - ZCH;
-        const int row = k2 / (DC / CE);
-        *reinterpret_cast<u32x4*>(&xl[ring_slot(t0 + row, t_first) * XP + (k2 % (DC / CE)) * CE]) = pre[i];
-      } else if (ck < NCH) {
-        const int k2 = ck - ZCH - XCH;
-        const int row = k2 / (DC / CE);
-        *reinterpret_cast<u32x4*>(&dyl[ring_slot(t0 + row, t_first) * XP + (k2 % (DC / CE)) * CE]) = pre[i];
-      }
+    if (halo && tid < 2 * HCH) {
+      const int k2 = tid % HCH;
+      const int o = (k2 / (DC / CE)) * XP + (k2 % (DC / CE)) * CE;
+      ET* dst = tid < HCH ? xl[buf] : dyl[buf];
+      const ET* src = tid < HCH ? xl[buf ^ 1] : dyl[buf ^ 1];
+      *reinterpret_cast<u32x4*>(dst + o) = *reinterpret_cast<const u32x4*>(src + o + S * XP);
     }
   };
 
-  // halo rows before the range: x (for g) and dy (rows of dx that other ranges store)
-  for (int ck = tid; ck < 2 * HALO * DC / CE; ck += kBlockThreads) {
-    const bool is_dy = ck >= HALO * DC / CE;
-    const int k2 = is_dy ? ck - HALO * DC / CE : ck;
+  // first tile: its HALO rows come from memory (zeros before t = 0)
+  if (tid < 2 * HCH) {
+    const int k2 = tid % HCH;
     const int row = k2 / (DC / CE), c = (k2 % (DC / CE)) * CE, t = t_first - HALO + row;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (t >= 0) v = load_chunk<ET>((is_dy ? dy + int64_t(t) * p.dys1 : x + int64_t(t) * p.xs1) + c_base, c,
-                                   p.D - c_base, act16);
-    *reinterpret_cast<u32x4*>(&(is_dy ? dyl : xl)[ring_slot(t, t_first) * XP + c]) = v;
+    const ET* src = tid < HCH ? x + int64_t(t) * p.xs1 : dy + int64_t(t) * p.dys1;
+    const bool ok = t >= 0 && c < xlimit;
+    *reinterpret_cast<u32x4*>(&(tid < HCH ? xl : dyl)[0][row * XP + c]) =
+        keep_if(stage16<FAST, ET>(src, c, ok, xlimit - c, tid < HCH ? xsafe : dysafe), uint32_t(ok), 0);
   }
-  prefetch(t_first);
-  commit(t_first);
+  Stage stA, stB;
+  prefetch(stA, t_first);
+  commit(stA, 0, 0, false);
   __syncthreads();
+  // prefetches are issued unconditionally (past the range every chunk reads as zero) so
+  // that the number of loads in flight, and with it each wait, is the same on every path
+  prefetch(stA, t_first + S);
 
   f32x4_t dU[RTN][JTN];
 #pragma unroll
@@ -758,115 +715,133 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankPara
     }
 
   RT* gw = gl[wv];
-  for (int t0 = t_first; t0 - (W - 1) < t_end; t0 += TT) {
-    const bool more = t0 + TT - (W - 1) < t_end;
-    if (more) prefetch(t0 + TT);
-    // regenerate the filters of tokens t0 .. t0 + 15
-    typename Mfma<ET>::F32k bfr[KS];
+  // one step: `cur` holds the loads of step t0 + S (in flight), `nxt` receives step t0 + 2S
+  auto step = [&](int t0, Stage& cur, Stage& nxt, const int buf) {
+    const int zbuf = ZB == 2 ? buf : 0;
+    const bool more = t0 + S - (W - 1) < t_end;
+    const bool do_g = t0 < t_end;
+    prefetch(nxt, t0 + 2 * S);
+    const ET* xt = &xl[buf][(HALO + n) * XP + xcol];   // x row of token t0 + n
+    const ET* dyt = &dyl[buf][(HALO + n) * XP + xcol];  // dy row of token t0 + n
+    ET* dxb = dx + int64_t(t0) * p.os1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (EB == 2) {
-        bfr[ks].v = *reinterpret_cast<const u16x8_t*>(&zl[n * ZP + 32 * ks + 8 * q]);
-      } else {
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int ts = t0 + sub * TT;
+      const bool do_dx = ts - (W - 1) < t_end;
+      if (!do_dx && !do_g) break;
+      const int t = ts + n;
+      float dyn[MT];
+      lds_read_run<ET, MT>(dyt + sub * TT * XP, dyn);
+      if (do_dx) {
+        // regenerate the filters of tokens ts .. ts + 15
+        typename Mfma<ET>::F32k bfr[KS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bfr[ks].v[e] = zl[n * ZP + 32 * ks + Mfma<ET>::k32(q, e)];
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (EB == 2) {
+            bfr[ks].v = *reinterpret_cast<const u16x8_t*>(&zl[zbuf][(sub * TT + n) * ZP + 32 * ks + 8 * q]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bfr[ks].v[e] = zl[zbuf][(sub * TT + n) * ZP + 32 * ks + Mfma<ET>::k32(q, e)];
+          }
+        }
+        float P[MT][4], dxs[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4_t a = binit[mt];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) a = Mfma<ET>::mma32(afr[mt][ks], bfr[ks], a);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) P[mt][i] = a[i] * dyn[mt];
+        }
+        // dx for token s = t - (W - 1)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          float acc;
+          if constexpr (LPC == 1) {
+            acc = shift_lanes<W - 1>(P[mt][0], Pprev[mt][0]);
+            if constexpr (W > 1) acc += shift_lanes<(W > 1 ? W - 2 : 0)>(P[mt][1], Pprev[mt][1]);
+            if constexpr (W > 2) acc += shift_lanes<(W > 2 ? W - 3 : 0)>(P[mt][2], Pprev[mt][2]);
+            if constexpr (W > 3) acc += shift_lanes<(W > 3 ? W - 4 : 0)>(P[mt][3], Pprev[mt][3]);
+          } else {
+            // even groups hold taps 0..3 (later by 4..1 tokens), odd groups tap 4 (same token)
+            const float even = shift_lanes<4>(P[mt][0], Pprev[mt][0]) + shift_lanes<3>(P[mt][1], Pprev[mt][1]) +
+                               shift_lanes<2>(P[mt][2], Pprev[mt][2]) + shift_lanes<1>(P[mt][3], Pprev[mt][3]);
+            const float mine = (q & 1) ? P[mt][0] : even;
+            acc = mine + __shfl_xor(mine, 16, 64);
+          }
+          dxs[mt] = acc;
+        }
+        const int s = t - (W - 1);
+        if ((q % LPC) == 0 && s >= t_first && s < t_end && cl_count > 0) {
+          float dys[MT];
+          lds_read_run<ET, MT>(dyt + (sub * TT - (W - 1)) * XP, dys);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) dxs[mt] += dys[mt];
+          global_store_run<ET, MT>(dxb + (sub * TT + n - (W - 1)) * int(p.os1) + cl, dxs, act16, cl_count);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Pprev[mt][i] = P[mt][i];
       }
-    }
-    float wv_[MT][4];
+      if (do_g) {
+        // g_k(t) = dy_t x_{t-k}, zero past the range; row t - t0 of the wave's g tile
+        // holds the lane's 4 taps of each of its MT channels
+        const bool tok_ok = t < t_end;
+        float g[MT][4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4_t a = binit[mt];
+        for (int i = 0; i < 4; ++i) {
+          const int tap = 4 * (q % LPC) + i;
+          // odd lane groups of a W = 5 filter hold tap 4 only: read a valid row (tap 0)
+          // for the others and zero the result
+          const int rtap = tap < W ? tap : 0;
+          float xr[MT] = {};
+          if (LPC == 2 || tap < W) lds_read_run<ET, MT>(xt + (sub * TT - rtap) * XP, xr);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) a = Mfma<ET>::mma32(afr[mt][ks], bfr[ks], a);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wv_[mt][i] = a[i];
-    }
-    const int t = t0 + n;
-    float dyn[MT];
-    lds_read_run<ET, MT>(&dyl[ring_slot(t, t_first) * XP + wv * CPW + lane_c], dyn);
-    // dx for token s = t - (W - 1)
-    float P[MT][4], dxs[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) P[mt][i] = wv_[mt][i] * dyn[mt];
-      float acc;
-      if constexpr (LPC == 1) {
-        acc = shift_lanes<W - 1>(P[mt][0], Pprev[mt][0]);
-        if constexpr (W > 1) acc += shift_lanes<(W > 1 ? W - 2 : 0)>(P[mt][1], Pprev[mt][1]);
-        if constexpr (W > 2) acc += shift_lanes<(W > 2 ? W - 3 : 0)>(P[mt][2], Pprev[mt][2]);
-        if constexpr (W > 3) acc += shift_lanes<(W > 3 ? W - 4 : 0)>(P[mt][3], Pprev[mt][3]);
-      } else {
-        // even groups hold taps 0..3 (later by 4..1 tokens), odd groups tap 4 (same token)
-        const float even = shift_lanes<4>(P[mt][0], Pprev[mt][0]) + shift_lanes<3>(P[mt][1], Pprev[mt][1]) +
-                           shift_lanes<2>(P[mt][2], Pprev[mt][2]) + shift_lanes<1>(P[mt][3], Pprev[mt][3]);
-        const float mine = (q & 1) ? P[mt][0] : even;
-        acc = mine + __shfl_xor(mine, 16, 64);
-      }
-      dxs[mt] = acc;
-    }
-    const int s = t - (W - 1);
-    if ((q % LPC) == 0 && s >= t_first && s < t_end && cl_count > 0) {
-      float dys[MT];
-      lds_read_run<ET, MT>(&dyl[ring_slot(s, t_first) * XP + wv * CPW + lane_c], dys);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) dxs[mt] += dys[mt];
-      global_store_run<ET, MT>(dx + int64_t(s) * p.os1 + cl, dxs, act16, cl_count);
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Pprev[mt][i] = P[mt][i];
-
-    if (t0 < t_end) {
-      // g_k(t) = dy_t x_{t-k}, zero past the range
-      const bool tok_ok = t < t_end;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tap = 4 * (q % LPC) + i;
-        float xr[MT];
-        if (tap < W) {
-          lds_read_run<ET, MT>(&xl[ring_slot(t - tap, t_first) * XP + wv * CPW + lane_c], xr);
-        } else {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) xr[mt] = 0.f;
+          for (int mt = 0; mt < MT; ++mt) {
+            g[mt][i] = (tok_ok && tap < W) ? dyn[mt] * xr[mt] : 0.f;
+            db[mt][i] += g[mt][i];
+          }
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const float g = (tok_ok && tap < W) ? dyn[mt] * xr[mt] : 0.f;
-          db[mt][i] += g;
-          P[mt][i] = g;  // reuse as the g tile of this lane
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        RT* dst = &gw[n * GP + (lane_c + mt) * WP + 4 * (q % LPC)];
-        if constexpr (EB == 2) {
-          *reinterpret_cast<u32x2*>(dst) =
-              u32x2{pack_bf16x2(P[mt][0], P[mt][1]), pack_bf16x2(P[mt][2], P[mt][3])};
-        } else {
-          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{P[mt][0], P[mt][1], P[mt][2], P[mt][3]};
-        }
-      }
-      wave_lds_sync();
-      // dU[r][col] += sum_n z_n[r] g_n[col] over the 16 tokens of the tile
-#pragma unroll
-      for (int rt = 0; rt < RTN; ++rt) {
-        typename Mfma<ET>::F16k afr16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) afr16.v[e] = zl[Mfma<ET>::k16(q, e) * ZP + rt * 16 + n];
-#pragma unroll
-        for (int jt = 0; jt < JTN; ++jt) {
-          typename Mfma<ET>::F16k bfr16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bfr16.v[e] = gw[Mfma<ET>::k16(q, e) * GP + jt * 16 + n];
-          dU[rt][jt] = Mfma<ET>::mma16(afr16, bfr16, dU[rt][jt]);
+          RT* dst = &gw[(sub * TT + n) * GP + (lane_c + mt) * WP + 4 * (q % LPC)];
+          if constexpr (EB == 2) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(g[mt][0], g[mt][1]), pack_bf16x2(g[mt][2], g[mt][3])};
+          } else {
+            *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{g[mt][0], g[mt][1], g[mt][2], g[mt][3]};
+          }
         }
       }
     }
+    if (do_g) {
+      wave_lds_sync();
+      // dU[r][col] += sum_t z_t[r] g_t[col] over the S tokens of the step (K = tokens;
+      // both operands are read down the columns of row-major tiles)
+#pragma unroll
+      for (int kk = 0; kk < S / 32; ++kk) {
+        typename Mfma<ET>::F32k gfr[JTN];
+#pragma unroll
+        for (int jt = 0; jt < JTN; ++jt) lds_colfrag<ET>(gfr[jt], gw, GP, 32 * kk, jt * 16);
+#pragma unroll
+        for (int rt = 0; rt < RTN; ++rt) {
+          typename Mfma<ET>::F32k zfr;
+          lds_colfrag<ET>(zfr, zl[zbuf], ZP, 32 * kk, rt * 16);
+#pragma unroll
+          for (int jt = 0; jt < JTN; ++jt) dU[rt][jt] = Mfma<ET>::mma32(zfr, gfr[jt], dU[rt][jt]);
+        }
+      }
+    }
+    // with two z buffers the other one was last read in the previous step, before the
+    // last barrier; with one, every wave must be done with it first
+    if constexpr (ZB == 1) __syncthreads();
+    if (more) commit(cur, buf ^ 1, ZB == 2 ? (buf ^ 1) : 0, true);
     __syncthreads();
-    if (more) commit(t0 + TT);
-    __syncthreads();
+  };
+  for (int t0 = t_first; t0 - (W - 1) < t_end; t0 += 2 * S) {
+    step(t0, stA, stB, 0);
+    if (!(t0 + S - (W - 1) < t_end)) break;
+    step(t0 + S, stB, stA, 1);
   }
 
   // db partial: sum over the 16 token lanes of each row, written by lane n == 0
@@ -901,36 +876,75 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankPara
     }
 }
 
+template <typename ET, int W, int KS>
+__global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankParams p) {
+  using Sh = LrBwdShape<ET, W, KS>;
+  __shared__ LrBwdSmem<ET, W, KS> sm;
+  const int c_base = lr_block(p).cs * Sh::DC;
+  // 16-byte loads throughout when every row and chunk of this workgroup allows them
+  const bool fast = p.act16 != 0 && p.z16 != 0 && p.R % Sh::CE == 0 && c_base + Sh::DC <= p.D;
+  if (fast) {
+    lowrank_bwd_body<true, ET, W, KS>(p, sm);
+  } else {
+    lowrank_bwd_body<false, ET, W, KS>(p, sm);
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // dz[t][r] = sum_j g_t[j] U[r][j], with g recomputed from x and dy.
-// A workgroup owns kLowrankDzTokens tokens of one sequence (each wave two 16-token
-// tiles) and walks the channels in chunks of CH: the chunk's U columns are staged in LDS
-// (padded to WP taps per channel); x (with its 4-token halo) and dy rows of the chunk
-// are staged in LDS too. Matrix cores: M = r, N = tokens, K = padded filter columns.
-// Lane (token n, group q) supplies g for a run of CH/4 (W <= 4) or CH/8 channels.
+// A workgroup owns kLowrankDzTokens tokens of one sequence (16 per wave) and walks the
+// channels in chunks of CH = 32: the chunk's U columns (all ranks), the x rows (with the
+// HALO tokens before) and the dy rows are staged in LDS, double-buffered when they fit,
+// with the loads of the next two chunks in flight.
+// Matrix cores: M = r, N = tokens, K = filter columns. Lane group q supplies g for the
+// run of CR = 8 channels q*CR .. (all W taps, CR*W consecutive columns j), so the
+// K step ks of group q covers columns q*CR*W + 8 ks .. + 7: the same map indexes the U
+// rows in LDS, and the channel / tap of each element is a compile-time constant.
 // ---------------------------------------------------------------------------------
 template <typename ET, int W, int KS>
-__global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParams p) {
+struct LrDzShape {
   using RT = typename Raw<ET>::type;
-  using R_ = Raw<ET>;
-  constexpr int EB = int(sizeof(ET));
-  constexpr int RP = 32 * KS;
+  static constexpr int EB = int(sizeof(ET));
+  static constexpr int RP = 32 * KS;
+  static constexpr int CH = kLowrankDzChunk;
+  static constexpr int UC = CH * W;          // columns of a chunk
+  static constexpr int CE = 16 / EB;
+  static constexpr int UP = UC + CE;         // U row pitch (elements)
+  static constexpr int TB = kLowrankDzTokens;
+  static constexpr int XR = TB + HALO;
+  static constexpr int XP = CH + CE;
+  static constexpr int STAGE = (RP * UP + XR * XP + TB * XP) * EB;
+  static constexpr int NBUF = 2 * STAGE <= 80 * 1024 ? 2 : 1;
+};
+
+template <typename ET, int W, int KS>
+struct LrDzSmem {
+  using Sh = LrDzShape<ET, W, KS>;
+  __align__(16) typename Sh::RT Ul[Sh::NBUF][Sh::RP * Sh::UP];
+  __align__(16) ET xl[Sh::NBUF][Sh::XR * Sh::XP];
+  __align__(16) ET dyl[Sh::NBUF][Sh::TB * Sh::XP];
+};
+
+template <bool FAST, typename ET, int W, int KS>
+__device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem<ET, W, KS>& sm) {
+  using Sh = LrDzShape<ET, W, KS>;
+  using RT = typename Raw<ET>::type;
+  constexpr int EB = Sh::EB, RP = Sh::RP, CH = Sh::CH, UC = Sh::UC, CE = Sh::CE, UP = Sh::UP;
+  constexpr int TB = Sh::TB, XR = Sh::XR, XP = Sh::XP, NBUF = Sh::NBUF;
   constexpr int RTN = RP / 16;
-  constexpr int CH = lowrank_dz_chunk(KS, EB, W);
-  constexpr int WP = lowrank_rows_per_channel(W);
-  constexpr int CPK = 8 / WP * 1;            // channels per lane per K step (2 or 1)
-  constexpr int CR = CH / 4;                 // channels of a lane group's run
-  constexpr int KSTEPS = CR / CPK;           // K steps per chunk
-  constexpr int UC = CH * WP;                // padded columns of a chunk
-  constexpr int UP = UC + 8;                 // U row pitch (elements)
-  constexpr int TB = kLowrankDzTokens;
-  constexpr int CE = 16 / EB;
-  constexpr int XP = CH + CE;
-  constexpr int TPW = TB / 64;               // 16-token tiles per wave
-  static_assert(CR % CPK == 0 && TB % 64 == 0, "dz tiling");
-  __shared__ __align__(16) RT Ul[RP * UP];
-  __shared__ __align__(16) ET xl[(TB + HALO) * XP];
-  __shared__ __align__(16) ET dyl[TB * XP];
+  constexpr int CR = CH / 4;          // channels of a lane group
+  constexpr int RUN = CR * W;         // columns of a lane group
+  constexpr int KST = RUN / 8;        // K steps per chunk
+  constexpr int UCH = RP * UC / CE;   // 16-byte chunks of U per stage
+  constexpr int XCH = XR * CH / CE;
+  constexpr int DCH = TB * CH / CE;
+  constexpr int US = (UCH + kBlockThreads - 1) / kBlockThreads;
+  constexpr int AS = (XCH + DCH + kBlockThreads - 1) / kBlockThreads;  // x and dy slots
+  constexpr int ND = CR * EB / 4;     // 32-bit words of a lane's run of one row
+  static_assert(RUN % 8 == 0 && UC % CE == 0 && TB == 64, "dz tiling");
+  auto& Ul = sm.Ul;
+  auto& xl = sm.xl;
+  auto& dyl = sm.dyl;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -941,88 +955,158 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParam
   const int nblk = (p.T + TB - 1) / TB;
   const int b = lb / nblk;
   const int tb0 = (lb % nblk) * TB;
-  const ET* x = static_cast<const ET*>(p.x) + b * p.xs0;
-  const ET* dy = static_cast<const ET*>(p.dy) + b * p.dys0;
+  // x rows from tb0 - HALO, dy rows from tb0 (row offsets below stay small)
+  const ET* x = static_cast<const ET*>(p.x) + b * p.xs0 + int64_t(tb0 - HALO) * p.xs1;
+  const ET* dy = static_cast<const ET*>(p.dy) + b * p.dys0 + int64_t(tb0) * p.dys1;
   const ET* U = static_cast<const ET*>(p.U);
-  const bool act16 = p.act16 != 0;
+  const ET* xsafe = static_cast<const ET*>(p.x);
+  const ET* dysafe = static_cast<const ET*>(p.dy);
+  const int nchunk = (p.D + CH - 1) / CH;
 
-  f32x4_t acc[TPW][RTN];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i)
-#pragma unroll
-    for (int j = 0; j < RTN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = 0; c0 < p.D; c0 += CH) {
+  struct Stage {
+    u32x4 u[US], a[AS];
+    uint32_t ok;  // bit i: u[i]; bit US + i: a[i]
+  };
+  static_assert(US + AS <= 32, "valid bits");
+  auto prefetch = [&](Stage& st, int c0) {
     const int climit = p.D - c0;
-    // stage U columns of channels c0 .. c0 + CH - 1, padded to WP taps, ranks to RP
-    for (int idx = tid; idx < RP * CH; idx += kBlockThreads) {
-      const int r = idx / CH, cc = idx % CH;
-      RT v[WP];
+    const int jlimit = p.J - c0 * W;
+    const ET* ub = U + int64_t(c0) * W;
+    uint32_t okm = 0;
 #pragma unroll
-      for (int k = 0; k < WP; ++k)
-        v[k] = (r < p.R && cc < climit && k < W) ? R_::from_mem(U, int64_t(r) * p.ldu + int64_t(c0 + cc) * W + k)
-                                                 : R_::zero();
-#pragma unroll
-      for (int k = 0; k < WP; ++k) Ul[r * UP + cc * WP + k] = v[k];
+    for (int i = 0; i < US; ++i) {
+      const int ck = tid + i * kBlockThreads;
+      const int r = ck / (UC / CE), c = (ck % (UC / CE)) * CE;
+      const bool ok = ck < UCH && r < p.R && c < jlimit;
+      st.u[i] = stage16<FAST, ET>(ub, r * int(p.ldu) + c, ok, jlimit - c, U);
+      okm |= uint32_t(ok) << i;
     }
-    // stage x rows tb0 - HALO .. tb0 + TB - 1 and dy rows tb0 .. tb0 + TB - 1 of the chunk
-    for (int ck = tid; ck < (2 * TB + HALO) * (CH / CE); ck += kBlockThreads) {
-      const int row = ck / (CH / CE), c = (ck % (CH / CE)) * CE;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < TB + HALO) {
-        const int t = tb0 - HALO + row;
-        if (t >= 0 && t < p.T) v = load_chunk<ET>(x + int64_t(t) * p.xs1 + c0, c, climit, act16);
-        *reinterpret_cast<u32x4*>(&xl[row * XP + c]) = v;
-      } else {
-        const int r2 = row - TB - HALO;
-        const int t = tb0 + r2;
-        if (t < p.T) v = load_chunk<ET>(dy + int64_t(t) * p.dys1 + c0, c, climit, act16);
-        *reinterpret_cast<u32x4*>(&dyl[r2 * XP + c]) = v;
+#pragma unroll
+    for (int i = 0; i < AS; ++i) {
+      const int ck = tid + i * kBlockThreads;
+      // x rows tb0 - HALO .. (ck < XCH), then dy rows tb0 ..
+      const bool isx = ck < XCH;
+      const int k2 = isx ? ck : ck - XCH;
+      const int row = k2 / (CH / CE), c = (k2 % (CH / CE)) * CE;
+      const int t = isx ? tb0 - HALO + row : tb0 + row;
+      const bool ok = (isx || k2 < DCH) && t >= 0 && t < p.T && c < climit;
+      st.a[i] = stage16<FAST, ET>(isx ? x + c0 : dy + c0, row * int(isx ? p.xs1 : p.dys1) + c, ok, climit - c,
+                                  isx ? xsafe : dysafe);
+      okm |= uint32_t(ok) << (US + i);
+    }
+    st.ok = okm;
+  };
+  auto commit = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < US; ++i) {
+      const int ck = tid + i * kBlockThreads;
+      if (ck < UCH)
+        *reinterpret_cast<u32x4*>(&Ul[buf][(ck / (UC / CE)) * UP + (ck % (UC / CE)) * CE]) = keep_if(st.u[i], st.ok, i);
+    }
+#pragma unroll
+    for (int i = 0; i < AS; ++i) {
+      const int ck = tid + i * kBlockThreads;
+      const u32x4 v = keep_if(st.a[i], st.ok, US + i);
+      if (ck < XCH) {
+        *reinterpret_cast<u32x4*>(&xl[buf][(ck / (CH / CE)) * XP + (ck % (CH / CE)) * CE]) = v;
+      } else if (ck - XCH < DCH) {
+        const int k2 = ck - XCH;
+        *reinterpret_cast<u32x4*>(&dyl[buf][(k2 / (CH / CE)) * XP + (k2 % (CH / CE)) * CE]) = v;
       }
     }
-    __syncthreads();
+  };
+
+  f32x4_t acc[RTN];
 #pragma unroll
-    for (int tile = 0; tile < TPW; ++tile) {
-      const int nt = (wv * TPW + tile) * 16 + n;  // token within the block
-      // the lane's dy and x rows for its channel run
-      float dyr[CR], xr[W][CR];
-      lds_read_run<ET, CR>(&dyl[nt * XP + q * CR], dyr);
+  for (int j = 0; j < RTN; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Stage stA, stB;
+  prefetch(stA, 0);
+  commit(stA, 0);
+  __syncthreads();
+  // prefetches are issued unconditionally (past the last chunk every chunk reads as
+  // zero) so that the number of loads in flight, and with it each wait, is the same on
+  // every path
+  prefetch(stA, CH);
+  const int nt = wv * TT + n;  // the lane's token within the block
+  // chunk ci: `cur` holds chunk ci + 1 (in flight), `nxt` receives chunk ci + 2
+  auto chunk = [&](int ci, Stage& cur, Stage& nxt) {
+    const int buf = NBUF == 2 ? (ci & 1) : 0;
+    const bool more = ci + 1 < nchunk;
+    prefetch(nxt, (ci + 2) * CH);
+    // the lane's dy row and x rows (taps 0 .. W-1) for its run of CR channels, as words
+    uint32_t dw_[ND], xw[W][ND];
+    {
+      const uint32_t* d = reinterpret_cast<const uint32_t*>(&dyl[buf][nt * XP + q * CR]);
 #pragma unroll
-      for (int k = 0; k < W; ++k) lds_read_run<ET, CR>(&xl[(nt + HALO - k) * XP + q * CR], xr[k]);
+      for (int i = 0; i < ND; i += 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(d + i);
+        dw_[i] = v[0]; dw_[i + 1] = v[1]; dw_[i + 2] = v[2]; dw_[i + 3] = v[3];
+      }
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        typename Mfma<ET>::F32k bfr;
+      for (int k = 0; k < W; ++k) {
+        const uint32_t* xs = reinterpret_cast<const uint32_t*>(&xl[buf][(nt + HALO - k) * XP + q * CR]);
+#pragma unroll
+        for (int i = 0; i < ND; i += 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xs + i);
+          xw[k][i] = v[0]; xw[k][i + 1] = v[1]; xw[k][i + 2] = v[2]; xw[k][i + 3] = v[3];
+        }
+      }
+    }
+    auto elem = [&](const uint32_t* w, int c) -> float {
+      if constexpr (EB == 2) {
+        return (c & 1) ? bf16_hi(w[c >> 1]) : bf16_lo(w[c >> 1]);
+      } else {
+        return __uint_as_float(w[c]);
+      }
+    };
+    float dyf[CR];
+#pragma unroll
+    for (int c = 0; c < CR; ++c) dyf[c] = elem(dw_, c);
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      typename Mfma<ET>::F32k bfr;
+      if constexpr (EB == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int c0_ = (8 * ks + e) / W, k0_ = (8 * ks + e) % W;
+          const int c1_ = (8 * ks + e + 1) / W, k1_ = (8 * ks + e + 1) % W;
+          const uint32_t w2 = pack_bf16x2(dyf[c0_] * elem(xw[k0_], c0_), dyf[c1_] * elem(xw[k1_], c1_));
+          bfr.v[e] = uint16_t(w2 & 0xffffu);
+          bfr.v[e + 1] = uint16_t(w2 >> 16);
+        }
+      } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          // slot e of lane group q <-> column (channel q*CR + ks*CPK + e / WP, tap e % WP);
-          // A below uses the same slot -> column map, which is all the contraction needs
-          const int cr = ks * CPK + e / WP;  // channel within the run
-          const int tap = e % WP;
-          const float g = tap < W ? dyr[cr] * xr[tap < W ? tap : 0][cr] : 0.f;
-          bfr.v[e] = R_::from_float(g);
-        }
-#pragma unroll
-        for (int rt = 0; rt < RTN; ++rt) {
-          typename Mfma<ET>::F32k afr;
-          const RT* src = &Ul[(rt * 16 + n) * UP + (q * CR + ks * CPK) * WP];
-          if constexpr (EB == 2) {
-            afr.v = *reinterpret_cast<const u16x8_t*>(src);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) afr.v[e] = src[e];
-          }
-          acc[tile][rt] = Mfma<ET>::mma32(afr, bfr, acc[tile][rt]);
+          const int c_ = (8 * ks + e) / W, k_ = (8 * ks + e) % W;
+          bfr.v[e] = dyf[c_] * elem(xw[k_], c_);
         }
       }
-    }
-    __syncthreads();
-  }
-  // lane holds dz[token n][r = rt*16 + 4q + ii] of each tile
-  ET* dz = static_cast<ET*>(p.dz) + b * p.dzs0;
 #pragma unroll
-  for (int tile = 0; tile < TPW; ++tile) {
-    const int t = tb0 + (wv * TPW + tile) * 16 + n;
-    if (t >= p.T) continue;
+      for (int rt = 0; rt < RTN; ++rt) {
+        typename Mfma<ET>::F32k afr;
+        const RT* src = &Ul[buf][(rt * 16 + n) * UP + q * RUN + 8 * ks];
+        if constexpr (EB == 2) {
+          afr.v = *reinterpret_cast<const u16x8_t*>(src);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) afr.v[e] = src[e];
+        }
+        acc[rt] = Mfma<ET>::mma32(afr, bfr, acc[rt]);
+      }
+    }
+    if constexpr (NBUF == 1) __syncthreads();
+    if (more) commit(cur, NBUF == 2 ? (buf ^ 1) : 0);
+    __syncthreads();
+  };
+  for (int ci = 0; ci < nchunk; ci += 2) {
+    chunk(ci, stA, stB);
+    if (ci + 1 < nchunk) chunk(ci + 1, stB, stA);
+  }
+  // lane holds dz[token n][r = rt*16 + 4q + ii]
+  ET* dz = static_cast<ET*>(p.dz) + b * p.dzs0;
+  const int t = tb0 + nt;
+  if (t < p.T) {
 #pragma unroll
     for (int rt = 0; rt < RTN; ++rt)
 #pragma unroll
@@ -1031,12 +1115,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParam
         if (r < p.R) {
           const int64_t o = int64_t(t) * p.dzs1 + r;
           if constexpr (EB == 2) {
-            reinterpret_cast<uint16_t*>(dz)[o] = to_bf16_bits(acc[tile][rt][ii]);
+            reinterpret_cast<uint16_t*>(dz)[o] = to_bf16_bits(acc[rt][ii]);
           } else {
-            dz[o] = acc[tile][rt][ii];
+            dz[o] = acc[rt][ii];
           }
         }
       }
+  }
+}
+
+template <typename ET, int W, int KS>
+__global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParams p) {
+  using Sh = LrDzShape<ET, W, KS>;
+  __shared__ LrDzSmem<ET, W, KS> sm;
+  // 16-byte loads throughout when every chunk of every row allows them
+  const bool fast = p.act16 != 0 && p.u16 != 0 && p.D % Sh::CH == 0;
+  if (fast) {
+    lowrank_dz_body<true, ET, W, KS>(p, sm);
+  } else {
+    lowrank_dz_body<false, ET, W, KS>(p, sm);
   }
 }
 
@@ -1097,7 +1194,8 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
   if (per_seq > max_ranges) per_seq = max_ranges;
   if (per_seq < 1) per_seq = 1;
   int64_t L = (T + per_seq - 1) / per_seq;
-  L = (L + TT - 1) / TT * TT;
+  const int64_t step = bwd ? kLowrankBwdStep : TT;
+  L = (L + step - 1) / step * step;
   pl.Ltok = int(L);
   pl.nTr = int((T + L - 1) / L);
   pl.blocks = B * int64_t(pl.nTr) * pl.nCs;
@@ -1105,8 +1203,7 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
   const int64_t nR = B * int64_t(pl.nTr);
   pl.ws_dU = 0;
   pl.ws_db = size_t(nR) * size_t(R) * size_t(J) * sizeof(float);
-  pl.ws_dz = pl.ws_db + size_t(nR) * size_t(J) * sizeof(float);
-  pl.ws_total = bwd ? pl.ws_dz : 0;
+  pl.ws_total = bwd ? pl.ws_db + size_t(nR) * size_t(J) * sizeof(float) : 0;
   (void)H;
   return pl;
 }
