@@ -82,6 +82,8 @@ struct LowRankParams {
   int64_t dzs0, dzs1;
   int32_t B, T, D, H, G, R, J;
   int32_t nCs;     // channel slices
+  int32_t cs0, nCsL;   // channel slices of one launch: cs0 .. cs0 + nCsL - 1
+  int32_t tbb0, nTbL;  // dz token blocks of one launch (per sequence): tbb0 .. + nTbL - 1
   int32_t Ltok;    // tokens per token range
   int32_t nTr;     // token ranges per sequence
   int32_t act16;   // every activation-shaped tensor allows 16-byte vectors

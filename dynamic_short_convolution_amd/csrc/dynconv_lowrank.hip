@@ -113,15 +113,16 @@ struct Mfma<float> {
 };
 
 // Block -> (sequence b, token range tr, channel slice cs), channel slice fastest, so the
-// workgroups that share a z tile run on the same XCD at about the same time.
+// workgroups that share a z tile run on the same XCD at about the same time. A launch
+// covers the channel slices cs0 .. cs0 + nCsL - 1.
 struct LrBlock {
   int b, tr, cs;
 };
 __device__ __forceinline__ LrBlock lr_block(const LowRankParams& p) {
   uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   LrBlock r;
-  r.cs = lb % p.nCs;
-  lb /= p.nCs;
+  r.cs = p.cs0 + int(lb % uint32_t(p.nCsL));
+  lb /= uint32_t(p.nCsL);
   r.tr = lb % p.nTr;
   r.b = lb / p.nTr;
   return r;
@@ -149,6 +150,34 @@ __device__ __forceinline__ u32x4 load_chunk(const ET* row, int c, int limit, boo
       } else {
         r[e] = __float_as_uint(reinterpret_cast<const float*>(row)[c + e]);
       }
+    }
+  }
+  return r;
+}
+
+// The first `limit` (>= 1) of the 16 bytes at row[0 ..] by element loads, all issued
+// before any is used (indices clamped into the row, the tail masked afterwards).
+template <typename ET>
+__device__ __forceinline__ u32x4 load_elems16(const ET* row, int limit) {
+  constexpr int E = 16 / int(sizeof(ET));
+  u32x4 r = {0u, 0u, 0u, 0u};
+  uint32_t h[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = min(e, limit - 1);
+    if constexpr (sizeof(ET) == 2) {
+      h[e] = reinterpret_cast<const uint16_t*>(row)[i];
+    } else {
+      h[e] = __float_as_uint(reinterpret_cast<const float*>(row)[i]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t v = e < limit ? h[e] : 0u;
+    if constexpr (sizeof(ET) == 2) {
+      r[e / 2] |= (e & 1) ? (v << 16) : v;
+    } else {
+      r[e] = v;
     }
   }
   return r;
@@ -470,7 +499,7 @@ __device__ __forceinline__ u32x4 stage16(const ET* base, int off, bool ok, int l
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
   } else {
     u32x4 r = {0u, 0u, 0u, 0u};
-    if (ok) r = load_chunk<ET>(base + off, 0, limit, false);
+    if (ok) r = load_elems16<ET>(base + off, limit);
     return r;
   }
 }
@@ -629,12 +658,32 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
   struct Stage {
     u32x4 z[ZS], x[XS], d[XS];
     uint32_t ok;  // bit i: z[i]; bit ZS + i: x[i]; bit ZS + XS + i: d[i]
+    bool full;    // every row of the step lies in the range: no masks
   };
   static_assert(ZS + 2 * XS <= 32, "valid bits");
   auto prefetch = [&](Stage& st, int t0) {
     const ET* zb = z + int64_t(t0) * p.zs1;
     const ET* xb = x + int64_t(t0) * p.xs1;
     const ET* db_ = dy + int64_t(t0) * p.dys1;
+    st.full = FAST && t0 + S <= t_end;
+    if (FAST && t0 + S <= t_end) {
+      // same loads as below with every chunk valid (z chunks are whole: R % 32 == 0)
+#pragma unroll
+      for (int i = 0; i < ZS; ++i) {
+        const int ck = tid + i * kBlockThreads;
+        st.z[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(zb + (ck / (RP / CE)) * int(p.zs1) + (ck % (RP / CE)) * CE));
+      }
+#pragma unroll
+      for (int i = 0; i < XS; ++i) {
+        const int ck = tid + i * kBlockThreads;
+        const int row = ck / (DC / CE), c = (ck % (DC / CE)) * CE;
+        st.x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb + row * int(p.xs1) + c));
+        st.d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(db_ + row * int(p.dys1) + c));
+      }
+      st.ok = ~0u;
+      return;
+    }
     uint32_t okm = 0;
 #pragma unroll
     for (int i = 0; i < ZS; ++i) {
@@ -659,20 +708,28 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
   // Writes a step's loads to x / dy buffer `buf` and z buffer `zbuf`; with `halo`, copies
   // the HALO rows that precede the step from the last rows of the other x / dy buffer.
   auto commit = [&](const Stage& st, int buf, int zbuf, bool halo) {
+    const uint32_t okm = st.full ? ~0u : st.ok;  // uniform choice: folded for full steps
+    auto put = [&](const uint32_t mask) {
 #pragma unroll
-    for (int i = 0; i < ZS; ++i) {
-      const int ck = tid + i * kBlockThreads;
-      if (ck < ZCH)
-        *reinterpret_cast<u32x4*>(&zl[zbuf][(ck / (RP / CE)) * ZP + (ck % (RP / CE)) * CE]) = keep_if(st.z[i], st.ok, i);
-    }
-#pragma unroll
-    for (int i = 0; i < XS; ++i) {
-      const int ck = tid + i * kBlockThreads;
-      if (ck < XCH) {
-        const int o = (HALO + ck / (DC / CE)) * XP + (ck % (DC / CE)) * CE;
-        *reinterpret_cast<u32x4*>(&xl[buf][o]) = keep_if(st.x[i], st.ok, ZS + i);
-        *reinterpret_cast<u32x4*>(&dyl[buf][o]) = keep_if(st.d[i], st.ok, ZS + XS + i);
+      for (int i = 0; i < ZS; ++i) {
+        const int ck = tid + i * kBlockThreads;
+        if (ck < ZCH)
+          *reinterpret_cast<u32x4*>(&zl[zbuf][(ck / (RP / CE)) * ZP + (ck % (RP / CE)) * CE]) = keep_if(st.z[i], mask, i);
       }
+#pragma unroll
+      for (int i = 0; i < XS; ++i) {
+        const int ck = tid + i * kBlockThreads;
+        if (ck < XCH) {
+          const int o = (HALO + ck / (DC / CE)) * XP + (ck % (DC / CE)) * CE;
+          *reinterpret_cast<u32x4*>(&xl[buf][o]) = keep_if(st.x[i], mask, ZS + i);
+          *reinterpret_cast<u32x4*>(&dyl[buf][o]) = keep_if(st.d[i], mask, ZS + XS + i);
+        }
+      }
+    };
+    if (st.full) {
+      put(~0u);
+    } else {
+      put(okm);
     }
     if (halo && tid < 2 * HCH) {
       const int k2 = tid % HCH;
@@ -787,7 +844,11 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
       if (do_g) {
         // g_k(t) = dy_t x_{t-k}, zero past the range; row t - t0 of the wave's g tile
         // holds the lane's 4 taps of each of its MT channels
-        const bool tok_ok = t < t_end;
+        // tokens of a step that ends inside the range need no mask
+        const bool tok_ok = t0 + S <= t_end || t < t_end;
+        float dyg[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) dyg[mt] = tok_ok ? dyn[mt] : 0.f;
         float g[MT][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -799,7 +860,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
           if (LPC == 2 || tap < W) lds_read_run<ET, MT>(xt + (sub * TT - rtap) * XP, xr);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            g[mt][i] = (tok_ok && tap < W) ? dyn[mt] * xr[mt] : 0.f;
+            g[mt][i] = tap < W ? dyg[mt] * xr[mt] : 0.f;
             db[mt][i] += g[mt][i];
           }
         }
@@ -876,18 +937,12 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
     }
 }
 
-template <typename ET, int W, int KS>
+// FAST: 16-byte loads throughout (the launch covers channel slices that lie inside D,
+// with aligned rows and R % 32 == 0); otherwise element loads where a chunk is partial.
+template <typename ET, int W, int KS, bool FAST>
 __global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankParams p) {
-  using Sh = LrBwdShape<ET, W, KS>;
   __shared__ LrBwdSmem<ET, W, KS> sm;
-  const int c_base = lr_block(p).cs * Sh::DC;
-  // 16-byte loads throughout when every row and chunk of this workgroup allows them
-  const bool fast = p.act16 != 0 && p.z16 != 0 && p.R % Sh::CE == 0 && c_base + Sh::DC <= p.D;
-  if (fast) {
-    lowrank_bwd_body<true, ET, W, KS>(p, sm);
-  } else {
-    lowrank_bwd_body<false, ET, W, KS>(p, sm);
-  }
+  lowrank_bwd_body<FAST, ET, W, KS>(p, sm);
 }
 
 // ---------------------------------------------------------------------------------
@@ -925,7 +980,7 @@ struct LrDzSmem {
   __align__(16) ET dyl[Sh::NBUF][Sh::TB * Sh::XP];
 };
 
-template <bool FAST, typename ET, int W, int KS>
+template <typename ET, int W, int KS>
 __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem<ET, W, KS>& sm) {
   using Sh = LrDzShape<ET, W, KS>;
   using RT = typename Raw<ET>::type;
@@ -952,9 +1007,8 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
   const int n = lane & 15;
   const int wv = tid >> 6;
   const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int nblk = (p.T + TB - 1) / TB;
-  const int b = lb / nblk;
-  const int tb0 = (lb % nblk) * TB;
+  const int b = int(lb / uint32_t(p.nTbL));
+  const int tb0 = (p.tbb0 + int(lb % uint32_t(p.nTbL))) * TB;
   // x rows from tb0 - HALO, dy rows from tb0 (row offsets below stay small)
   const ET* x = static_cast<const ET*>(p.x) + b * p.xs0 + int64_t(tb0 - HALO) * p.xs1;
   const ET* dy = static_cast<const ET*>(p.dy) + b * p.dys0 + int64_t(tb0) * p.dys1;
@@ -978,7 +1032,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
       const int ck = tid + i * kBlockThreads;
       const int r = ck / (UC / CE), c = (ck % (UC / CE)) * CE;
       const bool ok = ck < UCH && r < p.R && c < jlimit;
-      st.u[i] = stage16<FAST, ET>(ub, r * int(p.ldu) + c, ok, jlimit - c, U);
+      st.u[i] = stage16<false, ET>(ub, r * int(p.ldu) + c, ok, jlimit - c, U);
       okm |= uint32_t(ok) << i;
     }
 #pragma unroll
@@ -990,7 +1044,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
       const int row = k2 / (CH / CE), c = (k2 % (CH / CE)) * CE;
       const int t = isx ? tb0 - HALO + row : tb0 + row;
       const bool ok = (isx || k2 < DCH) && t >= 0 && t < p.T && c < climit;
-      st.a[i] = stage16<FAST, ET>(isx ? x + c0 : dy + c0, row * int(isx ? p.xs1 : p.dys1) + c, ok, climit - c,
+      st.a[i] = stage16<false, ET>(isx ? x + c0 : dy + c0, row * int(isx ? p.xs1 : p.dys1) + c, ok, climit - c,
                                   isx ? xsafe : dysafe);
       okm |= uint32_t(ok) << (US + i);
     }
@@ -1124,16 +1178,208 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
   }
 }
 
+// ---------------------------------------------------------------------------------
+// dz, bf16 interior blocks: the same computation as lowrank_dz_body, staged by LDS DMA
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base + 16 *
+// lane, no registers involved) into a ring of NST stages, two chunks ahead of the one
+// being computed. Each wave waits for its own transfers (vmcnt) and a barrier publishes
+// the stage; nothing else needs the loads, so no other wait is tied to them.
+// LDS rows are rotated by chunk so that the 16 lanes of a group that read the same
+// logical chunk of 16 different rows hit distinct banks:
+//   U row r (UCPR chunks): logical chunk c sits at (c + r % 16) % UCPR;
+//   x / dy row (4 chunks): logical chunk c sits at (c + row / 4) % 4.
+// ---------------------------------------------------------------------------------
+template <int W, int KS>
+struct LrDzDma {
+  static constexpr int RP = 32 * KS;
+  static constexpr int CH = kLowrankDzChunk;
+  static constexpr int UC = CH * W;            // filter columns of a chunk
+  static constexpr int UCPR = UC / 8;          // 16-byte chunks of a U row
+  static constexpr int TB = kLowrankDzTokens;
+  static constexpr int XR = TB + HALO;
+  static constexpr int XCPR = CH / 8;          // 16-byte chunks of an x / dy row
+  static constexpr int UCH = RP * UCPR, XCH = XR * XCPR, DCH = TB * XCPR;
+  static constexpr int NI_U = (UCH + 63) / 64, NI_X = (XCH + 63) / 64, NI_D = (DCH + 63) / 64;
+  static constexpr int NI = NI_U + NI_X + NI_D;  // wave-wide transfers per stage
+  static constexpr int X_OFF = NI_U * 64 * 16;   // byte offsets inside a stage
+  static constexpr int D_OFF = X_OFF + NI_X * 64 * 16;
+  static constexpr int STAGE = D_OFF + NI_D * 64 * 16;
+  static constexpr int NST = 3;
+  static constexpr int BYTES = NST * STAGE;
+  static_assert(XCPR == 4 && UC % 8 == 0, "dz DMA tiling");
+};
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+// Waits until at most N of this wave's vector memory operations are outstanding, then
+// joins the workgroup barrier; the memory clobber keeps LDS accesses on their side.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int W, int KS>
+__device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned char* smem, int b, int tb0) {
+  using D = LrDzDma<W, KS>;
+  constexpr int RP = D::RP, CH = D::CH, UC = D::UC, UCPR = D::UCPR;
+  constexpr int RTN = RP / 16;
+  constexpr int CR = CH / 4;   // channels of a lane group (one 16-byte chunk)
+  constexpr int KST = W;       // K steps per chunk: CR * W columns / 8
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = lane >> 4;
+  const int n = lane & 15;
+  const int wv = tid >> 6;
+  const int nchunk = p.D / CH;
+  const bf16_t* U = static_cast<const bf16_t*>(p.U);
+  const bf16_t* xb = static_cast<const bf16_t*>(p.x) + b * p.xs0 + int64_t(tb0 - HALO) * p.xs1;
+  const bf16_t* dyb = static_cast<const bf16_t*>(p.dy) + b * p.dys0 + int64_t(tb0) * p.dys1;
+
+  // this wave's transfers of a stage: instructions wv, wv + 4, ... of each region; per
+  // lane the element offset of its source chunk relative to the chunk's base
+  constexpr int SU = (D::NI_U + 3) / 4, SX = (D::NI_X + 3) / 4, SD = (D::NI_D + 3) / 4;
+  int uoffg[SU], xoffg[SX], doffg[SD];
+  bool uact[SU], xact[SX], dact[SD];
+#pragma unroll
+  for (int i = 0; i < SU; ++i) {
+    const int pidx = (wv + 4 * i) * 64 + lane;
+    const int r = pidx / UCPR, pc = pidx % UCPR;
+    const int c = (pc - (r & 15) % UCPR + UCPR) % UCPR;
+    uact[i] = pidx < D::UCH;
+    uoffg[i] = r * int(p.ldu) + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < SX; ++i) {
+    const int pidx = (wv + 4 * i) * 64 + lane;
+    const int row = pidx / 4, c = ((pidx % 4) - (row >> 2)) & 3;
+    xact[i] = pidx < D::XCH;
+    // rows before token 0 read token 0 instead (their products are zeroed below)
+    xoffg[i] = max(row, HALO - tb0) * int(p.xs1) + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < SD; ++i) {
+    const int pidx = (wv + 4 * i) * 64 + lane;
+    const int row = pidx / 4, c = ((pidx % 4) - (row >> 2)) & 3;
+    dact[i] = pidx < D::DCH;
+    doffg[i] = row * int(p.dys1) + c * 8;
+  }
+  // every wave issues at least this many transfers per stage
+  constexpr int NMIN = D::NI_U / 4 + D::NI_X / 4 + D::NI_D / 4;
+  auto issue = [&](int st, int ci) {
+    ci = min(ci, nchunk - 1);  // past the last chunk: reload it (never read)
+    const int c0 = ci * CH;
+    unsigned char* stage = smem + st * D::STAGE;
+    const bf16_t* ub = U + int64_t(c0) * W;
+#pragma unroll
+    for (int i = 0; i < SU; ++i)
+      if (uact[i]) dma16(ub + uoffg[i], stage + (wv + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < SX; ++i)
+      if (xact[i]) dma16(xb + c0 + xoffg[i], stage + D::X_OFF + (wv + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < SD; ++i)
+      if (dact[i]) dma16(dyb + c0 + doffg[i], stage + D::D_OFF + (wv + 4 * i) * 1024);
+  };
+
+  // per-lane LDS byte offsets inside a stage
+  const int nt = wv * TT + n;  // the lane's token within the block
+  const int dy_off = D::D_OFF + nt * 64 + ((q + (nt >> 2)) & 3) * 16;
+  int x_off[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    const int row = nt + HALO - k;
+    x_off[k] = D::X_OFF + row * 64 + ((q + (row >> 2)) & 3) * 16;
+  }
+  int u_off[KST];  // row rt * 16 + n adds rt * 16 * UC * 2 bytes (same rotation)
+#pragma unroll
+  for (int ks = 0; ks < KST; ++ks) u_off[ks] = n * UC * 2 + ((q * W + ks + n) % UCPR) * 16;
+
+  f32x4_t acc[RTN];
+#pragma unroll
+  for (int j = 0; j < RTN; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int ci = 0; ci < nchunk; ++ci) {
+    // this wave's transfers of stage ci were followed by at least NIW_MIN newer ones
+    vm_wait_barrier<NMIN>();
+    issue((ci + 2) % D::NST, ci + 2);
+    const unsigned char* stage = smem + (ci % D::NST) * D::STAGE;
+    uint32_t dw_[4], xw[W][4];
+    {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + dy_off);
+      dw_[0] = v[0]; dw_[1] = v[1]; dw_[2] = v[2]; dw_[3] = v[3];
+    }
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + x_off[k]);
+      xw[k][0] = v[0]; xw[k][1] = v[1]; xw[k][2] = v[2]; xw[k][3] = v[3];
+    }
+    if (tb0 < HALO) {
+      // zeros before t = 0
+#pragma unroll
+      for (int k = 1; k < W; ++k)
+        if (tb0 + nt - k < 0) xw[k][0] = xw[k][1] = xw[k][2] = xw[k][3] = 0u;
+    }
+    float dyf[CR];
+#pragma unroll
+    for (int c = 0; c < CR; ++c) dyf[c] = (c & 1) ? bf16_hi(dw_[c >> 1]) : bf16_lo(dw_[c >> 1]);
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      Mfma<bf16_t>::F32k bfr;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int c0_ = (8 * ks + e) / W, k0_ = (8 * ks + e) % W;
+        const int c1_ = (8 * ks + e + 1) / W, k1_ = (8 * ks + e + 1) % W;
+        const float x0 = (c0_ & 1) ? bf16_hi(xw[k0_][c0_ >> 1]) : bf16_lo(xw[k0_][c0_ >> 1]);
+        const float x1 = (c1_ & 1) ? bf16_hi(xw[k1_][c1_ >> 1]) : bf16_lo(xw[k1_][c1_ >> 1]);
+        const uint32_t w2 = pack_bf16x2(dyf[c0_] * x0, dyf[c1_] * x1);
+        bfr.v[e] = uint16_t(w2 & 0xffffu);
+        bfr.v[e + 1] = uint16_t(w2 >> 16);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RTN; ++rt) {
+        Mfma<bf16_t>::F32k afr;
+        afr.v = *reinterpret_cast<const u16x8_t*>(stage + u_off[ks] + rt * 16 * UC * 2);
+        acc[rt] = Mfma<bf16_t>::mma32(afr, bfr, acc[rt]);
+      }
+    }
+  }
+  // drain this wave's remaining transfers (into stages nobody reads) before leaving
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  bf16_t* dz = static_cast<bf16_t*>(p.dz) + b * p.dzs0;
+  const int t = tb0 + nt;
+#pragma unroll
+  for (int rt = 0; rt < RTN; ++rt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int r = rt * 16 + 4 * q + ii;
+      reinterpret_cast<uint16_t*>(dz)[int64_t(t) * p.dzs1 + r] = to_bf16_bits(acc[rt][ii]);
+    }
+}
+
+// The LDS DMA path serves bf16 token blocks that lie inside T when its stages fit.
 template <typename ET, int W, int KS>
+constexpr bool lowrank_dz_dma_ok() {
+  return sizeof(ET) == 2 && LrDzDma<W, KS>::BYTES <= 150 * 1024;
+}
+
+// DMA: the LDS DMA path (the launch covers whole token blocks, aligned rows, D % 32 == 0
+// and R % 32 == 0); otherwise the register-staged path with element loads where needed.
+template <typename ET, int W, int KS, bool DMA>
 __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParams p) {
-  using Sh = LrDzShape<ET, W, KS>;
-  __shared__ LrDzSmem<ET, W, KS> sm;
-  // 16-byte loads throughout when every chunk of every row allows them
-  const bool fast = p.act16 != 0 && p.u16 != 0 && p.D % Sh::CH == 0;
-  if (fast) {
-    lowrank_dz_body<true, ET, W, KS>(p, sm);
+  if constexpr (DMA) {
+    __shared__ __align__(16) unsigned char smem[LrDzDma<W, KS>::BYTES];
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    lowrank_dz_dma<W, KS>(p, smem, int(lb / uint32_t(p.nTbL)),
+                          (p.tbb0 + int(lb % uint32_t(p.nTbL))) * kLowrankDzTokens);
   } else {
-    lowrank_dz_body<false, ET, W, KS>(p, sm);
+    __shared__ LrDzSmem<ET, W, KS> sm;
+    lowrank_dz_body<ET, W, KS>(p, sm);
   }
 }
 
@@ -1142,17 +1388,55 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParam
 // ---------------------------------------------------------------------------------
 template <typename ET, int W, int KS>
 hipError_t lr_fwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_t s) {
-  hipLaunchKernelGGL((k_lowrank_fwd<ET, W, KS>), dim3(unsigned(pl.blocks)), dim3(kBlockThreads), 0, s, p);
+  LowRankParams q = p;
+  q.cs0 = 0;
+  q.nCsL = pl.nCs;
+  hipLaunchKernelGGL((k_lowrank_fwd<ET, W, KS>), dim3(unsigned(pl.blocks)), dim3(kBlockThreads), 0, s, q);
   return hipGetLastError();
 }
 
 template <typename ET, int W, int KS>
 hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_t s) {
-  hipLaunchKernelGGL((k_lowrank_bwd<ET, W, KS>), dim3(unsigned(pl.blocks)), dim3(kBlockThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t zblocks = int64_t(p.B) * ((p.T + kLowrankDzTokens - 1) / kLowrankDzTokens);
-  hipLaunchKernelGGL((k_lowrank_dz<ET, W, KS>), dim3(unsigned(zblocks)), dim3(kBlockThreads), 0, s, p);
+  // main kernel: the channel slices inside D on the 16-byte path, the rest on the other
+  const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;
+  const int nfull = vec ? p.D / lowrank_bwd_dc(W, KS) : 0;
+  LowRankParams q = p;
+  const int64_t per_slice = int64_t(p.B) * pl.nTr;
+  if (nfull > 0) {
+    q.cs0 = 0;
+    q.nCsL = nfull;
+    hipLaunchKernelGGL((k_lowrank_bwd<ET, W, KS, true>), dim3(unsigned(per_slice * nfull)), dim3(kBlockThreads), 0, s,
+                       q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nfull < pl.nCs) {
+    q.cs0 = nfull;
+    q.nCsL = pl.nCs - nfull;
+    hipLaunchKernelGGL((k_lowrank_bwd<ET, W, KS, false>), dim3(unsigned(per_slice * q.nCsL)), dim3(kBlockThreads), 0,
+                       s, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dz: token blocks inside T on the DMA path, the rest on the register path
+  const int nblk = (p.T + kLowrankDzTokens - 1) / kLowrankDzTokens;
+  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.act16 != 0 && p.u16 != 0 && p.D % kLowrankDzChunk == 0 &&
+                   p.R % 32 == 0;
+  const int nfb = dma ? p.T / kLowrankDzTokens : 0;
+  if (nfb > 0) {
+    q.tbb0 = 0;
+    q.nTbL = nfb;
+    hipLaunchKernelGGL((k_lowrank_dz<ET, W, KS, lowrank_dz_dma_ok<ET, W, KS>()>), dim3(unsigned(int64_t(p.B) * nfb)),
+                       dim3(kBlockThreads), 0, s, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nfb < nblk) {
+    q.tbb0 = nfb;
+    q.nTbL = nblk - nfb;
+    hipLaunchKernelGGL((k_lowrank_dz<ET, W, KS, false>), dim3(unsigned(int64_t(p.B) * q.nTbL)), dim3(kBlockThreads), 0,
+                       s, q);
+  }
   return hipGetLastError();
 }
 
