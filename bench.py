@@ -105,16 +105,21 @@ def gen(shape, std, seed, name, device):
 
 
 class Flusher:
-    """Writes 512 MiB between timed launches so neither the L2s nor the 256 MB Infinity
-    Cache still hold the previous launch's data."""
+    """Reads a 1 GiB buffer between timed launches, so that neither the L2s nor the 256 MB
+    Infinity Cache still hold the previous launch's data. A read leaves only clean lines
+    behind: a written flush buffer would leave dirty lines whose write-back the next
+    timed launch would pay for."""
 
     def __init__(self, device):
         import torch
 
-        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=device)
+        self.sink = torch.empty((), dtype=torch.float32, device=device)
 
     def __call__(self):
-        self.buf.fill_(1)
+        import torch
+
+        torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def time_launches(fn, reps, flush, warm=3):
