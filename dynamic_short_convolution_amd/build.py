@@ -19,6 +19,7 @@ SOURCES = [
     "dynconv_abi.hip",
     "dynconv_stream.hip",
     "dynconv_lowrank.hip",
+    "dynconv_lowrank_fast.hip",
 ]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated from ordinary float code.
@@ -33,6 +34,9 @@ COMPILE_FLAGS = [
     "-target-feature",
     "-Xclang",
     "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: no v_accvgpr_read copies before they are used
+    "-mllvm",
+    "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -121,6 +121,11 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
 
 dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   hipStream_t stream);
+// bf16 fast forward (LDS DMA pipeline; W <= 4, R in {32, 64, 128}, H == 1, 16-byte
+// aligned rows, D a multiple of 64). It plans its own token ranges.
+bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
+hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t stream);
+
 dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   float* dU, float* db, hipStream_t stream);
 

@@ -1494,6 +1494,10 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
 
 dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   hipStream_t stream) {
+  if (lowrank_fwd_fast_ok(p, W, dt)) {
+    const hipError_t e = launch_lowrank_fwd_fast(p, W, stream);
+    return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
+  }
   const hipError_t e = dt == DYNCONV_BF16 ? lr_dispatch_w<false, bf16_t>(p, plan, W, stream)
                                           : lr_dispatch_w<false, float>(p, plan, W, stream);
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);

@@ -151,3 +151,55 @@ def test_full_lowrank_r64_bwd():
         gab = _g_abs(xs, dys, wl.W)
         extra = (2.0**-8 * (gab @ np.abs(to64(U)).T)).reshape(1, -1, wl.R)[:, 4:]
         assert_close("dz", got, rdz[:, 4:], torch.bfloat16, extra=extra)
+
+
+# ---------------------------------------------------------------------------------
+# The bf16 forward fast path (W <= 4, R in {32, 64, 128}, D a multiple of 64, 16-byte
+# aligned rows): token ranges of whole 64-token steps, an x ring in LDS that carries the
+# W-1 rows before each step, buffer stores that drop rows past T.
+# ---------------------------------------------------------------------------------
+FAST = []
+for W in (1, 2, 3, 4):
+    for R in (32, 64, 128):
+        for (B, T, D) in ((1, 1, 64), (2, 65, 128), (3, 200, 192)):
+            FAST.append((W, R, B, T, D))
+
+
+@pytest.mark.parametrize("W,R,B,T,D", FAST)
+def test_fast_fwd_parity(W, R, B, T, D):
+    _check(B, T, D, W, R, "bf16", seed=1000 + 7 * W + R + T, bwd=False)
+
+
+@pytest.mark.parametrize("W", [1, 4])
+def test_fast_fwd_no_bias(W):
+    _check(2, 130, 128, W, 64, "bf16", seed=77 + W, bias=False, bwd=False)
+
+
+def test_fast_fwd_multistep_ranges():
+    """Token ranges of several 64-token steps (the LDS ring wraps), a partial last step,
+    and the rows before each range carried from memory; checked on sampled channels."""
+    B, T, D, W, R = 2, 3000, 2048, 4, 64
+    x, z, U, b, _ = _inputs(B, T, D, W, R, "bf16", 31)
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W)
+    chans = np.concatenate([np.arange(0, 64), np.arange(1088, 1152), np.arange(1984, 2048)])
+    ci = torch.as_tensor(chans)
+    cols = torch.as_tensor((chans[:, None] * W + np.arange(W)[None, :]).reshape(-1))
+    ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
+                      to64(b.index_select(0, cols)), W)
+    assert_close("y", y.index_select(2, ci.cuda()).cpu(), ref, torch.bfloat16)
+
+
+def test_fast_fwd_strided_views():
+    """x, z and y as column slices of wider row-major buffers (row strides above D, R)."""
+    B, T, D, W, R = 2, 150, 128, 3, 64
+    x, z, U, b, _ = _inputs(B, T, D, W, R, "bf16", 41)
+    xw = torch.zeros(B, T, 3 * D, dtype=torch.bfloat16)
+    xw[:, :, D : 2 * D] = x
+    zw = torch.zeros(B, T, R + 32, dtype=torch.bfloat16)
+    zw[:, :, 32:] = z
+    xg, zg = xw.cuda()[:, :, D : 2 * D], zw.cuda()[:, :, 32:]
+    yw = torch.zeros(B, T, 2 * D, dtype=torch.bfloat16, device="cuda")
+    dynconv_lowrank_fwd(xg, zg, U.cuda(), b.cuda(), W, out=yw[:, :, D:])
+    ref = lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W)
+    assert_close("y", yw[:, :, D:].cpu(), ref, torch.bfloat16)
+    assert torch.count_nonzero(yw[:, :, :D]) == 0, "write outside the output view"
