@@ -326,7 +326,7 @@ dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void*
   const int eb = elem_bytes(dtype);
   const Act acts[2] = {{x, xs}, {y, ys}};
   if (!act_align_ok(acts, 2, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
-  const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, false);
+  const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, false, dtype);
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
   p.act16 = act_align_ok(acts, 2, eb, 16) ? 1 : 0;
   p.z16 = (aligned(z, 16) && (zs[0] * eb) % 16 == 0 && (zs[1] * eb) % 16 == 0) ? 1 : 0;
@@ -340,7 +340,7 @@ size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32
                                           dynconv_dtype dtype) {
   if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK || R < 1 || R > 128 || H != 1) return 0;
   if (B == 0 || T == 0 || D == 0) return 0;
-  return plan_lowrank(B, T, D, W, H, R, true).ws_total;
+  return plan_lowrank(B, T, D, W, H, R, true, dtype).ws_total;
 }
 
 dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
@@ -368,7 +368,7 @@ dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void*
   const int eb = elem_bytes(dtype);
   const Act acts[3] = {{x, xs}, {dy, dys}, {dx, dxs}};
   if (!act_align_ok(acts, 3, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
-  const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, true);
+  const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, true, dtype);
   if (workspace == nullptr || workspace_bytes < plan.ws_total) return DYNCONV_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return DYNCONV_ERR_UNSUPPORTED;
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);

@@ -117,7 +117,7 @@ struct LowRankPlan {
   size_t ws_total;
 };
 
-LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bwd);
+LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bwd, dynconv_dtype dt);
 
 dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   hipStream_t stream);
@@ -125,6 +125,9 @@ dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& pla
 // aligned rows, D a multiple of 64). It plans its own token ranges.
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
 hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t stream);
+// bf16 fast dx of the backward (same conditions, on dy and dx); it plans its own ranges.
+bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
+hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t stream);
 
 dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   float* dU, float* db, hipStream_t stream);

@@ -380,6 +380,276 @@ hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Backward dx, k_lowrank_bwd_dx_fast:
+//   dx_s = dy_s + sum_k w_k(s + k) dy_{s+k}    (the adjoint of eq. 2 + eq. 3)
+// Same workgroup shape, staging and filter generation as the forward, with dy in place
+// of x (dx needs no x). Lane (n, q) holds the filters of tokens 4n .. 4n+3 of the step
+// and forms P_k(t) = w_k(t) dy_t for them. A term P_k(t) belongs to dx_{t-k}: to the
+// lane's own tokens when t - k >= 4n, else to the previous lane's tokens 4n-3 .. 4n-1
+// (three "outgoing" sums, O_1..O_3). Each lane receives the O sums of lane n + 1 by a
+// DPP rotate within its 16-lane row (row_ror:15). Lane 15 receives lane 0's sums, which
+// complete its tokens 61 .. 63 of the previous step: lane 15 keeps those three partial
+// sums from one step to the next and writes them then. A step's dx tile therefore holds
+// tokens t0 - 3 .. t0 + 60; the step after the range (tail) only completes its first
+// three rows, and the first step's first three rows belong to the previous range.
+// dy rows at or past T are zeroed, so the tail contributes nothing past the sequence.
+// ---------------------------------------------------------------------------------
+template <int KS>
+struct BwdDxFast {
+  static constexpr int NWV = 4;
+  static constexpr int CPB = 64;
+  static constexpr int XCPR = 8, XROW = 128;
+  static constexpr int XSTAGE = kStep * XROW;        // dy stage, dx tile
+  static constexpr int ZCPR = 4 * KS;
+  static constexpr int ZROW = 16 * ZCPR;
+  static constexpr int ZSTAGE = kStep * ZROW;
+  static constexpr int Z_OFF = 2 * XSTAGE;            // two dy stages
+  static constexpr int T_OFF = Z_OFF + 2 * ZSTAGE;    // two z stages, then two dx tiles
+  static constexpr int BYTES = T_OFF + 2 * XSTAGE;
+  static constexpr int DI = 2, ZI = KS, ND = DI + ZI, NS = 2;
+};
+
+template <int W, int KS>
+__global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams p) {
+  using F = BwdDxFast<KS>;
+  constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
+  constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF, T_OFF = F::T_OFF;
+  __shared__ __align__(16) unsigned char smem[F::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = lane >> 4;
+  const int n = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int cs = p.cs0 + int(lb % uint32_t(p.nCsL));
+  lb /= uint32_t(p.nCsL);
+  const int tr = int(lb % uint32_t(p.nTr));
+  const int b = int(lb / uint32_t(p.nTr));
+  const int c_base = cs * F::CPB;
+  const int t_first = tr * p.Ltok;
+  const int t_end = min(p.T, t_first + p.Ltok);
+  const int nsteps = (t_end - t_first + kStep - 1) / kStep;
+  const char* dyc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.dy) + b * p.dys0 + c_base);
+  const char* zc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.z) + b * p.zs0);
+  const int cw = c_base + 16 * wv;
+
+  // ---- LDS DMA of a step's dy and z rows (rows past T - 1 read row T - 1) ----
+  uint32_t doff[F::DI], zoff[F::ZI];
+  int drl[F::DI], zrl[F::ZI];
+#pragma unroll
+  for (int i = 0; i < F::DI; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int rl = idx / XCPR, pc = idx % XCPR;
+    const int c = (pc - (rl >> 2)) & (XCPR - 1);
+    drl[i] = rl;
+    doff[i] = uint32_t(rl * int(p.dys1) + 8 * c) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < F::ZI; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int rl = idx / ZCPR, pc = idx % ZCPR;
+    const int c = ((pc - (rl >> 2)) % ZCPR + ZCPR) % ZCPR;
+    zrl[i] = rl;
+    zoff[i] = uint32_t(rl * int(p.zs1) + 8 * c) * 2u;
+  }
+  auto issue = [&](int st, int t0) {
+    unsigned char* ds = smem + st * XSTAGE;
+    unsigned char* zs = smem + Z_OFF + st * ZSTAGE;
+    if (t0 + kStep <= p.T) {
+      const char* dg = dyc + int64_t(t0) * p.dys1 * 2;
+      const char* zg = zc + int64_t(t0) * p.zs1 * 2;
+#pragma unroll
+      for (int i = 0; i < F::DI; ++i) dma16(dg + doff[i], ds + (wv + 4 * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < F::ZI; ++i) dma16(zg + zoff[i], zs + (wv + 4 * i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < F::DI; ++i) {
+        const int t = min(t0 + drl[i], p.T - 1);
+        dma16(dyc + (int64_t(t) - drl[i]) * p.dys1 * 2 + doff[i], ds + (wv + 4 * i) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < F::ZI; ++i) {
+        const int t = min(t0 + zrl[i], p.T - 1);
+        dma16(zc + (int64_t(t) - zrl[i]) * p.zs1 * 2 + zoff[i], zs + (wv + 4 * i) * 1024);
+      }
+    }
+  };
+
+  // ---- A operands and bias, as in the forward ----
+  u16x8_t afr[4][KS];
+  f32x4_t binit[4];
+  {
+    const uint16_t* U = static_cast<const uint16_t*>(p.U);
+    const bool has_bias = p.bias != nullptr;
+    const uint16_t* bsrc = has_bias ? static_cast<const uint16_t*>(p.bias) : U;
+    const uint32_t bmask = has_bias ? ~0u : 0u;
+    const int tap = n & 3;
+    const int ltap = tap < W ? tap : W - 1;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int ch = cw + 4 * (n >> 2) + mt;
+      const int64_t col = int64_t(ch) * W + ltap;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t v = U[int64_t(32 * ks + 8 * q + e) * p.ldu + col];
+          afr[mt][ks][e] = tap < W ? v : uint16_t(0);
+        }
+      const int chq = cw + 4 * q + mt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t v = bsrc[(has_bias ? int64_t(chq) * W : 0) + (i < W ? i : W - 1)];
+        binit[mt][i] = __uint_as_float((uint32_t(v) << 16) & (i < W ? bmask : 0u));
+      }
+    }
+  }
+  issue(0, t_first);
+
+  // ---- per-lane LDS offsets ----
+  const int xc = 2 * wv + (q >> 1);  // logical 16-byte chunk of the lane's 4 channels
+  const int drd = 4 * n * XROW + ((xc + n) & (XCPR - 1)) * 16 + 8 * (q & 1);  // dy row 4n (+ j * XROW)
+  int zr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) zr[ks] = 4 * n * ZROW + ((4 * ks + q + n) % ZCPR) * 16;
+  // dx tile row of the lane's output j: token 4n + j sits in row 4n + j + 3; lane 15's
+  // outputs 1..3 are the previous step's tokens 61..63, rows 0..2
+  int trow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = (n == 15 && j > 0) ? j - 1 : 4 * n + j + 3;
+    trow[j] = r * XROW + ((xc + (r >> 2)) & (XCPR - 1)) * 16 + 8 * (q & 1);
+  }
+  __amdgpu_buffer_rsrc_t dxr = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<bf16_t*>(p.out) + b * p.os0, 0, int((int64_t(p.T - 1) * p.os1 + p.D) * 2), kBufWord3);
+  const int dstep = int(p.os1 * 2);
+  int ttr[F::NS], tgo[F::NS], trr[F::NS];
+#pragma unroll
+  for (int i = 0; i < F::NS; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int r = idx / XCPR, pc = idx % XCPR;
+    const int c = (pc - (r >> 2)) & (XCPR - 1);
+    ttr[i] = idx * 16;
+    trr[i] = r;
+    tgo[i] = int(((r - 3) * p.os1 + c_base + 8 * c) * 2);  // tile row r is token t0 - 3 + r
+  }
+  // Stores tile `buf` of step s (tokens t0 - 3 ..): the first step's rows 0..2 belong to
+  // the previous range and the tail's rows 3.. to the next; their offsets are pushed out
+  // of the buffer so the hardware drops them.
+  auto tflush = [&](int buf, int s, int t0) {
+    const unsigned char* tt = smem + T_OFF + buf * XSTAGE;
+#pragma unroll
+    for (int i = 0; i < F::NS; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tt + ttr[i]);
+      const bool keep = (s > 0 || trr[i] >= 3) && (s < nsteps || trr[i] < 3);
+      __builtin_amdgcn_raw_buffer_store_b128(v, dxr, keep ? tgo[i] + t0 * dstep : int(0x80000000u), 0, 0);
+    }
+  };
+
+  float pend[3][4];  // lane 15: tokens 61..63 of the previous step, without lane 0's terms
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pend[m][c] = 0.f;
+
+  for (int s = 0; s <= nsteps; ++s) {
+    const int t0 = t_first + s * kStep;
+    const int u = s & 1;
+    if (s >= 2) {
+      vm_wait_barrier<F::NS>();
+    } else {
+      vm_wait_barrier<0>();
+    }
+    if (s < nsteps) issue(u ^ 1, t0 + kStep);
+    if (s > 0) tflush(u ^ 1, s - 1, t0 - kStep);
+    // dy of the lane's tokens 4n .. 4n+3, 4 channels; zero at or past T
+    float dyv[4][4];
+    {
+      const unsigned char* ds = smem + u * XSTAGE + drd;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(ds + j * XROW);
+        dyv[j][0] = bf16_lo(v[0]);
+        dyv[j][1] = bf16_hi(v[0]);
+        dyv[j][2] = bf16_lo(v[1]);
+        dyv[j][3] = bf16_hi(v[1]);
+      }
+      if (t0 + kStep > p.T) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = t0 + 4 * n + j < p.T;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) dyv[j][c] = ok ? dyv[j][c] : 0.f;
+        }
+      }
+    }
+    const unsigned char* zs = smem + Z_OFF + u * ZSTAGE;
+    auto gen = [&](int j, f32x4_t (&acc)[4]) {
+      u16x8_t bfr[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8_t*>(zs + zr[ks] + j * ZROW);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        acc[mt] = mma32(afr[mt][0], bfr[0], binit[mt]);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32(afr[mt][ks], bfr[ks], acc[mt]);
+      }
+    };
+    // own[j]: dx of the lane's token j from its own terms; out[m]: terms for the previous
+    // lane's token m (1..3)
+    float own[4][4], out[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        own[j][c] = dyv[j][c];
+        out[j][c] = 0.f;
+      }
+    f32x4_t acc[2][4];
+    gen(0, acc[0]);
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+      if (jp + 1 < 4) gen(jp + 1, acc[(jp + 1) & 1]);
+      const f32x4_t(&a)[4] = acc[jp & 1];
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        const int j = jp - k;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (j >= 0) {
+            own[j][c] = fmaf(a[c][k], dyv[jp][c], own[j][c]);
+          } else {
+            out[4 + j][c] = fmaf(a[c][k], dyv[jp][c], out[4 + j][c]);
+          }
+        }
+      }
+    }
+    // the next lane's outgoing sums (lane 15: lane 0's, for the previous step's tokens)
+    float dxv[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dxv[0][c] = own[0][c];
+#pragma unroll
+    for (int m = 1; m < 4; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float in = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(out[m][c]), 0x12F, 0xf, 0xf, false));
+        const float base = n == 15 ? pend[m - 1][c] : own[m][c];
+        dxv[m][c] = base + in;
+        pend[m - 1][c] = own[m][c];
+      }
+    unsigned char* tt = smem + T_OFF + u * XSTAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x2*>(tt + trow[j]) = u32x2{pack_bf16x2(dxv[j][0], dxv[j][1]), pack_bf16x2(dxv[j][2], dxv[j][3])};
+  }
+  __syncthreads();
+  tflush(nsteps & 1, nsteps, t_first + nsteps * kStep);
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
 template <int KS>
 using FwdCfg = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD>;
 
@@ -467,6 +737,64 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t s)
     case 2: return fwd_fast_ks<2>(q, pl.blocks, s);
     case 3: return fwd_fast_ks<3>(q, pl.blocks, s);
     case 4: return fwd_fast_ks<4>(q, pl.blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dynconv
+
+namespace dynconv {
+
+namespace {
+
+template <int W, int KS>
+hipError_t bwd_dx_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<W, KS>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int W>
+hipError_t bwd_dx_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  switch (p.R / 32) {
+    case 1: return bwd_dx_inst<W, 1>(p, blocks, s);
+    case 2: return bwd_dx_inst<W, 2>(p, blocks, s);
+    case 4: return bwd_dx_inst<W, 4>(p, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
+  const int ks = p.R / 32;
+  return dt == DYNCONV_BF16 && p.H == 1 && W >= 1 && W <= 4 && p.R % 32 == 0 && (ks == 1 || ks == 2 || ks == 4) &&
+         p.D % 64 == 0 && p.act16 != 0 && p.z16 != 0 && (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
+         int64_t(kStep) * p.dys1 < (int64_t(1) << 30) && int64_t(kStep) * p.zs1 < (int64_t(1) << 30);
+}
+
+hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t s) {
+  // two or three workgroups per CU (48 KiB of LDS at R = 64): about 512 of them
+  LowRankPlan pl{};
+  pl.nCs = p.D / 64;
+  const int64_t target = 512;
+  int64_t per_seq = (target + int64_t(p.B) * pl.nCs - 1) / (int64_t(p.B) * pl.nCs);
+  const int64_t max_ranges = (p.T + kStep - 1) / kStep;
+  if (per_seq > max_ranges) per_seq = max_ranges;
+  if (per_seq < 1) per_seq = 1;
+  int64_t L = (p.T + per_seq - 1) / per_seq;
+  L = (L + kStep - 1) / kStep * kStep;
+  LowRankParams q = p;
+  q.cs0 = 0;
+  q.nCsL = pl.nCs;
+  q.nCs = pl.nCs;
+  q.Ltok = int(L);
+  q.nTr = int((p.T + L - 1) / L);
+  const int64_t blocks = int64_t(p.B) * q.nTr * pl.nCs;
+  switch (W) {
+    case 1: return bwd_dx_ks<1>(q, blocks, s);
+    case 2: return bwd_dx_ks<2>(q, blocks, s);
+    case 3: return bwd_dx_ks<3>(q, blocks, s);
+    case 4: return bwd_dx_ks<4>(q, blocks, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -154,9 +154,10 @@ def test_full_lowrank_r64_bwd():
 
 
 # ---------------------------------------------------------------------------------
-# The bf16 forward fast path (W <= 4, R in {32, 64, 128}, D a multiple of 64, 16-byte
-# aligned rows): token ranges of whole 64-token steps, an x ring in LDS that carries the
-# W-1 rows before each step, buffer stores that drop rows past T.
+# The bf16 fast paths (W <= 4, R in {32, 64, 128}, D a multiple of 64, 16-byte aligned
+# rows): token ranges of whole 64-token steps, an x ring in LDS that carries the W-1 rows
+# before each step (forward), dx completed across lanes, ranges and a tail step
+# (backward), buffer stores that drop rows past T.
 # ---------------------------------------------------------------------------------
 FAST = []
 for W in (1, 2, 3, 4):
@@ -166,13 +167,13 @@ for W in (1, 2, 3, 4):
 
 
 @pytest.mark.parametrize("W,R,B,T,D", FAST)
-def test_fast_fwd_parity(W, R, B, T, D):
-    _check(B, T, D, W, R, "bf16", seed=1000 + 7 * W + R + T, bwd=False)
+def test_fast_parity(W, R, B, T, D):
+    _check(B, T, D, W, R, "bf16", seed=1000 + 7 * W + R + T)
 
 
 @pytest.mark.parametrize("W", [1, 4])
-def test_fast_fwd_no_bias(W):
-    _check(2, 130, 128, W, 64, "bf16", seed=77 + W, bias=False, bwd=False)
+def test_fast_no_bias(W):
+    _check(2, 130, 128, W, 64, "bf16", seed=77 + W, bias=False)
 
 
 def test_fast_fwd_multistep_ranges():
@@ -203,3 +204,17 @@ def test_fast_fwd_strided_views():
     ref = lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W)
     assert_close("y", yw[:, :, D:].cpu(), ref, torch.bfloat16)
     assert torch.count_nonzero(yw[:, :, :D]) == 0, "write outside the output view"
+
+
+def test_fast_bwd_multistep_ranges():
+    """Backward dx over token ranges of several steps: the rows completed by the tail step
+    of one range and skipped by the first step of the next; sampled channels."""
+    B, T, D, W, R = 2, 3000, 2048, 4, 64
+    x, z, U, b, dy = _inputs(B, T, D, W, R, "bf16", 32)
+    dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W)
+    chans = np.concatenate([np.arange(0, 64), np.arange(1088, 1152), np.arange(1984, 2048)])
+    ci = torch.as_tensor(chans)
+    cols = torch.as_tensor((chans[:, None] * W + np.arange(W)[None, :]).reshape(-1))
+    rdx, _, _, _ = lowrank_bwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
+                               to64(b.index_select(0, cols)), to64(dy.index_select(2, ci)), W)
+    assert_close("dx", dx.index_select(2, ci.cuda()).cpu(), rdx, torch.bfloat16)
