@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "dynconv_internal.hpp"
+#include "dynconv_lowrank_internal.hpp"
 
 namespace dynconv {
 

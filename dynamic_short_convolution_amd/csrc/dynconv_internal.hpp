@@ -61,77 +61,6 @@ dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, 
 dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,
                                       hipStream_t stream);
 
-// ---------------------------------------------------------------------------------
-// Low-rank form
-// ---------------------------------------------------------------------------------
-struct LowRankParams {
-  const void* x;
-  const void* z;
-  const void* U;
-  const void* bias;  // may be null
-  const void* dy;
-  void* out;   // y (forward) or dx (backward)
-  void* dz;
-  float* part_dU;  // [nTr][R][J]   partial dU per token range
-  float* part_db;  // [nTr][J]      partial db per token range
-  int64_t xs0, xs1;
-  int64_t zs0, zs1;
-  int64_t ldu;
-  int64_t dys0, dys1;
-  int64_t os0, os1;
-  int64_t dzs0, dzs1;
-  int32_t B, T, D, H, G, R, J;
-  int32_t nCs;     // channel slices
-  int32_t cs0, nCsL;   // channel slices of one launch: cs0 .. cs0 + nCsL - 1
-  int32_t tbb0, nTbL;  // dz token blocks of one launch (per sequence): tbb0 .. + nTbL - 1
-  int32_t Ltok;    // tokens per token range
-  int32_t nTr;     // token ranges per sequence
-  int32_t act16;   // every activation-shaped tensor allows 16-byte vectors
-  int32_t z16;     // z rows allow 16-byte vectors
-  int32_t u16;     // U rows allow 16-byte vectors
-};
-
-// Low-rank forward tiling, shared by the planner and the kernel: each wave generates MT
-// 16-row MFMA tiles of filter columns; a filter of W <= 4 taps takes 4 rows (one lane
-// group), W = 5 takes 8 rows (two lane groups). A workgroup of 4 waves covers
-// 4 * MT * 16 / rows_per_channel channels.
-#ifndef LOWRANK_FWD_MT
-#define LOWRANK_FWD_MT 8
-#endif
-constexpr int lowrank_fwd_mt(int KS) { return KS <= 2 ? LOWRANK_FWD_MT : 4; }
-constexpr int lowrank_rows_per_channel(int W) { return W > 4 ? 8 : 4; }
-constexpr int lowrank_fwd_dc(int W, int KS) { return 4 * lowrank_fwd_mt(KS) * 16 / lowrank_rows_per_channel(W); }
-// Backward: fewer filter tiles per wave (its registers also hold dU accumulators); the
-// pipeline advances kLowrankBwdStep tokens per step.
-constexpr int lowrank_bwd_mt(int) { return 2; }
-constexpr int lowrank_bwd_dc(int W, int KS) { return 4 * lowrank_bwd_mt(KS) * 16 / lowrank_rows_per_channel(W); }
-constexpr int kLowrankBwdStep = 64;
-// dz kernel: tokens per workgroup (16 per wave) and channels per staged chunk.
-constexpr int kLowrankDzTokens = 64;
-constexpr int kLowrankDzChunk = 32;
-
-struct LowRankPlan {
-  int nCs, Ltok, nTr;
-  int64_t blocks;
-  size_t ws_dU, ws_db;  // byte offsets inside the workspace
-  size_t ws_total;
-};
-
-LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bwd, dynconv_dtype dt);
-
-dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
-                                  hipStream_t stream);
-// bf16 fast forward (LDS DMA pipeline; W <= 4, R in {32, 64, 128}, H == 1, 16-byte
-// aligned rows, D a multiple of 64). It plans its own token ranges.
-bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
-hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t stream);
-// bf16 fast dx of the backward (same conditions, on dy and dx); it plans its own ranges.
-bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
-hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t stream);
-
-dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
-                                  float* dU, float* db, hipStream_t stream);
-
 // Records a HIP failure for dynconv_last_hip_error(); returns DYNCONV_ERR_HIP.
 dynconv_status record_hip_error(hipError_t e);
 

@@ -23,6 +23,7 @@
 //   partial sums of dU and db are then added in a fixed order (run-to-run deterministic).
 #include "dynconv_common.hpp"
 #include "dynconv_internal.hpp"
+#include "dynconv_lowrank_internal.hpp"
 
 namespace dynconv {
 

@@ -29,6 +29,7 @@
 
 #include "dynconv_common.hpp"
 #include "dynconv_internal.hpp"
+#include "dynconv_lowrank_internal.hpp"
 
 namespace dynconv {
 
