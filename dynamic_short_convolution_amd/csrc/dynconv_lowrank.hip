@@ -575,9 +575,7 @@ struct LrBwdSmem {
   __align__(16) RT gl[4][Sh::S * Sh::GP];
 };
 
-// DX: dx is formed here (false when the bf16 fast dx kernel has produced it; the step
-// loop then ends with the range and the filters are not regenerated).
-template <bool FAST, typename ET, int W, int KS, bool DX>
+template <bool FAST, typename ET, int W, int KS>
 __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSmem<ET, W, KS>& sm) {
   using Sh = LrBwdShape<ET, W, KS>;
   using RT = typename Raw<ET>::type;
@@ -628,7 +626,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
   // regeneration operands, as in the forward
   typename Mfma<ET>::F32k afr[MT][KS];
   f32x4_t binit[MT];
-  if constexpr (DX) {
+  {
     const ET* U = static_cast<const ET*>(p.U);
     const ET* bias = static_cast<const ET*>(p.bias);
     const int m = n;
@@ -778,7 +776,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
   // one step: `cur` holds the loads of step t0 + S (in flight), `nxt` receives step t0 + 2S
   auto step = [&](int t0, Stage& cur, Stage& nxt, const int buf) {
     const int zbuf = ZB == 2 ? buf : 0;
-    const bool more = t0 + S - (DX ? W - 1 : 0) < t_end;
+    const bool more = t0 + S - (W - 1) < t_end;
     const bool do_g = t0 < t_end;
     prefetch(nxt, t0 + 2 * S);
     const ET* xt = &xl[buf][(HALO + n) * XP + xcol];   // x row of token t0 + n
@@ -787,7 +785,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const int ts = t0 + sub * TT;
-      const bool do_dx = DX && ts - (W - 1) < t_end;
+      const bool do_dx = ts - (W - 1) < t_end;
       if (!do_dx && !do_g) break;
       const int t = ts + n;
       float dyn[MT];
@@ -902,9 +900,9 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
     if (more) commit(cur, buf ^ 1, ZB == 2 ? (buf ^ 1) : 0, true);
     __syncthreads();
   };
-  for (int t0 = t_first; t0 - (DX ? W - 1 : 0) < t_end; t0 += 2 * S) {
+  for (int t0 = t_first; t0 - (W - 1) < t_end; t0 += 2 * S) {
     step(t0, stA, stB, 0);
-    if (!(t0 + S - (DX ? W - 1 : 0) < t_end)) break;
+    if (!(t0 + S - (W - 1) < t_end)) break;
     step(t0 + S, stB, stA, 1);
   }
 
@@ -942,24 +940,10 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
 
 // FAST: 16-byte loads throughout (the launch covers channel slices that lie inside D,
 // with aligned rows and R % 32 == 0); otherwise element loads where a chunk is partial.
-template <typename ET, int W, int KS, bool FAST, bool DX>
+template <typename ET, int W, int KS, bool FAST>
 __global__ __launch_bounds__(kBlockThreads) void k_lowrank_bwd(const LowRankParams p) {
   __shared__ LrBwdSmem<ET, W, KS> sm;
-  lowrank_bwd_body<FAST, ET, W, KS, DX>(p, sm);
-}
-
-// Launches the main backward kernel over channel slices cs0 .. cs0 + n - 1.
-template <typename ET, int W, int KS, bool FAST>
-hipError_t lr_bwd_main(const LowRankParams& q, int64_t blocks, bool dx, hipStream_t s) {
-  if constexpr (sizeof(ET) == 2 && W <= 4) {
-    if (!dx) {
-      hipLaunchKernelGGL((k_lowrank_bwd<ET, W, KS, FAST, false>), dim3(unsigned(blocks)), dim3(kBlockThreads), 0, s,
-                         q);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((k_lowrank_bwd<ET, W, KS, FAST, true>), dim3(unsigned(blocks)), dim3(kBlockThreads), 0, s, q);
-  return hipGetLastError();
+  lowrank_bwd_body<FAST, ET, W, KS>(p, sm);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1414,27 +1398,33 @@ hipError_t lr_fwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
 
 template <typename ET, int W, int KS>
 hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_t s) {
-  // dx: the bf16 fast kernel when it applies (then the main kernel forms only g, dU, db)
-  const bool dx_fast = lowrank_bwd_dx_fast_ok(p, W, sizeof(ET) == 2 ? DYNCONV_BF16 : DYNCONV_F32);
-  if (dx_fast) {
-    const hipError_t e = launch_lowrank_bwd_dx_fast(p, W, s);
-    if (e != hipSuccess) return e;
-  }
-  // main kernel: the channel slices inside D on the 16-byte path, the rest on the other
-  const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;
-  const int nfull = vec ? p.D / lowrank_bwd_dc(W, KS) : 0;
+  // bf16 fast path: dx, then the partial sums of dU and db, each by its own kernel;
+  // otherwise one main kernel (the channel slices inside D on the 16-byte path, the rest on
+  // the other)
+  const bool fast = lowrank_bwd_dx_fast_ok(p, W, sizeof(ET) == 2 ? DYNCONV_BF16 : DYNCONV_F32);
   LowRankParams q = p;
   const int64_t per_slice = int64_t(p.B) * pl.nTr;
-  if (nfull > 0) {
+  const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;
+  const int nfull = fast ? pl.nCs : vec ? p.D / lowrank_bwd_dc(W, KS) : 0;
+  if (fast) {
+    hipError_t e = launch_lowrank_bwd_dx_fast(p, W, s);
+    if (e != hipSuccess) return e;
+    e = launch_lowrank_bwd_gdu_fast(p, W, s);
+    if (e != hipSuccess) return e;
+  } else if (nfull > 0) {
     q.cs0 = 0;
     q.nCsL = nfull;
-    const hipError_t e = lr_bwd_main<ET, W, KS, true>(q, per_slice * nfull, !dx_fast, s);
+    hipLaunchKernelGGL((k_lowrank_bwd<ET, W, KS, true>), dim3(unsigned(per_slice * nfull)), dim3(kBlockThreads), 0, s,
+                       q);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (nfull < pl.nCs) {
     q.cs0 = nfull;
     q.nCsL = pl.nCs - nfull;
-    const hipError_t e = lr_bwd_main<ET, W, KS, false>(q, per_slice * q.nCsL, !dx_fast, s);
+    hipLaunchKernelGGL((k_lowrank_bwd<ET, W, KS, false>), dim3(unsigned(per_slice * q.nCsL)), dim3(kBlockThreads), 0,
+                       s, q);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // dz: token blocks inside T on the DMA path, the rest on the register path
@@ -1491,13 +1481,15 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
   const int DC = !bwd ? lowrank_fwd_dc(W, ks) : lowrank_bwd_dc(W, ks);
   pl.nCs = int((D + DC - 1) / DC);
   // About 1024 (forward) or 2048 (backward) workgroups, ranges in whole 16-token tiles.
-  // Where the bf16 fast dx kernel can serve the shape, the backward main kernel only forms
-  // g, dU and db: about 512 workgroups then, so that fewer float32 partial sums of dU are
-  // written and reduced (one per sequence at the pages' model shapes). The choice uses only
-  // what the workspace query knows; alignment may still send dx to the main kernel.
+  // Where the bf16 fast kernels can serve the backward, its partial sums of dU and db come
+  // from a kernel over 64-channel slices: about 512 workgroups then, so that fewer float32
+  // partial sums are written and reduced (two per sequence at the pages' model shapes).
+  // The choice uses only what the workspace query knows; if alignment then rules the fast
+  // kernels out, the main kernel runs with these token ranges instead.
   const bool lean = bwd && dt == DYNCONV_BF16 && H == 1 && W <= 4 && R % 32 == 0 && R != 96 && D % 64 == 0;
   const int64_t target = !bwd ? 1024 : lean ? 512 : 2048;
-  int64_t per_seq = (target + B * pl.nCs - 1) / (B * pl.nCs);
+  const int64_t slices = lean ? D / 64 : pl.nCs;  // the fast kernel's 64-channel slices
+  int64_t per_seq = (target + B * slices - 1) / (B * slices);
   const int64_t max_ranges = (T + TT - 1) / TT;
   if (per_seq > max_ranges) per_seq = max_ranges;
   if (per_seq < 1) per_seq = 1;

@@ -38,6 +38,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 using lds_void = __attribute__((address_space(3))) void;
 
 constexpr int kStep = 64;    // tokens per pipeline step
@@ -651,6 +652,333 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
+
+// Transposing LDS reads (ds_read_b64_tr_b16) of N 8-byte rows at 32-bit LDS byte offsets,
+// issued together and waited for inside the same asm block. They are written as asm
+// because the compiler places a full vmcnt wait (for every LDS DMA in flight, including
+// the next step's) in front of its own form of this read; here the DMA is waited for
+// explicitly at the step barrier. Outputs are early-clobber: a result that arrives must
+// not overwrite the address of a later read of the group.
+__device__ __forceinline__ void tr_read8(u32x2 (&o)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %9\n ds_read_b64_tr_b16 %2, %10\n"
+      "ds_read_b64_tr_b16 %3, %11\n ds_read_b64_tr_b16 %4, %12\n ds_read_b64_tr_b16 %5, %13\n"
+      "ds_read_b64_tr_b16 %6, %14\n ds_read_b64_tr_b16 %7, %15\n s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+__device__ __forceinline__ void tr_read9(u32x2 (&o)[9], const uint32_t (&a)[9]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %9\n ds_read_b64_tr_b16 %1, %10\n ds_read_b64_tr_b16 %2, %11\n"
+      "ds_read_b64_tr_b16 %3, %12\n ds_read_b64_tr_b16 %4, %13\n ds_read_b64_tr_b16 %5, %14\n"
+      "ds_read_b64_tr_b16 %6, %15\n ds_read_b64_tr_b16 %7, %16\n ds_read_b64_tr_b16 %8, %17\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(o[8])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]));
+}
+__device__ __forceinline__ void tr_read13(u32x2 (&o)[13], const uint32_t (&a)[13]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %13\n ds_read_b64_tr_b16 %1, %14\n ds_read_b64_tr_b16 %2, %15\n"
+      "ds_read_b64_tr_b16 %3, %16\n ds_read_b64_tr_b16 %4, %17\n ds_read_b64_tr_b16 %5, %18\n"
+      "ds_read_b64_tr_b16 %6, %19\n ds_read_b64_tr_b16 %7, %20\n ds_read_b64_tr_b16 %8, %21\n"
+      "ds_read_b64_tr_b16 %9, %22\n ds_read_b64_tr_b16 %10, %23\n ds_read_b64_tr_b16 %11, %24\n"
+      "ds_read_b64_tr_b16 %12, %25\n s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]),
+        "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]));
+}
+
+// 32-bit LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) unsigned char*)(p)));
+}
+
+// ---------------------------------------------------------------------------------
+// Backward filter gradient, k_lowrank_bwd_gdu_fast: per token range and 64-channel slice,
+// float32 partial sums of
+//   dU[r][g W + k] = sum_t z_t[r] g_t[g W + k],  db[g W + k] = sum_t g_t[g W + k],
+//   g_t[c W + k] = dy_t[c] x_{t-k}[c]
+// (the gradient of w = z U + b; g is the per-token filter gradient of eq. 2).
+// The contraction runs over tokens on the matrix cores with M = 16 channels of one tap,
+// N = 16 ranks and K = 32 tokens. Both operands come from LDS by transposing reads
+// (ds_read_b64_tr_b16), which hand lane i column i of 4 consecutive rows: the dy and x
+// columns of the lane's channel (x read 4 rows early and late, so each tap's shift is a
+// choice of registers) give g in the A layout directly, and the z columns give B. So g
+// never goes to LDS. x sits in a ring of 4 steps (its rows before a step are the previous
+// step's), dy and z in 3 stages each, all filled by LDS DMA two steps ahead; a row's
+// 16-byte chunks are rotated by 2 row so that the 4 rows of a transposing read hit
+// distinct banks.
+// ---------------------------------------------------------------------------------
+template <int KS>
+struct BwdGduFast {
+  static constexpr int CPR = 8, ROW = 128, STAGE = kStep * ROW;  // x, dy: 64 channels
+  static constexpr int ZCPR = 4 * KS, ZROW = 16 * ZCPR, ZSTAGE = kStep * ZROW;
+  static constexpr int XN = 4;   // x ring: the step, the previous one, two in flight
+  static constexpr int SN = 3;   // dy and z stages: the step and two in flight
+  static constexpr int D_OFF = XN * STAGE;
+  static constexpr int Z_OFF = D_OFF + SN * STAGE;
+  static constexpr int BYTES = Z_OFF + SN * ZSTAGE;
+  static constexpr int XI = 2, DI = 2, ZI = KS, ND = XI + DI + ZI;
+};
+
+template <int W, int KS>
+__global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParams p) {
+  using F = BwdGduFast<KS>;
+  constexpr int CPR = F::CPR, ROW = F::ROW, STAGE = F::STAGE, XN = F::XN;
+  constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, D_OFF = F::D_OFF, Z_OFF = F::Z_OFF;
+  constexpr int RT = 2 * KS;  // 16-rank tiles
+  constexpr int HR = W - 1;
+  __shared__ __align__(16) unsigned char smem[F::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = lane >> 4;
+  const int j = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int cs = int(lb % uint32_t(p.nCsL));
+  lb /= uint32_t(p.nCsL);
+  const int tr = int(lb % uint32_t(p.nTr));
+  const int b = int(lb / uint32_t(p.nTr));
+  const int c_base = cs * 64;
+  const int t_first = tr * p.Ltok;
+  const int t_end = min(p.T, t_first + p.Ltok);
+  const int nsteps = (t_end - t_first + kStep - 1) / kStep;
+  const char* xc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.x) + b * p.xs0 + c_base);
+  const char* dc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.dy) + b * p.dys0 + c_base);
+  const char* zc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.z) + b * p.zs0);
+
+  // ---- LDS DMA: per lane the byte offset of its source chunk from a step's first row ----
+  uint32_t xoff[2], doff[2], zoff[KS];
+  int arl[2], zrl[KS];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int rl = idx / CPR, pc = idx % CPR;
+    const int c = (pc - 2 * rl) & (CPR - 1);
+    arl[i] = rl;
+    xoff[i] = uint32_t(rl * int(p.xs1) + 8 * c) * 2u;
+    doff[i] = uint32_t(rl * int(p.dys1) + 8 * c) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < KS; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int rl = idx / ZCPR, pc = idx % ZCPR;
+    const int c = ((pc - 2 * rl) % ZCPR + ZCPR) % ZCPR;
+    zrl[i] = rl;
+    zoff[i] = uint32_t(rl * int(p.zs1) + 8 * c) * 2u;
+  }
+  auto issue = [&](int s, int t0) {
+    unsigned char* xs = smem + (s % XN) * STAGE;
+    unsigned char* ds = smem + D_OFF + (s % F::SN) * STAGE;
+    unsigned char* zs = smem + Z_OFF + (s % F::SN) * ZSTAGE;
+    if (t0 + kStep <= p.T) {
+      const int64_t o1 = int64_t(t0) * 2;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        dma16(xc + o1 * p.xs1 + xoff[i], xs + (wv + 4 * i) * 1024);
+        dma16(dc + o1 * p.dys1 + doff[i], ds + (wv + 4 * i) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < KS; ++i) dma16(zc + o1 * p.zs1 + zoff[i], zs + (wv + 4 * i) * 1024);
+    } else {
+      // rows past T - 1 read row T - 1; their dy is zeroed below
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t t = min(t0 + arl[i], p.T - 1) - arl[i];
+        dma16(xc + t * p.xs1 * 2 + xoff[i], xs + (wv + 4 * i) * 1024);
+        dma16(dc + t * p.dys1 * 2 + doff[i], ds + (wv + 4 * i) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        const int64_t t = min(t0 + zrl[i], p.T - 1) - zrl[i];
+        dma16(zc + t * p.zs1 * 2 + zoff[i], zs + (wv + 4 * i) * 1024);
+      }
+    }
+  };
+
+  // ---- the W-1 x rows before the range: the last rows of ring stage XN - 1 ----
+  if constexpr (HR > 0) {
+    unsigned char* hbase = smem + XN * STAGE - HR * ROW;
+    if (t_first > 0) {
+      if (wv == 0 && lane < HR * CPR) {
+        const int rl = kStep - HR + lane / CPR, pc = lane % CPR;
+        const int c = (pc - 2 * rl) & (CPR - 1);
+        dma16(xc + (int64_t(t_first - HR + lane / CPR) * p.xs1 + 8 * c) * 2, hbase);
+      }
+    } else if (tid < HR * ROW / 4) {
+      reinterpret_cast<uint32_t*>(hbase)[tid] = 0u;
+    }
+  }
+  issue(0, t_first);
+  if (nsteps > 1) issue(1, t_first + kStep);
+
+  // Transposing-read addresses. Lane (j, q) reads 8 bytes of row 8q + j/4 (+ 4), channel
+  // columns 16 wv + 4 (j % 4) .. + 3; lane i then holds column 16 wv + i of 4 rows.
+  const int trow = 8 * q + (j >> 2);
+  const int tch = 2 * wv + ((j & 3) >> 1);  // logical 16-byte chunk
+  const int thalf = 8 * (j & 1);
+  auto arow = [&](int row) { return row * ROW + ((tch + 2 * row) & (CPR - 1)) * 16 + thalf; };
+  // z: lane holds rank column 16 rt + i
+  auto zaddr = [&](int row, int rt) {
+    const int c = 2 * rt + ((j & 3) >> 1);
+    return row * ZROW + ((c + 2 * row) % ZCPR) * 16 + thalf;
+  };
+
+  f32x4_t dU[W][RT];
+#pragma unroll
+  for (int k = 0; k < W; ++k)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) dU[k][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float db[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) db[k] = 0.f;
+
+  const uint32_t lds0 = lds_addr(smem);
+  constexpr int NR = 5 + 2 * RT;  // transposing reads per K step: dy 2, x 3, z 2 per rank tile
+  auto bf = [](const u32x2& w, int e) {
+    return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+  };
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int t0 = t_first + s * kStep;
+    // this step's transfers were followed by the next step's, if there is one
+    if (s + 1 < nsteps) {
+      vm_wait_barrier<F::ND>();
+    } else {
+      vm_wait_barrier<0>();
+    }
+    if (s + 2 < nsteps) issue(s + 2, t0 + 2 * kStep);
+    const int ux = s % XN;
+    const uint32_t dsa = lds0 + D_OFF + (s % F::SN) * STAGE;
+    const uint32_t zsa = lds0 + Z_OFF + (s % F::SN) * ZSTAGE;
+    const bool partial = t0 + kStep > p.T;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int r0 = 32 * kk + trow;  // the lane's first row of this K step
+      // dy rows r0, r0 + 4; x rows r0 - 4, r0, r0 + 4 of the ring (rows before the stage
+      // are the previous one's); z rows r0, r0 + 4 of each rank tile
+      uint32_t a[NR];
+      a[0] = dsa + arow(r0);
+      a[1] = dsa + arow(r0 + 4);
+#pragma unroll
+      for (int h = 0; h < 3; ++h) {
+        const int xr = ux * kStep + r0 + 4 * (h - 1);
+        a[2 + h] = lds0 + arow(xr < 0 ? xr + XN * kStep : xr);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        a[5 + 2 * rt] = zsa + zaddr(r0, rt);
+        a[6 + 2 * rt] = zsa + zaddr(r0 + 4, rt);
+      }
+      u32x2 v[NR];
+      if constexpr (NR == 9) {
+        tr_read9(v, a);
+      } else if constexpr (NR == 13) {
+        tr_read13(v, a);
+      } else {
+        static_assert(NR == 21, "rank tiles");
+        uint32_t a1[13], a2[8];
+        u32x2 v1[13], v2[8];
+#pragma unroll
+        for (int i = 0; i < 13; ++i) a1[i] = a[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a2[i] = a[13 + i];
+        tr_read13(v1, a1);
+        tr_read8(v2, a2);
+#pragma unroll
+        for (int i = 0; i < 13; ++i) v[i] = v1[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[13 + i] = v2[i];
+      }
+      // lane i now holds, for its channel 16 wv + i (rank 16 rt + i for z), the rows
+      // r0 - 4 + e .. of each read, 4 per read
+      float dyv[8], xv[12];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dyv[e] = bf(v[0], e);
+        dyv[4 + e] = bf(v[1], e);
+        xv[e] = bf(v[2], e);
+        xv[4 + e] = bf(v[3], e);
+        xv[8 + e] = bf(v[4], e);
+      }
+      if (partial) {
+        const int tk = t0 + 32 * kk + 8 * q;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dyv[e] = tk + e < p.T ? dyv[e] : 0.f;
+      }
+      u16x8_t bz[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const u32x4 w = {v[5 + 2 * rt][0], v[5 + 2 * rt][1], v[6 + 2 * rt][0], v[6 + 2 * rt][1]};
+        bz[rt] = __builtin_bit_cast(u16x8_t, w);
+      }
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        float g[8];
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          g[e] = dyv[e] * xv[4 + e - k];
+          sum += g[e];
+        }
+        db[k] += sum;
+        const u32x4 w = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                         pack_bf16x2(g[6], g[7])};
+        const u16x8_t a16 = __builtin_bit_cast(u16x8_t, w);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) dU[k][rt] = mma32(a16, bz[rt], dU[k][rt]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+
+  // ---- partial sums of this (sequence, token range). Lane (n = j, q) holds rows 4q + i
+  // (channels) of rank column n for each tap and rank tile. They are staged in LDS (the
+  // stages are idle now) as rank rows of the slice's 64 W columns, so that each row goes
+  // to memory as one contiguous run of 64 W floats; a pitch of 64 W + 1 floats spreads
+  // the lanes' scattered writes over the banks. Up to 4 rank tiles at a time. ----
+  const int range = b * p.nTr + tr;
+  const int cw = c_base + 16 * wv;
+  constexpr int COLS = 64 * W;
+  constexpr int PITCH = COLS + 1;
+  constexpr int TPC = RT < 4 ? RT : 4;  // rank tiles per chunk
+  static_assert(16 * TPC * PITCH * 4 <= F::BYTES, "staging fits the stages");
+  float* st = reinterpret_cast<float*>(smem);
+  float* pdu = p.part_dU + int64_t(range) * p.R * p.J + int64_t(c_base) * W;
+#pragma unroll
+  for (int rt0 = 0; rt0 < RT; rt0 += TPC) {
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPC; ++t)
+#pragma unroll
+      for (int k = 0; k < W; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[(16 * t + j) * PITCH + (16 * wv + 4 * q + i) * W + k] = dU[k][rt0 + t][i];
+    __syncthreads();
+    // rows 16 rt0 .. 16 (rt0 + TPC) - 1, 4 floats per thread and pass
+    constexpr int PER_ROW = COLS / 4;
+#pragma unroll 4
+    for (int idx = tid; idx < 16 * TPC * PER_ROW; idx += 256) {
+      const int r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
+      const float* src = st + r * PITCH + c4;
+      const f32x4_t v = {src[0], src[1], src[2], src[3]};
+      *reinterpret_cast<f32x4_t*>(pdu + int64_t(16 * rt0 + r) * p.J + c4) = v;
+    }
+  }
+  if (p.part_db != nullptr) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      float v = db[k];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (q == 0) p.part_db[int64_t(range) * p.J + int64_t(cw + j) * W + k] = v;
+    }
+  }
+}
+
 template <int KS>
 using FwdCfg = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD>;
 
@@ -770,7 +1098,38 @@ bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   const int ks = p.R / 32;
   return dt == DYNCONV_BF16 && p.H == 1 && W >= 1 && W <= 4 && p.R % 32 == 0 && (ks == 1 || ks == 2 || ks == 4) &&
          p.D % 64 == 0 && p.act16 != 0 && p.z16 != 0 && (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
-         int64_t(kStep) * p.dys1 < (int64_t(1) << 30) && int64_t(kStep) * p.zs1 < (int64_t(1) << 30);
+         int64_t(kStep) * p.dys1 < (int64_t(1) << 30) && int64_t(kStep) * p.zs1 < (int64_t(1) << 30) &&
+         int64_t(kStep) * p.xs1 < (int64_t(1) << 30);
+}
+
+template <int W, int KS>
+hipError_t bwd_gdu_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<W, KS>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int W>
+hipError_t bwd_gdu_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  switch (p.R / 32) {
+    case 1: return bwd_gdu_inst<W, 1>(p, blocks, s);
+    case 2: return bwd_gdu_inst<W, 2>(p, blocks, s);
+    case 4: return bwd_gdu_inst<W, 4>(p, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, hipStream_t s) {
+  // token ranges as planned for the partial sums (Ltok, nTr), 64-channel slices
+  LowRankParams q = p;
+  q.nCsL = p.D / 64;
+  const int64_t blocks = int64_t(p.B) * p.nTr * q.nCsL;
+  switch (W) {
+    case 1: return bwd_gdu_ks<1>(q, blocks, s);
+    case 2: return bwd_gdu_ks<2>(q, blocks, s);
+    case 3: return bwd_gdu_ks<3>(q, blocks, s);
+    case 4: return bwd_gdu_ks<4>(q, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t s) {

@@ -72,6 +72,9 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t st
 // bf16 fast dx of the backward (same conditions, on dy and dx); it plans its own ranges.
 bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
 hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t stream);
+// bf16 fast g / dU / db partial sums (same conditions as the fast dx, on x too), over the
+// planned token ranges (Ltok, nTr) and 64-channel slices.
+hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, hipStream_t stream);
 
 dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   float* dU, float* db, hipStream_t stream);
