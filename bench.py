@@ -327,7 +327,7 @@ def run_cpu_baseline(min_seconds=10.0, max_seconds=30.0):
     xs, ws, dys = wl.x(), wl.w(), wl.dy()
     sec = 0.0
     passes = 0
-    while sec < min_seconds and passes < 4 * wl.B:
+    while sec < min_seconds and passes < 16 * wl.B:
         b = passes % wl.B
         x = synth.to_f64(xs[b : b + 1])
         w = synth.to_f64(ws[b : b + 1])
