@@ -212,6 +212,8 @@ ROWS = (
     "qkv_gqa_fused_bwd",
     "lowrank_r64_fwd",
     "lowrank_r64_bwd",
+    "decode_perchannel_b64",
+    "decode_lowrank_r64_b64",
 )
 
 
@@ -223,6 +225,26 @@ def make_row(name, device):
                                                dynconv_lowrank_bwd, dynconv_lowrank_bwd_workspace_size,
                                                dynconv_lowrank_fwd)
 
+    if name.startswith("decode"):
+        # one decoding step of 64 sequences at D = 2048, W = 4: x, filters (or z, U, b), the
+        # W-1 cached inputs read, y and one cache slot written
+        from dynamic_short_convolution_amd import dynconv_decode_step, dynconv_lowrank_decode_step, new_cache
+
+        B, D, W, R = 64, 2048, 4, 64
+        x = gen((B, D), 1.0, 6, "x", device)
+        cache = new_cache(B, D, W, torch.bfloat16, device)
+        cache.copy_(gen((B, W - 1, D), 1.0, 6, "c", device))
+        y = torch.empty_like(x)
+        io = (1 + (W - 1) + 1 + 1) * B * D * 2  # x, the W-1 cached inputs, y, one cache slot
+        if name == "decode_perchannel_b64":
+            w = gen((B, D, W), (1.0 / W) ** 0.5, 6, "w", device)
+            return (lambda: dynconv_decode_step(x, w, cache, 7, 1, out=y)), io + B * D * W * 2, None, \
+                f"decode step B{B} D{D} W{W} H1 bf16"
+        z = gen((B, R), 1.0, 6, "z", device)
+        U = gen((R, D * W), 0.1 / R**0.5, 6, "U", device)
+        b = gen((D * W,), 0.1**0.5, 6, "b", device)
+        return (lambda: dynconv_lowrank_decode_step(x, z, U, b, cache, 7, W, out=y)), \
+            io + B * R * 2 + R * D * W * 2 + D * W * 2, 2 * B * R * D * W, f"decode step B{B} D{D} W{W} R{R} bf16"
     if name.startswith("lowrank"):
         B, T, D, W, R = 8, 4096, 2048, 4, 64
         x = gen((B, T, D), 1.0, 4, "x", device)

@@ -2,15 +2,20 @@
 
 The Python surface mirrors the C entry points of include/dynconv.h:
 dynconv_fwd, dynconv_bwd, dynconv_lowrank_fwd, dynconv_lowrank_bwd (and the workspace
-queries). Importing this package does not load the library; the first call does, and
+queries), and for inference dynconv_cache_fill, dynconv_decode_step and
+dynconv_lowrank_decode_step (with new_cache for a zeroed rolling cache). Importing this package does not load the library; the first call does, and
 fails loudly if it has not been built.
 """
 from .ops import (  # noqa: F401
     dynconv_bwd,
     dynconv_bwd_workspace_size,
+    dynconv_cache_fill,
+    dynconv_decode_step,
     dynconv_fwd,
     dynconv_lowrank_bwd,
     dynconv_lowrank_bwd_workspace_size,
+    dynconv_lowrank_decode_step,
     dynconv_lowrank_fwd,
+    new_cache,
 )
 from ._lib import DynconvError, load  # noqa: F401

@@ -30,6 +30,9 @@ EXPORTS = (
     "dynconv_lowrank_fwd",
     "dynconv_lowrank_bwd",
     "dynconv_lowrank_bwd_workspace_size",
+    "dynconv_cache_fill",
+    "dynconv_decode_step",
+    "dynconv_lowrank_decode_step",
 )
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -58,6 +61,16 @@ _SIGNATURES = {
         ctypes.c_int,
     ),
     "dynconv_lowrank_bwd_workspace_size": ([_i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_int], _sz),
+    "dynconv_cache_fill": ([_vp, _i64p, _vp, _i64p, _i64, _i64, _i64, _i32, ctypes.c_int, _vp], ctypes.c_int),
+    "dynconv_decode_step": (
+        [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p, _i64, _i64, _i64, _i32, _i32, ctypes.c_int, _vp],
+        ctypes.c_int,
+    ),
+    "dynconv_lowrank_decode_step": (
+        [_vp, _i64p, _vp, _i64p, _vp, _i64, _vp, _vp, _i64p, _vp, _i64p, _i64, _i64, _i64, _i32, _i32, _i32,
+         ctypes.c_int, _vp],
+        ctypes.c_int,
+    ),
 }
 
 _lib = None

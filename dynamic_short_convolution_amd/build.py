@@ -20,6 +20,7 @@ SOURCES = [
     "dynconv_stream.hip",
     "dynconv_lowrank.hip",
     "dynconv_lowrank_fast.hip",
+    "dynconv_decode.hip",
 ]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated from ordinary float code.

@@ -2,6 +2,7 @@
 // kernel launchers. See include/dynconv.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include "dynconv_decode_internal.hpp"
 #include "dynconv_internal.hpp"
 #include "dynconv_lowrank_internal.hpp"
 
@@ -389,6 +390,122 @@ dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void*
   p.part_dU = reinterpret_cast<float*>(wsb + plan.ws_dU);
   p.part_db = db != nullptr ? reinterpret_cast<float*>(wsb + plan.ws_db) : nullptr;
   return launch_lowrank_bwd(p, plan, W, dtype, dU, db, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------
+// Inference: rolling cache of the last W-1 inputs, single-token decoding steps
+// ---------------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// A [B, W-1, D] cache (required when W > 1) and element alignment of every pointer.
+dynconv_status check_cache(const void* cache, const int64_t* cs, int32_t W, int eb) {
+  if (W == 1) return DYNCONV_OK;
+  if (cache == nullptr || cs == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (cs[2] != 1) return DYNCONV_ERR_UNSUPPORTED;
+  if (cs[0] < 0 || cs[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (!aligned(cache, eb)) return DYNCONV_ERR_UNSUPPORTED;
+  return DYNCONV_OK;
+}
+
+// A [B, D] row tensor with strides s[0..1].
+dynconv_status check_row(const void* p, const int64_t* s, int eb) {
+  if (p == nullptr || s == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (s[1] != 1) return DYNCONV_ERR_UNSUPPORTED;
+  if (s[0] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (!aligned(p, eb)) return DYNCONV_ERR_UNSUPPORTED;
+  return DYNCONV_OK;
+}
+
+DecodeParams decode_params(const void* x, const int64_t* xs, void* cache, const int64_t* cs, void* y,
+                           const int64_t* ys, int64_t t, int64_t B, int64_t D, int32_t W, int32_t H) {
+  DecodeParams p{};
+  p.x = x;
+  p.xs0 = xs[0];
+  p.cache = cache;
+  p.cs0 = W > 1 ? cs[0] : 0;
+  p.cs1 = W > 1 ? cs[1] : 0;
+  p.y = y;
+  p.ys0 = ys != nullptr ? ys[0] : 0;
+  p.t = t;
+  p.B = int32_t(B);
+  p.D = int32_t(D);
+  p.H = H;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_cache_fill(const void* x, const int64_t* xs, void* cache, const int64_t* cs, int64_t B,
+                                  int64_t T, int64_t D, int32_t W, dynconv_dtype dtype, void* stream) {
+  dynconv_status st = check_common(B, T, D, W, 1, dtype);
+  if (st != DYNCONV_OK) return st;
+  const int eb = elem_bytes(dtype);
+  if ((st = check_cache(cache, cs, W, eb)) != DYNCONV_OK) return st;
+  if (T > 0) {
+    if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
+    if (!aligned(x, eb)) return DYNCONV_ERR_UNSUPPORTED;
+    if (x == cache) return DYNCONV_ERR_INVALID_ARG;
+  }
+  if (W == 1 || B == 0 || D == 0) return DYNCONV_OK;
+  DecodeParams p = decode_params(x, xs != nullptr ? xs : cs, cache, cs, nullptr, nullptr, T, B, D, W, 1);
+  p.xs1 = (T > 0) ? xs[1] : 0;
+  return launch_cache_fill(p, W, dtype, static_cast<hipStream_t>(stream));
+}
+
+dynconv_status dynconv_decode_step(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                   void* cache, const int64_t* cs, void* y, const int64_t* ys, int64_t t,
+                                   int64_t B, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* stream) {
+  dynconv_status st = check_common(B, 1, D, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  const int eb = elem_bytes(dtype);
+  if (t < 0) return DYNCONV_ERR_INVALID_ARG;
+  if ((st = check_row(x, xs, eb)) != DYNCONV_OK) return st;
+  if ((st = check_row(y, ys, eb)) != DYNCONV_OK) return st;
+  if ((st = check_cache(cache, cs, W, eb)) != DYNCONV_OK) return st;
+  if (w == nullptr || ws == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (ws[2] != 1 || ws[1] != W || ws[0] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (!aligned(w, eb)) return DYNCONV_ERR_UNSUPPORTED;
+  if (y == x || y == w || (W > 1 && (y == cache || cache == x || cache == w))) return DYNCONV_ERR_INVALID_ARG;
+  if (B == 0 || D == 0) return DYNCONV_OK;
+  DecodeParams p = decode_params(x, xs, cache, cs, y, ys, t, B, D, W, H);
+  p.w = w;
+  p.ws0 = ws[0];
+  return launch_decode_step(p, W, dtype, static_cast<hipStream_t>(stream));
+}
+
+dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                           const void* U, int64_t ldu, const void* bias, void* cache,
+                                           const int64_t* cs, void* y, const int64_t* ys, int64_t t, int64_t B,
+                                           int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                           void* stream) {
+  dynconv_status st = check_common(B, 1, D, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  const int eb = elem_bytes(dtype);
+  if (t < 0 || R < 1) return DYNCONV_ERR_INVALID_ARG;
+  if (R > 128 || H != 1) return DYNCONV_ERR_UNSUPPORTED;
+  if ((st = check_row(x, xs, eb)) != DYNCONV_OK) return st;
+  if ((st = check_row(y, ys, eb)) != DYNCONV_OK) return st;
+  if ((st = check_row(z, zs, eb)) != DYNCONV_OK) return st;
+  if ((st = check_cache(cache, cs, W, eb)) != DYNCONV_OK) return st;
+  if (U == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (ldu < D * W) return DYNCONV_ERR_INVALID_ARG;
+  if (!aligned(U, eb) || (bias != nullptr && !aligned(bias, eb))) return DYNCONV_ERR_UNSUPPORTED;
+  if (y == x || y == z || y == U || (bias != nullptr && y == bias) ||
+      (W > 1 && (y == cache || cache == x || cache == z || cache == U)))
+    return DYNCONV_ERR_INVALID_ARG;
+  if (B == 0 || D == 0) return DYNCONV_OK;
+  DecodeParams p = decode_params(x, xs, cache, cs, y, ys, t, B, D, W, H);
+  p.z = z;
+  p.zs0 = zs[0];
+  p.U = U;
+  p.ldu = ldu;
+  p.bias = bias;
+  p.R = R;
+  return launch_lowrank_decode_step(p, W, dtype, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -136,3 +136,60 @@ def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = T
     )
     _lib.check("dynconv_lowrank_bwd", st)
     return dx, dz, dU, db
+
+
+# ----------------------------------------------------------------------------------
+# Inference: rolling cache of the last W-1 inputs, single-token decoding steps
+# ----------------------------------------------------------------------------------
+
+
+def new_cache(B: int, D: int, W: int, dtype, device) -> torch.Tensor | None:
+    """A zeroed [B, W-1, D] cache (None for W == 1)."""
+    if W == 1:
+        return None
+    return torch.zeros((B, W - 1, D), dtype=dtype, device=device)
+
+
+def dynconv_cache_fill(x, W: int, cache=None):
+    """Fills the cache with the last W-1 tokens of a prompt x [B,T,D] (zeros before t = 0)."""
+    B, T, D = x.shape
+    if cache is None:
+        cache = new_cache(B, D, W, x.dtype, x.device)
+    if cache is None:
+        return None
+    dev = _require_device(x, cache)
+    st = _lib.load().dynconv_cache_fill(_ptr(x), _lib.strides(x.stride()), _ptr(cache),
+                                        _lib.strides(cache.stride()), B, T, D, W, _dtype_code(x), _stream(dev))
+    _lib.check("dynconv_cache_fill", st)
+    return cache
+
+
+def dynconv_decode_step(x, w, cache, t: int, H: int = 1, out=None):
+    """y [B,D] of token t from x [B,D], its filters w [B,D/H,W] (or a static [D/H,W]) and
+    the cache of the previous W-1 inputs, which is updated in place."""
+    B, D = x.shape
+    W = w.shape[-1]
+    ws = [0, w.stride(0), w.stride(1)] if w.dim() == 2 else list(w.stride())
+    y = torch.empty_like(x) if out is None else out
+    dev = _require_device(x, w, y, cache)
+    cs = _lib.strides(cache.stride()) if cache is not None else None
+    st = _lib.load().dynconv_decode_step(_ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(ws), _ptr(cache),
+                                         cs, _ptr(y), _lib.strides(y.stride()), int(t), B, D, W, H, _dtype_code(x),
+                                         _stream(dev))
+    _lib.check("dynconv_decode_step", st)
+    return y
+
+
+def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None):
+    """y [B,D] of token t with filters z [B,R] U + bias generated on the GPU; the cache is
+    updated in place."""
+    B, D = x.shape
+    R = z.shape[-1]
+    y = torch.empty_like(x) if out is None else out
+    dev = _require_device(x, z, U, bias, y, cache)
+    cs = _lib.strides(cache.stride()) if cache is not None else None
+    st = _lib.load().dynconv_lowrank_decode_step(
+        _ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias),
+        _ptr(cache), cs, _ptr(y), _lib.strides(y.stride()), int(t), B, D, W, 1, R, _dtype_code(x), _stream(dev))
+    _lib.check("dynconv_lowrank_decode_step", st)
+    return y

@@ -138,6 +138,49 @@ dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void*
 size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
                                           dynconv_dtype dtype);
 
+/*
+ * Inference: decoding one token at a time (the reading note lists inference among the
+ * things it left unoptimised). A sequence keeps its last W-1 inputs in a rolling cache
+ *   cache [B, W-1, D] with strides cs[0..2] (cs[2] == 1), dtype `dtype`,
+ * where token s sits in slot s mod (W-1) and the slots of positions before 0 hold zeros
+ * (the zero padding before t = 0). The cache is read and written in place. W == 1 needs
+ * no cache (it may be NULL).
+ */
+
+/*
+ * After a prompt of T tokens (y from dynconv_fwd or dynconv_lowrank_fwd on x [B,T,D]):
+ * slot s mod (W-1) of each sequence receives x[b, s] for s = T-W+1 .. T-1, and zero for
+ * s < 0 (so T == 0 empties the cache). Decoding then continues at t = T.
+ */
+dynconv_status dynconv_cache_fill(const void* x, const int64_t* xs, void* cache, const int64_t* cs, int64_t B,
+                                  int64_t T, int64_t D, int32_t W, dynconv_dtype dtype, void* stream);
+
+/*
+ * One decoding step at token index t >= 0 (the same for every sequence of the batch):
+ *   y[b,d] = x[b,d] + sum_{k<W} w[b,g(d),k] * x_{t-k}[b,d],   x_{t-k} from the cache for k >= 1,
+ * after which x[b, :] is stored in slot t mod (W-1). Equal to row t of dynconv_fwd over the
+ * whole sequence.
+ *   x  [B, D] with strides xs[0..1] (xs[1] == 1)
+ *   w  [B, D/H, W] with strides ws[0..2] (ws[2] == 1, ws[1] == W), or a static filter
+ *      [D/H, W] given by ws[0] == 0
+ *   y  [B, D] with strides ys[0..1] (ys[1] == 1); y may not be x, w or the cache.
+ */
+dynconv_status dynconv_decode_step(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                   void* cache, const int64_t* cs, void* y, const int64_t* ys, int64_t t,
+                                   int64_t B, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* stream);
+
+/*
+ * Low-rank decoding step: the filters of the new token, w[b,g,k] = sum_r z[b,r] U[r, g*W+k]
+ * + bias[g*W+k], are formed on the GPU (float32) and applied as in dynconv_decode_step.
+ *   z  [B, R] with strides zs[0..1] (zs[1] == 1); U, ldu, bias as in dynconv_lowrank_fwd.
+ * H == 1, 1 <= R <= 128.
+ */
+dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                           const void* U, int64_t ldu, const void* bias, void* cache,
+                                           const int64_t* cs, void* y, const int64_t* ys, int64_t t, int64_t B,
+                                           int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

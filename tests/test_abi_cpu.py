@@ -134,3 +134,62 @@ def test_lowrank_validation(lib):
                                  S(800, 200, 1), P(0x990000), S(256, 64, 1), P(0x9a0000), None, 2, 4, 200, 4, 1, 64,
                                  BF16, P(0x9b0000), need - 1, None)
     assert st == WORKSPACE
+
+
+C = P(0xA00000)  # fake cache
+
+
+def dec(lib, x=X, xs=(200, 1), w=W_, ws=(200 * 4, 4, 1), cache=C, cs=(600, 200, 1), y=Y, ys=(200, 1), t=5, B=2,
+        D=200, W=4, H=1, dt=BF16):
+    return lib.dynconv_decode_step(x, S(*xs), w, S(*ws), cache, S(*cs) if cs else None, y, S(*ys), t, B, D, W, H, dt,
+                                   None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(t=-1), INVALID),
+        (dict(W=6), UNSUP),
+        (dict(x=P(0)), INVALID),
+        (dict(y=P(0)), INVALID),
+        (dict(w=P(0)), INVALID),
+        (dict(cache=P(0)), INVALID),
+        (dict(cs=None), INVALID),
+        (dict(cs=(600, 200, 2)), UNSUP),
+        (dict(xs=(200, 2)), UNSUP),
+        (dict(ws=(200 * 4, 3, 1)), UNSUP),  # taps of a group not contiguous
+        (dict(y=X), INVALID),
+        (dict(y=C), INVALID),
+        (dict(cache=X), INVALID),
+        (dict(x=P(0x10001)), UNSUP),  # bf16 needs element alignment
+        (dict(W=1, ws=(200, 1, 1), cache=P(0), cs=None, B=0), OK),  # no history: no cache needed
+        (dict(B=0), OK),
+        (dict(D=0), OK),
+    ],
+)
+def test_decode_validation(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_cache_fill_and_lowrank_decode_validation(lib):
+    fill = lambda **kw: lib.dynconv_cache_fill(kw.get("x", X), S(800, 200, 1), kw.get("cache", C), S(600, 200, 1), 2,
+                                               kw.get("T", 4), 200, kw.get("W", 4), BF16, None)
+    assert fill(W=0) == INVALID
+    assert fill(T=-1) == INVALID
+    assert fill(cache=P(0)) == INVALID
+    assert fill(x=P(0)) == INVALID
+
+    def lrd(**kw):
+        R = kw.get("R", 64)
+        return lib.dynconv_lowrank_decode_step(X, S(200, 1), kw.get("z", Z), S(R, 1), kw.get("U_", U), kw.get("ldu", 800),
+                                               None, C, S(600, 200, 1), kw.get("y", Y), S(200, 1), kw.get("t", 0), 2,
+                                               200, 4, kw.get("H", 1), R, BF16, None)
+
+    assert lrd(R=0) == INVALID
+    assert lrd(R=129) == UNSUP
+    assert lrd(H=2) == UNSUP
+    assert lrd(z=P(0)) == INVALID
+    assert lrd(U_=P(0)) == INVALID
+    assert lrd(ldu=100) == INVALID
+    assert lrd(y=Z) == INVALID
+    assert lrd(t=-3) == INVALID
