@@ -85,87 +85,158 @@ __global__ __launch_bounds__(256) void k_decode_step(const DecodeParams p) {
   decode_channel<ET, W>(p, b, d, w);
 }
 
-// Low-rank filters w[b,c,k] = sum_r z[b,r] U[r,cW+k] + bias[cW+k], generated per step.
-// A workgroup owns 32 channels (32 W filter columns) and up to 16 sequences. z of those
-// sequences and the workgroup's columns of U are staged in LDS as float32 (loads issued
-// in batches, so each batch costs one memory latency); two threads per column form it for
-// 8 sequences each from LDS; the filters go through LDS to the threads that apply them.
-constexpr int kDecCh = 32;
-constexpr int kDecSeq = 16;
-constexpr int kDecBatch = 32;  // independent loads per thread in flight while staging
+// Low-rank filters w[b,c,k] = sum_r z[b,r] U[r,cW+k] + bias[cW+k], generated per step on the
+// matrix cores. One wave owns 16 sequences x 16 channels. For each tap k the product of the
+// z rows and the columns cW+k of U is a 16x16 tile whose lane holds 4 sequences of a single
+// channel, so after the W products a lane holds every tap of its 4 (sequence, channel) pairs
+// and applies them from registers: no LDS and no barrier. Every global load of the wave (z,
+// U, bias, x and the cache) is issued before the first product, so a step costs one memory
+// latency. Lane (l, q) = (lane % 16, lane / 16) carries ranks 32s + 8q + e, e < 8, of rank
+// step s, for both operands.
+typedef __bf16 dec_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t dec_u16x8_t __attribute__((ext_vector_type(8)));
+typedef float dec_f32x8_t __attribute__((ext_vector_type(8)));
+typedef float dec_f32x4_t __attribute__((ext_vector_type(4)));
 
-// dst[i] = src(i) for i < n, element loads issued kDecBatch at a time per thread.
-template <typename F, typename G>
-__device__ __forceinline__ void stage(int n, F&& load, G&& store) {
-  for (int base = 0; base < n; base += 256 * kDecBatch) {
-    float v[kDecBatch];
+template <typename ET>
+struct DecMma;
+
+template <>
+struct DecMma<bf16_t> {
+  using RT = uint16_t;        // an element as stored
+  using Frag = dec_u16x8_t;   // 8 ranks of one operand row / column
+  static __device__ __forceinline__ float to_f(RT v) { return __uint_as_float(uint32_t(v) << 16); }
+  static __device__ __forceinline__ Frag load8(const RT* p) {
+    return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(p));
+  }
+  // 32 ranks in one 16x16x32 product.
+  static __device__ __forceinline__ dec_f32x4_t mma(const Frag& a, const Frag& b, dec_f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dec_bf16x8_t, a),
+                                                   __builtin_bit_cast(dec_bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct DecMma<float> {
+  using RT = float;
+  using Frag = dec_f32x8_t;
+  static __device__ __forceinline__ float to_f(RT v) { return v; }
+  static __device__ __forceinline__ Frag load8(const RT* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    return Frag{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  }
+  // 32 ranks in eight 16x16x4 products: product e takes rank 32s + 8q + e from lane group q.
+  static __device__ __forceinline__ dec_f32x4_t mma(const Frag& a, const Frag& b, dec_f32x4_t c) {
 #pragma unroll
-    for (int e = 0; e < kDecBatch; ++e) {
-      const int i = base + e * 256 + int(threadIdx.x);
-      v[e] = load(i < n ? i : n - 1);
-    }
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+  }
+};
+
+// W consecutive elements at p (one channel's taps); with VEC, W in {2, 4} is one vector load.
+template <typename RT, int W, bool VEC>
+__device__ __forceinline__ void load_taps(const RT* p, RT (&o)[W]) {
+  if constexpr (VEC && (W == 2 || W == 4) && W * sizeof(RT) <= 16) {
+    typedef RT V __attribute__((ext_vector_type(W)));
+    const V v = *reinterpret_cast<const V*>(p);
 #pragma unroll
-    for (int e = 0; e < kDecBatch; ++e) {
-      const int i = base + e * 256 + int(threadIdx.x);
-      if (i < n) store(i, v[e]);
-    }
+    for (int k = 0; k < W; ++k) o[k] = v[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < W; ++k) o[k] = p[k];
   }
 }
 
-template <typename ET, int W>
-__global__ __launch_bounds__(256) void k_lowrank_decode_step(const DecodeParams p) {
-  constexpr int HS = kDecSeq / 2;  // sequences per thread
-  constexpr int NC = kDecCh * W;   // filter columns of a workgroup
-  __shared__ __align__(16) float zs[kDecSeq][128];
-  __shared__ float us[128][NC];
-  __shared__ float wt[kDecSeq][NC];
-  const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * kDecCh;
-  const int b0 = blockIdx.y * kDecSeq;
-  const int nb = min(kDecSeq, p.B - b0);
-  const int ncol = min(kDecCh, p.D - c0) * W;
-  const int R4 = (p.R + 3) / 4 * 4;  // ranks padded with zeros to whole vectors
-  const int64_t j0 = int64_t(c0) * W;
-  stage(kDecSeq * R4,
-        [&](int i) {
-          const int bb = i / R4, r = i % R4;
-          return ldf<ET>(p.z, int64_t(b0 + min(bb, nb - 1)) * p.zs0 + min(r, p.R - 1));
-        },
-        [&](int i, float v) {
-          const int bb = i / R4, r = i % R4;
-          zs[bb][r] = (bb < nb && r < p.R) ? v : 0.f;
-        });
-  stage(p.R * ncol, [&](int i) { return ldf<ET>(p.U, int64_t(i / ncol) * p.ldu + j0 + i % ncol); },
-        [&](int i, float v) { us[i / ncol][i % ncol] = v; });
-  __syncthreads();
-  for (int task = tid; task < 2 * ncol; task += 256) {
-    const int col = task % ncol, half = task / ncol;
-    float acc[HS];
-    const float bv = p.bias != nullptr ? ldf<ET>(p.bias, j0 + col) : 0.f;
+// VEC: z rows, U rows and bias are aligned for vector loads and R % 8 == 0 (chosen on the
+// host, so that each variant's loads form one straight run before the first wait).
+template <typename ET, int W, int NK, bool VEC>
+__global__ __launch_bounds__(64) void k_lowrank_decode_step(const DecodeParams p) {
+  using M = DecMma<ET>;
+  using RT = typename M::RT;
+  using Frag = typename M::Frag;
+  constexpr int S = W - 1;
+  const int lane = threadIdx.x, l = lane & 15, q = lane >> 4;
+  const int c0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
+  const int ca = min(c0 + l, p.D - 1);  // channel of the lane's column (clamped; see stores)
+  const int R = p.R;
+  const RT* z = static_cast<const RT*>(p.z);
+  const RT* U = static_cast<const RT*>(p.U);
+
+  // The lane's pairs: sequences b0 + 4q + i, channel ca; x_t and the cached inputs.
+  int slot[W] = {};
+  if constexpr (S > 0) {
 #pragma unroll
-    for (int i = 0; i < HS; ++i) acc[i] = bv;
-    for (int r = 0; r < p.R; r += 4) {
-      float u[4];
+    for (int k = 1; k < W; ++k) slot[k] = int((p.t - k) % S + S) % S;
+  }
+  float xv[4], cv[4][W];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = r + e < p.R ? us[r + e][col] : 0.f;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t b = min(b0 + 4 * q + i, p.B - 1);
+    xv[i] = ldf<ET>(p.x, b * p.xs0 + ca);
 #pragma unroll
-      for (int i = 0; i < HS; ++i) {
-        const float4 zv = *reinterpret_cast<const float4*>(&zs[half * HS + i][r]);
-        acc[i] = fmaf(zv.x, u[0], fmaf(zv.y, u[1], fmaf(zv.z, u[2], fmaf(zv.w, u[3], acc[i]))));
+    for (int k = 1; k < W; ++k) cv[i][k] = ldf<ET>(p.cache, b * p.cs0 + slot[k] * p.cs1 + ca);
+  }
+
+  // z rows b0 + l (rows past B are clamped, computed and dropped), as the A operand.
+  const RT* zr = z + int64_t(min(b0 + l, p.B - 1)) * p.zs0;
+  Frag a[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    const int k0 = 32 * s + 8 * q;
+    if constexpr (VEC) {
+      const Frag v = M::load8(zr + min(k0, R - 8));
+      a[s] = k0 < R ? v : Frag{};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const RT v = zr[min(k0 + e, R - 1)];
+        a[s][e] = k0 + e < R ? v : RT(0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < HS; ++i) wt[half * HS + i][col] = acc[i];
   }
-  __syncthreads();
-  for (int i = tid; i < nb * kDecCh; i += 256) {
-    const int bb = i / kDecCh, cl = i % kDecCh;
-    const int d = c0 + cl;
-    if (d >= p.D) continue;
-    float w[W];
+
+  // Columns cW + k of U, ranks of step s, as the B operands of tap k.
+  Frag bt[NK][W];
 #pragma unroll
-    for (int k = 0; k < W; ++k) w[k] = wt[bb][cl * W + k];
-    decode_channel<ET, W>(p, b0 + bb, d, w);
+  for (int s = 0; s < NK; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 32 * s + 8 * q + e;
+      RT u[W];
+      load_taps<RT, W, VEC>(U + int64_t(min(r, R - 1)) * p.ldu + int64_t(ca) * W, u);
+#pragma unroll
+      for (int k = 0; k < W; ++k) bt[s][k][e] = r < R ? u[k] : RT(0);
+    }
+  }
+  RT bias[W];
+  if (p.bias != nullptr) {
+    load_taps<RT, W, VEC>(static_cast<const RT*>(p.bias) + int64_t(ca) * W, bias);
+  } else {
+#pragma unroll
+    for (int k = 0; k < W; ++k) bias[k] = RT(0);
+  }
+
+  // Every load is in flight before the first wait.
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Filters (float32, bias as the initial accumulator) and the convolution.
+  float y[4];
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    const float bk = M::to_f(bias[k]);
+    dec_f32x4_t acc = {bk, bk, bk, bk};
+#pragma unroll
+    for (int s = 0; s < NK; ++s) acc = M::mma(a[s], bt[s][k], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = k == 0 ? fmaf(acc[i], xv[i], xv[i]) : fmaf(acc[i], cv[i][k], y[i]);
+  }
+  if (c0 + l >= p.D) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = b0 + 4 * q + i;
+    if (b >= p.B) break;
+    stf<ET>(p.y, int64_t(b) * p.ys0 + ca, y[i]);
+    if constexpr (S > 0) stf<ET>(p.cache, int64_t(b) * p.cs0 + (p.t % S) * p.cs1 + ca, xv[i]);
   }
 }
 
@@ -214,11 +285,33 @@ dynconv_status launch_decode_step(const DecodeParams& p, int W, dynconv_dtype dt
 }
 
 dynconv_status launch_lowrank_decode_step(const DecodeParams& p, int W, dynconv_dtype dt, hipStream_t s) {
-  const dim3 grid(unsigned((p.D + kDecCh - 1) / kDecCh), unsigned((p.B + kDecSeq - 1) / kDecSeq));
+  const unsigned gy = unsigned((p.B + 15) / 16);
+  if (gy > 65535u) return DYNCONV_ERR_UNSUPPORTED;
+  const dim3 grid(unsigned((p.D + 15) / 16), gy);
+  const int nk = (p.R + 31) / 32;
+  const size_t eb = dt == DYNCONV_BF16 ? 2 : 4;
+  const auto al = [](const void* q, size_t a) { return reinterpret_cast<uintptr_t>(q) % a == 0; };
+  const bool vec = p.R % 8 == 0 && (p.zs0 * eb) % 16 == 0 && al(p.z, 16) && p.ldu % W == 0 && al(p.U, W * eb) &&
+                   (p.bias == nullptr || al(p.bias, W * eb));
   return status_of(by_w(W, dt, [&](auto et, auto wc) {
     using ET = decltype(et);
-    hipLaunchKernelGGL((k_lowrank_decode_step<ET, decltype(wc)::value>), grid, dim3(256), 0, s, p);
-    return hipGetLastError();
+    constexpr int WV = decltype(wc)::value;
+    const auto go = [&](auto nkc) {
+      constexpr int NK = decltype(nkc)::value;
+      if (vec) {
+        hipLaunchKernelGGL((k_lowrank_decode_step<ET, WV, NK, true>), grid, dim3(64), 0, s, p);
+      } else {
+        hipLaunchKernelGGL((k_lowrank_decode_step<ET, WV, NK, false>), grid, dim3(64), 0, s, p);
+      }
+      return hipGetLastError();
+    };
+    switch (nk) {
+      case 1: return go(std::integral_constant<int, 1>{});
+      case 2: return go(std::integral_constant<int, 2>{});
+      case 3: return go(std::integral_constant<int, 3>{});
+      case 4: return go(std::integral_constant<int, 4>{});
+      default: return hipErrorInvalidValue;
+    }
   }));
 }
 

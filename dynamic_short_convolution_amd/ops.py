@@ -96,10 +96,25 @@ def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True
     return (dx if need_dx else None), (dw if need_dw else None)
 
 
+def _check_lowrank_operands(x, z, U, bias, J: int):
+    """U is [R, J] with unit column stride (rows ldu = U.stride(0) apart), bias a contiguous
+    [J] vector or None, and every operand has the dtype of x."""
+    R = z.shape[-1]
+    if U.dim() != 2 or tuple(U.shape) != (R, J) or (J > 1 and U.stride(1) != 1):
+        raise ValueError(f"U must be [R, J] = [{R}, {J}] with unit column stride; got shape "
+                         f"{tuple(U.shape)} strides {tuple(U.stride())}")
+    if bias is not None and (bias.dim() != 1 or bias.numel() != J or (J > 1 and bias.stride(0) != 1)):
+        raise ValueError(f"bias must be a contiguous [{J}] vector")
+    for name, t in (("z", z), ("U", U), ("bias", bias)):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"{name} is {t.dtype} but x is {x.dtype}")
+
+
 def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None):
     """y = x + conv(x) with filters z U + bias generated on the GPU (never stored)."""
     B, T, D = x.shape
     R = z.shape[-1]
+    _check_lowrank_operands(x, z, U, bias, (D // H) * W)
     y = torch.empty_like(x) if out is None else out
     dev = _require_device(x, z, U, bias, y)
     lib = _lib.load()
@@ -120,6 +135,7 @@ def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = T
     B, T, D = x.shape
     R = z.shape[-1]
     J = (D // H) * W
+    _check_lowrank_operands(x, z, U, bias, J)
     dx = torch.empty_like(x)
     dz = torch.empty_like(z)
     dU = torch.empty((R, J), dtype=torch.float32, device=x.device)
@@ -185,6 +201,7 @@ def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None):
     updated in place."""
     B, D = x.shape
     R = z.shape[-1]
+    _check_lowrank_operands(x, z, U, bias, D * W)
     y = torch.empty_like(x) if out is None else out
     dev = _require_device(x, z, U, bias, y, cache)
     cs = _lib.strides(cache.stride()) if cache is not None else None

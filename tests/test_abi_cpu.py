@@ -193,3 +193,29 @@ def test_cache_fill_and_lowrank_decode_validation(lib):
     assert lrd(ldu=100) == INVALID
     assert lrd(y=Z) == INVALID
     assert lrd(t=-3) == INVALID
+
+
+def test_lowrank_bindings_reject_bad_operands():
+    """The Python bindings refuse a transposed U, a strided bias and mixed dtypes before any
+    device work (CPU tensors suffice: these checks come first)."""
+    import torch
+
+    from dynamic_short_convolution_amd import dynconv_lowrank_decode_step, dynconv_lowrank_fwd
+
+    B, T, D, W, R = 2, 3, 8, 4, 16
+    x = torch.zeros((B, T, D), dtype=torch.bfloat16)
+    z = torch.zeros((B, T, R), dtype=torch.bfloat16)
+    U = torch.zeros((R, D * W), dtype=torch.bfloat16)
+    b = torch.zeros((D * W,), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="unit column stride"):
+        dynconv_lowrank_fwd(x, z, torch.zeros((D * W, R), dtype=torch.bfloat16).t(), b, W)
+    with pytest.raises(ValueError, match=r"\[R, J\]"):
+        dynconv_lowrank_fwd(x, z, U[:, : D * W - 1], b, W)
+    with pytest.raises(ValueError, match="bias"):
+        dynconv_lowrank_fwd(x, z, U, torch.zeros((2 * D * W,), dtype=torch.bfloat16)[::2], W)
+    with pytest.raises(TypeError, match="U is torch.float32"):
+        dynconv_lowrank_fwd(x, z, U.float(), b, W)
+    with pytest.raises(RuntimeError, match="GPU only"):
+        dynconv_lowrank_fwd(x, z, U, b, W)
+    with pytest.raises(ValueError, match="unit column stride"):
+        dynconv_lowrank_decode_step(x[:, 0], z[:, 0], U.t().contiguous().t(), b, None, 0, W)

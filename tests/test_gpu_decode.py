@@ -55,7 +55,7 @@ def test_decode_matches_full_sequence(dtype, W, H, static, T0):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("W,R,T0", [(1, 16, 3), (3, 20, 0), (4, 64, 5), (5, 128, 2)])
+@pytest.mark.parametrize("W,R,T0", [(1, 16, 3), (2, 40, 1), (3, 20, 0), (4, 64, 5), (4, 96, 0), (5, 128, 2)])
 def test_lowrank_decode_matches_full_sequence(dtype, W, R, T0):
     B, Ttot, D = 19, 10, 136  # two groups of sequences, a partial group of channels
     seed = 900 + W + R + T0
@@ -84,6 +84,26 @@ def test_lowrank_decode_without_bias():
     for t in range(Ttot):
         yt = dynconv_lowrank_decode_step(x[:, t].cuda(), z[:, t].cuda(), U.cuda(), None, cache, t, W)
         assert_close(f"y[{t}]", yt, ref[:, t], torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W", [2, 4])
+def test_lowrank_decode_unaligned_operands(dtype, W):
+    """z rows, U and bias starting one element past a 16-byte boundary, U rows ldu = D*W + 4
+    apart: the element-wise load paths, against the same oracle."""
+    B, Ttot, D, R = 5, 4, 40, 48
+    x = synth.draw((B, Ttot, D), 1.0, 31 + W, "x", dtype)
+    zw = synth.draw((B, Ttot, R + 1), 1.0, 31 + W, "z", dtype)
+    Uw = synth.draw((R, D * W + 4), 0.3 / R**0.5, 31 + W, "U", dtype)
+    bw = synth.draw((D * W + 1,), 0.3, 31 + W, "b", dtype)
+    z, U, b = zw[:, :, 1:], Uw[:, 1 : 1 + D * W], bw[1:]
+    ref = lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W)
+    zg, Ug, bg = zw.cuda()[:, :, 1:], Uw.cuda()[:, 1 : 1 + D * W], bw.cuda()[1:]
+    assert Ug.stride(0) == D * W + 4 and Ug.data_ptr() % 16 != 0 and zg.data_ptr() % 16 != 0
+    cache = new_cache(B, D, W, TD[dtype], "cuda")
+    for t in range(Ttot):
+        yt = dynconv_lowrank_decode_step(x[:, t].cuda(), zg[:, t], Ug, bg, cache, t, W)
+        assert_close(f"y[{t}]", yt, ref[:, t], TD[dtype])
 
 
 def test_cache_fill_contents():
