@@ -29,7 +29,11 @@ Readings where the page leaves a step open (each also listed in the design notes
 * the filters carry no nonlinearity (affine generator), and the convolution itself
   has no bias;
 * the generator's input is the normalised block input, not X itself, so x and w are
-  independent inputs and dx has no path through w.
+  independent inputs and dx has no path through w;
+* packed sequences (several documents in one row; the RubiConv page's point that a
+  convolution must not read across a document start): an optional segment id per token,
+  seq_idx (B, T) of integers, and tap k of token t is present only when token t - k
+  carries the same id as token t. Without seq_idx every row is one document.
 
 Everything is float64; bfloat16 and float32 inputs are exact in float64. Arrays are
 processed one sequence (one b) at a time; no blocking, fusion or reordering beyond
@@ -56,8 +60,18 @@ def _filters_for_sequence(w: np.ndarray, b: int, D: int, H: int) -> np.ndarray:
     return np.repeat(w[b], H, axis=1)  # (T, D/H, W) -> (T, D, W)
 
 
-def conv_fwd(x, w, H: int = 1) -> np.ndarray:
-    """Forward of eq. 2 + eq. 3: y_t = x_t + sum_{k<W} w_k^{(t)} * x_{t-k}, zero for t-k < 0.
+def _same_segment(seq_idx, b: int, k: int, T: int):
+    """(T - k, 1) array: 1.0 where token t - k has the segment id of token t (t = k .. T-1),
+    else 0.0; all ones without seq_idx."""
+    if seq_idx is None:
+        return np.ones((T - k, 1))
+    s = np.asarray(seq_idx)[b]
+    return (s[k:] == s[: T - k]).astype(np.float64)[:, None]
+
+
+def conv_fwd(x, w, H: int = 1, seq_idx=None) -> np.ndarray:
+    """Forward of eq. 2 + eq. 3: y_t = x_t + sum_{k<W} w_k^{(t)} * x_{t-k}, zero for t-k < 0
+    (and, with seq_idx, for t-k in another segment than t).
 
     x: (B, T, D). w: (B, T, D/H, W) per-token filters, or (D/H, W) for a static filter
     (eq. 1). Returns y: (B, T, D) in float64.
@@ -73,19 +87,21 @@ def conv_fwd(x, w, H: int = 1) -> np.ndarray:
             if k >= T:
                 break
             # term k reads x_{t-k}; rows t < k have no term (zeros before t = 0)
+            m = _same_segment(seq_idx, b, k, T)
             if wf.ndim == 2:
-                y[b, k:, :] += wf[None, :, k] * x[b, : T - k, :]
+                y[b, k:, :] += m * wf[None, :, k] * x[b, : T - k, :]
             else:
-                y[b, k:, :] += wf[k:, :, k] * x[b, : T - k, :]
+                y[b, k:, :] += m * wf[k:, :, k] * x[b, : T - k, :]
     return y
 
 
-def conv_bwd(x, w, dy, H: int = 1):
-    """Gradients of <dy, y> for y = conv_fwd(x, w, H).
+def conv_bwd(x, w, dy, H: int = 1, seq_idx=None):
+    """Gradients of <dy, y> for y = conv_fwd(x, w, H, seq_idx).
 
     Since y is bilinear in (x, w):
-      dx_s = dy_s + sum_k w_k^{(s+k)} * dy_{s+k}            (terms with s + k < T),
-      dwfull[t, d, k] = dy_t[d] * x_{t-k}[d]               (zero for t - k < 0),
+      dx_s = dy_s + sum_k w_k^{(s+k)} * dy_{s+k}            (terms with s + k < T and,
+                                                            with seq_idx, s in the segment of s + k),
+      dwfull[t, d, k] = dy_t[d] * x_{t-k}[d]               (zero for t - k < 0 or across segments),
       dw[t, g, k] = sum over the H channels d of group g of dwfull[t, d, k];
     for a static filter, dw[g, k] is additionally summed over every (b, t).
     Returns (dx, dw) in float64, dw in the layout of w.
@@ -107,11 +123,12 @@ def conv_bwd(x, w, dy, H: int = 1):
         for k in range(W):
             if k >= T:
                 break
+            m = _same_segment(seq_idx, b, k, T)  # m[t - k]: tap k of token t present
             if wf.ndim == 2:
-                dx[b, : T - k, :] += wf[None, :, k] * dy[b, k:, :]
+                dx[b, : T - k, :] += m * wf[None, :, k] * dy[b, k:, :]
             else:
-                dx[b, : T - k, :] += wf[k:, :, k] * dy[b, k:, :]
-            dwf[k:, :, k] = dy[b, k:, :] * x[b, : T - k, :]
+                dx[b, : T - k, :] += m * wf[k:, :, k] * dy[b, k:, :]
+            dwf[k:, :, k] = m * dy[b, k:, :] * x[b, : T - k, :]
         dwg = dwf.reshape(T, G, H, W).sum(axis=2)  # sum over the H channels of a group
         if w.ndim == 2:
             dw += dwg.sum(axis=0)
@@ -136,13 +153,13 @@ def lowrank_filters(z, U, bias, W: int) -> np.ndarray:
     return wf.reshape(B, T, J // W, W)
 
 
-def lowrank_fwd(x, z, U, bias, W: int, H: int = 1) -> np.ndarray:
+def lowrank_fwd(x, z, U, bias, W: int, H: int = 1, seq_idx=None) -> np.ndarray:
     """Low-rank form: filters z U + b (never stored by the kernel), then eq. 2 + eq. 3."""
-    return conv_fwd(x, lowrank_filters(z, U, bias, W), H)
+    return conv_fwd(x, lowrank_filters(z, U, bias, W), H, seq_idx)
 
 
-def lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1):
-    """Gradients of <dy, y> for y = lowrank_fwd(x, z, U, bias, W, H).
+def lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, seq_idx=None):
+    """Gradients of <dy, y> for y = lowrank_fwd(x, z, U, bias, W, H, seq_idx).
 
     With g_t = dw_t flattened to (D/H)*W columns (from conv_bwd):
       dz_t = g_t U^T,   dU = sum_t z_t^T g_t,   db = sum_t g_t.
@@ -151,7 +168,7 @@ def lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1):
     z = _f64(z)
     U = _f64(U)
     wf = lowrank_filters(z, U, bias, W)
-    dx, dw = conv_bwd(x, wf, dy, H)
+    dx, dw = conv_bwd(x, wf, dy, H, seq_idx)
     B, T, R = z.shape
     J = U.shape[1]
     g = dw.reshape(B * T, J)

@@ -568,3 +568,124 @@ def test_pins_reject_lowrank_mutants():
     taps = bias.reshape(D, W)
     ref = np.stack([np.convolve(x[0, :, d], taps[d])[:T] for d in range(D)], axis=1)
     assert not np.allclose(y[0] - x[0], ref, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------
+# packed sequences (segment ids): a row holding several documents must give, on each
+# document, exactly what that document gives alone as its own zero-padded sequence
+# ----------------------------------------------------------------------------------
+
+PACKED_DOCS = ([1, 4, 2, 6], [7, 1, 1, 4])  # per row; lengths 1 and 2 are shorter than W - 1
+
+
+def _packed_inputs(W, H, static, seed, D=8):
+    r = _rng(seed)
+    T = sum(PACKED_DOCS[0])
+    assert all(sum(d) == T for d in PACKED_DOCS)
+    B = len(PACKED_DOCS)
+    seq = np.zeros((B, T), dtype=np.int32)
+    for b, docs in enumerate(PACKED_DOCS):
+        seq[b] = np.repeat(np.arange(len(docs)) + 10 * b, docs)
+    x = r.standard_normal((B, T, D))
+    dy = r.standard_normal((B, T, D))
+    w = r.standard_normal((D // H, W) if static else (B, T, D // H, W))
+    return x, w, dy, seq
+
+
+def _doc_ranges(b):
+    s = 0
+    for n in PACKED_DOCS[b]:
+        yield s, s + n
+        s += n
+
+
+def pin_packed_fwd(fwd, W, H, static, seed):
+    x, w, _, seq = _packed_inputs(W, H, static, seed)
+    y = fwd(x, w, H, seq)
+    for b in range(x.shape[0]):
+        for s, e in _doc_ranges(b):
+            wd = w if static else w[b : b + 1, s:e]
+            if not np.array_equal(y[b, s:e], conv_fwd(x[b : b + 1, s:e], wd, H)[0]):
+                return False
+    return True
+
+
+def pin_packed_bwd(bwd, W, H, static, seed):
+    x, w, dy, seq = _packed_inputs(W, H, static, seed)
+    dx, dw = bwd(x, w, dy, H, seq)
+    dw_sum = np.zeros_like(w) if static else None
+    for b in range(x.shape[0]):
+        for s, e in _doc_ranges(b):
+            wd = w if static else w[b : b + 1, s:e]
+            rdx, rdw = conv_bwd(x[b : b + 1, s:e], wd, dy[b : b + 1, s:e], H)
+            if not np.array_equal(dx[b, s:e], rdx[0]):
+                return False
+            if static:
+                dw_sum += rdw
+            elif not np.array_equal(dw[b, s:e], rdw[0]):
+                return False
+    return (not static) or np.allclose(dw, dw_sum, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("H,static", [(1, False), (2, False), (1, True), (4, True)])
+def test_packed_equals_separate_documents(W, H, static):
+    assert pin_packed_fwd(conv_fwd, W, H, static, seed=40 + W)
+    assert pin_packed_bwd(conv_bwd, W, H, static, seed=50 + W)
+
+
+@pytest.mark.parametrize("W", [2, 4, 5])
+def test_packed_equals_separate_documents_lowrank(W):
+    r = _rng(60 + W)
+    B, T, D, R = 2, sum(PACKED_DOCS[0]), 6, 3
+    _, _, _, seq = _packed_inputs(W, 1, False, 61)
+    x, dy = r.standard_normal((B, T, D)), r.standard_normal((B, T, D))
+    z, U, bias = r.standard_normal((B, T, R)), r.standard_normal((R, D * W)), r.standard_normal(D * W)
+    y = lowrank_fwd(x, z, U, bias, W, 1, seq)
+    dx, dz, dU, db = lowrank_bwd(x, z, U, bias, dy, W, 1, seq)
+    sU, sb = np.zeros_like(dU), np.zeros_like(db)
+    for b in range(B):
+        for s, e in _doc_ranges(b):
+            args = (x[b : b + 1, s:e], z[b : b + 1, s:e], U, bias)
+            np.testing.assert_allclose(y[b, s:e], lowrank_fwd(*args, W)[0], rtol=1e-13, atol=1e-13)
+            rdx, rdz, rdU, rdb = lowrank_bwd(*args, dy[b : b + 1, s:e], W)
+            np.testing.assert_allclose(dx[b, s:e], rdx[0], rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(dz[b, s:e], rdz[0], rtol=1e-12, atol=1e-12)
+            sU += rdU
+            sb += rdb
+    np.testing.assert_allclose(dU, sU, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(db, sb, rtol=1e-12, atol=1e-12)
+
+
+def test_single_segment_equals_unpacked():
+    x, w, dy, _ = _packed_inputs(4, 2, False, 70)
+    seq = np.full(x.shape[:2], 3, dtype=np.int32)
+    assert np.array_equal(conv_fwd(x, w, 2, seq), conv_fwd(x, w, 2))
+    for a, b in zip(conv_bwd(x, w, dy, 2, seq), conv_bwd(x, w, dy, 2)):
+        assert np.array_equal(a, b)
+
+
+def _mut_packed_adjacent_only(x, w, H=1, seq_idx=None):
+    """Wrong: a tap is cut only when token t-1 (not t-k) is in another segment."""
+    x = np.asarray(x, float)
+    seq = np.asarray(seq_idx)
+    y = conv_fwd(x, w, H)
+    B, T, _ = x.shape
+    for b in range(B):
+        for t in range(1, T):
+            if seq[b, t] != seq[b, t - 1]:
+                # start of a segment: drop every tap of this token only
+                y[b, t] = conv_fwd(x[b : b + 1, t : t + 1], w if np.ndim(w) == 2 else w[b : b + 1, t : t + 1], H)[0, 0]
+    return y
+
+
+def _mut_packed_bwd_unmasked_dx(x, w, dy, H=1, seq_idx=None):
+    """Wrong: dw is masked but dx still collects the next segment's terms."""
+    _, dw = conv_bwd(x, w, dy, H, seq_idx)
+    dx, _ = conv_bwd(x, w, dy, H)
+    return dx, dw
+
+
+def test_pins_reject_packed_mutants():
+    assert not all(pin_packed_fwd(_mut_packed_adjacent_only, W, 1, False, 80 + W) for W in (3, 4))
+    assert not pin_packed_bwd(_mut_packed_bwd_unmasked_dx, 4, 1, False, 81)
