@@ -33,6 +33,11 @@ EXPORTS = (
     "dynconv_cache_fill",
     "dynconv_decode_step",
     "dynconv_lowrank_decode_step",
+    "dynconv_fwd_varlen",
+    "dynconv_bwd_varlen",
+    "dynconv_lowrank_fwd_varlen",
+    "dynconv_lowrank_bwd_varlen",
+    "dynconv_cache_fill_varlen",
 )
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -72,6 +77,18 @@ _SIGNATURES = {
         ctypes.c_int,
     ),
 }
+# The packed-sequence variants take (seq_idx, ss) after the filter (w, ws), after the
+# bias (low-rank), or after x (cache fill).
+_SIGNATURES["dynconv_fwd_varlen"] = (
+    _SIGNATURES["dynconv_fwd"][0][:4] + [_vp, _i64p] + _SIGNATURES["dynconv_fwd"][0][4:], ctypes.c_int)
+_SIGNATURES["dynconv_bwd_varlen"] = (
+    _SIGNATURES["dynconv_bwd"][0][:4] + [_vp, _i64p] + _SIGNATURES["dynconv_bwd"][0][4:], ctypes.c_int)
+_SIGNATURES["dynconv_lowrank_fwd_varlen"] = (
+    _SIGNATURES["dynconv_lowrank_fwd"][0][:7] + [_vp, _i64p] + _SIGNATURES["dynconv_lowrank_fwd"][0][7:], ctypes.c_int)
+_SIGNATURES["dynconv_lowrank_bwd_varlen"] = (
+    _SIGNATURES["dynconv_lowrank_bwd"][0][:7] + [_vp, _i64p] + _SIGNATURES["dynconv_lowrank_bwd"][0][7:], ctypes.c_int)
+_SIGNATURES["dynconv_cache_fill_varlen"] = (
+    _SIGNATURES["dynconv_cache_fill"][0][:2] + [_vp, _i64p] + _SIGNATURES["dynconv_cache_fill"][0][2:], ctypes.c_int)
 
 _lib = None
 

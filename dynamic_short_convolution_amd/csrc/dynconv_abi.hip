@@ -96,6 +96,15 @@ dynconv_status check_filter(const void* w, const int64_t* ws, int32_t W, int32_t
   return DYNCONV_OK;
 }
 
+// Segment ids of packed sequences: int32 [B,T] with strides ss[0..1] >= 0 (any strides,
+// read one id per token), 4-byte aligned.
+dynconv_status check_seg(const int32_t* seg, const int64_t* ss) {
+  if (seg == nullptr || ss == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (ss[0] < 0 || ss[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (!aligned(seg, 4)) return DYNCONV_ERR_UNSUPPORTED;
+  return DYNCONV_OK;
+}
+
 }  // namespace
 
 dynconv_status record_hip_error(hipError_t e) {
@@ -124,9 +133,13 @@ const char* dynconv_status_string(dynconv_status s) {
 
 int dynconv_last_hip_error(void) { return dynconv::last_hip_error(); }
 
-dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws, void* y,
-                           const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
-                           dynconv_dtype dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dynconv_status fwd_impl(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const int32_t* seg,
+                        const int64_t* ss, void* y, const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W,
+                        int32_t H, dynconv_dtype dtype, void* stream) {
   dynconv_status st = check_common(B, T, D, W, H, dtype);
   if (st != DYNCONV_OK) return st;
   if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
@@ -145,6 +158,11 @@ dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, cons
   p.x = x;
   p.w = w;
   p.out = y;
+  if (seg != nullptr) {
+    p.seg = seg;
+    p.ss0 = ss[0];
+    p.ss1 = ss[1];
+  }
   p.xs0 = xs[0];
   p.xs1 = xs[1];
   p.ws0 = ws[0];
@@ -166,6 +184,24 @@ dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, cons
   return launch_stream_fwd(p, plan, W, dtype, fi.is_static, static_cast<hipStream_t>(stream));
 }
 
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws, void* y,
+                           const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                           dynconv_dtype dtype, void* stream) {
+  return fwd_impl(x, xs, w, ws, nullptr, nullptr, y, ys, B, T, D, W, H, dtype, stream);
+}
+
+dynconv_status dynconv_fwd_varlen(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                  const int32_t* seq_idx, const int64_t* ss, void* y, const int64_t* ys, int64_t B,
+                                  int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* stream) {
+  const dynconv_status st = check_seg(seq_idx, ss);
+  if (st != DYNCONV_OK) return st;
+  return fwd_impl(x, xs, w, ws, seq_idx, ss, y, ys, B, T, D, W, H, dtype, stream);
+}
+
 size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int is_static,
                                   dynconv_dtype dtype) {
   if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK) return 0;
@@ -182,10 +218,14 @@ size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, in
   return best;
 }
 
-dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const void* dy,
-                           const int64_t* dys, void* dx, const int64_t* dxs, void* dw, const int64_t* dws, int64_t B,
-                           int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const int32_t* seg,
+                        const int64_t* ss, const void* dy, const int64_t* dys, void* dx, const int64_t* dxs, void* dw,
+                        const int64_t* dws, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   dynconv_status st = check_common(B, T, D, W, H, dtype);
   if (st != DYNCONV_OK) return st;
   if (dx == nullptr && dw == nullptr) return DYNCONV_ERR_INVALID_ARG;
@@ -233,6 +273,11 @@ dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, cons
   p.out = dx;
   p.dw = fi.is_static ? nullptr : dw;
   p.partial = partial;
+  if (seg != nullptr) {
+    p.seg = seg;
+    p.ss0 = ss[0];
+    p.ss1 = ss[1];
+  }
   p.xs0 = xs[0];
   p.xs1 = xs[1];
   p.ws0 = ws[0];
@@ -261,6 +306,29 @@ dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, cons
   p.nTb = plan.nTb;
   return launch_stream_bwd(p, plan, W, dtype, fi.is_static, fi.is_static ? static_cast<float*>(dw) : nullptr,
                            static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const void* dy,
+                           const int64_t* dys, void* dx, const int64_t* dxs, void* dw, const int64_t* dws, int64_t B,
+                           int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return bwd_impl(x, xs, w, ws, nullptr, nullptr, dy, dys, dx, dxs, dw, dws, B, T, D, W, H, dtype, workspace,
+                  workspace_bytes, stream);
+}
+
+dynconv_status dynconv_bwd_varlen(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                  const int32_t* seq_idx, const int64_t* ss, const void* dy, const int64_t* dys,
+                                  void* dx, const int64_t* dxs, void* dw, const int64_t* dws, int64_t B, int64_t T,
+                                  int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  const dynconv_status st = check_seg(seq_idx, ss);
+  if (st != DYNCONV_OK) return st;
+  return bwd_impl(x, xs, w, ws, seq_idx, ss, dy, dys, dx, dxs, dw, dws, B, T, D, W, H, dtype, workspace,
+                  workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -317,9 +385,14 @@ LowRankParams lowrank_params(const void* x, const int64_t* xs, const void* z, co
 
 extern "C" {
 
-dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
-                                   int64_t ldu, const void* bias, void* y, const int64_t* ys, int64_t B, int64_t T,
-                                   int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dynconv_status lowrank_fwd_impl(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                                int64_t ldu, const void* bias, const int32_t* seg, const int64_t* ss, void* y,
+                                const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                dynconv_dtype dtype, void* stream) {
   dynconv_status st = check_lowrank(x, xs, z, zs, U, ldu, B, T, D, W, H, R, dtype);
   if (st != DYNCONV_OK) return st;
   if ((st = check_act(y, ys, true)) != DYNCONV_OK) return st;
@@ -335,7 +408,32 @@ dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void*
   p.out = y;
   p.os0 = ys[0];
   p.os1 = ys[1];
+  if (seg != nullptr) {
+    p.seg = seg;
+    p.ss0 = ss[0];
+    p.ss1 = ss[1];
+  }
   return launch_lowrank_fwd(p, plan, W, dtype, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                                   int64_t ldu, const void* bias, void* y, const int64_t* ys, int64_t B, int64_t T,
+                                   int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype, void* stream) {
+  return lowrank_fwd_impl(x, xs, z, zs, U, ldu, bias, nullptr, nullptr, y, ys, B, T, D, W, H, R, dtype, stream);
+}
+
+dynconv_status dynconv_lowrank_fwd_varlen(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                          const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                          const int64_t* ss, void* y, const int64_t* ys, int64_t B, int64_t T,
+                                          int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                          void* stream) {
+  const dynconv_status st = check_seg(seq_idx, ss);
+  if (st != DYNCONV_OK) return st;
+  return lowrank_fwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, y, ys, B, T, D, W, H, R, dtype, stream);
 }
 
 size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
@@ -345,11 +443,16 @@ size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32
   return plan_lowrank(B, T, D, W, H, R, true, dtype).ws_total;
 }
 
-dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
-                                   int64_t ldu, const void* bias, const void* dy, const int64_t* dys, void* dx,
-                                   const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db, int64_t B,
-                                   int64_t T, int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dynconv_status lowrank_bwd_impl(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                                int64_t ldu, const void* bias, const int32_t* seg, const int64_t* ss, const void* dy,
+                                const int64_t* dys, void* dx, const int64_t* dxs, void* dz, const int64_t* dzs,
+                                float* dU, float* db, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                                int32_t R, dynconv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   dynconv_status st = check_lowrank(x, xs, z, zs, U, ldu, B, T, D, W, H, R, dtype);
   if (st != DYNCONV_OK) return st;
   if ((st = check_act(dy, dys, true)) != DYNCONV_OK) return st;
@@ -389,7 +492,38 @@ dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void*
   char* wsb = static_cast<char*>(workspace);
   p.part_dU = reinterpret_cast<float*>(wsb + plan.ws_dU);
   p.part_db = db != nullptr ? reinterpret_cast<float*>(wsb + plan.ws_db) : nullptr;
+  if (seg != nullptr) {
+    p.seg = seg;
+    p.ss0 = ss[0];
+    p.ss1 = ss[1];
+  }
   return launch_lowrank_bwd(p, plan, W, dtype, dU, db, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
+                                   int64_t ldu, const void* bias, const void* dy, const int64_t* dys, void* dx,
+                                   const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db, int64_t B,
+                                   int64_t T, int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return lowrank_bwd_impl(x, xs, z, zs, U, ldu, bias, nullptr, nullptr, dy, dys, dx, dxs, dz, dzs, dU, db, B, T, D,
+                          W, H, R, dtype, workspace, workspace_bytes, stream);
+}
+
+dynconv_status dynconv_lowrank_bwd_varlen(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                          const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                          const int64_t* ss, const void* dy, const int64_t* dys, void* dx,
+                                          const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db,
+                                          int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                          dynconv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  const dynconv_status st = check_seg(seq_idx, ss);
+  if (st != DYNCONV_OK) return st;
+  return lowrank_bwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, dy, dys, dx, dxs, dz, dzs, dU, db, B, T, D, W, H,
+                          R, dtype, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------
@@ -439,8 +573,13 @@ DecodeParams decode_params(const void* x, const int64_t* xs, void* cache, const 
 
 extern "C" {
 
-dynconv_status dynconv_cache_fill(const void* x, const int64_t* xs, void* cache, const int64_t* cs, int64_t B,
-                                  int64_t T, int64_t D, int32_t W, dynconv_dtype dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dynconv_status cache_fill_impl(const void* x, const int64_t* xs, const int32_t* seg, const int64_t* ss, void* cache,
+                               const int64_t* cs, int64_t B, int64_t T, int64_t D, int32_t W, dynconv_dtype dtype,
+                               void* stream) {
   dynconv_status st = check_common(B, T, D, W, 1, dtype);
   if (st != DYNCONV_OK) return st;
   const int eb = elem_bytes(dtype);
@@ -453,7 +592,29 @@ dynconv_status dynconv_cache_fill(const void* x, const int64_t* xs, void* cache,
   if (W == 1 || B == 0 || D == 0) return DYNCONV_OK;
   DecodeParams p = decode_params(x, xs != nullptr ? xs : cs, cache, cs, nullptr, nullptr, T, B, D, W, 1);
   p.xs1 = (T > 0) ? xs[1] : 0;
+  if (seg != nullptr && T > 0) {
+    p.seg = seg;
+    p.ss0 = ss[0];
+    p.ss1 = ss[1];
+  }
   return launch_cache_fill(p, W, dtype, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_cache_fill(const void* x, const int64_t* xs, void* cache, const int64_t* cs, int64_t B,
+                                  int64_t T, int64_t D, int32_t W, dynconv_dtype dtype, void* stream) {
+  return cache_fill_impl(x, xs, nullptr, nullptr, cache, cs, B, T, D, W, dtype, stream);
+}
+
+dynconv_status dynconv_cache_fill_varlen(const void* x, const int64_t* xs, const int32_t* seq_idx, const int64_t* ss,
+                                         void* cache, const int64_t* cs, int64_t B, int64_t T, int64_t D, int32_t W,
+                                         dynconv_dtype dtype, void* stream) {
+  const dynconv_status st = check_seg(seq_idx, ss);
+  if (st != DYNCONV_OK) return st;
+  return cache_fill_impl(x, xs, seq_idx, ss, cache, cs, B, T, D, W, dtype, stream);
 }
 
 dynconv_status dynconv_decode_step(const void* x, const int64_t* xs, const void* w, const int64_t* ws,

@@ -37,7 +37,9 @@ __device__ __forceinline__ void stf(void* p, int64_t i, float v) {
 }
 
 // Cache fill after a prompt of T = p.t tokens: slot m receives the prompt token s in
-// T-(W-1) .. T-1 with s mod (W-1) == m, or zero when s < 0. One thread per (b, m, d).
+// T-(W-1) .. T-1 with s mod (W-1) == m, or zero when s < 0. For a packed prompt, decoding
+// continues its last document, so tokens of other segments than token T-1 count as zero
+// too. One thread per (b, m, d).
 template <typename ET, int W>
 __global__ __launch_bounds__(256) void k_cache_fill(const DecodeParams p) {
   constexpr int S = W - 1;
@@ -48,7 +50,12 @@ __global__ __launch_bounds__(256) void k_cache_fill(const DecodeParams p) {
   const int b = int(idx / (int64_t(p.D) * S));
   const int64_t s0 = p.t - S;
   const int64_t s = s0 + (((m - s0) % S) + S) % S;
-  const float v = s >= 0 ? ldf<ET>(p.x, b * p.xs0 + s * p.xs1 + d) : 0.f;
+  bool keep = s >= 0;
+  if (keep && p.seg != nullptr) {
+    const int32_t* sg = p.seg + b * p.ss0;
+    keep = sg[s * p.ss1] == sg[(p.t - 1) * p.ss1];
+  }
+  const float v = keep ? ldf<ET>(p.x, b * p.xs0 + s * p.xs1 + d) : 0.f;
   stf<ET>(p.cache, b * p.cs0 + int64_t(m) * p.cs1 + d, v);
 }
 

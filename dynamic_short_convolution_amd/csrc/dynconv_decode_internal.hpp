@@ -20,6 +20,8 @@ struct DecodeParams {
   int64_t xs0, xs1, ws0, zs0, ldu, cs0, cs1, ys0;
   int64_t t;        // decoding step: index of the new token; cache fill: prompt length T
   int32_t B, D, H, R;
+  const int32_t* seg;  // cache fill of packed prompts: segment id per token [B,T] (ss0, ss1), or null
+  int64_t ss0, ss1;
 };
 
 dynconv_status launch_cache_fill(const DecodeParams& p, int W, dynconv_dtype dt, hipStream_t s);

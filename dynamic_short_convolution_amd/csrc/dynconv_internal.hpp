@@ -27,6 +27,8 @@ struct StreamParams {
   void* out;        // y (forward) or dx (backward, may be null)
   void* dw;         // per-token dw (backward, may be null)
   float* partial;   // static dw: per (b, time chunk) partial sums [B*nTw][G][W]
+  const int32_t* seg;  // packed sequences: segment id per token [B,T] (strides ss0, ss1), or null
+  int64_t ss0, ss1;
   int64_t xs0, xs1;
   int64_t ws0, ws1;
   int64_t dys0, dys1;

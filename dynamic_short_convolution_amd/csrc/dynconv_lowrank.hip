@@ -286,6 +286,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
   static_assert(DC % CE == 0 && RP % CE == 0, "tiles hold whole 16-byte chunks");
   __shared__ __align__(16) RT zl[TT * ZP];
   __shared__ __align__(16) ET xl[RING * XP];
+  __shared__ int sl[RING];  // segment ids of the ring's tokens (packed sequences)
 
   const LrBlock blk = lr_block(p);
   const int tid = threadIdx.x;
@@ -302,6 +303,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
   ET* y = static_cast<ET*>(p.out) + blk.b * p.os0;
   const bool act16 = p.act16 != 0;
   const bool z16 = p.z16 != 0;
+  // packed sequences: tap k of token t is present only when token t-k has t's segment id
+  const bool segs = p.seg != nullptr;
+  const int32_t* sgp = segs ? p.seg + blk.b * p.ss0 : nullptr;
 
   // A operands (U columns in the lane-run order above) and bias, once per workgroup.
   const int cw0 = c_base + wv * CPW;
@@ -338,7 +342,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
   // Staging of one tile: z rows (zero past the range / R) and x rows (zero past D); the
   // loads of tile i+1 are issued before tile i is computed.
   u32x4 zpre_s[1][ZCH], xpre_s[1][XCH];
+  int spre = INT32_MIN;
   auto prefetch = [&](u32x4 (&zpre)[ZCH], u32x4 (&xpre)[XCH], int t0) {
+    if (segs && tid < TT) spre = t0 + tid < t_end ? sgp[int64_t(t0 + tid) * p.ss1] : INT32_MIN;
 #pragma unroll
     for (int i = 0; i < ZCH; ++i) {
       const int ck = tid + i * kBlockThreads;
@@ -377,6 +383,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
         *reinterpret_cast<u32x4*>(&xl[ring_slot(t0 + row, t_first) * XP + (ck % (DC / CE)) * CE]) = xpre[i];
       }
     }
+    if (segs && tid < TT) sl[ring_slot(t0 + tid, t_first)] = spre;
   };
 
   // halo: the HALO tokens before the range
@@ -387,6 +394,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
     u32x4 v = {0u, 0u, 0u, 0u};
     if (t >= 0) v = load_chunk<ET>(x + int64_t(t) * p.xs1 + c_base, c, p.D - c_base, act16);
     *reinterpret_cast<u32x4*>(&xl[ring_slot(t, t_first) * XP + c]) = v;
+  }
+  if (segs && tid < HALO) {
+    const int t = t_first - HALO + tid;
+    sl[ring_slot(t, t_first)] = t >= 0 ? sgp[int64_t(t) * p.ss1] : INT32_MIN;
   }
   prefetch(zpre_s[0], xpre_s[0], t_first);
   commit(zpre_s[0], xpre_s[0], t_first);
@@ -416,6 +427,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
     }
     // conv + residual for token t0 + n, channels cw0 + lane_c .. + MT - 1
     const int t = t0 + n;
+    const int sc = segs ? sl[ring_slot(t, t_first)] : 0;
     float sum[MT], xcur[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -425,7 +437,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tap = 4 * (q % LPC) + i;
-      if (tap < W) {
+      if (tap < W && (!segs || sl[ring_slot(t - tap, t_first)] == sc)) {
         float xv[MT];
         lds_read_run<ET, MT>(&xl[ring_slot(t - tap, t_first) * XP + wv * CPW + lane_c], xv);
 #pragma unroll
@@ -573,6 +585,7 @@ struct LrBwdSmem {
   __align__(16) ET xl[2][Sh::XR * Sh::XP];
   __align__(16) ET dyl[2][Sh::XR * Sh::XP];
   __align__(16) RT gl[4][Sh::S * Sh::GP];
+  int sgl[2][Sh::XR];  // segment ids of the x / dy tile rows (packed sequences)
 };
 
 template <bool FAST, typename ET, int W, int KS>
@@ -622,6 +635,10 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
   const int cl = cw0 + lane_c;
   const int cl_count = p.D - cl;
   const int xcol = wv * CPW + lane_c;  // the lane's column in the x / dy tiles
+  // packed sequences: tap k of token t is present only when token t-k has t's segment id
+  const bool segs = p.seg != nullptr;
+  const int32_t* sgp = segs ? p.seg + blk.b * p.ss0 : nullptr;
+  auto& sgl = sm.sgl;
 
   // regeneration operands, as in the forward
   typename Mfma<ET>::F32k afr[MT][KS];
@@ -660,12 +677,14 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
     u32x4 z[ZS], x[XS], d[XS];
     uint32_t ok;  // bit i: z[i]; bit ZS + i: x[i]; bit ZS + XS + i: d[i]
     bool full;    // every row of the step lies in the range: no masks
+    int sid;      // segment id of token t0 + tid (tid < S)
   };
   static_assert(ZS + 2 * XS <= 32, "valid bits");
   auto prefetch = [&](Stage& st, int t0) {
     const ET* zb = z + int64_t(t0) * p.zs1;
     const ET* xb = x + int64_t(t0) * p.xs1;
     const ET* db_ = dy + int64_t(t0) * p.dys1;
+    if (segs && tid < S) st.sid = t0 + tid < t_need ? sgp[int64_t(t0 + tid) * p.ss1] : INT32_MIN;
     st.full = FAST && t0 + S <= t_end;
     if (FAST && t0 + S <= t_end) {
       // same loads as below with every chunk valid (z chunks are whole: R % 32 == 0)
@@ -732,6 +751,10 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
     } else {
       put(okm);
     }
+    if (segs) {
+      if (tid < S) sgl[buf][HALO + tid] = st.sid;
+      if (halo && tid < HALO) sgl[buf][tid] = sgl[buf ^ 1][tid + S];
+    }
     if (halo && tid < 2 * HCH) {
       const int k2 = tid % HCH;
       const int o = (k2 / (DC / CE)) * XP + (k2 % (DC / CE)) * CE;
@@ -742,6 +765,10 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
   };
 
   // first tile: its HALO rows come from memory (zeros before t = 0)
+  if (segs && tid < HALO) {
+    const int t = t_first - HALO + tid;
+    sgl[0][tid] = t >= 0 ? sgp[int64_t(t) * p.ss1] : INT32_MIN;
+  }
   if (tid < 2 * HCH) {
     const int k2 = tid % HCH;
     const int row = k2 / (DC / CE), c = (k2 % (DC / CE)) * CE, t = t_first - HALO + row;
@@ -788,6 +815,17 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
       const bool do_dx = ts - (W - 1) < t_end;
       if (!do_dx && !do_g) break;
       const int t = ts + n;
+      // presence of the lane's taps for token t (packed sequences)
+      bool tp[4];
+      {
+        const int* srow = &sgl[buf][HALO + sub * TT + n];
+        const int sc = segs ? srow[0] : 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tap = 4 * (q % LPC) + i;
+          tp[i] = !segs || tap >= W || srow[-tap] == sc;
+        }
+      }
       float dyn[MT];
       lds_read_run<ET, MT>(dyt + sub * TT * XP, dyn);
       if (do_dx) {
@@ -809,7 +847,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) a = Mfma<ET>::mma32(afr[mt][ks], bfr[ks], a);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) P[mt][i] = a[i] * dyn[mt];
+          for (int i = 0; i < 4; ++i) P[mt][i] = tp[i] ? a[i] * dyn[mt] : 0.f;
         }
         // dx for token s = t - (W - 1)
 #pragma unroll
@@ -861,7 +899,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
           if (LPC == 2 || tap < W) lds_read_run<ET, MT>(xt + (sub * TT - rtap) * XP, xr);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            g[mt][i] = tap < W ? dyg[mt] * xr[mt] : 0.f;
+            g[mt][i] = (tap < W && tp[i]) ? dyg[mt] * xr[mt] : 0.f;
             db[mt][i] += g[mt][i];
           }
         }
@@ -1084,6 +1122,17 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
   // every path
   prefetch(stA, CH);
   const int nt = wv * TT + n;  // the lane's token within the block
+  // packed sequences: taps of the lane's token that reach into another segment
+  bool tp[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) tp[k] = true;
+  if (p.seg != nullptr) {
+    const int32_t* sgp = p.seg + b * p.ss0;
+    const int t = min(tb0 + nt, p.T - 1);
+    const int cur = sgp[int64_t(t) * p.ss1];
+#pragma unroll
+    for (int k = 1; k < W; ++k) tp[k] = t - k < 0 || sgp[int64_t(t - k) * p.ss1] == cur;
+  }
   // chunk ci: `cur` holds chunk ci + 1 (in flight), `nxt` receives chunk ci + 2
   auto chunk = [&](int ci, Stage& cur, Stage& nxt) {
     const int buf = NBUF == 2 ? (ci & 1) : 0;
@@ -1103,7 +1152,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
         const uint32_t* xs = reinterpret_cast<const uint32_t*>(&xl[buf][(nt + HALO - k) * XP + q * CR]);
 #pragma unroll
         for (int i = 0; i < ND; i += 4) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(xs + i);
+          const u32x4 v = tp[k] ? *reinterpret_cast<const u32x4*>(xs + i) : u32x4{0u, 0u, 0u, 0u};
           xw[k][i] = v[0]; xw[k][i + 1] = v[1]; xw[k][i + 2] = v[2]; xw[k][i + 3] = v[3];
         }
       }
@@ -1401,7 +1450,8 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   // bf16 fast path: dx, then the partial sums of dU and db, each by its own kernel;
   // otherwise one main kernel (the channel slices inside D on the 16-byte path, the rest on
   // the other)
-  const bool fast = lowrank_bwd_dx_fast_ok(p, W, sizeof(ET) == 2 ? DYNCONV_BF16 : DYNCONV_F32);
+  // (packed sequences take the general kernels)
+  const bool fast = p.seg == nullptr && lowrank_bwd_dx_fast_ok(p, W, sizeof(ET) == 2 ? DYNCONV_BF16 : DYNCONV_F32);
   LowRankParams q = p;
   const int64_t per_slice = int64_t(p.B) * pl.nTr;
   const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;
@@ -1429,8 +1479,8 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   }
   // dz: token blocks inside T on the DMA path, the rest on the register path
   const int nblk = (p.T + kLowrankDzTokens - 1) / kLowrankDzTokens;
-  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.act16 != 0 && p.u16 != 0 && p.D % kLowrankDzChunk == 0 &&
-                   p.R % 32 == 0;
+  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.seg == nullptr && p.act16 != 0 && p.u16 != 0 &&
+                   p.D % kLowrankDzChunk == 0 && p.R % 32 == 0;
   const int nfb = dma ? p.T / kLowrankDzTokens : 0;
   if (nfb > 0) {
     q.tbb0 = 0;
@@ -1510,7 +1560,7 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
 
 dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   hipStream_t stream) {
-  if (lowrank_fwd_fast_ok(p, W, dt)) {
+  if (p.seg == nullptr && lowrank_fwd_fast_ok(p, W, dt)) {
     const hipError_t e = launch_lowrank_fwd_fast(p, W, stream);
     return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
   }

@@ -33,6 +33,8 @@ struct LowRankParams {
   int32_t act16;   // every activation-shaped tensor allows 16-byte vectors
   int32_t z16;     // z rows allow 16-byte vectors
   int32_t u16;     // U rows allow 16-byte vectors
+  const int32_t* seg;  // packed sequences: segment id per token [B,T] (strides ss0, ss1), or null
+  int64_t ss0, ss1;
 };
 
 // Low-rank forward tiling, shared by the planner and the kernel: each wave generates MT

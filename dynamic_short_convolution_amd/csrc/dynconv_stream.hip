@@ -182,7 +182,7 @@ template <bool CHANNEL_FASTEST>
 __device__ __forceinline__ WaveTile wave_tile(const StreamParams& p, int vec) {
   WaveTile wt;
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wv = threadIdx.x / kWaveSize;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   int tb, db;
   if constexpr (CHANNEL_FASTEST) {
@@ -206,10 +206,48 @@ __device__ __forceinline__ WaveTile wave_tile(const StreamParams& p, int vec) {
   return wt;
 }
 
+// Segment ids of packed sequences (several documents in one row): tap k of token t is
+// present only when token t-k carries the id of token t. Every lane of a wave is at the
+// same token, so the ids are wave-uniform and read through the scalar cache; before the
+// step at token t, id[j] holds the id of token t-1-j, the step shifts in the id of t.
+typedef const __attribute__((address_space(4))) int32_t* seg_ptr;
+
+template <int W, bool SEG>
+struct Segs {
+  int id[W > 1 ? W - 1 : 1];
+  seg_ptr base;
+  int64_t s1;
+  __device__ __forceinline__ void init(const StreamParams& p, int b, int t0) {
+    if constexpr (SEG) {
+      base = (seg_ptr)(p.seg + int64_t(b) * p.ss0);
+      s1 = p.ss1;
+#pragma unroll
+      for (int k = 1; k < W; ++k) id[k - 1] = t0 - k >= 0 ? load(t0 - k) : INT32_MIN;
+    }
+  }
+  __device__ __forceinline__ int load(int t) const {
+    if constexpr (SEG) return base[int64_t(t) * s1];
+    return 0;
+  }
+  // Presence of taps k = 1..W-1 of the token with id `cur` (m[0] is always true).
+  __device__ __forceinline__ void mask(int cur, bool (&m)[W]) const {
+    m[0] = true;
+#pragma unroll
+    for (int k = 1; k < W; ++k) m[k] = !SEG || id[k - 1] == cur;
+  }
+  __device__ __forceinline__ void push(int cur) {
+    if constexpr (SEG && W > 1) {
+#pragma unroll
+      for (int j = W - 2; j >= 1; --j) id[j] = id[j - 1];
+      id[0] = cur;
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------------
 // Forward: y_t = x_t + sum_k w_k^(t) x_{t-k}
 // ---------------------------------------------------------------------------------
-template <typename ET, int W, int VEC, bool PERCH, bool STATIC>
+template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool SEG>
 __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams p) {
   using XR = Words<ET, VEC>;
   using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
@@ -249,8 +287,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
 #pragma unroll
       for (int k = 0; k < W; ++k) wst[v][k] = tap_of(r, v, k, W, PERCH);
   }
+  Segs<W, SEG> sg;
+  sg.init(p, wt.b, wt.t0);
 
-  auto step = [&](int t, const XR& xr, const TR& wr) {
+  auto step = [&](int t, const XR& xr, const TR& wr, int sid) {
+    bool m[W];
+    sg.mask(sid, m);
+    sg.push(sid);
 #pragma unroll
     for (int k = W - 1; k >= 1; --k)
 #pragma unroll
@@ -264,7 +307,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         const float f = STATIC ? wst[PERCH ? v : 0][k] : tap_of(wr, v, k, W, PERCH);
-        acc = fmaf(f, xh[k][v], acc);
+        acc = fmaf(m[k] ? f : 0.f, xh[k][v], acc);
       }
       yv[v] = acc;
     }
@@ -275,20 +318,22 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
   for (; t + U <= wt.t1; t += U) {
     XR xr[U];
     TR wr[U];
+    int sid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       xr[u].load(xb + (t + u) * p.xs1);
       if constexpr (!STATIC) wr[u].load(wb + (t + u) * p.ws1);
+      sid[u] = sg.load(t + u);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(t + u, xr[u], wr[u]);
+    for (int u = 0; u < U; ++u) step(t + u, xr[u], wr[u], sid[u]);
   }
   for (; t < wt.t1; ++t) {
     XR xr;
     TR wr;
     xr.load(xb + t * p.xs1);
     if constexpr (!STATIC) wr.load(wb + t * p.ws1);
-    step(t, xr, wr);
+    step(t, xr, wr, sg.load(t));
   }
 }
 
@@ -307,7 +352,7 @@ __device__ __forceinline__ float group_sum(float v, int lanes) {
 // ALL: both dx and dw are wanted, known at compile time (static filters only: their
 // runtime output tests had split every batch of loads into branches, 91.5 -> 79.1 us at
 // B8 T4096 D2048 W3; the other forms measured no gain).
-template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL>
+template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL, bool SEG>
 __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams p) {
   using XR = Words<ET, VEC>;
   using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
@@ -355,6 +400,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       }
     }
   }
+  Segs<W, SEG> sg;
+  sg.init(p, wt.b, wt.t0);
   float wst[NC][W];
   float sdw[NC][W];  // static: per-lane partial sums of dw over the chunk
   if constexpr (STATIC) {
@@ -370,7 +417,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   }
 
   // One step at token t. MAIN: t inside the chunk (x is read, dw produced); HAVE: t < T.
-  auto step = [&](int t, bool main, bool have, const XR& dyr, const TR& wr, const XR& xr) {
+  auto step = [&](int t, bool main, bool have, const XR& dyr, const TR& wr, const XR& xr, int sid) {
+    bool m[W];
+    sg.mask(sid, m);
+    sg.push(sid);
     float dyv[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) dyv[v] = have ? dyr.at(v) : 0.f;
@@ -380,7 +430,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       for (int v = 0; v < VEC; ++v) {
         d[0][v] = dyv[v] * xr.at(v);
 #pragma unroll
-        for (int k = 1; k < W; ++k) d[k][v] = dyv[v] * xh[k - 1][v];
+        for (int k = 1; k < W; ++k) d[k][v] = m[k] ? dyv[v] * xh[k - 1][v] : 0.f;
       }
       if constexpr (PERCH) {
         if constexpr (STATIC) {
@@ -427,7 +477,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           const float fj = STATIC ? wst[PERCH ? v : 0][j] : (have ? tap_of(wr, v, j, W, PERCH) : 0.f);
-          acc[j - 1][v] = fmaf(fj, dyv[v], acc[j - 1][v]);
+          acc[j - 1][v] = fmaf(m[j] ? fj : 0.f, dyv[v], acc[j - 1][v]);
         }
       const int s = t - (W - 1);
       if (s >= wt.t0 && s < wt.t1) {
@@ -461,10 +511,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   struct Batch {
     XR x[U], dy[U];
     TR w[U];
+    int sid[U];
   };
   auto load_batch = [&](Batch& bt, int tb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      bt.sid[u] = sg.load(tb + u);
       bt.dy[u].load(dyb + (tb + u) * p.dys1);
       if (want_dw) {
         bt.x[u].load(xb + (tb + u) * p.xs1);
@@ -482,18 +534,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   };
   auto run_batch = [&](const Batch& bt, int tb) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(tb + u, true, true, bt.dy[u], bt.w[u], bt.x[u]);
+    for (int u = 0; u < U; ++u) step(tb + u, true, true, bt.dy[u], bt.w[u], bt.x[u], bt.sid[u]);
   };
   // The future halo: the W-1 tokens after the chunk complete its last dx rows. Their
   // loads are issued first, so that they are in by the end of the chunk.
   XR hx[WM], hdy[WM];
   TR hw[WM];
+  int hsid[WM];
   if (want_dx) {
 #pragma unroll
     for (int e = 0; e < W - 1; ++e) {
       const int tt = wt.t1 + e;
       hx[e].zero();
+      hsid[e] = INT32_MIN;
       if (tt < p.T) {
+        hsid[e] = sg.load(tt);
         hdy[e].load(dyb + tt * p.dys1);
         if constexpr (!STATIC) hw[e].load(wb + tt * p.ws1);
       } else {
@@ -538,13 +593,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
         wr.zero();
       }
     }
-    step(t, true, true, dyr, wr, xr);
+    step(t, true, true, dyr, wr, xr, sg.load(t));
   }
   if (want_dx) {
 #pragma unroll
     for (int e = 0; e < W - 1; ++e) {
       const int tt = wt.t1 + e;
-      step(tt, false, tt < p.T, hdy[e], hw[e], hx[e]);
+      step(tt, false, tt < p.T, hdy[e], hw[e], hx[e], hsid[e]);
     }
   }
   if constexpr (STATIC) {
@@ -597,15 +652,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials(const float* 
 
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC>
 hipError_t launch_fwd_inst(const StreamParams& p, const StreamPlan& plan, hipStream_t s) {
-  hipLaunchKernelGGL((k_stream_fwd<ET, W, VEC, PERCH, STATIC>), dim3(unsigned(plan.blocks)), dim3(kBlockThreads), 0,
-                     s, p);
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_stream_fwd<ET, W, VEC, PERCH, STATIC, true>), dim3(unsigned(plan.blocks)),
+                       dim3(kBlockThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_stream_fwd<ET, W, VEC, PERCH, STATIC, false>), dim3(unsigned(plan.blocks)),
+                       dim3(kBlockThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL = false>
 hipError_t launch_bwd_inst(const StreamParams& p, const StreamPlan& plan, hipStream_t s) {
-  hipLaunchKernelGGL((k_stream_bwd<ET, W, VEC, PERCH, STATIC, ALL>), dim3(unsigned(plan.blocks)),
-                     dim3(kBlockThreads), 0, s, p);
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_stream_bwd<ET, W, VEC, PERCH, STATIC, ALL, true>), dim3(unsigned(plan.blocks)),
+                       dim3(kBlockThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_stream_bwd<ET, W, VEC, PERCH, STATIC, ALL, false>), dim3(unsigned(plan.blocks)),
+                       dim3(kBlockThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -52,17 +52,28 @@ def filter_strides(w: torch.Tensor):
     return list(w.stride())
 
 
-def dynconv_fwd(x: torch.Tensor, w: torch.Tensor, H: int = 1, out: torch.Tensor | None = None) -> torch.Tensor:
-    """y = x + causal depthwise conv of x with per-token (or static) filters w."""
+def _seg_args(seq_idx, B: int, T: int):
+    """(pointer, strides) of packed-sequence segment ids: int32 [B, T] (any strides)."""
+    if seq_idx.dtype != torch.int32 or tuple(seq_idx.shape) != (B, T):
+        raise ValueError(f"seq_idx must be int32 [B, T] = [{B}, {T}]; got {seq_idx.dtype} {tuple(seq_idx.shape)}")
+    return _ptr(seq_idx), _lib.strides(seq_idx.stride())
+
+
+def dynconv_fwd(x: torch.Tensor, w: torch.Tensor, H: int = 1, out: torch.Tensor | None = None,
+                seq_idx: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x + causal depthwise conv of x with per-token (or static) filters w. With seq_idx
+    (int32 [B, T] segment ids of packed sequences) no tap crosses into another segment."""
     B, T, D = x.shape
     W = w.shape[-1]
     y = torch.empty_like(x) if out is None else out
-    dev = _require_device(x, w, y)
+    dev = _require_device(x, w, y, seq_idx)
     lib = _lib.load()
-    st = lib.dynconv_fwd(
-        _ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)), _ptr(y), _lib.strides(y.stride()),
-        B, T, D, W, H, _dtype_code(x), _stream(dev),
-    )
+    head = (_ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)))
+    tail = (_ptr(y), _lib.strides(y.stride()), B, T, D, W, H, _dtype_code(x), _stream(dev))
+    if seq_idx is None:
+        st = lib.dynconv_fwd(*head, *tail)
+    else:
+        st = lib.dynconv_fwd_varlen(*head, *_seg_args(seq_idx, B, T), *tail)
     _lib.check("dynconv_fwd", st)
     return y
 
@@ -71,8 +82,9 @@ def dynconv_bwd_workspace_size(B, T, D, W, H, is_static, dtype) -> int:
     return int(_lib.load().dynconv_bwd_workspace_size(B, T, D, W, H, int(bool(is_static)), _DTYPE[dtype]))
 
 
-def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True, dx=None, dw=None):
-    """(dx, dw) of <dy, dynconv_fwd(x, w, H)>; dw of a static filter is float32 [D/H, W]."""
+def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True, dx=None, dw=None, seq_idx=None):
+    """(dx, dw) of <dy, dynconv_fwd(x, w, H, seq_idx=seq_idx)>; dw of a static filter is
+    float32 [D/H, W]."""
     B, T, D = x.shape
     W = w.shape[-1]
     is_static = w.dim() == 2
@@ -81,17 +93,21 @@ def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True
     if need_dw and dw is None:
         dw = (torch.empty((D // H, W), dtype=torch.float32, device=x.device) if is_static
               else torch.empty((B, T, D // H, W), dtype=x.dtype, device=x.device))
-    dev = _require_device(x, w, dy, dx, dw)
+    dev = _require_device(x, w, dy, dx, dw, seq_idx)
     lib = _lib.load()
     ws_bytes = dynconv_bwd_workspace_size(B, T, D, W, H, is_static and need_dw, x.dtype)
     work = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device) if ws_bytes else None
-    st = lib.dynconv_bwd(
-        _ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)),
+    head = (_ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)))
+    tail = (
         _ptr(dy), _lib.strides(dy.stride()),
         _ptr(dx if need_dx else None), _lib.strides(dx.stride()) if need_dx else None,
         _ptr(dw if need_dw else None), _lib.strides(dw.stride()) if (need_dw and not is_static) else None,
         B, T, D, W, H, _dtype_code(x), _ptr(work), ws_bytes, _stream(dev),
     )
+    if seq_idx is None:
+        st = lib.dynconv_bwd(*head, *tail)
+    else:
+        st = lib.dynconv_bwd_varlen(*head, *_seg_args(seq_idx, B, T), *tail)
     _lib.check("dynconv_bwd", st)
     return (dx if need_dx else None), (dw if need_dw else None)
 
@@ -110,18 +126,21 @@ def _check_lowrank_operands(x, z, U, bias, J: int):
             raise TypeError(f"{name} is {t.dtype} but x is {x.dtype}")
 
 
-def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None):
-    """y = x + conv(x) with filters z U + bias generated on the GPU (never stored)."""
+def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None, seq_idx=None):
+    """y = x + conv(x) with filters z U + bias generated on the GPU (never stored); with
+    seq_idx (int32 [B, T]) no tap crosses into another segment."""
     B, T, D = x.shape
     R = z.shape[-1]
     _check_lowrank_operands(x, z, U, bias, (D // H) * W)
     y = torch.empty_like(x) if out is None else out
-    dev = _require_device(x, z, U, bias, y)
+    dev = _require_device(x, z, U, bias, y, seq_idx)
     lib = _lib.load()
-    st = lib.dynconv_lowrank_fwd(
-        _ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias),
-        _ptr(y), _lib.strides(y.stride()), B, T, D, W, H, R, _dtype_code(x), _stream(dev),
-    )
+    head = (_ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias))
+    tail = (_ptr(y), _lib.strides(y.stride()), B, T, D, W, H, R, _dtype_code(x), _stream(dev))
+    if seq_idx is None:
+        st = lib.dynconv_lowrank_fwd(*head, *tail)
+    else:
+        st = lib.dynconv_lowrank_fwd_varlen(*head, *_seg_args(seq_idx, B, T), *tail)
     _lib.check("dynconv_lowrank_fwd", st)
     return y
 
@@ -130,7 +149,8 @@ def dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dtype) -> int:
     return int(_lib.load().dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, _DTYPE[dtype]))
 
 
-def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = True, workspace=None):
+def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = True, workspace=None,
+                        seq_idx=None):
     """(dx, dz, dU, db) of <dy, dynconv_lowrank_fwd(...)>; dU and db are float32."""
     B, T, D = x.shape
     R = z.shape[-1]
@@ -140,16 +160,20 @@ def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = T
     dz = torch.empty_like(z)
     dU = torch.empty((R, J), dtype=torch.float32, device=x.device)
     db = torch.empty((J,), dtype=torch.float32, device=x.device) if need_db else None
-    dev = _require_device(x, z, U, bias, dy)
+    dev = _require_device(x, z, U, bias, dy, seq_idx)
     lib = _lib.load()
     ws_bytes = dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
-    st = lib.dynconv_lowrank_bwd(
-        _ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias),
+    head = (_ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias))
+    tail = (
         _ptr(dy), _lib.strides(dy.stride()), _ptr(dx), _lib.strides(dx.stride()), _ptr(dz), _lib.strides(dz.stride()),
         _ptr(dU), _ptr(db), B, T, D, W, H, R, _dtype_code(x), _ptr(workspace), ws_bytes, _stream(dev),
     )
+    if seq_idx is None:
+        st = lib.dynconv_lowrank_bwd(*head, *tail)
+    else:
+        st = lib.dynconv_lowrank_bwd_varlen(*head, *_seg_args(seq_idx, B, T), *tail)
     _lib.check("dynconv_lowrank_bwd", st)
     return dx, dz, dU, db
 
@@ -166,16 +190,23 @@ def new_cache(B: int, D: int, W: int, dtype, device) -> torch.Tensor | None:
     return torch.zeros((B, W - 1, D), dtype=dtype, device=device)
 
 
-def dynconv_cache_fill(x, W: int, cache=None):
-    """Fills the cache with the last W-1 tokens of a prompt x [B,T,D] (zeros before t = 0)."""
+def dynconv_cache_fill(x, W: int, cache=None, seq_idx=None):
+    """Fills the cache with the last W-1 tokens of a prompt x [B,T,D] (zeros before t = 0).
+    With seq_idx (int32 [B, T]) of a packed prompt, only the tokens of the last document
+    (the segment of token T-1) are kept."""
     B, T, D = x.shape
     if cache is None:
         cache = new_cache(B, D, W, x.dtype, x.device)
     if cache is None:
         return None
-    dev = _require_device(x, cache)
-    st = _lib.load().dynconv_cache_fill(_ptr(x), _lib.strides(x.stride()), _ptr(cache),
-                                        _lib.strides(cache.stride()), B, T, D, W, _dtype_code(x), _stream(dev))
+    dev = _require_device(x, cache, seq_idx)
+    lib = _lib.load()
+    if seq_idx is None:
+        st = lib.dynconv_cache_fill(_ptr(x), _lib.strides(x.stride()), _ptr(cache), _lib.strides(cache.stride()),
+                                    B, T, D, W, _dtype_code(x), _stream(dev))
+    else:
+        st = lib.dynconv_cache_fill_varlen(_ptr(x), _lib.strides(x.stride()), *_seg_args(seq_idx, B, T), _ptr(cache),
+                                           _lib.strides(cache.stride()), B, T, D, W, _dtype_code(x), _stream(dev))
     _lib.check("dynconv_cache_fill", st)
     return cache
 

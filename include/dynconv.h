@@ -181,6 +181,51 @@ dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, con
                                            int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
                                            void* stream);
 
+/*
+ * Packed sequences (several documents in one row of x): the same calls with a segment id
+ * per token,
+ *   seq_idx  int32 [B,T] with strides ss[0..1] >= 0 (elements), 4-byte aligned,
+ * after which tap k of token t is present only when seq_idx[b,t-k] == seq_idx[b,t]: a
+ * document never reads the inputs of the one before it (the RubiConv page's point that
+ * a convolution over packed sequences must not cross a document start). Documents are
+ * normally contiguous runs of equal ids; any ids work, the test is equality. Gradients
+ * are those of the masked forward. The low-rank calls take the general kernels (not the
+ * bf16 fast path). seq_idx == NULL returns DYNCONV_ERR_INVALID_ARG; every other argument
+ * is as in the call without the suffix.
+ */
+dynconv_status dynconv_fwd_varlen(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                  const int32_t* seq_idx, const int64_t* ss, void* y, const int64_t* ys, int64_t B,
+                                  int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* stream);
+
+dynconv_status dynconv_bwd_varlen(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                  const int32_t* seq_idx, const int64_t* ss, const void* dy, const int64_t* dys,
+                                  void* dx, const int64_t* dxs, void* dw, const int64_t* dws, int64_t B, int64_t T,
+                                  int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+dynconv_status dynconv_lowrank_fwd_varlen(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                          const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                          const int64_t* ss, void* y, const int64_t* ys, int64_t B, int64_t T,
+                                          int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                          void* stream);
+
+dynconv_status dynconv_lowrank_bwd_varlen(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                          const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                          const int64_t* ss, const void* dy, const int64_t* dys, void* dx,
+                                          const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db,
+                                          int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                          dynconv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
+ * Cache fill after a packed prompt: decoding continues the document of token T-1, so the
+ * slots of tokens with another segment id than token T-1 are zero (the start of that
+ * document). T == 0 empties the cache as in dynconv_cache_fill.
+ */
+dynconv_status dynconv_cache_fill_varlen(const void* x, const int64_t* xs, const int32_t* seq_idx, const int64_t* ss,
+                                         void* cache, const int64_t* cs, int64_t B, int64_t T, int64_t D, int32_t W,
+                                         dynconv_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

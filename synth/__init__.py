@@ -28,6 +28,7 @@ TENSOR_STREAM = {
     "b": 5,
     "w_static": 6,
     "probe": 7,
+    "seg": 8,
 }
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -51,6 +52,27 @@ def draw(shape, std: float, seed: int, name: str, dtype: str) -> torch.Tensor:
             a *= np.float32(std)
         out[s:e] = torch.from_numpy(a).to(DTYPES[dtype])
     return out.reshape(shape)
+
+
+def segments(B: int, T: int, mean_len: float, seed: int, first=()) -> torch.Tensor:
+    """Segment ids int32 [B, T] of packed sequences: each row is a run of documents whose
+    lengths are 1 + round(Exponential(mean_len - 1)) (the last one cut at T), with ids
+    0, 1, 2, ... along the row. ``first`` lists the lengths of row 0's leading documents
+    (e.g. 1 and 2 to put documents shorter than the filter at the start).
+    Generator: ``numpy.random.default_rng([seed, TENSOR_STREAM["seg"]])``."""
+    rng = np.random.default_rng([int(seed), TENSOR_STREAM["seg"]])
+    out = np.zeros((B, T), dtype=np.int32)
+    for b in range(B):
+        lens = list(first) if b == 0 else []
+        while sum(lens) < T:
+            lens.append(1 + int(round(rng.exponential(max(mean_len - 1.0, 1e-9)))))
+        pos = 0
+        for i, n in enumerate(lens):
+            out[b, pos : min(T, pos + n)] = i
+            pos += n
+            if pos >= T:
+                break
+    return torch.from_numpy(out)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

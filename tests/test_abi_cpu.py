@@ -219,3 +219,41 @@ def test_lowrank_bindings_reject_bad_operands():
         dynconv_lowrank_fwd(x, z, U, b, W)
     with pytest.raises(ValueError, match="unit column stride"):
         dynconv_lowrank_decode_step(x[:, 0], z[:, 0], U.t().contiguous().t(), b, None, 0, W)
+
+
+SEG = P(0x90000)
+
+
+def test_varlen_validation(lib):
+    """The packed-sequence calls check their segment ids first, then everything the call
+    without the suffix checks (B == 0 stays a no-op)."""
+    def fv(seg=SEG, ss=(4, 1), **kw):
+        x, y = kw.get("x", X), kw.get("y", Y)
+        return lib.dynconv_fwd_varlen(x, S(800, 200, 1), W_, S(800 * 4, 200 * 4, 4, 1), seg,
+                                      S(*ss) if ss is not None else None, y, S(800, 200, 1), kw.get("B", 2), 4, 200,
+                                      4, 1, BF16, None)
+
+    assert fv(seg=P(0)) == INVALID
+    assert fv(ss=None) == INVALID
+    assert fv(ss=(-4, 1)) == UNSUP
+    assert fv(seg=P(0x90002)) == UNSUP  # ids are 4-byte aligned
+    assert fv(x=P(0)) == INVALID
+    assert fv(y=X) == INVALID
+    assert fv(B=0) == OK
+    assert lib.dynconv_bwd_varlen(X, S(800, 200, 1), W_, S(800 * 4, 200 * 4, 4, 1), P(0), S(4, 1), DY,
+                                  S(800, 200, 1), DX, S(800, 200, 1), None, None, 2, 4, 200, 4, 1, BF16, None, 0,
+                                  None) == INVALID
+    assert lib.dynconv_bwd_varlen(X, S(800, 200, 1), W_, S(800 * 4, 200 * 4, 4, 1), SEG, S(4, 1), DY,
+                                  S(800, 200, 1), None, None, None, None, 2, 4, 200, 4, 1, BF16, None, 0,
+                                  None) == INVALID  # neither output
+    assert lib.dynconv_lowrank_fwd_varlen(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, P(0), S(4, 1), Y,
+                                          S(800, 200, 1), 2, 4, 200, 4, 1, 64, BF16, None) == INVALID
+    assert lib.dynconv_lowrank_fwd_varlen(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, SEG, S(4, -1), Y,
+                                          S(800, 200, 1), 2, 4, 200, 4, 1, 64, BF16, None) == UNSUP
+    assert lib.dynconv_lowrank_bwd_varlen(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, P(0), S(4, 1), DY,
+                                          S(800, 200, 1), DX, S(800, 200, 1), P(0x70000), S(256, 64, 1),
+                                          P(0x80000), None, 2, 4, 200, 4, 1, 64, BF16, None, 0, None) == INVALID
+    assert lib.dynconv_cache_fill_varlen(X, S(800, 200, 1), P(0), S(4, 1), P(0xa0000), S(600, 200, 1), 2, 4, 200,
+                                         4, BF16, None) == INVALID
+    assert lib.dynconv_cache_fill_varlen(X, S(800, 200, 1), SEG, S(4, 1), P(0xa0000), S(600, 200, 1), 0, 4, 200,
+                                         4, BF16, None) == OK
