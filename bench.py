@@ -214,12 +214,32 @@ ROWS = (
     "lowrank_r64_bwd",
     "decode_perchannel_b64",
     "decode_lowrank_r64_b64",
+    "packed_perchannel_h1_fwd",
+    "packed_perchannel_h1_bwd",
+    "packed_lowrank_r64_fwd",
+    "packed_lowrank_r64_bwd",
 )
+PACKED_MEAN_DOC = 512.0  # mean document length of the packed rows (tokens)
 
 
 def make_row(name, device):
-    """Returns (callable, algorithmic bytes, flops or None, description)."""
+    """Returns (callable, algorithmic bytes, flops or None, description).
+
+    packed_*: the same workload with rows packed from documents of mean length
+    PACKED_MEAN_DOC (int32 segment id per token, counted in the bytes)."""
     import torch
+
+    import synth
+
+    packed = name.startswith("packed_")
+    if packed:
+        name = name[len("packed_"):]
+
+    def segs(B, T):
+        return synth.segments(B, T, PACKED_MEAN_DOC, 9).to(device) if packed else None
+
+    def tag(desc, B, T):
+        return desc + (f" packed (mean document {PACKED_MEAN_DOC:.0f} tokens)" if packed else "")
 
     from dynamic_short_convolution_amd import (dynconv_bwd, dynconv_bwd_workspace_size, dynconv_fwd,
                                                dynconv_lowrank_bwd, dynconv_lowrank_bwd_workspace_size,
@@ -251,16 +271,18 @@ def make_row(name, device):
         z = gen((B, T, R), 1.0, 4, "z", device)
         U = gen((R, D * W), 0.1 / R**0.5, 4, "U", device)
         b = gen((D * W,), 0.1**0.5, 4, "b", device)
-        desc = f"B{B} T{T} D{D} W{W} R{R} bf16"
+        desc = tag(f"B{B} T{T} D{D} W{W} R{R} bf16", B, T)
+        seq = segs(B, T)
+        sb = 4 * B * T if packed else 0
         if name.endswith("fwd"):
             y = torch.empty_like(x)
-            return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, out=y)), lowrank_bytes(B, T, D, W, R), \
-                lowrank_flops(B, T, D, W, R), desc
+            return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, out=y, seq_idx=seq)), \
+                lowrank_bytes(B, T, D, W, R) + sb, lowrank_flops(B, T, D, W, R), desc
         dy = gen((B, T, D), 1.0, 4, "dy", device)
         ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, 1, R, torch.bfloat16), dtype=torch.uint8,
                          device=device)
-        return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, workspace=ws)), \
-            lowrank_bytes(B, T, D, W, R, fwd=False), lowrank_flops(B, T, D, W, R, fwd=False), desc
+        return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, workspace=ws, seq_idx=seq)), \
+            lowrank_bytes(B, T, D, W, R, fwd=False) + sb, lowrank_flops(B, T, D, W, R, fwd=False), desc
     if name.startswith("qkv"):
         B, T, D, W, H = 4, 8192, 3072, 4, 1
     else:
@@ -270,16 +292,19 @@ def make_row(name, device):
     static = name.startswith("static")
     x = gen((B, T, D), 1.0, 2, "x", device)
     w = gen((D // H, W) if static else (B, T, D // H, W), (1.0 / W) ** 0.5, 2, "w", device)
-    desc = f"B{B} T{T} D{D} W{W} H{H}{' static' if static else ''} bf16"
+    desc = tag(f"B{B} T{T} D{D} W{W} H{H}{' static' if static else ''} bf16", B, T)
+    seq = segs(B, T)
+    sb = 4 * B * T if packed else 0
     if name.endswith("fwd"):
         y = torch.empty_like(x)
-        return (lambda: dynconv_fwd(x, w, H, out=y)), stream_bytes(B, T, D, W, H, static=static, bwd=False), None, desc
+        return (lambda: dynconv_fwd(x, w, H, out=y, seq_idx=seq)), \
+            stream_bytes(B, T, D, W, H, static=static, bwd=False) + sb, None, desc
     dy = gen((B, T, D), 1.0, 2, "dy", device)
     dx = torch.empty_like(x)
     dw = torch.empty((D // H, W), dtype=torch.float32, device=device) if static else torch.empty_like(w)
     assert dynconv_bwd_workspace_size(B, T, D, W, H, static, torch.bfloat16) >= 0
-    return (lambda: dynconv_bwd(x, w, dy, H, dx=dx, dw=dw)), stream_bytes(B, T, D, W, H, static=static, fwd=False), \
-        None, desc
+    return (lambda: dynconv_bwd(x, w, dy, H, dx=dx, dw=dw, seq_idx=seq)), \
+        stream_bytes(B, T, D, W, H, static=static, fwd=False) + sb, None, desc
 
 
 def run_rows(args, device):

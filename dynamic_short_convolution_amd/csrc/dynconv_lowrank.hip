@@ -1352,6 +1352,22 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 #pragma unroll
   for (int j = 0; j < RTN; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Taps of the lane's token whose x row is zero: before t = 0 and, for packed
+  // sequences, in another segment. The ids are read (and waited for) before the first
+  // transfer, so that every wait below counts LDS transfers only.
+  bool tp[W];
+  const bool cut = tb0 < HALO || p.seg != nullptr;
+#pragma unroll
+  for (int k = 0; k < W; ++k) tp[k] = tb0 + nt - k >= 0;
+  if (p.seg != nullptr) {
+    const int32_t* sgp = p.seg + b * p.ss0;
+    const int t = tb0 + nt;  // whole token blocks inside T
+    const int cur = sgp[int64_t(t) * p.ss1];
+#pragma unroll
+    for (int k = 1; k < W; ++k) tp[k] = tp[k] && sgp[int64_t(max(t - k, 0)) * p.ss1] == cur;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
   issue(0, 0);
   issue(1, 1);
   for (int ci = 0; ci < nchunk; ++ci) {
@@ -1369,11 +1385,10 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + x_off[k]);
       xw[k][0] = v[0]; xw[k][1] = v[1]; xw[k][2] = v[2]; xw[k][3] = v[3];
     }
-    if (tb0 < HALO) {
-      // zeros before t = 0
+    if (cut) {
 #pragma unroll
       for (int k = 1; k < W; ++k)
-        if (tb0 + nt - k < 0) xw[k][0] = xw[k][1] = xw[k][2] = xw[k][3] = 0u;
+        if (!tp[k]) xw[k][0] = xw[k][1] = xw[k][2] = xw[k][3] = 0u;
     }
     float dyf[CR];
 #pragma unroll
@@ -1479,8 +1494,8 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   }
   // dz: token blocks inside T on the DMA path, the rest on the register path
   const int nblk = (p.T + kLowrankDzTokens - 1) / kLowrankDzTokens;
-  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.seg == nullptr && p.act16 != 0 && p.u16 != 0 &&
-                   p.D % kLowrankDzChunk == 0 && p.R % 32 == 0;
+  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.act16 != 0 && p.u16 != 0 && p.D % kLowrankDzChunk == 0 &&
+                   p.R % 32 == 0;
   const int nfb = dma ? p.T / kLowrankDzTokens : 0;
   if (nfb > 0) {
     q.tbb0 = 0;

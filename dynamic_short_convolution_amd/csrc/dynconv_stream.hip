@@ -182,7 +182,7 @@ template <bool CHANNEL_FASTEST>
 __device__ __forceinline__ WaveTile wave_tile(const StreamParams& p, int vec) {
   WaveTile wt;
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int wv = threadIdx.x / kWaveSize;
   uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   int tb, db;
   if constexpr (CHANNEL_FASTEST) {
@@ -208,8 +208,10 @@ __device__ __forceinline__ WaveTile wave_tile(const StreamParams& p, int vec) {
 
 // Segment ids of packed sequences (several documents in one row): tap k of token t is
 // present only when token t-k carries the id of token t. Every lane of a wave is at the
-// same token, so the ids are wave-uniform and read through the scalar cache; before the
-// step at token t, id[j] holds the id of token t-1-j, the step shifts in the id of t.
+// same token, so the ids are wave-uniform and read through the scalar cache (the sequence
+// and token indices are marked uniform here only: doing it for the wave index of every
+// kernel slowed the head-wise forward, 75 -> 83 us at H = 4); before the step at token t,
+// id[j] holds the id of token t-1-j, the step shifts in the id of t.
 typedef const __attribute__((address_space(4))) int32_t* seg_ptr;
 
 template <int W, bool SEG>
@@ -219,14 +221,14 @@ struct Segs {
   int64_t s1;
   __device__ __forceinline__ void init(const StreamParams& p, int b, int t0) {
     if constexpr (SEG) {
-      base = (seg_ptr)(p.seg + int64_t(b) * p.ss0);
+      base = (seg_ptr)(p.seg + int64_t(__builtin_amdgcn_readfirstlane(b)) * p.ss0);
       s1 = p.ss1;
 #pragma unroll
       for (int k = 1; k < W; ++k) id[k - 1] = t0 - k >= 0 ? load(t0 - k) : INT32_MIN;
     }
   }
   __device__ __forceinline__ int load(int t) const {
-    if constexpr (SEG) return base[int64_t(t) * s1];
+    if constexpr (SEG) return base[int64_t(__builtin_amdgcn_readfirstlane(t)) * s1];
     return 0;
   }
   // Presence of taps k = 1..W-1 of the token with id `cur` (m[0] is always true).
