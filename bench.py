@@ -214,6 +214,8 @@ ROWS = (
     "lowrank_r64_bwd",
     "decode_perchannel_b64",
     "decode_lowrank_r64_b64",
+    "perchannel_w8_fwd",
+    "perchannel_w8_bwd",
     "packed_perchannel_h1_fwd",
     "packed_perchannel_h1_bwd",
     "packed_lowrank_r64_fwd",
@@ -287,7 +289,7 @@ def make_row(name, device):
         B, T, D, W, H = 4, 8192, 3072, 4, 1
     else:
         B, T, D = 8, 4096, 2048
-        W = 3 if name.startswith("static") else 4
+        W = 3 if name.startswith("static") else 8 if name.startswith("perchannel_w8") else 4
         H = {"perchannel_h1": 1, "headwise_h4": 4, "headwise_h16": 16}.get(name.rsplit("_", 1)[0], 1)
     static = name.startswith("static")
     x = gen((B, T, D), 1.0, 2, "x", device)

@@ -47,7 +47,7 @@ dynconv_status check_common(int64_t B, int64_t T, int64_t D, int32_t W, int32_t 
   if (dt != DYNCONV_F32 && dt != DYNCONV_BF16) return DYNCONV_ERR_INVALID_ARG;
   if (B < 0 || T < 0 || D < 0) return DYNCONV_ERR_INVALID_ARG;
   if (W < 1 || H < 1) return DYNCONV_ERR_INVALID_ARG;
-  if (W > 5) return DYNCONV_ERR_UNSUPPORTED;
+  if (W > kMaxW) return DYNCONV_ERR_UNSUPPORTED;
   if (D > 0 && D % H != 0) return DYNCONV_ERR_INVALID_ARG;
   if (H > 1 && !is_pow2(H)) return DYNCONV_ERR_UNSUPPORTED;
   if (B > INT32_MAX || T > INT32_MAX || D > INT32_MAX) return DYNCONV_ERR_UNSUPPORTED;
@@ -345,6 +345,7 @@ dynconv_status check_lowrank(const void* x, const int64_t* xs, const void* z, co
   if (st != DYNCONV_OK) return st;
   if (R < 1) return DYNCONV_ERR_INVALID_ARG;
   if (R > 128) return DYNCONV_ERR_UNSUPPORTED;
+  if (W > kMaxLowrankW) return DYNCONV_ERR_UNSUPPORTED;
   if (H != 1) return DYNCONV_ERR_UNSUPPORTED;  // head-wise low-rank generation is not built
   if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
   if (z == nullptr || zs == nullptr) return DYNCONV_ERR_INVALID_ARG;
@@ -438,7 +439,7 @@ dynconv_status dynconv_lowrank_fwd_varlen(const void* x, const int64_t* xs, cons
 
 size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
                                           dynconv_dtype dtype) {
-  if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK || R < 1 || R > 128 || H != 1) return 0;
+  if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK || R < 1 || R > 128 || H != 1 || W > kMaxLowrankW) return 0;
   if (B == 0 || T == 0 || D == 0) return 0;
   return plan_lowrank(B, T, D, W, H, R, true, dtype).ws_total;
 }
@@ -647,7 +648,7 @@ dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, con
   if (st != DYNCONV_OK) return st;
   const int eb = elem_bytes(dtype);
   if (t < 0 || R < 1) return DYNCONV_ERR_INVALID_ARG;
-  if (R > 128 || H != 1) return DYNCONV_ERR_UNSUPPORTED;
+  if (R > 128 || H != 1 || W > kMaxLowrankW) return DYNCONV_ERR_UNSUPPORTED;
   if ((st = check_row(x, xs, eb)) != DYNCONV_OK) return st;
   if ((st = check_row(y, ys, eb)) != DYNCONV_OK) return st;
   if ((st = check_row(z, zs, eb)) != DYNCONV_OK) return st;

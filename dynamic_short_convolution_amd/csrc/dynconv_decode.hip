@@ -261,6 +261,9 @@ hipError_t by_w(int W, dynconv_dtype dt, F&& f) {
     case 3: return by_dtype<3>(dt, f);
     case 4: return by_dtype<4>(dt, f);
     case 5: return by_dtype<5>(dt, f);
+    case 6: return by_dtype<6>(dt, f);
+    case 7: return by_dtype<7>(dt, f);
+    case 8: return by_dtype<8>(dt, f);
     default: return hipErrorInvalidValue;
   }
 }
@@ -305,12 +308,16 @@ dynconv_status launch_lowrank_decode_step(const DecodeParams& p, int W, dynconv_
     constexpr int WV = decltype(wc)::value;
     const auto go = [&](auto nkc) {
       constexpr int NK = decltype(nkc)::value;
-      if (vec) {
-        hipLaunchKernelGGL((k_lowrank_decode_step<ET, WV, NK, true>), grid, dim3(64), 0, s, p);
+      if constexpr (WV > kMaxLowrankW) {
+        return hipErrorInvalidValue;  // rejected by the C ABI before this point
       } else {
-        hipLaunchKernelGGL((k_lowrank_decode_step<ET, WV, NK, false>), grid, dim3(64), 0, s, p);
+        if (vec) {
+          hipLaunchKernelGGL((k_lowrank_decode_step<ET, WV, NK, true>), grid, dim3(64), 0, s, p);
+        } else {
+          hipLaunchKernelGGL((k_lowrank_decode_step<ET, WV, NK, false>), grid, dim3(64), 0, s, p);
+        }
+        return hipGetLastError();
       }
-      return hipGetLastError();
     };
     switch (nk) {
       case 1: return go(std::integral_constant<int, 1>{});

@@ -10,6 +10,8 @@
 namespace dynconv {
 
 constexpr int kWaveSize = 64;
+constexpr int kMaxW = 8;         // widest filter (materialised, static and head-wise forms, decoding)
+constexpr int kMaxLowrankW = 5;  // widest filter of the low-rank form (its kernels keep a 4-token halo)
 constexpr int kBlockThreads = 256;  // 4 waves per workgroup
 
 // Lane mapping of the streaming kernels: each lane owns VEC consecutive channels and

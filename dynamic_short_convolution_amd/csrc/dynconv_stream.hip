@@ -255,7 +255,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
   using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
   constexpr int NC = PERCH ? VEC : 1;
   constexpr int LB = VEC * int(sizeof(ET)) + (STATIC ? 0 : TapsRaw<ET, W, VEC, PERCH>::bytes);
-  constexpr int U = DYNCONV_FWD_UNROLL > 0 ? DYNCONV_FWD_UNROLL : clamp_unroll(pow2_floor(DYNCONV_FWD_INFLIGHT / LB));
+  // (more than 32 bytes of loads per token, i.e. per-channel W = 8: 4 tokens, 305 -> 296 us)
+  constexpr int U = DYNCONV_FWD_UNROLL > 0 ? DYNCONV_FWD_UNROLL
+                    : LB > 32              ? 4
+                                           : clamp_unroll(pow2_floor(DYNCONV_FWD_INFLIGHT / LB));
   constexpr bool NT = false;
 
   const WaveTile wt = wave_tile<STATIC>(p, VEC);
@@ -560,7 +563,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
     }
   }
   int t = wt.t0;
-  if constexpr (DYNCONV_BWD_PIPELINE && (!PERCH || STATIC)) {
+  // (per-channel: only the widest filters gain, W = 8 713 -> 659 us; W = 4 loses 276 -> 279)
+  if constexpr (DYNCONV_BWD_PIPELINE && (!PERCH || STATIC || W >= 6)) {
     Batch b0, b1;
     if (t + U <= wt.t1) load_batch(b0, t);
     while (t + U <= wt.t1) {
@@ -704,6 +708,9 @@ hipError_t dispatch_w(const StreamParams& p, const StreamPlan& plan, int W, bool
     case 3: return dispatch_mode<BWD, ET, 3>(p, plan, st, s);
     case 4: return dispatch_mode<BWD, ET, 4>(p, plan, st, s);
     case 5: return dispatch_mode<BWD, ET, 5>(p, plan, st, s);
+    case 6: return dispatch_mode<BWD, ET, 6>(p, plan, st, s);
+    case 7: return dispatch_mode<BWD, ET, 7>(p, plan, st, s);
+    case 8: return dispatch_mode<BWD, ET, 8>(p, plan, st, s);
     default: return hipErrorInvalidValue;
   }
 }

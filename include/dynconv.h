@@ -31,7 +31,7 @@
  * - Arithmetic is float32 (products and sums), bf16 results are rounded to nearest even.
  * - Validation happens before any HIP call; invalid input returns a status, never aborts.
  *   B == 0 or T == 0 or D == 0 is a no-op returning DYNCONV_OK.
- * - Supported parameters: 1 <= W <= 5; H == 1 or H a power of two that divides D, with
+ * - Supported parameters: 1 <= W <= 8 (low-rank form: W <= 5); H == 1 or H a power of two that divides D, with
  *   H / VEC <= 64 where VEC = min(H, widest lane vector allowed by the alignment below /
  *   element size), i.e. H <= 512 (bf16) or 256 (float32) with 16-byte aligned
  *   activations; low-rank form: H == 1 and 1 <= R <= 128.

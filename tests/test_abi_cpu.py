@@ -64,7 +64,7 @@ def fwd(lib, x=X, xs=(800, 200, 1), w=W_, ws=(800 * 4, 200 * 4, 4, 1), y=Y, ys=(
         (dict(dt=7), INVALID),
         (dict(B=-1), INVALID),
         (dict(W=0), INVALID),
-        (dict(W=6), UNSUP),
+        (dict(W=9), UNSUP),
         (dict(H=0), INVALID),
         (dict(D=200, H=3), INVALID),  # 3 does not divide 200
         (dict(D=198, H=3, xs=(792, 198, 1), ys=(792, 198, 1), ws=(264 * 4, 66 * 4, 4, 1)), UNSUP),  # not a power of 2
@@ -110,7 +110,9 @@ def test_bwd_validation(lib):
 
 def test_workspace_queries(lib):
     assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 3, 1, 1, BF16) % 4 == 0
-    assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 6, 1, 1, BF16) == 0  # invalid W
+    assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 9, 1, 1, BF16) == 0  # invalid W
+    assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 8, 1, 1, BF16) > 0
+    assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 6, 1, 64, BF16) == 0  # low-rank: W <= 5
     n = lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 64, BF16)
     assert n >= 64 * 2048 * 4 * 4  # at least one float32 dU partial
     assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 0, BF16) == 0
@@ -129,6 +131,7 @@ def test_lowrank_validation(lib):
     assert lr_fwd(lib, y=X) == INVALID
     assert lr_fwd(lib, ldu=100) == INVALID  # row shorter than (D/H)*W
     assert lr_fwd(lib, H=2) == UNSUP  # head-wise low-rank is not built
+    assert lr_fwd(lib, W=6, ldu=1200) == UNSUP  # the low-rank kernels take W <= 5
     need = lib.dynconv_lowrank_bwd_workspace_size(2, 4, 200, 4, 1, 64, BF16)
     st = lib.dynconv_lowrank_bwd(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, DY, S(800, 200, 1), DX,
                                  S(800, 200, 1), P(0x990000), S(256, 64, 1), P(0x9a0000), None, 2, 4, 200, 4, 1, 64,
@@ -149,7 +152,7 @@ def dec(lib, x=X, xs=(200, 1), w=W_, ws=(200 * 4, 4, 1), cache=C, cs=(600, 200, 
     "kw,status",
     [
         (dict(t=-1), INVALID),
-        (dict(W=6), UNSUP),
+        (dict(W=9), UNSUP),
         (dict(x=P(0)), INVALID),
         (dict(y=P(0)), INVALID),
         (dict(w=P(0)), INVALID),

@@ -31,7 +31,7 @@ def _device():
 
 CASES = []
 for dtype in ("f32", "bf16"):
-    for W in (1, 2, 3, 4, 5):
+    for W in (1, 2, 3, 4, 5, 6, 7, 8):
         for H, static in ((1, False), (4, False), (1, True)):
             for T0 in (0, 2, 7):
                 CASES.append((dtype, W, H, static, T0))
@@ -110,7 +110,7 @@ def test_cache_fill_contents():
     """The ring after a prompt of T tokens holds x[T-W+1 .. T-1] in slots s mod (W-1), and
     zeros for positions before 0: an exact copy."""
     B, D = 2, 40
-    for W in (2, 4, 5):
+    for W in (2, 4, 5, 8):
         for T in (0, 1, 3, 9):
             x = synth.draw((B, max(T, 1), D), 1.0, 11 + T + W, "x", "bf16")[:, :T]
             cache = dynconv_cache_fill(x.cuda(), W).cpu()

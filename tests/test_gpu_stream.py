@@ -65,6 +65,15 @@ for dtype in ("f32", "bf16"):
                     SMALL.append((dtype, W, H, static, D, T))
 
 
+# the widest filters (W = 6..8; the pages' ablation reaches W = 6)
+for dtype in ("f32", "bf16"):
+    for W in (6, 7, 8):
+        for H in (1, 2, 4, 16):
+            for static in (False, True):
+                for T in (5, 333):
+                    SMALL.append((dtype, W, H, static, 200 if H == 1 else 640, T))
+
+
 @pytest.mark.parametrize("dtype,W,H,static,D,T", SMALL)
 def test_small_parity(dtype, W, H, static, D, T):
     _check_case(2, T, D, W, H, dtype, static, seed=W * 7 + H + T)

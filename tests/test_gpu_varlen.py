@@ -54,7 +54,7 @@ def _stream_case(B, T, D, W, H, dtype, static, seed, mean_len=20.0, seq=None):
 
 STREAM = []
 for dtype in ("f32", "bf16"):
-    for W in (1, 2, 3, 4, 5):
+    for W in (1, 2, 3, 4, 5, 6, 8):
         for H, static in ((1, False), (4, False), (16, False), (1, True), (4, True)):
             STREAM.append((dtype, W, H, static))
 
@@ -144,7 +144,7 @@ def test_packed_lowrank_parity(dtype, W, R, D):
     assert_close("db", db, rdb, rt, rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("W", [2, 4, 5])
+@pytest.mark.parametrize("W", [2, 4, 5, 8])
 def test_packed_prompt_cache_fill_and_decode(W):
     """The cache after a packed prompt holds only the last document's tokens; decoding
     then continues that document (row t of the oracle over the packed row, with the new

@@ -202,7 +202,7 @@ def test_golden_handworked_lowrank():
         assert np.array_equal(db, c["db"])
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("H", [1, 2, 4])
 @pytest.mark.parametrize("T", [1, 3, 9])
 @pytest.mark.parametrize("static", [False, True])
@@ -210,7 +210,7 @@ def test_matrix_form(W, H, T, static):
     assert pin_matrix_form(conv_fwd, conv_bwd, 2, T, 8, W, H, static, seed=W * 100 + H * 10 + T)
 
 
-@pytest.mark.parametrize("W", [1, 3, 4, 5])
+@pytest.mark.parametrize("W", [1, 3, 4, 5, 8])
 @pytest.mark.parametrize("H", [1, 4])
 def test_static_matches_library_fir(W, H):
     assert pin_static_library(conv_fwd, 2, 17, 8, W, H, seed=W + 7 * H)
@@ -231,7 +231,7 @@ def test_constant_in_t_dynamic_equals_static():
 
 
 @pytest.mark.parametrize("static", [False, True])
-@pytest.mark.parametrize("W,H,T", [(1, 1, 4), (3, 2, 5), (4, 1, 6), (5, 4, 3), (4, 2, 7)])
+@pytest.mark.parametrize("W,H,T", [(1, 1, 4), (3, 2, 5), (4, 1, 6), (5, 4, 3), (4, 2, 7), (8, 1, 10), (7, 2, 5)])
 def test_finite_differences_conv(W, H, T, static):
     assert pin_fd_conv(conv_fwd, conv_bwd, 2, T, 4 * H if H > 1 else 4, W, H, static, seed=W * 31 + T)
 
