@@ -73,17 +73,19 @@ def stream_bytes(B, T, D, W, H, eb=2, static=False, fwd=True, bwd=True):
     return total
 
 
-def lowrank_bytes(B, T, D, W, R, eb=2, fwd=True):
+def lowrank_bytes(B, T, D, W, R, eb=2, fwd=True, H=1):
     tc = B * T * D
-    J = D * W
+    J = (D // H) * W
     if fwd:
         return 2 * tc * eb + B * T * R * eb + R * J * eb + J * eb
     # x, dy, dx; z, dz; U, b; dU, db (float32)
     return 3 * tc * eb + 2 * B * T * R * eb + R * J * eb + J * eb + R * J * 4 + J * 4
 
 
-def lowrank_flops(B, T, D, W, R, fwd=True):
-    per = 2 * B * T * R * D * W
+def lowrank_flops(B, T, D, W, R, fwd=True, H=1):
+    """Algorithmic flops: the (D/H)*W filter columns of a token once (the general kernels
+    form them once per channel)."""
+    per = 2 * B * T * R * (D // H) * W
     return per if fwd else 3 * per
 
 
@@ -214,6 +216,8 @@ ROWS = (
     "lowrank_r64_bwd",
     "decode_perchannel_b64",
     "decode_lowrank_r64_b64",
+    "lowrank_h4_r64_fwd",
+    "lowrank_h4_r64_bwd",
     "perchannel_w8_fwd",
     "perchannel_w8_bwd",
     "packed_perchannel_h1_fwd",
@@ -268,23 +272,26 @@ def make_row(name, device):
         return (lambda: dynconv_lowrank_decode_step(x, z, U, b, cache, 7, W, out=y)), \
             io + B * R * 2 + R * D * W * 2 + D * W * 2, 2 * B * R * D * W, f"decode step B{B} D{D} W{W} R{R} bf16"
     if name.startswith("lowrank"):
+        # lowrank_h4_*: head-wise generation, U of R x (D/4)*W (the general kernels)
         B, T, D, W, R = 8, 4096, 2048, 4, 64
+        H = 4 if name.startswith("lowrank_h4") else 1
+        J = (D // H) * W
         x = gen((B, T, D), 1.0, 4, "x", device)
         z = gen((B, T, R), 1.0, 4, "z", device)
-        U = gen((R, D * W), 0.1 / R**0.5, 4, "U", device)
-        b = gen((D * W,), 0.1**0.5, 4, "b", device)
-        desc = tag(f"B{B} T{T} D{D} W{W} R{R} bf16", B, T)
+        U = gen((R, J), 0.1 / R**0.5, 4, "U", device)
+        b = gen((J,), 0.1**0.5, 4, "b", device)
+        desc = tag(f"B{B} T{T} D{D} W{W} R{R}{f' H{H}' if H > 1 else ''} bf16", B, T)
         seq = segs(B, T)
         sb = 4 * B * T if packed else 0
         if name.endswith("fwd"):
             y = torch.empty_like(x)
-            return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, out=y, seq_idx=seq)), \
-                lowrank_bytes(B, T, D, W, R) + sb, lowrank_flops(B, T, D, W, R), desc
+            return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, H, out=y, seq_idx=seq)), \
+                lowrank_bytes(B, T, D, W, R, H=H) + sb, lowrank_flops(B, T, D, W, R, H=H), desc
         dy = gen((B, T, D), 1.0, 4, "dy", device)
-        ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, 1, R, torch.bfloat16), dtype=torch.uint8,
+        ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, torch.bfloat16), dtype=torch.uint8,
                          device=device)
-        return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, workspace=ws, seq_idx=seq)), \
-            lowrank_bytes(B, T, D, W, R, fwd=False) + sb, lowrank_flops(B, T, D, W, R, fwd=False), desc
+        return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, H, workspace=ws, seq_idx=seq)), \
+            lowrank_bytes(B, T, D, W, R, fwd=False, H=H) + sb, lowrank_flops(B, T, D, W, R, fwd=False, H=H), desc
     if name.startswith("qkv"):
         B, T, D, W, H = 4, 8192, 3072, 4, 1
     else:

@@ -346,7 +346,6 @@ dynconv_status check_lowrank(const void* x, const int64_t* xs, const void* z, co
   if (R < 1) return DYNCONV_ERR_INVALID_ARG;
   if (R > 128) return DYNCONV_ERR_UNSUPPORTED;
   if (W > kMaxLowrankW) return DYNCONV_ERR_UNSUPPORTED;
-  if (H != 1) return DYNCONV_ERR_UNSUPPORTED;  // head-wise low-rank generation is not built
   if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
   if (z == nullptr || zs == nullptr) return DYNCONV_ERR_INVALID_ARG;
   if (zs[2] != 1) return DYNCONV_ERR_UNSUPPORTED;
@@ -439,7 +438,7 @@ dynconv_status dynconv_lowrank_fwd_varlen(const void* x, const int64_t* xs, cons
 
 size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
                                           dynconv_dtype dtype) {
-  if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK || R < 1 || R > 128 || H != 1 || W > kMaxLowrankW) return 0;
+  if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK || R < 1 || R > 128 || W > kMaxLowrankW) return 0;
   if (B == 0 || T == 0 || D == 0) return 0;
   return plan_lowrank(B, T, D, W, H, R, true, dtype).ws_total;
 }
@@ -648,13 +647,13 @@ dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, con
   if (st != DYNCONV_OK) return st;
   const int eb = elem_bytes(dtype);
   if (t < 0 || R < 1) return DYNCONV_ERR_INVALID_ARG;
-  if (R > 128 || H != 1 || W > kMaxLowrankW) return DYNCONV_ERR_UNSUPPORTED;
+  if (R > 128 || W > kMaxLowrankW) return DYNCONV_ERR_UNSUPPORTED;
   if ((st = check_row(x, xs, eb)) != DYNCONV_OK) return st;
   if ((st = check_row(y, ys, eb)) != DYNCONV_OK) return st;
   if ((st = check_row(z, zs, eb)) != DYNCONV_OK) return st;
   if ((st = check_cache(cache, cs, W, eb)) != DYNCONV_OK) return st;
   if (U == nullptr) return DYNCONV_ERR_INVALID_ARG;
-  if (ldu < D * W) return DYNCONV_ERR_INVALID_ARG;
+  if (ldu < (D / H) * W) return DYNCONV_ERR_INVALID_ARG;
   if (!aligned(U, eb) || (bias != nullptr && !aligned(bias, eb))) return DYNCONV_ERR_UNSUPPORTED;
   if (y == x || y == z || y == U || (bias != nullptr && y == bias) ||
       (W > 1 && (y == cache || cache == x || cache == z || cache == U)))

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void k_decode_step(const DecodeParams p) {
   decode_channel<ET, W>(p, b, d, w);
 }
 
-// Low-rank filters w[b,c,k] = sum_r z[b,r] U[r,cW+k] + bias[cW+k], generated per step on the
+// Low-rank filters w[b,c,k] = sum_r z[b,r] U[r,gW+k] + bias[gW+k] with g = c / H (H = 1 per
+// channel, H > 1 head-wise: the H channels of a group read the same columns), generated per step on the
 // matrix cores. One wave owns 16 sequences x 16 channels. For each tap k the product of the
 // z rows and the columns cW+k of U is a 16x16 tile whose lane holds 4 sequences of a single
 // channel, so after the W products a lane holds every tap of its 4 (sequence, channel) pairs
@@ -210,14 +211,14 @@ __global__ __launch_bounds__(64) void k_lowrank_decode_step(const DecodeParams p
     for (int e = 0; e < 8; ++e) {
       const int r = 32 * s + 8 * q + e;
       RT u[W];
-      load_taps<RT, W, VEC>(U + int64_t(min(r, R - 1)) * p.ldu + int64_t(ca) * W, u);
+      load_taps<RT, W, VEC>(U + int64_t(min(r, R - 1)) * p.ldu + int64_t(ca / p.H) * W, u);
 #pragma unroll
       for (int k = 0; k < W; ++k) bt[s][k][e] = r < R ? u[k] : RT(0);
     }
   }
   RT bias[W];
   if (p.bias != nullptr) {
-    load_taps<RT, W, VEC>(static_cast<const RT*>(p.bias) + int64_t(ca) * W, bias);
+    load_taps<RT, W, VEC>(static_cast<const RT*>(p.bias) + int64_t(ca / p.H) * W, bias);
   } else {
 #pragma unroll
     for (int k = 0; k < W; ++k) bias[k] = RT(0);

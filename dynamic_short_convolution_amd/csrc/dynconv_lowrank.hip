@@ -156,6 +156,36 @@ __device__ __forceinline__ u32x4 load_chunk(const ET* row, int c, int limit, boo
   return r;
 }
 
+// Head-wise low-rank: 16 bytes of per-channel filter columns jj = j0 .. of the channels from
+// c0 (column jj is tap jj % W of channel c0 + jj / W), read from the U row of their groups
+// (column ((c0 + jj / W) / H) * W + jj % W); the first `limit` (>= 1) are valid.
+template <typename ET>
+__device__ __forceinline__ u32x4 load_group_cols(const ET* urow, int c0, int j0, int limit, int W, int H) {
+  constexpr int E = 16 / int(sizeof(ET));
+  u32x4 r = {0u, 0u, 0u, 0u};
+  uint32_t h[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int jj = j0 + min(e, limit - 1);
+    const int64_t col = int64_t((c0 + jj / W) / H) * W + jj % W;
+    if constexpr (sizeof(ET) == 2) {
+      h[e] = reinterpret_cast<const uint16_t*>(urow)[col];
+    } else {
+      h[e] = __float_as_uint(reinterpret_cast<const float*>(urow)[col]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t v = e < limit ? h[e] : 0u;
+    if constexpr (sizeof(ET) == 2) {
+      r[e / 2] |= (e & 1) ? (v << 16) : v;
+    } else {
+      r[e] = v;
+    }
+  }
+  return r;
+}
+
 // The first `limit` (>= 1) of the 16 bytes at row[0 ..] by element loads, all issued
 // before any is used (indices clamped into the row, the tail masked afterwards).
 template <typename ET>
@@ -320,7 +350,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
       const int ch = cw0 + ((m >> 2) / LPC) * MT + mt;
       const int tap = 4 * ((m >> 2) % LPC) + (m & 3);
       const bool ok = ch < p.D && tap < W;
-      const int64_t col = int64_t(ch) * W + tap;
+      const int64_t col = int64_t(ch / p.H) * W + tap;  // group ch / H (head-wise: H > 1)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -333,7 +363,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
       for (int i = 0; i < 4; ++i) {
         const int tq = 4 * (q % LPC) + i;
         binit[mt][i] = (bias != nullptr && chq < p.D && tq < W)
-                           ? Raw<ET>::to_float(Raw<ET>::from_mem(bias, int64_t(chq) * W + tq))
+                           ? Raw<ET>::to_float(Raw<ET>::from_mem(bias, int64_t(chq / p.H) * W + tq))
                            : 0.f;
       }
     }
@@ -652,7 +682,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
       const int ch = cw0 + ((m >> 2) / LPC) * MT + mt;
       const int tap = 4 * ((m >> 2) % LPC) + (m & 3);
       const bool ok = ch < p.D && tap < W;
-      const int64_t col = int64_t(ch) * W + tap;
+      const int64_t col = int64_t(ch / p.H) * W + tap;  // group ch / H (head-wise: H > 1)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -664,7 +694,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
       for (int i = 0; i < 4; ++i) {
         const int tq = 4 * (q % LPC) + i;
         binit[mt][i] = (bias != nullptr && cl + mt < p.D && tq < W)
-                           ? R_::to_float(R_::from_mem(bias, int64_t(cl + mt) * W + tq))
+                           ? R_::to_float(R_::from_mem(bias, int64_t((cl + mt) / p.H) * W + tq))
                            : 0.f;
       }
     }
@@ -955,8 +985,10 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
       v += __shfl_xor(v, 4, 64);
       v += __shfl_xor(v, 8, 64);
       const int tap = 4 * (q % LPC) + i;
-      if (p.part_db != nullptr && n == 0 && tap < W && cl + mt < p.D)
-        p.part_db[int64_t(range) * p.J + int64_t(cl + mt) * W + tap] = v;
+      // head-wise: one partial per (range, channel of the group), summed by the reduce
+      const int c = cl + mt;
+      if (p.part_db != nullptr && n == 0 && tap < W && c < p.D)
+        p.part_db[(int64_t(range) * p.H + c % p.H) * p.J + int64_t(c / p.H) * W + tap] = v;
     }
   // dU partial: lane holds rows rt*16 + 4q + ii of padded column jt*16 + n
 #pragma unroll
@@ -970,7 +1002,9 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = rt * 16 + 4 * q + ii;
-          if (r < p.R) p.part_dU[(int64_t(range) * p.R + r) * p.J + int64_t(ch) * W + tap] = dU[rt][jt][ii];
+          if (r < p.R)
+            p.part_dU[((int64_t(range) * p.H + ch % p.H) * p.R + r) * p.J + int64_t(ch / p.H) * W + tap] =
+                dU[rt][jt][ii];
         }
       }
     }
@@ -1063,7 +1097,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
   static_assert(US + AS <= 32, "valid bits");
   auto prefetch = [&](Stage& st, int c0) {
     const int climit = p.D - c0;
-    const int jlimit = p.J - c0 * W;
+    const int jlimit = climit * W;  // filter columns (channel, tap) of the chunk inside D
     const ET* ub = U + int64_t(c0) * W;
     uint32_t okm = 0;
 #pragma unroll
@@ -1071,7 +1105,12 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
       const int ck = tid + i * kBlockThreads;
       const int r = ck / (UC / CE), c = (ck % (UC / CE)) * CE;
       const bool ok = ck < UCH && r < p.R && c < jlimit;
-      st.u[i] = stage16<false, ET>(ub, r * int(p.ldu) + c, ok, jlimit - c, U);
+      if (p.H == 1) {
+        st.u[i] = stage16<false, ET>(ub, r * int(p.ldu) + c, ok, jlimit - c, U);
+      } else {
+        // head-wise: column (c0 + cc) / H * W + k of U for the chunk's column cc * W + k
+        st.u[i] = ok ? load_group_cols<ET>(U + int64_t(r) * p.ldu, c0, c, jlimit - c, W, p.H) : u32x4{0u, 0u, 0u, 0u};
+      }
       okm |= uint32_t(ok) << i;
     }
 #pragma unroll
@@ -1494,8 +1533,8 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   }
   // dz: token blocks inside T on the DMA path, the rest on the register path
   const int nblk = (p.T + kLowrankDzTokens - 1) / kLowrankDzTokens;
-  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.act16 != 0 && p.u16 != 0 && p.D % kLowrankDzChunk == 0 &&
-                   p.R % 32 == 0;
+  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.H == 1 && p.act16 != 0 && p.u16 != 0 &&
+                   p.D % kLowrankDzChunk == 0 && p.R % 32 == 0;
   const int nfb = dma ? p.T / kLowrankDzTokens : 0;
   if (nfb > 0) {
     q.tbb0 = 0;
@@ -1566,10 +1605,10 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
   pl.blocks = B * int64_t(pl.nTr) * pl.nCs;
   const int64_t J = (D / H) * W;
   const int64_t nR = B * int64_t(pl.nTr);
+  // one partial per (token range, channel of a group): H of them per group column
   pl.ws_dU = 0;
-  pl.ws_db = size_t(nR) * size_t(R) * size_t(J) * sizeof(float);
-  pl.ws_total = bwd ? pl.ws_db + size_t(nR) * size_t(J) * sizeof(float) : 0;
-  (void)H;
+  pl.ws_db = size_t(nR) * size_t(H) * size_t(R) * size_t(J) * sizeof(float);
+  pl.ws_total = bwd ? pl.ws_db + size_t(nR) * size_t(H) * size_t(J) * sizeof(float) : 0;
   return pl;
 }
 
@@ -1589,7 +1628,7 @@ dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& pla
   const hipError_t e = dt == DYNCONV_BF16 ? lr_dispatch_w<true, bf16_t>(p, plan, W, stream)
                                           : lr_dispatch_w<true, float>(p, plan, W, stream);
   if (e != hipSuccess) return record_hip_error(e);
-  const int64_t nR = int64_t(p.B) * plan.nTr;
+  const int64_t nR = int64_t(p.B) * plan.nTr * p.H;  // partials per (token range, channel of a group)
   dynconv_status st = launch_reduce_partials(p.part_dU, nR, int64_t(p.R) * p.J, dU, stream);
   if (st != DYNCONV_OK || db == nullptr) return st;
   return launch_reduce_partials(p.part_db, nR, p.J, db, stream);

@@ -227,17 +227,17 @@ def dynconv_decode_step(x, w, cache, t: int, H: int = 1, out=None):
     return y
 
 
-def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None):
-    """y [B,D] of token t with filters z [B,R] U + bias generated on the GPU; the cache is
-    updated in place."""
+def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None, H: int = 1):
+    """y [B,D] of token t with filters z [B,R] U + bias generated on the GPU (U: [R, (D/H)*W]);
+    the cache is updated in place."""
     B, D = x.shape
     R = z.shape[-1]
-    _check_lowrank_operands(x, z, U, bias, D * W)
+    _check_lowrank_operands(x, z, U, bias, (D // H) * W)
     y = torch.empty_like(x) if out is None else out
     dev = _require_device(x, z, U, bias, y, cache)
     cs = _lib.strides(cache.stride()) if cache is not None else None
     st = _lib.load().dynconv_lowrank_decode_step(
         _ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias),
-        _ptr(cache), cs, _ptr(y), _lib.strides(y.stride()), int(t), B, D, W, 1, R, _dtype_code(x), _stream(dev))
+        _ptr(cache), cs, _ptr(y), _lib.strides(y.stride()), int(t), B, D, W, H, R, _dtype_code(x), _stream(dev))
     _lib.check("dynconv_lowrank_decode_step", st)
     return y

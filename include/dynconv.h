@@ -34,7 +34,7 @@
  * - Supported parameters: 1 <= W <= 8 (low-rank form: W <= 5); H == 1 or H a power of two that divides D, with
  *   H / VEC <= 64 where VEC = min(H, widest lane vector allowed by the alignment below /
  *   element size), i.e. H <= 512 (bf16) or 256 (float32) with 16-byte aligned
- *   activations; low-rank form: H == 1 and 1 <= R <= 128.
+ *   activations; low-rank form: 1 <= R <= 128 (H > 1 takes the general kernels).
  * - Alignment: base pointers of activation-shaped tensors and their s[0], s[1] (in bytes)
  *   must be multiples of 4 bytes (bf16: D even); wider lane vectors (8 or 16 bytes) are
  *   used when every activation-shaped tensor of the call allows them. Filters: base and
@@ -173,7 +173,7 @@ dynconv_status dynconv_decode_step(const void* x, const int64_t* xs, const void*
  * Low-rank decoding step: the filters of the new token, w[b,g,k] = sum_r z[b,r] U[r, g*W+k]
  * + bias[g*W+k], are formed on the GPU (float32) and applied as in dynconv_decode_step.
  *   z  [B, R] with strides zs[0..1] (zs[1] == 1); U, ldu, bias as in dynconv_lowrank_fwd.
- * H == 1, 1 <= R <= 128.
+ * 1 <= R <= 128, W <= 5.
  */
 dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
                                            const void* U, int64_t ldu, const void* bias, void* cache,

@@ -130,7 +130,8 @@ def test_lowrank_validation(lib):
     assert lr_fwd(lib, U_=P(0)) == INVALID
     assert lr_fwd(lib, y=X) == INVALID
     assert lr_fwd(lib, ldu=100) == INVALID  # row shorter than (D/H)*W
-    assert lr_fwd(lib, H=2) == UNSUP  # head-wise low-rank is not built
+    assert lr_fwd(lib, H=3) == INVALID  # 3 does not divide D = 200
+    assert lr_fwd(lib, H=2, ldu=399) == INVALID  # head-wise: rows hold (D/H)*W = 400 columns
     assert lr_fwd(lib, W=6, ldu=1200) == UNSUP  # the low-rank kernels take W <= 5
     need = lib.dynconv_lowrank_bwd_workspace_size(2, 4, 200, 4, 1, 64, BF16)
     st = lib.dynconv_lowrank_bwd(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, DY, S(800, 200, 1), DX,
@@ -190,7 +191,7 @@ def test_cache_fill_and_lowrank_decode_validation(lib):
 
     assert lrd(R=0) == INVALID
     assert lrd(R=129) == UNSUP
-    assert lrd(H=2) == UNSUP
+    assert lrd(H=3) == INVALID  # 3 does not divide D = 200
     assert lrd(z=P(0)) == INVALID
     assert lrd(U_=P(0)) == INVALID
     assert lrd(ldu=100) == INVALID

@@ -74,6 +74,27 @@ def test_lowrank_decode_matches_full_sequence(dtype, W, R, T0):
         assert_close(f"y[{t}]", yt, ref[:, t], TD[dtype])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H,W,R", [(4, 4, 64), (2, 3, 20), (16, 5, 32)])
+def test_headwise_lowrank_decode(dtype, H, W, R):
+    """U of R x (D/H)*W: the H channels of a group share the generated filter."""
+    B, Ttot, D = 5, 8, 96
+    seed = 950 + H + W
+    x = synth.draw((B, Ttot, D), 1.0, seed, "x", dtype)
+    z = synth.draw((B, Ttot, R), 1.0, seed, "z", dtype)
+    U = synth.draw((R, (D // H) * W), 0.3 / R**0.5, seed, "U", dtype)
+    b = synth.draw(((D // H) * W,), 0.3, seed, "b", dtype)
+    ref = lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W, H)
+    xg, zg, Ug, bg = x.cuda(), z.cuda(), U.cuda(), b.cuda()
+    T0 = 3
+    y0 = dynconv_lowrank_fwd(xg[:, :T0].contiguous(), zg[:, :T0].contiguous(), Ug, bg, W, H)
+    assert_close("prefill", y0, ref[:, :T0], TD[dtype])
+    cache = dynconv_cache_fill(xg[:, :T0], W)
+    for t in range(T0, Ttot):
+        yt = dynconv_lowrank_decode_step(xg[:, t], zg[:, t], Ug, bg, cache, t, W, H=H)
+        assert_close(f"y[{t}]", yt, ref[:, t], TD[dtype])
+
+
 def test_lowrank_decode_without_bias():
     B, Ttot, D, W, R = 4, 6, 64, 4, 32
     x = synth.draw((B, Ttot, D), 1.0, 77, "x", "bf16")

@@ -218,3 +218,42 @@ def test_fast_bwd_multistep_ranges():
     rdx, _, _, _ = lowrank_bwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
                                to64(b.index_select(0, cols)), to64(dy.index_select(2, ci)), W)
     assert_close("dx", dx.index_select(2, ci.cuda()).cpu(), rdx, torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------
+# head-wise generation: U is R x (D/H)*W, the H channels of a group share its filter
+# ------------------------------------------------------------------------------------
+
+HEADWISE = []
+for dtype in ("f32", "bf16"):
+    for H in (2, 4, 16):
+        for W, R in ((1, 16), (3, 40), (4, 64), (5, 128)):
+            HEADWISE.append((dtype, H, W, R))
+
+
+@pytest.mark.parametrize("dtype,H,W,R", HEADWISE)
+def test_headwise_lowrank_parity(dtype, H, W, R):
+    B, T, D = 2, 150, 128
+    seed = 80 + H + W + R
+    td = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    G = D // H
+    x = synth.draw((B, T, D), 1.0, seed, "x", dtype)
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", dtype)
+    z = synth.draw((B, T, R), 1.0, seed, "z", dtype)
+    U = synth.draw((R, G * W), 0.3 / R**0.5, seed, "U", dtype)
+    b = synth.draw((G * W,), 0.3, seed, "b", dtype)
+    x64, z64, U64, b64, dy64 = to64(x), to64(z), to64(U), to64(b), to64(dy)
+    xg, zg, Ug, bg, dyg = x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda()
+    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, H)
+    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W, H), td)
+    dx, dz, dU, db = dynconv_lowrank_bwd(xg, zg, Ug, bg, dyg, W, H)
+    rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, H)
+    assert_close("dx", dx, rdx, td)
+    # |g| of a group: the sum of its channels' |dy x| terms
+    _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, G, W)), np.abs(dy64), H)
+    gabs = gabs.reshape(B * T, G * W)
+    u = 2.0**-8 if td == torch.bfloat16 else 2.0**-22
+    assert_close("dz", dz, rdz, td, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
+    rt = torch.float32 if td == torch.float32 else td
+    assert_close("dU", dU, rdU, rt, rtol=1e-5, atol=1e-5, extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
+    assert_close("db", db, rdb, rt, rtol=1e-5, atol=1e-5)

@@ -108,35 +108,33 @@ def test_packed_strided_segment_ids():
         assert_close("dw", dw, rdw, torch.bfloat16)
 
 
-def _g_abs(x64, dy64, W):
-    B, T, D = x64.shape
-    _, dwabs = conv_bwd(np.abs(x64), np.zeros((B, T, D, W)), np.abs(dy64), 1)
-    return dwabs.reshape(B * T, D * W)
+LOWRANK = [("bf16", 4, 64, 128, 1), ("bf16", 2, 32, 128, 1), ("bf16", 3, 64, 192, 1), ("bf16", 5, 40, 72, 1),
+           ("f32", 1, 16, 64, 1), ("f32", 3, 64, 136, 1), ("f32", 4, 128, 64, 1), ("bf16", 4, 64, 128, 4),
+           ("f32", 3, 32, 64, 8)]
 
 
-LOWRANK = [("bf16", 4, 64, 128), ("bf16", 2, 32, 128), ("bf16", 3, 64, 192), ("bf16", 5, 40, 72),
-           ("f32", 1, 16, 64), ("f32", 3, 64, 136), ("f32", 4, 128, 64)]
-
-
-@pytest.mark.parametrize("dtype,W,R,D", LOWRANK)
-def test_packed_lowrank_parity(dtype, W, R, D):
-    """Includes bf16 shapes that would take the fast kernels without segment ids."""
-    B, T, seed = 2, 300, 700 + W + R
+@pytest.mark.parametrize("dtype,W,R,D,H", LOWRANK)
+def test_packed_lowrank_parity(dtype, W, R, D, H):
+    """Includes bf16 shapes that would take the fast kernels without segment ids, and
+    head-wise generation."""
+    B, T, seed = 2, 300, 700 + W + R + H
     td = DT[dtype]
+    G = D // H
     x = synth.draw((B, T, D), 1.0, seed, "x", dtype)
     dy = synth.draw((B, T, D), 1.0, seed, "dy", dtype)
     z = synth.draw((B, T, R), 1.0, seed, "z", dtype)
-    U = synth.draw((R, D * W), 0.3 / R**0.5, seed, "U", dtype)
-    b = synth.draw((D * W,), 0.3, seed, "b", dtype)
+    U = synth.draw((R, G * W), 0.3 / R**0.5, seed, "U", dtype)
+    b = synth.draw((G * W,), 0.3, seed, "b", dtype)
     seq = synth.segments(B, T, 24.0, seed, first=(1, 2, 3))
     xg, zg, Ug, bg, dyg, sg = x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), seq.cuda()
     x64, z64, U64, b64, dy64, s64 = to64(x), to64(z), to64(U), to64(b), to64(dy), seq.numpy()
-    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, seq_idx=sg)
-    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W, 1, s64), td)
-    dx, dz, dU, db = dynconv_lowrank_bwd(xg, zg, Ug, bg, dyg, W, seq_idx=sg)
-    rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, 1, s64)
+    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, H, seq_idx=sg)
+    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W, H, s64), td)
+    dx, dz, dU, db = dynconv_lowrank_bwd(xg, zg, Ug, bg, dyg, W, H, seq_idx=sg)
+    rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, H, s64)
     assert_close("dx", dx, rdx, td)
-    gabs = _g_abs(x64, dy64, W)
+    _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, G, W)), np.abs(dy64), H)
+    gabs = gabs.reshape(B * T, G * W)
     u = 2.0**-8 if td == torch.bfloat16 else 2.0**-22
     assert_close("dz", dz, rdz, td, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
     rt = torch.float32 if td == torch.float32 else td
