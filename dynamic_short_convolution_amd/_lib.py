@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdynconv.
 
 DYNCONV_F32 = 0
 DYNCONV_BF16 = 1
+DYNCONV_F16 = 2
 
 STATUS = {
     0: "DYNCONV_OK",

@@ -14,7 +14,7 @@ thread_local int g_last_hip_error = 0;
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-int elem_bytes(dynconv_dtype dt) { return dt == DYNCONV_BF16 ? 2 : 4; }
+int elem_bytes(dynconv_dtype dt) { return dt == DYNCONV_F32 ? 4 : 2; }
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % uint64_t(a)) == 0; }
 
@@ -44,7 +44,7 @@ bool act_align_ok(const Act* a, int n, int eb, int64_t align_bytes) {
 }
 
 dynconv_status check_common(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dt) {
-  if (dt != DYNCONV_F32 && dt != DYNCONV_BF16) return DYNCONV_ERR_INVALID_ARG;
+  if (dt != DYNCONV_F32 && dt != DYNCONV_BF16 && dt != DYNCONV_F16) return DYNCONV_ERR_INVALID_ARG;
   if (B < 0 || T < 0 || D < 0) return DYNCONV_ERR_INVALID_ARG;
   if (W < 1 || H < 1) return DYNCONV_ERR_INVALID_ARG;
   if (W > kMaxW) return DYNCONV_ERR_UNSUPPORTED;

@@ -6,9 +6,13 @@
 
 namespace dynconv {
 
-// Storage element types. bf16 travels as raw 16-bit patterns; every product and sum
-// is float32; bf16 results are rounded to nearest even by v_cvt_pk_bf16_f32.
+// Storage element types. bf16 and fp16 travel as raw 16-bit patterns; every product and
+// sum is float32; 16-bit results are rounded to nearest even (v_cvt_pk_bf16_f32,
+// v_cvt_f16_f32).
 struct bf16_t {
+  uint16_t bits;
+};
+struct f16_t {
   uint16_t bits;
 };
 
@@ -30,96 +34,32 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// ---------------------------------------------------------------------------------
-// N contiguous elements starting at an address aligned to min(16, N * sizeof) bytes
-// (4 bytes at least), converted to float.
-// ---------------------------------------------------------------------------------
-template <typename ET, int N>
-struct Vec;
+// Conversions of a 16-bit storage type: the low / high half of a 32-bit word to float, a
+// pair of floats to a word, one float to its bits (round to nearest even).
+template <typename ET>
+struct Cvt;
 
-template <int N>
-struct Vec<bf16_t, N> {
-  static_assert(N % 2 == 0, "bf16 vectors hold an even number of elements");
-  static __device__ __forceinline__ void load(const bf16_t* p, float (&o)[N]) {
-    if constexpr (N == 8) {
-      u32x4 u = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[2 * i] = bf16_lo(u[i]);
-        o[2 * i + 1] = bf16_hi(u[i]);
-      }
-    } else {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-      for (int i = 0; i < N / 2; ++i) {
-        uint32_t u = q[i];
-        o[2 * i] = bf16_lo(u);
-        o[2 * i + 1] = bf16_hi(u);
-      }
-    }
-  }
-  static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[N]) {
-    if constexpr (N == 8) {
-      u32x4 u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-      *reinterpret_cast<u32x4*>(p) = u;
-    } else {
-      uint32_t* q = reinterpret_cast<uint32_t*>(p);
-#pragma unroll
-      for (int i = 0; i < N / 2; ++i) q[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    }
-  }
+template <>
+struct Cvt<bf16_t> {
+  static __device__ __forceinline__ float lo(uint32_t u) { return bf16_lo(u); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return bf16_hi(u); }
+  static __device__ __forceinline__ float of_bits(uint32_t h) { return __uint_as_float(h << 16); }
+  static __device__ __forceinline__ uint32_t pack2(float l, float h) { return pack_bf16x2(l, h); }
+  static __device__ __forceinline__ uint16_t bits(float f) { return to_bf16_bits(f); }
 };
 
-template <int N>
-struct Vec<float, N> {
-  static __device__ __forceinline__ void load(const float* p, float (&o)[N]) {
-    if constexpr (N == 4) {
-      float4 u = *reinterpret_cast<const float4*>(p);
-      o[0] = u.x;
-      o[1] = u.y;
-      o[2] = u.z;
-      o[3] = u.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) o[i] = p[i];
-    }
+template <>
+struct Cvt<f16_t> {
+  static __device__ __forceinline__ float of_bits(uint32_t h) {
+    return float(__builtin_bit_cast(_Float16, uint16_t(h)));
   }
-  static __device__ __forceinline__ void store(float* p, const float (&v)[N]) {
-    if constexpr (N == 4) {
-      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) p[i] = v[i];
-    }
+  static __device__ __forceinline__ float lo(uint32_t u) { return of_bits(u & 0xffffu); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return of_bits(u >> 16); }
+  static __device__ __forceinline__ uint16_t bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+  static __device__ __forceinline__ uint32_t pack2(float l, float h) {
+    return uint32_t(bits(l)) | (uint32_t(bits(h)) << 16);
   }
 };
-
-// N contiguous elements with only natural (element) alignment.
-template <typename ET, int N>
-__device__ __forceinline__ void load_unaligned(const ET* p, float (&o)[N]) {
-  if constexpr (sizeof(ET) == 2) {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-#pragma unroll
-    for (int i = 0; i < N; ++i) o[i] = __uint_as_float(uint32_t(q[i]) << 16);
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) o[i] = reinterpret_cast<const float*>(p)[i];
-  }
-}
-
-template <typename ET, int N>
-__device__ __forceinline__ void store_unaligned(ET* p, const float (&v)[N]) {
-  if constexpr (sizeof(ET) == 2) {
-    uint16_t* q = reinterpret_cast<uint16_t*>(p);
-#pragma unroll
-    for (int i = 0; i < N; ++i) q[i] = to_bf16_bits(v[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) reinterpret_cast<float*>(p)[i] = v[i];
-  }
-}
 
 // ---------------------------------------------------------------------------------
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD i % 8),

@@ -21,7 +21,7 @@ namespace {
 template <typename ET>
 __device__ __forceinline__ float ldf(const void* p, int64_t i) {
   if constexpr (sizeof(ET) == 2) {
-    return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+    return Cvt<ET>::of_bits(static_cast<const uint16_t*>(p)[i]);
   } else {
     return static_cast<const float*>(p)[i];
   }
@@ -30,7 +30,7 @@ __device__ __forceinline__ float ldf(const void* p, int64_t i) {
 template <typename ET>
 __device__ __forceinline__ void stf(void* p, int64_t i, float v) {
   if constexpr (sizeof(ET) == 2) {
-    static_cast<uint16_t*>(p)[i] = to_bf16_bits(v);
+    static_cast<uint16_t*>(p)[i] = Cvt<ET>::bits(v);
   } else {
     static_cast<float*>(p)[i] = v;
   }
@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256) void k_decode_step(const DecodeParams p) {
 // latency. Lane (l, q) = (lane % 16, lane / 16) carries ranks 32s + 8q + e, e < 8, of rank
 // step s, for both operands.
 typedef __bf16 dec_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 dec_f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t dec_u16x8_t __attribute__((ext_vector_type(8)));
 typedef float dec_f32x8_t __attribute__((ext_vector_type(8)));
 typedef float dec_f32x4_t __attribute__((ext_vector_type(4)));
@@ -121,6 +122,20 @@ struct DecMma<bf16_t> {
   static __device__ __forceinline__ dec_f32x4_t mma(const Frag& a, const Frag& b, dec_f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dec_bf16x8_t, a),
                                                    __builtin_bit_cast(dec_bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct DecMma<f16_t> {
+  using RT = uint16_t;
+  using Frag = dec_u16x8_t;
+  static __device__ __forceinline__ float to_f(RT v) { return Cvt<f16_t>::of_bits(v); }
+  static __device__ __forceinline__ Frag load8(const RT* p) {
+    return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(p));
+  }
+  static __device__ __forceinline__ dec_f32x4_t mma(const Frag& a, const Frag& b, dec_f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(dec_f16x8_t, a),
+                                                  __builtin_bit_cast(dec_f16x8_t, b), c, 0, 0, 0);
   }
 };
 
@@ -250,8 +265,9 @@ __global__ __launch_bounds__(64) void k_lowrank_decode_step(const DecodeParams p
 
 template <int W, typename F>
 hipError_t by_dtype(dynconv_dtype dt, F&& f) {
-  return dt == DYNCONV_BF16 ? f(bf16_t{}, std::integral_constant<int, W>{})
-                            : f(float{}, std::integral_constant<int, W>{});
+  return dt == DYNCONV_BF16  ? f(bf16_t{}, std::integral_constant<int, W>{})
+         : dt == DYNCONV_F16 ? f(f16_t{}, std::integral_constant<int, W>{})
+                             : f(float{}, std::integral_constant<int, W>{});
 }
 
 template <typename F>
@@ -300,7 +316,7 @@ dynconv_status launch_lowrank_decode_step(const DecodeParams& p, int W, dynconv_
   if (gy > 65535u) return DYNCONV_ERR_UNSUPPORTED;
   const dim3 grid(unsigned((p.D + 15) / 16), gy);
   const int nk = (p.R + 31) / 32;
-  const size_t eb = dt == DYNCONV_BF16 ? 2 : 4;
+  const size_t eb = dt == DYNCONV_F32 ? 4 : 2;
   const auto al = [](const void* q, size_t a) { return reinterpret_cast<uintptr_t>(q) % a == 0; };
   const bool vec = p.R % 8 == 0 && (p.zs0 * eb) % 16 == 0 && al(p.z, 16) && p.ldu % W == 0 && al(p.U, W * eb) &&
                    (p.bias == nullptr || al(p.bias, W * eb));

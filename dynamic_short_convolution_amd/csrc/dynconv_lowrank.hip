@@ -21,6 +21,8 @@
 //                   with g recomputed from x and dy, looping over channel chunks, so dz is
 //                   complete without partial sums.
 //   partial sums of dU and db are then added in a fixed order (run-to-run deterministic).
+#include <type_traits>
+
 #include "dynconv_common.hpp"
 #include "dynconv_internal.hpp"
 #include "dynconv_lowrank_internal.hpp"
@@ -30,6 +32,8 @@ namespace dynconv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -51,6 +55,16 @@ struct Raw<bf16_t> {
   }
   static __device__ __forceinline__ uint16_t from_float(float f) { return to_bf16_bits(f); }
   static __device__ __forceinline__ float to_float(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
+  static __device__ __forceinline__ uint16_t zero() { return 0; }
+};
+template <>
+struct Raw<f16_t> {
+  using type = uint16_t;
+  static __device__ __forceinline__ uint16_t from_mem(const f16_t* p, int64_t i) {
+    return reinterpret_cast<const uint16_t*>(p)[i];
+  }
+  static __device__ __forceinline__ uint16_t from_float(float f) { return Cvt<f16_t>::bits(f); }
+  static __device__ __forceinline__ float to_float(uint16_t u) { return Cvt<f16_t>::of_bits(u); }
   static __device__ __forceinline__ uint16_t zero() { return 0; }
 };
 template <>
@@ -88,6 +102,26 @@ struct Mfma<bf16_t> {
   static __device__ __forceinline__ f32x4_t mma16(const F16k& a, const F16k& b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a.v), __builtin_bit_cast(s16x4_t, b.v),
                                                      c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<f16_t> {
+  struct F32k {
+    u16x8_t v;
+  };
+  struct F16k {
+    u16x4_t v;
+  };
+  static __device__ __forceinline__ int k32(int q, int e) { return 8 * q + e; }
+  static __device__ __forceinline__ int k16(int q, int e) { return 4 * q + e; }
+  static __device__ __forceinline__ f32x4_t mma32(const F32k& a, const F32k& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a.v), __builtin_bit_cast(f16x8_t, b.v),
+                                                  c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mma16(const F16k& a, const F16k& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a.v), __builtin_bit_cast(f16x4_t, b.v),
+                                                 c, 0, 0, 0);
   }
 };
 
@@ -240,7 +274,7 @@ __device__ __forceinline__ void lds_read_run(const ET* p, float (&o)[N]) {
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     if constexpr (sizeof(ET) == 2) {
-      o[e] = (e & 1) ? bf16_hi(u[e >> 1]) : bf16_lo(u[e >> 1]);
+      o[e] = (e & 1) ? Cvt<ET>::hi(u[e >> 1]) : Cvt<ET>::lo(u[e >> 1]);
     } else {
       o[e] = __uint_as_float(u[e]);
     }
@@ -258,7 +292,7 @@ __device__ __forceinline__ void global_store_run(ET* p, const float (&v)[N], boo
 #pragma unroll
     for (int i = 0; i < BYTES / 4; ++i) {
       if constexpr (sizeof(ET) == 2) {
-        u[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+        u[i] = Cvt<ET>::pack2(v[2 * i], v[2 * i + 1]);
       } else {
         u[i] = __float_as_uint(v[i]);
       }
@@ -280,7 +314,7 @@ __device__ __forceinline__ void global_store_run(ET* p, const float (&v)[N], boo
   for (int e = 0; e < N; ++e) {
     if (e < count) {
       if constexpr (sizeof(ET) == 2) {
-        reinterpret_cast<uint16_t*>(p)[e] = to_bf16_bits(v[e]);
+        reinterpret_cast<uint16_t*>(p)[e] = Cvt<ET>::bits(v[e]);
       } else {
         reinterpret_cast<float*>(p)[e] = v[e];
       }
@@ -937,7 +971,8 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
         for (int mt = 0; mt < MT; ++mt) {
           RT* dst = &gw[(sub * TT + n) * GP + (lane_c + mt) * WP + 4 * (q % LPC)];
           if constexpr (EB == 2) {
-            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(g[mt][0], g[mt][1]), pack_bf16x2(g[mt][2], g[mt][3])};
+            *reinterpret_cast<u32x2*>(dst) =
+                u32x2{Cvt<ET>::pack2(g[mt][0], g[mt][1]), Cvt<ET>::pack2(g[mt][2], g[mt][3])};
           } else {
             *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{g[mt][0], g[mt][1], g[mt][2], g[mt][3]};
           }
@@ -1198,7 +1233,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
     }
     auto elem = [&](const uint32_t* w, int c) -> float {
       if constexpr (EB == 2) {
-        return (c & 1) ? bf16_hi(w[c >> 1]) : bf16_lo(w[c >> 1]);
+        return (c & 1) ? Cvt<ET>::hi(w[c >> 1]) : Cvt<ET>::lo(w[c >> 1]);
       } else {
         return __uint_as_float(w[c]);
       }
@@ -1214,7 +1249,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
         for (int e = 0; e < 8; e += 2) {
           const int c0_ = (8 * ks + e) / W, k0_ = (8 * ks + e) % W;
           const int c1_ = (8 * ks + e + 1) / W, k1_ = (8 * ks + e + 1) % W;
-          const uint32_t w2 = pack_bf16x2(dyf[c0_] * elem(xw[k0_], c0_), dyf[c1_] * elem(xw[k1_], c1_));
+          const uint32_t w2 = Cvt<ET>::pack2(dyf[c0_] * elem(xw[k0_], c0_), dyf[c1_] * elem(xw[k1_], c1_));
           bfr.v[e] = uint16_t(w2 & 0xffffu);
           bfr.v[e + 1] = uint16_t(w2 >> 16);
         }
@@ -1258,7 +1293,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
         if (r < p.R) {
           const int64_t o = int64_t(t) * p.dzs1 + r;
           if constexpr (EB == 2) {
-            reinterpret_cast<uint16_t*>(dz)[o] = to_bf16_bits(acc[rt][ii]);
+            reinterpret_cast<uint16_t*>(dz)[o] = Cvt<ET>::bits(acc[rt][ii]);
           } else {
             dz[o] = acc[rt][ii];
           }
@@ -1469,7 +1504,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 // The LDS DMA path serves bf16 token blocks that lie inside T when its stages fit.
 template <typename ET, int W, int KS>
 constexpr bool lowrank_dz_dma_ok() {
-  return sizeof(ET) == 2 && LrDzDma<W, KS>::BYTES <= 150 * 1024;
+  return std::is_same<ET, bf16_t>::value && LrDzDma<W, KS>::BYTES <= 150 * 1024;
 }
 
 // DMA: the LDS DMA path (the launch covers whole token blocks, aligned rows, D % 32 == 0
@@ -1505,7 +1540,7 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   // otherwise one main kernel (the channel slices inside D on the 16-byte path, the rest on
   // the other)
   // (packed sequences take the general kernels)
-  const bool fast = p.seg == nullptr && lowrank_bwd_dx_fast_ok(p, W, sizeof(ET) == 2 ? DYNCONV_BF16 : DYNCONV_F32);
+  const bool fast = p.seg == nullptr && std::is_same<ET, bf16_t>::value && lowrank_bwd_dx_fast_ok(p, W, DYNCONV_BF16);
   LowRankParams q = p;
   const int64_t per_slice = int64_t(p.B) * pl.nTr;
   const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;
@@ -1618,15 +1653,17 @@ dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& pla
     const hipError_t e = launch_lowrank_fwd_fast(p, W, stream);
     return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
   }
-  const hipError_t e = dt == DYNCONV_BF16 ? lr_dispatch_w<false, bf16_t>(p, plan, W, stream)
-                                          : lr_dispatch_w<false, float>(p, plan, W, stream);
+  const hipError_t e = dt == DYNCONV_BF16   ? lr_dispatch_w<false, bf16_t>(p, plan, W, stream)
+                       : dt == DYNCONV_F16 ? lr_dispatch_w<false, f16_t>(p, plan, W, stream)
+                                           : lr_dispatch_w<false, float>(p, plan, W, stream);
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
 }
 
 dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   float* dU, float* db, hipStream_t stream) {
-  const hipError_t e = dt == DYNCONV_BF16 ? lr_dispatch_w<true, bf16_t>(p, plan, W, stream)
-                                          : lr_dispatch_w<true, float>(p, plan, W, stream);
+  const hipError_t e = dt == DYNCONV_BF16   ? lr_dispatch_w<true, bf16_t>(p, plan, W, stream)
+                       : dt == DYNCONV_F16 ? lr_dispatch_w<true, f16_t>(p, plan, W, stream)
+                                           : lr_dispatch_w<true, float>(p, plan, W, stream);
   if (e != hipSuccess) return record_hip_error(e);
   const int64_t nR = int64_t(p.B) * plan.nTr * p.H;  // partials per (token range, channel of a group)
   dynconv_status st = launch_reduce_partials(p.part_dU, nR, int64_t(p.R) * p.J, dU, stream);

@@ -103,14 +103,14 @@ struct Words {
   }
   __device__ __forceinline__ float at(int i) const {
     if constexpr (sizeof(ET) == 2) {
-      return (i & 1) ? bf16_hi(u[i >> 1]) : bf16_lo(u[i >> 1]);
+      return (i & 1) ? Cvt<ET>::hi(u[i >> 1]) : Cvt<ET>::lo(u[i >> 1]);
     } else {
       return __uint_as_float(u[i]);
     }
   }
 };
 
-// N contiguous elements with only element alignment (bf16 filter groups of odd W).
+// N contiguous elements with only element alignment (16-bit filter groups of odd W).
 template <typename ET, int N>
 struct Halves {
   uint16_t h[N];
@@ -123,7 +123,7 @@ struct Halves {
 #pragma unroll
     for (int i = 0; i < N; ++i) h[i] = 0;
   }
-  __device__ __forceinline__ float at(int i) const { return __uint_as_float(uint32_t(h[i]) << 16); }
+  __device__ __forceinline__ float at(int i) const { return Cvt<ET>::of_bits(h[i]); }
 };
 
 template <bool NT, typename ET, int N>
@@ -131,7 +131,7 @@ __device__ __forceinline__ void store_words(ET* p, const float (&v)[N]) {
   uint32_t* q = reinterpret_cast<uint32_t*>(p);
   if constexpr (sizeof(ET) == 2) {
 #pragma unroll
-    for (int i = 0; i < N / 2; ++i) st32<NT>(q + i, pack_bf16x2(v[2 * i], v[2 * i + 1]));
+    for (int i = 0; i < N / 2; ++i) st32<NT>(q + i, Cvt<ET>::pack2(v[2 * i], v[2 * i + 1]));
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) st32<NT>(q + i, __float_as_uint(v[i]));
@@ -145,7 +145,7 @@ __device__ __forceinline__ void store_elems(ET* p, const float (&v)[N]) {
   if constexpr (sizeof(ET) == 2 && !WORDS) {
     uint16_t* q = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
-    for (int i = 0; i < N; ++i) st16<NT>(q + i, to_bf16_bits(v[i]));
+    for (int i = 0; i < N; ++i) st16<NT>(q + i, Cvt<ET>::bits(v[i]));
   } else {
     store_words<NT, ET, N>(p, v);
   }
@@ -778,15 +778,17 @@ StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, i
 
 dynconv_status launch_stream_fwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
                                  bool is_static, hipStream_t stream) {
-  const hipError_t e = dt == DYNCONV_BF16 ? dispatch_w<false, bf16_t>(p, plan, W, is_static, stream)
-                                          : dispatch_w<false, float>(p, plan, W, is_static, stream);
+  const hipError_t e = dt == DYNCONV_BF16   ? dispatch_w<false, bf16_t>(p, plan, W, is_static, stream)
+                       : dt == DYNCONV_F16 ? dispatch_w<false, f16_t>(p, plan, W, is_static, stream)
+                                           : dispatch_w<false, float>(p, plan, W, is_static, stream);
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
 }
 
 dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
                                  bool is_static, float* dw_static_out, hipStream_t stream) {
-  hipError_t e = dt == DYNCONV_BF16 ? dispatch_w<true, bf16_t>(p, plan, W, is_static, stream)
-                                    : dispatch_w<true, float>(p, plan, W, is_static, stream);
+  hipError_t e = dt == DYNCONV_BF16   ? dispatch_w<true, bf16_t>(p, plan, W, is_static, stream)
+                 : dt == DYNCONV_F16 ? dispatch_w<true, f16_t>(p, plan, W, is_static, stream)
+                                     : dispatch_w<true, float>(p, plan, W, is_static, stream);
   if (e != hipSuccess) return record_hip_error(e);
   if (is_static && p.partial != nullptr) {
     return launch_reduce_partials(p.partial, int64_t(p.B) * plan.nTw, int64_t(p.G) * W, dw_static_out, stream);

@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 
-_DTYPE = {torch.float32: _lib.DYNCONV_F32, torch.bfloat16: _lib.DYNCONV_BF16}
+_DTYPE = {torch.float32: _lib.DYNCONV_F32, torch.bfloat16: _lib.DYNCONV_BF16, torch.float16: _lib.DYNCONV_F16}
 
 
 def _ptr(t):
@@ -21,7 +21,7 @@ def _ptr(t):
 
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPE:
-        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float16")
     return _DTYPE[t.dtype]
 
 

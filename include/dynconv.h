@@ -26,9 +26,11 @@
  *   (w, dw) are [B, T, D/H, W] with strides s[0..3], s[3] == 1 and s[2] == W (the W taps
  *   of one group are contiguous). w with s[0] == s[1] == 0 is a static filter [D/H, W].
  *   z and dz are [B, T, R] with strides s[0..2], s[2] == 1.
- * - Element types: x, w, z, U, bias, y, dy, dx, dw (per token) and dz all have `dtype`.
- *   Reduced parameter gradients (static dw, dU, db) are always float32 and contiguous.
- * - Arithmetic is float32 (products and sums), bf16 results are rounded to nearest even.
+ * - Element types: x, w, z, U, bias, y, dy, dx, dw (per token) and dz all have `dtype`
+ *   (float32, bfloat16 or float16). Reduced parameter gradients (static dw, dU, db) are
+ *   always float32 and contiguous.
+ * - Arithmetic is float32 (products and sums), 16-bit results are rounded to nearest even.
+ *   The bf16 fast low-rank kernels serve bfloat16 only; float16 takes the general ones.
  * - Validation happens before any HIP call; invalid input returns a status, never aborts.
  *   B == 0 or T == 0 or D == 0 is a no-op returning DYNCONV_OK.
  * - Supported parameters: 1 <= W <= 8 (low-rank form: W <= 5); H == 1 or H a power of two that divides D, with
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-typedef enum { DYNCONV_F32 = 0, DYNCONV_BF16 = 1 } dynconv_dtype;
+typedef enum { DYNCONV_F32 = 0, DYNCONV_BF16 = 1, DYNCONV_F16 = 2 } dynconv_dtype;
 
 typedef enum {
   DYNCONV_OK = 0,

@@ -31,7 +31,7 @@ TENSOR_STREAM = {
     "seg": 8,
 }
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def draw(shape, std: float, seed: int, name: str, dtype: str) -> torch.Tensor:

@@ -261,3 +261,11 @@ def test_varlen_validation(lib):
                                          4, BF16, None) == INVALID
     assert lib.dynconv_cache_fill_varlen(X, S(800, 200, 1), SEG, S(4, 1), P(0xa0000), S(600, 200, 1), 0, 4, 200,
                                          4, BF16, None) == OK
+
+
+def test_float16_dtype_code(lib):
+    """float16 (code 2) is a storage type like the others; codes past it are invalid."""
+    assert fwd(lib, dt=2, B=0) == OK
+    assert fwd(lib, dt=2, x=P(0x10002)) == UNSUP  # 16-bit activations need 4-byte alignment
+    assert fwd(lib, dt=3) == INVALID
+    assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 3, 1, 1, 2) > 0

@@ -19,7 +19,7 @@ from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
 
-TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -30,7 +30,7 @@ def _device():
 
 
 CASES = []
-for dtype in ("f32", "bf16"):
+for dtype in ("f32", "bf16", "f16"):
     for W in (1, 2, 3, 4, 5, 6, 7, 8):
         for H, static in ((1, False), (4, False), (1, True)):
             for T0 in (0, 2, 7):
@@ -54,7 +54,7 @@ def test_decode_matches_full_sequence(dtype, W, H, static, T0):
         assert_close(f"y[{t}]", yt, ref[:, t], TD[dtype])
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("W,R,T0", [(1, 16, 3), (2, 40, 1), (3, 20, 0), (4, 64, 5), (4, 96, 0), (5, 128, 2)])
 def test_lowrank_decode_matches_full_sequence(dtype, W, R, T0):
     B, Ttot, D = 19, 10, 136  # two groups of sequences, a partial group of channels
@@ -74,7 +74,7 @@ def test_lowrank_decode_matches_full_sequence(dtype, W, R, T0):
         assert_close(f"y[{t}]", yt, ref[:, t], TD[dtype])
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("H,W,R", [(4, 4, 64), (2, 3, 20), (16, 5, 32)])
 def test_headwise_lowrank_decode(dtype, H, W, R):
     """U of R x (D/H)*W: the H channels of a group share the generated filter."""

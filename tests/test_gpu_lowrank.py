@@ -41,7 +41,7 @@ def _g_abs(x64, dy64, W):
 
 
 def _check(B, T, D, W, R, dtype, seed, bias=True, bwd=True):
-    td = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    td = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     x, z, U, b, dy = _inputs(B, T, D, W, R, dtype, seed, bias)
     xg, zg, Ug, dyg = x.cuda(), z.cuda(), U.cuda(), dy.cuda()
     bg = b.cuda() if b is not None else None
@@ -55,7 +55,7 @@ def _check(B, T, D, W, R, dtype, seed, bias=True, bwd=True):
     rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W)
     assert_close("dx", dx, rdx, td)
     gabs = _g_abs(x64, dy64, W)
-    u = 2.0**-8 if td == torch.bfloat16 else 2.0**-22
+    u = {torch.bfloat16: 2.0**-8, torch.float16: 2.0**-11}.get(td, 2.0**-22)
     extra_dz = (u * (gabs @ np.abs(U64).T)).reshape(B, T, R)
     extra_dU = u * (np.abs(z64).reshape(B * T, R).T @ gabs)
     assert_close("dz", dz, rdz, td, extra=extra_dz)
@@ -65,7 +65,7 @@ def _check(B, T, D, W, R, dtype, seed, bias=True, bwd=True):
 
 
 SMALL = []
-for dtype in ("f32", "bf16"):
+for dtype in ("f32", "bf16", "f16"):
     for W in (1, 2, 3, 4, 5):
         for R in (1, 20, 33, 64, 128):
             SMALL.append((dtype, W, R))
@@ -225,7 +225,7 @@ def test_fast_bwd_multistep_ranges():
 # ------------------------------------------------------------------------------------
 
 HEADWISE = []
-for dtype in ("f32", "bf16"):
+for dtype in ("f32", "bf16", "f16"):
     for H in (2, 4, 16):
         for W, R in ((1, 16), (3, 40), (4, 64), (5, 128)):
             HEADWISE.append((dtype, H, W, R))
@@ -235,7 +235,7 @@ for dtype in ("f32", "bf16"):
 def test_headwise_lowrank_parity(dtype, H, W, R):
     B, T, D = 2, 150, 128
     seed = 80 + H + W + R
-    td = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    td = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     G = D // H
     x = synth.draw((B, T, D), 1.0, seed, "x", dtype)
     dy = synth.draw((B, T, D), 1.0, seed, "dy", dtype)
@@ -252,7 +252,7 @@ def test_headwise_lowrank_parity(dtype, H, W, R):
     # |g| of a group: the sum of its channels' |dy x| terms
     _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, G, W)), np.abs(dy64), H)
     gabs = gabs.reshape(B * T, G * W)
-    u = 2.0**-8 if td == torch.bfloat16 else 2.0**-22
+    u = {torch.bfloat16: 2.0**-8, torch.float16: 2.0**-11}.get(td, 2.0**-22)
     assert_close("dz", dz, rdz, td, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
     rt = torch.float32 if td == torch.float32 else td
     assert_close("dU", dU, rdU, rt, rtol=1e-5, atol=1e-5, extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))

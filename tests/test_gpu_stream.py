@@ -16,7 +16,7 @@ from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -64,6 +64,12 @@ for dtype in ("f32", "bf16"):
                 for T in (3, 100, 333):
                     SMALL.append((dtype, W, H, static, D, T))
 
+
+# float16 storage (the same kernels with float16 conversions)
+for W in (1, 2, 3, 4, 5, 8):
+    for H in (1, 4, 16):
+        for static in (False, True):
+            SMALL.append(("f16", W, H, static, 200 if H == 1 else 640, 333))
 
 # the widest filters (W = 6..8; the pages' ablation reaches W = 6)
 for dtype in ("f32", "bf16"):

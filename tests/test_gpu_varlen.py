@@ -19,7 +19,7 @@ from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,7 +53,7 @@ def _stream_case(B, T, D, W, H, dtype, static, seed, mean_len=20.0, seq=None):
 
 
 STREAM = []
-for dtype in ("f32", "bf16"):
+for dtype in ("f32", "bf16", "f16"):
     for W in (1, 2, 3, 4, 5, 6, 8):
         for H, static in ((1, False), (4, False), (16, False), (1, True), (4, True)):
             STREAM.append((dtype, W, H, static))
@@ -110,7 +110,7 @@ def test_packed_strided_segment_ids():
 
 LOWRANK = [("bf16", 4, 64, 128, 1), ("bf16", 2, 32, 128, 1), ("bf16", 3, 64, 192, 1), ("bf16", 5, 40, 72, 1),
            ("f32", 1, 16, 64, 1), ("f32", 3, 64, 136, 1), ("f32", 4, 128, 64, 1), ("bf16", 4, 64, 128, 4),
-           ("f32", 3, 32, 64, 8)]
+           ("f32", 3, 32, 64, 8), ("f16", 4, 64, 128, 1), ("f16", 3, 40, 96, 2)]
 
 
 @pytest.mark.parametrize("dtype,W,R,D,H", LOWRANK)
@@ -135,7 +135,7 @@ def test_packed_lowrank_parity(dtype, W, R, D, H):
     assert_close("dx", dx, rdx, td)
     _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, G, W)), np.abs(dy64), H)
     gabs = gabs.reshape(B * T, G * W)
-    u = 2.0**-8 if td == torch.bfloat16 else 2.0**-22
+    u = {torch.bfloat16: 2.0**-8, torch.float16: 2.0**-11}.get(td, 2.0**-22)
     assert_close("dz", dz, rdz, td, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
     rt = torch.float32 if td == torch.float32 else td
     assert_close("dU", dU, rdU, rt, rtol=1e-5, atol=1e-5, extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
