@@ -36,7 +36,8 @@ HEADLINE = dict(B=8, T=4096, D=2048, W=4, H=1)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "dynamic_short_convolution_amd", "csrc", f)
-    for f in ("dynconv_stream.hip", "dynconv_common.hpp", "dynconv_internal.hpp")
+    for f in ("dynconv_stream.hip", "dynconv_stream_kernels.hpp", "dynconv_stream_bf16.hip", "dynconv_common.hpp",
+              "dynconv_internal.hpp")
 ]
 
 

@@ -18,7 +18,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = [
     "dynconv_abi.hip",
     "dynconv_stream.hip",
+    "dynconv_stream_f32.hip",
+    "dynconv_stream_bf16.hip",
+    "dynconv_stream_f16.hip",
     "dynconv_lowrank.hip",
+    "dynconv_lowrank_f32.hip",
+    "dynconv_lowrank_bf16.hip",
+    "dynconv_lowrank_f16.hip",
     "dynconv_lowrank_fast.hip",
     "dynconv_decode.hip",
 ]

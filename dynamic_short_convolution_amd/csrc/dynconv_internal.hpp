@@ -56,6 +56,14 @@ struct StreamPlan {
 StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, int act_align, bool bwd,
                        bool is_static);
 
+// The streaming kernels for one storage type (one translation unit each).
+hipError_t stream_dispatch_f32(const StreamParams& p, const StreamPlan& plan, int W, bool is_static, bool bwd,
+                               hipStream_t s);
+hipError_t stream_dispatch_bf16(const StreamParams& p, const StreamPlan& plan, int W, bool is_static, bool bwd,
+                                hipStream_t s);
+hipError_t stream_dispatch_f16(const StreamParams& p, const StreamPlan& plan, int W, bool is_static, bool bwd,
+                               hipStream_t s);
+
 dynconv_status launch_stream_fwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
                                  bool is_static, hipStream_t stream);
 dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,

@@ -8,6 +8,8 @@ namespace dynconv {
 // ---------------------------------------------------------------------------------
 // Low-rank form
 // ---------------------------------------------------------------------------------
+constexpr int kLowrankTT = 16;  // tokens per tile of the general kernels (one MFMA's N or K extent)
+
 struct LowRankParams {
   const void* x;
   const void* z;
@@ -62,6 +64,11 @@ struct LowRankPlan {
   size_t ws_dU, ws_db;  // byte offsets inside the workspace
   size_t ws_total;
 };
+
+// The general low-rank kernels for one storage type (one translation unit each).
+hipError_t lowrank_dispatch_f32(const LowRankParams& p, const LowRankPlan& pl, int W, bool bwd, hipStream_t s);
+hipError_t lowrank_dispatch_bf16(const LowRankParams& p, const LowRankPlan& pl, int W, bool bwd, hipStream_t s);
+hipError_t lowrank_dispatch_f16(const LowRankParams& p, const LowRankPlan& pl, int W, bool bwd, hipStream_t s);
 
 LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bwd, dynconv_dtype dt);
 
