@@ -4,6 +4,7 @@ Used by the tests, the package smoke check and the benchmark's CPU-baseline leg;
 by the product path. See ``dynconv_oracle`` for what it computes and where it comes from.
 """
 from .dynconv_oracle import (  # noqa: F401
+    conv_bias_grad,
     conv_bwd,
     conv_fwd,
     lowrank_bwd,

@@ -30,6 +30,10 @@ Readings where the page leaves a step open (each also listed in the design notes
   has no bias;
 * the generator's input is the normalised block input, not X itself, so x and w are
   independent inputs and dx has no path through w;
+* optional convolution bias (the Conv1D module of the convolution technical report, whose
+  initialisation study randomises both its weights and its bias; the dynamic-convolution
+  page itself has no bias in the convolution): a per-channel vector c added to every output token,
+  y_t = x_t + sum_k w_k x_{t-k} + c, with gradient dc = sum over (b, t) of dy;
 * packed sequences (several documents in one row; the RubiConv page's point that a
   convolution must not read across a document start): an optional segment id per token,
   seq_idx (B, T) of integers, and tap k of token t is present only when token t - k
@@ -69,9 +73,9 @@ def _same_segment(seq_idx, b: int, k: int, T: int):
     return (s[k:] == s[: T - k]).astype(np.float64)[:, None]
 
 
-def conv_fwd(x, w, H: int = 1, seq_idx=None) -> np.ndarray:
+def conv_fwd(x, w, H: int = 1, seq_idx=None, conv_bias=None) -> np.ndarray:
     """Forward of eq. 2 + eq. 3: y_t = x_t + sum_{k<W} w_k^{(t)} * x_{t-k}, zero for t-k < 0
-    (and, with seq_idx, for t-k in another segment than t).
+    (and, with seq_idx, for t-k in another segment than t), plus conv_bias (D,) if given.
 
     x: (B, T, D). w: (B, T, D/H, W) per-token filters, or (D/H, W) for a static filter
     (eq. 1). Returns y: (B, T, D) in float64.
@@ -92,7 +96,15 @@ def conv_fwd(x, w, H: int = 1, seq_idx=None) -> np.ndarray:
                 y[b, k:, :] += m * wf[None, :, k] * x[b, : T - k, :]
             else:
                 y[b, k:, :] += m * wf[k:, :, k] * x[b, : T - k, :]
+    if conv_bias is not None:
+        y += _f64(conv_bias)[None, None, :]  # every token, every sequence
     return y
+
+
+def conv_bias_grad(dy) -> np.ndarray:
+    """Gradient of <dy, y> with respect to the convolution bias: y is c plus terms free of
+    c, so dc[d] = sum over every (b, t) of dy[b, t, d]. Returns (D,) float64."""
+    return _f64(dy).sum(axis=(0, 1))
 
 
 def conv_bwd(x, w, dy, H: int = 1, seq_idx=None):

@@ -689,3 +689,54 @@ def _mut_packed_bwd_unmasked_dx(x, w, dy, H=1, seq_idx=None):
 def test_pins_reject_packed_mutants():
     assert not all(pin_packed_fwd(_mut_packed_adjacent_only, W, 1, False, 80 + W) for W in (3, 4))
     assert not pin_packed_bwd(_mut_packed_bwd_unmasked_dx, 4, 1, False, 81)
+
+
+# ----------------------------------------------------------------------------------
+# optional convolution bias (a per-channel vector added to every output token)
+# ----------------------------------------------------------------------------------
+from oracle import conv_bias_grad  # noqa: E402
+
+
+def pin_conv_bias(fwd, bgrad, seed):
+    """Zero filters: y = x + c exactly at every token, including t < W - 1; dc from central
+    differences of <dy, y> (affine in c) and equal to the plain sum of dy."""
+    r = _rng(seed)
+    B, T, D, W = 2, 7, 6, 4
+    x, dy, c = r.standard_normal((B, T, D)), r.standard_normal((B, T, D)), r.standard_normal(D)
+    if not np.array_equal(fwd(x, np.zeros((B, T, D, W)), 1, None, c), x + c[None, None, :]):
+        return False
+    w = r.standard_normal((B, T, D, W))
+    dc = bgrad(dy)
+    h = 0.5
+    for d in range(D):
+        e = np.zeros(D)
+        e[d] = h
+        num = (np.sum(dy * fwd(x, w, 1, None, c + e)) - np.sum(dy * fwd(x, w, 1, None, c - e))) / (2 * h)
+        if abs(num - dc[d]) > 1e-9 * (1 + abs(dc[d])):
+            return False
+    return True
+
+
+def test_conv_bias():
+    assert pin_conv_bias(conv_fwd, conv_bias_grad, 90)
+    # the bias does not change the other gradients: y is c plus terms free of c
+    r = _rng(91)
+    x, w, dy = r.standard_normal((2, 9, 8)), r.standard_normal((2, 9, 4, 3)), r.standard_normal((2, 9, 8))
+    assert np.array_equal(conv_fwd(x, w, 2, None, np.zeros(8)), conv_fwd(x, w, 2))
+
+
+def _mut_bias_full_window_only(x, w, H=1, seq_idx=None, conv_bias=None):
+    """Wrong: the bias is added only once the filter window is full (t >= W - 1)."""
+    y = conv_fwd(x, w, H, seq_idx)
+    if conv_bias is not None:
+        y[:, np.shape(w)[-1] - 1 :, :] += np.asarray(conv_bias, float)[None, None, :]
+    return y
+
+
+def _mut_bias_grad_mean(dy):
+    return np.asarray(dy, float).mean(axis=(0, 1))  # wrong: averages instead of summing
+
+
+def test_pins_reject_conv_bias_mutants():
+    assert not pin_conv_bias(_mut_bias_full_window_only, conv_bias_grad, 92)
+    assert not pin_conv_bias(conv_fwd, _mut_bias_grad_mean, 93)
