@@ -221,6 +221,8 @@ ROWS = (
     "lowrank_h4_r64_bwd",
     "perchannel_w8_fwd",
     "perchannel_w8_bwd",
+    "convbias_perchannel_h1_fwd",
+    "convbias_perchannel_h1_bwd",
     "packed_perchannel_h1_fwd",
     "packed_perchannel_h1_bwd",
     "packed_lowrank_r64_fwd",
@@ -241,6 +243,9 @@ def make_row(name, device):
     packed = name.startswith("packed_")
     if packed:
         name = name[len("packed_"):]
+    cbias = name.startswith("convbias_")  # with the optional per-channel convolution bias
+    if cbias:
+        name = name[len("convbias_"):]
 
     def segs(B, T):
         return synth.segments(B, T, PACKED_MEAN_DOC, 9).to(device) if packed else None
@@ -305,16 +310,19 @@ def make_row(name, device):
     desc = tag(f"B{B} T{T} D{D} W{W} H{H}{' static' if static else ''} bf16", B, T)
     seq = segs(B, T)
     sb = 4 * B * T if packed else 0
+    cb = gen((D,), 0.5, 2, "b", device) if cbias else None
+    if cbias:
+        desc += " + convolution bias"
     if name.endswith("fwd"):
         y = torch.empty_like(x)
-        return (lambda: dynconv_fwd(x, w, H, out=y, seq_idx=seq)), \
-            stream_bytes(B, T, D, W, H, static=static, bwd=False) + sb, None, desc
+        return (lambda: dynconv_fwd(x, w, H, out=y, seq_idx=seq, conv_bias=cb)), \
+            stream_bytes(B, T, D, W, H, static=static, bwd=False) + sb + (2 * D if cbias else 0), None, desc
     dy = gen((B, T, D), 1.0, 2, "dy", device)
     dx = torch.empty_like(x)
     dw = torch.empty((D // H, W), dtype=torch.float32, device=device) if static else torch.empty_like(w)
     assert dynconv_bwd_workspace_size(B, T, D, W, H, static, torch.bfloat16) >= 0
-    return (lambda: dynconv_bwd(x, w, dy, H, dx=dx, dw=dw, seq_idx=seq)), \
-        stream_bytes(B, T, D, W, H, static=static, fwd=False) + sb, None, desc
+    return (lambda: dynconv_bwd(x, w, dy, H, dx=dx, dw=dw, seq_idx=seq, want_dconv_bias=cbias)), \
+        stream_bytes(B, T, D, W, H, static=static, fwd=False) + sb + (4 * D if cbias else 0), None, desc
 
 
 def run_rows(args, device):

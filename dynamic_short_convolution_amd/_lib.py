@@ -39,6 +39,10 @@ EXPORTS = (
     "dynconv_lowrank_fwd_varlen",
     "dynconv_lowrank_bwd_varlen",
     "dynconv_cache_fill_varlen",
+    "dynconv_fwd_ex",
+    "dynconv_bwd_ex",
+    "dynconv_bwd_ex_workspace_size",
+    "dynconv_decode_step_ex",
 )
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -88,6 +92,17 @@ _SIGNATURES["dynconv_lowrank_fwd_varlen"] = (
     _SIGNATURES["dynconv_lowrank_fwd"][0][:7] + [_vp, _i64p] + _SIGNATURES["dynconv_lowrank_fwd"][0][7:], ctypes.c_int)
 _SIGNATURES["dynconv_lowrank_bwd_varlen"] = (
     _SIGNATURES["dynconv_lowrank_bwd"][0][:7] + [_vp, _i64p] + _SIGNATURES["dynconv_lowrank_bwd"][0][7:], ctypes.c_int)
+# (seq_idx, ss, conv_bias) after the filter; bwd: (seq_idx, ss) after the filter and
+# dconv_bias after dw; decoding: conv_bias after the filter.
+_SIGNATURES["dynconv_fwd_ex"] = (
+    _SIGNATURES["dynconv_fwd"][0][:4] + [_vp, _i64p, _vp] + _SIGNATURES["dynconv_fwd"][0][4:], ctypes.c_int)
+_SIGNATURES["dynconv_bwd_ex"] = (
+    _SIGNATURES["dynconv_bwd"][0][:4] + [_vp, _i64p] + _SIGNATURES["dynconv_bwd"][0][4:10] + [_vp]
+    + _SIGNATURES["dynconv_bwd"][0][10:], ctypes.c_int)
+_SIGNATURES["dynconv_bwd_ex_workspace_size"] = ([_i64, _i64, _i64, _i32, _i32, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int], _sz)
+_SIGNATURES["dynconv_decode_step_ex"] = (
+    _SIGNATURES["dynconv_decode_step"][0][:4] + [_vp] + _SIGNATURES["dynconv_decode_step"][0][4:], ctypes.c_int)
 _SIGNATURES["dynconv_cache_fill_varlen"] = (
     _SIGNATURES["dynconv_cache_fill"][0][:2] + [_vp, _i64p] + _SIGNATURES["dynconv_cache_fill"][0][2:], ctypes.c_int)
 

@@ -138,8 +138,8 @@ int dynconv_last_hip_error(void) { return dynconv::last_hip_error(); }
 namespace {
 
 dynconv_status fwd_impl(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const int32_t* seg,
-                        const int64_t* ss, void* y, const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W,
-                        int32_t H, dynconv_dtype dtype, void* stream) {
+                        const int64_t* ss, const void* cbias, void* y, const int64_t* ys, int64_t B, int64_t T,
+                        int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* stream) {
   dynconv_status st = check_common(B, T, D, W, H, dtype);
   if (st != DYNCONV_OK) return st;
   if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
@@ -147,7 +147,8 @@ dynconv_status fwd_impl(const void* x, const int64_t* xs, const void* w, const i
   const int eb = elem_bytes(dtype);
   FilterInfo fi{};
   if ((st = check_filter(w, ws, W, H, eb, false, &fi)) != DYNCONV_OK) return st;
-  if (y == x || y == w) return DYNCONV_ERR_INVALID_ARG;
+  if (y == x || y == w || (cbias != nullptr && y == cbias)) return DYNCONV_ERR_INVALID_ARG;
+  if (cbias != nullptr && !aligned(cbias, 4)) return DYNCONV_ERR_UNSUPPORTED;
   if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
   const Act acts[2] = {{x, xs}, {y, ys}};
   const int align = act_alignment(acts, 2, eb);
@@ -158,6 +159,7 @@ dynconv_status fwd_impl(const void* x, const int64_t* xs, const void* w, const i
   p.x = x;
   p.w = w;
   p.out = y;
+  p.cbias = cbias;
   if (seg != nullptr) {
     p.seg = seg;
     p.ss0 = ss[0];
@@ -191,7 +193,7 @@ extern "C" {
 dynconv_status dynconv_fwd(const void* x, const int64_t* xs, const void* w, const int64_t* ws, void* y,
                            const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
                            dynconv_dtype dtype, void* stream) {
-  return fwd_impl(x, xs, w, ws, nullptr, nullptr, y, ys, B, T, D, W, H, dtype, stream);
+  return fwd_impl(x, xs, w, ws, nullptr, nullptr, nullptr, y, ys, B, T, D, W, H, dtype, stream);
 }
 
 dynconv_status dynconv_fwd_varlen(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
@@ -199,23 +201,59 @@ dynconv_status dynconv_fwd_varlen(const void* x, const int64_t* xs, const void* 
                                   int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* stream) {
   const dynconv_status st = check_seg(seq_idx, ss);
   if (st != DYNCONV_OK) return st;
-  return fwd_impl(x, xs, w, ws, seq_idx, ss, y, ys, B, T, D, W, H, dtype, stream);
+  return fwd_impl(x, xs, w, ws, seq_idx, ss, nullptr, y, ys, B, T, D, W, H, dtype, stream);
 }
 
-size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int is_static,
-                                  dynconv_dtype dtype) {
+dynconv_status dynconv_fwd_ex(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                              const int32_t* seq_idx, const int64_t* ss, const void* conv_bias, void* y,
+                              const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                              dynconv_dtype dtype, void* stream) {
+  if (seq_idx != nullptr) {
+    const dynconv_status st = check_seg(seq_idx, ss);
+    if (st != DYNCONV_OK) return st;
+  }
+  return fwd_impl(x, xs, w, ws, seq_idx, ss, conv_bias, y, ys, B, T, D, W, H, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the backward: float32 partial sums per (sequence, time chunk), of the
+// static filter gradient [D/H][W] and/or of the convolution-bias gradient [D] (in that
+// order). The chunking depends on the lane vector width only through nDw; take the
+// largest over the possible widths.
+size_t bwd_partial_floats(const StreamPlan& pl, int64_t B, int64_t D, int32_t W, int32_t H, bool static_dw,
+                          bool dcbias) {
+  return size_t(B) * size_t(pl.nTw) * ((static_dw ? size_t(D / H) * size_t(W) : 0) + (dcbias ? size_t(D) : 0));
+}
+
+size_t bwd_workspace(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, bool is_static, bool dcbias,
+                     dynconv_dtype dtype) {
   if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK) return 0;
-  if (!is_static || B == 0 || T == 0 || D == 0) return 0;
+  if ((!is_static && !dcbias) || B == 0 || T == 0 || D == 0) return 0;
   const int eb = elem_bytes(dtype);
-  // The chunking does not depend on the vector width for the static partial count
-  // except through nDw; take the larger of the two possible chunk counts.
   size_t best = 0;
   for (int align : {4, 8, 16}) {
-    const StreamPlan pl = plan_stream(B, T, D, H, eb, align, true, true);
-    const size_t need = size_t(B) * size_t(pl.nTw) * size_t(D / H) * size_t(W) * sizeof(float);
+    const StreamPlan pl = plan_stream(B, T, D, H, eb, align, true, is_static);
+    const size_t need = bwd_partial_floats(pl, B, D, W, H, is_static, dcbias) * sizeof(float);
     if (need > best) best = need;
   }
   return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int is_static,
+                                  dynconv_dtype dtype) {
+  return bwd_workspace(B, T, D, W, H, is_static != 0, false, dtype);
+}
+
+size_t dynconv_bwd_ex_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int is_static,
+                                     int want_dconv_bias, dynconv_dtype dtype) {
+  return bwd_workspace(B, T, D, W, H, is_static != 0, want_dconv_bias != 0, dtype);
 }
 
 }  // extern "C"
@@ -224,11 +262,12 @@ namespace {
 
 dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const int32_t* seg,
                         const int64_t* ss, const void* dy, const int64_t* dys, void* dx, const int64_t* dxs, void* dw,
-                        const int64_t* dws, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        const int64_t* dws, float* dcb, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                        dynconv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   dynconv_status st = check_common(B, T, D, W, H, dtype);
   if (st != DYNCONV_OK) return st;
   if (dx == nullptr && dw == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (dcb != nullptr && !aligned(dcb, 4)) return DYNCONV_ERR_UNSUPPORTED;
   if ((st = check_act(x, xs, true)) != DYNCONV_OK) return st;
   if ((st = check_act(dy, dys, true)) != DYNCONV_OK) return st;
   if ((st = check_act(dx, dxs, false)) != DYNCONV_OK) return st;
@@ -251,6 +290,11 @@ dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const i
     if (dw != nullptr && dw == in) return DYNCONV_ERR_INVALID_ARG;
   }
   if (dx != nullptr && dx == dw) return DYNCONV_ERR_INVALID_ARG;
+  if (dcb != nullptr) {
+    const void* others[5] = {x, w, dy, dx, dw};
+    for (const void* o : others)
+      if (o != nullptr && o == dcb) return DYNCONV_ERR_INVALID_ARG;
+  }
   if (B == 0 || T == 0 || D == 0) {
     return DYNCONV_OK;
   }
@@ -260,11 +304,15 @@ dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const i
 
   const StreamPlan plan = plan_stream(B, T, D, H, eb, align, true, fi.is_static);
   float* partial = nullptr;
-  if (fi.is_static && dw != nullptr) {
-    const size_t need = size_t(B) * size_t(plan.nTw) * size_t(D / H) * size_t(W) * sizeof(float);
+  float* cb_partial = nullptr;
+  const bool static_dw = fi.is_static && dw != nullptr;
+  if (static_dw || dcb != nullptr) {
+    const size_t need = bwd_partial_floats(plan, B, D, W, H, static_dw, dcb != nullptr) * sizeof(float);
     if (workspace == nullptr || workspace_bytes < need) return DYNCONV_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return DYNCONV_ERR_UNSUPPORTED;
-    partial = static_cast<float*>(workspace);
+    float* wsf = static_cast<float*>(workspace);
+    if (static_dw) partial = wsf;
+    if (dcb != nullptr) cb_partial = wsf + bwd_partial_floats(plan, B, D, W, H, static_dw, false);
   }
   StreamParams p{};
   p.x = x;
@@ -273,6 +321,7 @@ dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const i
   p.out = dx;
   p.dw = fi.is_static ? nullptr : dw;
   p.partial = partial;
+  p.cb_partial = cb_partial;
   if (seg != nullptr) {
     p.seg = seg;
     p.ss0 = ss[0];
@@ -304,7 +353,7 @@ dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const i
   p.WT = plan.WT;
   p.nDb = plan.nDb;
   p.nTb = plan.nTb;
-  return launch_stream_bwd(p, plan, W, dtype, fi.is_static, fi.is_static ? static_cast<float*>(dw) : nullptr,
+  return launch_stream_bwd(p, plan, W, dtype, fi.is_static, fi.is_static ? static_cast<float*>(dw) : nullptr, dcb,
                            static_cast<hipStream_t>(stream));
 }
 
@@ -316,7 +365,7 @@ dynconv_status dynconv_bwd(const void* x, const int64_t* xs, const void* w, cons
                            const int64_t* dys, void* dx, const int64_t* dxs, void* dw, const int64_t* dws, int64_t B,
                            int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return bwd_impl(x, xs, w, ws, nullptr, nullptr, dy, dys, dx, dxs, dw, dws, B, T, D, W, H, dtype, workspace,
+  return bwd_impl(x, xs, w, ws, nullptr, nullptr, dy, dys, dx, dxs, dw, dws, nullptr, B, T, D, W, H, dtype, workspace,
                   workspace_bytes, stream);
 }
 
@@ -327,7 +376,20 @@ dynconv_status dynconv_bwd_varlen(const void* x, const int64_t* xs, const void* 
                                   size_t workspace_bytes, void* stream) {
   const dynconv_status st = check_seg(seq_idx, ss);
   if (st != DYNCONV_OK) return st;
-  return bwd_impl(x, xs, w, ws, seq_idx, ss, dy, dys, dx, dxs, dw, dws, B, T, D, W, H, dtype, workspace,
+  return bwd_impl(x, xs, w, ws, seq_idx, ss, dy, dys, dx, dxs, dw, dws, nullptr, B, T, D, W, H, dtype, workspace,
+                  workspace_bytes, stream);
+}
+
+dynconv_status dynconv_bwd_ex(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                              const int32_t* seq_idx, const int64_t* ss, const void* dy, const int64_t* dys, void* dx,
+                              const int64_t* dxs, void* dw, const int64_t* dws, float* dconv_bias, int64_t B,
+                              int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (seq_idx != nullptr) {
+    const dynconv_status st = check_seg(seq_idx, ss);
+    if (st != DYNCONV_OK) return st;
+  }
+  return bwd_impl(x, xs, w, ws, seq_idx, ss, dy, dys, dx, dxs, dw, dws, dconv_bias, B, T, D, W, H, dtype, workspace,
                   workspace_bytes, stream);
 }
 
@@ -620,6 +682,13 @@ dynconv_status dynconv_cache_fill_varlen(const void* x, const int64_t* xs, const
 dynconv_status dynconv_decode_step(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
                                    void* cache, const int64_t* cs, void* y, const int64_t* ys, int64_t t,
                                    int64_t B, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* stream) {
+  return dynconv_decode_step_ex(x, xs, w, ws, nullptr, cache, cs, y, ys, t, B, D, W, H, dtype, stream);
+}
+
+dynconv_status dynconv_decode_step_ex(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                      const void* conv_bias, void* cache, const int64_t* cs, void* y,
+                                      const int64_t* ys, int64_t t, int64_t B, int64_t D, int32_t W, int32_t H,
+                                      dynconv_dtype dtype, void* stream) {
   dynconv_status st = check_common(B, 1, D, W, H, dtype);
   if (st != DYNCONV_OK) return st;
   const int eb = elem_bytes(dtype);
@@ -631,10 +700,15 @@ dynconv_status dynconv_decode_step(const void* x, const int64_t* xs, const void*
   if (ws[2] != 1 || ws[1] != W || ws[0] < 0) return DYNCONV_ERR_UNSUPPORTED;
   if (!aligned(w, eb)) return DYNCONV_ERR_UNSUPPORTED;
   if (y == x || y == w || (W > 1 && (y == cache || cache == x || cache == w))) return DYNCONV_ERR_INVALID_ARG;
+  if (conv_bias != nullptr) {
+    if (conv_bias == y || conv_bias == cache) return DYNCONV_ERR_INVALID_ARG;
+    if (!aligned(conv_bias, eb)) return DYNCONV_ERR_UNSUPPORTED;
+  }
   if (B == 0 || D == 0) return DYNCONV_OK;
   DecodeParams p = decode_params(x, xs, cache, cs, y, ys, t, B, D, W, H);
   p.w = w;
   p.ws0 = ws[0];
+  p.cbias = conv_bias;
   return launch_decode_step(p, W, dtype, static_cast<hipStream_t>(stream));
 }
 

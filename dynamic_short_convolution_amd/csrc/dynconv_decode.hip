@@ -60,12 +60,13 @@ __global__ __launch_bounds__(256) void k_cache_fill(const DecodeParams p) {
 }
 
 // The step for channel d of sequence b given its taps w[0..W-1] (float32): y = x_t +
-// sum_k w_k x_{t-k}, the ring updated with x_t.
+// sum_k w_k x_{t-k} (+ the optional convolution bias), the ring updated with x_t.
 template <typename ET, int W>
 __device__ __forceinline__ void decode_channel(const DecodeParams& p, int b, int d, const float (&w)[W]) {
   constexpr int S = W - 1;
   const float xt = ldf<ET>(p.x, b * p.xs0 + d);
-  float acc = fmaf(w[0], xt, xt);
+  const float cb = p.cbias != nullptr ? ldf<ET>(p.cbias, d) : 0.f;
+  float acc = fmaf(w[0], xt, xt + cb);
   if constexpr (S > 0) {
     const int64_t cb = b * p.cs0 + d;
 #pragma unroll

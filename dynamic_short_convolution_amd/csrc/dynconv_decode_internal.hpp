@@ -20,6 +20,7 @@ struct DecodeParams {
   int64_t xs0, xs1, ws0, zs0, ldu, cs0, cs1, ys0;
   int64_t t;        // decoding step: index of the new token; cache fill: prompt length T
   int32_t B, D, H, R;
+  const void* cbias;   // decoding step (materialised filters): optional convolution bias [D], or null
   const int32_t* seg;  // cache fill of packed prompts: segment id per token [B,T] (ss0, ss1), or null
   int64_t ss0, ss1;
 };

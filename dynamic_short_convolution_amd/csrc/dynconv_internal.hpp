@@ -29,6 +29,8 @@ struct StreamParams {
   void* out;        // y (forward) or dx (backward, may be null)
   void* dw;         // per-token dw (backward, may be null)
   float* partial;   // static dw: per (b, time chunk) partial sums [B*nTw][G][W]
+  const void* cbias;   // forward: optional convolution bias [D] (dtype), or null
+  float* cb_partial;   // backward: per (b, time chunk) sums of dy [B*nTw][D] for the bias gradient, or null
   const int32_t* seg;  // packed sequences: segment id per token [B,T] (strides ss0, ss1), or null
   int64_t ss0, ss1;
   int64_t xs0, xs1;
@@ -67,7 +69,7 @@ hipError_t stream_dispatch_f16(const StreamParams& p, const StreamPlan& plan, in
 dynconv_status launch_stream_fwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
                                  bool is_static, hipStream_t stream);
 dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
-                                 bool is_static, float* dw_static_out, hipStream_t stream);
+                                 bool is_static, float* dw_static_out, float* dcbias_out, hipStream_t stream);
 
 // Fixed-order sum of [nchunk][n] float32 partials into out[n].
 dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,

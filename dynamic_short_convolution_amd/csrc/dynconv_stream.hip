@@ -121,13 +121,18 @@ dynconv_status launch_stream_fwd(const StreamParams& p, const StreamPlan& plan, 
 }
 
 dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, int W, dynconv_dtype dt,
-                                 bool is_static, float* dw_static_out, hipStream_t stream) {
+                                 bool is_static, float* dw_static_out, float* dcbias_out, hipStream_t stream) {
   hipError_t e = dt == DYNCONV_BF16   ? stream_dispatch_bf16(p, plan, W, is_static, true, stream)
                  : dt == DYNCONV_F16 ? stream_dispatch_f16(p, plan, W, is_static, true, stream)
                                      : stream_dispatch_f32(p, plan, W, is_static, true, stream);
   if (e != hipSuccess) return record_hip_error(e);
   if (is_static && p.partial != nullptr) {
-    return launch_reduce_partials(p.partial, int64_t(p.B) * plan.nTw, int64_t(p.G) * W, dw_static_out, stream);
+    const dynconv_status st =
+        launch_reduce_partials(p.partial, int64_t(p.B) * plan.nTw, int64_t(p.G) * W, dw_static_out, stream);
+    if (st != DYNCONV_OK) return st;
+  }
+  if (p.cb_partial != nullptr) {
+    return launch_reduce_partials(p.cb_partial, int64_t(p.B) * plan.nTw, p.D, dcbias_out, stream);
   }
   return DYNCONV_OK;
 }

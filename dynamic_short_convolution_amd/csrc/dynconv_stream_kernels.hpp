@@ -241,8 +241,16 @@ struct Segs {
 // ---------------------------------------------------------------------------------
 // Forward: y_t = x_t + sum_k w_k^(t) x_{t-k}
 // ---------------------------------------------------------------------------------
+// The forward's grid holds about 2 waves per SIMD (8 per CU). For the per-channel form the
+// compiler may spend registers on loads in flight rather than on occupancy it would never
+// get: chasing 8 waves per SIMD it had serialised the filter loads (135 -> 209 us at
+// B8 T4096 D2048 W4; W = 8 296 -> 262 us with the cap). The head-wise and static forms run
+// faster without it (H = 4: 75 vs 83 us).
+constexpr int fwd_max_waves_per_simd(bool perch, bool is_static) { return perch && !is_static ? 4 : 8; }
+
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool SEG>
-__global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams p) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(
+    1, fwd_max_waves_per_simd(PERCH, STATIC)))) void k_stream_fwd(const StreamParams p) {
   using XR = Words<ET, VEC>;
   using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
   constexpr int NC = PERCH ? VEC : 1;
@@ -286,6 +294,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
   }
   Segs<W, SEG> sg;
   sg.init(p, wt.b, wt.t0);
+  // optional convolution bias of the lane's channels (zero without one)
+  float cb[VEC];
+  {
+    XR r;
+    if (p.cbias != nullptr) {
+      r.load(static_cast<const ET*>(p.cbias) + wt.c0);
+    } else {
+      r.zero();
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) cb[v] = r.at(v);
+  }
 
   auto step = [&](int t, const XR& xr, const TR& wr, int sid) {
     bool m[W];
@@ -300,7 +320,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_fwd(const StreamParams
     float yv[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-      float acc = xh[0][v];
+      float acc = xh[0][v] + cb[v];
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         const float f = STATIC ? wst[PERCH ? v : 0][k] : tap_of(wr, v, k, W, PERCH);
@@ -399,6 +419,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   }
   Segs<W, SEG> sg;
   sg.init(p, wt.b, wt.t0);
+  float sdy[VEC];  // sums of dy over the chunk's tokens: the convolution-bias gradient
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) sdy[v] = 0.f;
   float wst[NC][W];
   float sdw[NC][W];  // static: per-lane partial sums of dw over the chunk
   if constexpr (STATIC) {
@@ -421,6 +444,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
     float dyv[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) dyv[v] = have ? dyr.at(v) : 0.f;
+    if (main) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) sdy[v] += dyv[v];
+    }
     if (main && want_dw) {
       float d[W][VEC];
 #pragma unroll
@@ -599,6 +626,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       const int tt = wt.t1 + e;
       step(tt, false, tt < p.T, hdy[e], hw[e], hx[e], hsid[e]);
     }
+  }
+  if (p.cb_partial != nullptr) {
+    float* part = p.cb_partial + int64_t(wt.chunk) * p.D + wt.c0;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) part[v] = sdy[v];
   }
   if constexpr (STATIC) {
     if (want_dw) {

@@ -59,18 +59,32 @@ def _seg_args(seq_idx, B: int, T: int):
     return _ptr(seq_idx), _lib.strides(seq_idx.stride())
 
 
+def _conv_bias_arg(conv_bias, x):
+    if conv_bias is None:
+        return None
+    D = x.shape[-1]
+    if conv_bias.dim() != 1 or conv_bias.numel() != D or conv_bias.stride(0) != 1 or conv_bias.dtype != x.dtype:
+        raise ValueError(f"conv_bias must be a contiguous [{D}] vector of dtype {x.dtype}")
+    return conv_bias
+
+
 def dynconv_fwd(x: torch.Tensor, w: torch.Tensor, H: int = 1, out: torch.Tensor | None = None,
-                seq_idx: torch.Tensor | None = None) -> torch.Tensor:
-    """y = x + causal depthwise conv of x with per-token (or static) filters w. With seq_idx
-    (int32 [B, T] segment ids of packed sequences) no tap crosses into another segment."""
+                seq_idx: torch.Tensor | None = None, conv_bias: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x + causal depthwise conv of x with per-token (or static) filters w (+ conv_bias
+    [D] on every token). With seq_idx (int32 [B, T] segment ids of packed sequences) no tap
+    crosses into another segment."""
     B, T, D = x.shape
     W = w.shape[-1]
+    conv_bias = _conv_bias_arg(conv_bias, x)
     y = torch.empty_like(x) if out is None else out
-    dev = _require_device(x, w, y, seq_idx)
+    dev = _require_device(x, w, y, seq_idx, conv_bias)
     lib = _lib.load()
     head = (_ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)))
     tail = (_ptr(y), _lib.strides(y.stride()), B, T, D, W, H, _dtype_code(x), _stream(dev))
-    if seq_idx is None:
+    if conv_bias is not None:
+        seg = _seg_args(seq_idx, B, T) if seq_idx is not None else (None, None)
+        st = lib.dynconv_fwd_ex(*head, *seg, _ptr(conv_bias), *tail)
+    elif seq_idx is None:
         st = lib.dynconv_fwd(*head, *tail)
     else:
         st = lib.dynconv_fwd_varlen(*head, *_seg_args(seq_idx, B, T), *tail)
@@ -82,9 +96,11 @@ def dynconv_bwd_workspace_size(B, T, D, W, H, is_static, dtype) -> int:
     return int(_lib.load().dynconv_bwd_workspace_size(B, T, D, W, H, int(bool(is_static)), _DTYPE[dtype]))
 
 
-def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True, dx=None, dw=None, seq_idx=None):
+def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True, dx=None, dw=None, seq_idx=None,
+                want_dconv_bias: bool = False):
     """(dx, dw) of <dy, dynconv_fwd(x, w, H, seq_idx=seq_idx)>; dw of a static filter is
-    float32 [D/H, W]."""
+    float32 [D/H, W]. With want_dconv_bias, (dx, dw, dconv_bias) where dconv_bias is the
+    float32 [D] gradient of a convolution bias (the sum of dy over every token)."""
     B, T, D = x.shape
     W = w.shape[-1]
     is_static = w.dim() == 2
@@ -95,7 +111,12 @@ def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True
               else torch.empty((B, T, D // H, W), dtype=x.dtype, device=x.device))
     dev = _require_device(x, w, dy, dx, dw, seq_idx)
     lib = _lib.load()
-    ws_bytes = dynconv_bwd_workspace_size(B, T, D, W, H, is_static and need_dw, x.dtype)
+    if want_dconv_bias:
+        dcb = torch.empty((D,), dtype=torch.float32, device=x.device)
+        ws_bytes = int(lib.dynconv_bwd_ex_workspace_size(B, T, D, W, H, int(is_static and need_dw), 1,
+                                                         _DTYPE[x.dtype]))
+    else:
+        ws_bytes = dynconv_bwd_workspace_size(B, T, D, W, H, is_static and need_dw, x.dtype)
     work = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device) if ws_bytes else None
     head = (_ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)))
     tail = (
@@ -104,6 +125,11 @@ def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True
         _ptr(dw if need_dw else None), _lib.strides(dw.stride()) if (need_dw and not is_static) else None,
         B, T, D, W, H, _dtype_code(x), _ptr(work), ws_bytes, _stream(dev),
     )
+    if want_dconv_bias:
+        seg = _seg_args(seq_idx, B, T) if seq_idx is not None else (None, None)
+        st = lib.dynconv_bwd_ex(*head, *seg, *tail[:6], _ptr(dcb), *tail[6:])
+        _lib.check("dynconv_bwd", st)
+        return (dx if need_dx else None), (dw if need_dw else None), dcb
     if seq_idx is None:
         st = lib.dynconv_bwd(*head, *tail)
     else:
@@ -211,18 +237,19 @@ def dynconv_cache_fill(x, W: int, cache=None, seq_idx=None):
     return cache
 
 
-def dynconv_decode_step(x, w, cache, t: int, H: int = 1, out=None):
+def dynconv_decode_step(x, w, cache, t: int, H: int = 1, out=None, conv_bias=None):
     """y [B,D] of token t from x [B,D], its filters w [B,D/H,W] (or a static [D/H,W]) and
-    the cache of the previous W-1 inputs, which is updated in place."""
+    the cache of the previous W-1 inputs, which is updated in place (+ conv_bias [D])."""
     B, D = x.shape
     W = w.shape[-1]
     ws = [0, w.stride(0), w.stride(1)] if w.dim() == 2 else list(w.stride())
     y = torch.empty_like(x) if out is None else out
-    dev = _require_device(x, w, y, cache)
+    conv_bias = _conv_bias_arg(conv_bias, x)
+    dev = _require_device(x, w, y, cache, conv_bias)
     cs = _lib.strides(cache.stride()) if cache is not None else None
-    st = _lib.load().dynconv_decode_step(_ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(ws), _ptr(cache),
-                                         cs, _ptr(y), _lib.strides(y.stride()), int(t), B, D, W, H, _dtype_code(x),
-                                         _stream(dev))
+    st = _lib.load().dynconv_decode_step_ex(_ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(ws),
+                                            _ptr(conv_bias), _ptr(cache), cs, _ptr(y), _lib.strides(y.stride()),
+                                            int(t), B, D, W, H, _dtype_code(x), _stream(dev))
     _lib.check("dynconv_decode_step", st)
     return y
 

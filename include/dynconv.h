@@ -220,6 +220,35 @@ dynconv_status dynconv_lowrank_bwd_varlen(const void* x, const int64_t* xs, cons
                                           void* stream);
 
 /*
+ * Optional convolution bias (the Conv1D module of the convolution technical report: a
+ * per-channel bias c added to every output, y = x + conv(x) + c), together with optional
+ * segment ids (seq_idx == NULL: one document per row, ss ignored):
+ *   conv_bias   [D] of `dtype`, contiguous, 4-byte aligned, or NULL
+ *   dconv_bias  [D] float32, overwritten with sum over (b, t) of dy (NULL to skip)
+ * The backward's workspace then holds float32 partial sums of dy per (sequence, time
+ * chunk) after those of a static filter: size it with dynconv_bwd_ex_workspace_size.
+ * Materialised, static and head-wise forms; the decoding step adds c to its output.
+ */
+dynconv_status dynconv_fwd_ex(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                              const int32_t* seq_idx, const int64_t* ss, const void* conv_bias, void* y,
+                              const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                              dynconv_dtype dtype, void* stream);
+
+size_t dynconv_bwd_ex_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int is_static,
+                                     int want_dconv_bias, dynconv_dtype dtype);
+
+dynconv_status dynconv_bwd_ex(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                              const int32_t* seq_idx, const int64_t* ss, const void* dy, const int64_t* dys, void* dx,
+                              const int64_t* dxs, void* dw, const int64_t* dws, float* dconv_bias, int64_t B,
+                              int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+dynconv_status dynconv_decode_step_ex(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                      const void* conv_bias, void* cache, const int64_t* cs, void* y,
+                                      const int64_t* ys, int64_t t, int64_t B, int64_t D, int32_t W, int32_t H,
+                                      dynconv_dtype dtype, void* stream);
+
+/*
  * Cache fill after a packed prompt: decoding continues the document of token T-1, so the
  * slots of tokens with another segment id than token T-1 are zero (the start of that
  * document). T == 0 empties the cache as in dynconv_cache_fill.

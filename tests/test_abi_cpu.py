@@ -269,3 +269,29 @@ def test_float16_dtype_code(lib):
     assert fwd(lib, dt=2, x=P(0x10002)) == UNSUP  # 16-bit activations need 4-byte alignment
     assert fwd(lib, dt=3) == INVALID
     assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 3, 1, 1, 2) > 0
+
+
+def test_conv_bias_validation(lib):
+    CB, DCB = P(0xb0000), P(0xc0000)
+
+    def fx(cb=CB, y=Y, B=2):
+        return lib.dynconv_fwd_ex(X, S(800, 200, 1), W_, S(800 * 4, 200 * 4, 4, 1), None, None, cb, y, S(800, 200, 1),
+                                  B, 4, 200, 4, 1, BF16, None)
+
+    assert fx(cb=P(0xb0002)) == UNSUP  # 4-byte alignment
+    assert fx(cb=Y) == INVALID  # the bias may not be the output
+    assert fx(B=0) == OK
+    need = lib.dynconv_bwd_ex_workspace_size(2, 4, 200, 4, 1, 0, 1, BF16)
+    assert need >= 200 * 4  # one float32 partial per channel and time chunk at least
+    assert lib.dynconv_bwd_ex_workspace_size(2, 4, 200, 4, 1, 1, 1, BF16) > lib.dynconv_bwd_workspace_size(
+        2, 4, 200, 4, 1, 1, BF16)
+
+    def bx(dcb=DCB, wsp=P(0x900000), wsb=need, dx=DX):
+        return lib.dynconv_bwd_ex(X, S(800, 200, 1), W_, S(800 * 4, 200 * 4, 4, 1), None, None, DY, S(800, 200, 1), dx,
+                                  S(800, 200, 1), None, None, dcb, 2, 4, 200, 4, 1, BF16, wsp, wsb, None)
+
+    assert bx(wsb=need - 1) == WORKSPACE
+    assert bx(wsp=None, wsb=0) == WORKSPACE
+    assert bx(dcb=DX) == INVALID  # aliasing dx
+    assert bx(dcb=P(0xc0002)) == UNSUP
+    assert bx(dx=None) == INVALID  # neither dx nor dw
