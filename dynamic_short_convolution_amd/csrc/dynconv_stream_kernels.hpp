@@ -369,7 +369,9 @@ __device__ __forceinline__ float group_sum(float v, int lanes) {
 // ALL: both dx and dw are wanted, known at compile time (static filters only: their
 // runtime output tests had split every batch of loads into branches, 91.5 -> 79.1 us at
 // B8 T4096 D2048 W3; the other forms measured no gain).
-template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL, bool SEG>
+// CB: the convolution-bias gradient is wanted (sums of dy per chunk; a separate variant so
+// that the sweep without it carries no extra work).
+template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL, bool SEG, bool CB>
 __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams p) {
   using XR = Words<ET, VEC>;
   using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
@@ -444,9 +446,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
     float dyv[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) dyv[v] = have ? dyr.at(v) : 0.f;
-    if (main) {
+    if constexpr (CB) {
+      if (main) {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) sdy[v] += dyv[v];
+        for (int v = 0; v < VEC; ++v) sdy[v] += dyv[v];
+      }
     }
     if (main && want_dw) {
       float d[W][VEC];
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       step(tt, false, tt < p.T, hdy[e], hw[e], hx[e], hsid[e]);
     }
   }
-  if (p.cb_partial != nullptr) {
+  if constexpr (CB) {
     float* part = p.cb_partial + int64_t(wt.chunk) * p.D + wt.c0;
 #pragma unroll
     for (int v = 0; v < VEC; ++v) part[v] = sdy[v];
@@ -666,14 +670,23 @@ hipError_t launch_fwd_inst(const StreamParams& p, const StreamPlan& plan, hipStr
   return hipGetLastError();
 }
 
+template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL, bool SEG>
+void launch_bwd_cb(const StreamParams& p, const StreamPlan& plan, hipStream_t s) {
+  if (p.cb_partial != nullptr) {
+    hipLaunchKernelGGL((k_stream_bwd<ET, W, VEC, PERCH, STATIC, ALL, SEG, true>), dim3(unsigned(plan.blocks)),
+                       dim3(kBlockThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_stream_bwd<ET, W, VEC, PERCH, STATIC, ALL, SEG, false>), dim3(unsigned(plan.blocks)),
+                       dim3(kBlockThreads), 0, s, p);
+  }
+}
+
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL = false>
 hipError_t launch_bwd_inst(const StreamParams& p, const StreamPlan& plan, hipStream_t s) {
   if (p.seg != nullptr) {
-    hipLaunchKernelGGL((k_stream_bwd<ET, W, VEC, PERCH, STATIC, ALL, true>), dim3(unsigned(plan.blocks)),
-                       dim3(kBlockThreads), 0, s, p);
+    launch_bwd_cb<ET, W, VEC, PERCH, STATIC, ALL, true>(p, plan, s);
   } else {
-    hipLaunchKernelGGL((k_stream_bwd<ET, W, VEC, PERCH, STATIC, ALL, false>), dim3(unsigned(plan.blocks)),
-                       dim3(kBlockThreads), 0, s, p);
+    launch_bwd_cb<ET, W, VEC, PERCH, STATIC, ALL, false>(p, plan, s);
   }
   return hipGetLastError();
 }
