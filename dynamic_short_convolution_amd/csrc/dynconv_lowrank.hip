@@ -42,7 +42,7 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
 
 dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   hipStream_t stream) {
-  if (p.seg == nullptr && lowrank_fwd_fast_ok(p, W, dt)) {
+  if (lowrank_fwd_fast_ok(p, W, dt) && (p.seg == nullptr || lowrank_seg_fast_ok(p))) {
     const hipError_t e = launch_lowrank_fwd_fast(p, W, stream);
     return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
   }

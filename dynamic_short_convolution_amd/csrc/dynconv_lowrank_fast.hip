@@ -85,9 +85,14 @@ __device__ __forceinline__ f32x4_t mma32(const u16x8_t& a, const u16x8_t& b, f32
                                                  0, 0, 0);
 }
 
-template <int KS, int NWV_, int XN_, int XD_, int ZN_, int ZD_>
+template <int KS, int NWV_, int XN_, int XD_, int ZN_, int ZD_, int SG_ = 0>
 struct FwdFast {
   static constexpr int NWV = NWV_, XN = XN_, XD = XD_, ZN = ZN_, ZD = ZD_;
+  // SG: packed sequences. Each step also stages the segment ids of tokens t0 - 4 .. t0 + 63
+  // (17 chunks of 16 bytes, 5 per wave: every wave issues exactly one more transfer, right
+  // before its x transfers, so it is complete whenever x is).
+  static constexpr int SG = SG_;
+  static constexpr int SCH = 17, SPW = 5, SSTAGE = NWV_ * SPW * 16;
   static constexpr int NT = 64 * NWV;                // threads
   static constexpr int CPB = 16 * NWV;               // channels per workgroup
   static constexpr int XCPR = CPB / 8;               // 16-byte chunks of an x (or y) row
@@ -98,23 +103,26 @@ struct FwdFast {
   static constexpr int ZSTAGE = kStep * ZROW;
   static constexpr int Z_OFF = XN * XSTAGE;
   static constexpr int Y_OFF = Z_OFF + ZN * ZSTAGE;
-  static constexpr int BYTES = Y_OFF + 2 * XSTAGE;  // two y tiles
+  static constexpr int S_OFF = Y_OFF + 2 * XSTAGE;   // two y tiles, then the id stages
+  static constexpr int BYTES = S_OFF + (SG ? XN * SSTAGE : 0);
   static constexpr int XI = kStep * XCPR / 64 / NWV;  // x transfers per wave per step (2)
   static constexpr int ZI = kStep * ZCPR / 64 / NWV;  // z transfers per wave per step
   static constexpr int NS = kStep * XCPR / 64 / NWV;  // y stores per wave per step (2)
   static_assert((kStep * ZCPR) % (64 * NWV) == 0, "z transfers split evenly over the waves");
   static_assert(XD >= 1 && XD <= XN - 2 && ZD >= 1 && ZD <= ZN - 1 && ZD <= XD, "pipeline depths");
   static_assert((XCPR & (XCPR - 1)) == 0 && 16 % XCPR == 0, "x row rotation");
+  static_assert(!SG || NWV * SPW >= SCH, "id chunks spread over the waves");
+  static constexpr int XG = XI + SG;  // operations of the x group (ids first)
 
   // Issue order of one wave's vector memory operations: a prologue x(0), z(0), x(1),
   // z(1), ... (z only below ZD, x below XD); then step k issues x(k + XD), z(k + ZD) and,
   // from k = 1 on, the stores of step k - 1. Returns how many operations follow the later
   // of x(s) and z(s) when step s waits for them.
-  static constexpr int step_ops(int k) { return XI + ZI + (k >= 1 ? NS : 0); }
+  static constexpr int step_ops(int k) { return XG + ZI + (k >= 1 ? NS : 0); }
   static constexpr int prologue_end_x(int i) {
     int pos = 0;
-    for (int a = 0; a < i; ++a) pos += XI + (a < ZD ? ZI : 0);
-    return pos + XI;
+    for (int a = 0; a < i; ++a) pos += XG + (a < ZD ? ZI : 0);
+    return pos + XG;
   }
   static constexpr int prologue_ops() { return prologue_end_x(XD - 1) + (XD - 1 < ZD ? ZI : 0); }
   static constexpr int steps_before(int k) {
@@ -123,8 +131,8 @@ struct FwdFast {
     return pos;
   }
   static constexpr int wait_after(int s) {
-    const int end_x = s < XD ? prologue_end_x(s) : steps_before(s - XD) + XI;
-    const int end_z = s < ZD ? prologue_end_x(s) + ZI : steps_before(s - ZD) + XI + ZI;
+    const int end_x = s < XD ? prologue_end_x(s) : steps_before(s - XD) + XG;
+    const int end_z = s < ZD ? prologue_end_x(s) + ZI : steps_before(s - ZD) + XG + ZI;
     const int last = end_x > end_z ? end_x : end_z;
     return steps_before(s) - last;
   }
@@ -144,9 +152,9 @@ __device__ __forceinline__ void step_wait(int s) {
   }
 }
 
-template <int W, int KS>
+template <int W, int KS, int SG>
 __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRankParams p) {
-  using F = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD>;
+  using F = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD, SG>;
   constexpr int NWV = F::NWV, XN = F::XN, XD = F::XD, ZN = F::ZN, ZD = F::ZD, CPB = F::CPB;
   constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF, Y_OFF = F::Y_OFF;
@@ -214,6 +222,19 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
       }
     }
   };
+  // segment ids (SG): chunk sc = 5 wv + lane holds the ids of tokens t0 - 4 + 4 sc .. + 3
+  // (clamped into 0 .. T - 1: before t = 0 the x rows are zero, past T nothing is stored)
+  const int sc = F::SPW * wv + lane;
+  const bool sact = SG && lane < F::SPW && sc < F::SCH;
+  const char* sgc = SG ? reinterpret_cast<const char*>(p.seg + b * p.ss0) : nullptr;
+  auto issue_s = [&](int st, int t0) {
+    if constexpr (SG) {
+      if (sact) {
+        const int tk = min(max(t0 - 4 + 4 * sc, 0), p.T - 4);
+        dma16(sgc + int64_t(tk) * 4, smem + F::S_OFF + st * F::SSTAGE + wv * F::SPW * 16);
+      }
+    }
+  };
   auto issue_z = [&](int st, int t0) {
     unsigned char* zs = smem + Z_OFF + st * ZSTAGE;
     if (t0 + kStep <= p.T) {
@@ -276,6 +297,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   }
 #pragma unroll
   for (int i = 0; i < XD; ++i) {
+    issue_s(i, t_first + i * kStep);
     issue_x(i, t_first + i * kStep);
     if (i < ZD) issue_z(i, t_first + i * kStep);
   }
@@ -321,9 +343,18 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
     const int t0 = t_first + s * kStep;
     const int ux = s % XN, uz = s % ZN;
     step_wait<F, 0>(s);
+    issue_s((s + XD) % XN, t0 + XD * kStep);
     issue_x((s + XD) % XN, t0 + XD * kStep);
     issue_z((s + ZD) % ZN, t0 + ZD * kStep);
     if (s > 0) yflush((s - 1) & 1, t0 - kStep);
+    // ids of rows 4n - 4 .. 4n + 3 (tap k of the lane's token 4n + j: kept when the id of
+    // row 4n + j - k equals that of row 4n + j)
+    int idv[8] = {};
+    if constexpr (SG) {
+      const int* ids = reinterpret_cast<const int*>(smem + F::S_OFF + ux * F::SSTAGE) + 4 * n;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) idv[i] = ids[i];
+    }
     // x rows 4n + MLO .. 4n + 3 of the lane's channels, as float32
     const unsigned char* xst = smem + ux * XSTAGE;
     const int lo = xlo + (ux == 0 ? xwrap : 0);
@@ -363,7 +394,10 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
         const float xt = xv[j - MLO][mt];
         float y = fmaf(a[mt][0], xt, xt);
 #pragma unroll
-        for (int k = 1; k < W; ++k) y = fmaf(a[mt][k], xv[j - k - MLO][mt], y);
+        for (int k = 1; k < W; ++k) {
+          const float ak = (!SG || idv[j + 4 - k] == idv[j + 4]) ? a[mt][k] : 0.f;
+          y = fmaf(ak, xv[j - k - MLO][mt], y);
+        }
         yv[mt] = y;
       }
       *reinterpret_cast<u32x2*>(yt + j * XROW) = u32x2{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
@@ -378,7 +412,11 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
 
 template <int W, int KS>
 hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((k_lowrank_fwd_fast<W, KS>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_lowrank_fwd_fast<W, KS, 1>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_lowrank_fwd_fast<W, KS, 0>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -979,9 +1017,6 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
   }
 }
 
-template <int KS>
-using FwdCfg = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD>;
-
 // A rank of 32 KS is served when its z transfers split evenly over the waves.
 constexpr bool fwd_fast_rank_ok(int ks) {
   return (ks == 1 || ks == 2 || ks == 4) && (kStep * 4 * ks) % (64 * LRF_NWV) == 0;
@@ -1016,7 +1051,7 @@ hipError_t fwd_fast_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
 template <int KS>
 constexpr int fwd_fast_lds_ks() {
   if constexpr (fwd_fast_rank_ok(KS)) {
-    return FwdCfg<KS>::BYTES;
+    return FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD, 1>::BYTES;  // with the id stages
   } else {
     return 160 * 1024;
   }
@@ -1034,6 +1069,12 @@ bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
          p.D % (16 * LRF_NWV) == 0 && p.act16 != 0 && p.z16 != 0 &&
          (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) && int64_t(kStep) * p.xs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.zs1 < (int64_t(1) << 30);
+}
+
+bool lowrank_seg_fast_ok(const LowRankParams& p) {
+  // id rows contiguous and 16-byte aligned, whole 16-byte chunks of ids
+  return p.seg != nullptr && p.ss1 == 1 && reinterpret_cast<uintptr_t>(p.seg) % 16 == 0 && p.ss0 % 4 == 0 &&
+         p.T % 4 == 0 && p.T >= 4;
 }
 
 LowRankPlan plan_lowrank_fwd_fast(int64_t B, int64_t T, int64_t D, int ks) {

@@ -76,6 +76,8 @@ dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& pla
                                   hipStream_t stream);
 // bf16 fast forward (LDS DMA pipeline; W <= 4, R in {32, 64, 128}, H == 1, 16-byte
 // aligned rows, D a multiple of 64). It plans its own token ranges.
+// Packed sequences on the fast forward: contiguous, 16-byte aligned id rows, T % 4 == 0.
+bool lowrank_seg_fast_ok(const LowRankParams& p);
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
 hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t stream);
 // bf16 fast dx of the backward (same conditions, on dy and dx); it plans its own ranges.

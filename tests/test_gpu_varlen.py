@@ -186,3 +186,21 @@ def test_full_packed_perchannel_sampled():
     assert_close("dx", dxs, rdx, torch.bfloat16)
     assert_close("dw", dws, rdw, torch.bfloat16)
     torch.cuda.empty_cache()
+
+
+def test_full_packed_lowrank_sampled():
+    """B8 T4096 D2048 W4 R64 with documents of mean length 512 (the fast forward with
+    segment ids and the general backward), every token of sampled channel blocks."""
+    wl = synth.workloads()["lowrank_r64"]
+    x, z, U, b = wl.x(), wl.z(), wl.U(), wl.b()
+    W = wl.W
+    seq = synth.segments(wl.B, wl.T, 512.0, wl.seed, first=(1, 2, 3))
+    xg, zg, Ug, bg, sg = x.cuda(), z.cuda(), U.cuda(), b.cuda(), seq.cuda()
+    ci = torch.as_tensor(np.concatenate([np.arange(0, 64), np.arange(1984, 2048)]))
+    cols = torch.as_tensor((ci.numpy()[:, None] * W + np.arange(W)[None, :]).reshape(-1))
+    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, seq_idx=sg).index_select(2, ci.cuda()).cpu()
+    del xg
+    ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
+                      to64(b.index_select(0, cols)), W, 1, seq.numpy())
+    assert_close("y", y, ref, torch.bfloat16)
+    torch.cuda.empty_cache()
