@@ -435,9 +435,12 @@ hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) 
 // three rows, and the first step's first three rows belong to the previous range.
 // dy rows at or past T are zeroed, so the tail contributes nothing past the sequence.
 // ---------------------------------------------------------------------------------
-template <int KS>
+template <int KS, int SG = 0>
 struct BwdDxFast {
   static constexpr int NWV = 4;
+  // SG: packed sequences; the ids of tokens t0 - 4 .. t0 + 63 ride with each step's dy
+  // (one more transfer per wave, issued first)
+  static constexpr int SCH = 17, SPW = 5, SSTAGE = NWV * SPW * 16;
   static constexpr int CPB = 64;
   static constexpr int XCPR = 8, XROW = 128;
   static constexpr int XSTAGE = kStep * XROW;        // dy stage, dx tile
@@ -446,13 +449,14 @@ struct BwdDxFast {
   static constexpr int ZSTAGE = kStep * ZROW;
   static constexpr int Z_OFF = 2 * XSTAGE;            // two dy stages
   static constexpr int T_OFF = Z_OFF + 2 * ZSTAGE;    // two z stages, then two dx tiles
-  static constexpr int BYTES = T_OFF + 2 * XSTAGE;
+  static constexpr int S_OFF = T_OFF + 2 * XSTAGE;    // then two id stages (SG)
+  static constexpr int BYTES = S_OFF + (SG ? 2 * SSTAGE : 0);
   static constexpr int DI = 2, ZI = KS, ND = DI + ZI, NS = 2;
 };
 
-template <int W, int KS>
+template <int W, int KS, int SG>
 __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams p) {
-  using F = BwdDxFast<KS>;
+  using F = BwdDxFast<KS, SG>;
   constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF, T_OFF = F::T_OFF;
   __shared__ __align__(16) unsigned char smem[F::BYTES];
@@ -494,9 +498,19 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
     zrl[i] = rl;
     zoff[i] = uint32_t(rl * int(p.zs1) + 8 * c) * 2u;
   }
+  // segment ids (SG): chunk sc = 5 wv + lane holds the ids of tokens t0 - 4 + 4 sc .. + 3
+  const int sc = F::SPW * wv + lane;
+  const bool sact = SG && lane < F::SPW && sc < F::SCH;
+  const char* sgc = SG ? reinterpret_cast<const char*>(p.seg + b * p.ss0) : nullptr;
   auto issue = [&](int st, int t0) {
     unsigned char* ds = smem + st * XSTAGE;
     unsigned char* zs = smem + Z_OFF + st * ZSTAGE;
+    if constexpr (SG) {
+      if (sact) {
+        const int tk = min(max(t0 - 4 + 4 * sc, 0), p.T - 4);
+        dma16(sgc + int64_t(tk) * 4, smem + F::S_OFF + st * F::SSTAGE + wv * F::SPW * 16);
+      }
+    }
     if (t0 + kStep <= p.T) {
       const char* dg = dyc + int64_t(t0) * p.dys1 * 2;
       const char* zg = zc + int64_t(t0) * p.zs1 * 2;
@@ -627,6 +641,14 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
       }
     }
     const unsigned char* zs = smem + Z_OFF + u * ZSTAGE;
+    // ids of rows 4n - 4 .. 4n + 3 (SG): the term of tap k of token 4n + jp is kept when
+    // row 4n + jp - k has the id of row 4n + jp
+    int idv[8] = {};
+    if constexpr (SG) {
+      const int* ids = reinterpret_cast<const int*>(smem + F::S_OFF + u * F::SSTAGE) + 4 * n;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) idv[i] = ids[i];
+    }
     auto gen = [&](int j, f32x4_t (&acc)[4]) {
       u16x8_t bfr[KS];
 #pragma unroll
@@ -657,12 +679,14 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         const int j = jp - k;
+        const bool keep = !SG || k == 0 || idv[4 + jp - k] == idv[4 + jp];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
+          const float ak = keep ? a[c][k] : 0.f;
           if (j >= 0) {
-            own[j][c] = fmaf(a[c][k], dyv[jp][c], own[j][c]);
+            own[j][c] = fmaf(ak, dyv[jp][c], own[j][c]);
           } else {
-            out[4 + j][c] = fmaf(a[c][k], dyv[jp][c], out[4 + j][c]);
+            out[4 + j][c] = fmaf(ak, dyv[jp][c], out[4 + j][c]);
           }
         }
       }
@@ -749,21 +773,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16-byte chunks are rotated by 2 row so that the 4 rows of a transposing read hit
 // distinct banks.
 // ---------------------------------------------------------------------------------
-template <int KS>
+template <int KS, int SG_ = 0>
 struct BwdGduFast {
   static constexpr int CPR = 8, ROW = 128, STAGE = kStep * ROW;  // x, dy: 64 channels
   static constexpr int ZCPR = 4 * KS, ZROW = 16 * ZCPR, ZSTAGE = kStep * ZROW;
+  // SG: packed sequences. The ids of tokens t0 - 4 .. t0 + 63 ride with each step (one
+  // more transfer per wave, issued first). The stages then load one step ahead instead of
+  // two (two dy / z stages, 16 KiB less), which keeps two workgroups per CU at R = 64 with
+  // the id stages (80 KiB each without them).
+  static constexpr int SG = SG_;
+  static constexpr int DIST = SG ? 1 : 2;   // steps loaded ahead
   static constexpr int XN = 4;   // x ring: the step, the previous one, two in flight
-  static constexpr int SN = 3;   // dy and z stages: the step and two in flight
+  static constexpr int SN = DIST + 1;       // dy and z stages: the step and those in flight
+  static constexpr int SCH = 17, SPW = 5, SSTAGE = 4 * SPW * 16;
   static constexpr int D_OFF = XN * STAGE;
   static constexpr int Z_OFF = D_OFF + SN * STAGE;
-  static constexpr int BYTES = Z_OFF + SN * ZSTAGE;
-  static constexpr int XI = 2, DI = 2, ZI = KS, ND = XI + DI + ZI;
+  static constexpr int S_OFF = Z_OFF + SN * ZSTAGE;
+  static constexpr int BYTES = S_OFF + (SG ? SN * SSTAGE : 0);
+  static constexpr int XI = 2, DI = 2, ZI = KS, ND = XI + DI + ZI + SG;
 };
 
-template <int W, int KS>
+template <int W, int KS, int SG>
 __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParams p) {
-  using F = BwdGduFast<KS>;
+  using F = BwdGduFast<KS, SG>;
   constexpr int CPR = F::CPR, ROW = F::ROW, STAGE = F::STAGE, XN = F::XN;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, D_OFF = F::D_OFF, Z_OFF = F::Z_OFF;
   constexpr int RT = 2 * KS;  // 16-rank tiles
@@ -808,10 +840,19 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
     zrl[i] = rl;
     zoff[i] = uint32_t(rl * int(p.zs1) + 8 * c) * 2u;
   }
+  const int sc = F::SPW * wv + lane;
+  const bool sact = SG && lane < F::SPW && sc < F::SCH;
+  const char* sgc = SG ? reinterpret_cast<const char*>(p.seg + b * p.ss0) : nullptr;
   auto issue = [&](int s, int t0) {
     unsigned char* xs = smem + (s % XN) * STAGE;
     unsigned char* ds = smem + D_OFF + (s % F::SN) * STAGE;
     unsigned char* zs = smem + Z_OFF + (s % F::SN) * ZSTAGE;
+    if constexpr (SG) {
+      if (sact) {
+        const int tk = min(max(t0 - 4 + 4 * sc, 0), p.T - 4);
+        dma16(sgc + int64_t(tk) * 4, smem + F::S_OFF + (s % F::SN) * F::SSTAGE + wv * F::SPW * 16);
+      }
+    }
     if (t0 + kStep <= p.T) {
       const int64_t o1 = int64_t(t0) * 2;
 #pragma unroll
@@ -851,7 +892,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
     }
   }
   issue(0, t_first);
-  if (nsteps > 1) issue(1, t_first + kStep);
+  if (F::DIST > 1 && nsteps > 1) issue(1, t_first + kStep);
 
   // Transposing-read addresses. Lane (j, q) reads 8 bytes of row 8q + j/4 (+ 4), channel
   // columns 16 wv + 4 (j % 4) .. + 3; lane i then holds column 16 wv + i of 4 rows.
@@ -882,13 +923,14 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
 
   for (int s = 0; s < nsteps; ++s) {
     const int t0 = t_first + s * kStep;
-    // this step's transfers were followed by the next step's, if there is one
-    if (s + 1 < nsteps) {
+    // this step's transfers were followed by the next step's, if there is one (loading two
+    // steps ahead); loading one step ahead, nothing newer is in flight
+    if (F::DIST > 1 && s + 1 < nsteps) {
       vm_wait_barrier<F::ND>();
     } else {
       vm_wait_barrier<0>();
     }
-    if (s + 2 < nsteps) issue(s + 2, t0 + 2 * kStep);
+    if (s + F::DIST < nsteps) issue(s + F::DIST, t0 + F::DIST * kStep);
     const int ux = s % XN;
     const uint32_t dsa = lds0 + D_OFF + (s % F::SN) * STAGE;
     const uint32_t zsa = lds0 + Z_OFF + (s % F::SN) * ZSTAGE;
@@ -947,6 +989,15 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
 #pragma unroll
         for (int e = 0; e < 8; ++e) dyv[e] = tk + e < p.T ? dyv[e] : 0.f;
       }
+      // ids of rows rb - 4 .. rb + 7, rb = 32 kk + 8 q (SG): g_k of token rb + e is kept
+      // when row rb + e - k has the id of row rb + e
+      int idv[12] = {};
+      if constexpr (SG) {
+        const int* ids =
+            reinterpret_cast<const int*>(smem + F::S_OFF + (s % F::SN) * F::SSTAGE) + 32 * kk + 8 * q;
+#pragma unroll
+        for (int i = 0; i < 12; ++i) idv[i] = ids[i];
+      }
       u16x8_t bz[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -959,7 +1010,8 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
         float sum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          g[e] = dyv[e] * xv[4 + e - k];
+          const bool keep = !SG || k == 0 || idv[4 + e - k] == idv[4 + e];
+          g[e] = keep ? dyv[e] * xv[4 + e - k] : 0.f;
           sum += g[e];
         }
         db[k] += sum;
@@ -1119,7 +1171,11 @@ namespace {
 
 template <int W, int KS>
 hipError_t bwd_dx_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<W, KS>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -1145,7 +1201,11 @@ bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
 
 template <int W, int KS>
 hipError_t bwd_gdu_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<W, KS>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -1543,8 +1543,9 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   // bf16 fast path: dx, then the partial sums of dU and db, each by its own kernel;
   // otherwise one main kernel (the channel slices inside D on the 16-byte path, the rest on
   // the other)
-  // (packed sequences take the general kernels)
-  const bool fast = p.seg == nullptr && std::is_same<ET, bf16_t>::value && lowrank_bwd_dx_fast_ok(p, W, DYNCONV_BF16);
+  // (packed sequences: with contiguous, aligned id rows and T % 4 == 0)
+  const bool fast = (p.seg == nullptr || lowrank_seg_fast_ok(p)) && std::is_same<ET, bf16_t>::value &&
+                    lowrank_bwd_dx_fast_ok(p, W, DYNCONV_BF16);
   LowRankParams q = p;
   const int64_t per_slice = int64_t(p.B) * pl.nTr;
   const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;

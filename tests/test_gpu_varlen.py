@@ -199,8 +199,32 @@ def test_full_packed_lowrank_sampled():
     ci = torch.as_tensor(np.concatenate([np.arange(0, 64), np.arange(1984, 2048)]))
     cols = torch.as_tensor((ci.numpy()[:, None] * W + np.arange(W)[None, :]).reshape(-1))
     y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, seq_idx=sg).index_select(2, ci.cuda()).cpu()
-    del xg
-    ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
-                      to64(b.index_select(0, cols)), W, 1, seq.numpy())
+    s64 = seq.numpy()
+    U64s, b64s = to64(U.index_select(1, cols)), to64(b.index_select(0, cols))
+    ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), U64s, b64s, W, 1, s64)
     assert_close("y", y, ref, torch.bfloat16)
+    # backward (the fast kernels with segment ids): dx, dU and db on the sampled channels;
+    # dz needs every channel, so it is checked exactly on a few tokens
+    dy = wl.dy()
+    dx, dz, dU, db = dynconv_lowrank_bwd(xg, zg, Ug, bg, dy.cuda(), W, seq_idx=sg)
+    dxs, dUs, dbs = dx.index_select(2, ci.cuda()).cpu(), dU.index_select(1, cols.cuda()).cpu(), db[cols.cuda()].cpu()
+    dz = dz.cpu()
+    del xg, dx
+    rdx, _, rdU, rdb = lowrank_bwd(to64(x.index_select(2, ci)), to64(z), U64s, b64s, to64(dy.index_select(2, ci)),
+                                   W, 1, s64)
+    assert_close("dx", dxs, rdx, torch.bfloat16)
+    # g is rounded to bf16 as a matrix-core operand: allow 2^-8 of sum |z| |g| (as elsewhere)
+    x64s, dy64s = to64(x.index_select(2, ci)), to64(dy.index_select(2, ci))
+    _, gabs = conv_bwd(np.abs(x64s), np.zeros(x64s.shape + (W,)), np.abs(dy64s), 1, s64)
+    gabs = gabs.reshape(-1, len(ci) * W)
+    extra_dU = 2.0**-8 * (np.abs(to64(z)).reshape(-1, z.shape[-1]).T @ gabs)
+    assert_close("dU", dUs, rdU, torch.bfloat16, rtol=1e-5, atol=1e-5, extra=extra_dU)
+    assert_close("db", dbs, rdb, torch.bfloat16, rtol=1e-5, atol=1e-5)
+    for bb, t in ((0, 0), (0, 1), (0, 5), (3, 511), (3, 512), (7, 2047), (7, 4095)):
+        lo = max(0, t - W + 1)
+        xw, dyw = to64(x[bb : bb + 1, lo : t + 1]), to64(dy[bb : bb + 1, lo : t + 1])
+        zw, sw = to64(z[bb : bb + 1, lo : t + 1]), s64[bb : bb + 1, lo : t + 1]
+        _, rdz, _, _ = lowrank_bwd(xw, zw, to64(U), to64(b), dyw, W, 1, sw)
+        # the window's last row is token t; its g needs only x_{t-k}, which the window holds
+        assert_close(f"dz[{bb},{t}]", dz[bb, t], rdz[0, -1], torch.bfloat16, extra=2.0**-8 * np.abs(rdz[0, -1]).max())
     torch.cuda.empty_cache()
