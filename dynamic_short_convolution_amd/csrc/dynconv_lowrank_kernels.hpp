@@ -1312,20 +1312,30 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
 // lane, no registers involved) into a ring of NST stages, two chunks ahead of the one
 // being computed. Each wave waits for its own transfers (vmcnt) and a barrier publishes
 // the stage; nothing else needs the loads, so no other wait is tied to them.
+// A chunk is 32 filter groups: 32 channels per-channel, 32 * HG channels when HG
+// consecutive channels share a filter (HG = 2 or 4). The filter columns of consecutive
+// groups are consecutive in U, so a chunk's U tile is 32 * W whole columns for every HG;
+// a lane owns 8 groups (HG 16-byte runs of x and dy per row) and sums its products over
+// the HG channels of a group before the matrix-core step (1/HG of the per-channel
+// matrix work, and U read 1/HG as often).
 // LDS rows are rotated by chunk so that the 16 lanes of a group that read the same
 // logical chunk of 16 different rows hit distinct banks:
 //   U row r (UCPR chunks): logical chunk c sits at (c + r % 16) % UCPR;
-//   x / dy row (4 chunks): logical chunk c sits at (c + row / 4) % 4.
+//   x / dy row (XCPR = 4 * HG chunks, 64 * HG bytes): logical chunk c sits at
+//   (c + row / (4 / HG)) % XCPR, so that the rows of one 256-byte bank sweep differ.
 // ---------------------------------------------------------------------------------
-template <int W, int KS>
+template <int W, int KS, int HG>
 struct LrDzDma {
+  static_assert(HG == 1 || HG == 2 || HG == 4, "group size of the DMA dz path");
   static constexpr int RP = 32 * KS;
-  static constexpr int CH = kLowrankDzChunk;
+  static constexpr int CH = kLowrankDzChunk;   // filter groups of a chunk
+  static constexpr int CHC = CH * HG;          // channels of a chunk
   static constexpr int UC = CH * W;            // filter columns of a chunk
   static constexpr int UCPR = UC / 8;          // 16-byte chunks of a U row
   static constexpr int TB = kLowrankDzTokens;
   static constexpr int XR = TB + HALO;
-  static constexpr int XCPR = CH / 8;          // 16-byte chunks of an x / dy row
+  static constexpr int XCPR = CHC / 8;         // 16-byte chunks of an x / dy row
+  static constexpr int RPB = 4 / HG;           // x / dy rows per 256 bytes
   static constexpr int UCH = RP * UCPR, XCH = XR * XCPR, DCH = TB * XCPR;
   static constexpr int NI_U = (UCH + 63) / 64, NI_X = (XCH + 63) / 64, NI_D = (DCH + 63) / 64;
   static constexpr int NI = NI_U + NI_X + NI_D;  // wave-wide transfers per stage
@@ -1334,7 +1344,9 @@ struct LrDzDma {
   static constexpr int STAGE = D_OFF + NI_D * 64 * 16;
   static constexpr int NST = 3;
   static constexpr int BYTES = NST * STAGE;
-  static_assert(XCPR == 4 && UC % 8 == 0, "dz DMA tiling");
+  static_assert(XCPR == 4 * HG && UC % 8 == 0, "dz DMA tiling");
+  // physical 16-byte slot of logical chunk c of x / dy row `row`
+  static __device__ __forceinline__ int xslot(int row, int c) { return (c + row / RPB) & (XCPR - 1); }
 };
 
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
@@ -1350,19 +1362,19 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int W, int KS>
+template <int W, int KS, int HG>
 __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned char* smem, int b, int tb0) {
-  using D = LrDzDma<W, KS>;
-  constexpr int RP = D::RP, CH = D::CH, UC = D::UC, UCPR = D::UCPR;
+  using D = LrDzDma<W, KS, HG>;
+  constexpr int RP = D::RP, CH = D::CH, UC = D::UC, UCPR = D::UCPR, XCPR = D::XCPR;
   constexpr int RTN = RP / 16;
-  constexpr int CR = CH / 4;   // channels of a lane group (one 16-byte chunk)
-  constexpr int KST = W;       // K steps per chunk: CR * W columns / 8
+  constexpr int GL = CH / 4;   // filter groups of a lane (HG 16-byte runs of channels)
+  constexpr int KST = W;       // K steps per chunk: GL * W columns / 8
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = lane >> 4;
   const int n = lane & 15;
   const int wv = tid >> 6;
-  const int nchunk = p.D / CH;
+  const int nchunk = p.D / D::CHC;
   const bf16_t* U = static_cast<const bf16_t*>(p.U);
   const bf16_t* xb = static_cast<const bf16_t*>(p.x) + b * p.xs0 + int64_t(tb0 - HALO) * p.xs1;
   const bf16_t* dyb = static_cast<const bf16_t*>(p.dy) + b * p.dys0 + int64_t(tb0) * p.dys1;
@@ -1383,7 +1395,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 #pragma unroll
   for (int i = 0; i < SX; ++i) {
     const int pidx = (wv + 4 * i) * 64 + lane;
-    const int row = pidx / 4, c = ((pidx % 4) - (row >> 2)) & 3;
+    const int row = pidx / XCPR, c = ((pidx % XCPR) - row / D::RPB) & (XCPR - 1);
     xact[i] = pidx < D::XCH;
     // rows before token 0 read token 0 instead (their products are zeroed below)
     xoffg[i] = max(row, HALO - tb0) * int(p.xs1) + c * 8;
@@ -1391,7 +1403,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 #pragma unroll
   for (int i = 0; i < SD; ++i) {
     const int pidx = (wv + 4 * i) * 64 + lane;
-    const int row = pidx / 4, c = ((pidx % 4) - (row >> 2)) & 3;
+    const int row = pidx / XCPR, c = ((pidx % XCPR) - row / D::RPB) & (XCPR - 1);
     dact[i] = pidx < D::DCH;
     doffg[i] = row * int(p.dys1) + c * 8;
   }
@@ -1399,9 +1411,9 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
   constexpr int NMIN = D::NI_U / 4 + D::NI_X / 4 + D::NI_D / 4;
   auto issue = [&](int st, int ci) {
     ci = min(ci, nchunk - 1);  // past the last chunk: reload it (never read)
-    const int c0 = ci * CH;
+    const int c0 = ci * D::CHC;  // first channel; the chunk's filter columns start at ci * CH * W
     unsigned char* stage = smem + st * D::STAGE;
-    const bf16_t* ub = U + int64_t(c0) * W;
+    const bf16_t* ub = U + int64_t(ci) * (CH * W);
 #pragma unroll
     for (int i = 0; i < SU; ++i)
       if (uact[i]) dma16(ub + uoffg[i], stage + (wv + 4 * i) * 1024);
@@ -1415,12 +1427,16 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 
   // per-lane LDS byte offsets inside a stage
   const int nt = wv * TT + n;  // the lane's token within the block
-  const int dy_off = D::D_OFF + nt * 64 + ((q + (nt >> 2)) & 3) * 16;
-  int x_off[W];
+  // the lane's runs are logical chunks q * HG + h of its rows
+  int dy_off[HG], x_off[W][HG];
 #pragma unroll
-  for (int k = 0; k < W; ++k) {
-    const int row = nt + HALO - k;
-    x_off[k] = D::X_OFF + row * 64 + ((q + (row >> 2)) & 3) * 16;
+  for (int h = 0; h < HG; ++h) {
+    dy_off[h] = D::D_OFF + nt * (XCPR * 16) + D::xslot(nt, q * HG + h) * 16;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      const int row = nt + HALO - k;
+      x_off[k][h] = D::X_OFF + row * (XCPR * 16) + D::xslot(row, q * HG + h) * 16;
+    }
   }
   int u_off[KST];  // row rt * 16 + n adds rt * 16 * UC * 2 bytes (same rotation)
 #pragma unroll
@@ -1453,24 +1469,40 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
     vm_wait_barrier<NMIN>();
     issue((ci + 2) % D::NST, ci + 2);
     const unsigned char* stage = smem + (ci % D::NST) * D::STAGE;
-    uint32_t dw_[4], xw[W][4];
-    {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + dy_off);
-      dw_[0] = v[0]; dw_[1] = v[1]; dw_[2] = v[2]; dw_[3] = v[3];
-    }
+    // words of the lane's dy run and x runs (taps 0 .. W-1); channel j of the lane is
+    // word (j % 8) / 2 of run j / 8
+    uint32_t dw_[HG][4], xw[W][HG][4];
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + x_off[k]);
-      xw[k][0] = v[0]; xw[k][1] = v[1]; xw[k][2] = v[2]; xw[k][3] = v[3];
+    for (int h = 0; h < HG; ++h) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + dy_off[h]);
+      dw_[h][0] = v[0]; dw_[h][1] = v[1]; dw_[h][2] = v[2]; dw_[h][3] = v[3];
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(stage + x_off[k][h]);
+        xw[k][h][0] = u[0]; xw[k][h][1] = u[1]; xw[k][h][2] = u[2]; xw[k][h][3] = u[3];
+      }
     }
     if (cut) {
 #pragma unroll
       for (int k = 1; k < W; ++k)
-        if (!tp[k]) xw[k][0] = xw[k][1] = xw[k][2] = xw[k][3] = 0u;
-    }
-    float dyf[CR];
 #pragma unroll
-    for (int c = 0; c < CR; ++c) dyf[c] = (c & 1) ? bf16_hi(dw_[c >> 1]) : bf16_lo(dw_[c >> 1]);
+        for (int h = 0; h < HG; ++h)
+          if (!tp[k]) xw[k][h][0] = xw[k][h][1] = xw[k][h][2] = xw[k][h][3] = 0u;
+    }
+    float dyf[8 * HG];
+#pragma unroll
+    for (int j = 0; j < 8 * HG; ++j) dyf[j] = (j & 1) ? bf16_hi(dw_[j >> 3][(j & 7) >> 1]) : bf16_lo(dw_[j >> 3][(j & 7) >> 1]);
+    // column (group g of the lane, tap k): the sum over the group's HG channels
+    auto col = [&](int g, int k) -> float {
+      auto prod = [&](int j) {
+        const uint32_t wd = xw[k][j >> 3][(j & 7) >> 1];
+        return dyf[j] * ((j & 1) ? bf16_hi(wd) : bf16_lo(wd));
+      };
+      float v = prod(g * HG);
+#pragma unroll
+      for (int h = 1; h < HG; ++h) v += prod(g * HG + h);
+      return v;
+    };
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
       Mfma<bf16_t>::F32k bfr;
@@ -1478,9 +1510,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
       for (int e = 0; e < 8; e += 2) {
         const int c0_ = (8 * ks + e) / W, k0_ = (8 * ks + e) % W;
         const int c1_ = (8 * ks + e + 1) / W, k1_ = (8 * ks + e + 1) % W;
-        const float x0 = (c0_ & 1) ? bf16_hi(xw[k0_][c0_ >> 1]) : bf16_lo(xw[k0_][c0_ >> 1]);
-        const float x1 = (c1_ & 1) ? bf16_hi(xw[k1_][c1_ >> 1]) : bf16_lo(xw[k1_][c1_ >> 1]);
-        const uint32_t w2 = pack_bf16x2(dyf[c0_] * x0, dyf[c1_] * x1);
+        const uint32_t w2 = pack_bf16x2(col(c0_, k0_), col(c1_, k1_));
         bfr.v[e] = uint16_t(w2 & 0xffffu);
         bfr.v[e + 1] = uint16_t(w2 >> 16);
       }
@@ -1506,23 +1536,38 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 }
 
 // The LDS DMA path serves bf16 token blocks that lie inside T when its stages fit.
-template <typename ET, int W, int KS>
+template <typename ET, int W, int KS, int HG>
 constexpr bool lowrank_dz_dma_ok() {
-  return std::is_same<ET, bf16_t>::value && LrDzDma<W, KS>::BYTES <= 150 * 1024;
+  return std::is_same<ET, bf16_t>::value && LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
 }
 
-// DMA: the LDS DMA path (the launch covers whole token blocks, aligned rows, D % 32 == 0
-// and R % 32 == 0); otherwise the register-staged path with element loads where needed.
-template <typename ET, int W, int KS, bool DMA>
+// The register-staged path: any storage type, ragged token blocks, unaligned rows, any
+// group size (head-wise: each channel's column of U loaded element by element).
+template <typename ET, int W, int KS>
 __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParams p) {
-  if constexpr (DMA) {
-    __shared__ __align__(16) unsigned char smem[LrDzDma<W, KS>::BYTES];
-    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    lowrank_dz_dma<W, KS>(p, smem, int(lb / uint32_t(p.nTbL)),
-                          (p.tbb0 + int(lb % uint32_t(p.nTbL))) * kLowrankDzTokens);
+  __shared__ LrDzSmem<ET, W, KS> sm;
+  lowrank_dz_body<ET, W, KS>(p, sm);
+}
+
+// The LDS DMA path: the launch covers whole token blocks; aligned rows, D % (32 * HG) == 0
+// and R % 32 == 0.
+template <int W, int KS, int HG>
+__global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz_dma(const LowRankParams p) {
+  __shared__ __align__(16) unsigned char smem[LrDzDma<W, KS, HG>::BYTES];
+  const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  lowrank_dz_dma<W, KS, HG>(p, smem, int(lb / uint32_t(p.nTbL)),
+                            (p.tbb0 + int(lb % uint32_t(p.nTbL))) * kLowrankDzTokens);
+}
+
+// Launches the DMA dz kernel for group size HG over q.nTbL whole token blocks per sequence.
+template <typename ET, int W, int KS, int HG>
+hipError_t launch_dz_dma(const LowRankParams& q, hipStream_t s) {
+  if constexpr (lowrank_dz_dma_ok<ET, W, KS, HG>()) {
+    hipLaunchKernelGGL((k_lowrank_dz_dma<W, KS, HG>), dim3(unsigned(int64_t(q.B) * q.nTbL)), dim3(kBlockThreads), 0,
+                       s, q);
+    return hipGetLastError();
   } else {
-    __shared__ LrDzSmem<ET, W, KS> sm;
-    lowrank_dz_body<ET, W, KS>(p, sm);
+    return hipErrorInvalidValue;
   }
 }
 
@@ -1571,24 +1616,27 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // dz: token blocks inside T on the DMA path, the rest on the register path
+  // dz: token blocks inside T on the DMA path (group sizes 1, 2, 4 whose stages fit), the
+  // rest on the register path
   const int nblk = (p.T + kLowrankDzTokens - 1) / kLowrankDzTokens;
-  const bool dma = lowrank_dz_dma_ok<ET, W, KS>() && p.H == 1 && p.act16 != 0 && p.u16 != 0 &&
-                   p.D % kLowrankDzChunk == 0 && p.R % 32 == 0;
+  const bool hg_ok = p.H == 1   ? lowrank_dz_dma_ok<ET, W, KS, 1>()
+                     : p.H == 2 ? lowrank_dz_dma_ok<ET, W, KS, 2>()
+                     : p.H == 4 ? lowrank_dz_dma_ok<ET, W, KS, 4>()
+                                : false;
+  const bool dma = hg_ok && p.act16 != 0 && p.u16 != 0 && p.D % (kLowrankDzChunk * p.H) == 0 && p.R % 32 == 0;
   const int nfb = dma ? p.T / kLowrankDzTokens : 0;
   if (nfb > 0) {
     q.tbb0 = 0;
     q.nTbL = nfb;
-    hipLaunchKernelGGL((k_lowrank_dz<ET, W, KS, lowrank_dz_dma_ok<ET, W, KS>()>), dim3(unsigned(int64_t(p.B) * nfb)),
-                       dim3(kBlockThreads), 0, s, q);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = p.H == 1   ? launch_dz_dma<ET, W, KS, 1>(q, s)
+                         : p.H == 2 ? launch_dz_dma<ET, W, KS, 2>(q, s)
+                                    : launch_dz_dma<ET, W, KS, 4>(q, s);
     if (e != hipSuccess) return e;
   }
   if (nfb < nblk) {
     q.tbb0 = nfb;
     q.nTbL = nblk - nfb;
-    hipLaunchKernelGGL((k_lowrank_dz<ET, W, KS, false>), dim3(unsigned(int64_t(p.B) * q.nTbL)), dim3(kBlockThreads), 0,
-                       s, q);
+    hipLaunchKernelGGL((k_lowrank_dz<ET, W, KS>), dim3(unsigned(int64_t(p.B) * q.nTbL)), dim3(kBlockThreads), 0, s, q);
   }
   return hipGetLastError();
 }

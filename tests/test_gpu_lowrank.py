@@ -257,3 +257,34 @@ def test_headwise_lowrank_parity(dtype, H, W, R):
     rt = torch.float32 if td == torch.float32 else td
     assert_close("dU", dU, rdU, rt, rtol=1e-5, atol=1e-5, extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
     assert_close("db", db, rdb, rt, rtol=1e-5, atol=1e-5)
+
+
+# head-wise dz on the LDS DMA path: bf16, group sizes 2 and 4, chunks of 32 groups
+# (32 * H channels) over five chunks so that the three-stage ring wraps, three whole
+# 64-token blocks and a ragged tail of 8 tokens (register path); every R that divides
+# into 32-row tiles, every W (the shapes whose stages do not fit take the register path)
+HEADWISE_DMA = [(H, W, R) for H in (2, 4) for W in (1, 2, 3, 4, 5) for R in (32, 64, 96, 128)]
+
+
+@pytest.mark.parametrize("H,W,R", HEADWISE_DMA)
+def test_headwise_lowrank_dz_dma(H, W, R):
+    B, T = 2, 200
+    D = 5 * 32 * H
+    G = D // H
+    seed = 900 + 10 * H + W + R
+    x = synth.draw((B, T, D), 1.0, seed, "x", "bf16")
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", "bf16")
+    z = synth.draw((B, T, R), 1.0, seed, "z", "bf16")
+    U = synth.draw((R, G * W), 0.3 / R**0.5, seed, "U", "bf16")
+    b = synth.draw((G * W,), 0.3, seed, "b", "bf16")
+    x64, z64, U64, b64, dy64 = to64(x), to64(z), to64(U), to64(b), to64(dy)
+    dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W, H)
+    rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, H)
+    _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, G, W)), np.abs(dy64), H)
+    gabs = gabs.reshape(B * T, G * W)
+    u = 2.0**-8
+    assert_close("dz", dz, rdz, torch.bfloat16, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
+    assert_close("dx", dx, rdx, torch.bfloat16)
+    assert_close("dU", dU, rdU, torch.bfloat16, rtol=1e-5, atol=1e-5,
+                 extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
+    assert_close("db", db, rdb, torch.bfloat16, rtol=1e-5, atol=1e-5)
