@@ -755,7 +755,11 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
     if (segs && tid < S) st.sid = t0 + tid < t_need ? sgp[int64_t(t0 + tid) * p.ss1] : INT32_MIN;
     st.full = FAST && t0 + S <= t_end;
     if (FAST && t0 + S <= t_end) {
-      // same loads as below with every chunk valid (z chunks are whole: R % 32 == 0)
+      // same loads as below with every chunk valid (z chunks are whole: R % 32 == 0). A
+      // thread past the step's chunks (XCH not a multiple of the block: W = 5 slices of
+      // 16-bit channels) would address rows beyond the step, past the tensor's end on the
+      // last steps; it loads the tensor's first chunk instead, which commit never stores.
+      static_assert(ZCH % kBlockThreads == 0, "every thread owns z chunks of the step");
 #pragma unroll
       for (int i = 0; i < ZS; ++i) {
         const int ck = tid + i * kBlockThreads;
