@@ -18,7 +18,7 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
   // partial sums are written and reduced (two per sequence at the pages' model shapes).
   // The choice uses only what the workspace query knows; if alignment then rules the fast
   // kernels out, the main kernel runs with these token ranges instead.
-  const bool lean = bwd && dt == DYNCONV_BF16 && H == 1 && W <= 4 && R % 32 == 0 && R != 96 && D % 64 == 0;
+  const bool lean = bwd && dt == DYNCONV_BF16 && lowrank_fast_group_ok(H) && W <= 4 && R % 32 == 0 && R != 96 && D % 64 == 0;
   const int64_t target = !bwd ? 1024 : lean ? 512 : 2048;
   const int64_t slices = lean ? D / 64 : pl.nCs;  // the fast kernel's 64-channel slices
   int64_t per_seq = (target + B * slices - 1) / (B * slices);
@@ -58,7 +58,9 @@ dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& pla
                        : dt == DYNCONV_F16 ? lowrank_dispatch_f16(p, plan, W, true, stream)
                                            : lowrank_dispatch_f32(p, plan, W, true, stream);
   if (e != hipSuccess) return record_hip_error(e);
-  const int64_t nR = int64_t(p.B) * plan.nTr * p.H;  // partials per (token range, channel of a group)
+  // partials per filter column: one per token range on the fast kernels, one per (token
+  // range, channel of the group) on the general kernel
+  const int64_t nR = int64_t(p.B) * plan.nTr * (lowrank_bwd_fast(p, W, dt) ? 1 : p.H);
   dynconv_status st = launch_reduce_partials(p.part_dU, nR, int64_t(p.R) * p.J, dU, stream);
   if (st != DYNCONV_OK || db == nullptr) return st;
   return launch_reduce_partials(p.part_db, nR, p.J, db, stream);

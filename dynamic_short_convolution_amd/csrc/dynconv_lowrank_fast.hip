@@ -262,10 +262,11 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
     const uint32_t bmask = has_bias ? ~0u : 0u;
     const int tap = n & 3;
     const int ltap = tap < W ? tap : W - 1;
+    const int hsh = __builtin_ctz(unsigned(p.H));  // channel c takes group c / H's columns
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int ch = cw + 4 * (n >> 2) + mt;
-      const int64_t col = int64_t(ch) * W + ltap;
+      const int64_t col = int64_t(ch >> hsh) * W + ltap;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
       const int chq = cw + 4 * q + mt;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t v = bsrc[(has_bias ? int64_t(chq) * W : 0) + (i < W ? i : W - 1)];
+        const uint16_t v = bsrc[(has_bias ? int64_t(chq >> hsh) * W : 0) + (i < W ? i : W - 1)];
         binit[mt][i] = __uint_as_float((uint32_t(v) << 16) & (i < W ? bmask : 0u));
       }
     }
@@ -542,10 +543,11 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
     const uint32_t bmask = has_bias ? ~0u : 0u;
     const int tap = n & 3;
     const int ltap = tap < W ? tap : W - 1;
+    const int hsh = __builtin_ctz(unsigned(p.H));  // channel c takes group c / H's columns
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int ch = cw + 4 * (n >> 2) + mt;
-      const int64_t col = int64_t(ch) * W + ltap;
+      const int64_t col = int64_t(ch >> hsh) * W + ltap;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
       const int chq = cw + 4 * q + mt;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t v = bsrc[(has_bias ? int64_t(chq) * W : 0) + (i < W ? i : W - 1)];
+        const uint16_t v = bsrc[(has_bias ? int64_t(chq >> hsh) * W : 0) + (i < W ? i : W - 1)];
         binit[mt][i] = __uint_as_float((uint32_t(v) << 16) & (i < W ? bmask : 0u));
       }
     }
@@ -1036,8 +1038,13 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
   constexpr int PITCH = COLS + 1;
   constexpr int TPC = RT < 4 ? RT : 4;  // rank tiles per chunk
   static_assert(16 * TPC * PITCH * 4 <= F::BYTES, "staging fits the stages");
+  // Head-wise generation (H consecutive channels share a group's columns, H <= 16): the H
+  // channels of a group are summed here, in channel order, so that one partial per
+  // (sequence, token range) and group column is written.
+  const int H = p.H;
+  const int hsh = __builtin_ctz(unsigned(H));
   float* st = reinterpret_cast<float*>(smem);
-  float* pdu = p.part_dU + int64_t(range) * p.R * p.J + int64_t(c_base) * W;
+  float* pdu = p.part_dU + int64_t(range) * p.R * p.J + int64_t(c_base >> hsh) * W;
 #pragma unroll
   for (int rt0 = 0; rt0 < RT; rt0 += TPC) {
     __syncthreads();
@@ -1049,13 +1056,30 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
         for (int i = 0; i < 4; ++i) st[(16 * t + j) * PITCH + (16 * wv + 4 * q + i) * W + k] = dU[k][rt0 + t][i];
     __syncthreads();
     // rows 16 rt0 .. 16 (rt0 + TPC) - 1, 4 floats per thread and pass
-    constexpr int PER_ROW = COLS / 4;
+    if (H == 1) {
+      constexpr int PER_ROW = COLS / 4;
 #pragma unroll 4
-    for (int idx = tid; idx < 16 * TPC * PER_ROW; idx += 256) {
-      const int r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
-      const float* src = st + r * PITCH + c4;
-      const f32x4_t v = {src[0], src[1], src[2], src[3]};
-      *reinterpret_cast<f32x4_t*>(pdu + int64_t(16 * rt0 + r) * p.J + c4) = v;
+      for (int idx = tid; idx < 16 * TPC * PER_ROW; idx += 256) {
+        const int r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
+        const float* src = st + r * PITCH + c4;
+        const f32x4_t v = {src[0], src[1], src[2], src[3]};
+        *reinterpret_cast<f32x4_t*>(pdu + int64_t(16 * rt0 + r) * p.J + c4) = v;
+      }
+    } else {
+      const int per_row = (COLS >> hsh) / 4;  // group columns of the slice, 4 at a time
+      for (int idx = tid; idx < 16 * TPC * per_row; idx += 256) {
+        const int r = idx / per_row, c4 = (idx % per_row) * 4;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int g = (c4 + e) / W, k = (c4 + e) % W;
+          const float* src = st + r * PITCH + (g << hsh) * W + k;
+          float v = src[0];
+          for (int h = 1; h < H; ++h) v += src[h * W];
+          o[e] = v;
+        }
+        *reinterpret_cast<f32x4_t*>(pdu + int64_t(16 * rt0 + r) * p.J + c4) = f32x4_t{o[0], o[1], o[2], o[3]};
+      }
     }
   }
   if (p.part_db != nullptr) {
@@ -1064,7 +1088,8 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
       float v = db[k];
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
-      if (q == 0) p.part_db[int64_t(range) * p.J + int64_t(cw + j) * W + k] = v;
+      for (int m = 1; m < H; m <<= 1) v += __shfl_xor(v, m, 64);  // the group's lanes j
+      if (q == 0 && (j & (H - 1)) == 0) p.part_db[int64_t(range) * p.J + int64_t((cw + j) >> hsh) * W + k] = v;
     }
   }
 }
@@ -1115,9 +1140,11 @@ int fwd_fast_lds(int ks) {
 
 }  // namespace
 
+bool lowrank_fast_group_ok(int H) { return H == 1 || H == 2 || H == 4 || H == 8 || H == 16; }
+
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   const int ks = p.R / 32;
-  return dt == DYNCONV_BF16 && p.H == 1 && W >= 1 && W <= 4 && p.R % 32 == 0 && fwd_fast_rank_ok(ks) &&
+  return dt == DYNCONV_BF16 && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 && p.R % 32 == 0 && fwd_fast_rank_ok(ks) &&
          p.D % (16 * LRF_NWV) == 0 && p.act16 != 0 && p.z16 != 0 &&
          (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) && int64_t(kStep) * p.xs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.zs1 < (int64_t(1) << 30);
@@ -1193,8 +1220,8 @@ hipError_t bwd_dx_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
 
 bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   const int ks = p.R / 32;
-  return dt == DYNCONV_BF16 && p.H == 1 && W >= 1 && W <= 4 && p.R % 32 == 0 && (ks == 1 || ks == 2 || ks == 4) &&
-         p.D % 64 == 0 && p.act16 != 0 && p.z16 != 0 && (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
+  return dt == DYNCONV_BF16 && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 && p.R % 32 == 0 &&
+         (ks == 1 || ks == 2 || ks == 4) && p.D % 64 == 0 && p.act16 != 0 && p.z16 != 0 && (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
          int64_t(kStep) * p.dys1 < (int64_t(1) << 30) && int64_t(kStep) * p.zs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.xs1 < (int64_t(1) << 30);
 }
@@ -1217,6 +1244,10 @@ hipError_t bwd_gdu_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
     case 4: return bwd_gdu_inst<W, 4>(p, blocks, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool lowrank_bwd_fast(const LowRankParams& p, int W, dynconv_dtype dt) {
+  return dt == DYNCONV_BF16 && (p.seg == nullptr || lowrank_seg_fast_ok(p)) && lowrank_bwd_dx_fast_ok(p, W, dt);
 }
 
 hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, hipStream_t s) {

@@ -74,7 +74,10 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
 
 dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   hipStream_t stream);
-// bf16 fast forward (LDS DMA pipeline; W <= 4, R in {32, 64, 128}, H == 1, 16-byte
+// Group sizes the fast bf16 kernels serve: H in {1, 2, 4, 8, 16}, so that a 64-channel
+// slice holds whole groups (each channel loads its group's columns of U and of the bias).
+bool lowrank_fast_group_ok(int H);
+// bf16 fast forward (LDS DMA pipeline; W <= 4, R in {32, 64, 128}, those H, 16-byte
 // aligned rows, D a multiple of 64). It plans its own token ranges.
 // Packed sequences on the fast forward: contiguous, 16-byte aligned id rows, T % 4 == 0.
 bool lowrank_seg_fast_ok(const LowRankParams& p);
@@ -84,8 +87,12 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t st
 bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
 hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t stream);
 // bf16 fast g / dU / db partial sums (same conditions as the fast dx, on x too), over the
-// planned token ranges (Ltok, nTr) and 64-channel slices.
+// planned token ranges (Ltok, nTr) and 64-channel slices; one partial per token range and
+// group column (a group's H channels summed inside the workgroup).
 hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, hipStream_t stream);
+// Whether the backward runs on the fast kernels (dx, then g / dU / db): they write
+// B * nTr partials per filter column, the general kernel B * nTr * H.
+bool lowrank_bwd_fast(const LowRankParams& p, int W, dynconv_dtype dt);
 
 dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   float* dU, float* db, hipStream_t stream);

@@ -769,9 +769,11 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
 #pragma unroll
       for (int i = 0; i < XS; ++i) {
         const int ck = tid + i * kBlockThreads;
+        const bool in = XCH % kBlockThreads == 0 || ck < XCH;
         const int row = ck / (DC / CE), c = (ck % (DC / CE)) * CE;
-        st.x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb + row * int(p.xs1) + c));
-        st.d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(db_ + row * int(p.dys1) + c));
+        st.x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in ? xb + row * int(p.xs1) + c : xsafe));
+        st.d[i] =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in ? db_ + row * int(p.dys1) + c : dysafe));
       }
       st.ok = ~0u;
       return;
@@ -1593,8 +1595,7 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   // otherwise one main kernel (the channel slices inside D on the 16-byte path, the rest on
   // the other)
   // (packed sequences: with contiguous, aligned id rows and T % 4 == 0)
-  const bool fast = (p.seg == nullptr || lowrank_seg_fast_ok(p)) && std::is_same<ET, bf16_t>::value &&
-                    lowrank_bwd_dx_fast_ok(p, W, DYNCONV_BF16);
+  const bool fast = std::is_same<ET, bf16_t>::value && lowrank_bwd_fast(p, W, DYNCONV_BF16);
   LowRankParams q = p;
   const int64_t per_slice = int64_t(p.B) * pl.nTr;
   const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;

@@ -259,15 +259,16 @@ def test_headwise_lowrank_parity(dtype, H, W, R):
     assert_close("db", db, rdb, rt, rtol=1e-5, atol=1e-5)
 
 
-# head-wise dz on the LDS DMA path: bf16, group sizes 2 and 4, chunks of 32 groups
-# (32 * H channels) over five chunks so that the three-stage ring wraps, three whole
-# 64-token blocks and a ragged tail of 8 tokens (register path); every R that divides
-# into 32-row tiles, every W (the shapes whose stages do not fit take the register path)
-HEADWISE_DMA = [(H, W, R) for H in (2, 4) for W in (1, 2, 3, 4, 5) for R in (32, 64, 96, 128)]
+# head-wise generation on the bf16 fast kernels (forward, dx, g/dU/db with the group's H
+# channels summed in the workgroup: H <= 16, W <= 4, R in {32, 64, 128}) and dz on the LDS
+# DMA path (H = 2, 4: chunks of 32 groups, 32 * H channels); five dz chunks so that the
+# three-stage ring wraps, three whole 64-token blocks and a ragged tail of 8 tokens
+# (register path); the other W, R and H take the general kernels
+HEADWISE_DMA = [(H, W, R) for H in (2, 4, 8, 16) for W in (1, 2, 3, 4, 5) for R in (32, 64, 96, 128)]
 
 
 @pytest.mark.parametrize("H,W,R", HEADWISE_DMA)
-def test_headwise_lowrank_dz_dma(H, W, R):
+def test_headwise_lowrank_fast_kernels(H, W, R):
     B, T = 2, 200
     D = 5 * 32 * H
     G = D // H
@@ -278,6 +279,8 @@ def test_headwise_lowrank_dz_dma(H, W, R):
     U = synth.draw((R, G * W), 0.3 / R**0.5, seed, "U", "bf16")
     b = synth.draw((G * W,), 0.3, seed, "b", "bf16")
     x64, z64, U64, b64, dy64 = to64(x), to64(z), to64(U), to64(b), to64(dy)
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W, H)
+    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W, H), torch.bfloat16)
     dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W, H)
     rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, H)
     _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, G, W)), np.abs(dy64), H)
