@@ -84,8 +84,8 @@ def lowrank_bytes(B, T, D, W, R, eb=2, fwd=True, H=1):
 
 
 def lowrank_flops(B, T, D, W, R, fwd=True, H=1):
-    """Algorithmic flops: the (D/H)*W filter columns of a token once (the general kernels
-    form them once per channel)."""
+    """Algorithmic flops: the (D/H)*W filter columns of a token once (the forward and dx
+    kernels form them once per channel)."""
     per = 2 * B * T * R * (D // H) * W
     return per if fwd else 3 * per
 
@@ -278,7 +278,7 @@ def make_row(name, device):
         return (lambda: dynconv_lowrank_decode_step(x, z, U, b, cache, 7, W, out=y)), \
             io + B * R * 2 + R * D * W * 2 + D * W * 2, 2 * B * R * D * W, f"decode step B{B} D{D} W{W} R{R} bf16"
     if name.startswith("lowrank"):
-        # lowrank_h4_*: head-wise generation, U of R x (D/4)*W (the general kernels)
+        # lowrank_h4_*: head-wise generation, U of R x (D/4)*W
         B, T, D, W, R = 8, 4096, 2048, 4, 64
         H = 4 if name.startswith("lowrank_h4") else 1
         J = (D // H) * W

@@ -36,7 +36,7 @@
  * - Supported parameters: 1 <= W <= 8 (low-rank form: W <= 5); H == 1 or H a power of two that divides D, with
  *   H / VEC <= 64 where VEC = min(H, widest lane vector allowed by the alignment below /
  *   element size), i.e. H <= 512 (bf16) or 256 (float32) with 16-byte aligned
- *   activations; low-rank form: 1 <= R <= 128 (H > 1 takes the general kernels).
+ *   activations; low-rank form: 1 <= R <= 128.
  * - Alignment: base pointers of activation-shaped tensors and their s[0], s[1] (in bytes)
  *   must be multiples of 4 bytes (bf16: D even); wider lane vectors (8 or 16 bytes) are
  *   used when every activation-shaped tensor of the call allows them. Filters: base and
@@ -191,9 +191,10 @@ dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, con
  * document never reads the inputs of the one before it (the RubiConv page's point that
  * a convolution over packed sequences must not cross a document start). Documents are
  * normally contiguous runs of equal ids; any ids work, the test is equality. Gradients
- * are those of the masked forward. The low-rank calls take the general kernels (not the
- * bf16 fast path). seq_idx == NULL returns DYNCONV_ERR_INVALID_ARG; every other argument
- * is as in the call without the suffix.
+ * are those of the masked forward. The bf16 fast low-rank kernels take packed calls whose
+ * id rows are contiguous, 16-byte aligned and T % 4 == 0; others take the general kernels.
+ * seq_idx == NULL returns DYNCONV_ERR_INVALID_ARG; every other argument is as in the call
+ * without the suffix.
  */
 dynconv_status dynconv_fwd_varlen(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
                                   const int32_t* seq_idx, const int64_t* ss, void* y, const int64_t* ys, int64_t B,
