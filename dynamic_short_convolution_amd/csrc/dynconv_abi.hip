@@ -154,7 +154,7 @@ dynconv_status fwd_impl(const void* x, const int64_t* xs, const void* w, const i
   const int align = act_alignment(acts, 2, eb);
   if ((st = check_stream_layout(D, H, eb, align)) != DYNCONV_OK) return st;
 
-  const StreamPlan plan = plan_stream(B, T, D, H, eb, align, false, fi.is_static);
+  const StreamPlan plan = plan_stream(B, T, D, W, H, eb, align, false, fi.is_static);
   StreamParams p{};
   p.x = x;
   p.w = w;
@@ -235,7 +235,7 @@ size_t bwd_workspace(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, bool
   const int eb = elem_bytes(dtype);
   size_t best = 0;
   for (int align : {4, 8, 16}) {
-    const StreamPlan pl = plan_stream(B, T, D, H, eb, align, true, is_static);
+    const StreamPlan pl = plan_stream(B, T, D, W, H, eb, align, true, is_static);
     const size_t need = bwd_partial_floats(pl, B, D, W, H, is_static, dcbias) * sizeof(float);
     if (need > best) best = need;
   }
@@ -302,7 +302,7 @@ dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const i
   const int align = act_alignment(acts, 3, eb);
   if ((st = check_stream_layout(D, H, eb, align)) != DYNCONV_OK) return st;
 
-  const StreamPlan plan = plan_stream(B, T, D, H, eb, align, true, fi.is_static);
+  const StreamPlan plan = plan_stream(B, T, D, W, H, eb, align, true, fi.is_static);
   float* partial = nullptr;
   float* cb_partial = nullptr;
   const bool static_dw = fi.is_static && dw != nullptr;

@@ -55,7 +55,7 @@ struct StreamPlan {
 
 // Chooses the lane vector width and the time chunking. `act_align` (4, 8 or 16) is the
 // widest lane vector, in bytes, that every activation-shaped tensor allows.
-StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, int act_align, bool bwd,
+StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int W, int H, int elem_bytes, int act_align, bool bwd,
                        bool is_static);
 
 // The streaming kernels for one storage type (one translation unit each).

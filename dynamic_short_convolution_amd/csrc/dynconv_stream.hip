@@ -18,6 +18,12 @@
 #ifndef DYNCONV_BWD_STATIC_WAVES_PER_CU
 #define DYNCONV_BWD_STATIC_WAVES_PER_CU 8
 #endif
+// Per-channel backward with W >= 7: its registers (about 150 VGPRs) hold 3 waves per SIMD,
+// not the 4 the target above assumes, and whole rounds of 2 per SIMD measured fastest (W = 8
+// at B8 T4096 D2048: 653 us at 16 waves per CU, 683 at 12, 594 at 8, 591 at 6).
+#ifndef DYNCONV_BWD_WIDE_WAVES_PER_CU
+#define DYNCONV_BWD_WIDE_WAVES_PER_CU 8
+#endif
 
 namespace dynconv {
 
@@ -53,7 +59,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials(const float* 
 }  // namespace
 
 
-StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, int act_align, bool bwd,
+StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int W, int H, int elem_bytes, int act_align, bool bwd,
                        bool is_static) {
   StreamPlan pl{};
   if (H == 1) {
@@ -80,6 +86,7 @@ StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int H, int elem_bytes, i
   const int waves_per_cu = !bwd ? DYNCONV_FWD_WAVES_PER_CU
                            : is_static ? DYNCONV_BWD_STATIC_WAVES_PER_CU
                            : H > 1     ? DYNCONV_BWD_GROUP_WAVES_PER_CU
+                           : W >= 7    ? DYNCONV_BWD_WIDE_WAVES_PER_CU
                                        : DYNCONV_BWD_WAVES_PER_CU;
   const double target_blocks = 256.0 * waves_per_cu / (kBlockThreads / kWaveSize);
   const int64_t min_len = (bwd && is_static) ? 64 : 16;
