@@ -18,11 +18,16 @@
 #ifndef DYNCONV_BWD_STATIC_WAVES_PER_CU
 #define DYNCONV_BWD_STATIC_WAVES_PER_CU 8
 #endif
-// Per-channel backward with W >= 7: its registers (about 150 VGPRs) hold 3 waves per SIMD,
-// not the 4 the target above assumes, and whole rounds of 2 per SIMD measured fastest (W = 8
-// at B8 T4096 D2048: 653 us at 16 waves per CU, 683 at 12, 594 at 8, 591 at 6).
+// Per-channel dynamic filters with W >= 7 stream twice the filter bytes per lane and token,
+// so fewer, longer streams keep as many bytes in flight. Backward: its registers (about 150
+// VGPRs) hold 3 waves per SIMD, not the 4 the target above assumes, and whole rounds of 2
+// per SIMD measured fastest (W = 8 at B8 T4096 D2048: 653 us at 16 waves per CU, 683 at 12,
+// 594 at 8, 591 at 6). Forward: 259 us at 8 waves per CU, 235 at 4.
 #ifndef DYNCONV_BWD_WIDE_WAVES_PER_CU
 #define DYNCONV_BWD_WIDE_WAVES_PER_CU 8
+#endif
+#ifndef DYNCONV_FWD_WIDE_WAVES_PER_CU
+#define DYNCONV_FWD_WIDE_WAVES_PER_CU 4
 #endif
 
 namespace dynconv {
@@ -83,10 +88,11 @@ StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int W, int H, int elem_b
   // over the 256 CUs (a grid of 4.03 workgroups per CU runs as long as one of 5). Chunks
   // hold a multiple of 4 tokens and at least 16 (64 for the static backward, which writes
   // one partial sum per chunk).
-  const int waves_per_cu = !bwd ? DYNCONV_FWD_WAVES_PER_CU
+  const bool wide = H == 1 && !is_static && W >= 7;
+  const int waves_per_cu = !bwd ? (wide ? DYNCONV_FWD_WIDE_WAVES_PER_CU : DYNCONV_FWD_WAVES_PER_CU)
                            : is_static ? DYNCONV_BWD_STATIC_WAVES_PER_CU
                            : H > 1     ? DYNCONV_BWD_GROUP_WAVES_PER_CU
-                           : W >= 7    ? DYNCONV_BWD_WIDE_WAVES_PER_CU
+                           : wide      ? DYNCONV_BWD_WIDE_WAVES_PER_CU
                                        : DYNCONV_BWD_WAVES_PER_CU;
   const double target_blocks = 256.0 * waves_per_cu / (kBlockThreads / kWaveSize);
   const int64_t min_len = (bwd && is_static) ? 64 : 16;
