@@ -345,6 +345,18 @@ def run_rows(args, device):
         log(f"{name}: {r['median_us']} us, {r['gbs']} GB/s")
         del fn
         torch.cuda.empty_cache()
+    # context, not the library: the runtime's own device copy (1 GiB read + 1 GiB written),
+    # timed the same way, as the streaming rate a plain read/write kernel reaches on this part
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=device).fill_(3)
+    b_ = torch.empty_like(a)
+    med, mean = time_launches(lambda: b_.copy_(a), args.reps, flush)
+    gbs = round(2.0 * (1 << 30) / (med * 1e-3) / 1e9, 1)
+    out["reference_device_copy"] = dict(config="runtime device copy, 1 GiB read + 1 GiB written",
+                                        median_us=round(med * 1e3, 2), gbs=gbs,
+                                        pct_hbm_peak=round(100.0 * gbs / HBM_PEAK_GBS, 1))
+    log(f"reference device copy: {out['reference_device_copy']['median_us']} us, {gbs} GB/s")
+    del a, b_
+    torch.cuda.empty_cache()
     # orderings the pages report for their kernels (latency falls with H; low-rank below H=1)
     out["orderings"] = {
         "fwd_h16_lt_h4_lt_h1": out["headwise_h16_fwd"]["median_us"] < out["headwise_h4_fwd"]["median_us"]

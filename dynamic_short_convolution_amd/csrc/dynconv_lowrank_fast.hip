@@ -17,6 +17,9 @@
 //    (n, q = lane / 16) receives the W taps of channels 4q .. 4q+3 of the wave's 16
 //    (one per 16-row tile mt). The bias enters as the accumulator's initial value.
 //    A lane thus holds the filters of 4 consecutive tokens 4n .. 4n+3 for 4 channels.
+//    Head-wise generation (H consecutive channels share a group's filter, H <= 16): each
+//    channel's rows of A are its group's columns of U, so the matrix work repeats per
+//    channel while the x / y traffic is that of H = 1.
 //  * Convolution: the lane reads x rows 4n-3 .. 4n+3 of its 4 channels (8 bytes each),
 //    converts each once, and forms y = x_t + sum_k w_k(t) x_{t-k} in float32.
 //  * Stores: the step's y goes to an LDS tile and is written one step later by the same

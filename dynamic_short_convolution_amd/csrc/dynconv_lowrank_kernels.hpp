@@ -23,7 +23,9 @@
 //                   over the token range; writes one float32 partial per token range.
 //   k_lowrank_dz    per (sequence, 64-token block): dz = g U^T (MFMA, K = filter columns)
 //                   with g recomputed from x and dy, looping over channel chunks, so dz is
-//                   complete without partial sums.
+//                   complete without partial sums (register-staged: any type and shape).
+//   k_lowrank_dz_dma the same for bf16 whole token blocks, staged by LDS DMA; head-wise
+//                   groups of 2 or 4 channels are summed before the matrix step.
 //   partial sums of dU and db are then added in a fixed order (run-to-run deterministic).
 #include <type_traits>
 
