@@ -66,6 +66,40 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials(const float* 
   }
 }
 
+// The same sums, 4 consecutive columns per thread (16-byte loads and stores): n % 4 == 0
+// and 16-byte aligned pointers. Each column is summed in the order above, so the results
+// are bit-identical to k_reduce_partials.
+constexpr int kRedCols4 = 4 * kRedCols;
+
+__global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4(const float* __restrict__ part, int64_t nchunk,
+                                                                    int64_t n, float* __restrict__ out) {
+  __shared__ double red[kRedGroups][kRedCols][4];
+  const int col = threadIdx.x % kRedCols;
+  const int grp = threadIdx.x / kRedCols;
+  const int64_t i = int64_t(blockIdx.x) * kRedCols4 + 4 * col;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  if (i < n) {
+    for (int64_t c = grp; c < nchunk; c += kRedGroups) {
+      const float4 v = *reinterpret_cast<const float4*>(part + c * n + i);
+      s[0] += double(v.x);
+      s[1] += double(v.y);
+      s[2] += double(v.z);
+      s[3] += double(v.w);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[grp][col][e] = s[e];
+  __syncthreads();
+  if (grp == 0 && i < n) {
+    double tot[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int r = 0; r < kRedGroups; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tot[e] += red[r][col][e];
+    *reinterpret_cast<float4*>(out + i) = float4{float(tot[0]), float(tot[1]), float(tot[2]), float(tot[3])};
+  }
+}
+
 }  // namespace
 
 
@@ -159,9 +193,17 @@ dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, 
 
 dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,
                                       hipStream_t stream) {
-  const int64_t blocks = (n + kRedCols - 1) / kRedCols;
-  hipLaunchKernelGGL(k_reduce_partials, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk, n,
-                     out);
+  const bool vec = n % 4 == 0 && reinterpret_cast<uintptr_t>(partial) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  if (vec) {
+    const int64_t blocks = (n + kRedCols4 - 1) / kRedCols4;
+    hipLaunchKernelGGL(k_reduce_partials4, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk,
+                       n, out);
+  } else {
+    const int64_t blocks = (n + kRedCols - 1) / kRedCols;
+    hipLaunchKernelGGL(k_reduce_partials, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk, n,
+                       out);
+  }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
 }
