@@ -1326,12 +1326,33 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
 // a lane owns 8 groups (HG 16-byte runs of x and dy per row) and sums its products over
 // the HG channels of a group before the matrix-core step (1/HG of the per-channel
 // matrix work, and U read 1/HG as often).
-// LDS rows are rotated by chunk so that the 16 lanes of a group that read the same
-// logical chunk of 16 different rows hit distinct banks:
-//   U row r (UCPR chunks): logical chunk c sits at (c + r % 16) % UCPR;
-//   x / dy row (XCPR = 4 * HG chunks, 64 * HG bytes): logical chunk c sits at
-//   (c + row / (4 / HG)) % XCPR, so that the rows of one 256-byte bank sweep differ.
+// LDS placement. The bank-conflict counts measured on this kernel (4 extra cycles per
+// colliding 16-byte read) fit 16-byte reads served in passes of 16 lanes over 256 bytes:
+// lanes 0-7 with 16-23, 8-15 with 24-31, 32-39 with 48-55, 40-47 with 56-63. A pass thus
+// reads 8 consecutive rows, each at two logical chunks (of lane groups q and q + 1).
+// LdsPlace<CPR> maps logical chunk c of row r to a slot:
+//   CPR == 16 (256-byte rows: U at W = 4, x / dy at H = 4): rotate by
+//     r % 4 + 8 * ((r / 4) % 2), which puts the 16 reads of a pass on distinct slots;
+//   CPR % 8 == 4 (rows of 64, 192, 320 bytes): rotate by r / 2 (conflict-free for 64-byte
+//     rows, x / dy at H = 1);
+//   CPR == 8 (128-byte rows): rotate by r.
+// U rows use r % 16 (the row within a 16-row tile), so every tile has the same slots.
 // ---------------------------------------------------------------------------------
+template <int CPR>
+struct LdsPlace {
+  static_assert(CPR % 8 == 4 || CPR == 8 || CPR == 16, "LDS row length of the dz kernel");
+  static __device__ __forceinline__ int slot(int r, int c) {
+    if constexpr (CPR == 16) return (c + r % 4 + 8 * ((r / 4) % 2)) % 16;
+    else if constexpr (CPR == 8) return (c + r) % 8;
+    else return (c + r / 2) % CPR;
+  }
+  static __device__ __forceinline__ int chunk(int r, int p) {  // inverse of slot for row r
+    if constexpr (CPR == 16) return (p - r % 4 - 8 * ((r / 4) % 2) + 16) % 16;
+    else if constexpr (CPR == 8) return ((p - r % 8) % 8 + 8) % 8;
+    else return ((p - (r / 2) % CPR) % CPR + CPR) % CPR;
+  }
+};
+
 template <int W, int KS, int HG>
 struct LrDzDma {
   static_assert(HG == 1 || HG == 2 || HG == 4, "group size of the DMA dz path");
@@ -1343,7 +1364,6 @@ struct LrDzDma {
   static constexpr int TB = kLowrankDzTokens;
   static constexpr int XR = TB + HALO;
   static constexpr int XCPR = CHC / 8;         // 16-byte chunks of an x / dy row
-  static constexpr int RPB = 4 / HG;           // x / dy rows per 256 bytes
   static constexpr int UCH = RP * UCPR, XCH = XR * XCPR, DCH = TB * XCPR;
   static constexpr int NI_U = (UCH + 63) / 64, NI_X = (XCH + 63) / 64, NI_D = (DCH + 63) / 64;
   static constexpr int NI = NI_U + NI_X + NI_D;  // wave-wide transfers per stage
@@ -1353,8 +1373,8 @@ struct LrDzDma {
   static constexpr int NST = 3;
   static constexpr int BYTES = NST * STAGE;
   static_assert(XCPR == 4 * HG && UC % 8 == 0, "dz DMA tiling");
-  // physical 16-byte slot of logical chunk c of x / dy row `row`
-  static __device__ __forceinline__ int xslot(int row, int c) { return (c + row / RPB) & (XCPR - 1); }
+  using UPlace = LdsPlace<UCPR>;
+  using XPlace = LdsPlace<XCPR>;
 };
 
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
@@ -1396,14 +1416,14 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
   for (int i = 0; i < SU; ++i) {
     const int pidx = (wv + 4 * i) * 64 + lane;
     const int r = pidx / UCPR, pc = pidx % UCPR;
-    const int c = (pc - (r & 15) % UCPR + UCPR) % UCPR;
+    const int c = D::UPlace::chunk(r & 15, pc);
     uact[i] = pidx < D::UCH;
     uoffg[i] = r * int(p.ldu) + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < SX; ++i) {
     const int pidx = (wv + 4 * i) * 64 + lane;
-    const int row = pidx / XCPR, c = ((pidx % XCPR) - row / D::RPB) & (XCPR - 1);
+    const int row = pidx / XCPR, c = D::XPlace::chunk(row, pidx % XCPR);
     xact[i] = pidx < D::XCH;
     // rows before token 0 read token 0 instead (their products are zeroed below)
     xoffg[i] = max(row, HALO - tb0) * int(p.xs1) + c * 8;
@@ -1411,7 +1431,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 #pragma unroll
   for (int i = 0; i < SD; ++i) {
     const int pidx = (wv + 4 * i) * 64 + lane;
-    const int row = pidx / XCPR, c = ((pidx % XCPR) - row / D::RPB) & (XCPR - 1);
+    const int row = pidx / XCPR, c = D::XPlace::chunk(row, pidx % XCPR);
     dact[i] = pidx < D::DCH;
     doffg[i] = row * int(p.dys1) + c * 8;
   }
@@ -1439,16 +1459,16 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
   int dy_off[HG], x_off[W][HG];
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
-    dy_off[h] = D::D_OFF + nt * (XCPR * 16) + D::xslot(nt, q * HG + h) * 16;
+    dy_off[h] = D::D_OFF + nt * (XCPR * 16) + D::XPlace::slot(nt, q * HG + h) * 16;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
       const int row = nt + HALO - k;
-      x_off[k][h] = D::X_OFF + row * (XCPR * 16) + D::xslot(row, q * HG + h) * 16;
+      x_off[k][h] = D::X_OFF + row * (XCPR * 16) + D::XPlace::slot(row, q * HG + h) * 16;
     }
   }
   int u_off[KST];  // row rt * 16 + n adds rt * 16 * UC * 2 bytes (same rotation)
 #pragma unroll
-  for (int ks = 0; ks < KST; ++ks) u_off[ks] = n * UC * 2 + ((q * W + ks + n) % UCPR) * 16;
+  for (int ks = 0; ks < KST; ++ks) u_off[ks] = n * UC * 2 + D::UPlace::slot(n, q * W + ks) * 16;
 
   f32x4_t acc[RTN];
 #pragma unroll
