@@ -295,3 +295,22 @@ def test_full_headwise_h4_bwd():
 
 def test_full_headwise_h16_bwd():
     _full_check(synth.workloads()["headwise_h16_bwd"], do_fwd=False)
+
+
+# The fixed-order reduce of the static backward's per-chunk partials has a 16-byte path
+# (row length n = D/H * W a multiple of 4, aligned pointers) and a 4-byte one; both sum
+# each column in the same order. n = 594 and a dw output one float off a 16-byte boundary
+# take the 4-byte path, n = 600 the 16-byte path.
+@pytest.mark.parametrize("D,offset", [(198, 0), (200, 0), (200, 1)])
+def test_static_dw_reduce_paths(D, offset):
+    B, T, W, H = 3, 700, 3, 1
+    x, w, dy = _inputs(B, T, D, W, H, "bf16", True, 31 + D + offset)
+    buf = torch.full((D * W + offset,), float("nan"), dtype=torch.float32, device="cuda")
+    dw = buf[offset:].view(D, W)
+    dx, dw_out = dynconv_bwd(x.cuda(), w.cuda(), dy.cuda(), H, dw=dw)
+    assert dw_out.data_ptr() == dw.data_ptr()
+    rdx, rdw = conv_bwd(to64(x), to64(w), to64(dy), H)
+    assert_close("dx", dx, rdx, torch.bfloat16)
+    assert_close("dw_static", dw, rdw, torch.float32, rtol=1e-5, atol=1e-5)
+    if offset:
+        assert torch.isnan(buf[:offset]).all()
