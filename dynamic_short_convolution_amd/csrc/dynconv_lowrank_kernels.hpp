@@ -1320,12 +1320,13 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
 // lane, no registers involved) into a ring of NST stages, two chunks ahead of the one
 // being computed. Each wave waits for its own transfers (vmcnt) and a barrier publishes
 // the stage; nothing else needs the loads, so no other wait is tied to them.
-// A chunk is 32 filter groups: 32 channels per-channel, 32 * HG channels when HG
-// consecutive channels share a filter (HG = 2 or 4). The filter columns of consecutive
-// groups are consecutive in U, so a chunk's U tile is 32 * W whole columns for every HG;
-// a lane owns 8 groups (HG 16-byte runs of x and dy per row) and sums its products over
-// the HG channels of a group before the matrix-core step (1/HG of the per-channel
-// matrix work, and U read 1/HG as often).
+// A lane owns GL filter groups (GL = 8 for HG <= 4, 32 / HG for HG = 8, 16), a chunk the
+// 4 GL groups of the 4 lane groups: 32 channels per-channel, 32 * HG channels when HG
+// consecutive channels share a filter (HG = 2, 4), 128 channels for HG = 8, 16. The filter
+// columns of consecutive groups are consecutive in U, so a chunk's U tile is 4 GL W whole
+// columns; a lane reads GL * HG / 8 16-byte runs of x and dy per row and sums its products
+// over the HG channels of a group before the matrix-core step (1/HG of the per-channel
+// matrix work, and U read 1/HG as often). Its GL * W columns must fill whole K steps of 8.
 // LDS placement. The bank-conflict counts measured on this kernel (4 extra cycles per
 // colliding 16-byte read) fit 16-byte reads served in passes of 16 lanes over 256 bytes:
 // lanes 0-7 with 16-23, 8-15 with 24-31, 32-39 with 48-55, 40-47 with 56-63. A pass thus
@@ -1355,9 +1356,12 @@ struct LdsPlace {
 
 template <int W, int KS, int HG>
 struct LrDzDma {
-  static_assert(HG == 1 || HG == 2 || HG == 4, "group size of the DMA dz path");
+  static_assert(HG == 1 || HG == 2 || HG == 4 || HG == 8 || HG == 16, "group size of the DMA dz path");
   static constexpr int RP = 32 * KS;
-  static constexpr int CH = kLowrankDzChunk;   // filter groups of a chunk
+  static constexpr int GL = HG <= 4 ? 8 : 32 / HG;  // filter groups of a lane
+  static constexpr int RUNS = GL * HG / 8;          // 16-byte runs of a lane's row
+  static constexpr bool SHAPE_OK = (GL * W) % 8 == 0;
+  static constexpr int CH = 4 * GL;            // filter groups of a chunk
   static constexpr int CHC = CH * HG;          // channels of a chunk
   static constexpr int UC = CH * W;            // filter columns of a chunk
   static constexpr int UCPR = UC / 8;          // 16-byte chunks of a U row
@@ -1372,7 +1376,7 @@ struct LrDzDma {
   static constexpr int STAGE = D_OFF + NI_D * 64 * 16;
   static constexpr int NST = 3;
   static constexpr int BYTES = NST * STAGE;
-  static_assert(XCPR == 4 * HG && UC % 8 == 0, "dz DMA tiling");
+  static_assert(XCPR == 4 * RUNS && UC % 8 == 0, "dz DMA tiling");
   using UPlace = LdsPlace<UCPR>;
   using XPlace = LdsPlace<XCPR>;
 };
@@ -1395,8 +1399,9 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
   using D = LrDzDma<W, KS, HG>;
   constexpr int RP = D::RP, CH = D::CH, UC = D::UC, UCPR = D::UCPR, XCPR = D::XCPR;
   constexpr int RTN = RP / 16;
-  constexpr int GL = CH / 4;   // filter groups of a lane (HG 16-byte runs of channels)
-  constexpr int KST = W;       // K steps per chunk: GL * W columns / 8
+  constexpr int GL = D::GL, RUNS = D::RUNS;
+  constexpr int KST = GL * W / 8;  // K steps per chunk: the lane's GL * W columns / 8
+  static_assert(D::SHAPE_OK, "whole K steps");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = lane >> 4;
@@ -1455,20 +1460,20 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 
   // per-lane LDS byte offsets inside a stage
   const int nt = wv * TT + n;  // the lane's token within the block
-  // the lane's runs are logical chunks q * HG + h of its rows
-  int dy_off[HG], x_off[W][HG];
+  // the lane's runs are logical chunks q * RUNS + h of its rows
+  int dy_off[RUNS], x_off[W][RUNS];
 #pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    dy_off[h] = D::D_OFF + nt * (XCPR * 16) + D::XPlace::slot(nt, q * HG + h) * 16;
+  for (int h = 0; h < RUNS; ++h) {
+    dy_off[h] = D::D_OFF + nt * (XCPR * 16) + D::XPlace::slot(nt, q * RUNS + h) * 16;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
       const int row = nt + HALO - k;
-      x_off[k][h] = D::X_OFF + row * (XCPR * 16) + D::XPlace::slot(row, q * HG + h) * 16;
+      x_off[k][h] = D::X_OFF + row * (XCPR * 16) + D::XPlace::slot(row, q * RUNS + h) * 16;
     }
   }
   int u_off[KST];  // row rt * 16 + n adds rt * 16 * UC * 2 bytes (same rotation)
 #pragma unroll
-  for (int ks = 0; ks < KST; ++ks) u_off[ks] = n * UC * 2 + D::UPlace::slot(n, q * W + ks) * 16;
+  for (int ks = 0; ks < KST; ++ks) u_off[ks] = n * UC * 2 + D::UPlace::slot(n, q * KST + ks) * 16;
 
   f32x4_t acc[RTN];
 #pragma unroll
@@ -1499,9 +1504,9 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
     const unsigned char* stage = smem + (ci % D::NST) * D::STAGE;
     // words of the lane's dy run and x runs (taps 0 .. W-1); channel j of the lane is
     // word (j % 8) / 2 of run j / 8
-    uint32_t dw_[HG][4], xw[W][HG][4];
+    uint32_t dw_[RUNS][4], xw[W][RUNS][4];
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
+    for (int h = 0; h < RUNS; ++h) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + dy_off[h]);
       dw_[h][0] = v[0]; dw_[h][1] = v[1]; dw_[h][2] = v[2]; dw_[h][3] = v[3];
 #pragma unroll
@@ -1514,12 +1519,12 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 #pragma unroll
       for (int k = 1; k < W; ++k)
 #pragma unroll
-        for (int h = 0; h < HG; ++h)
+        for (int h = 0; h < RUNS; ++h)
           if (!tp[k]) xw[k][h][0] = xw[k][h][1] = xw[k][h][2] = xw[k][h][3] = 0u;
     }
-    float dyf[8 * HG];
+    float dyf[8 * RUNS];
 #pragma unroll
-    for (int j = 0; j < 8 * HG; ++j) dyf[j] = (j & 1) ? bf16_hi(dw_[j >> 3][(j & 7) >> 1]) : bf16_lo(dw_[j >> 3][(j & 7) >> 1]);
+    for (int j = 0; j < 8 * RUNS; ++j) dyf[j] = (j & 1) ? bf16_hi(dw_[j >> 3][(j & 7) >> 1]) : bf16_lo(dw_[j >> 3][(j & 7) >> 1]);
     // column (group g of the lane, tap k): the sum over the group's HG channels
     auto col = [&](int g, int k) -> float {
       auto prod = [&](int j) {
@@ -1566,7 +1571,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 // The LDS DMA path serves bf16 token blocks that lie inside T when its stages fit.
 template <typename ET, int W, int KS, int HG>
 constexpr bool lowrank_dz_dma_ok() {
-  return std::is_same<ET, bf16_t>::value && LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
+  return std::is_same<ET, bf16_t>::value && LrDzDma<W, KS, HG>::SHAPE_OK && LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
 }
 
 // The register-staged path: any storage type, ragged token blocks, unaligned rows, any
@@ -1646,18 +1651,23 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   // dz: token blocks inside T on the DMA path (group sizes 1, 2, 4 whose stages fit), the
   // rest on the register path
   const int nblk = (p.T + kLowrankDzTokens - 1) / kLowrankDzTokens;
-  const bool hg_ok = p.H == 1   ? lowrank_dz_dma_ok<ET, W, KS, 1>()
-                     : p.H == 2 ? lowrank_dz_dma_ok<ET, W, KS, 2>()
-                     : p.H == 4 ? lowrank_dz_dma_ok<ET, W, KS, 4>()
-                                : false;
-  const bool dma = hg_ok && p.act16 != 0 && p.u16 != 0 && p.D % (kLowrankDzChunk * p.H) == 0 && p.R % 32 == 0;
+  const bool hg_ok = p.H == 1    ? lowrank_dz_dma_ok<ET, W, KS, 1>()
+                     : p.H == 2  ? lowrank_dz_dma_ok<ET, W, KS, 2>()
+                     : p.H == 4  ? lowrank_dz_dma_ok<ET, W, KS, 4>()
+                     : p.H == 8  ? lowrank_dz_dma_ok<ET, W, KS, 8>()
+                     : p.H == 16 ? lowrank_dz_dma_ok<ET, W, KS, 16>()
+                                 : false;
+  const int chunk_channels = p.H <= 4 ? kLowrankDzChunk * p.H : 128;
+  const bool dma = hg_ok && p.act16 != 0 && p.u16 != 0 && p.D % chunk_channels == 0 && p.R % 32 == 0;
   const int nfb = dma ? p.T / kLowrankDzTokens : 0;
   if (nfb > 0) {
     q.tbb0 = 0;
     q.nTbL = nfb;
     const hipError_t e = p.H == 1   ? launch_dz_dma<ET, W, KS, 1>(q, s)
                          : p.H == 2 ? launch_dz_dma<ET, W, KS, 2>(q, s)
-                                    : launch_dz_dma<ET, W, KS, 4>(q, s);
+                         : p.H == 4 ? launch_dz_dma<ET, W, KS, 4>(q, s)
+                         : p.H == 8 ? launch_dz_dma<ET, W, KS, 8>(q, s)
+                                    : launch_dz_dma<ET, W, KS, 16>(q, s);
     if (e != hipSuccess) return e;
   }
   if (nfb < nblk) {
