@@ -111,7 +111,8 @@ def test_packed_strided_segment_ids():
 LOWRANK = [("bf16", 4, 64, 128, 1), ("bf16", 2, 32, 128, 1), ("bf16", 3, 64, 192, 1), ("bf16", 5, 40, 72, 1),
            ("f32", 1, 16, 64, 1), ("f32", 3, 64, 136, 1), ("f32", 4, 128, 64, 1), ("bf16", 4, 64, 128, 4),
            ("f32", 3, 32, 64, 8), ("f16", 4, 64, 128, 1), ("f16", 3, 40, 96, 2), ("bf16", 4, 64, 512, 4),
-           ("bf16", 3, 32, 320, 2), ("bf16", 5, 64, 192, 2)]
+           ("bf16", 3, 32, 320, 2), ("bf16", 5, 64, 192, 2),
+           ("bf16", 4, 64, 1024, 8), ("bf16", 4, 64, 1024, 16), ("bf16", 2, 32, 512, 8)]
 
 
 @pytest.mark.parametrize("dtype,W,R,D,H", LOWRANK)
