@@ -18,7 +18,7 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
   // partial sums are written and reduced (two per sequence at the pages' model shapes).
   // The choice uses only what the workspace query knows; if alignment then rules the fast
   // kernels out, the main kernel runs with these token ranges instead.
-  const bool lean = bwd && dt == DYNCONV_BF16 && lowrank_fast_group_ok(H) && W <= 4 && R % 32 == 0 && R != 96 && D % 64 == 0;
+  const bool lean = bwd && (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(H) && W <= 4 && R % 32 == 0 && R != 96 && D % 64 == 0;
   const int64_t target = !bwd ? 1024 : lean ? 512 : 2048;
   const int64_t slices = lean ? D / 64 : pl.nCs;  // the fast kernel's 64-channel slices
   int64_t per_seq = (target + B * slices - 1) / (B * slices);
@@ -43,7 +43,7 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
 dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& plan, int W, dynconv_dtype dt,
                                   hipStream_t stream) {
   if (lowrank_fwd_fast_ok(p, W, dt) && (p.seg == nullptr || lowrank_seg_fast_ok(p))) {
-    const hipError_t e = launch_lowrank_fwd_fast(p, W, stream);
+    const hipError_t e = launch_lowrank_fwd_fast(p, W, dt, stream);
     return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
   }
   const hipError_t e = dt == DYNCONV_BF16   ? lowrank_dispatch_bf16(p, plan, W, false, stream)

@@ -1,4 +1,4 @@
-// Low-rank dynamic short convolution, bf16 fast path for gfx950: the filters w = z U + b
+// Low-rank dynamic short convolution, 16-bit (bf16, float16) fast path for gfx950: the filters w = z U + b
 // are formed on the matrix cores and consumed in registers; they never reach HBM.
 //
 // From "Dynamic Short Convolutions Improve Transformers" (reading note): section
@@ -39,6 +39,7 @@ namespace dynconv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -83,9 +84,16 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// 16x16x32 matrix-core product of 16-bit operands (bf16 or float16 storage)
+template <typename ET>
 __device__ __forceinline__ f32x4_t mma32(const u16x8_t& a, const u16x8_t& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
+  if constexpr (std::is_same<ET, bf16_t>::value) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                  0, 0);
+  }
 }
 
 template <int KS, int NWV_, int XN_, int XD_, int ZN_, int ZD_, int SG_ = 0>
@@ -155,7 +163,7 @@ __device__ __forceinline__ void step_wait(int s) {
   }
 }
 
-template <int W, int KS, int SG>
+template <typename ET, int W, int KS, int SG>
 __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRankParams p) {
   using F = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD, SG>;
   constexpr int NWV = F::NWV, XN = F::XN, XD = F::XD, ZN = F::ZN, ZD = F::ZD, CPB = F::CPB;
@@ -181,8 +189,8 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   const int t_first = tr * p.Ltok;
   const int t_end = min(p.T, t_first + p.Ltok);
   const int nsteps = (t_end - t_first + kStep - 1) / kStep;
-  const bf16_t* xb = static_cast<const bf16_t*>(p.x) + b * p.xs0 + c_base;
-  const bf16_t* zb = static_cast<const bf16_t*>(p.z) + b * p.zs0;
+  const ET* xb = static_cast<const ET*>(p.x) + b * p.xs0 + c_base;
+  const ET* zb = static_cast<const ET*>(p.z) + b * p.zs0;
   const int cw = c_base + 16 * wv;  // the wave's first channel
 
   // ---- LDS DMA of one step: rows t0 .. t0 + 63 (clamped to T - 1) ----
@@ -262,7 +270,6 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
     const uint16_t* U = static_cast<const uint16_t*>(p.U);
     const bool has_bias = p.bias != nullptr;
     const uint16_t* bsrc = has_bias ? static_cast<const uint16_t*>(p.bias) : U;
-    const uint32_t bmask = has_bias ? ~0u : 0u;
     const int tap = n & 3;
     const int ltap = tap < W ? tap : W - 1;
     const int hsh = __builtin_ctz(unsigned(p.H));  // channel c takes group c / H's columns
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint16_t v = bsrc[(has_bias ? int64_t(chq >> hsh) * W : 0) + (i < W ? i : W - 1)];
-        binit[mt][i] = __uint_as_float((uint32_t(v) << 16) & (i < W ? bmask : 0u));
+        binit[mt][i] = (i < W && has_bias) ? Cvt<ET>::of_bits(v) : 0.f;
       }
     }
   }
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
 
   // y: buffer resource spanning this sequence's rows 0 .. T-1 (stores past it are dropped)
   __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<bf16_t*>(p.out) + b * p.os0, 0, int((int64_t(p.T - 1) * p.os1 + p.D) * 2), kBufWord3);
+      static_cast<ET*>(p.out) + b * p.os0, 0, int((int64_t(p.T - 1) * p.os1 + p.D) * 2), kBufWord3);
   const int ystep = int(p.os1 * 2);
   // a step's y tile is stored by the same waves one step later, 16 bytes per lane, whole
   // rows: store i of wave wv covers tile slot wv + NWV i
@@ -367,10 +374,10 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
     for (int mi = 0; mi < NM; ++mi) {
       const int m = MLO + mi;
       const u32x2 v = *reinterpret_cast<const u32x2*>(xst + (m < 0 ? lo : xhi) + m * XROW);
-      xv[mi][0] = bf16_lo(v[0]);
-      xv[mi][1] = bf16_hi(v[0]);
-      xv[mi][2] = bf16_lo(v[1]);
-      xv[mi][3] = bf16_hi(v[1]);
+      xv[mi][0] = Cvt<ET>::lo(v[0]);
+      xv[mi][1] = Cvt<ET>::hi(v[0]);
+      xv[mi][2] = Cvt<ET>::lo(v[1]);
+      xv[mi][3] = Cvt<ET>::hi(v[1]);
     }
     const unsigned char* zs = smem + Z_OFF + uz * ZSTAGE;
     unsigned char* yt = smem + Y_OFF + (s & 1) * XSTAGE + ytw;
@@ -381,9 +388,9 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
       for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8_t*>(zs + zr[ks] + j * ZROW);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        acc[mt] = mma32(afr[mt][0], bfr[0], binit[mt]);
+        acc[mt] = mma32<ET>(afr[mt][0], bfr[0], binit[mt]);
 #pragma unroll
-        for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32(afr[mt][ks], bfr[ks], acc[mt]);
+        for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32<ET>(afr[mt][ks], bfr[ks], acc[mt]);
       }
     };
     f32x4_t acc[2][4];
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
         }
         yv[mt] = y;
       }
-      *reinterpret_cast<u32x2*>(yt + j * XROW) = u32x2{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
+      *reinterpret_cast<u32x2*>(yt + j * XROW) = u32x2{Cvt<ET>::pack2(yv[0], yv[1]), Cvt<ET>::pack2(yv[2], yv[3])};
     }
   }
   __syncthreads();
@@ -414,12 +421,12 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <int W, int KS>
+template <typename ET, int W, int KS>
 hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   if (p.seg != nullptr) {
-    hipLaunchKernelGGL((k_lowrank_fwd_fast<W, KS, 1>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_fwd_fast<ET, W, KS, 1>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_lowrank_fwd_fast<W, KS, 0>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_fwd_fast<ET, W, KS, 0>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -458,7 +465,7 @@ struct BwdDxFast {
   static constexpr int DI = 2, ZI = KS, ND = DI + ZI, NS = 2;
 };
 
-template <int W, int KS, int SG>
+template <typename ET, int W, int KS, int SG>
 __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams p) {
   using F = BwdDxFast<KS, SG>;
   constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
@@ -479,8 +486,8 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
   const int t_first = tr * p.Ltok;
   const int t_end = min(p.T, t_first + p.Ltok);
   const int nsteps = (t_end - t_first + kStep - 1) / kStep;
-  const char* dyc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.dy) + b * p.dys0 + c_base);
-  const char* zc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.z) + b * p.zs0);
+  const char* dyc = reinterpret_cast<const char*>(static_cast<const ET*>(p.dy) + b * p.dys0 + c_base);
+  const char* zc = reinterpret_cast<const char*>(static_cast<const ET*>(p.z) + b * p.zs0);
   const int cw = c_base + 16 * wv;
 
   // ---- LDS DMA of a step's dy and z rows (rows past T - 1 read row T - 1) ----
@@ -543,7 +550,6 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
     const uint16_t* U = static_cast<const uint16_t*>(p.U);
     const bool has_bias = p.bias != nullptr;
     const uint16_t* bsrc = has_bias ? static_cast<const uint16_t*>(p.bias) : U;
-    const uint32_t bmask = has_bias ? ~0u : 0u;
     const int tap = n & 3;
     const int ltap = tap < W ? tap : W - 1;
     const int hsh = __builtin_ctz(unsigned(p.H));  // channel c takes group c / H's columns
@@ -562,7 +568,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint16_t v = bsrc[(has_bias ? int64_t(chq >> hsh) * W : 0) + (i < W ? i : W - 1)];
-        binit[mt][i] = __uint_as_float((uint32_t(v) << 16) & (i < W ? bmask : 0u));
+        binit[mt][i] = (i < W && has_bias) ? Cvt<ET>::of_bits(v) : 0.f;
       }
     }
   }
@@ -583,7 +589,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
     trow[j] = r * XROW + ((xc + (r >> 2)) & (XCPR - 1)) * 16 + 8 * (q & 1);
   }
   __amdgpu_buffer_rsrc_t dxr = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<bf16_t*>(p.out) + b * p.os0, 0, int((int64_t(p.T - 1) * p.os1 + p.D) * 2), kBufWord3);
+      static_cast<ET*>(p.out) + b * p.os0, 0, int((int64_t(p.T - 1) * p.os1 + p.D) * 2), kBufWord3);
   const int dstep = int(p.os1 * 2);
   int ttr[F::NS], tgo[F::NS], trr[F::NS];
 #pragma unroll
@@ -631,10 +637,10 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(ds + j * XROW);
-        dyv[j][0] = bf16_lo(v[0]);
-        dyv[j][1] = bf16_hi(v[0]);
-        dyv[j][2] = bf16_lo(v[1]);
-        dyv[j][3] = bf16_hi(v[1]);
+        dyv[j][0] = Cvt<ET>::lo(v[0]);
+        dyv[j][1] = Cvt<ET>::hi(v[0]);
+        dyv[j][2] = Cvt<ET>::lo(v[1]);
+        dyv[j][3] = Cvt<ET>::hi(v[1]);
       }
       if (t0 + kStep > p.T) {
 #pragma unroll
@@ -660,9 +666,9 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
       for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8_t*>(zs + zr[ks] + j * ZROW);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        acc[mt] = mma32(afr[mt][0], bfr[0], binit[mt]);
+        acc[mt] = mma32<ET>(afr[mt][0], bfr[0], binit[mt]);
 #pragma unroll
-        for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32(afr[mt][ks], bfr[ks], acc[mt]);
+        for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32<ET>(afr[mt][ks], bfr[ks], acc[mt]);
       }
     };
     // own[j]: dx of the lane's token j from its own terms; out[m]: terms for the previous
@@ -712,7 +718,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
     unsigned char* tt = smem + T_OFF + u * XSTAGE;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x2*>(tt + trow[j]) = u32x2{pack_bf16x2(dxv[j][0], dxv[j][1]), pack_bf16x2(dxv[j][2], dxv[j][3])};
+      *reinterpret_cast<u32x2*>(tt + trow[j]) = u32x2{Cvt<ET>::pack2(dxv[j][0], dxv[j][1]), Cvt<ET>::pack2(dxv[j][2], dxv[j][3])};
   }
   __syncthreads();
   tflush(nsteps & 1, nsteps, t_first + nsteps * kStep);
@@ -798,7 +804,7 @@ struct BwdGduFast {
   static constexpr int XI = 2, DI = 2, ZI = KS, ND = XI + DI + ZI + SG;
 };
 
-template <int W, int KS, int SG>
+template <typename ET, int W, int KS, int SG>
 __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParams p) {
   using F = BwdGduFast<KS, SG>;
   constexpr int CPR = F::CPR, ROW = F::ROW, STAGE = F::STAGE, XN = F::XN;
@@ -821,9 +827,9 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
   const int t_first = tr * p.Ltok;
   const int t_end = min(p.T, t_first + p.Ltok);
   const int nsteps = (t_end - t_first + kStep - 1) / kStep;
-  const char* xc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.x) + b * p.xs0 + c_base);
-  const char* dc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.dy) + b * p.dys0 + c_base);
-  const char* zc = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.z) + b * p.zs0);
+  const char* xc = reinterpret_cast<const char*>(static_cast<const ET*>(p.x) + b * p.xs0 + c_base);
+  const char* dc = reinterpret_cast<const char*>(static_cast<const ET*>(p.dy) + b * p.dys0 + c_base);
+  const char* zc = reinterpret_cast<const char*>(static_cast<const ET*>(p.z) + b * p.zs0);
 
   // ---- LDS DMA: per lane the byte offset of its source chunk from a step's first row ----
   uint32_t xoff[2], doff[2], zoff[KS];
@@ -922,9 +928,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
 
   const uint32_t lds0 = lds_addr(smem);
   constexpr int NR = 5 + 2 * RT;  // transposing reads per K step: dy 2, x 3, z 2 per rank tile
-  auto bf = [](const u32x2& w, int e) {
-    return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
-  };
+  auto bf = [](const u32x2& w, int e) { return (e & 1) ? Cvt<ET>::hi(w[e >> 1]) : Cvt<ET>::lo(w[e >> 1]); };
 
   for (int s = 0; s < nsteps; ++s) {
     const int t0 = t_first + s * kStep;
@@ -1020,11 +1024,11 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
           sum += g[e];
         }
         db[k] += sum;
-        const u32x4 w = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
-                         pack_bf16x2(g[6], g[7])};
+        const u32x4 w = {Cvt<ET>::pack2(g[0], g[1]), Cvt<ET>::pack2(g[2], g[3]), Cvt<ET>::pack2(g[4], g[5]),
+                         Cvt<ET>::pack2(g[6], g[7])};
         const u16x8_t a16 = __builtin_bit_cast(u16x8_t, w);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) dU[k][rt] = mma32(a16, bz[rt], dU[k][rt]);
+        for (int rt = 0; rt < RT; ++rt) dU[k][rt] = mma32<ET>(a16, bz[rt], dU[k][rt]);
       }
     }
   }
@@ -1109,21 +1113,21 @@ constexpr int fwd_fast_resident(int lds_bytes) {
   return by_lds < by_waves ? by_lds : by_waves;
 }
 
-template <int W, int KS>
+template <typename ET, int W, int KS>
 hipError_t fwd_fast_try(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   if constexpr (fwd_fast_rank_ok(KS)) {
-    return fwd_fast_inst<W, KS>(p, blocks, s);
+    return fwd_fast_inst<ET, W, KS>(p, blocks, s);
   } else {
     return hipErrorInvalidValue;
   }
 }
 
-template <int W>
+template <typename ET, int W>
 hipError_t fwd_fast_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   switch (p.R / 32) {
-    case 1: return fwd_fast_try<W, 1>(p, blocks, s);
-    case 2: return fwd_fast_try<W, 2>(p, blocks, s);
-    case 4: return fwd_fast_try<W, 4>(p, blocks, s);
+    case 1: return fwd_fast_try<ET, W, 1>(p, blocks, s);
+    case 2: return fwd_fast_try<ET, W, 2>(p, blocks, s);
+    case 4: return fwd_fast_try<ET, W, 4>(p, blocks, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1147,7 +1151,8 @@ bool lowrank_fast_group_ok(int H) { return H == 1 || H == 2 || H == 4 || H == 8 
 
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   const int ks = p.R / 32;
-  return dt == DYNCONV_BF16 && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 && p.R % 32 == 0 && fwd_fast_rank_ok(ks) &&
+  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 && p.R % 32 == 0 &&
+         fwd_fast_rank_ok(ks) &&
          p.D % (16 * LRF_NWV) == 0 && p.act16 != 0 && p.z16 != 0 &&
          (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) && int64_t(kStep) * p.xs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.zs1 < (int64_t(1) << 30);
@@ -1176,7 +1181,7 @@ LowRankPlan plan_lowrank_fwd_fast(int64_t B, int64_t T, int64_t D, int ks) {
   return pl;
 }
 
-hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t s) {
+hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t s) {
   const LowRankPlan pl = plan_lowrank_fwd_fast(p.B, p.T, p.D, p.R / 32);
   LowRankParams q = p;
   q.cs0 = 0;
@@ -1184,13 +1189,17 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t s)
   q.nCs = pl.nCs;
   q.Ltok = pl.Ltok;
   q.nTr = pl.nTr;
-  switch (W) {
-    case 1: return fwd_fast_ks<1>(q, pl.blocks, s);
-    case 2: return fwd_fast_ks<2>(q, pl.blocks, s);
-    case 3: return fwd_fast_ks<3>(q, pl.blocks, s);
-    case 4: return fwd_fast_ks<4>(q, pl.blocks, s);
-    default: return hipErrorInvalidValue;
-  }
+  auto by_w = [&](auto tag) -> hipError_t {
+    using ET = decltype(tag);
+    switch (W) {
+      case 1: return fwd_fast_ks<ET, 1>(q, pl.blocks, s);
+      case 2: return fwd_fast_ks<ET, 2>(q, pl.blocks, s);
+      case 3: return fwd_fast_ks<ET, 3>(q, pl.blocks, s);
+      case 4: return fwd_fast_ks<ET, 4>(q, pl.blocks, s);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return dt == DYNCONV_F16 ? by_w(f16_t{}) : by_w(bf16_t{});
 }
 
 }  // namespace dynconv
@@ -1199,22 +1208,22 @@ namespace dynconv {
 
 namespace {
 
-template <int W, int KS>
+template <typename ET, int W, int KS>
 hipError_t bwd_dx_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   if (p.seg != nullptr) {
-    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int W>
+template <typename ET, int W>
 hipError_t bwd_dx_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   switch (p.R / 32) {
-    case 1: return bwd_dx_inst<W, 1>(p, blocks, s);
-    case 2: return bwd_dx_inst<W, 2>(p, blocks, s);
-    case 4: return bwd_dx_inst<W, 4>(p, blocks, s);
+    case 1: return bwd_dx_inst<ET, W, 1>(p, blocks, s);
+    case 2: return bwd_dx_inst<ET, W, 2>(p, blocks, s);
+    case 4: return bwd_dx_inst<ET, W, 4>(p, blocks, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1223,51 +1232,55 @@ hipError_t bwd_dx_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
 
 bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   const int ks = p.R / 32;
-  return dt == DYNCONV_BF16 && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 && p.R % 32 == 0 &&
-         (ks == 1 || ks == 2 || ks == 4) && p.D % 64 == 0 && p.act16 != 0 && p.z16 != 0 && (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
+  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 &&
+         p.R % 32 == 0 && (ks == 1 || ks == 2 || ks == 4) && p.D % 64 == 0 && p.act16 != 0 && p.z16 != 0 && (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
          int64_t(kStep) * p.dys1 < (int64_t(1) << 30) && int64_t(kStep) * p.zs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.xs1 < (int64_t(1) << 30);
 }
 
-template <int W, int KS>
+template <typename ET, int W, int KS>
 hipError_t bwd_gdu_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   if (p.seg != nullptr) {
-    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int W>
+template <typename ET, int W>
 hipError_t bwd_gdu_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   switch (p.R / 32) {
-    case 1: return bwd_gdu_inst<W, 1>(p, blocks, s);
-    case 2: return bwd_gdu_inst<W, 2>(p, blocks, s);
-    case 4: return bwd_gdu_inst<W, 4>(p, blocks, s);
+    case 1: return bwd_gdu_inst<ET, W, 1>(p, blocks, s);
+    case 2: return bwd_gdu_inst<ET, W, 2>(p, blocks, s);
+    case 4: return bwd_gdu_inst<ET, W, 4>(p, blocks, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 bool lowrank_bwd_fast(const LowRankParams& p, int W, dynconv_dtype dt) {
-  return dt == DYNCONV_BF16 && (p.seg == nullptr || lowrank_seg_fast_ok(p)) && lowrank_bwd_dx_fast_ok(p, W, dt);
+  return (p.seg == nullptr || lowrank_seg_fast_ok(p)) && lowrank_bwd_dx_fast_ok(p, W, dt);
 }
 
-hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, hipStream_t s) {
+hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t s) {
   // token ranges as planned for the partial sums (Ltok, nTr), 64-channel slices
   LowRankParams q = p;
   q.nCsL = p.D / 64;
   const int64_t blocks = int64_t(p.B) * p.nTr * q.nCsL;
-  switch (W) {
-    case 1: return bwd_gdu_ks<1>(q, blocks, s);
-    case 2: return bwd_gdu_ks<2>(q, blocks, s);
-    case 3: return bwd_gdu_ks<3>(q, blocks, s);
-    case 4: return bwd_gdu_ks<4>(q, blocks, s);
-    default: return hipErrorInvalidValue;
-  }
+  auto by_w = [&](auto tag) -> hipError_t {
+    using ET = decltype(tag);
+    switch (W) {
+      case 1: return bwd_gdu_ks<ET, 1>(q, blocks, s);
+      case 2: return bwd_gdu_ks<ET, 2>(q, blocks, s);
+      case 3: return bwd_gdu_ks<ET, 3>(q, blocks, s);
+      case 4: return bwd_gdu_ks<ET, 4>(q, blocks, s);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return dt == DYNCONV_F16 ? by_w(f16_t{}) : by_w(bf16_t{});
 }
 
-hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t s) {
+hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t s) {
   // two or three workgroups per CU (48 KiB of LDS at R = 64): about 512 of them
   LowRankPlan pl{};
   pl.nCs = p.D / 64;
@@ -1285,13 +1298,17 @@ hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t
   q.Ltok = int(L);
   q.nTr = int((p.T + L - 1) / L);
   const int64_t blocks = int64_t(p.B) * q.nTr * pl.nCs;
-  switch (W) {
-    case 1: return bwd_dx_ks<1>(q, blocks, s);
-    case 2: return bwd_dx_ks<2>(q, blocks, s);
-    case 3: return bwd_dx_ks<3>(q, blocks, s);
-    case 4: return bwd_dx_ks<4>(q, blocks, s);
-    default: return hipErrorInvalidValue;
-  }
+  auto by_w = [&](auto tag) -> hipError_t {
+    using ET = decltype(tag);
+    switch (W) {
+      case 1: return bwd_dx_ks<ET, 1>(q, blocks, s);
+      case 2: return bwd_dx_ks<ET, 2>(q, blocks, s);
+      case 3: return bwd_dx_ks<ET, 3>(q, blocks, s);
+      case 4: return bwd_dx_ks<ET, 4>(q, blocks, s);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return dt == DYNCONV_F16 ? by_w(f16_t{}) : by_w(bf16_t{});
 }
 
 }  // namespace dynconv

@@ -77,19 +77,19 @@ dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& pla
 // Group sizes the fast bf16 kernels serve: H in {1, 2, 4, 8, 16}, so that a 64-channel
 // slice holds whole groups (each channel loads its group's columns of U and of the bias).
 bool lowrank_fast_group_ok(int H);
-// bf16 fast forward (LDS DMA pipeline; W <= 4, R in {32, 64, 128}, those H, 16-byte
-// aligned rows, D a multiple of 64). It plans its own token ranges.
+// 16-bit (bf16, float16) fast forward (LDS DMA pipeline; W <= 4, R in {32, 64, 128}, those
+// H, 16-byte aligned rows, D a multiple of 64). It plans its own token ranges.
 // Packed sequences on the fast forward: contiguous, 16-byte aligned id rows, T % 4 == 0.
 bool lowrank_seg_fast_ok(const LowRankParams& p);
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
-hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, hipStream_t stream);
-// bf16 fast dx of the backward (same conditions, on dy and dx); it plans its own ranges.
+hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
+// 16-bit fast dx of the backward (same conditions, on dy and dx); it plans its own ranges.
 bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
-hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, hipStream_t stream);
-// bf16 fast g / dU / db partial sums (same conditions as the fast dx, on x too), over the
+hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
+// 16-bit fast g / dU / db partial sums (same conditions as the fast dx, on x too), over the
 // planned token ranges (Ltok, nTr) and 64-channel slices; one partial per token range and
 // group column (a group's H channels summed inside the workgroup).
-hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, hipStream_t stream);
+hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
 // Whether the backward runs on the fast kernels (dx, then g / dU / db): they write
 // B * nTr partials per filter column, the general kernel B * nTr * H.
 bool lowrank_bwd_fast(const LowRankParams& p, int W, dynconv_dtype dt);

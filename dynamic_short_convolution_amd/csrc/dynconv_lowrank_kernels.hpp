@@ -1394,7 +1394,7 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int W, int KS, int HG>
+template <typename ET, int W, int KS, int HG>
 __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned char* smem, int b, int tb0) {
   using D = LrDzDma<W, KS, HG>;
   constexpr int RP = D::RP, CH = D::CH, UC = D::UC, UCPR = D::UCPR, XCPR = D::XCPR;
@@ -1408,9 +1408,9 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
   const int n = lane & 15;
   const int wv = tid >> 6;
   const int nchunk = p.D / D::CHC;
-  const bf16_t* U = static_cast<const bf16_t*>(p.U);
-  const bf16_t* xb = static_cast<const bf16_t*>(p.x) + b * p.xs0 + int64_t(tb0 - HALO) * p.xs1;
-  const bf16_t* dyb = static_cast<const bf16_t*>(p.dy) + b * p.dys0 + int64_t(tb0) * p.dys1;
+  const ET* U = static_cast<const ET*>(p.U);
+  const ET* xb = static_cast<const ET*>(p.x) + b * p.xs0 + int64_t(tb0 - HALO) * p.xs1;
+  const ET* dyb = static_cast<const ET*>(p.dy) + b * p.dys0 + int64_t(tb0) * p.dys1;
 
   // this wave's transfers of a stage: instructions wv, wv + 4, ... of each region; per
   // lane the element offset of its source chunk relative to the chunk's base
@@ -1446,7 +1446,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
     ci = min(ci, nchunk - 1);  // past the last chunk: reload it (never read)
     const int c0 = ci * D::CHC;  // first channel; the chunk's filter columns start at ci * CH * W
     unsigned char* stage = smem + st * D::STAGE;
-    const bf16_t* ub = U + int64_t(ci) * (CH * W);
+    const ET* ub = U + int64_t(ci) * (CH * W);
 #pragma unroll
     for (int i = 0; i < SU; ++i)
       if (uact[i]) dma16(ub + uoffg[i], stage + (wv + 4 * i) * 1024);
@@ -1524,12 +1524,12 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
     }
     float dyf[8 * RUNS];
 #pragma unroll
-    for (int j = 0; j < 8 * RUNS; ++j) dyf[j] = (j & 1) ? bf16_hi(dw_[j >> 3][(j & 7) >> 1]) : bf16_lo(dw_[j >> 3][(j & 7) >> 1]);
+    for (int j = 0; j < 8 * RUNS; ++j) dyf[j] = (j & 1) ? Cvt<ET>::hi(dw_[j >> 3][(j & 7) >> 1]) : Cvt<ET>::lo(dw_[j >> 3][(j & 7) >> 1]);
     // column (group g of the lane, tap k): the sum over the group's HG channels
     auto col = [&](int g, int k) -> float {
       auto prod = [&](int j) {
         const uint32_t wd = xw[k][j >> 3][(j & 7) >> 1];
-        return dyf[j] * ((j & 1) ? bf16_hi(wd) : bf16_lo(wd));
+        return dyf[j] * ((j & 1) ? Cvt<ET>::hi(wd) : Cvt<ET>::lo(wd));
       };
       float v = prod(g * HG);
 #pragma unroll
@@ -1538,40 +1538,41 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
     };
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
-      Mfma<bf16_t>::F32k bfr;
+      typename Mfma<ET>::F32k bfr;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const int c0_ = (8 * ks + e) / W, k0_ = (8 * ks + e) % W;
         const int c1_ = (8 * ks + e + 1) / W, k1_ = (8 * ks + e + 1) % W;
-        const uint32_t w2 = pack_bf16x2(col(c0_, k0_), col(c1_, k1_));
+        const uint32_t w2 = Cvt<ET>::pack2(col(c0_, k0_), col(c1_, k1_));
         bfr.v[e] = uint16_t(w2 & 0xffffu);
         bfr.v[e + 1] = uint16_t(w2 >> 16);
       }
 #pragma unroll
       for (int rt = 0; rt < RTN; ++rt) {
-        Mfma<bf16_t>::F32k afr;
+        typename Mfma<ET>::F32k afr;
         afr.v = *reinterpret_cast<const u16x8_t*>(stage + u_off[ks] + rt * 16 * UC * 2);
-        acc[rt] = Mfma<bf16_t>::mma32(afr, bfr, acc[rt]);
+        acc[rt] = Mfma<ET>::mma32(afr, bfr, acc[rt]);
       }
     }
   }
   // drain this wave's remaining transfers (into stages nobody reads) before leaving
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-  bf16_t* dz = static_cast<bf16_t*>(p.dz) + b * p.dzs0;
+  ET* dz = static_cast<ET*>(p.dz) + b * p.dzs0;
   const int t = tb0 + nt;
 #pragma unroll
   for (int rt = 0; rt < RTN; ++rt)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int r = rt * 16 + 4 * q + ii;
-      reinterpret_cast<uint16_t*>(dz)[int64_t(t) * p.dzs1 + r] = to_bf16_bits(acc[rt][ii]);
+      reinterpret_cast<uint16_t*>(dz)[int64_t(t) * p.dzs1 + r] = Cvt<ET>::bits(acc[rt][ii]);
     }
 }
 
-// The LDS DMA path serves bf16 token blocks that lie inside T when its stages fit.
+// The LDS DMA path serves 16-bit (bf16, float16) token blocks that lie inside T when its
+// stages fit.
 template <typename ET, int W, int KS, int HG>
 constexpr bool lowrank_dz_dma_ok() {
-  return std::is_same<ET, bf16_t>::value && LrDzDma<W, KS, HG>::SHAPE_OK && LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
+  return (std::is_same<ET, bf16_t>::value || std::is_same<ET, f16_t>::value) && LrDzDma<W, KS, HG>::SHAPE_OK && LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
 }
 
 // The register-staged path: any storage type, ragged token blocks, unaligned rows, any
@@ -1584,11 +1585,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParam
 
 // The LDS DMA path: the launch covers whole token blocks; aligned rows, D % (32 * HG) == 0
 // and R % 32 == 0.
-template <int W, int KS, int HG>
+template <typename ET, int W, int KS, int HG>
 __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz_dma(const LowRankParams p) {
   __shared__ __align__(16) unsigned char smem[LrDzDma<W, KS, HG>::BYTES];
   const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  lowrank_dz_dma<W, KS, HG>(p, smem, int(lb / uint32_t(p.nTbL)),
+  lowrank_dz_dma<ET, W, KS, HG>(p, smem, int(lb / uint32_t(p.nTbL)),
                             (p.tbb0 + int(lb % uint32_t(p.nTbL))) * kLowrankDzTokens);
 }
 
@@ -1596,7 +1597,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz_dma(const LowRankP
 template <typename ET, int W, int KS, int HG>
 hipError_t launch_dz_dma(const LowRankParams& q, hipStream_t s) {
   if constexpr (lowrank_dz_dma_ok<ET, W, KS, HG>()) {
-    hipLaunchKernelGGL((k_lowrank_dz_dma<W, KS, HG>), dim3(unsigned(int64_t(q.B) * q.nTbL)), dim3(kBlockThreads), 0,
+    hipLaunchKernelGGL((k_lowrank_dz_dma<ET, W, KS, HG>), dim3(unsigned(int64_t(q.B) * q.nTbL)), dim3(kBlockThreads), 0,
                        s, q);
     return hipGetLastError();
   } else {
@@ -1622,15 +1623,17 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   // otherwise one main kernel (the channel slices inside D on the 16-byte path, the rest on
   // the other)
   // (packed sequences: with contiguous, aligned id rows and T % 4 == 0)
-  const bool fast = std::is_same<ET, bf16_t>::value && lowrank_bwd_fast(p, W, DYNCONV_BF16);
+  constexpr bool h16 = std::is_same<ET, bf16_t>::value || std::is_same<ET, f16_t>::value;
+  constexpr dynconv_dtype dt = std::is_same<ET, f16_t>::value ? DYNCONV_F16 : DYNCONV_BF16;
+  const bool fast = h16 && lowrank_bwd_fast(p, W, dt);
   LowRankParams q = p;
   const int64_t per_slice = int64_t(p.B) * pl.nTr;
   const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;
   const int nfull = fast ? pl.nCs : vec ? p.D / lowrank_bwd_dc(W, KS) : 0;
   if (fast) {
-    hipError_t e = launch_lowrank_bwd_dx_fast(p, W, s);
+    hipError_t e = launch_lowrank_bwd_dx_fast(p, W, dt, s);
     if (e != hipSuccess) return e;
-    e = launch_lowrank_bwd_gdu_fast(p, W, s);
+    e = launch_lowrank_bwd_gdu_fast(p, W, dt, s);
     if (e != hipSuccess) return e;
   } else if (nfull > 0) {
     q.cs0 = 0;

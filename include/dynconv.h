@@ -30,7 +30,7 @@
  *   (float32, bfloat16 or float16). Reduced parameter gradients (static dw, dU, db) are
  *   always float32 and contiguous.
  * - Arithmetic is float32 (products and sums), 16-bit results are rounded to nearest even.
- *   The bf16 fast low-rank kernels serve bfloat16 only; float16 takes the general ones.
+ *   The fast low-rank kernels serve bfloat16 and float16; float32 takes the general ones.
  * - Validation happens before any HIP call; invalid input returns a status, never aborts.
  *   B == 0 or T == 0 or D == 0 is a no-op returning DYNCONV_OK.
  * - Supported parameters: 1 <= W <= 8 (low-rank form: W <= 5); H == 1 or H a power of two that divides D, with

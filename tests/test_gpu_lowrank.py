@@ -166,28 +166,31 @@ for W in (1, 2, 3, 4):
             FAST.append((W, R, B, T, D))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("W,R,B,T,D", FAST)
-def test_fast_parity(W, R, B, T, D):
-    _check(B, T, D, W, R, "bf16", seed=1000 + 7 * W + R + T)
+def test_fast_parity(W, R, B, T, D, dtype):
+    _check(B, T, D, W, R, dtype, seed=1000 + 7 * W + R + T)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("W", [1, 4])
-def test_fast_no_bias(W):
-    _check(2, 130, 128, W, 64, "bf16", seed=77 + W, bias=False)
+def test_fast_no_bias(W, dtype):
+    _check(2, 130, 128, W, 64, dtype, seed=77 + W, bias=False)
 
 
-def test_fast_fwd_multistep_ranges():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fast_fwd_multistep_ranges(dtype):
     """Token ranges of several 64-token steps (the LDS ring wraps), a partial last step,
     and the rows before each range carried from memory; checked on sampled channels."""
     B, T, D, W, R = 2, 3000, 2048, 4, 64
-    x, z, U, b, _ = _inputs(B, T, D, W, R, "bf16", 31)
+    x, z, U, b, _ = _inputs(B, T, D, W, R, dtype, 31)
     y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W)
     chans = np.concatenate([np.arange(0, 64), np.arange(1088, 1152), np.arange(1984, 2048)])
     ci = torch.as_tensor(chans)
     cols = torch.as_tensor((chans[:, None] * W + np.arange(W)[None, :]).reshape(-1))
     ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
                       to64(b.index_select(0, cols)), W)
-    assert_close("y", y.index_select(2, ci.cuda()).cpu(), ref, torch.bfloat16)
+    assert_close("y", y.index_select(2, ci.cuda()).cpu(), ref, y.dtype)
 
 
 def test_fast_fwd_strided_views():
@@ -206,18 +209,19 @@ def test_fast_fwd_strided_views():
     assert torch.count_nonzero(yw[:, :, :D]) == 0, "write outside the output view"
 
 
-def test_fast_bwd_multistep_ranges():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fast_bwd_multistep_ranges(dtype):
     """Backward dx over token ranges of several steps: the rows completed by the tail step
     of one range and skipped by the first step of the next; sampled channels."""
     B, T, D, W, R = 2, 3000, 2048, 4, 64
-    x, z, U, b, dy = _inputs(B, T, D, W, R, "bf16", 32)
+    x, z, U, b, dy = _inputs(B, T, D, W, R, dtype, 32)
     dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W)
     chans = np.concatenate([np.arange(0, 64), np.arange(1088, 1152), np.arange(1984, 2048)])
     ci = torch.as_tensor(chans)
     cols = torch.as_tensor((chans[:, None] * W + np.arange(W)[None, :]).reshape(-1))
     rdx, _, _, _ = lowrank_bwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
                                to64(b.index_select(0, cols)), to64(dy.index_select(2, ci)), W)
-    assert_close("dx", dx.index_select(2, ci.cuda()).cpu(), rdx, torch.bfloat16)
+    assert_close("dx", dx.index_select(2, ci.cuda()).cpu(), rdx, dx.dtype)
 
 
 # ------------------------------------------------------------------------------------
@@ -267,27 +271,28 @@ def test_headwise_lowrank_parity(dtype, H, W, R):
 HEADWISE_DMA = [(H, W, R) for H in (2, 4, 8, 16) for W in (1, 2, 3, 4, 5) for R in (32, 64, 96, 128)]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("H,W,R", HEADWISE_DMA)
-def test_headwise_lowrank_fast_kernels(H, W, R):
+def test_headwise_lowrank_fast_kernels(H, W, R, dtype):
     B, T = 2, 200
     D = 5 * 32 * H
     G = D // H
     seed = 900 + 10 * H + W + R
-    x = synth.draw((B, T, D), 1.0, seed, "x", "bf16")
-    dy = synth.draw((B, T, D), 1.0, seed, "dy", "bf16")
-    z = synth.draw((B, T, R), 1.0, seed, "z", "bf16")
-    U = synth.draw((R, G * W), 0.3 / R**0.5, seed, "U", "bf16")
-    b = synth.draw((G * W,), 0.3, seed, "b", "bf16")
+    td = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    x = synth.draw((B, T, D), 1.0, seed, "x", dtype)
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", dtype)
+    z = synth.draw((B, T, R), 1.0, seed, "z", dtype)
+    U = synth.draw((R, G * W), 0.3 / R**0.5, seed, "U", dtype)
+    b = synth.draw((G * W,), 0.3, seed, "b", dtype)
     x64, z64, U64, b64, dy64 = to64(x), to64(z), to64(U), to64(b), to64(dy)
     y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W, H)
-    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W, H), torch.bfloat16)
+    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W, H), td)
     dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W, H)
     rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, H)
     _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, G, W)), np.abs(dy64), H)
     gabs = gabs.reshape(B * T, G * W)
-    u = 2.0**-8
-    assert_close("dz", dz, rdz, torch.bfloat16, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
-    assert_close("dx", dx, rdx, torch.bfloat16)
-    assert_close("dU", dU, rdU, torch.bfloat16, rtol=1e-5, atol=1e-5,
-                 extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
-    assert_close("db", db, rdb, torch.bfloat16, rtol=1e-5, atol=1e-5)
+    u = {torch.bfloat16: 2.0**-8, torch.float16: 2.0**-11}[td]
+    assert_close("dz", dz, rdz, td, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
+    assert_close("dx", dx, rdx, td)
+    assert_close("dU", dU, rdU, td, rtol=1e-5, atol=1e-5, extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
+    assert_close("db", db, rdb, td, rtol=1e-5, atol=1e-5)
