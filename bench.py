@@ -227,6 +227,8 @@ ROWS = (
     "packed_perchannel_h1_bwd",
     "packed_lowrank_r64_fwd",
     "packed_lowrank_r64_bwd",
+    "lowrank_r64_f16_fwd",
+    "lowrank_r64_f16_bwd",
 )
 PACKED_MEAN_DOC = 512.0  # mean document length of the packed rows (tokens)
 
@@ -278,24 +280,25 @@ def make_row(name, device):
         return (lambda: dynconv_lowrank_decode_step(x, z, U, b, cache, 7, W, out=y)), \
             io + B * R * 2 + R * D * W * 2 + D * W * 2, 2 * B * R * D * W, f"decode step B{B} D{D} W{W} R{R} bf16"
     if name.startswith("lowrank"):
-        # lowrank_h4_*: head-wise generation, U of R x (D/4)*W
+        # lowrank_h4_*: head-wise generation, U of R x (D/4)*W; *_f16_*: float16 storage
         B, T, D, W, R = 8, 4096, 2048, 4, 64
         H = 4 if name.startswith("lowrank_h4") else 1
+        dt = torch.float16 if "_f16_" in name else torch.bfloat16
         J = (D // H) * W
-        x = gen((B, T, D), 1.0, 4, "x", device)
-        z = gen((B, T, R), 1.0, 4, "z", device)
-        U = gen((R, J), 0.1 / R**0.5, 4, "U", device)
-        b = gen((J,), 0.1**0.5, 4, "b", device)
-        desc = tag(f"B{B} T{T} D{D} W{W} R{R}{f' H{H}' if H > 1 else ''} bf16", B, T)
+        x = gen((B, T, D), 1.0, 4, "x", device).to(dt)
+        z = gen((B, T, R), 1.0, 4, "z", device).to(dt)
+        U = gen((R, J), 0.1 / R**0.5, 4, "U", device).to(dt)
+        b = gen((J,), 0.1**0.5, 4, "b", device).to(dt)
+        desc = tag(f"B{B} T{T} D{D} W{W} R{R}{f' H{H}' if H > 1 else ''} {'f16' if dt == torch.float16 else 'bf16'}",
+                   B, T)
         seq = segs(B, T)
         sb = 4 * B * T if packed else 0
         if name.endswith("fwd"):
             y = torch.empty_like(x)
             return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, H, out=y, seq_idx=seq)), \
                 lowrank_bytes(B, T, D, W, R, H=H) + sb, lowrank_flops(B, T, D, W, R, H=H), desc
-        dy = gen((B, T, D), 1.0, 4, "dy", device)
-        ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, torch.bfloat16), dtype=torch.uint8,
-                         device=device)
+        dy = gen((B, T, D), 1.0, 4, "dy", device).to(dt)
+        ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dt), dtype=torch.uint8, device=device)
         return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, H, workspace=ws, seq_idx=seq)), \
             lowrank_bytes(B, T, D, W, R, fwd=False, H=H) + sb, lowrank_flops(B, T, D, W, R, fwd=False, H=H), desc
     if name.startswith("qkv"):
