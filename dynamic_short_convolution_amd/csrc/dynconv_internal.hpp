@@ -74,6 +74,10 @@ dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, 
 // Fixed-order sum of [nchunk][n] float32 partials into out[n].
 dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,
                                       hipStream_t stream);
+// The same for two sums over the same number of chunks, in one launch where both allow
+// 16-byte loads (else two launches). Each result is bit-identical to its own reduce.
+dynconv_status launch_reduce_partials2(const float* part0, int64_t n0, float* out0, const float* part1, int64_t n1,
+                                       float* out1, int64_t nchunk, hipStream_t stream);
 
 // Records a HIP failure for dynconv_last_hip_error(); returns DYNCONV_ERR_HIP.
 dynconv_status record_hip_error(hipError_t e);

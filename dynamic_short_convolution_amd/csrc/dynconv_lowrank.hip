@@ -61,9 +61,8 @@ dynconv_status launch_lowrank_bwd(const LowRankParams& p, const LowRankPlan& pla
   // partials per filter column: one per token range on the fast kernels, one per (token
   // range, channel of the group) on the general kernel
   const int64_t nR = int64_t(p.B) * plan.nTr * (lowrank_bwd_fast(p, W, dt) ? 1 : p.H);
-  dynconv_status st = launch_reduce_partials(p.part_dU, nR, int64_t(p.R) * p.J, dU, stream);
-  if (st != DYNCONV_OK || db == nullptr) return st;
-  return launch_reduce_partials(p.part_db, nR, p.J, db, stream);
+  if (db == nullptr) return launch_reduce_partials(p.part_dU, nR, int64_t(p.R) * p.J, dU, stream);
+  return launch_reduce_partials2(p.part_dU, int64_t(p.R) * p.J, dU, p.part_db, p.J, db, nR, stream);
 }
 
 }  // namespace dynconv

@@ -71,12 +71,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials(const float* 
 // are bit-identical to k_reduce_partials.
 constexpr int kRedCols4 = 4 * kRedCols;
 
-__global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4(const float* __restrict__ part, int64_t nchunk,
-                                                                    int64_t n, float* __restrict__ out) {
+__device__ __forceinline__ void reduce4_block(const float* __restrict__ part, int64_t nchunk, int64_t n,
+                                              float* __restrict__ out, int64_t blk) {
   __shared__ double red[kRedGroups][kRedCols][4];
   const int col = threadIdx.x % kRedCols;
   const int grp = threadIdx.x / kRedCols;
-  const int64_t i = int64_t(blockIdx.x) * kRedCols4 + 4 * col;
+  const int64_t i = blk * kRedCols4 + 4 * col;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
   if (i < n) {
     for (int64_t c = grp; c < nchunk; c += kRedGroups) {
@@ -98,6 +98,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4(const float*
       for (int e = 0; e < 4; ++e) tot[e] += red[r][col][e];
     *reinterpret_cast<float4*>(out + i) = float4{float(tot[0]), float(tot[1]), float(tot[2]), float(tot[3])};
   }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4(const float* __restrict__ part, int64_t nchunk,
+                                                                    int64_t n, float* __restrict__ out) {
+  reduce4_block(part, nchunk, n, out, blockIdx.x);
+}
+
+// Two independent sums with the same number of chunks in one launch (one dispatch gap
+// fewer): workgroups below nblk0 take the first, the others the second.
+__global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4x2(const float* __restrict__ part0, int64_t n0,
+                                                                      float* __restrict__ out0, int64_t nblk0,
+                                                                      const float* __restrict__ part1, int64_t n1,
+                                                                      float* __restrict__ out1, int64_t nchunk) {
+  if (int64_t(blockIdx.x) < nblk0) {
+    reduce4_block(part0, nchunk, n0, out0, blockIdx.x);
+  } else {
+    reduce4_block(part1, nchunk, n1, out1, int64_t(blockIdx.x) - nblk0);
+  }
+}
+
+bool reduce4_ok(const float* part, int64_t n, const float* out) {
+  return n % 4 == 0 && reinterpret_cast<uintptr_t>(part) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
 }
 
 }  // namespace
@@ -180,22 +202,20 @@ dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, 
                  : dt == DYNCONV_F16 ? stream_dispatch_f16(p, plan, W, is_static, true, stream)
                                      : stream_dispatch_f32(p, plan, W, is_static, true, stream);
   if (e != hipSuccess) return record_hip_error(e);
-  if (is_static && p.partial != nullptr) {
-    const dynconv_status st =
-        launch_reduce_partials(p.partial, int64_t(p.B) * plan.nTw, int64_t(p.G) * W, dw_static_out, stream);
-    if (st != DYNCONV_OK) return st;
+  const int64_t nchunk = int64_t(p.B) * plan.nTw;
+  const bool sdw = is_static && p.partial != nullptr;
+  if (sdw && p.cb_partial != nullptr) {
+    return launch_reduce_partials2(p.partial, int64_t(p.G) * W, dw_static_out, p.cb_partial, p.D, dcbias_out, nchunk,
+                                   stream);
   }
-  if (p.cb_partial != nullptr) {
-    return launch_reduce_partials(p.cb_partial, int64_t(p.B) * plan.nTw, p.D, dcbias_out, stream);
-  }
+  if (sdw) return launch_reduce_partials(p.partial, nchunk, int64_t(p.G) * W, dw_static_out, stream);
+  if (p.cb_partial != nullptr) return launch_reduce_partials(p.cb_partial, nchunk, p.D, dcbias_out, stream);
   return DYNCONV_OK;
 }
 
 dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,
                                       hipStream_t stream) {
-  const bool vec = n % 4 == 0 && reinterpret_cast<uintptr_t>(partial) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(out) % 16 == 0;
-  if (vec) {
+  if (reduce4_ok(partial, n, out)) {
     const int64_t blocks = (n + kRedCols4 - 1) / kRedCols4;
     hipLaunchKernelGGL(k_reduce_partials4, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk,
                        n, out);
@@ -204,6 +224,21 @@ dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int6
     hipLaunchKernelGGL(k_reduce_partials, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk, n,
                        out);
   }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
+}
+
+dynconv_status launch_reduce_partials2(const float* part0, int64_t n0, float* out0, const float* part1, int64_t n1,
+                                       float* out1, int64_t nchunk, hipStream_t stream) {
+  if (!reduce4_ok(part0, n0, out0) || !reduce4_ok(part1, n1, out1)) {
+    const dynconv_status st = launch_reduce_partials(part0, nchunk, n0, out0, stream);
+    if (st != DYNCONV_OK) return st;
+    return launch_reduce_partials(part1, nchunk, n1, out1, stream);
+  }
+  const int64_t nblk0 = (n0 + kRedCols4 - 1) / kRedCols4;
+  const int64_t nblk1 = (n1 + kRedCols4 - 1) / kRedCols4;
+  hipLaunchKernelGGL(k_reduce_partials4x2, dim3(unsigned(nblk0 + nblk1)), dim3(kBlockThreads), 0, stream, part0, n0,
+                     out0, nblk0, part1, n1, out1, nchunk);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
 }
