@@ -106,9 +106,11 @@ def test_deterministic():
             assert torch.equal(a, c)
 
 
-def test_full_lowrank_r64_fwd():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_full_lowrank_r64_fwd(dtype):
+    # float16: the same bf16-drawn values (exact in float16 but for a few tiny ones)
     wl = synth.workloads()["lowrank_r64"]
-    x, z, U, b = wl.x(), wl.z(), wl.U(), wl.b()
+    x, z, U, b = (t.to(dtype) for t in (wl.x(), wl.z(), wl.U(), wl.b()))
     y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), wl.W)
     # every token of sampled channel blocks
     chans = np.concatenate([np.arange(0, 64), np.arange(992, 1056), np.arange(1984, 2048)])
@@ -116,12 +118,14 @@ def test_full_lowrank_r64_fwd():
     cols = torch.as_tensor((chans[:, None] * wl.W + np.arange(wl.W)[None, :]).reshape(-1))
     ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), to64(U.index_select(1, cols)),
                       to64(b.index_select(0, cols)), wl.W)
-    assert_close("y", y.index_select(2, ci.cuda()).cpu(), ref, torch.bfloat16)
+    assert_close("y", y.index_select(2, ci.cuda()).cpu(), ref, dtype)
 
 
-def test_full_lowrank_r64_bwd():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_full_lowrank_r64_bwd(dtype):
     wl = synth.workloads()["lowrank_r64_bwd"]
-    x, z, U, b, dy = wl.x(), wl.z(), wl.U(), wl.b(), wl.dy()
+    x, z, U, b, dy = (t.to(dtype) for t in (wl.x(), wl.z(), wl.U(), wl.b(), wl.dy()))
+    u = {torch.bfloat16: 2.0**-8, torch.float16: 2.0**-11}[dtype]
     dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), wl.W)
     # dx, dU, db on sampled channel blocks (all tokens); dz needs every channel, so it is
     # checked on whole sequences 0 and B-1 over a token window.
@@ -135,12 +139,12 @@ def test_full_lowrank_r64_bwd():
     b64 = to64(b.index_select(0, cols))
     z64 = to64(z)
     rdx, _, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, wl.W)
-    assert_close("dx", dx.index_select(2, ci.cuda()).cpu(), rdx, torch.bfloat16)
+    assert_close("dx", dx.index_select(2, ci.cuda()).cpu(), rdx, dtype)
     gabs = _g_abs(x64, dy64, wl.W)
-    extra_dU = 2.0**-8 * (np.abs(z64).reshape(-1, wl.R).T @ gabs)
-    assert_close("dU", dU.index_select(1, cols.cuda()).cpu(), rdU, torch.bfloat16, rtol=1e-5, atol=1e-5,
+    extra_dU = u * (np.abs(z64).reshape(-1, wl.R).T @ gabs)
+    assert_close("dU", dU.index_select(1, cols.cuda()).cpu(), rdU, dtype, rtol=1e-5, atol=1e-5,
                  extra=extra_dU)
-    assert_close("db", db.index_select(0, cols.cuda()).cpu(), rdb, torch.bfloat16, rtol=1e-5, atol=1e-5)
+    assert_close("db", db.index_select(0, cols.cuda()).cpu(), rdb, dtype, rtol=1e-5, atol=1e-5)
     for bsel in (0, wl.B - 1):
         t0, t1 = 1000, 1100  # window; dz_t only needs x_{t-3..t} and dy_t
         xs = to64(x[bsel : bsel + 1, t0 - 4 : t1])
@@ -149,12 +153,12 @@ def test_full_lowrank_r64_bwd():
         _, rdz, _, _ = lowrank_bwd(xs, zs, to64(U), to64(b), dys, wl.W)
         got = dz[bsel : bsel + 1, t0:t1].cpu()
         gab = _g_abs(xs, dys, wl.W)
-        extra = (2.0**-8 * (gab @ np.abs(to64(U)).T)).reshape(1, -1, wl.R)[:, 4:]
-        assert_close("dz", got, rdz[:, 4:], torch.bfloat16, extra=extra)
+        extra = (u * (gab @ np.abs(to64(U)).T)).reshape(1, -1, wl.R)[:, 4:]
+        assert_close("dz", got, rdz[:, 4:], dtype, extra=extra)
 
 
 # ---------------------------------------------------------------------------------
-# The bf16 fast paths (W <= 4, R in {32, 64, 128}, D a multiple of 64, 16-byte aligned
+# The 16-bit fast paths (W <= 4, R in {32, 64, 128}, D a multiple of 64, 16-byte aligned
 # rows): token ranges of whole 64-token steps, an x ring in LDS that carries the W-1 rows
 # before each step (forward), dx completed across lanes, ranges and a tail step
 # (backward), buffer stores that drop rows past T.
