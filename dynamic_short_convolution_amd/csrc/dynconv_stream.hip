@@ -67,19 +67,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials(const float* 
 }
 
 // The same sums, 4 consecutive columns per thread (16-byte loads and stores): n % 4 == 0
-// and 16-byte aligned pointers. Each column is summed in the order above, so the results
-// are bit-identical to k_reduce_partials.
-constexpr int kRedCols4 = 4 * kRedCols;
+// and 16-byte aligned pointers. G thread groups split the chunks (group g takes chunks
+// g, g + G, ... in order, float64) and the G group sums are added in order g = 0 .. G-1.
+// G = 8 gives exactly the order of k_reduce_partials (bit-identical results); G = 32 serves
+// many chunks (short dependent chains, 4x the workgroups for the same columns). Either
+// order depends only on (nchunk, n): results are run-to-run identical.
+constexpr int kRedTallChunks = 64;  // from this many chunks on, G = 32
+constexpr int red_groups(int64_t nchunk) { return nchunk >= kRedTallChunks ? 32 : kRedGroups; }
 
+template <int G>
 __device__ __forceinline__ void reduce4_block(const float* __restrict__ part, int64_t nchunk, int64_t n,
                                               float* __restrict__ out, int64_t blk) {
-  __shared__ double red[kRedGroups][kRedCols][4];
-  const int col = threadIdx.x % kRedCols;
-  const int grp = threadIdx.x / kRedCols;
-  const int64_t i = blk * kRedCols4 + 4 * col;
+  constexpr int C = kBlockThreads / G;  // float4 columns of a workgroup
+  __shared__ double red[G][C][4];
+  const int col = threadIdx.x % C;
+  const int grp = threadIdx.x / C;
+  const int64_t i = blk * (4 * C) + 4 * col;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
   if (i < n) {
-    for (int64_t c = grp; c < nchunk; c += kRedGroups) {
+    for (int64_t c = grp; c < nchunk; c += G) {
       const float4 v = *reinterpret_cast<const float4*>(part + c * n + i);
       s[0] += double(v.x);
       s[1] += double(v.y);
@@ -92,29 +98,31 @@ __device__ __forceinline__ void reduce4_block(const float* __restrict__ part, in
   __syncthreads();
   if (grp == 0 && i < n) {
     double tot[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int r = 0; r < kRedGroups; ++r)
+#pragma unroll 8
+    for (int r = 0; r < G; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) tot[e] += red[r][col][e];
     *reinterpret_cast<float4*>(out + i) = float4{float(tot[0]), float(tot[1]), float(tot[2]), float(tot[3])};
   }
 }
 
+template <int G>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4(const float* __restrict__ part, int64_t nchunk,
                                                                     int64_t n, float* __restrict__ out) {
-  reduce4_block(part, nchunk, n, out, blockIdx.x);
+  reduce4_block<G>(part, nchunk, n, out, blockIdx.x);
 }
 
 // Two independent sums with the same number of chunks in one launch (one dispatch gap
 // fewer): workgroups below nblk0 take the first, the others the second.
+template <int G>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4x2(const float* __restrict__ part0, int64_t n0,
                                                                       float* __restrict__ out0, int64_t nblk0,
                                                                       const float* __restrict__ part1, int64_t n1,
                                                                       float* __restrict__ out1, int64_t nchunk) {
   if (int64_t(blockIdx.x) < nblk0) {
-    reduce4_block(part0, nchunk, n0, out0, blockIdx.x);
+    reduce4_block<G>(part0, nchunk, n0, out0, blockIdx.x);
   } else {
-    reduce4_block(part1, nchunk, n1, out1, int64_t(blockIdx.x) - nblk0);
+    reduce4_block<G>(part1, nchunk, n1, out1, int64_t(blockIdx.x) - nblk0);
   }
 }
 
@@ -216,9 +224,16 @@ dynconv_status launch_stream_bwd(const StreamParams& p, const StreamPlan& plan, 
 dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int64_t n, float* out,
                                       hipStream_t stream) {
   if (reduce4_ok(partial, n, out)) {
-    const int64_t blocks = (n + kRedCols4 - 1) / kRedCols4;
-    hipLaunchKernelGGL(k_reduce_partials4, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk,
-                       n, out);
+    const int G = red_groups(nchunk);
+    const int64_t cols = 4 * (kBlockThreads / G);
+    const int64_t blocks = (n + cols - 1) / cols;
+    if (G == 32) {
+      hipLaunchKernelGGL(k_reduce_partials4<32>, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial,
+                         nchunk, n, out);
+    } else {
+      hipLaunchKernelGGL(k_reduce_partials4<kRedGroups>, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream,
+                         partial, nchunk, n, out);
+    }
   } else {
     const int64_t blocks = (n + kRedCols - 1) / kRedCols;
     hipLaunchKernelGGL(k_reduce_partials, dim3(unsigned(blocks)), dim3(kBlockThreads), 0, stream, partial, nchunk, n,
@@ -235,10 +250,17 @@ dynconv_status launch_reduce_partials2(const float* part0, int64_t n0, float* ou
     if (st != DYNCONV_OK) return st;
     return launch_reduce_partials(part1, nchunk, n1, out1, stream);
   }
-  const int64_t nblk0 = (n0 + kRedCols4 - 1) / kRedCols4;
-  const int64_t nblk1 = (n1 + kRedCols4 - 1) / kRedCols4;
-  hipLaunchKernelGGL(k_reduce_partials4x2, dim3(unsigned(nblk0 + nblk1)), dim3(kBlockThreads), 0, stream, part0, n0,
-                     out0, nblk0, part1, n1, out1, nchunk);
+  const int G = red_groups(nchunk);
+  const int64_t cols = 4 * (kBlockThreads / G);
+  const int64_t nblk0 = (n0 + cols - 1) / cols;
+  const int64_t nblk1 = (n1 + cols - 1) / cols;
+  if (G == 32) {
+    hipLaunchKernelGGL(k_reduce_partials4x2<32>, dim3(unsigned(nblk0 + nblk1)), dim3(kBlockThreads), 0, stream, part0,
+                       n0, out0, nblk0, part1, n1, out1, nchunk);
+  } else {
+    hipLaunchKernelGGL(k_reduce_partials4x2<kRedGroups>, dim3(unsigned(nblk0 + nblk1)), dim3(kBlockThreads), 0,
+                       stream, part0, n0, out0, nblk0, part1, n1, out1, nchunk);
+  }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
 }
