@@ -68,14 +68,48 @@ def _conv_bias_arg(conv_bias, x):
     return conv_bias
 
 
+def _expect(name: str, t, shape, dtype) -> None:
+    """Raises unless t (if given) has exactly this shape and dtype: the C ABI receives
+    strides, not extents, so a tensor of the wrong size would be read or written out of
+    bounds instead of being refused."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}; got {list(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} is {t.dtype} but must be {dtype}")
+
+
+def _groups(D: int, H: int) -> int:
+    if H < 1 or D % H != 0:
+        raise ValueError(f"H = {H} must be a positive divisor of D = {D}")
+    return D // H
+
+
+def _check_act3(x: torch.Tensor) -> tuple:
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, T, D]; got shape {list(x.shape)}")
+    return tuple(x.shape)
+
+
+def _check_filter(w: torch.Tensor, x: torch.Tensor, H: int) -> int:
+    """w is per-token [B, T, D/H, W] or static [D/H, W], of x's dtype; returns W."""
+    B, T, D = x.shape
+    G = _groups(D, H)
+    W = w.shape[-1]
+    _expect("w", w, (G, W) if w.dim() == 2 else (B, T, G, W), x.dtype)
+    return W
+
+
 def dynconv_fwd(x: torch.Tensor, w: torch.Tensor, H: int = 1, out: torch.Tensor | None = None,
                 seq_idx: torch.Tensor | None = None, conv_bias: torch.Tensor | None = None) -> torch.Tensor:
     """y = x + causal depthwise conv of x with per-token (or static) filters w (+ conv_bias
     [D] on every token). With seq_idx (int32 [B, T] segment ids of packed sequences) no tap
     crosses into another segment."""
-    B, T, D = x.shape
-    W = w.shape[-1]
+    B, T, D = _check_act3(x)
+    W = _check_filter(w, x, H)
     conv_bias = _conv_bias_arg(conv_bias, x)
+    _expect("out", out, (B, T, D), x.dtype)
     y = torch.empty_like(x) if out is None else out
     dev = _require_device(x, w, y, seq_idx, conv_bias)
     lib = _lib.load()
@@ -101,9 +135,12 @@ def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True
     """(dx, dw) of <dy, dynconv_fwd(x, w, H, seq_idx=seq_idx)>; dw of a static filter is
     float32 [D/H, W]. With want_dconv_bias, (dx, dw, dconv_bias) where dconv_bias is the
     float32 [D] gradient of a convolution bias (the sum of dy over every token)."""
-    B, T, D = x.shape
-    W = w.shape[-1]
+    B, T, D = _check_act3(x)
+    W = _check_filter(w, x, H)
     is_static = w.dim() == 2
+    _expect("dy", dy, (B, T, D), x.dtype)
+    _expect("dx", dx, (B, T, D), x.dtype)
+    _expect("dw", dw, (D // H, W) if is_static else (B, T, D // H, W), torch.float32 if is_static else x.dtype)
     if need_dx and dx is None:
         dx = torch.empty_like(x)
     if need_dw and dw is None:
@@ -139,9 +176,12 @@ def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True
 
 
 def _check_lowrank_operands(x, z, U, bias, J: int):
-    """U is [R, J] with unit column stride (rows ldu = U.stride(0) apart), bias a contiguous
-    [J] vector or None, and every operand has the dtype of x."""
+    """z is [B, T, R] (or [B, R] for a decoding step, x [B, D]), U is [R, J] with unit
+    column stride (rows ldu = U.stride(0) apart), bias a contiguous [J] vector or None, and
+    every operand has the dtype of x."""
     R = z.shape[-1]
+    if z.dim() != x.dim() or tuple(z.shape[:-1]) != tuple(x.shape[:-1]):
+        raise ValueError(f"z must be {list(x.shape[:-1]) + ['R']}; got shape {list(z.shape)}")
     if U.dim() != 2 or tuple(U.shape) != (R, J) or (J > 1 and U.stride(1) != 1):
         raise ValueError(f"U must be [R, J] = [{R}, {J}] with unit column stride; got shape "
                          f"{tuple(U.shape)} strides {tuple(U.stride())}")
@@ -155,9 +195,10 @@ def _check_lowrank_operands(x, z, U, bias, J: int):
 def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None, seq_idx=None):
     """y = x + conv(x) with filters z U + bias generated on the GPU (never stored); with
     seq_idx (int32 [B, T]) no tap crosses into another segment."""
-    B, T, D = x.shape
+    B, T, D = _check_act3(x)
     R = z.shape[-1]
-    _check_lowrank_operands(x, z, U, bias, (D // H) * W)
+    _check_lowrank_operands(x, z, U, bias, _groups(D, H) * W)
+    _expect("out", out, (B, T, D), x.dtype)
     y = torch.empty_like(x) if out is None else out
     dev = _require_device(x, z, U, bias, y, seq_idx)
     lib = _lib.load()
@@ -177,20 +218,27 @@ def dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dtype) -> int:
 
 def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = True, workspace=None,
                         seq_idx=None):
-    """(dx, dz, dU, db) of <dy, dynconv_lowrank_fwd(...)>; dU and db are float32."""
-    B, T, D = x.shape
+    """(dx, dz, dU, db) of <dy, dynconv_lowrank_fwd(...)>; dU and db are float32. A caller's
+    workspace must be a contiguous tensor on x's device of at least
+    dynconv_lowrank_bwd_workspace_size(...) bytes (the library checks the size)."""
+    B, T, D = _check_act3(x)
     R = z.shape[-1]
-    J = (D // H) * W
+    J = _groups(D, H) * W
     _check_lowrank_operands(x, z, U, bias, J)
+    _expect("dy", dy, (B, T, D), x.dtype)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    dev = _require_device(x, z, U, bias, dy, seq_idx, workspace)
     dx = torch.empty_like(x)
     dz = torch.empty_like(z)
     dU = torch.empty((R, J), dtype=torch.float32, device=x.device)
     db = torch.empty((J,), dtype=torch.float32, device=x.device) if need_db else None
-    dev = _require_device(x, z, U, bias, dy, seq_idx)
     lib = _lib.load()
-    ws_bytes = dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, x.dtype)
     if workspace is None:
+        ws_bytes = dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, x.dtype)
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
     head = (_ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias))
     tail = (
         _ptr(dy), _lib.strides(dy.stride()), _ptr(dx), _lib.strides(dx.stride()), _ptr(dz), _lib.strides(dz.stride()),
@@ -220,7 +268,10 @@ def dynconv_cache_fill(x, W: int, cache=None, seq_idx=None):
     """Fills the cache with the last W-1 tokens of a prompt x [B,T,D] (zeros before t = 0).
     With seq_idx (int32 [B, T]) of a packed prompt, only the tokens of the last document
     (the segment of token T-1) are kept."""
-    B, T, D = x.shape
+    B, T, D = _check_act3(x)
+    if W < 1:
+        raise ValueError(f"W = {W} must be positive")
+    _expect("cache", cache, (B, W - 1, D), x.dtype)
     if cache is None:
         cache = new_cache(B, D, W, x.dtype, x.device)
     if cache is None:
@@ -240,8 +291,16 @@ def dynconv_cache_fill(x, W: int, cache=None, seq_idx=None):
 def dynconv_decode_step(x, w, cache, t: int, H: int = 1, out=None, conv_bias=None):
     """y [B,D] of token t from x [B,D], its filters w [B,D/H,W] (or a static [D/H,W]) and
     the cache of the previous W-1 inputs, which is updated in place (+ conv_bias [D])."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [B, D]; got shape {list(x.shape)}")
     B, D = x.shape
+    G = _groups(D, H)
     W = w.shape[-1]
+    _expect("w", w, (G, W) if w.dim() == 2 else (B, G, W), x.dtype)
+    _expect("cache", cache, (B, W - 1, D), x.dtype)
+    if cache is None and W > 1:
+        raise ValueError("a cache [B, W-1, D] is required for W > 1")
+    _expect("out", out, (B, D), x.dtype)
     ws = [0, w.stride(0), w.stride(1)] if w.dim() == 2 else list(w.stride())
     y = torch.empty_like(x) if out is None else out
     conv_bias = _conv_bias_arg(conv_bias, x)
@@ -257,9 +316,15 @@ def dynconv_decode_step(x, w, cache, t: int, H: int = 1, out=None, conv_bias=Non
 def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None, H: int = 1):
     """y [B,D] of token t with filters z [B,R] U + bias generated on the GPU (U: [R, (D/H)*W]);
     the cache is updated in place."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [B, D]; got shape {list(x.shape)}")
     B, D = x.shape
     R = z.shape[-1]
-    _check_lowrank_operands(x, z, U, bias, (D // H) * W)
+    _check_lowrank_operands(x, z, U, bias, _groups(D, H) * W)
+    _expect("cache", cache, (B, W - 1, D), x.dtype)
+    if cache is None and W > 1:
+        raise ValueError("a cache [B, W-1, D] is required for W > 1")
+    _expect("out", out, (B, D), x.dtype)
     y = torch.empty_like(x) if out is None else out
     dev = _require_device(x, z, U, bias, y, cache)
     cs = _lib.strides(cache.stride()) if cache is not None else None

@@ -295,3 +295,67 @@ def test_conv_bias_validation(lib):
     assert bx(dcb=DX) == INVALID  # aliasing dx
     assert bx(dcb=P(0xc0002)) == UNSUP
     assert bx(dx=None) == INVALID  # neither dx nor dw
+
+
+def test_bindings_reject_mismatched_shapes_and_dtypes():
+    """The bindings check every tensor's full shape and dtype against x and H before any
+    device work: the C ABI receives strides, not extents, so a mismatch would otherwise be
+    an out-of-bounds access. CPU tensors suffice, these checks come first."""
+    import torch
+
+    from dynamic_short_convolution_amd import (dynconv_bwd, dynconv_cache_fill, dynconv_decode_step, dynconv_fwd,
+                                               dynconv_lowrank_bwd, dynconv_lowrank_decode_step, dynconv_lowrank_fwd)
+
+    B, T, D, W, R = 2, 5, 32, 4, 16
+    bf = torch.bfloat16
+    x = torch.zeros((B, T, D), dtype=bf)
+    w1 = torch.zeros((B, T, D, W), dtype=bf)
+    with pytest.raises(ValueError, match="w must have shape"):
+        dynconv_fwd(x, torch.zeros((B, T, D // 16, W), dtype=bf), 1)  # head-wise filters with H = 1
+    with pytest.raises(ValueError, match="w must have shape"):
+        dynconv_fwd(x, w1, 4)  # per-channel filters with H = 4
+    with pytest.raises(ValueError, match="w must have shape"):
+        dynconv_fwd(x, torch.zeros((B, T - 1, D, W), dtype=bf), 1)  # fewer tokens
+    with pytest.raises(ValueError, match="w must have shape"):
+        dynconv_fwd(x, torch.zeros((D // 2, W), dtype=bf), 1)  # static filter of the wrong group count
+    with pytest.raises(TypeError, match="w is torch.float32"):
+        dynconv_fwd(x, w1.float(), 1)
+    with pytest.raises(ValueError, match="divisor"):
+        dynconv_fwd(x, w1, 3)
+    with pytest.raises(ValueError, match="out must have shape"):
+        dynconv_fwd(x, w1, 1, out=torch.zeros((B, T, D // 2), dtype=bf))
+    with pytest.raises(ValueError, match=r"x must be \[B, T, D\]"):
+        dynconv_fwd(x[0], w1[0], 1)
+    with pytest.raises(ValueError, match="dy must have shape"):
+        dynconv_bwd(x, w1, torch.zeros((B, T - 1, D), dtype=bf), 1)
+    with pytest.raises(TypeError, match="dy is torch.float16"):
+        dynconv_bwd(x, w1, torch.zeros((B, T, D), dtype=torch.float16), 1)
+    with pytest.raises(ValueError, match="dx must have shape"):
+        dynconv_bwd(x, w1, x, 1, dx=torch.zeros((B, T, D + 2), dtype=bf))
+    with pytest.raises(ValueError, match="dw must have shape"):
+        dynconv_bwd(x, w1, x, 1, dw=torch.zeros((B, T, D // 2, W), dtype=bf))
+    with pytest.raises(TypeError, match="dw is torch.bfloat16"):
+        dynconv_bwd(x, torch.zeros((D, W), dtype=bf), x, 1, dw=torch.zeros((D, W), dtype=bf))  # static dw is fp32
+    z = torch.zeros((B, T, R), dtype=bf)
+    U = torch.zeros((R, D * W), dtype=bf)
+    b = torch.zeros((D * W,), dtype=bf)
+    with pytest.raises(ValueError, match="z must be"):
+        dynconv_lowrank_fwd(x, torch.zeros((B, T - 1, R), dtype=bf), U, b, W)
+    with pytest.raises(ValueError, match="z must be"):
+        dynconv_lowrank_bwd(x, torch.zeros((B + 1, T, R), dtype=bf), U, b, x, W)
+    with pytest.raises(ValueError, match="dy must have shape"):
+        dynconv_lowrank_bwd(x, z, U, b, torch.zeros((B, T, D // 2), dtype=bf), W)
+    with pytest.raises(ValueError, match="out must have shape"):
+        dynconv_lowrank_fwd(x, z, U, b, W, out=torch.zeros((B, T - 1, D), dtype=bf))
+    with pytest.raises(ValueError, match="workspace must be contiguous"):
+        dynconv_lowrank_bwd(x, z, U, b, x, W, workspace=torch.zeros((64, 2), dtype=torch.uint8).t())
+    with pytest.raises(ValueError, match="cache must have shape"):
+        dynconv_cache_fill(x, W, cache=torch.zeros((B, W, D), dtype=bf))
+    with pytest.raises(ValueError, match="w must have shape"):
+        dynconv_decode_step(x[:, 0], torch.zeros((B, D // 2, W), dtype=bf), torch.zeros((B, W - 1, D), dtype=bf), 0)
+    with pytest.raises(ValueError, match="cache must have shape"):
+        dynconv_decode_step(x[:, 0], w1[:, 0], torch.zeros((B, W - 1, D // 2), dtype=bf), 0)
+    with pytest.raises(ValueError, match="cache .* is required"):
+        dynconv_decode_step(x[:, 0], w1[:, 0], None, 0)
+    with pytest.raises(ValueError, match="z must be"):
+        dynconv_lowrank_decode_step(x[:, 0], z, U, b, torch.zeros((B, W - 1, D), dtype=bf), 0, W)
