@@ -211,6 +211,8 @@ ROWS = (
     "headwise_h16_bwd",
     "static_w3_fwd",
     "static_w3_bwd",
+    "static_w4_fwd",
+    "static_w4_bwd",
     "qkv_gqa_fused_fwd",
     "qkv_gqa_fused_bwd",
     "lowrank_r64_fwd",
@@ -305,7 +307,7 @@ def make_row(name, device):
         B, T, D, W, H = 4, 8192, 3072, 4, 1
     else:
         B, T, D = 8, 4096, 2048
-        W = 3 if name.startswith("static") else 8 if name.startswith("perchannel_w8") else 4
+        W = int(name.split("_")[1][1:]) if name.startswith("static") else 8 if name.startswith("perchannel_w8") else 4
         H = {"perchannel_h1": 1, "headwise_h4": 4, "headwise_h16": 16}.get(name.rsplit("_", 1)[0], 1)
     static = name.startswith("static")
     x = gen((B, T, D), 1.0, 2, "x", device)
@@ -368,6 +370,16 @@ def run_rows(args, device):
         < out["perchannel_h1_bwd"]["median_us"],
         "lowrank_fwd_lt_h1_fwd": out["lowrank_r64_fwd"]["median_us"] < out["perchannel_h1_fwd"]["median_us"],
         "lowrank_bwd_lt_h1_bwd": out["lowrank_r64_bwd"]["median_us"] < out["perchannel_h1_bwd"]["median_us"],
+        # the pages: at H = 16 the dynamic kernel beats their optimised static convolution.
+        # Here both stream at the same fraction of HBM, and H = 16 moves x, y and w/16
+        # (2.25 elements per token-channel) against the static form's 2, so it is expected
+        # to be about 12 % slower; reported, not assumed.
+        "h16_fwd_lt_static_w4_fwd": out["headwise_h16_fwd"]["median_us"] < out["static_w4_fwd"]["median_us"],
+        "h16_bwd_lt_static_w4_bwd": out["headwise_h16_bwd"]["median_us"] < out["static_w4_bwd"]["median_us"],
+        "h16_fwd_over_static_w4_fwd": round(out["headwise_h16_fwd"]["median_us"] / out["static_w4_fwd"]["median_us"],
+                                            3),
+        "h16_bwd_over_static_w4_bwd": round(out["headwise_h16_bwd"]["median_us"] / out["static_w4_bwd"]["median_us"],
+                                            3),
     }
     return out
 
@@ -397,14 +409,61 @@ def run_only(args, device):
 # ----------------------------------------------------------------------------------
 
 
+def _bf16_bits_to_f64(a):
+    """float64 values of bfloat16 bit patterns (uint16), exactly (numpy only)."""
+    import numpy as np
+
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+_POOL_INPUTS = {}  # the workload's bf16 bits, inherited by forked workers
+
+
+def _oracle_slice(task):
+    """One pool task: oracle fwd + bwd of sequence b, channels c0 .. c1 - 1 (per-channel
+    filters, so channel slices are independent). Returns its oracle seconds."""
+    from oracle import conv_bwd, conv_fwd
+
+    b, c0, c1 = task
+    x = _bf16_bits_to_f64(_POOL_INPUTS["x"][b:b + 1, :, c0:c1])
+    w = _bf16_bits_to_f64(_POOL_INPUTS["w"][b:b + 1, :, c0:c1])
+    dy = _bf16_bits_to_f64(_POOL_INPUTS["dy"][b:b + 1, :, c0:c1])
+    t0 = time.perf_counter()
+    conv_fwd(x, w, 1)
+    conv_bwd(x, w, dy, 1)
+    return time.perf_counter() - t0
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_cpu_baseline(min_seconds=10.0, max_seconds=30.0):
-    """The oracle, as it is, fwd + bwd one sequence at a time over the headline workload's
-    sequences (cycling 0..B-1) until at least `min_seconds` of oracle time have run."""
+    """The oracle, as it is, fwd + bwd on the headline workload, in two settings:
+    1 core: one sequence at a time (cycling 0..B-1) in this process until at least
+    `min_seconds` of oracle time have run;
+    P cores: a pool of P forked workers (P = the CPUs this process may use, at most 16)
+    over (sequence, 512-channel slice) tasks, whole passes over the workload until at least
+    `min_seconds` of wall time. Must run before the process touches the GPU (the workers
+    are forked)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
     import synth
     from oracle import conv_bwd, conv_fwd
 
     wl = synth.Workload("perchannel_h1", seed=5, **HEADLINE)
     xs, ws, dys = wl.x(), wl.w(), wl.dy()
+    per_seq = stream_bytes(1, HEADLINE["T"], HEADLINE["D"], HEADLINE["W"], 1)
+    # 1 core
     sec = 0.0
     passes = 0
     while sec < min_seconds and passes < 16 * wl.B:
@@ -419,17 +478,48 @@ def run_cpu_baseline(min_seconds=10.0, max_seconds=30.0):
         passes += 1
         if sec > max_seconds:
             break
-    nbytes = passes * stream_bytes(1, HEADLINE["T"], HEADLINE["D"], HEADLINE["W"], 1)
+    one = dict(value=round(passes * per_seq / sec / 1e9, 3), unit="GB/s", cores=1, seconds=round(sec, 2),
+               sample=f"{passes} single-sequence fwd+bwd passes (sequences cycled 0..{wl.B - 1}), one process")
+    # P cores
+    P = max(1, min(16, len(os.sched_getaffinity(0))))
+    _POOL_INPUTS["x"] = xs.view(torch_int16()).numpy().view(np.uint16)
+    _POOL_INPUTS["w"] = ws.view(torch_int16()).numpy().view(np.uint16)
+    _POOL_INPUTS["dy"] = dys.view(torch_int16()).numpy().view(np.uint16)
+    Dc = 512
+    tasks = [(b, c0, min(wl.D, c0 + Dc)) for b in range(wl.B) for c0 in range(0, wl.D, Dc)]
+    with mp.get_context("fork").Pool(P) as pool:
+        pool.map(_oracle_slice, tasks[:P])  # workers started and warm
+        wall = 0.0
+        npass = 0
+        while wall < min_seconds and npass < 64:
+            t0 = time.perf_counter()
+            pool.map(_oracle_slice, tasks, chunksize=1)
+            wall += time.perf_counter() - t0
+            npass += 1
+            if wall > max_seconds:
+                break
+    _POOL_INPUTS.clear()
+    many = dict(value=round(npass * wl.B * per_seq / wall / 1e9, 3), unit="GB/s", cores=P, seconds=round(wall, 2),
+                sample=f"{npass} whole passes over the B{wl.B} T{wl.T} D{wl.D} W{wl.W} H1 workload, "
+                       f"{len(tasks)} (sequence, {Dc}-channel) tasks each, on a pool of {P} forked processes")
     return dict(
-        value=round(nbytes / sec / 1e9, 3),
+        value=many["value"],
         unit="GB/s",
-        cores=1,
+        cores=P,
         kind="oracle",
-        sample=f"{passes} single-sequence fwd+bwd passes (sequences cycled 0..{wl.B - 1}) of the B8 T4096 D2048 "
-               f"W4 H1 workload, float64 NumPy in one process: {sec:.1f} s for {nbytes} bf16-equivalent "
-               f"algorithmic bytes",
-        seconds=round(sec, 2),
+        sample=f"float64 NumPy oracle, fwd+bwd, bf16-equivalent algorithmic bytes per second: {many['sample']} "
+               f"({many['seconds']} s wall). The 1-core setting is under one_core.",
+        seconds=many["seconds"],
+        one_core=one,
+        cpu_model=cpu_model(),
+        cpus_available=len(os.sched_getaffinity(0)),
     )
+
+
+def torch_int16():
+    import torch
+
+    return torch.int16
 
 
 def traffic_from_profiles(kernel_key):
@@ -451,6 +541,11 @@ def main():
         print(f"bench.py measures one GPU: every box in this setup has one MI355X, and the path has no "
               f"multi-GPU component (got --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    cpu = None
+    if not args.only and not args.no_cpu_baseline:
+        # before any GPU call: its P-core setting forks worker processes
+        log("cpu baseline: float64 oracle on a sample (1 core, then P cores)")
+        cpu = run_cpu_baseline()
     import torch
 
     if not torch.cuda.is_available():
@@ -506,11 +601,7 @@ def main():
     }
     if not args.no_rows:
         result["rows"] = run_rows(args, device)
-    if not args.no_cpu_baseline:
-        log("cpu baseline: float64 oracle on a sample")
-        result["cpu_baseline"] = run_cpu_baseline()
-    else:
-        result["cpu_baseline"] = None
+    result["cpu_baseline"] = cpu
     print(json.dumps(result))
 
 
