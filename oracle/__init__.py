@@ -7,7 +7,10 @@ from .dynconv_oracle import (  # noqa: F401
     conv_bias_grad,
     conv_bwd,
     conv_fwd,
+    gemm_conv_fwd,
+    gemm_lowrank_fwd,
     lowrank_bwd,
     lowrank_filters,
     lowrank_fwd,
+    projection,
 )

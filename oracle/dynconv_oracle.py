@@ -39,6 +39,14 @@ Readings where the page leaves a step open (each also listed in the design notes
   seq_idx (B, T) of integers, and tap k of token t is present only when token t - k
   carries the same id as token t. Without seq_idx every row is one document.
 
+* the convolution in the epilogue of the producing projection (the closing analysis of
+  the end-to-end throughput section: fusing the dynamic convolution into the matmul
+  epilogue cuts memory traffic; the "Parameterization" section places the convolution
+  on the outputs of the QKV projection): the projection output X = A W_p^T, with A the
+  (B, T, K) activations and W_p the (N, K) weight of a linear layer, followed by eq. 2 +
+  eq. 3 on X. The fused kernel never stores X; the oracle forms it with a plain matmul
+  and calls the convolution above.
+
 Everything is float64; bfloat16 and float32 inputs are exact in float64. Arrays are
 processed one sequence (one b) at a time; no blocking, fusion or reordering beyond
 the sums written out below.
@@ -189,3 +197,23 @@ def lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, seq_idx=None):
     dU = np.matmul(zf.T, g)
     db = g.sum(axis=0)
     return dx, dz, dU, db
+
+
+def projection(A, Wp) -> np.ndarray:
+    """X = A W_p^T: A (B, T, K) activations, W_p (N, K) a linear layer's weight (out x in).
+    Returns (B, T, N) float64."""
+    A = _f64(A)
+    Wp = _f64(Wp)
+    B, T, K = A.shape
+    return np.matmul(A.reshape(B * T, K), Wp.T).reshape(B, T, Wp.shape[0])
+
+
+def gemm_conv_fwd(A, Wp, w, H: int = 1) -> np.ndarray:
+    """The convolution applied to the projection's output: y = X + conv(X) with
+    X = A W_p^T and per-token (B, T, N/H, W) or static (N/H, W) filters w."""
+    return conv_fwd(projection(A, Wp), w, H)
+
+
+def gemm_lowrank_fwd(A, Wp, z, U, bias, W: int, H: int = 1) -> np.ndarray:
+    """The same with low-rank filters z U + bias (U: (R, (N/H)*W), column j = g*W + k)."""
+    return lowrank_fwd(projection(A, Wp), z, U, bias, W, H)

@@ -740,3 +740,100 @@ def _mut_bias_grad_mean(dy):
 def test_pins_reject_conv_bias_mutants():
     assert not pin_conv_bias(_mut_bias_full_window_only, conv_bias_grad, 92)
     assert not pin_conv_bias(conv_fwd, _mut_bias_grad_mean, 93)
+
+
+# ----------------------------------------------------------------------------------
+# The convolution on a projection's output (the epilogue fusion of the end-to-end
+# throughput section): X = A W_p^T, then eq. 2 + eq. 3 on X.
+# ----------------------------------------------------------------------------------
+from oracle import gemm_conv_fwd, gemm_lowrank_fwd, projection  # noqa: E402
+
+
+def _brute_gemm_conv(A, Wp, w, H):
+    """Pure-Python loops: X[b,t,n] = sum_k A[b,t,k] Wp[n,k]; y = X + sum_j w[b,t,n//H,j] X[b,t-j,n]."""
+    B, T, K = A.shape
+    N = Wp.shape[0]
+    W = w.shape[-1]
+    X = [[[sum(float(A[b, t, k]) * float(Wp[n, k]) for k in range(K)) for n in range(N)] for t in range(T)]
+         for b in range(B)]
+    y = np.zeros((B, T, N))
+    for b in range(B):
+        for t in range(T):
+            for n in range(N):
+                acc = X[b][t][n]
+                for j in range(W):
+                    if t - j >= 0:
+                        f = w[n // H, j] if w.ndim == 2 else w[b, t, n // H, j]
+                        acc += float(f) * X[b][t - j][n]
+                y[b, t, n] = acc
+    return y
+
+
+def pin_gemm_conv(fn, seed) -> bool:
+    """Brute force on tiny shapes, identity and permutation projections, linearity in A."""
+    rng = _rng(seed, 90)
+    ok = True
+    for (B, T, K, N, W, H) in ((1, 6, 3, 4, 4, 1), (2, 5, 5, 4, 3, 2), (1, 3, 2, 2, 5, 1)):
+        A = rng.standard_normal((B, T, K))
+        Wp = rng.standard_normal((N, K))
+        w = rng.standard_normal((B, T, N // H, W))
+        ok &= np.allclose(fn(A, Wp, w, H), _brute_gemm_conv(A, Wp, w, H), rtol=1e-13, atol=1e-13)
+    B, T, N, W = 2, 9, 6, 4
+    A = rng.standard_normal((B, T, N))
+    w = rng.standard_normal((B, T, N, W))
+    ok &= np.array_equal(fn(A, np.eye(N), w, 1), conv_fwd(A, w, 1))  # identity projection
+    perm = np.array([2, 0, 5, 1, 3, 4])  # not an involution: a transposed W_p picks other columns
+    P = np.zeros((N, N))
+    P[np.arange(N), perm] = 1.0  # output column n reads input column perm[n]
+    ok &= np.array_equal(fn(A, P, w, 1), conv_fwd(A[..., perm], w, 1))
+    K = 7
+    A1, A2 = rng.standard_normal((B, T, K)), rng.standard_normal((B, T, K))
+    Wp = rng.standard_normal((N, K))
+    ok &= np.allclose(fn(A1 + A2, Wp, w, 1), fn(A1, Wp, w, 1) + fn(A2, Wp, w, 1), rtol=1e-12, atol=1e-12)
+    return bool(ok)
+
+
+def test_gemm_conv_pins():
+    assert pin_gemm_conv(gemm_conv_fwd, 1)
+
+
+def test_gemm_conv_static_filter_and_projection_shape():
+    rng = _rng(3, 91)
+    A = rng.standard_normal((2, 7, 5))
+    Wp = rng.standard_normal((8, 5))
+    w = rng.standard_normal((4, 3))
+    assert projection(A, Wp).shape == (2, 7, 8)
+    assert np.allclose(gemm_conv_fwd(A, Wp, w, 2), _brute_gemm_conv(A, Wp, w, 2), rtol=1e-13, atol=1e-13)
+
+
+def test_gemm_lowrank_equals_materialised_filters():
+    """Low-rank filters in the epilogue == the materialised z U + b on the same projection;
+    with the identity projection == the low-rank convolution of A itself."""
+    rng = _rng(4, 92)
+    B, T, K, N, W, R, H = 2, 11, 6, 8, 4, 3, 2
+    A = rng.standard_normal((B, T, K))
+    Wp = rng.standard_normal((N, K))
+    z = rng.standard_normal((B, T, R))
+    U = rng.standard_normal((R, (N // H) * W))
+    bias = rng.standard_normal(((N // H) * W,))
+    wf = np.einsum("btr,rj->btj", z, U) + bias
+    ref = _brute_gemm_conv(A, Wp, wf.reshape(B, T, N // H, W), H)
+    assert np.allclose(gemm_lowrank_fwd(A, Wp, z, U, bias, W, H), ref, rtol=1e-12, atol=1e-12)
+    A2 = rng.standard_normal((B, T, N))
+    assert np.array_equal(gemm_lowrank_fwd(A2, np.eye(N), z, U, bias, W, H), lowrank_fwd(A2, z, U, bias, W, H))
+
+
+def _mut_gemm_transposed(A, Wp, w, H=1):
+    return conv_fwd(np.matmul(A, Wp) if Wp.shape[0] == Wp.shape[1] else projection(A, Wp), w, H)
+
+
+def _mut_gemm_conv_first(A, Wp, w, H=1):
+    # the convolution on A, then the projection: only equal when W_p commutes with it
+    if A.shape[-1] != Wp.shape[0]:
+        return gemm_conv_fwd(A, Wp, w, H) + 1.0
+    return projection(conv_fwd(A, w, H), Wp)
+
+
+def test_pins_reject_gemm_mutants():
+    assert not pin_gemm_conv(_mut_gemm_transposed, 1)
+    assert not pin_gemm_conv(_mut_gemm_conv_first, 1)
