@@ -43,7 +43,11 @@ EXPORTS = (
     "dynconv_bwd_ex",
     "dynconv_bwd_ex_workspace_size",
     "dynconv_decode_step_ex",
+    "dynconv_bwd_ex_noalloc",
 )
+
+# Bytes of the per-GPU scratch array of dynconv_bwd_ex_noalloc (DYNCONV_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _vp = ctypes.c_void_p
@@ -103,6 +107,9 @@ _SIGNATURES["dynconv_bwd_ex_workspace_size"] = ([_i64, _i64, _i64, _i32, _i32, c
                                                  ctypes.c_int], _sz)
 _SIGNATURES["dynconv_decode_step_ex"] = (
     _SIGNATURES["dynconv_decode_step"][0][:4] + [_vp] + _SIGNATURES["dynconv_decode_step"][0][4:], ctypes.c_int)
+# the workspace pointer and size of dynconv_bwd_ex dropped
+_SIGNATURES["dynconv_bwd_ex_noalloc"] = (
+    _SIGNATURES["dynconv_bwd_ex"][0][:-3] + [_vp], ctypes.c_int)
 _SIGNATURES["dynconv_cache_fill_varlen"] = (
     _SIGNATURES["dynconv_cache_fill"][0][:2] + [_vp, _i64p] + _SIGNATURES["dynconv_cache_fill"][0][2:], ctypes.c_int)
 

@@ -2,6 +2,8 @@
 // kernel launchers. See include/dynconv.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "dynconv_decode_internal.hpp"
 #include "dynconv_internal.hpp"
 #include "dynconv_lowrank_internal.hpp"
@@ -258,12 +260,53 @@ size_t dynconv_bwd_ex_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W,
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------------
+// Scratch memory of the allocation-free backward (dynconv_bwd_ex_noalloc): a file-scope
+// device array, one copy per GPU, resolved to a device address once per device with
+// hipGetSymbolAddress. Host code never passes the array's own name to a kernel or a copy
+// (in host code that name is a host-side stand-in, not a device address); it uses the
+// resolved pointer.
+// ---------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = DYNCONV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array (resolved on the first call on
+// that device; the call must not be inside a graph capture then).
+dynconv_status current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return record_hip_error(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return DYNCONV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return record_hip_error(e);
+    if (ptr == nullptr) return record_hip_error(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DYNCONV_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// use_scratch: the partial sums go to the current device's scratch array instead of a
+// caller's workspace (workspace / workspace_bytes are then ignored); a call that needs
+// more than kScratchBytes returns DYNCONV_ERR_WORKSPACE.
 dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const int64_t* ws, const int32_t* seg,
                         const int64_t* ss, const void* dy, const int64_t* dys, void* dx, const int64_t* dxs, void* dw,
                         const int64_t* dws, float* dcb, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
-                        dynconv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                        dynconv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        bool use_scratch = false) {
   dynconv_status st = check_common(B, T, D, W, H, dtype);
   if (st != DYNCONV_OK) return st;
   if (dx == nullptr && dw == nullptr) return DYNCONV_ERR_INVALID_ARG;
@@ -308,6 +351,11 @@ dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const i
   const bool static_dw = fi.is_static && dw != nullptr;
   if (static_dw || dcb != nullptr) {
     const size_t need = bwd_partial_floats(plan, B, D, W, H, static_dw, dcb != nullptr) * sizeof(float);
+    if (use_scratch) {
+      if (need > kScratchBytes) return DYNCONV_ERR_WORKSPACE;
+      if ((st = current_scratch(&workspace)) != DYNCONV_OK) return st;
+      workspace_bytes = kScratchBytes;
+    }
     if (workspace == nullptr || workspace_bytes < need) return DYNCONV_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return DYNCONV_ERR_UNSUPPORTED;
     float* wsf = static_cast<float*>(workspace);
@@ -391,6 +439,19 @@ dynconv_status dynconv_bwd_ex(const void* x, const int64_t* xs, const void* w, c
   }
   return bwd_impl(x, xs, w, ws, seq_idx, ss, dy, dys, dx, dxs, dw, dws, dconv_bias, B, T, D, W, H, dtype, workspace,
                   workspace_bytes, stream);
+}
+
+dynconv_status dynconv_bwd_ex_noalloc(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                      const int32_t* seq_idx, const int64_t* ss, const void* dy, const int64_t* dys,
+                                      void* dx, const int64_t* dxs, void* dw, const int64_t* dws, float* dconv_bias,
+                                      int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype,
+                                      void* stream) {
+  if (seq_idx != nullptr) {
+    const dynconv_status st = check_seg(seq_idx, ss);
+    if (st != DYNCONV_OK) return st;
+  }
+  return bwd_impl(x, xs, w, ws, seq_idx, ss, dy, dys, dx, dxs, dw, dws, dconv_bias, B, T, D, W, H, dtype, nullptr, 0,
+                  stream, true);
 }
 
 }  // extern "C"

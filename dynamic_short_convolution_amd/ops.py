@@ -175,6 +175,30 @@ def dynconv_bwd(x, w, dy, H: int = 1, need_dx: bool = True, need_dw: bool = True
     return (dx if need_dx else None), (dw if need_dw else None)
 
 
+def dynconv_bwd_ex_noalloc(x, w, dy, H: int = 1, dx=None, dw=None, dconv_bias=None, seq_idx=None):
+    """The allocation-free backward: (dx, dw, dconv_bias) as dynconv_bwd(..., want_dconv_bias=
+    dconv_bias is not None) computes them, with the partial sums in the library's per-GPU
+    scratch array instead of a workspace. The caller passes every output it wants (dx
+    [B,T,D], dw per-token [B,T,D/H,W] or float32 [D/H,W] for a static w, dconv_bias float32
+    [D]); this binding allocates nothing either. Calls that overlap on one GPU race."""
+    B, T, D = _check_act3(x)
+    W = _check_filter(w, x, H)
+    is_static = w.dim() == 2
+    _expect("dy", dy, (B, T, D), x.dtype)
+    _expect("dx", dx, (B, T, D), x.dtype)
+    _expect("dw", dw, (D // H, W) if is_static else (B, T, D // H, W), torch.float32 if is_static else x.dtype)
+    _expect("dconv_bias", dconv_bias, (D,), torch.float32)
+    dev = _require_device(x, w, dy, dx, dw, dconv_bias, seq_idx)
+    seg = _seg_args(seq_idx, B, T) if seq_idx is not None else (None, None)
+    st = _lib.load().dynconv_bwd_ex_noalloc(
+        _ptr(x), _lib.strides(x.stride()), _ptr(w), _lib.strides(filter_strides(w)), *seg,
+        _ptr(dy), _lib.strides(dy.stride()), _ptr(dx), _lib.strides(dx.stride()) if dx is not None else None,
+        _ptr(dw), _lib.strides(dw.stride()) if (dw is not None and not is_static) else None, _ptr(dconv_bias),
+        B, T, D, W, H, _dtype_code(x), _stream(dev))
+    _lib.check("dynconv_bwd_ex_noalloc", st)
+    return dx, dw, dconv_bias
+
+
 def _check_lowrank_operands(x, z, U, bias, J: int):
     """z is [B, T, R] (or [B, R] for a decoding step, x [B, D]), U is [R, J] with unit
     column stride (rows ldu = U.stride(0) apart), bias a contiguous [J] vector or None, and

@@ -18,7 +18,8 @@
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers. The caller owns every buffer, including
  *   the workspace; the library never allocates or frees device memory, never
- *   synchronises, and keeps no mutable global state (thread-safe).
+ *   synchronises, and keeps no mutable global state (thread-safe) apart from the
+ *   per-device address of dynconv_bwd_ex_noalloc's scratch array (set once, under a lock).
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *   returns without waiting.
  * - Strides are in ELEMENTS, int64, in PyTorch .stride() order. Activation-shaped tensors
@@ -248,6 +249,33 @@ dynconv_status dynconv_decode_step_ex(const void* x, const int64_t* xs, const vo
                                       const void* conv_bias, void* cache, const int64_t* cs, void* y,
                                       const int64_t* ys, int64_t t, int64_t B, int64_t D, int32_t W, int32_t H,
                                       dynconv_dtype dtype, void* stream);
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The same
+ * operation and arguments as dynconv_bwd_ex, without a workspace: the float32 partial
+ * sums of a static filter's dw and of dconv_bias go to a scratch array that the library
+ * holds in device memory, DYNCONV_NOALLOC_SCRATCH_BYTES per GPU, kept from the library's
+ * load until the process ends. Calls that need no partial sums (per-token filters without
+ * dconv_bias) do not touch it.
+ *   - A call whose partial sums need more than DYNCONV_NOALLOC_SCRATCH_BYTES (the bytes
+ *     dynconv_bwd_ex_workspace_size reports) returns DYNCONV_ERR_WORKSPACE.
+ *   - The scratch array of the CURRENT device is used: `stream` must belong to it. Its
+ *     device address is resolved on the first call on each device (hipGetSymbolAddress),
+ *     so that first call must not be made during a graph capture.
+ *   - Every call on a GPU shares that GPU's array: calls that overlap in time on one GPU
+ *     (on different streams, or from different threads without ordering) race and give
+ *     wrong sums. Calls ordered on one stream are safe; each call overwrites every
+ *     partial it later reads, so nothing has to start at zero.
+ *   - No hipMalloc, hipFree or allocating library routine is called.
+ */
+#define DYNCONV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+dynconv_status dynconv_bwd_ex_noalloc(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
+                                      const int32_t* seq_idx, const int64_t* ss, const void* dy, const int64_t* dys,
+                                      void* dx, const int64_t* dxs, void* dw, const int64_t* dws, float* dconv_bias,
+                                      int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, dynconv_dtype dtype,
+                                      void* stream);
 
 /*
  * Cache fill after a packed prompt: decoding continues the document of token T-1, so the

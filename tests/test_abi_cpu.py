@@ -359,3 +359,34 @@ def test_bindings_reject_mismatched_shapes_and_dtypes():
         dynconv_decode_step(x[:, 0], w1[:, 0], None, 0)
     with pytest.raises(ValueError, match="z must be"):
         dynconv_lowrank_decode_step(x[:, 0], z, U, b, torch.zeros((B, W - 1, D), dtype=bf), 0, W)
+
+
+def test_noalloc_validation(lib):
+    """dynconv_bwd_ex_noalloc validates like dynconv_bwd_ex, and refuses a call whose
+    partial sums exceed its scratch array (DYNCONV_ERR_WORKSPACE) before any HIP call."""
+    DCB = P(0xc0000)
+
+    def nx(B=2, T=4, D=200, W=4, ws=(800 * 4, 200 * 4, 4, 1), dw=None, dcb=DCB, dx=DX, seg=None, ss=None):
+        return lib.dynconv_bwd_ex_noalloc(X, S(T * D, D, 1), W_, S(*ws), seg, S(*ss) if ss else None, DY,
+                                          S(T * D, D, 1), dx, S(T * D, D, 1), dw, None, dcb, B, T, D, W, 1, BF16, None)
+
+    assert nx(dx=None, dcb=None) == INVALID  # neither dx nor dw
+    assert nx(dcb=DX) == INVALID
+    assert nx(dcb=P(0xc0002)) == UNSUP
+    assert nx(seg=P(0x90002), ss=(4, 1)) == UNSUP  # ids are 4-byte aligned
+    assert nx(B=0) == OK
+    assert nx(W=9) == UNSUP
+    B, T, D, W = 512, 64, 8192, 4
+    need = lib.dynconv_bwd_ex_workspace_size(B, T, D, W, 1, 1, 1, BF16)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert nx(B=B, T=T, D=D, W=W, ws=(0, 0, W, 1), dw=P(0xd0000)) == WORKSPACE
+    B = 1024
+    need = lib.dynconv_bwd_ex_workspace_size(B, T, D, W, 1, 0, 1, BF16)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert nx(B=B, T=T, D=D, W=W, ws=(T * D * W, D * W, W, 1)) == WORKSPACE
+
+
+def test_noalloc_scratch_constant_matches_header():
+    with open(os.path.join(ROOT, "include", "dynconv.h")) as f:
+        m = re.search(r"#define DYNCONV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
