@@ -231,7 +231,13 @@ ROWS = (
     "packed_lowrank_r64_bwd",
     "lowrank_r64_f16_fwd",
     "lowrank_r64_f16_bwd",
+    "gemm_conv_qkv_fwd",
+    "gemm_lowrank_qkv_fwd",
+    "reference_unfused_gemm_conv_qkv_fwd",
+    "reference_unfused_gemm_lowrank_qkv_fwd",
 )
+# the projection feeding the Q|K|V convolution: B4 T8192, K = 2048 -> N = 2048 + 512 + 512
+GEMM_QKV = dict(B=4, T=8192, K=2048, N=3072, W=4, R=64)
 PACKED_MEAN_DOC = 512.0  # mean document length of the packed rows (tokens)
 
 
@@ -261,6 +267,48 @@ def make_row(name, device):
                                                dynconv_lowrank_bwd, dynconv_lowrank_bwd_workspace_size,
                                                dynconv_lowrank_fwd)
 
+    if name.startswith("gemm") or name.startswith("reference_unfused"):
+        # the convolution in the projection's epilogue (X never stored) and, as the reference
+        # it replaces, the library matmul writing X followed by the convolution kernel reading it
+        from dynamic_short_convolution_amd import dynconv_gemm_fwd, dynconv_gemm_lowrank_fwd
+
+        g = GEMM_QKV
+        B, T, K, N, W, R = g["B"], g["T"], g["K"], g["N"], g["W"], g["R"]
+        A = gen((B, T, K), 1.0, 7, "A", device)
+        Wp = gen((N, K), (1.0 / K) ** 0.5, 7, "Wp", device)
+        y = torch.empty((B, T, N), dtype=torch.bfloat16, device=device)
+        io = B * T * K * 2 + N * K * 2 + B * T * N * 2  # A, Wp read, y written
+        flops = 2 * B * T * N * K
+        low = "lowrank" in name
+        if low:
+            z = gen((B, T, R), 1.0, 7, "z", device)
+            U = gen((R, N * W), 0.1 / R**0.5, 7, "U", device)
+            b = gen((N * W,), 0.1**0.5, 7, "b", device)
+            io += B * T * R * 2 + R * N * W * 2 + N * W * 2
+            flops += 2 * B * T * R * N * W
+            desc = f"B{B} T{T} K{K} -> N{N} (Q|K|V) W{W} R{R} bf16"
+        else:
+            w = gen((B, T, N, W), (1.0 / W) ** 0.5, 7, "w", device)
+            io += B * T * N * W * 2
+            desc = f"B{B} T{T} K{K} -> N{N} (Q|K|V) W{W} H1 bf16"
+        if name.startswith("gemm"):
+            if low:
+                return (lambda: dynconv_gemm_lowrank_fwd(A, Wp, z, U, b, W, out=y)), io, flops, \
+                    desc + ", projection + low-rank convolution in one kernel"
+            return (lambda: dynconv_gemm_fwd(A, Wp, w, 1, out=y)), io, flops, \
+                desc + ", projection + convolution in one kernel"
+        X = torch.empty((B, T, N), dtype=torch.bfloat16, device=device)
+        WpT = Wp.t().contiguous()  # [K, N] row-major: a plain 2-D product, no transposed view
+        A2, X2 = A.view(B * T, K), X.view(B * T, N)
+
+        def unfused():
+            torch.mm(A2, WpT, out=X2)
+            if low:
+                dynconv_lowrank_fwd(X, z, U, b, W, out=y)
+            else:
+                dynconv_fwd(X, w, 1, out=y)
+
+        return unfused, io + 2 * B * T * N * 2, flops, desc + ", library matmul writing X, then the convolution"
     if name.startswith("decode"):
         # one decoding step of 64 sequences at D = 2048, W = 4: x, filters (or z, U, b), the
         # W-1 cached inputs read, y and one cache slot written
@@ -374,6 +422,10 @@ def run_rows(args, device):
         # Here both stream at the same fraction of HBM, and H = 16 moves x, y and w/16
         # (2.25 elements per token-channel) against the static form's 2, so it is expected
         # to be about 12 % slower; reported, not assumed.
+        "gemm_lowrank_fused_over_unfused": round(out["gemm_lowrank_qkv_fwd"]["median_us"]
+                                                 / out["reference_unfused_gemm_lowrank_qkv_fwd"]["median_us"], 3),
+        "gemm_conv_fused_over_unfused": round(out["gemm_conv_qkv_fwd"]["median_us"]
+                                              / out["reference_unfused_gemm_conv_qkv_fwd"]["median_us"], 3),
         "h16_fwd_lt_static_w4_fwd": out["headwise_h16_fwd"]["median_us"] < out["static_w4_fwd"]["median_us"],
         "h16_bwd_lt_static_w4_bwd": out["headwise_h16_bwd"]["median_us"] < out["static_w4_bwd"]["median_us"],
         "h16_fwd_over_static_w4_fwd": round(out["headwise_h16_fwd"]["median_us"] / out["static_w4_fwd"]["median_us"],

@@ -44,6 +44,8 @@ EXPORTS = (
     "dynconv_bwd_ex_workspace_size",
     "dynconv_decode_step_ex",
     "dynconv_bwd_ex_noalloc",
+    "dynconv_gemm_fwd",
+    "dynconv_gemm_lowrank_fwd",
 )
 
 # Bytes of the per-GPU scratch array of dynconv_bwd_ex_noalloc (DYNCONV_NOALLOC_SCRATCH_BYTES).
@@ -107,6 +109,13 @@ _SIGNATURES["dynconv_bwd_ex_workspace_size"] = ([_i64, _i64, _i64, _i32, _i32, c
                                                  ctypes.c_int], _sz)
 _SIGNATURES["dynconv_decode_step_ex"] = (
     _SIGNATURES["dynconv_decode_step"][0][:4] + [_vp] + _SIGNATURES["dynconv_decode_step"][0][4:], ctypes.c_int)
+_SIGNATURES["dynconv_gemm_fwd"] = (
+    [_vp, _i64p, _vp, _i64, _vp, _i64p, _vp, _i64p, _i64, _i64, _i64, _i64, _i32, _i32, ctypes.c_int, _vp],
+    ctypes.c_int)
+_SIGNATURES["dynconv_gemm_lowrank_fwd"] = (
+    [_vp, _i64p, _vp, _i64, _vp, _i64p, _vp, _i64, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+     ctypes.c_int, _vp],
+    ctypes.c_int)
 # the workspace pointer and size of dynconv_bwd_ex dropped
 _SIGNATURES["dynconv_bwd_ex_noalloc"] = (
     _SIGNATURES["dynconv_bwd_ex"][0][:-3] + [_vp], ctypes.c_int)

@@ -27,6 +27,7 @@ SOURCES = [
     "dynconv_lowrank_f16.hip",
     "dynconv_lowrank_fast.hip",
     "dynconv_decode.hip",
+    "dynconv_gemm.hip",
 ]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated from ordinary float code.

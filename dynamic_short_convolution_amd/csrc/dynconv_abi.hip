@@ -5,6 +5,7 @@
 #include <mutex>
 
 #include "dynconv_decode_internal.hpp"
+#include "dynconv_gemm_internal.hpp"
 #include "dynconv_internal.hpp"
 #include "dynconv_lowrank_internal.hpp"
 
@@ -802,6 +803,108 @@ dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, con
   p.bias = bias;
   p.R = R;
   return launch_lowrank_decode_step(p, W, dtype, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// The convolution in the epilogue of the producing projection
+// ---------------------------------------------------------------------------------
+namespace {
+
+dynconv_status check_gemm(const void* A, const int64_t* as, const void* Wp, int64_t ldw, const void* y,
+                          const int64_t* ys, int64_t B, int64_t T, int64_t N, int64_t K, int32_t W, int32_t H,
+                          dynconv_dtype dtype) {
+  dynconv_status st = check_common(B, T, N, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  if (K < 0) return DYNCONV_ERR_INVALID_ARG;
+  if (A == nullptr || as == nullptr || Wp == nullptr || y == nullptr || ys == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (ldw < K) return DYNCONV_ERR_INVALID_ARG;
+  if (dtype == DYNCONV_F32) return DYNCONV_ERR_UNSUPPORTED;  // matrix cores on 16-bit operands
+  if (W > 5 || H > 16) return DYNCONV_ERR_UNSUPPORTED;
+  if (as[2] != 1 || ys[2] != 1) return DYNCONV_ERR_UNSUPPORTED;
+  if (as[0] < 0 || as[1] < 0 || ys[0] < 0 || ys[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (K == 0 || K % kGemmK != 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (N % kGemmCols != 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (B * T > INT32_MAX) return DYNCONV_ERR_UNSUPPORTED;
+  // 16-byte rows of A and W_p (LDS DMA of 16-byte chunks), 16-bit elements of y
+  if (!aligned(A, 16) || (as[0] * 2) % 16 != 0 || (as[1] * 2) % 16 != 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (!aligned(Wp, 16) || (ldw * 2) % 16 != 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (!aligned(y, 2)) return DYNCONV_ERR_UNSUPPORTED;
+  if (y == A || y == Wp) return DYNCONV_ERR_INVALID_ARG;
+  return DYNCONV_OK;
+}
+
+GemmParams gemm_params(const void* A, const int64_t* as, const void* Wp, int64_t ldw, void* y, const int64_t* ys,
+                       int64_t B, int64_t T, int64_t N, int64_t K, int32_t H) {
+  GemmParams p{};
+  p.A = A;
+  p.Wp = Wp;
+  p.y = y;
+  p.as0 = as[0];
+  p.as1 = as[1];
+  p.ldw = ldw;
+  p.ys0 = ys[0];
+  p.ys1 = ys[1];
+  p.B = int32_t(B);
+  p.T = int32_t(T);
+  p.N = int32_t(N);
+  p.K = int32_t(K);
+  p.H = H;
+  p.M = int32_t(B * T);
+  p.nTm = int32_t((B * T + kGemmOutRows - 1) / kGemmOutRows);
+  p.nTn = int32_t(N / kGemmCols);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+dynconv_status dynconv_gemm_fwd(const void* A, const int64_t* as, const void* Wp, int64_t ldw, const void* w,
+                                const int64_t* ws, void* y, const int64_t* ys, int64_t B, int64_t T, int64_t N,
+                                int64_t K, int32_t W, int32_t H, dynconv_dtype dtype, void* stream) {
+  dynconv_status st = check_gemm(A, as, Wp, ldw, y, ys, B, T, N, K, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  if (w == nullptr || ws == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (ws[3] != 1 || ws[2] != W || ws[0] < 0 || ws[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (!aligned(w, 2)) return DYNCONV_ERR_UNSUPPORTED;
+  if (y == w) return DYNCONV_ERR_INVALID_ARG;
+  if (B == 0 || T == 0 || N == 0) return DYNCONV_OK;
+  GemmParams p = gemm_params(A, as, Wp, ldw, y, ys, B, T, N, K, H);
+  p.w = w;
+  p.ws0 = ws[0];
+  p.ws1 = ws[1];
+  const bool wvec = W == 4 && aligned(w, 8) && (ws[0] * 2) % 8 == 0 && (ws[1] * 2) % 8 == 0;
+  const hipError_t e = launch_gemm_conv(p, W, wvec, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
+}
+
+dynconv_status dynconv_gemm_lowrank_fwd(const void* A, const int64_t* as, const void* Wp, int64_t ldw, const void* z,
+                                        const int64_t* zs, const void* U, int64_t ldu, const void* bias, void* y,
+                                        const int64_t* ys, int64_t B, int64_t T, int64_t N, int64_t K, int32_t W,
+                                        int32_t H, int32_t R, dynconv_dtype dtype, void* stream) {
+  dynconv_status st = check_gemm(A, as, Wp, ldw, y, ys, B, T, N, K, W, H, dtype);
+  if (st != DYNCONV_OK) return st;
+  if (R < 1) return DYNCONV_ERR_INVALID_ARG;
+  if (R > 128) return DYNCONV_ERR_UNSUPPORTED;
+  if (z == nullptr || zs == nullptr || U == nullptr) return DYNCONV_ERR_INVALID_ARG;
+  if (zs[2] != 1 || zs[0] < 0 || zs[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (ldu < (N / H) * W) return DYNCONV_ERR_INVALID_ARG;
+  if (!aligned(z, 2) || !aligned(U, 2) || (bias != nullptr && !aligned(bias, 2))) return DYNCONV_ERR_UNSUPPORTED;
+  if (!gemm_lowrank_fits(W, R)) return DYNCONV_ERR_UNSUPPORTED;
+  if (y == z || y == U || (bias != nullptr && y == bias)) return DYNCONV_ERR_INVALID_ARG;
+  if (B == 0 || T == 0 || N == 0) return DYNCONV_OK;
+  GemmParams p = gemm_params(A, as, Wp, ldw, y, ys, B, T, N, K, H);
+  p.z = z;
+  p.zs0 = zs[0];
+  p.zs1 = zs[1];
+  p.U = U;
+  p.ldu = ldu;
+  p.bias = bias;
+  p.R = R;
+  const hipError_t e = launch_gemm_lowrank(p, W, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
 }
 
 }  // extern "C"

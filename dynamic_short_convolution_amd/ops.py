@@ -277,6 +277,55 @@ def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = T
 
 
 # ----------------------------------------------------------------------------------
+# The convolution in the epilogue of the producing projection: X = A Wp^T is formed in
+# the same kernel and never stored
+# ----------------------------------------------------------------------------------
+
+
+def _check_projection(A, Wp, H: int):
+    B, T, K = _check_act3(A)
+    if Wp.dim() != 2 or Wp.shape[1] != K or (K > 1 and Wp.stride(1) != 1):
+        raise ValueError(f"Wp must be [N, K={K}] with unit column stride; got shape {list(Wp.shape)} "
+                         f"strides {list(Wp.stride())}")
+    if Wp.dtype != A.dtype:
+        raise TypeError(f"Wp is {Wp.dtype} but A is {A.dtype}")
+    N = Wp.shape[0]
+    return B, T, K, N, _groups(N, H)
+
+
+def dynconv_gemm_fwd(A, Wp, w, H: int = 1, out=None):
+    """y = X + conv(X) with X = A Wp^T (A [B,T,K], Wp [N,K]) computed in the same kernel;
+    w: per-token filters [B,T,N/H,W] or a static [N/H,W]."""
+    B, T, K, N, G = _check_projection(A, Wp, H)
+    W = w.shape[-1]
+    _expect("w", w, (G, W) if w.dim() == 2 else (B, T, G, W), A.dtype)
+    _expect("out", out, (B, T, N), A.dtype)
+    dev = _require_device(A, Wp, w, out)
+    y = torch.empty((B, T, N), dtype=A.dtype, device=A.device) if out is None else out
+    st = _lib.load().dynconv_gemm_fwd(_ptr(A), _lib.strides(A.stride()), _ptr(Wp), Wp.stride(0), _ptr(w),
+                                      _lib.strides(filter_strides(w)), _ptr(y), _lib.strides(y.stride()), B, T, N, K,
+                                      W, H, _dtype_code(A), _stream(dev))
+    _lib.check("dynconv_gemm_fwd", st)
+    return y
+
+
+def dynconv_gemm_lowrank_fwd(A, Wp, z, U, bias, W: int, H: int = 1, out=None):
+    """y = X + conv(X) with X = A Wp^T and filters z U + bias, both formed in the same kernel
+    (neither X nor the filters are stored). z [B,T,R], U [R,(N/H)*W], bias [(N/H)*W] or None."""
+    B, T, K, N, G = _check_projection(A, Wp, H)
+    R = z.shape[-1]
+    _check_lowrank_operands(A, z, U, bias, G * W)  # z [B, T, R] like A's leading dims, A's dtype
+    _expect("out", out, (B, T, N), A.dtype)
+    dev = _require_device(A, Wp, z, U, bias, out)
+    y = torch.empty((B, T, N), dtype=A.dtype, device=A.device) if out is None else out
+    st = _lib.load().dynconv_gemm_lowrank_fwd(
+        _ptr(A), _lib.strides(A.stride()), _ptr(Wp), Wp.stride(0), _ptr(z), _lib.strides(z.stride()), _ptr(U),
+        U.stride(0), _ptr(bias), _ptr(y), _lib.strides(y.stride()), B, T, N, K, W, H, R, _dtype_code(A), _stream(dev))
+    _lib.check("dynconv_gemm_lowrank_fwd", st)
+    return y
+
+
+# ----------------------------------------------------------------------------------
 # Inference: rolling cache of the last W-1 inputs, single-token decoding steps
 # ----------------------------------------------------------------------------------
 

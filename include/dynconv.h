@@ -251,6 +251,36 @@ dynconv_status dynconv_decode_step_ex(const void* x, const int64_t* xs, const vo
                                       dynconv_dtype dtype, void* stream);
 
 /*
+ * The convolution in the epilogue of the producing projection (the reading note's
+ * end-to-end throughput section, closing analysis: fusing the dynamic convolution into
+ * the matmul epilogue removes memory traffic; its "Parameterization" section puts the
+ * convolution on the QKV projection's outputs). One kernel computes
+ *   X = A W_p^T          (the projection; X is never written to memory)
+ *   y = X + conv(X)      (eq. 2 + eq. 3 on X, zeros before t = 0 of every sequence)
+ * with float32 accumulation (X is not rounded before the convolution).
+ *   A   [B,T,K] activations with strides as[0..2], as[2] == 1
+ *   Wp  [N,K] projection weight (a linear layer's out x in layout), rows ldw apart
+ *   y   [B,T,N] with strides ys[0..2], ys[2] == 1
+ * dynconv_gemm_fwd takes per-token filters w [B,T,N/H,W] (strides ws, ws[3] == 1,
+ * ws[2] == W; ws[0] == ws[1] == 0: a static [N/H,W] filter); dynconv_gemm_lowrank_fwd
+ * forms them as w = z U + bias on the matrix cores (z [B,T,R] strides zs, zs[2] == 1;
+ * U [R,(N/H)*W] rows ldu apart, column g*W + k; bias [(N/H)*W] or NULL).
+ * Limits (DYNCONV_ERR_UNSUPPORTED otherwise): bfloat16 or float16; 1 <= W <= 5;
+ * H in {1, 2, 4, 8, 16}; K a positive multiple of 64; N a multiple of 128; B*T < 2^31;
+ * A and W_p rows 16-byte aligned (base, as[0], as[1], ldw); low-rank: R <= 128 with
+ * W * (32 ceil(R/32) + 8) <= 552 (R <= 128 at W <= 4, R <= 96 at W = 5).
+ * y may not be any input (DYNCONV_ERR_INVALID_ARG). Forward only.
+ */
+dynconv_status dynconv_gemm_fwd(const void* A, const int64_t* as, const void* Wp, int64_t ldw, const void* w,
+                                const int64_t* ws, void* y, const int64_t* ys, int64_t B, int64_t T, int64_t N,
+                                int64_t K, int32_t W, int32_t H, dynconv_dtype dtype, void* stream);
+
+dynconv_status dynconv_gemm_lowrank_fwd(const void* A, const int64_t* as, const void* Wp, int64_t ldw, const void* z,
+                                        const int64_t* zs, const void* U, int64_t ldu, const void* bias, void* y,
+                                        const int64_t* ys, int64_t B, int64_t T, int64_t N, int64_t K, int32_t W,
+                                        int32_t H, int32_t R, dynconv_dtype dtype, void* stream);
+
+/*
  * Allocation-free backward, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The same
  * operation and arguments as dynconv_bwd_ex, without a workspace: the float32 partial

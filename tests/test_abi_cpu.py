@@ -390,3 +390,42 @@ def test_noalloc_scratch_constant_matches_header():
     with open(os.path.join(ROOT, "include", "dynconv.h")) as f:
         m = re.search(r"#define DYNCONV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
     assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_gemm_validation(lib):
+    """The projection + convolution calls reject bad arguments before any HIP call."""
+    A, WP, WF, YY, ZZ, UU = (P(0x100000 * (i + 1)) for i in range(6))
+    B, T, K, N, W = 2, 10, 128, 256, 4
+
+    def g(A_=A, as_=(T * K, K, 1), wp=WP, ldw=K, w=WF, ws=(T * N * W, N * W, W, 1), y=YY, ys=(T * N, N, 1), B_=B,
+          K_=K, N_=N, W_=W, H=1, dt=BF16):
+        return lib.dynconv_gemm_fwd(A_, S(*as_), wp, ldw, w, S(*ws), y, S(*ys), B_, T, N_, K_, W_, H, dt, None)
+
+    assert g(B_=0) == OK
+    assert g(A_=P(0)) == INVALID
+    assert g(w=P(0)) == INVALID
+    assert g(y=A) == INVALID and g(y=WF) == INVALID
+    assert g(ldw=K - 8) == INVALID
+    assert g(dt=F32) == UNSUP
+    assert g(W_=6, ws=(T * N * 6, N * 6, 6, 1)) == UNSUP
+    assert g(H=32, ws=(T * 8 * W, 8 * W, W, 1)) == UNSUP
+    assert g(H=3) == INVALID  # H must divide N
+    assert g(K_=96, as_=(T * 96, 96, 1), ldw=96) == UNSUP  # K % 64
+    assert g(N_=192, ws=(T * 192 * W, 192 * W, W, 1)) == UNSUP  # N % 128
+    assert g(A_=P(0x100008)) == UNSUP  # 16-byte rows of A
+    assert g(as_=(T * (K + 4), K + 4, 1)) == UNSUP
+    assert g(ldw=K + 4) == UNSUP
+    assert g(ws=(T * N * W, N * W, W + 1, 1)) == UNSUP
+
+    def gl(R=64, W_=4, z=ZZ, zs=(T * 64, 64, 1), U_=UU, ldu=N * 4, bias=None, y=YY):
+        return lib.dynconv_gemm_lowrank_fwd(A, S(T * K, K, 1), WP, K, z, S(*zs), U_, ldu, bias, y, S(T * N, N, 1), B, T,
+                                            N, K, W_, 1, R, BF16, None)
+
+    assert gl(R=0) == INVALID
+    assert gl(R=129) == UNSUP
+    assert gl(R=128, W_=5, ldu=N * 5) == UNSUP  # the LDS copy of U would not fit
+    assert gl(z=P(0)) == INVALID
+    assert gl(U_=P(0)) == INVALID
+    assert gl(ldu=N * 4 - 1) == INVALID
+    assert gl(y=ZZ) == INVALID and gl(y=UU) == INVALID
+    assert gl(zs=(T * 64, 64, 2)) == UNSUP
