@@ -903,6 +903,8 @@ dynconv_status dynconv_gemm_lowrank_fwd(const void* A, const int64_t* as, const 
   p.ldu = ldu;
   p.bias = bias;
   p.R = R;
+  p.uvec = aligned(U, 16) && ldu % 8 == 0;
+  p.zvec = aligned(z, 16) && zs[0] % 8 == 0 && zs[1] % 8 == 0 && R % 8 == 0;
   const hipError_t e = launch_gemm_lowrank(p, W, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
 }

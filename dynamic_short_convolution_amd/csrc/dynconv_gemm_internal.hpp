@@ -25,6 +25,8 @@ struct GemmParams {
   int32_t B, T, N, K, H, R;
   int32_t M;         // B * T
   int32_t nTm, nTn;  // tiles along the rows and the columns
+  int32_t uvec;      // low-rank: U rows allow 16-byte loads (base and ldu)
+  int32_t zvec;      // low-rank: z rows allow 16-byte loads and R % 8 == 0
 };
 
 // Whether the kernels serve these sizes (the C ABI has checked everything else).
