@@ -169,64 +169,43 @@ def test_packed_prompt_cache_fill_and_decode(W):
         assert_close(f"y[{t}]", yt, ref[:, t], torch.bfloat16)
 
 
-def test_full_packed_perchannel_sampled():
-    """B8 T4096 D2048 W4 with documents of mean length 512, every token of sampled channel
-    blocks, in the launch configuration of the benchmark's packed rows."""
+def test_full_packed_perchannel():
+    """B8 T4096 D2048 W4 with documents of mean length 512, every element (one sequence at a
+    time), in the launch configuration of the benchmark's packed rows."""
     wl = synth.workloads()["perchannel_h1"]
     x, w, dy = wl.x(), wl.w(), wl.dy()
     seq = synth.segments(wl.B, wl.T, 512.0, wl.seed, first=(1, 2, 3))
     xg, wg, dyg, sg = x.cuda(), w.cuda(), dy.cuda(), seq.cuda()
-    ci = torch.as_tensor(np.concatenate([np.arange(0, 64), np.arange(992, 1056), np.arange(1984, 2048)]))
-    y = dynconv_fwd(xg, wg, 1, seq_idx=sg).index_select(2, ci.cuda()).cpu()
+    y = dynconv_fwd(xg, wg, 1, seq_idx=sg).cpu()
     dx, dw = dynconv_bwd(xg, wg, dyg, 1, seq_idx=sg)
-    dxs, dws = dx.index_select(2, ci.cuda()).cpu(), dw.index_select(2, ci.cuda()).cpu()
-    del dx, dw, xg, wg, dyg
-    x64, w64 = to64(x.index_select(2, ci)), to64(w.index_select(2, ci))
-    s64 = seq.numpy()
-    assert_close("y", y, conv_fwd(x64, w64, 1, s64), torch.bfloat16)
-    rdx, rdw = conv_bwd(x64, w64, to64(dy.index_select(2, ci)), 1, s64)
-    assert_close("dx", dxs, rdx, torch.bfloat16)
-    assert_close("dw", dws, rdw, torch.bfloat16)
+    dx, dw = dx.cpu(), dw.cpu()
+    del xg, wg, dyg
     torch.cuda.empty_cache()
+    s64 = seq.numpy()
+    for b in range(wl.B):
+        x64, w64, sq = to64(x[b : b + 1]), to64(w[b : b + 1]), s64[b : b + 1]
+        assert_close(f"y[{b}]", y[b : b + 1], conv_fwd(x64, w64, 1, sq), torch.bfloat16)
+        rdx, rdw = conv_bwd(x64, w64, to64(dy[b : b + 1]), 1, sq)
+        assert_close(f"dx[{b}]", dx[b : b + 1], rdx, torch.bfloat16)
+        assert_close(f"dw[{b}]", dw[b : b + 1], rdw, torch.bfloat16)
 
 
-def test_full_packed_lowrank_sampled():
-    """B8 T4096 D2048 W4 R64 with documents of mean length 512 (the fast forward with
-    segment ids and the general backward), every token of sampled channel blocks."""
+def test_full_packed_lowrank():
+    """B8 T4096 D2048 W4 R64 with documents of mean length 512 (the fast kernels with
+    segment ids), every element of y, dx, dz, dU and db."""
+    from tests.test_gpu_lowrank import check_lowrank_full_bwd
+
     wl = synth.workloads()["lowrank_r64"]
-    x, z, U, b = wl.x(), wl.z(), wl.U(), wl.b()
+    x, z, U, b, dy = wl.x(), wl.z(), wl.U(), wl.b(), wl.dy()
     W = wl.W
     seq = synth.segments(wl.B, wl.T, 512.0, wl.seed, first=(1, 2, 3))
     xg, zg, Ug, bg, sg = x.cuda(), z.cuda(), U.cuda(), b.cuda(), seq.cuda()
-    ci = torch.as_tensor(np.concatenate([np.arange(0, 64), np.arange(1984, 2048)]))
-    cols = torch.as_tensor((ci.numpy()[:, None] * W + np.arange(W)[None, :]).reshape(-1))
-    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, seq_idx=sg).index_select(2, ci.cuda()).cpu()
+    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, seq_idx=sg).cpu()
+    got = dynconv_lowrank_bwd(xg, zg, Ug, bg, dy.cuda(), W, seq_idx=sg)
     s64 = seq.numpy()
-    U64s, b64s = to64(U.index_select(1, cols)), to64(b.index_select(0, cols))
-    ref = lowrank_fwd(to64(x.index_select(2, ci)), to64(z), U64s, b64s, W, 1, s64)
-    assert_close("y", y, ref, torch.bfloat16)
-    # backward (the fast kernels with segment ids): dx, dU and db on the sampled channels;
-    # dz needs every channel, so it is checked exactly on a few tokens
-    dy = wl.dy()
-    dx, dz, dU, db = dynconv_lowrank_bwd(xg, zg, Ug, bg, dy.cuda(), W, seq_idx=sg)
-    dxs, dUs, dbs = dx.index_select(2, ci.cuda()).cpu(), dU.index_select(1, cols.cuda()).cpu(), db[cols.cuda()].cpu()
-    dz = dz.cpu()
-    del xg, dx
-    rdx, _, rdU, rdb = lowrank_bwd(to64(x.index_select(2, ci)), to64(z), U64s, b64s, to64(dy.index_select(2, ci)),
-                                   W, 1, s64)
-    assert_close("dx", dxs, rdx, torch.bfloat16)
-    # g is rounded to bf16 as a matrix-core operand: allow 2^-8 of sum |z| |g| (as elsewhere)
-    x64s, dy64s = to64(x.index_select(2, ci)), to64(dy.index_select(2, ci))
-    _, gabs = conv_bwd(np.abs(x64s), np.zeros(x64s.shape + (W,)), np.abs(dy64s), 1, s64)
-    gabs = gabs.reshape(-1, len(ci) * W)
-    extra_dU = 2.0**-8 * (np.abs(to64(z)).reshape(-1, z.shape[-1]).T @ gabs)
-    assert_close("dU", dUs, rdU, torch.bfloat16, rtol=1e-5, atol=1e-5, extra=extra_dU)
-    assert_close("db", dbs, rdb, torch.bfloat16, rtol=1e-5, atol=1e-5)
-    for bb, t in ((0, 0), (0, 1), (0, 5), (3, 511), (3, 512), (7, 2047), (7, 4095)):
-        lo = max(0, t - W + 1)
-        xw, dyw = to64(x[bb : bb + 1, lo : t + 1]), to64(dy[bb : bb + 1, lo : t + 1])
-        zw, sw = to64(z[bb : bb + 1, lo : t + 1]), s64[bb : bb + 1, lo : t + 1]
-        _, rdz, _, _ = lowrank_bwd(xw, zw, to64(U), to64(b), dyw, W, 1, sw)
-        # the window's last row is token t; its g needs only x_{t-k}, which the window holds
-        assert_close(f"dz[{bb},{t}]", dz[bb, t], rdz[0, -1], torch.bfloat16, extra=2.0**-8 * np.abs(rdz[0, -1]).max())
+    U64, b64 = to64(U), to64(b)
+    for bb in range(wl.B):
+        ref = lowrank_fwd(to64(x[bb : bb + 1]), to64(z[bb : bb + 1]), U64, b64, W, 1, s64[bb : bb + 1])
+        assert_close(f"y[{bb}]", y[bb : bb + 1], ref, torch.bfloat16)
+    check_lowrank_full_bwd(x, z, U, b, dy, W, torch.bfloat16, got, seq_idx=s64)
     torch.cuda.empty_cache()
