@@ -231,6 +231,12 @@ ROWS = (
     "packed_lowrank_r64_bwd",
     "lowrank_r64_f16_fwd",
     "lowrank_r64_f16_bwd",
+    "lowrank_r16_fwd",
+    "lowrank_r16_bwd",
+    "lowrank_r20_fwd",
+    "lowrank_r20_bwd",
+    "lowrank_r52_fwd",
+    "lowrank_r52_bwd",
     "gemm_conv_qkv_fwd",
     "gemm_lowrank_qkv_fwd",
     "reference_unfused_gemm_conv_qkv_fwd",
@@ -330,8 +336,13 @@ def make_row(name, device):
         return (lambda: dynconv_lowrank_decode_step(x, z, U, b, cache, 7, W, out=y)), \
             io + B * R * 2 + R * D * W * 2 + D * W * 2, 2 * B * R * D * W, f"decode step B{B} D{D} W{W} R{R} bf16"
     if name.startswith("lowrank"):
-        # lowrank_h4_*: head-wise generation, U of R x (D/4)*W; *_f16_*: float16 storage
-        B, T, D, W, R = 8, 4096, 2048, 4, 64
+        # lowrank_h4_*: head-wise generation, U of R x (D/4)*W; *_f16_*: float16 storage;
+        # lowrank_rN_*: rank N (the pages' models use 16..52; 20 and 52 are zero-padded on
+        # the fast kernels, their contiguous z rows staged in 4-byte pieces)
+        import re
+
+        B, T, D, W = 8, 4096, 2048, 4
+        R = int(re.search(r"_r(\d+)", name).group(1))
         H = 4 if name.startswith("lowrank_h4") else 1
         dt = torch.float16 if "_f16_" in name else torch.bfloat16
         J = (D // H) * W

@@ -529,6 +529,7 @@ dynconv_status lowrank_fwd_impl(const void* x, const int64_t* xs, const void* z,
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
   p.act16 = act_align_ok(acts, 2, eb, 16) ? 1 : 0;
   p.z16 = (aligned(z, 16) && (zs[0] * eb) % 16 == 0 && (zs[1] * eb) % 16 == 0) ? 1 : 0;
+  p.z4 = (aligned(z, 4) && (zs[0] * eb) % 4 == 0 && (zs[1] * eb) % 4 == 0) ? 1 : 0;
   p.out = y;
   p.os0 = ys[0];
   p.os1 = ys[1];
@@ -603,6 +604,7 @@ dynconv_status lowrank_bwd_impl(const void* x, const int64_t* xs, const void* z,
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
   p.act16 = act_align_ok(acts, 3, eb, 16) ? 1 : 0;
   p.z16 = (aligned(z, 16) && (zs[0] * eb) % 16 == 0 && (zs[1] * eb) % 16 == 0) ? 1 : 0;
+  p.z4 = (aligned(z, 4) && (zs[0] * eb) % 4 == 0 && (zs[1] * eb) % 4 == 0) ? 1 : 0;
   p.u16 = (aligned(U, 16) && (ldu * eb) % 16 == 0) ? 1 : 0;
   p.dy = dy;
   p.dys0 = dys[0];

@@ -74,6 +74,41 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds_wave_bas
   __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_wave_base), 16, 0, 0);
 }
 
+// z rows go to LDS in ZB-byte pieces per lane: 16 when the rows are 16-byte aligned and
+// R % 8 == 0, else 4 (rows 4-byte aligned, R even). Ranks from R up to 32 KS (the padding
+// of the matrix-core K extent) are read from this zero word instead.
+__device__ __align__(16) uint32_t g_lr_zero16[4];
+
+template <int ZB>
+__device__ __forceinline__ void dmaz(const void* g, unsigned char* lds_wave_base) {
+  static_assert(ZB == 16 || ZB == 4, "z piece");
+  if constexpr (ZB == 16) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_wave_base), 16, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_wave_base), 4, 0, 0);
+  }
+}
+
+// Source of z piece `idx` (ZB bytes each) of a stage whose rows are ZROW bytes with their
+// 16-byte chunks rotated by rot (logical chunk c sits at position (c + rot) % (ZROW / 16)):
+// the row, the byte offset inside the row, and whether the piece holds ranks below R.
+struct ZPiece {
+  int row;
+  int byte;
+  bool valid;
+};
+template <int ZB, int ZROW>
+__device__ __forceinline__ ZPiece z_piece(int idx, int R, int (*rot)(int)) {
+  constexpr int ZCPR = ZROW / 16;
+  const int o = idx * ZB;
+  const int row = o / ZROW, ob = o % ZROW;
+  const int c = ((ob / 16 - rot(row)) % ZCPR + ZCPR) % ZCPR;
+  const int gb = 16 * c + (ob & 15);
+  return ZPiece{row, gb, gb / 2 < R};
+}
+__device__ __forceinline__ int rot_quarter(int row) { return row >> 2; }
+__device__ __forceinline__ int rot_double(int row) { return 2 * row; }
+
 // Waits until at most N of this wave's vector memory operations are outstanding (they
 // complete in issue order) and its LDS operations are done, then joins the workgroup
 // barrier.
@@ -96,9 +131,10 @@ __device__ __forceinline__ f32x4_t mma32(const u16x8_t& a, const u16x8_t& b, f32
   }
 }
 
-template <int KS, int NWV_, int XN_, int XD_, int ZN_, int ZD_, int SG_ = 0>
+template <int KS, int NWV_, int XN_, int XD_, int ZN_, int ZD_, int SG_ = 0, int ZB_ = 16>
 struct FwdFast {
   static constexpr int NWV = NWV_, XN = XN_, XD = XD_, ZN = ZN_, ZD = ZD_;
+  static constexpr int ZB = ZB_;  // bytes of a z piece per lane and transfer
   // SG: packed sequences. Each step also stages the segment ids of tokens t0 - 4 .. t0 + 63
   // (17 chunks of 16 bytes, 5 per wave: every wave issues exactly one more transfer, right
   // before its x transfers, so it is complete whenever x is).
@@ -117,9 +153,9 @@ struct FwdFast {
   static constexpr int S_OFF = Y_OFF + 2 * XSTAGE;   // two y tiles, then the id stages
   static constexpr int BYTES = S_OFF + (SG ? XN * SSTAGE : 0);
   static constexpr int XI = kStep * XCPR / 64 / NWV;  // x transfers per wave per step (2)
-  static constexpr int ZI = kStep * ZCPR / 64 / NWV;  // z transfers per wave per step
+  static constexpr int ZI = kStep * ZROW / (64 * ZB) / NWV;  // z transfers per wave per step
   static constexpr int NS = kStep * XCPR / 64 / NWV;  // y stores per wave per step (2)
-  static_assert((kStep * ZCPR) % (64 * NWV) == 0, "z transfers split evenly over the waves");
+  static_assert((kStep * ZROW) % (64 * ZB * NWV) == 0, "z transfers split evenly over the waves");
   static_assert(XD >= 1 && XD <= XN - 2 && ZD >= 1 && ZD <= ZN - 1 && ZD <= XD, "pipeline depths");
   static_assert((XCPR & (XCPR - 1)) == 0 && 16 % XCPR == 0, "x row rotation");
   static_assert(!SG || NWV * SPW >= SCH, "id chunks spread over the waves");
@@ -163,9 +199,9 @@ __device__ __forceinline__ void step_wait(int s) {
   }
 }
 
-template <typename ET, int W, int KS, int SG>
+template <typename ET, int W, int KS, int SG, int ZB>
 __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRankParams p) {
-  using F = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD, SG>;
+  using F = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD, SG, ZB>;
   constexpr int NWV = F::NWV, XN = F::XN, XD = F::XD, ZN = F::ZN, ZD = F::ZD, CPB = F::CPB;
   constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF, Y_OFF = F::Y_OFF;
@@ -199,6 +235,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   // by (row / 4) within the row.
   uint32_t xoff[XI], zoff[ZI];
   int xrl[XI], zrl[ZI];
+  bool zval[ZI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int idx = (wv + NWV * i) * 64 + lane;
@@ -209,14 +246,14 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   }
 #pragma unroll
   for (int i = 0; i < ZI; ++i) {
-    const int idx = (wv + NWV * i) * 64 + lane;
-    const int rl = idx / ZCPR, pc = idx % ZCPR;
-    const int c = ((pc - (rl >> 2)) % ZCPR + ZCPR) % ZCPR;
-    zrl[i] = rl;
-    zoff[i] = uint32_t(rl * int(p.zs1) + 8 * c) * 2u;
+    const ZPiece zp = z_piece<ZB, ZROW>((wv + NWV * i) * 64 + lane, p.R, rot_quarter);
+    zrl[i] = zp.row;
+    zval[i] = zp.valid;
+    zoff[i] = uint32_t(zp.row * int(p.zs1)) * 2u + uint32_t(zp.byte);
   }
   const char* xbc = reinterpret_cast<const char*>(xb);
   const char* zbc = reinterpret_cast<const char*>(zb);
+  const char* zero = reinterpret_cast<const char*>(g_lr_zero16);
   auto issue_x = [&](int st, int t0) {
     unsigned char* xs = smem + st * XSTAGE;
     if (t0 + kStep <= p.T) {
@@ -251,12 +288,13 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
     if (t0 + kStep <= p.T) {
       const char* zg = zbc + int64_t(t0) * p.zs1 * 2;
 #pragma unroll
-      for (int i = 0; i < ZI; ++i) dma16(zg + zoff[i], zs + (wv + NWV * i) * 1024);
+      for (int i = 0; i < ZI; ++i) dmaz<ZB>(zval[i] ? zg + zoff[i] : zero, zs + (wv + NWV * i) * (64 * ZB));
     } else {
 #pragma unroll
       for (int i = 0; i < ZI; ++i) {
         const int t = min(t0 + zrl[i], p.T - 1);
-        dma16(zbc + (int64_t(t) - zrl[i]) * p.zs1 * 2 + zoff[i], zs + (wv + NWV * i) * 1024);
+        dmaz<ZB>(zval[i] ? zbc + (int64_t(t) - zrl[i]) * p.zs1 * 2 + zoff[i] : zero,
+                 zs + (wv + NWV * i) * (64 * ZB));
       }
     }
   };
@@ -281,8 +319,10 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint16_t v = U[int64_t(32 * ks + 8 * q + e) * p.ldu + col];
-          afr[mt][ks][e] = tap < W ? v : uint16_t(0);
+          // ranks from R up to 32 KS are zero (the row read is clamped inside U)
+          const int r = 32 * ks + 8 * q + e;
+          const uint16_t v = U[int64_t(min(r, p.R - 1)) * p.ldu + col];
+          afr[mt][ks][e] = (tap < W && r < p.R) ? v : uint16_t(0);
         }
       const int chq = cw + 4 * q + mt;
 #pragma unroll
@@ -421,14 +461,22 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <typename ET, int W, int KS>
-hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+// z pieces of 16 bytes where the rows allow them and R % 8 == 0, else 4 bytes.
+bool z_pieces16(const LowRankParams& p) { return p.z16 != 0 && p.R % 8 == 0; }
+
+template <typename ET, int W, int KS, int ZB>
+hipError_t fwd_fast_zb(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   if (p.seg != nullptr) {
-    hipLaunchKernelGGL((k_lowrank_fwd_fast<ET, W, KS, 1>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_fwd_fast<ET, W, KS, 1, ZB>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_lowrank_fwd_fast<ET, W, KS, 0>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_fwd_fast<ET, W, KS, 0, ZB>), dim3(unsigned(blocks)), dim3(64 * LRF_NWV), 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <typename ET, int W, int KS>
+hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  return z_pieces16(p) ? fwd_fast_zb<ET, W, KS, 16>(p, blocks, s) : fwd_fast_zb<ET, W, KS, 4>(p, blocks, s);
 }
 
 // ---------------------------------------------------------------------------------
@@ -446,7 +494,7 @@ hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) 
 // three rows, and the first step's first three rows belong to the previous range.
 // dy rows at or past T are zeroed, so the tail contributes nothing past the sequence.
 // ---------------------------------------------------------------------------------
-template <int KS, int SG = 0>
+template <int KS, int SG = 0, int ZB = 16>
 struct BwdDxFast {
   static constexpr int NWV = 4;
   // SG: packed sequences; the ids of tokens t0 - 4 .. t0 + 63 ride with each step's dy
@@ -462,12 +510,12 @@ struct BwdDxFast {
   static constexpr int T_OFF = Z_OFF + 2 * ZSTAGE;    // two z stages, then two dx tiles
   static constexpr int S_OFF = T_OFF + 2 * XSTAGE;    // then two id stages (SG)
   static constexpr int BYTES = S_OFF + (SG ? 2 * SSTAGE : 0);
-  static constexpr int DI = 2, ZI = KS, ND = DI + ZI, NS = 2;
+  static constexpr int DI = 2, ZI = kStep * ZROW / (64 * ZB) / NWV, ND = DI + ZI, NS = 2;
 };
 
-template <typename ET, int W, int KS, int SG>
+template <typename ET, int W, int KS, int SG, int ZB>
 __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams p) {
-  using F = BwdDxFast<KS, SG>;
+  using F = BwdDxFast<KS, SG, ZB>;
   constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF, T_OFF = F::T_OFF;
   __shared__ __align__(16) unsigned char smem[F::BYTES];
@@ -493,6 +541,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
   // ---- LDS DMA of a step's dy and z rows (rows past T - 1 read row T - 1) ----
   uint32_t doff[F::DI], zoff[F::ZI];
   int drl[F::DI], zrl[F::ZI];
+  bool zval[F::ZI];
 #pragma unroll
   for (int i = 0; i < F::DI; ++i) {
     const int idx = (wv + 4 * i) * 64 + lane;
@@ -503,12 +552,12 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
   }
 #pragma unroll
   for (int i = 0; i < F::ZI; ++i) {
-    const int idx = (wv + 4 * i) * 64 + lane;
-    const int rl = idx / ZCPR, pc = idx % ZCPR;
-    const int c = ((pc - (rl >> 2)) % ZCPR + ZCPR) % ZCPR;
-    zrl[i] = rl;
-    zoff[i] = uint32_t(rl * int(p.zs1) + 8 * c) * 2u;
+    const ZPiece zp = z_piece<ZB, ZROW>((wv + 4 * i) * 64 + lane, p.R, rot_quarter);
+    zrl[i] = zp.row;
+    zval[i] = zp.valid;
+    zoff[i] = uint32_t(zp.row * int(p.zs1)) * 2u + uint32_t(zp.byte);
   }
+  const char* zero = reinterpret_cast<const char*>(g_lr_zero16);
   // segment ids (SG): chunk sc = 5 wv + lane holds the ids of tokens t0 - 4 + 4 sc .. + 3
   const int sc = F::SPW * wv + lane;
   const bool sact = SG && lane < F::SPW && sc < F::SCH;
@@ -528,7 +577,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
 #pragma unroll
       for (int i = 0; i < F::DI; ++i) dma16(dg + doff[i], ds + (wv + 4 * i) * 1024);
 #pragma unroll
-      for (int i = 0; i < F::ZI; ++i) dma16(zg + zoff[i], zs + (wv + 4 * i) * 1024);
+      for (int i = 0; i < F::ZI; ++i) dmaz<ZB>(zval[i] ? zg + zoff[i] : zero, zs + (wv + 4 * i) * (64 * ZB));
     } else {
 #pragma unroll
       for (int i = 0; i < F::DI; ++i) {
@@ -538,7 +587,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
 #pragma unroll
       for (int i = 0; i < F::ZI; ++i) {
         const int t = min(t0 + zrl[i], p.T - 1);
-        dma16(zc + (int64_t(t) - zrl[i]) * p.zs1 * 2 + zoff[i], zs + (wv + 4 * i) * 1024);
+        dmaz<ZB>(zval[i] ? zc + (int64_t(t) - zrl[i]) * p.zs1 * 2 + zoff[i] : zero, zs + (wv + 4 * i) * (64 * ZB));
       }
     }
   };
@@ -561,8 +610,10 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint16_t v = U[int64_t(32 * ks + 8 * q + e) * p.ldu + col];
-          afr[mt][ks][e] = tap < W ? v : uint16_t(0);
+          // ranks from R up to 32 KS are zero (the row read is clamped inside U)
+          const int r = 32 * ks + 8 * q + e;
+          const uint16_t v = U[int64_t(min(r, p.R - 1)) * p.ldu + col];
+          afr[mt][ks][e] = (tap < W && r < p.R) ? v : uint16_t(0);
         }
       const int chq = cw + 4 * q + mt;
 #pragma unroll
@@ -784,7 +835,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16-byte chunks are rotated by 2 row so that the 4 rows of a transposing read hit
 // distinct banks.
 // ---------------------------------------------------------------------------------
-template <int KS, int SG_ = 0>
+template <int KS, int SG_ = 0, int ZB = 16>
 struct BwdGduFast {
   static constexpr int CPR = 8, ROW = 128, STAGE = kStep * ROW;  // x, dy: 64 channels
   static constexpr int ZCPR = 4 * KS, ZROW = 16 * ZCPR, ZSTAGE = kStep * ZROW;
@@ -801,12 +852,12 @@ struct BwdGduFast {
   static constexpr int Z_OFF = D_OFF + SN * STAGE;
   static constexpr int S_OFF = Z_OFF + SN * ZSTAGE;
   static constexpr int BYTES = S_OFF + (SG ? SN * SSTAGE : 0);
-  static constexpr int XI = 2, DI = 2, ZI = KS, ND = XI + DI + ZI + SG;
+  static constexpr int XI = 2, DI = 2, ZI = kStep * ZROW / (64 * ZB) / 4, ND = XI + DI + ZI + SG;
 };
 
-template <typename ET, int W, int KS, int SG>
+template <typename ET, int W, int KS, int SG, int ZB>
 __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParams p) {
-  using F = BwdGduFast<KS, SG>;
+  using F = BwdGduFast<KS, SG, ZB>;
   constexpr int CPR = F::CPR, ROW = F::ROW, STAGE = F::STAGE, XN = F::XN;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, D_OFF = F::D_OFF, Z_OFF = F::Z_OFF;
   constexpr int RT = 2 * KS;  // 16-rank tiles
@@ -832,8 +883,9 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
   const char* zc = reinterpret_cast<const char*>(static_cast<const ET*>(p.z) + b * p.zs0);
 
   // ---- LDS DMA: per lane the byte offset of its source chunk from a step's first row ----
-  uint32_t xoff[2], doff[2], zoff[KS];
-  int arl[2], zrl[KS];
+  uint32_t xoff[2], doff[2], zoff[F::ZI];
+  int arl[2], zrl[F::ZI];
+  bool zval[F::ZI];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int idx = (wv + 4 * i) * 64 + lane;
@@ -844,13 +896,13 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
     doff[i] = uint32_t(rl * int(p.dys1) + 8 * c) * 2u;
   }
 #pragma unroll
-  for (int i = 0; i < KS; ++i) {
-    const int idx = (wv + 4 * i) * 64 + lane;
-    const int rl = idx / ZCPR, pc = idx % ZCPR;
-    const int c = ((pc - 2 * rl) % ZCPR + ZCPR) % ZCPR;
-    zrl[i] = rl;
-    zoff[i] = uint32_t(rl * int(p.zs1) + 8 * c) * 2u;
+  for (int i = 0; i < F::ZI; ++i) {
+    const ZPiece zp = z_piece<ZB, ZROW>((wv + 4 * i) * 64 + lane, p.R, rot_double);
+    zrl[i] = zp.row;
+    zval[i] = zp.valid;
+    zoff[i] = uint32_t(zp.row * int(p.zs1)) * 2u + uint32_t(zp.byte);
   }
+  const char* zero = reinterpret_cast<const char*>(g_lr_zero16);
   const int sc = F::SPW * wv + lane;
   const bool sact = SG && lane < F::SPW && sc < F::SCH;
   const char* sgc = SG ? reinterpret_cast<const char*>(p.seg + b * p.ss0) : nullptr;
@@ -872,7 +924,8 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
         dma16(dc + o1 * p.dys1 + doff[i], ds + (wv + 4 * i) * 1024);
       }
 #pragma unroll
-      for (int i = 0; i < KS; ++i) dma16(zc + o1 * p.zs1 + zoff[i], zs + (wv + 4 * i) * 1024);
+      for (int i = 0; i < F::ZI; ++i)
+        dmaz<ZB>(zval[i] ? zc + o1 * p.zs1 + zoff[i] : zero, zs + (wv + 4 * i) * (64 * ZB));
     } else {
       // rows past T - 1 read row T - 1; their dy is zeroed below
 #pragma unroll
@@ -882,9 +935,9 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
         dma16(dc + t * p.dys1 * 2 + doff[i], ds + (wv + 4 * i) * 1024);
       }
 #pragma unroll
-      for (int i = 0; i < KS; ++i) {
+      for (int i = 0; i < F::ZI; ++i) {
         const int64_t t = min(t0 + zrl[i], p.T - 1) - zrl[i];
-        dma16(zc + t * p.zs1 * 2 + zoff[i], zs + (wv + 4 * i) * 1024);
+        dmaz<ZB>(zval[i] ? zc + t * p.zs1 * 2 + zoff[i] : zero, zs + (wv + 4 * i) * (64 * ZB));
       }
     }
   };
@@ -1068,6 +1121,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
 #pragma unroll 4
       for (int idx = tid; idx < 16 * TPC * PER_ROW; idx += 256) {
         const int r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
+        if (16 * rt0 + r >= p.R) continue;  // padding ranks: nothing to store
         const float* src = st + r * PITCH + c4;
         const f32x4_t v = {src[0], src[1], src[2], src[3]};
         *reinterpret_cast<f32x4_t*>(pdu + int64_t(16 * rt0 + r) * p.J + c4) = v;
@@ -1076,6 +1130,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
       const int per_row = (COLS >> hsh) / 4;  // group columns of the slice, 4 at a time
       for (int idx = tid; idx < 16 * TPC * per_row; idx += 256) {
         const int r = idx / per_row, c4 = (idx % per_row) * 4;
+        if (16 * rt0 + r >= p.R) continue;  // padding ranks: nothing to store
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1124,7 +1179,7 @@ hipError_t fwd_fast_try(const LowRankParams& p, int64_t blocks, hipStream_t s) {
 
 template <typename ET, int W>
 hipError_t fwd_fast_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  switch (p.R / 32) {
+  switch ((p.R + 31) / 32) {
     case 1: return fwd_fast_try<ET, W, 1>(p, blocks, s);
     case 2: return fwd_fast_try<ET, W, 2>(p, blocks, s);
     case 4: return fwd_fast_try<ET, W, 4>(p, blocks, s);
@@ -1149,11 +1204,19 @@ int fwd_fast_lds(int ks) {
 
 bool lowrank_fast_group_ok(int H) { return H == 1 || H == 2 || H == 4 || H == 8 || H == 16; }
 
+// Ranks served by the fast kernels: R zero-padded to 32 KS with KS in {1, 2, 4} (R <= 64 or
+// 97 <= R <= 128), z rows staged in 16-byte pieces (aligned rows, R % 8 == 0) or 4-byte
+// pieces (4-byte aligned rows, R even).
+bool lowrank_fast_rank_ok(const LowRankParams& p) {
+  const int ks = (p.R + 31) / 32;
+  return (ks == 1 || ks == 2 || ks == 4) && (z_pieces16(p) || (p.z4 != 0 && p.R % 2 == 0));
+}
+
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
-  const int ks = p.R / 32;
-  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 && p.R % 32 == 0 &&
-         fwd_fast_rank_ok(ks) &&
-         p.D % (16 * LRF_NWV) == 0 && p.act16 != 0 && p.z16 != 0 &&
+  const int ks = (p.R + 31) / 32;
+  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 &&
+         lowrank_fast_rank_ok(p) && fwd_fast_rank_ok(ks) &&
+         p.D % (16 * LRF_NWV) == 0 && p.act16 != 0 &&
          (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) && int64_t(kStep) * p.xs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.zs1 < (int64_t(1) << 30);
 }
@@ -1182,7 +1245,7 @@ LowRankPlan plan_lowrank_fwd_fast(int64_t B, int64_t T, int64_t D, int ks) {
 }
 
 hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t s) {
-  const LowRankPlan pl = plan_lowrank_fwd_fast(p.B, p.T, p.D, p.R / 32);
+  const LowRankPlan pl = plan_lowrank_fwd_fast(p.B, p.T, p.D, (p.R + 31) / 32);
   LowRankParams q = p;
   q.cs0 = 0;
   q.nCsL = pl.nCs;
@@ -1208,19 +1271,24 @@ namespace dynconv {
 
 namespace {
 
-template <typename ET, int W, int KS>
-hipError_t bwd_dx_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+template <typename ET, int W, int KS, int ZB>
+hipError_t bwd_dx_zb(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   if (p.seg != nullptr) {
-    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 1, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 0, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
 
+template <typename ET, int W, int KS>
+hipError_t bwd_dx_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  return z_pieces16(p) ? bwd_dx_zb<ET, W, KS, 16>(p, blocks, s) : bwd_dx_zb<ET, W, KS, 4>(p, blocks, s);
+}
+
 template <typename ET, int W>
 hipError_t bwd_dx_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  switch (p.R / 32) {
+  switch ((p.R + 31) / 32) {
     case 1: return bwd_dx_inst<ET, W, 1>(p, blocks, s);
     case 2: return bwd_dx_inst<ET, W, 2>(p, blocks, s);
     case 4: return bwd_dx_inst<ET, W, 4>(p, blocks, s);
@@ -1231,26 +1299,31 @@ hipError_t bwd_dx_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
 }  // namespace
 
 bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
-  const int ks = p.R / 32;
   return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 &&
-         p.R % 32 == 0 && (ks == 1 || ks == 2 || ks == 4) && p.D % 64 == 0 && p.act16 != 0 && p.z16 != 0 && (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
+         lowrank_fast_rank_ok(p) && p.D % 64 == 0 && p.act16 != 0 &&
+         (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
          int64_t(kStep) * p.dys1 < (int64_t(1) << 30) && int64_t(kStep) * p.zs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.xs1 < (int64_t(1) << 30);
 }
 
-template <typename ET, int W, int KS>
-hipError_t bwd_gdu_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+template <typename ET, int W, int KS, int ZB>
+hipError_t bwd_gdu_zb(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   if (p.seg != nullptr) {
-    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 1>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 1, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 0>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 0, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
 
+template <typename ET, int W, int KS>
+hipError_t bwd_gdu_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  return z_pieces16(p) ? bwd_gdu_zb<ET, W, KS, 16>(p, blocks, s) : bwd_gdu_zb<ET, W, KS, 4>(p, blocks, s);
+}
+
 template <typename ET, int W>
 hipError_t bwd_gdu_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  switch (p.R / 32) {
+  switch ((p.R + 31) / 32) {
     case 1: return bwd_gdu_inst<ET, W, 1>(p, blocks, s);
     case 2: return bwd_gdu_inst<ET, W, 2>(p, blocks, s);
     case 4: return bwd_gdu_inst<ET, W, 4>(p, blocks, s);

@@ -1385,6 +1385,9 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
 }
 
+// Source of the U rows from R up to 32 KS (the padding of the matrix-core extent): zeros.
+__device__ __align__(16) uint32_t g_dz_zero16[4];
+
 // Waits until at most N of this wave's vector memory operations are outstanding, then
 // joins the workgroup barrier; the memory clobber keeps LDS accesses on their side.
 template <int N>
@@ -1416,15 +1419,17 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
   // lane the element offset of its source chunk relative to the chunk's base
   constexpr int SU = (D::NI_U + 3) / 4, SX = (D::NI_X + 3) / 4, SD = (D::NI_D + 3) / 4;
   int uoffg[SU], xoffg[SX], doffg[SD];
-  bool uact[SU], xact[SX], dact[SD];
+  bool uact[SU], xact[SX], dact[SD], uzero[SU];
 #pragma unroll
   for (int i = 0; i < SU; ++i) {
     const int pidx = (wv + 4 * i) * 64 + lane;
     const int r = pidx / UCPR, pc = pidx % UCPR;
     const int c = D::UPlace::chunk(r & 15, pc);
     uact[i] = pidx < D::UCH;
+    uzero[i] = r >= p.R;  // a padding rank: zeros, never a row past U
     uoffg[i] = r * int(p.ldu) + c * 8;
   }
+  const ET* uzsrc = reinterpret_cast<const ET*>(g_dz_zero16);
 #pragma unroll
   for (int i = 0; i < SX; ++i) {
     const int pidx = (wv + 4 * i) * 64 + lane;
@@ -1449,7 +1454,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
     const ET* ub = U + int64_t(ci) * (CH * W);
 #pragma unroll
     for (int i = 0; i < SU; ++i)
-      if (uact[i]) dma16(ub + uoffg[i], stage + (wv + 4 * i) * 1024);
+      if (uact[i]) dma16(uzero[i] ? uzsrc : ub + uoffg[i], stage + (wv + 4 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < SX; ++i)
       if (xact[i]) dma16(xb + c0 + xoffg[i], stage + D::X_OFF + (wv + 4 * i) * 1024);
@@ -1564,7 +1569,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int r = rt * 16 + 4 * q + ii;
-      reinterpret_cast<uint16_t*>(dz)[int64_t(t) * p.dzs1 + r] = Cvt<ET>::bits(acc[rt][ii]);
+      if (r < p.R) reinterpret_cast<uint16_t*>(dz)[int64_t(t) * p.dzs1 + r] = Cvt<ET>::bits(acc[rt][ii]);
     }
 }
 
@@ -1583,8 +1588,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz(const LowRankParam
   lowrank_dz_body<ET, W, KS>(p, sm);
 }
 
-// The LDS DMA path: the launch covers whole token blocks; aligned rows, D % (32 * HG) == 0
-// and R % 32 == 0.
+// The LDS DMA path: the launch covers whole token blocks; aligned rows, D % (32 * HG) == 0;
+// R zero-padded to 32 KS (the U rows past R read zeros, dz columns past R are not stored).
 template <typename ET, int W, int KS, int HG>
 __global__ __launch_bounds__(kBlockThreads) void k_lowrank_dz_dma(const LowRankParams p) {
   __shared__ __align__(16) unsigned char smem[LrDzDma<W, KS, HG>::BYTES];
@@ -1661,7 +1666,7 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
                      : p.H == 16 ? lowrank_dz_dma_ok<ET, W, KS, 16>()
                                  : false;
   const int chunk_channels = p.H <= 4 ? kLowrankDzChunk * p.H : 128;
-  const bool dma = hg_ok && p.act16 != 0 && p.u16 != 0 && p.D % chunk_channels == 0 && p.R % 32 == 0;
+  const bool dma = hg_ok && p.act16 != 0 && p.u16 != 0 && p.D % chunk_channels == 0;
   const int nfb = dma ? p.T / kLowrankDzTokens : 0;
   if (nfb > 0) {
     q.tbb0 = 0;

@@ -187,9 +187,12 @@ def test_full_lowrank_r64_bwd(dtype):
 # before each step (forward), dx completed across lanes, ranges and a tail step
 # (backward), buffer stores that drop rows past T.
 # ---------------------------------------------------------------------------------
+# Ranks that are not a multiple of 32 are zero-padded to 32, 64 or 128 on the fast kernels:
+# z rows of 16-byte pieces where they are 16-byte aligned and R % 8 == 0 (8, 16, 40), of
+# 4-byte pieces otherwise (2, 20, 26, 42, 52, 100: the pages' ranks among them).
 FAST = []
 for W in (1, 2, 3, 4):
-    for R in (32, 64, 128):
+    for R in (2, 8, 16, 20, 26, 32, 40, 42, 52, 64, 100, 128):
         for (B, T, D) in ((1, 1, 64), (2, 65, 128), (3, 200, 192)):
             FAST.append((W, R, B, T, D))
 
@@ -287,6 +290,7 @@ def test_headwise_lowrank_parity(dtype, H, W, R):
 # three-stage ring wraps, three whole 64-token blocks and a ragged tail of 8 tokens
 # (register path); the other W, R and H take the general kernels
 HEADWISE_DMA = [(H, W, R) for H in (2, 4, 8, 16) for W in (1, 2, 3, 4, 5) for R in (32, 64, 96, 128)]
+HEADWISE_DMA += [(H, W, R) for H in (4, 16) for W in (2, 4) for R in (20, 52)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -314,3 +318,24 @@ def test_headwise_lowrank_fast_kernels(H, W, R, dtype):
     assert_close("dx", dx, rdx, td)
     assert_close("dU", dU, rdU, td, rtol=1e-5, atol=1e-5, extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
     assert_close("db", db, rdb, td, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("R", [20, 52])
+def test_full_lowrank_pages_ranks(R):
+    """The pages' ranks at B8 T4096 D2048 W4 on the fast kernels (contiguous z: rows of
+    40 or 104 bytes, staged in 4-byte pieces, ranks zero-padded to 32 or 64): every
+    element of y, dx, dz, dU and db."""
+    B, T, D, W = 8, 4096, 2048, 4
+    seed = 300 + R
+    x = synth.draw((B, T, D), 1.0, seed, "x", "bf16")
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", "bf16")
+    z = synth.draw((B, T, R), 1.0, seed, "z", "bf16")
+    U = synth.draw((R, D * W), 0.1 / R**0.5, seed, "U", "bf16")
+    b = synth.draw((D * W,), 0.1**0.5, seed, "b", "bf16")
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W).cpu()
+    U64, b64 = to64(U), to64(b)
+    for s_ in range(B):
+        ref = lowrank_fwd(to64(x[s_ : s_ + 1]), to64(z[s_ : s_ + 1]), U64, b64, W)
+        assert_close(f"y[{s_}]", y[s_ : s_ + 1], ref, torch.bfloat16)
+    got = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W)
+    check_lowrank_full_bwd(x, z, U, b, dy, W, torch.bfloat16, got)

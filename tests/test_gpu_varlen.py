@@ -209,3 +209,31 @@ def test_full_packed_lowrank():
         assert_close(f"y[{bb}]", y[bb : bb + 1], ref, torch.bfloat16)
     check_lowrank_full_bwd(x, z, U, b, dy, W, torch.bfloat16, got, seq_idx=s64)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("R", [20, 64])
+def test_packed_lowrank_fast_padded_rank(R):
+    """Packed sequences on the fast low-rank kernels with a rank that is zero-padded (20:
+    4-byte z pieces) and one that is not."""
+    B, T, D, W = 2, 640, 256, 4
+    seed = 400 + R
+    x = synth.draw((B, T, D), 1.0, seed, "x", "bf16")
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", "bf16")
+    z = synth.draw((B, T, R), 1.0, seed, "z", "bf16")
+    U = synth.draw((R, D * W), 0.3 / R**0.5, seed, "U", "bf16")
+    b = synth.draw((D * W,), 0.3, seed, "b", "bf16")
+    seq = synth.segments(B, T, 40.0, seed, first=(1, 2, 3))
+    sg = seq.cuda()
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W, seq_idx=sg)
+    x64, z64, U64, b64, dy64, s64 = to64(x), to64(z), to64(U), to64(b), to64(dy), seq.numpy()
+    assert_close("y", y, lowrank_fwd(x64, z64, U64, b64, W, 1, s64), torch.bfloat16)
+    dx, dz, dU, db = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W, seq_idx=sg)
+    rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, 1, s64)
+    _, gabs = conv_bwd(np.abs(x64), np.zeros((B, T, D, W)), np.abs(dy64), 1, s64)
+    gabs = gabs.reshape(B * T, D * W)
+    u = 2.0**-8
+    assert_close("dx", dx, rdx, torch.bfloat16)
+    assert_close("dz", dz, rdz, torch.bfloat16, extra=(u * (gabs @ np.abs(U64).T)).reshape(B, T, R))
+    assert_close("dU", dU, rdU, torch.bfloat16, rtol=1e-5, atol=1e-5,
+                 extra=u * (np.abs(z64).reshape(B * T, R).T @ gabs))
+    assert_close("db", db, rdb, torch.bfloat16, rtol=1e-5, atol=1e-5)
