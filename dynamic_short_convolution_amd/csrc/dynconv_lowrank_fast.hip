@@ -108,6 +108,10 @@ __device__ __forceinline__ ZPiece z_piece(int idx, int R, int (*rot)(int)) {
 }
 __device__ __forceinline__ int rot_quarter(int row) { return row >> 2; }
 __device__ __forceinline__ int rot_double(int row) { return 2 * row; }
+// Stages shared by both roles of the fused backward: the four rows of a transposing read
+// (8q + e, e = 0..3) land on distinct chunk positions as with 2 row, and the 16 rows
+// 4n + j that the dx role reads at once spread over 8 positions.
+__device__ __forceinline__ int rot_fused(int row) { return 2 * row + (row >> 2); }
 
 // Waits until at most N of this wave's vector memory operations are outstanding (they
 // complete in issue order) and its LDS operations are done, then joins the workgroup
@@ -513,19 +517,40 @@ struct BwdDxFast {
   static constexpr int DI = 2, ZI = kStep * ZROW / (64 * ZB) / NWV, ND = DI + ZI, NS = 2;
 };
 
-template <typename ET, int W, int KS, int SG, int ZB>
-__global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams p) {
+// Layout of the fused backward (k_lowrank_bwd_fast, 8 waves): x in a ring of 4 steps, dy,
+// z (and the ids of packed sequences) in 3 stages each, loaded two steps ahead by the
+// filter-gradient role, then the dx role's two output tiles.
+template <int KS, int SG_, int ZB>
+struct BwdFused {
+  static constexpr int SG = SG_;
+  static constexpr int CPR = 8, ROW = 128, STAGE = kStep * ROW;  // x, dy: 64 channels
+  static constexpr int ZCPR = 4 * KS, ZROW = 16 * ZCPR, ZSTAGE = kStep * ZROW;
+  static constexpr int DIST = 2, XN = 4, SN = 3;
+  static constexpr int SCH = 17, SPW = 5, SSTAGE = 4 * SPW * 16;
+  static constexpr int D_OFF = XN * STAGE;
+  static constexpr int Z_OFF = D_OFF + SN * STAGE;
+  static constexpr int S_OFF = Z_OFF + SN * ZSTAGE;
+  static constexpr int T_OFF = S_OFF + (SG ? SN * SSTAGE : 0);
+  static constexpr int BYTES = T_OFF + 2 * STAGE;
+  static constexpr int XI = 2, DI = 2, ZI = kStep * ZROW / (64 * ZB) / 4, ND = XI + DI + ZI + SG;
+};
+
+// The dx computation. Standalone (FUSED false): its own kernel, staging dy and z itself.
+// FUSED: waves 0..3 of the fused backward, reading dy, z and ids from the stages of layout
+// FL that the other role fills, writing its tiles at FL::T_OFF, and running one barrier per
+// step (the range's steps and the tail step) plus the epilogue's.
+template <typename ET, int W, int KS, int SG, int ZB, bool FUSED, class FL>
+__device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned char* smem, int tid,
+                                                uint32_t lb) {
   using F = BwdDxFast<KS, SG, ZB>;
   constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
-  constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF, T_OFF = F::T_OFF;
-  __shared__ __align__(16) unsigned char smem[F::BYTES];
+  constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF;
+  constexpr int T_OFF = FUSED ? FL::T_OFF : F::T_OFF;
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = lane >> 4;
   const int n = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int cs = p.cs0 + int(lb % uint32_t(p.nCsL));
   lb /= uint32_t(p.nCsL);
   const int tr = int(lb % uint32_t(p.nTr));
@@ -623,7 +648,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
       }
     }
   }
-  issue(0, t_first);
+  if constexpr (!FUSED) issue(0, t_first);
 
   // ---- per-lane LDS offsets ----
   const int xc = 2 * wv + (q >> 1);  // logical 16-byte chunk of the lane's 4 channels
@@ -631,6 +656,46 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
   int zr[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) zr[ks] = 4 * n * ZROW + ((4 * ks + q + n) % ZCPR) * 16;
+  // dy row 4n + j and the chunk 4 ks + q of z row 4n + j inside a step's stage: rotation
+  // row / 4 in the kernel's own stages, the shared one in the fused kernel's
+  auto dy_at = [&](int j) -> int {
+    if constexpr (FUSED) {
+      const int r = 4 * n + j;
+      return r * XROW + ((xc + rot_fused(r)) & (XCPR - 1)) * 16 + 8 * (q & 1);
+    } else {
+      return drd + j * XROW;
+    }
+  };
+  // byte offsets of step s's dy, z and id stages
+  auto dy_stage = [&](int s) -> int {
+    if constexpr (FUSED) {
+      return FL::D_OFF + (s % FL::SN) * FL::STAGE;
+    } else {
+      return (s & 1) * XSTAGE;
+    }
+  };
+  auto z_stage = [&](int s) -> int {
+    if constexpr (FUSED) {
+      return FL::Z_OFF + (s % FL::SN) * FL::ZSTAGE;
+    } else {
+      return Z_OFF + (s & 1) * ZSTAGE;
+    }
+  };
+  auto id_stage = [&](int s) -> int {
+    if constexpr (FUSED) {
+      return FL::S_OFF + (s % FL::SN) * FL::SSTAGE;
+    } else {
+      return F::S_OFF + (s & 1) * F::SSTAGE;
+    }
+  };
+  auto z_at = [&](int j, int ks) -> int {
+    if constexpr (FUSED) {
+      const int r = 4 * n + j;
+      return r * ZROW + ((4 * ks + q + rot_fused(r)) % ZCPR) * 16;
+    } else {
+      return zr[ks] + j * ZROW;
+    }
+  };
   // dx tile row of the lane's output j: token 4n + j sits in row 4n + j + 3; lane 15's
   // outputs 1..3 are the previous step's tokens 61..63, rows 0..2
   int trow[4];
@@ -679,15 +744,17 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
     } else {
       vm_wait_barrier<0>();
     }
-    if (s < nsteps) issue(u ^ 1, t0 + kStep);
+    if constexpr (!FUSED) {
+      if (s < nsteps) issue(u ^ 1, t0 + kStep);
+    }
     if (s > 0) tflush(u ^ 1, s - 1, t0 - kStep);
     // dy of the lane's tokens 4n .. 4n+3, 4 channels; zero at or past T
     float dyv[4][4];
     {
-      const unsigned char* ds = smem + u * XSTAGE + drd;
+      const unsigned char* ds = smem + dy_stage(s);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(ds + j * XROW);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(ds + dy_at(j));
         dyv[j][0] = Cvt<ET>::lo(v[0]);
         dyv[j][1] = Cvt<ET>::hi(v[0]);
         dyv[j][2] = Cvt<ET>::lo(v[1]);
@@ -702,19 +769,19 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
         }
       }
     }
-    const unsigned char* zs = smem + Z_OFF + u * ZSTAGE;
+    const unsigned char* zs = smem + z_stage(s);
     // ids of rows 4n - 4 .. 4n + 3 (SG): the term of tap k of token 4n + jp is kept when
     // row 4n + jp - k has the id of row 4n + jp
     int idv[8] = {};
     if constexpr (SG) {
-      const int* ids = reinterpret_cast<const int*>(smem + F::S_OFF + u * F::SSTAGE) + 4 * n;
+      const int* ids = reinterpret_cast<const int*>(smem + id_stage(s)) + 4 * n;
 #pragma unroll
       for (int i = 0; i < 8; ++i) idv[i] = ids[i];
     }
     auto gen = [&](int j, f32x4_t (&acc)[4]) {
       u16x8_t bfr[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8_t*>(zs + zr[ks] + j * ZROW);
+      for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8_t*>(zs + z_at(j, ks));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         acc[mt] = mma32<ET>(afr[mt][0], bfr[0], binit[mt]);
@@ -773,7 +840,20 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams
   }
   __syncthreads();
   tflush(nsteps & 1, nsteps, t_first + nsteps * kStep);
+  if constexpr (FUSED) {
+    // the filter-gradient role's epilogue: two barriers per chunk of its partial sums
+    constexpr int RT = 2 * KS, TPC = RT < 4 ? RT : 4;
+#pragma unroll
+    for (int c = 0; c < 2 * (RT / TPC); ++c) __syncthreads();
+  }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+template <typename ET, int W, int KS, int SG, int ZB>
+__global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams p) {
+  using F = BwdDxFast<KS, SG, ZB>;
+  __shared__ __align__(16) unsigned char smem[F::BYTES];
+  lowrank_dx_role<ET, W, KS, SG, ZB, false, F>(p, smem, threadIdx.x, xcd_logical_block(blockIdx.x, gridDim.x));
 }
 
 
@@ -855,21 +935,24 @@ struct BwdGduFast {
   static constexpr int XI = 2, DI = 2, ZI = kStep * ZROW / (64 * ZB) / 4, ND = XI + DI + ZI + SG;
 };
 
-template <typename ET, int W, int KS, int SG, int ZB>
-__global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParams p) {
-  using F = BwdGduFast<KS, SG, ZB>;
+// The g / dU / db partial sums. Standalone (FUSED false): its own kernel with layout
+// BwdGduFast. FUSED: waves 4..7 of the fused backward with layout BwdFused, which also
+// stage dy and z for the tail step (s == nsteps) that the dx role needs, stay in step with
+// it (one barrier per step, the tail included) and meet its epilogue barriers.
+template <typename ET, int W, int KS, int SG, int ZB, bool FUSED, class F>
+__device__ __forceinline__ void lowrank_gdu_role(const LowRankParams& p, unsigned char* smem, int tid,
+                                                 uint32_t lb) {
   constexpr int CPR = F::CPR, ROW = F::ROW, STAGE = F::STAGE, XN = F::XN;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, D_OFF = F::D_OFF, Z_OFF = F::Z_OFF;
   constexpr int RT = 2 * KS;  // 16-rank tiles
   constexpr int HR = W - 1;
-  __shared__ __align__(16) unsigned char smem[F::BYTES];
+  constexpr int TAIL = FUSED ? 1 : 0;  // the dx role's tail step
+  auto rot = [](int row) { return FUSED ? rot_fused(row) : rot_double(row); };
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = lane >> 4;
   const int j = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int cs = int(lb % uint32_t(p.nCsL));
   lb /= uint32_t(p.nCsL);
   const int tr = int(lb % uint32_t(p.nTr));
@@ -890,14 +973,14 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
   for (int i = 0; i < 2; ++i) {
     const int idx = (wv + 4 * i) * 64 + lane;
     const int rl = idx / CPR, pc = idx % CPR;
-    const int c = (pc - 2 * rl) & (CPR - 1);
+    const int c = (pc - rot(rl)) & (CPR - 1);
     arl[i] = rl;
     xoff[i] = uint32_t(rl * int(p.xs1) + 8 * c) * 2u;
     doff[i] = uint32_t(rl * int(p.dys1) + 8 * c) * 2u;
   }
 #pragma unroll
   for (int i = 0; i < F::ZI; ++i) {
-    const ZPiece zp = z_piece<ZB, ZROW>((wv + 4 * i) * 64 + lane, p.R, rot_double);
+    const ZPiece zp = z_piece<ZB, ZROW>((wv + 4 * i) * 64 + lane, p.R, FUSED ? rot_fused : rot_double);
     zrl[i] = zp.row;
     zval[i] = zp.valid;
     zoff[i] = uint32_t(zp.row * int(p.zs1)) * 2u + uint32_t(zp.byte);
@@ -948,7 +1031,7 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
     if (t_first > 0) {
       if (wv == 0 && lane < HR * CPR) {
         const int rl = kStep - HR + lane / CPR, pc = lane % CPR;
-        const int c = (pc - 2 * rl) & (CPR - 1);
+        const int c = (pc - rot(rl)) & (CPR - 1);
         dma16(xc + (int64_t(t_first - HR + lane / CPR) * p.xs1 + 8 * c) * 2, hbase);
       }
     } else if (tid < HR * ROW / 4) {
@@ -956,18 +1039,18 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
     }
   }
   issue(0, t_first);
-  if (F::DIST > 1 && nsteps > 1) issue(1, t_first + kStep);
+  if (F::DIST > 1 && nsteps + TAIL > 1) issue(1, t_first + kStep);
 
   // Transposing-read addresses. Lane (j, q) reads 8 bytes of row 8q + j/4 (+ 4), channel
   // columns 16 wv + 4 (j % 4) .. + 3; lane i then holds column 16 wv + i of 4 rows.
   const int trow = 8 * q + (j >> 2);
   const int tch = 2 * wv + ((j & 3) >> 1);  // logical 16-byte chunk
   const int thalf = 8 * (j & 1);
-  auto arow = [&](int row) { return row * ROW + ((tch + 2 * row) & (CPR - 1)) * 16 + thalf; };
+  auto arow = [&](int row) { return row * ROW + ((tch + rot(row)) & (CPR - 1)) * 16 + thalf; };
   // z: lane holds rank column 16 rt + i
   auto zaddr = [&](int row, int rt) {
     const int c = 2 * rt + ((j & 3) >> 1);
-    return row * ZROW + ((c + 2 * row) % ZCPR) * 16 + thalf;
+    return row * ZROW + ((c + rot(row)) % ZCPR) * 16 + thalf;
   };
 
   f32x4_t dU[W][RT];
@@ -983,16 +1066,17 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
   constexpr int NR = 5 + 2 * RT;  // transposing reads per K step: dy 2, x 3, z 2 per rank tile
   auto bf = [](const u32x2& w, int e) { return (e & 1) ? Cvt<ET>::hi(w[e >> 1]) : Cvt<ET>::lo(w[e >> 1]); };
 
-  for (int s = 0; s < nsteps; ++s) {
+  for (int s = 0; s < nsteps + TAIL; ++s) {
     const int t0 = t_first + s * kStep;
     // this step's transfers were followed by the next step's, if there is one (loading two
     // steps ahead); loading one step ahead, nothing newer is in flight
-    if (F::DIST > 1 && s + 1 < nsteps) {
+    if (F::DIST > 1 && s + 1 < nsteps + TAIL) {
       vm_wait_barrier<F::ND>();
     } else {
       vm_wait_barrier<0>();
     }
-    if (s + F::DIST < nsteps) issue(s + F::DIST, t0 + F::DIST * kStep);
+    if (s + F::DIST < nsteps + TAIL) issue(s + F::DIST, t0 + F::DIST * kStep);
+    if (FUSED && s == nsteps) continue;  // the tail step's rows are the dx role's alone
     const int ux = s % XN;
     const uint32_t dsa = lds0 + D_OFF + (s % F::SN) * STAGE;
     const uint32_t zsa = lds0 + Z_OFF + (s % F::SN) * ZSTAGE;
@@ -1098,6 +1182,10 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
   constexpr int PITCH = COLS + 1;
   constexpr int TPC = RT < 4 ? RT : 4;  // rank tiles per chunk
   static_assert(16 * TPC * PITCH * 4 <= F::BYTES, "staging fits the stages");
+  if constexpr (FUSED) {
+    static_assert(16 * TPC * PITCH * 4 <= F::T_OFF, "the staging leaves the dx tiles alone");
+    __syncthreads();  // the dx role's last tile is complete before its final stores
+  }
   // Head-wise generation (H consecutive channels share a group's columns, H <= 16): the H
   // channels of a group are summed here, in channel order, so that one partial per
   // (sequence, token range) and group column is written.
@@ -1153,6 +1241,35 @@ __global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParam
       for (int m = 1; m < H; m <<= 1) v += __shfl_xor(v, m, 64);  // the group's lanes j
       if (q == 0 && (j & (H - 1)) == 0) p.part_db[int64_t(range) * p.J + int64_t((cw + j) >> hsh) * W + k] = v;
     }
+  }
+}
+
+template <typename ET, int W, int KS, int SG, int ZB>
+__global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParams p) {
+  using F = BwdGduFast<KS, SG, ZB>;
+  __shared__ __align__(16) unsigned char smem[F::BYTES];
+  lowrank_gdu_role<ET, W, KS, SG, ZB, false, F>(p, smem, threadIdx.x, xcd_logical_block(blockIdx.x, gridDim.x));
+}
+
+// ---------------------------------------------------------------------------------
+// Fused backward, k_lowrank_bwd_fast: dx and the g / dU / db partial sums in one pass over
+// x, dy and z. A workgroup of 8 waves owns one (sequence, token range, 64-channel slice):
+// waves 4..7 stage x (a ring of 4 steps), dy and z (3 stages each) by LDS DMA two steps
+// ahead and form the partial sums (lowrank_gdu_role); waves 0..3 form dx from the same dy
+// and z stages (lowrank_dx_role). Each role runs its own loop, so the two roles' registers
+// are never live together; both loops run the range's steps plus dx's tail step with one
+// barrier each, and the epilogues meet at the same barriers. dy and z are read from memory
+// once instead of twice.
+// ---------------------------------------------------------------------------------
+template <typename ET, int W, int KS, int SG, int ZB>
+__global__ __launch_bounds__(512) void k_lowrank_bwd_fast(const LowRankParams p) {
+  using FL = BwdFused<KS, SG, ZB>;
+  __shared__ __align__(16) unsigned char smem[FL::BYTES];
+  const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (__builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 8) == 0) {
+    lowrank_dx_role<ET, W, KS, SG, ZB, true, FL>(p, smem, int(threadIdx.x) & 255, lb);
+  } else {
+    lowrank_gdu_role<ET, W, KS, SG, ZB, true, FL>(p, smem, int(threadIdx.x) & 255, lb);
   }
 }
 
@@ -1347,6 +1464,47 @@ hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, dynconv_dt
       case 2: return bwd_gdu_ks<ET, 2>(q, blocks, s);
       case 3: return bwd_gdu_ks<ET, 3>(q, blocks, s);
       case 4: return bwd_gdu_ks<ET, 4>(q, blocks, s);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return dt == DYNCONV_F16 ? by_w(f16_t{}) : by_w(bf16_t{});
+}
+
+template <typename ET, int W, int KS, int ZB>
+hipError_t bwd_fused_zb(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_lowrank_bwd_fast<ET, W, KS, 1, ZB>), dim3(unsigned(blocks)), dim3(512), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_lowrank_bwd_fast<ET, W, KS, 0, ZB>), dim3(unsigned(blocks)), dim3(512), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename ET, int W>
+hipError_t bwd_fused_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  const bool z16 = z_pieces16(p);
+  switch ((p.R + 31) / 32) {
+    case 1: return z16 ? bwd_fused_zb<ET, W, 1, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 1, 4>(p, blocks, s);
+    case 2: return z16 ? bwd_fused_zb<ET, W, 2, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 2, 4>(p, blocks, s);
+    case 4: return z16 ? bwd_fused_zb<ET, W, 4, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 4, 4>(p, blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_lowrank_bwd_fused(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t s) {
+  // one workgroup of 8 waves per (sequence, planned token range, 64-channel slice)
+  LowRankParams q = p;
+  q.cs0 = 0;
+  q.nCsL = p.D / 64;
+  q.nCs = q.nCsL;
+  const int64_t blocks = int64_t(p.B) * p.nTr * q.nCsL;
+  auto by_w = [&](auto tag) -> hipError_t {
+    using ET = decltype(tag);
+    switch (W) {
+      case 1: return bwd_fused_ks<ET, 1>(q, blocks, s);
+      case 2: return bwd_fused_ks<ET, 2>(q, blocks, s);
+      case 3: return bwd_fused_ks<ET, 3>(q, blocks, s);
+      case 4: return bwd_fused_ks<ET, 4>(q, blocks, s);
       default: return hipErrorInvalidValue;
     }
   };

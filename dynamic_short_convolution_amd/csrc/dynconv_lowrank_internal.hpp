@@ -93,6 +93,9 @@ hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, dynconv_dty
 // planned token ranges (Ltok, nTr) and 64-channel slices; one partial per token range and
 // group column (a group's H channels summed inside the workgroup).
 hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
+// The same two computations in one kernel (8 waves: dx and g / dU / db roles sharing the
+// staged dy and z), over the planned token ranges and 64-channel slices.
+hipError_t launch_lowrank_bwd_fused(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
 // Whether the backward runs on the fast kernels (dx, then g / dU / db): they write
 // B * nTr partials per filter column, the general kernel B * nTr * H.
 bool lowrank_bwd_fast(const LowRankParams& p, int W, dynconv_dtype dt);

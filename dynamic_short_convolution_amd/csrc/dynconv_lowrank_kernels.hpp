@@ -1636,9 +1636,7 @@ hipError_t lr_bwd_inst(const LowRankParams& p, const LowRankPlan& pl, hipStream_
   const bool vec = p.act16 != 0 && p.z16 != 0 && p.R % 32 == 0;
   const int nfull = fast ? pl.nCs : vec ? p.D / lowrank_bwd_dc(W, KS) : 0;
   if (fast) {
-    hipError_t e = launch_lowrank_bwd_dx_fast(p, W, dt, s);
-    if (e != hipSuccess) return e;
-    e = launch_lowrank_bwd_gdu_fast(p, W, dt, s);
+    const hipError_t e = launch_lowrank_bwd_fused(p, W, dt, s);
     if (e != hipSuccess) return e;
   } else if (nfull > 0) {
     q.cs0 = 0;
