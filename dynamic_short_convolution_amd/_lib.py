@@ -139,11 +139,12 @@ class DynconvError(RuntimeError):
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
-    """Loads libdynconv.so once; raises if it is missing."""
+    """Loads libdynconv.so once (or the file DYNCONV_LIBRARY names, such as the host-only
+    sanitized build); raises if it is missing."""
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    path = path or os.environ.get("DYNCONV_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is not built; run `python -m dynamic_short_convolution_amd.build` "

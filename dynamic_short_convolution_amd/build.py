@@ -74,6 +74,63 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host-side code only, with AddressSanitizer and UndefinedBehaviorSanitizer on the host
+# compile. Each object embeds the same device bundle of an empty source file instead of its
+# kernels, so the library registers no kernels: only argument checking, planning and size
+# queries can run (a launch would fail). Loaded with the clang ASan runtime
+# preloaded (SANITIZER_RUNTIME) by a process that selects it through DYNCONV_LIBRARY.
+ASAN_DIR = os.path.join(PKG_DIR, "_build_asan")
+ASAN_LIB_PATH = os.path.join(ASAN_DIR, "libdynconv_hostsan.so")
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang ASan runtime matching hipcc's compiler."""
+    res = subprocess.run([os.path.join(os.path.dirname(HIPCC), "..", "lib", "llvm", "bin", "clang"),
+                          "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"no ASan runtime found ({res.stdout} {res.stderr})")
+    return path
+
+
+def build_host_sanitized() -> str:
+    """Builds the host-only sanitized library; returns its path."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    empty_src = os.path.join(ASAN_DIR, "empty.hip")
+    empty_bin = os.path.join(ASAN_DIR, "empty.fatbin")
+    with open(empty_src, "w") as f:
+        f.write("// no kernels\n")
+    cmd = [HIPCC, "-x", "hip", "--offload-arch=gfx950", "--cuda-device-only", "--no-offload-new-driver", "-c",
+           empty_src, "-o", empty_bin]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"empty device bundle failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+
+    def one(src: str) -> str:
+        obj = os.path.join(ASAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, "-x", "hip", "--cuda-host-only", "--no-offload-new-driver", "-Xclang", "-fcuda-include-gpubinary",
+               "-Xclang", empty_bin, "-O1", "-g", "-std=c++17", "-fPIC", *SANITIZE_FLAGS, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    cmd = [HIPCC, "-shared", "-fPIC", *SANITIZE_FLAGS, "-shared-libasan", *objs, "-o", ASAN_LIB_PATH]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return ASAN_LIB_PATH
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -54,6 +54,13 @@ dynconv_status check_common(int64_t B, int64_t T, int64_t D, int32_t W, int32_t 
   if (D > 0 && D % H != 0) return DYNCONV_ERR_INVALID_ARG;
   if (H > 1 && !is_pow2(H)) return DYNCONV_ERR_UNSUPPORTED;
   if (B > INT32_MAX || T > INT32_MAX || D > INT32_MAX) return DYNCONV_ERR_UNSUPPORTED;
+  // Token indices, and a token plus a step of lookahead, stay in int; so do the filter
+  // column counts (D/H)*W.
+  if (T > INT32_MAX - 65536 || D * W > INT32_MAX) return DYNCONV_ERR_UNSUPPORTED;
+  // Every kernel's workgroup covers at least 16 tokens (or all of T) and 16 channels (or
+  // all of D), so this bounds every grid by INT32_MAX workgroups.
+  const int64_t bt = B * ((T + 15) / 16);
+  if (bt > 0 && (D + 15) / 16 > INT32_MAX / bt) return DYNCONV_ERR_UNSUPPORTED;
   return DYNCONV_OK;
 }
 
@@ -476,6 +483,8 @@ dynconv_status check_lowrank(const void* x, const int64_t* xs, const void* z, co
   if (zs[0] < 0 || zs[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
   if (U == nullptr) return DYNCONV_ERR_INVALID_ARG;
   if (ldu < (D / H) * W) return DYNCONV_ERR_INVALID_ARG;
+  if (xs[1] >= kLowrankMaxRowStride || zs[1] >= kLowrankMaxRowStride || ldu >= kLowrankMaxRowStride)
+    return DYNCONV_ERR_UNSUPPORTED;
   return DYNCONV_OK;
 }
 
@@ -520,6 +529,7 @@ dynconv_status lowrank_fwd_impl(const void* x, const int64_t* xs, const void* z,
   dynconv_status st = check_lowrank(x, xs, z, zs, U, ldu, B, T, D, W, H, R, dtype);
   if (st != DYNCONV_OK) return st;
   if ((st = check_act(y, ys, true)) != DYNCONV_OK) return st;
+  if (ys[1] >= kLowrankMaxRowStride) return DYNCONV_ERR_UNSUPPORTED;
   if (y == x || y == z || y == U || (bias != nullptr && y == bias)) return DYNCONV_ERR_INVALID_ARG;
   if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
   const int eb = elem_bytes(dtype);
@@ -584,6 +594,7 @@ dynconv_status lowrank_bwd_impl(const void* x, const int64_t* xs, const void* z,
   if ((st = check_act(dx, dxs, true)) != DYNCONV_OK) return st;
   if (dz == nullptr || dzs == nullptr || dU == nullptr) return DYNCONV_ERR_INVALID_ARG;
   if (dzs[2] != 1 || dzs[0] < 0 || dzs[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
+  if (dys[1] >= kLowrankMaxRowStride || dxs[1] >= kLowrankMaxRowStride) return DYNCONV_ERR_UNSUPPORTED;
   const void* ins[5] = {x, z, U, bias, dy};
   const void* outs[4] = {dx, dz, dU, db};
   for (const void* o : outs) {

@@ -59,15 +59,19 @@
 extern "C" {
 #endif
 
-typedef enum { DYNCONV_F32 = 0, DYNCONV_BF16 = 1, DYNCONV_F16 = 2 } dynconv_dtype;
+/* Element type codes and status codes are plain 32-bit integers, so that any value a caller
+ * passes is well defined (an unknown dtype code is refused with DYNCONV_ERR_INVALID_ARG). */
+typedef int32_t dynconv_dtype;
+enum { DYNCONV_F32 = 0, DYNCONV_BF16 = 1, DYNCONV_F16 = 2 };
 
-typedef enum {
+typedef int32_t dynconv_status;
+enum {
   DYNCONV_OK = 0,
   DYNCONV_ERR_INVALID_ARG = 1, /* null / negative / inconsistent argument, aliasing */
   DYNCONV_ERR_UNSUPPORTED = 2, /* valid per the equations but outside this library's limits */
   DYNCONV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query */
   DYNCONV_ERR_HIP = 4          /* a HIP launch failed */
-} dynconv_status;
+};
 
 /* Human-readable name of a status code (static storage). */
 const char* dynconv_status_string(dynconv_status s);
@@ -114,6 +118,8 @@ size_t dynconv_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, in
  *   z     [B,T,R] with strides zs
  *   U     [R, (D/H)*W] with row stride ldu (elements), column j = g*W + k
  *   bias  [(D/H)*W] or NULL (zero bias)
+ * Row strides (xs[1], zs[1], ys[1], ldu; and dys[1], dxs[1] of the backward) must be below
+ * 2^24 elements (DYNCONV_ERR_UNSUPPORTED otherwise).
  */
 dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
                                    const void* U, int64_t ldu, const void* bias, void* y, const int64_t* ys,

@@ -1,0 +1,606 @@
+"""Host emulation of the global-memory accesses of the DMA-staged and chunk-loop kernels.
+
+Each emulator restates, for every workgroup, wave, lane and pipeline step of one launch,
+the index arithmetic of one kernel's loads and stores (the expressions of the kernel
+source, with its variable names) and records every access as
+(tensor, sequence b, row t, first element of the row, width in elements). `Accesses.check`
+then asserts that each access lies inside its tensor's logical extent [B, T, C], so that a
+strided view's gaps and the rows of other sequences count as outside too. Pieces that a
+kernel reads from a static zero word, and stores that the hardware drops (buffer stores
+past the resource's extent, whose own bound is checked), are counted, not recorded.
+Offsets that a kernel forms in 32-bit arithmetic are recorded with `int32` and checked to
+stay in range (below 2^31, or 2^32 where the kernel takes them as unsigned).
+
+Kernels (dynamic_short_convolution_amd/csrc):
+  k_gemm_conv            projection + convolution (per-token or low-rank filters)
+  k_lowrank_fwd_fast     low-rank forward, LDS DMA ring
+  k_lowrank_bwd_fast     fused low-rank backward: dx role and filter-gradient role
+  k_lowrank_dz_dma       dz over whole 64-token blocks, LDS DMA stages
+  k_lowrank_fwd          general low-rank forward (16-token tiles, register staging)
+  k_lowrank_bwd          general low-rank backward (64-token steps; FAST and masked
+                         loads, including the surplus threads' "safe" chunk)
+"""
+from __future__ import annotations
+
+from collections import defaultdict
+
+import numpy as np
+
+STEP = 64  # tokens per pipeline step (fast kernels, general backward, dz blocks)
+TT = 16  # tokens per tile of the general forward
+HALO = 4  # rows before a range that the general kernels stage (W - 1 for W = 5)
+I32 = 1 << 31
+U32 = 1 << 32
+MAX_ROW_STRIDE = 1 << 24  # the ABI's bound on the low-rank form's row strides
+
+
+def xcd_logical_block(bid, n):
+    """The kernels' XCD-grouping map of workgroup ids (a bijection of 0 .. n-1)."""
+    bid = np.asarray(bid)
+    q, r = n // 8, n % 8
+    x = bid % 8
+    return x * q + np.minimum(x, r) + bid // 8
+
+
+class Accesses:
+    def __init__(self):
+        self.spans = defaultdict(list)
+        self.zero = 0  # pieces read from a static zero word
+        self.dropped = 0  # 16-byte stores past a buffer resource's extent
+        self.i32 = []  # (what, max, min, limit)
+
+    def add(self, name, b, t, c0, width):
+        b, t, c0, width = np.broadcast_arrays(np.asarray(b), np.asarray(t), np.asarray(c0), np.asarray(width))
+        if b.size:
+            self.spans[name].append((b.ravel().astype(np.int64), t.ravel().astype(np.int64),
+                                     c0.ravel().astype(np.int64), width.ravel().astype(np.int64)))
+
+    def int32(self, what, values, limit=I32):
+        v = np.asarray(values, dtype=np.int64)
+        if v.size:
+            self.i32.append((what, int(v.max()), int(v.min()), limit))
+
+    def check(self, extents):
+        """extents: tensor name -> (B, T, C). Raises AssertionError naming the first bad access."""
+        for what, hi, lo, limit in self.i32:
+            assert lo >= 0 and hi < limit, f"32-bit offset {what} reaches {lo} .. {hi} (limit {limit})"
+        for name, lst in self.spans.items():
+            B, T, C = extents[name]
+            for b, t, c0, w in lst:
+                bad = (b < 0) | (b >= B) | (t < 0) | (t >= T) | (c0 < 0) | (w < 1) | (c0 + w > C)
+                if np.any(bad):
+                    i = int(np.argmax(bad))
+                    raise AssertionError(f"{name}: access b={b[i]} t={t[i]} elements {c0[i]}..{c0[i] + w[i] - 1}"
+                                         f" outside [B={B}, T={T}, C={C}]")
+        return True
+
+    def cover(self, name, B, T, C):
+        """Boolean [B, T, C] map of the elements a tensor's accesses touch."""
+        m = np.zeros((B, T, C), dtype=bool)
+        for b, t, c0, w in self.spans.get(name, []):
+            for wv in np.unique(w):
+                sel = w == wv
+                for k in range(int(wv)):
+                    m[b[sel], t[sel], c0[sel] + k] = True
+        return m
+
+
+def _log2(h):
+    assert h >= 1 and h & (h - 1) == 0
+    return h.bit_length() - 1
+
+
+# ---------------------------------------------------------------------------------------
+# k_gemm_conv: 256 computed rows (16 of them the halo of the next 240) x 128 columns per
+# workgroup, K in steps of 64, 8 waves (4 along the rows, 2 along the columns)
+# ---------------------------------------------------------------------------------------
+
+def gemm_conv(B, T, K, N, W, H, R=0, lowrank=False, zvec=True, uvec=True, has_bias=True):
+    GBM, GHALO, GBN, GKT, GNT = 256, 16, 128, 64, 512
+    GBMO = GBM - GHALO
+    M = B * T
+    nTm, nTn = (M + GBMO - 1) // GBMO, N // GBN
+    nk = K // GKT
+    CPR = GKT // 8
+    AI, BI = GBM * GKT * 2 // 16 // GNT, GBN * GKT * 2 // 16 // GNT
+    hsh = _log2(H)
+    acc = Accesses()
+    nblk = nTm * nTn
+    lb = xcd_logical_block(np.arange(nblk), nblk)
+    per_group = 8 * nTn
+    grp, rem = lb // per_group, lb % per_group
+    rows_in_grp = np.minimum(8, nTm - 8 * grp)
+    tm = 8 * grp + rem % rows_in_grp
+    tn = rem // rows_in_grp
+    assert len(set(zip(tm.tolist(), tn.tolist()))) == nblk, "tile map is not a bijection"
+    assert tm.max() < nTm and tn.max() < nTn
+    m0 = tm * GBMO - GHALO
+    n0 = tn * GBN
+    swz = (lambda r: r & 7) if GKT == 64 else (lambda r: (r >> 2) & 3)
+    for wv in range(8):
+        for i in range(AI):
+            pidx = (wv + 8 * i) * 64 + np.arange(64)
+            row, c = pidx // CPR, (pidx % CPR) ^ swz(pidx // CPR)
+            m = np.clip(m0[:, None] + row[None, :], 0, M - 1)
+            for s in range(nk):
+                acc.add("A", m // T, m % T, 8 * c[None, :] + s * GKT, 8)
+        for i in range(BI):
+            pidx = (wv + 8 * i) * 64 + np.arange(64)
+            row, c = pidx // CPR, (pidx % CPR) ^ swz(pidx // CPR)
+            for s in range(nk):
+                acc.add("Wp", 0, n0[:, None] + row[None, :], 8 * c[None, :] + s * GKT, 8)
+    # epilogue: tile row r is token m0 + r (clamped into 0 .. M-1 for loads)
+    r = np.arange(GBM)
+    m = m0[:, None] + r[None, :]
+    mc = np.clip(m, 0, M - 1)
+    out = (r[None, :] >= GHALO) & (m < M)
+    acc.add("y", (mc // T)[out], (mc % T)[out], np.broadcast_to(n0[:, None], m.shape)[out], GBN)
+    bb, tt = (mc // T)[:, :, None], (mc % T)[:, :, None]
+    col = n0[:, None, None] + np.arange(GBN)[None, None, :]
+    if not lowrank:
+        acc.add("w", bb, tt, (col >> hsh) * W, W)
+        return acc
+    KS = (R + 31) // 32
+    # z fragments of every tile row: ranks 32 ks + 8 q (+ e) below R
+    ranks = np.arange(32 * KS)
+    if zvec:
+        acc.add("z", bb, tt, ranks[(ranks % 8 == 0) & (ranks < R)][None, None, :], 8)
+    else:
+        acc.add("z", bb, tt, ranks[ranks < R][None, None, :], 1)
+    # U: the tile's columns (groups G0 .. G0 + 128/H - 1, all taps), rank rows below R
+    G0 = n0 // H
+    ucols = (GBN >> hsh) * W
+    assert ucols % 8 == 0
+    rr = np.arange(R)
+    if uvec:
+        ch = np.arange(ucols // 8)
+        acc.add("U", 0, rr[None, :, None], (G0 * W)[:, None, None] + 8 * ch[None, None, :], 8)
+    else:
+        acc.add("U", 0, rr[None, :, None], (G0 * W)[:, None, None] + np.arange(ucols)[None, None, :], 1)
+    if has_bias:
+        acc.add("bias", 0, 0, (col[:, 0, :] >> hsh) * W, W)
+    return acc
+
+
+# ---------------------------------------------------------------------------------------
+# fast low-rank kernels (64 channels per workgroup, 64-token steps staged by LDS DMA)
+# ---------------------------------------------------------------------------------------
+
+def rot_quarter(r):
+    return r >> 2
+
+
+def rot_double(r):
+    return 2 * r
+
+
+def rot_fused(r):
+    return 2 * r + (r >> 2)
+
+
+def z_pieces(ZB, KS, R, rot):
+    """(row, first element, valid) of every z piece of a stage (piece idx = (wv + 4 i) 64 + lane)."""
+    ZROW = 16 * 4 * KS
+    ZCPR = ZROW // 16
+    idx = np.arange(STEP * ZROW // ZB)
+    o = idx * ZB
+    row, ob = o // ZROW, o % ZROW
+    c = ((ob // 16 - rot(row)) % ZCPR + ZCPR) % ZCPR
+    gb = 16 * c + (ob & 15)
+    return row, gb // 2, gb // 2 < R
+
+
+def step_rows(t0, rl, T):
+    """Row that staged row rl of the step at t0 reads: rows past T - 1 read row T - 1."""
+    if t0 + STEP <= T:
+        return t0 + rl
+    return np.minimum(t0 + rl, T - 1)
+
+
+def _x_chunks(rot):
+    """(row, logical chunk) of the 512 x (or dy) pieces of a step: 8 chunks of a 64-channel row."""
+    idx = np.arange(STEP * 8)
+    rl, pc = idx // 8, idx % 8
+    return rl, (pc - rot(rl)) & 7
+
+
+def _seg_loads(acc, b, t0, T):
+    sc = np.arange(17)  # id chunk sc: tokens t0 - 4 + 4 sc .. + 3, clamped into 0 .. T - 4
+    tk = np.minimum(np.maximum(t0 - 4 + 4 * sc, 0), T - 4)
+    acc.add("seg", b, tk, 0, 1)
+    acc.add("seg", b, tk + 3, 0, 1)
+
+
+def _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias):
+    """U^T rows and bias of the 64 channels: rank rows clamped to R - 1, taps to W - 1; U
+    stands in for a missing bias (element 0 .. W - 1)."""
+    hsh = _log2(H)
+    ch = c_base + np.arange(64)
+    r = np.minimum(np.arange(32 * KS), R - 1)
+    acc.add("U", 0, r[:, None], ((ch >> hsh) * W)[None, :], W)
+    if has_bias:
+        acc.add("bias", 0, 0, (ch >> hsh) * W, W)
+    else:
+        acc.add("U", 0, 0, 0, W)
+
+
+def _fast_offsets(acc, what, stride):
+    # (rl * int(stride) + 8 c) as int, then times 2 as unsigned; rl < 64
+    acc.int32(what + " (elements, int)", 63 * stride + 56)
+    acc.int32(what + " (bytes, unsigned)", (63 * stride + 56) * 2 + 16, U32)
+
+
+def plan_fwd_fast(B, T, D, KS):
+    lds = 3 * 8192 + 2 * STEP * 64 * KS + 2 * 8192 + 3 * 320  # with the id stages
+    resident = min(160 * 1024 // lds, 2)
+    nCs = D // 64
+    per_seq = (256 * resident + B * nCs - 1) // (B * nCs)
+    per_seq = max(1, min(per_seq, (T + STEP - 1) // STEP))
+    L = (T + per_seq - 1) // per_seq
+    L = (L + STEP - 1) // STEP * STEP
+    return nCs, L, (T + L - 1) // L
+
+
+def fast_fwd_ok(T, D, W, H, R, xs1, zs1, os1):
+    KS = (R + 31) // 32
+    return (KS in (1, 2, 4) and R % 2 == 0 and 1 <= W <= 4 and H in (1, 2, 4, 8, 16) and D % 64 == 0
+            and (T + STEP) * os1 * 2 < I32 and STEP * xs1 < (1 << 30) and STEP * zs1 < (1 << 30))
+
+
+def lowrank_fwd_fast(B, T, D, W, H, R, ZB, xs1, zs1, os1, seg=False, has_bias=True):
+    assert fast_fwd_ok(T, D, W, H, R, xs1, zs1, os1) and (ZB == 4 or R % 8 == 0)
+    KS = (R + 31) // 32
+    nCs, L, nTr = plan_fwd_fast(B, T, D, KS)
+    acc = Accesses()
+    HR = W - 1
+    XD = 1  # x and z are fetched one step ahead
+    zrow, zel, zval = z_pieces(ZB, KS, R, rot_quarter)
+    rl, c = _x_chunks(rot_quarter)
+    _fast_offsets(acc, "x piece", xs1)
+    _fast_offsets(acc, "z piece", zs1)
+    nblk = B * nTr * nCs
+    assert sorted(xcd_logical_block(np.arange(nblk), nblk).tolist()) == list(range(nblk))
+    for lb in range(nblk):
+        cs, tr, b = lb % nCs, (lb // nCs) % nTr, lb // (nCs * nTr)
+        c_base, t_first = cs * 64, tr * L
+        t_end = min(T, t_first + L)
+        nsteps = (t_end - t_first + STEP - 1) // STEP
+        for s in range(nsteps + XD):  # the prologue's step 0 and, at step s, step s + 1
+            t0 = t_first + s * STEP
+            acc.add("x", b, step_rows(t0, rl, T), c_base + 8 * c, 8)
+            acc.add("z", b, step_rows(t0, zrow[zval], T), zel[zval], ZB // 2)
+            acc.zero += int((~zval).sum())
+            if seg:
+                _seg_loads(acc, b, t0, T)
+        if HR > 0 and t_first > 0:
+            acc.add("x", b, t_first - HR + np.arange(HR)[:, None], c_base + 8 * np.arange(8)[None, :], 8)
+        _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias)
+        # y: 16-byte pieces of rows t0 .. t0 + 63 through a buffer resource whose extent ends
+        # with row T - 1 (32-bit byte offsets ygo + t0 * ystep)
+        for s in range(nsteps):
+            t = t_first + s * STEP + np.arange(STEP)
+            keep = t < T
+            acc.add("y", b, t[keep][:, None], c_base + 8 * np.arange(8)[None, :], 8)
+            acc.dropped += int((~keep).sum()) * 8
+            acc.int32("y store offset", (t * os1 + c_base + 56) * 2)
+    acc.int32("y buffer extent", ((T - 1) * os1 + D) * 2)
+    return acc
+
+
+def plan_lowrank_bwd(B, T, D, W, H, R, lean):
+    """Token ranges of the backward (the lean plan where the fast kernels can serve it)."""
+    KS = (R + 31) // 32
+    WP = 8 if W > 4 else 4
+    DC = 4 * 2 * 16 // WP
+    nCs = (D + DC - 1) // DC
+    target = 512 if lean else 2048
+    slices = D // 64 if lean else nCs
+    per_seq = (target + B * slices - 1) // (B * slices)
+    per_seq = max(1, min(per_seq, (T + TT - 1) // TT))
+    L = (T + per_seq - 1) // per_seq
+    L = (L + STEP - 1) // STEP * STEP
+    return nCs, L, (T + L - 1) // L, DC, KS
+
+
+def fast_bwd_ok(T, D, W, H, R, xs1, zs1, dys1, os1):
+    KS = (R + 31) // 32
+    return (KS in (1, 2, 4) and R % 2 == 0 and 1 <= W <= 4 and H in (1, 2, 4, 8, 16) and D % 64 == 0
+            and (T + STEP) * os1 * 2 < I32 and STEP * dys1 < (1 << 30) and STEP * zs1 < (1 << 30)
+            and STEP * xs1 < (1 << 30))
+
+
+def lowrank_bwd_fused(B, T, D, W, H, R, ZB, xs1, zs1, dys1, os1, seg=False, has_bias=True, want_db=True):
+    assert fast_bwd_ok(T, D, W, H, R, xs1, zs1, dys1, os1) and (ZB == 4 or R % 8 == 0)
+    _, L, nTr, _, KS = plan_lowrank_bwd(B, T, D, W, H, R, lean=True)
+    slices = D // 64
+    acc = Accesses()
+    HR = W - 1
+    hsh = _log2(H)
+    zrow, zel, zval = z_pieces(ZB, KS, R, rot_fused)
+    rl, c = _x_chunks(rot_fused)
+    for what, st in (("x piece", xs1), ("dy piece", dys1), ("z piece", zs1)):
+        _fast_offsets(acc, what, st)
+    for lb in range(B * nTr * slices):
+        cs, tr, b = lb % slices, (lb // slices) % nTr, lb // (slices * nTr)
+        c_base, t_first = cs * 64, tr * L
+        t_end = min(T, t_first + L)
+        nsteps = (t_end - t_first + STEP - 1) // STEP
+        # filter-gradient role (waves 4..7): stages of steps 0 .. nsteps (dx's tail step too)
+        for s in range(nsteps + 1):
+            t0 = t_first + s * STEP
+            rows = step_rows(t0, rl, T)
+            acc.add("x", b, rows, c_base + 8 * c, 8)
+            acc.add("dy", b, rows, c_base + 8 * c, 8)
+            acc.add("z", b, step_rows(t0, zrow[zval], T), zel[zval], ZB // 2)
+            acc.zero += int((~zval).sum())
+            if seg:
+                _seg_loads(acc, b, t0, T)
+        if HR > 0 and t_first > 0:
+            acc.add("x", b, t_first - HR + np.arange(HR)[:, None], c_base + 8 * np.arange(8)[None, :], 8)
+        rng = b * nTr + tr
+        cols = (64 >> hsh) * W
+        acc.add("part_dU", 0, rng * R + np.arange(R)[:, None], (c_base >> hsh) * W + np.arange(0, cols, 4)[None, :], 4)
+        if want_db:
+            acc.add("part_db", 0, rng, (((c_base + np.arange(64)) >> hsh) * W)[:, None] + np.arange(W)[None, :], 1)
+        # dx role (waves 0..3): tile rows r of steps 0 .. nsteps are tokens t0 - 3 + r; the
+        # first step keeps rows >= 3, the tail rows < 3, the rest are pushed out (offset
+        # 0x80000000, past every extent)
+        _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias)
+        for s in range(nsteps + 1):
+            t0 = t_first + s * STEP
+            r = np.arange(STEP)
+            keep = ((s > 0) | (r >= 3)) & ((s < nsteps) | (r < 3))
+            t = t0 - 3 + r[keep]
+            inb = t < T
+            acc.add("dx", b, t[inb][:, None], c_base + 8 * np.arange(8)[None, :], 8)
+            acc.dropped += int((~inb).sum()) * 8
+            acc.int32("dx store offset", (t * os1 + c_base + 56) * 2)
+    acc.int32("dx buffer extent", ((T - 1) * os1 + D) * 2)
+    return acc, nTr
+
+
+# ---------------------------------------------------------------------------------------
+# k_lowrank_dz_dma: one workgroup per 64-token block inside T, chunks of CH filter groups
+# ---------------------------------------------------------------------------------------
+
+def dz_dma_shape(W, KS, HG):
+    GL = 8 if HG <= 4 else 32 // HG
+    CH = 4 * GL
+    CHC, UC = CH * HG, CH * W
+    RP = 32 * KS
+    UCPR, XCPR = UC // 8, CHC // 8
+    XR = STEP + HALO
+    UCH, XCH, DCH = RP * UCPR, XR * XCPR, STEP * XCPR
+    ni = lambda n: (n + 63) // 64  # noqa: E731
+    stage = (ni(UCH) + ni(XCH) + ni(DCH)) * 64 * 16
+    ok = (GL * W) % 8 == 0 and 3 * stage <= 150 * 1024
+    return dict(GL=GL, CH=CH, CHC=CHC, UC=UC, UCPR=UCPR, XCPR=XCPR, XR=XR, UCH=UCH, XCH=XCH, DCH=DCH, ok=ok)
+
+
+def dz_dma(B, T, D, W, H, R, xs1, dys1, ldu):
+    KS = (R + 31) // 32
+    S = dz_dma_shape(W, KS, H)
+    assert S["ok"] and D % S["CHC"] == 0
+    nchunk = D // S["CHC"]
+    acc = Accesses()
+    pidx = np.arange(S["UCH"])
+    r, pc = pidx // S["UCPR"], pidx % S["UCPR"]
+    uz = r >= R  # a padding rank: the zero word, never a row past U
+    acc.int32("U offset r*int(ldu) + 8c", r[~uz] * ldu + 8 * (S["UCPR"] - 1))
+    acc.int32("x offset row*int(xs1) + 8c", (S["XR"] - 1) * xs1 + 8 * (S["XCPR"] - 1))
+    acc.int32("dy offset row*int(dys1) + 8c", (STEP - 1) * dys1 + 8 * (S["XCPR"] - 1))
+    xp = np.arange(S["XCH"])
+    xrow, xc = xp // S["XCPR"], xp % S["XCPR"]
+    dp = np.arange(S["DCH"])
+    drow, dc = dp // S["XCPR"], dp % S["XCPR"]
+    for b in range(B):
+        for tb in range(T // STEP):
+            tb0 = tb * STEP
+            # issue(ci) for ci = 0 .. nchunk + 1, clamped to the last chunk; the chunk
+            # positions within a row are a permutation of 0 .. CPR - 1
+            for ci in sorted({min(i, nchunk - 1) for i in range(nchunk + 2)}):
+                acc.add("U", 0, r[~uz], ci * S["UC"] + 8 * pc[~uz], 8)
+                acc.zero += int(uz.sum())
+                xr = np.maximum(xrow, HALO - tb0)  # rows before token 0 read token 0
+                acc.add("x", b, tb0 - HALO + xr, ci * S["CHC"] + 8 * xc, 8)
+                acc.add("dy", b, tb0 + drow, ci * S["CHC"] + 8 * dc, 8)
+            acc.add("dz", b, tb0 + np.arange(STEP)[:, None], np.arange(R)[None, :], 1)
+    return acc
+
+
+# ---------------------------------------------------------------------------------------
+# general low-rank kernels (register-staged 16-byte chunks; any dtype, ragged D)
+# ---------------------------------------------------------------------------------------
+
+def _chunk_span(c, limit, CE, vec):
+    """Elements that load_chunk reads: the whole chunk when vec and c + CE <= limit, else
+    elements c .. min(c + CE, limit) - 1 one by one."""
+    c = np.asarray(c)
+    return np.where(vec & (c + CE <= limit), CE, np.minimum(CE, limit - c))
+
+
+def plan_fwd_general(B, T, D, W, R):
+    KS = (R + 31) // 32
+    MT = 8 if KS <= 2 else 4
+    WP = 8 if W > 4 else 4
+    DC = 4 * MT * 16 // WP
+    nCs = (D + DC - 1) // DC
+    per_seq = (1024 + B * nCs - 1) // (B * nCs)
+    per_seq = max(1, min(per_seq, (T + TT - 1) // TT))
+    L = (T + per_seq - 1) // per_seq
+    L = (L + TT - 1) // TT * TT
+    return nCs, L, (T + L - 1) // L, DC, KS, MT
+
+
+def lowrank_fwd_general(B, T, D, W, H, R, eb, act16, z16, seg=False, has_bias=True):
+    nCs, L, nTr, DC, KS, MT = plan_fwd_general(B, T, D, W, R)
+    CE = 16 // eb
+    RP = 32 * KS
+    WP = 8 if W > 4 else 4
+    CPW = MT * 4 // (WP // 4)
+    acc = Accesses()
+    zck = np.arange(TT * RP // CE)
+    zrow, zc = zck // (RP // CE), (zck % (RP // CE)) * CE
+    xck = np.arange(TT * DC // CE)
+    xrow, xc = xck // (DC // CE), (xck % (DC // CE)) * CE
+    hck = np.arange(HALO * DC // CE)
+    hrow, hc = hck // (DC // CE), (hck % (DC // CE)) * CE
+    for b in range(B):
+        for tr in range(nTr):
+            t_first = tr * L
+            t_end = min(T, t_first + L)
+            if t_first >= T:
+                continue
+            for cs in range(nCs):
+                c_base = cs * DC
+                lim = D - c_base
+                t = t_first - HALO + hrow
+                ok = (t >= 0) & (hc < lim)
+                acc.add("x", b, t[ok], c_base + hc[ok], _chunk_span(hc[ok], lim, CE, act16))
+                for t0 in range(t_first, t_end, TT):
+                    tz = t0 + zrow
+                    okz = (tz < t_end) & (zc < R)
+                    acc.add("z", b, tz[okz], zc[okz], _chunk_span(zc[okz], R, CE, z16))
+                    tx = t0 + xrow
+                    okx = (tx < t_end) & (xc < lim)
+                    acc.add("x", b, tx[okx], c_base + xc[okx], _chunk_span(xc[okx], lim, CE, act16))
+                    if seg:
+                        ts = t0 + np.arange(TT)
+                        acc.add("seg", b, ts[ts < t_end], 0, 1)
+                if seg:
+                    ts = t_first - HALO + np.arange(HALO)
+                    acc.add("seg", b, ts[ts >= 0], 0, 1)
+                # y: each lane's run of MT channels, clipped at D
+                for wv in range(4):
+                    for q in range(4):
+                        cg = c_base + wv * CPW + (q // (WP // 4)) * MT
+                        if cg < D:
+                            acc.add("y", b, np.arange(t_first, t_end), cg, min(MT, D - cg))
+                ch = c_base + np.arange(DC)
+                ch = ch[ch < D]
+                acc.add("U", 0, np.arange(R)[:, None], ((ch // H) * W)[None, :], W)
+                if has_bias:
+                    acc.add("bias", 0, 0, (ch // H) * W, W)
+    return acc
+
+
+def lowrank_bwd_general(B, T, D, W, H, R, eb, fast, seg=False, has_bias=True, want_db=True, xs1=None, zs1=None,
+                        dys1=None, os1=None, lean=False):
+    """k_lowrank_bwd over every channel slice it is launched on: with `fast`, the FAST
+    instantiation covers the slices inside D (16-byte loads; R % 32 == 0) and the other
+    one the rest (masked element loads)."""
+    nCs, L, nTr, DC, KS = plan_lowrank_bwd(B, T, D, W, H, R, lean)
+    xs1 = D if xs1 is None else xs1
+    zs1 = R if zs1 is None else zs1
+    dys1 = D if dys1 is None else dys1
+    os1 = D if os1 is None else os1
+    CE = 16 // eb
+    RP = 32 * KS
+    S = STEP
+    MT = 2
+    WP = 8 if W > 4 else 4
+    LPC = WP // 4
+    CPW = MT * 4 // LPC
+    ZCH, XCH = S * RP // CE, S * DC // CE
+    NT = 256
+    ZS, XS = (ZCH + NT - 1) // NT, (XCH + NT - 1) // NT
+    HCH = HALO * DC // CE
+    assert not fast or R % 32 == 0
+    acc = Accesses()
+    acc.int32("z row offset row*int(zs1) + c", (S - 1) * zs1 + RP)
+    acc.int32("x row offset row*int(xs1) + c", (S - 1) * xs1 + DC)
+    acc.int32("dy row offset row*int(dys1) + c", (S - 1) * dys1 + DC)
+    acc.int32("dx row offset (sub TT + n - (W-1))*int(os1) + cl", (S - 1) * os1 + D)
+    nfull = D // DC if fast else 0
+    tid = np.arange(NT)
+    safe = lambda name, n: acc.add(name, 0, 0, 0, np.full(int(n), CE))  # noqa: E731
+    for b in range(B):
+        for tr in range(nTr):
+            t_first = tr * L
+            t_end = min(T, t_first + L)
+            t_need = min(T, t_end + HALO)
+            rng = b * nTr + tr
+            for cs in range(nCs):
+                FAST = cs < nfull
+                c_base = cs * DC
+                xlimit = D - c_base
+                # the HALO rows of x and dy before the range (zeros before t = 0)
+                th = tid[tid < 2 * HCH]
+                k2 = th % HCH
+                isx = th < HCH
+                row, c = k2 // (DC // CE), (k2 % (DC // CE)) * CE
+                t = t_first - HALO + row
+                ok = (t >= 0) & (c < xlimit)
+                w = np.full(c.shape, CE) if FAST else np.minimum(CE, xlimit - c)
+                acc.add("x", b, t[ok & isx], c_base + c[ok & isx], w[ok & isx])
+                acc.add("dy", b, t[ok & ~isx], c_base + c[ok & ~isx], w[ok & ~isx])
+                if FAST:
+                    safe("x", (~ok & isx).sum())
+                    safe("dy", (~ok & ~isx).sum())
+                # steps t0 = t_first, t_first + S, ... while t0 - (W - 1) < t_end, two per
+                # pass; prefetched: t_first, t_first + S and t0 + 2 S at each step
+                steps = []
+                t0 = t_first
+                while t0 - (W - 1) < t_end:
+                    steps.append(t0)
+                    if not (t0 + S - (W - 1) < t_end):
+                        break
+                    steps.append(t0 + S)
+                    t0 += 2 * S
+                for t0 in sorted({t_first, t_first + S} | {s + 2 * S for s in steps}):
+                    if seg:
+                        tt = t0 + tid[tid < S]
+                        acc.add("seg", b, tt[tt < t_need], 0, 1)
+                    if FAST and t0 + S <= t_end:
+                        for i in range(ZS):
+                            ck = tid + i * NT
+                            acc.add("z", b, t0 + ck // (RP // CE), (ck % (RP // CE)) * CE, CE)
+                        for i in range(XS):
+                            ck = tid + i * NT
+                            inn = ck < XCH
+                            row, c = ck // (DC // CE), (ck % (DC // CE)) * CE
+                            acc.add("x", b, t0 + row[inn], c_base + c[inn], CE)
+                            acc.add("dy", b, t0 + row[inn], c_base + c[inn], CE)
+                            safe("x", (~inn).sum())
+                            safe("dy", (~inn).sum())
+                        continue
+                    for i in range(ZS):
+                        ck = tid + i * NT
+                        row, c = ck // (RP // CE), (ck % (RP // CE)) * CE
+                        ok = (ck < ZCH) & (t0 + row < t_need) & (c < R)
+                        w = np.full(c.shape, CE) if FAST else np.minimum(CE, R - c)
+                        acc.add("z", b, t0 + row[ok], c[ok], w[ok])
+                        if FAST:
+                            safe("z", (~ok).sum())
+                    for i in range(XS):
+                        ck = tid + i * NT
+                        row, c = ck // (DC // CE), (ck % (DC // CE)) * CE
+                        ok = (ck < XCH) & (c < xlimit)
+                        okx, okd = ok & (t0 + row < t_end), ok & (t0 + row < t_need)
+                        w = np.full(c.shape, CE) if FAST else np.minimum(CE, xlimit - c)
+                        acc.add("x", b, t0 + row[okx], c_base + c[okx], w[okx])
+                        acc.add("dy", b, t0 + row[okd], c_base + c[okd], w[okd])
+                        if FAST:
+                            safe("x", (~okx).sum())
+                            safe("dy", (~okd).sum())
+                # dx: token s of the range from the lanes whose run of MT channels starts
+                # inside D (clipped at D)
+                for wv in range(4):
+                    for q in range(0, 4, LPC):
+                        cl = c_base + wv * CPW + (q // LPC) * MT
+                        if cl < D:
+                            acc.add("dx", b, np.arange(t_first, t_end), cl, min(MT, D - cl))
+                # partial sums, one per (range, channel of the group), and the generation
+                # operands of the wave's channels
+                for wv in range(4):
+                    ch = c_base + wv * CPW + np.arange(CPW)
+                    ch = ch[ch < D]
+                    cols = (ch // H) * W
+                    prow = rng * H + ch % H
+                    acc.add("part_dU", 0, prow[None, :] * R + np.arange(R)[:, None], cols[None, :], W)
+                    if want_db:
+                        acc.add("part_db", 0, prow, cols, W)
+                    acc.add("U", 0, np.arange(R)[:, None], cols[None, :], W)
+                    if has_bias:
+                        acc.add("bias", 0, 0, cols, W)
+    return acc, nTr

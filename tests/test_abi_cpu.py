@@ -5,6 +5,7 @@ Pointers below are fake, non-null addresses: the calls must reject the arguments
 before touching them.
 """
 import ctypes
+import itertools
 import os
 import re
 
@@ -138,6 +139,27 @@ def test_lowrank_validation(lib):
                                  S(800, 200, 1), P(0x990000), S(256, 64, 1), P(0x9a0000), None, 2, 4, 200, 4, 1, 64,
                                  BF16, P(0x9b0000), need - 1, None)
     assert st == WORKSPACE
+
+
+def test_lowrank_row_stride_bound(lib):
+    """Row strides of 2^24 elements or more are refused before any launch: the low-rank
+    kernels form the offsets of up to 128 rows in 32-bit arithmetic."""
+    big = 1 << 24
+
+    def fwd_(xs1=200, zs1=64, ys1=200, ldu=800):
+        return lib.dynconv_lowrank_fwd(X, S(4 * xs1, xs1, 1), Z, S(4 * zs1, zs1, 1), U, ldu, None, Y,
+                                       S(4 * ys1, ys1, 1), 2, 4, 200, 4, 1, 64, BF16, None)
+
+    def bwd_(dys1=200, dxs1=200):
+        need = lib.dynconv_lowrank_bwd_workspace_size(2, 4, 200, 4, 1, 64, BF16)
+        return lib.dynconv_lowrank_bwd(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, DY, S(4 * dys1, dys1, 1),
+                                       DX, S(4 * dxs1, dxs1, 1), P(0x990000), S(256, 64, 1), P(0x9a0000), None, 2, 4,
+                                       200, 4, 1, 64, BF16, P(0x9b0000), need, None)
+
+    for kw in (dict(xs1=big), dict(zs1=big), dict(ys1=big), dict(ldu=big)):
+        assert fwd_(**kw) == UNSUP, kw
+    for kw in (dict(dys1=big), dict(dxs1=big)):
+        assert bwd_(**kw) == UNSUP, kw
 
 
 C = P(0xA00000)  # fake cache
@@ -429,3 +451,37 @@ def test_gemm_validation(lib):
     assert gl(ldu=N * 4 - 1) == INVALID
     assert gl(y=ZZ) == INVALID and gl(y=UU) == INVALID
     assert gl(zs=(T * 64, 64, 2)) == UNSUP
+
+
+EXTREME = [1, 7, 1 << 20, (1 << 31) - 1]
+EXTREME_T = [1, 16, 4096, (1 << 31) - 65537, (1 << 31) - 65536, (1 << 31) - 1]
+EXTREME_D = [2, 2048, 1 << 20, (1 << 31) - 2]
+
+
+def test_size_queries_at_extreme_sizes(lib):
+    """Workspace queries over extreme B, T, D (no launch): 0 for refused sizes, otherwise a
+    size that fits the partial sums and stays far from 64-bit wrap-around."""
+    for B, T, D in itertools.product(EXTREME, EXTREME_T, EXTREME_D):
+        for W, H, dt in itertools.product([1, 4, 5, 8], [1, 2, 16], [BF16, 7]):
+            for st in (0, 1):
+                n = lib.dynconv_bwd_workspace_size(B, T, D, W, H, st, dt)
+                assert 0 <= n < (1 << 50), (B, T, D, W, H, st, dt, n)
+                if dt == 7 or st == 0:
+                    assert n == 0
+            for R in (1, 64, 128):
+                n = lib.dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dt)
+                assert 0 <= n < (1 << 50), (B, T, D, W, H, R, dt, n)
+                if n:
+                    assert n >= R * (D // H) * W * 4
+
+
+def test_sizes_past_the_grid_bound_are_refused(lib):
+    """Sizes whose grids or token arithmetic would not fit 32 bits are refused before any
+    launch."""
+    big_t = (1 << 31) - 1
+    assert fwd(lib, T=big_t) == UNSUP  # a token plus a step would pass INT32_MAX
+    # B * ceil(T / 16) * ceil(D / 16) above INT32_MAX workgroups
+    assert fwd(lib, B=1 << 20, T=4096, D=2048, xs=(4096 * 2048, 2048, 1), ys=(4096 * 2048, 2048, 1),
+               ws=(4096 * 2048 * 4, 2048 * 4, 4, 1)) == UNSUP
+    assert lib.dynconv_lowrank_bwd_workspace_size(1 << 20, 4096, 2048, 4, 1, 64, BF16) == 0
+    assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 64, BF16) > 0

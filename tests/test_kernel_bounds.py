@@ -1,0 +1,254 @@
+"""Every global load and store of the DMA-staged and chunk-loop kernels stays inside its
+tensor, over sweeps of dtype, W, R, H, D, T and strided layouts (host emulation of the
+kernels' index arithmetic, tests/kernel_bounds.py). Each case also checks that the
+emulated stores cover the whole output, so that an emulation which drops work cannot pass.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import kernel_bounds as kb
+
+
+def _full(acc, name, B, T, C):
+    cov = acc.cover(name, B, T, C)
+    assert cov.all(), f"{name}: {int((~cov).sum())} of {cov.size} elements never touched"
+
+
+# ---------------------------------------------------------------------------------------
+# projection + convolution
+# ---------------------------------------------------------------------------------------
+GEMM = [
+    # B, T, K, N, W, H
+    (1, 1, 64, 128, 4, 1),
+    (2, 300, 128, 256, 3, 2),
+    (1, 481, 64, 384, 5, 16),
+    (3, 100, 192, 128, 1, 4),
+    (1, 2000, 64, 256, 4, 8),
+]
+
+
+@pytest.mark.parametrize("B,T,K,N,W,H", GEMM)
+def test_gemm_conv_bounds(B, T, K, N, W, H):
+    acc = kb.gemm_conv(B, T, K, N, W, H)
+    G = N // H
+    acc.check({"A": (B, T, K), "Wp": (1, N, K), "w": (B, T, G * W), "y": (B, T, N)})
+    _full(acc, "y", B, T, N)
+    _full(acc, "A", B, T, K)
+
+
+@pytest.mark.parametrize("B,T,K,N,W,H", GEMM)
+@pytest.mark.parametrize("R", [8, 20, 64, 100, 128])
+@pytest.mark.parametrize("vec", [True, False])
+def test_gemm_lowrank_bounds(B, T, K, N, W, H, R, vec):
+    zvec = vec and R % 8 == 0
+    acc = kb.gemm_conv(B, T, K, N, W, H, R=R, lowrank=True, zvec=zvec, uvec=vec, has_bias=R % 2 == 0)
+    J = (N // H) * W
+    acc.check({"A": (B, T, K), "Wp": (1, N, K), "z": (B, T, R), "U": (1, R, J), "bias": (1, 1, J),
+               "y": (B, T, N)})
+    _full(acc, "y", B, T, N)
+    _full(acc, "U", 1, R, J)
+
+
+# ---------------------------------------------------------------------------------------
+# fast low-rank forward and fused backward
+# ---------------------------------------------------------------------------------------
+FAST_SHAPES = [
+    # B, T, D
+    (1, 1, 64),
+    (2, 4, 64),
+    (1, 63, 128),
+    (2, 64, 64),
+    (1, 65, 192),
+    (2, 200, 128),
+    (1, 1000, 64),
+]
+FAST_RANKS = [2, 20, 26, 64, 100, 128]
+
+
+def _fast_cases():
+    for (B, T, D), W, H, R in itertools.product(FAST_SHAPES, [1, 2, 3, 4], [1, 4, 16], FAST_RANKS):
+        if D % H:
+            continue
+        for ZB in ([16, 4] if R % 8 == 0 else [4]):
+            yield B, T, D, W, H, R, ZB
+
+
+FAST_CASES = list(_fast_cases())
+# a deterministic subset keeps the CPU suite short; every shape, W, H, R and ZB appears
+FAST_PICK = FAST_CASES[::7]
+
+
+def _layout(D, R, ZB, strided):
+    """Row strides: dense, or views into wider rows (16-byte multiples for the activations,
+    ZB-byte multiples for z)."""
+    if not strided:
+        return D, R, D, D
+    zpad = 8 if ZB == 16 else 2
+    return D + 64, (R + zpad + (zpad - 1)) // zpad * zpad, D + 8, D + 128
+
+
+@pytest.mark.parametrize("B,T,D,W,H,R,ZB", FAST_PICK)
+@pytest.mark.parametrize("strided", [False, True])
+def test_lowrank_fwd_fast_bounds(B, T, D, W, H, R, ZB, strided):
+    xs1, zs1, dys1, os1 = _layout(D, R, ZB, strided)
+    seg = T % 4 == 0 and T >= 4
+    acc = kb.lowrank_fwd_fast(B, T, D, W, H, R, ZB, xs1, zs1, os1, seg=seg, has_bias=(T % 2 == 0))
+    J = (D // H) * W
+    acc.check({"x": (B, T, D), "z": (B, T, R), "U": (1, R, J), "bias": (1, 1, J), "y": (B, T, D),
+               "seg": (B, T, 1)})
+    _full(acc, "y", B, T, D)
+    _full(acc, "x", B, T, D)
+    _full(acc, "z", B, T, R)
+
+
+@pytest.mark.parametrize("B,T,D,W,H,R,ZB", FAST_PICK)
+@pytest.mark.parametrize("strided", [False, True])
+def test_lowrank_bwd_fused_bounds(B, T, D, W, H, R, ZB, strided):
+    xs1, zs1, dys1, os1 = _layout(D, R, ZB, strided)
+    seg = T % 4 == 0 and T >= 4
+    acc, nTr = kb.lowrank_bwd_fused(B, T, D, W, H, R, ZB, xs1, zs1, dys1, os1, seg=seg, has_bias=(T % 2 == 1))
+    J = (D // H) * W
+    nR = B * nTr
+    acc.check({"x": (B, T, D), "dy": (B, T, D), "z": (B, T, R), "U": (1, R, J), "bias": (1, 1, J),
+               "dx": (B, T, D), "seg": (B, T, 1), "part_dU": (1, nR * R, J), "part_db": (1, nR, J)})
+    _full(acc, "dx", B, T, D)
+    _full(acc, "part_dU", 1, nR * R, J)
+    _full(acc, "part_db", 1, nR, J)
+    _full(acc, "dy", B, T, D)
+
+
+def test_fast_case_list_is_wide():
+    ws = {c[3] for c in FAST_PICK}
+    hs = {c[4] for c in FAST_PICK}
+    rs = {c[5] for c in FAST_PICK}
+    zbs = {c[6] for c in FAST_PICK}
+    shapes = {c[:3] for c in FAST_PICK}
+    assert ws == {1, 2, 3, 4} and hs == {1, 4, 16} and rs == set(FAST_RANKS) and zbs == {4, 16}
+    assert shapes == set(FAST_SHAPES)
+
+
+# ---------------------------------------------------------------------------------------
+# DMA dz
+# ---------------------------------------------------------------------------------------
+
+def _dz_cases():
+    for W, H, R, T in itertools.product([1, 2, 3, 4, 5], [1, 2, 4, 8, 16], [2, 20, 64, 100, 128], [64, 130]):
+        KS = (R + 31) // 32
+        s = kb.dz_dma_shape(W, KS, H)
+        if not s["ok"]:
+            continue
+        D = s["CHC"] * (2 if H <= 4 else 1)
+        yield 1, T, D, W, H, R
+
+
+DZ_CASES = list(_dz_cases())
+
+
+@pytest.mark.parametrize("B,T,D,W,H,R", DZ_CASES[::3])
+@pytest.mark.parametrize("strided", [False, True])
+def test_dz_dma_bounds(B, T, D, W, H, R, strided):
+    J = (D // H) * W
+    xs1, dys1, ldu = (D + 64, D + 8, J + 8) if strided else (D, D, J)
+    acc = kb.dz_dma(B, T, D, W, H, R, xs1, dys1, ldu)
+    acc.check({"x": (B, T, D), "dy": (B, T, D), "U": (1, R, J), "dz": (B, T, R)})
+    T64 = T // 64 * 64
+    _full(acc, "dz", B, T64, R)
+    _full(acc, "U", 1, R, J)
+
+
+def test_dz_cases_cover_every_group_size_and_width():
+    assert {c[4] for c in DZ_CASES[::3]} == {1, 2, 4, 8, 16}
+    assert {c[3] for c in DZ_CASES[::3]} == {1, 2, 3, 4, 5}
+
+
+# ---------------------------------------------------------------------------------------
+# general kernels
+# ---------------------------------------------------------------------------------------
+GEN = [
+    # B, T, D, H
+    (1, 1, 8, 1),
+    (2, 17, 40, 2),
+    (1, 100, 130, 1),
+    (1, 300, 96, 4),
+]
+
+
+@pytest.mark.parametrize("B,T,D,H", GEN)
+@pytest.mark.parametrize("W", [1, 3, 4, 5])
+@pytest.mark.parametrize("R", [1, 3, 20, 64, 100])
+@pytest.mark.parametrize("eb", [2, 4])
+def test_lowrank_fwd_general_bounds(B, T, D, H, W, R, eb):
+    vec = (T + W + R) % 2 == 0
+    acc = kb.lowrank_fwd_general(B, T, D, W, H, R, eb, act16=vec, z16=not vec, seg=T % 3 == 1,
+                                 has_bias=R % 2 == 0)
+    J = (D // H) * W
+    acc.check({"x": (B, T, D), "z": (B, T, R), "U": (1, R, J), "bias": (1, 1, J), "y": (B, T, D), "seg": (B, T, 1)})
+    _full(acc, "y", B, T, D)
+    _full(acc, "x", B, T, D)
+
+
+GEN_BWD = [
+    # B, T, D, H
+    (1, 1, 16, 1),
+    (2, 5, 40, 2),
+    (1, 64, 32, 1),
+    (1, 65, 48, 4),
+    (1, 150, 96, 1),
+    (2, 300, 64, 2),
+]
+
+
+@pytest.mark.parametrize("B,T,D,H", GEN_BWD)
+@pytest.mark.parametrize("W", [1, 2, 4, 5])
+@pytest.mark.parametrize("R", [3, 32, 64, 100, 128])
+@pytest.mark.parametrize("eb", [2, 4])
+def test_lowrank_bwd_general_bounds(B, T, D, H, W, R, eb):
+    fast = R % 32 == 0
+    acc, nTr = kb.lowrank_bwd_general(B, T, D, W, H, R, eb, fast, seg=T % 2 == 1, has_bias=W % 2 == 0,
+                                      want_db=R != 64, lean=(eb == 2 and W <= 4 and D % 64 == 0))
+    J = (D // H) * W
+    nR = B * nTr
+    acc.check({"x": (B, T, D), "dy": (B, T, D), "z": (B, T, R), "U": (1, R, J), "bias": (1, 1, J),
+               "dx": (B, T, D), "seg": (B, T, 1), "part_dU": (1, nR * H * R, J), "part_db": (1, nR * H, J)})
+    _full(acc, "dx", B, T, D)
+    _full(acc, "part_dU", 1, nR * H * R, J)
+
+
+# ---------------------------------------------------------------------------------------
+# 32-bit offsets at the largest row strides the ABI admits
+# ---------------------------------------------------------------------------------------
+BIG = kb.MAX_ROW_STRIDE - 64  # a multiple of 16 bytes for every dtype
+
+
+def test_largest_admitted_strides_keep_32bit_offsets():
+    kb.dz_dma(1, 64, 64, 4, 1, 128, BIG, BIG, BIG).check({"x": (1, 64, 64), "dy": (1, 64, 64),
+                                                          "U": (1, 128, 256), "dz": (1, 64, 128)})
+    acc, nTr = kb.lowrank_bwd_general(1, 70, 32, 4, 1, 128, 2, True, xs1=BIG, zs1=BIG, dys1=BIG, os1=BIG)
+    acc.check({"x": (1, 70, 32), "dy": (1, 70, 32), "z": (1, 70, 128), "U": (1, 128, 128), "bias": (1, 1, 128),
+               "dx": (1, 70, 32), "part_dU": (1, nTr * 128, 128), "part_db": (1, nTr, 128)})
+
+
+def test_strides_past_the_bound_would_overflow():
+    """The reason for the ABI's bound: a few times past it the kernels' 32-bit offsets wrap
+    (U's 128 rank rows at twice the bound, a 64-token step's rows at four times)."""
+    over = 4 * kb.MAX_ROW_STRIDE
+    with pytest.raises(AssertionError, match="32-bit offset"):
+        kb.dz_dma(1, 64, 64, 4, 1, 128, 64, 64, over).check({})
+    with pytest.raises(AssertionError, match="32-bit offset"):
+        kb.lowrank_bwd_general(1, 70, 32, 4, 1, 128, 2, True, xs1=over)[0].check({})
+
+
+def test_emulation_detects_a_misplaced_row():
+    """A planted off-by-one (the fast forward's last partial step reading row T instead of
+    T - 1) is reported."""
+    orig = kb.step_rows
+    try:
+        kb.step_rows = lambda t0, rl, T: t0 + rl
+        acc = kb.lowrank_fwd_fast(1, 65, 64, 4, 1, 64, 16, 64, 64, 64)
+        with pytest.raises(AssertionError, match="x: access"):
+            acc.check({"x": (1, 65, 64), "z": (1, 65, 64), "U": (1, 64, 256), "bias": (1, 1, 256),
+                       "y": (1, 65, 64)})
+    finally:
+        kb.step_rows = orig
