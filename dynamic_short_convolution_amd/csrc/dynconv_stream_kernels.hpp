@@ -28,13 +28,12 @@
 #include "dynconv_internal.hpp"
 
 // Tuning, measured on MI355X at the pages' model shapes (B8 T4096 D2048 and B4 T8192
-// D3072, W = 4): the forward streams best with about 128 bytes of loads in flight per lane
-// (unroll 4 for the per-channel form) at 8 waves per CU; the per-channel backward with
-// unroll 2 and 16 waves per CU; the head-wise and static backward at 12 and 8 waves per CU;
-// the static forms prefer neighbouring workgroups to walk channels rather than time. Stores
-// are plain everywhere: with non-temporal stores the per-channel backward took 272.5 us
-// instead of 244.0 at W = 4, 591.9 instead of 500.4 at W = 8 (bf16), 268.6 instead of
-// 234.7 at W = 4 in float32. Each constant can be overridden at build time for a sweep.
+// D3072, W = 4): the forward streams best with plain stores and about 128 bytes of loads
+// in flight per lane (unroll 4 for the per-channel form) at 8 waves per CU; the per-channel
+// backward with non-temporal stores, unroll 2 and 16 waves per CU; the head-wise and
+// static backward with plain stores at 12 and 8 waves per CU; the static forms prefer
+// neighbouring workgroups to walk channels rather than time. Each constant can be
+// overridden at build time for a sweep.
 #ifndef DYNCONV_FWD_INFLIGHT
 #define DYNCONV_FWD_INFLIGHT 128
 #endif
@@ -61,6 +60,22 @@ namespace {
 // Every streamed input is read once, so loads carry the non-temporal hint.
 __device__ __forceinline__ uint32_t ld32(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ uint16_t ld16(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+template <bool NT>
+__device__ __forceinline__ void st32(uint32_t* p, uint32_t v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void st16(uint16_t* p, uint16_t v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
 
 // N contiguous elements at a 4-byte aligned address, kept as raw 32-bit words until
 // they are used (the compiler fuses the word loads into dwordx2/x3/x4).
@@ -103,28 +118,28 @@ struct Halves {
   __device__ __forceinline__ float at(int i) const { return Cvt<ET>::of_bits(h[i]); }
 };
 
-template <typename ET, int N>
+template <bool NT, typename ET, int N>
 __device__ __forceinline__ void store_words(ET* p, const float (&v)[N]) {
   uint32_t* q = reinterpret_cast<uint32_t*>(p);
   if constexpr (sizeof(ET) == 2) {
 #pragma unroll
-    for (int i = 0; i < N / 2; ++i) q[i] = Cvt<ET>::pack2(v[2 * i], v[2 * i + 1]);
+    for (int i = 0; i < N / 2; ++i) st32<NT>(q + i, Cvt<ET>::pack2(v[2 * i], v[2 * i + 1]));
   } else {
 #pragma unroll
-    for (int i = 0; i < N; ++i) q[i] = __float_as_uint(v[i]);
+    for (int i = 0; i < N; ++i) st32<NT>(q + i, __float_as_uint(v[i]));
   }
 }
 
 // N elements at element alignment; words when N elements fill whole 32-bit words and the
 // caller guarantees 4-byte alignment (WORDS), 16-bit stores otherwise.
-template <bool WORDS, typename ET, int N>
+template <bool NT, bool WORDS, typename ET, int N>
 __device__ __forceinline__ void store_elems(ET* p, const float (&v)[N]) {
   if constexpr (sizeof(ET) == 2 && !WORDS) {
     uint16_t* q = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
-    for (int i = 0; i < N; ++i) q[i] = Cvt<ET>::bits(v[i]);
+    for (int i = 0; i < N; ++i) st16<NT>(q + i, Cvt<ET>::bits(v[i]));
   } else {
-    store_words<ET, N>(p, v);
+    store_words<NT, ET, N>(p, v);
   }
 }
 
@@ -248,6 +263,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int U = DYNCONV_FWD_UNROLL > 0 ? DYNCONV_FWD_UNROLL
                     : LB > 32              ? 4
                                            : clamp_unroll(pow2_floor(DYNCONV_FWD_INFLIGHT / LB));
+  constexpr bool NT = false;
 
   const WaveTile wt = wave_tile<STATIC, false>(p, VEC);
   if (!wt.valid) return;
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(
       }
       yv[v] = acc;
     }
-    store_words<ET, VEC>(yb + t * p.os1, yv);
+    store_words<NT, ET, VEC>(yb + t * p.os1, yv);
   };
 
   int t = wt.t0;
@@ -367,6 +383,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   constexpr int NC = PERCH ? VEC : 1;
   constexpr int LB = 2 * VEC * int(sizeof(ET)) + (STATIC ? 0 : TapsRaw<ET, W, VEC, PERCH>::bytes);
   constexpr int U = DYNCONV_BWD_UNROLL > 0 ? DYNCONV_BWD_UNROLL : clamp_unroll(pow2_floor(DYNCONV_BWD_INFLIGHT / LB));
+  constexpr bool NT = PERCH && !STATIC;
 
   const WaveTile wt = wave_tile<STATIC, true>(p, VEC);
   // Group reductions need every lane of a group; a whole group is either valid or not
@@ -459,7 +476,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
           for (int v = 0; v < VEC; ++v)
 #pragma unroll
             for (int k = 0; k < W; ++k) o[v * W + k] = d[k][v];
-          store_words<ET, VEC * W>(dwb + t * p.dws1, o);
+          store_words<NT, ET, VEC * W>(dwb + t * p.dws1, o);
         }
       } else {
         float s[W];
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
         } else {
 #pragma unroll
           for (int k = 0; k < W; ++k) s[k] = group_sum(s[k], lanes_per_group);
-          if (group_lead) store_elems<TapsRaw<ET, W, VEC, PERCH>::group_words, ET, W>(dwb + t * p.dws1, s);
+          if (group_lead) store_elems<NT, TapsRaw<ET, W, VEC, PERCH>::group_words, ET, W>(dwb + t * p.dws1, s);
         }
       }
     }
@@ -497,9 +514,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       const int s = t - (W - 1);
       if (s >= wt.t0 && s < wt.t1) {
         if constexpr (W == 1) {
-          store_words<ET, VEC>(dxb + s * p.os1, nacc);
+          store_words<NT, ET, VEC>(dxb + s * p.os1, nacc);
         } else {
-          store_words<ET, VEC>(dxb + s * p.os1, acc[W - 2]);
+          store_words<NT, ET, VEC>(dxb + s * p.os1, acc[W - 2]);
         }
       }
 #pragma unroll
