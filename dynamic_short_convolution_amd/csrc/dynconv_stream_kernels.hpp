@@ -30,7 +30,7 @@
 // Tuning, measured on MI355X at the pages' model shapes (B8 T4096 D2048 and B4 T8192
 // D3072, W = 4): the forward streams best with plain stores and about 128 bytes of loads
 // in flight per lane (unroll 4 for the per-channel form) at 8 waves per CU; the per-channel
-// backward with non-temporal stores, unroll 2 and 16 waves per CU; the head-wise and
+// backward with non-temporal stores (up to W = 5), unroll 2 and 16 waves per CU; the head-wise and
 // static backward with plain stores at 12 and 8 waves per CU; the static forms prefer
 // neighbouring workgroups to walk channels rather than time. Each constant can be
 // overridden at build time for a sweep.
@@ -383,7 +383,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   constexpr int NC = PERCH ? VEC : 1;
   constexpr int LB = 2 * VEC * int(sizeof(ET)) + (STATIC ? 0 : TapsRaw<ET, W, VEC, PERCH>::bytes);
   constexpr int U = DYNCONV_BWD_UNROLL > 0 ? DYNCONV_BWD_UNROLL : clamp_unroll(pow2_floor(DYNCONV_BWD_INFLIGHT / LB));
-  constexpr bool NT = PERCH && !STATIC;
+  // Non-temporal stores up to W = 5; wider filters store plain (their taps take several
+  // store instructions per lane). Measured as back-to-back forward + backward steps at B8
+  // T4096 D2048 bf16 (per-launch timings after a cache flush leave a kernel's last dirty
+  // lines to the untimed flush and mislead here): non-temporal vs plain 401.5 vs 424.8 us
+  // at W = 4, 571.7 vs 581.2 at W = 5, 702.0 vs 678.4 at W = 6, 772.5 vs 761.1 at W = 7,
+  // 832.5 vs 800.3 at W = 8.
+  constexpr bool NT = PERCH && !STATIC && W <= 5;
 
   const WaveTile wt = wave_tile<STATIC, true>(p, VEC);
   // Group reductions need every lane of a group; a whole group is either valid or not
