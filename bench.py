@@ -49,7 +49,8 @@ def parse_args():
     ap.add_argument("--no-rows", action="store_true", help="skip the per-form measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--only", default=None,
-                    help="run only this row's kernel in a loop (for profiler runs): one of ROWS, or 'copy'")
+                    help="run only this row's kernel in a loop (for profiler runs): one of ROWS, or 'copy'; "
+                         "'references' times the runtime's own streaming kernels and prints them")
     ap.add_argument("--reps", type=int, default=20, help="timed launches per row")
     return ap.parse_args()
 
@@ -409,18 +410,10 @@ def run_rows(args, device):
         log(f"{name}: {r['median_us']} us, {r['gbs']} GB/s")
         del fn
         torch.cuda.empty_cache()
-    # context, not the library: the runtime's own device copy (1 GiB read + 1 GiB written),
-    # timed the same way, as the streaming rate a plain read/write kernel reaches on this part
-    a = torch.empty(1 << 30, dtype=torch.uint8, device=device).fill_(3)
-    b_ = torch.empty_like(a)
-    med, mean = time_launches(lambda: b_.copy_(a), args.reps, flush)
-    gbs = round(2.0 * (1 << 30) / (med * 1e-3) / 1e9, 1)
-    out["reference_device_copy"] = dict(config="runtime device copy, 1 GiB read + 1 GiB written",
-                                        median_us=round(med * 1e3, 2), gbs=gbs,
-                                        pct_hbm_peak=round(100.0 * gbs / HBM_PEAK_GBS, 1))
-    log(f"reference device copy: {out['reference_device_copy']['median_us']} us, {gbs} GB/s")
-    del a, b_
-    torch.cuda.empty_cache()
+    # context, not the library: the runtime's own streaming kernels, timed the same way, as
+    # the rates plain kernels reach on this part at several read/write mixes (a practical
+    # ceiling next to the 8 TB/s peak)
+    out.update(reference_streams(args, device, flush))
     # orderings the pages report for their kernels (latency falls with H; low-rank below H=1)
     out["orderings"] = {
         "fwd_h16_lt_h4_lt_h1": out["headwise_h16_fwd"]["median_us"] < out["headwise_h4_fwd"]["median_us"]
@@ -447,10 +440,45 @@ def run_rows(args, device):
     return out
 
 
+def reference_streams(args, device, flush):
+    """The device copy (1 GiB read + 1 GiB written), a sum over 1 GiB (read only) and
+    elementwise add / addcmul over 512 MiB operands (2 and 3 reads per write)."""
+    import torch
+
+    out = {}
+    n = 1 << 29  # bf16 elements: 1 GiB
+    h = n // 2  # 512 MiB operands
+    a = torch.empty(n, dtype=torch.bfloat16, device=device).fill_(1.0)
+    b_ = torch.empty_like(a)
+    s = torch.empty((), dtype=torch.float32, device=device)
+    x1, x2, x3 = (torch.empty(h, dtype=torch.bfloat16, device=device).fill_(0.5) for _ in range(3))
+    o = torch.empty_like(x1)
+    cases = [
+        ("reference_device_copy", "runtime device copy, 1 GiB read + 1 GiB written", lambda: b_.copy_(a), 2 * 2 * n),
+        ("reference_read_sum", "runtime sum, 1 GiB read", lambda: torch.sum(a, dtype=torch.float32, out=s), 2 * n),
+        ("reference_add_2r1w", "runtime add, 2 x 512 MiB read + 512 MiB written", lambda: torch.add(x1, x2, out=o),
+         3 * 2 * h),
+        ("reference_addcmul_3r1w", "runtime addcmul, 3 x 512 MiB read + 512 MiB written",
+         lambda: torch.addcmul(x1, x2, x3, out=o), 4 * 2 * h),
+    ]
+    for key, desc, fn, nbytes in cases:
+        med, mean = time_launches(fn, args.reps, flush)
+        gbs = round(nbytes / (med * 1e-3) / 1e9, 1)
+        out[key] = dict(config=desc, median_us=round(med * 1e3, 2), bytes=nbytes, gbs=gbs,
+                        pct_hbm_peak=round(100.0 * gbs / HBM_PEAK_GBS, 1))
+        log(f"{key}: {out[key]['median_us']} us, {gbs} GB/s")
+    del a, b_, s, x1, x2, x3, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_only(args, device):
     """A plain loop of one row (or a 1 GiB device copy) for profiler runs."""
     import torch
 
+    if args.only == "references":
+        print(json.dumps(reference_streams(args, device, Flusher(device))))
+        return
     if args.only == "copy":
         a = torch.empty(1 << 30, dtype=torch.uint8, device=device)
         a.fill_(3)
