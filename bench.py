@@ -455,7 +455,7 @@ def reference_streams(args, device, flush):
     o = torch.empty_like(x1)
     cases = [
         ("reference_device_copy", "runtime device copy, 1 GiB read + 1 GiB written", lambda: b_.copy_(a), 2 * 2 * n),
-        ("reference_read_sum", "runtime sum, 1 GiB read", lambda: torch.sum(a, dtype=torch.float32, out=s), 2 * n),
+        ("reference_read_sum", "runtime sum, 1 GiB read", lambda: torch.sum(a, dim=0, dtype=torch.float32, out=s), 2 * n),
         ("reference_add_2r1w", "runtime add, 2 x 512 MiB read + 512 MiB written", lambda: torch.add(x1, x2, out=o),
          3 * 2 * h),
         ("reference_addcmul_3r1w", "runtime addcmul, 3 x 512 MiB read + 512 MiB written",
