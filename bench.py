@@ -411,7 +411,7 @@ def run_rows(args, device):
         del fn
         torch.cuda.empty_cache()
     # context, not the library: the runtime's own streaming kernels, timed the same way, as
-    # the rates plain kernels reach on this part at several read/write mixes (a practical
+    # the rates plain kernels reach on this part at three read/write mixes (a practical
     # ceiling next to the 8 TB/s peak)
     out.update(reference_streams(args, device, flush))
     # orderings the pages report for their kernels (latency falls with H; low-rank below H=1)
@@ -441,8 +441,8 @@ def run_rows(args, device):
 
 
 def reference_streams(args, device, flush):
-    """The device copy (1 GiB read + 1 GiB written), a sum over 1 GiB (read only) and
-    elementwise add / addcmul over 512 MiB operands (2 and 3 reads per write)."""
+    """The device copy (1 GiB read + 1 GiB written) and elementwise add / addcmul over
+    512 MiB operands (2 and 3 reads per write)."""
     import torch
 
     out = {}
@@ -450,12 +450,10 @@ def reference_streams(args, device, flush):
     h = n // 2  # 512 MiB operands
     a = torch.empty(n, dtype=torch.bfloat16, device=device).fill_(1.0)
     b_ = torch.empty_like(a)
-    s = torch.empty((), dtype=torch.float32, device=device)
     x1, x2, x3 = (torch.empty(h, dtype=torch.bfloat16, device=device).fill_(0.5) for _ in range(3))
     o = torch.empty_like(x1)
     cases = [
         ("reference_device_copy", "runtime device copy, 1 GiB read + 1 GiB written", lambda: b_.copy_(a), 2 * 2 * n),
-        ("reference_read_sum", "runtime sum, 1 GiB read", lambda: torch.sum(a, dim=0, dtype=torch.float32, out=s), 2 * n),
         ("reference_add_2r1w", "runtime add, 2 x 512 MiB read + 512 MiB written", lambda: torch.add(x1, x2, out=o),
          3 * 2 * h),
         ("reference_addcmul_3r1w", "runtime addcmul, 3 x 512 MiB read + 512 MiB written",
@@ -467,7 +465,7 @@ def reference_streams(args, device, flush):
         out[key] = dict(config=desc, median_us=round(med * 1e3, 2), bytes=nbytes, gbs=gbs,
                         pct_hbm_peak=round(100.0 * gbs / HBM_PEAK_GBS, 1))
         log(f"{key}: {out[key]['median_us']} us, {gbs} GB/s")
-    del a, b_, s, x1, x2, x3, o
+    del a, b_, x1, x2, x3, o
     torch.cuda.empty_cache()
     return out
 

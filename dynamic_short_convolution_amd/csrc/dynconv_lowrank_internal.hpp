@@ -86,15 +86,13 @@ bool lowrank_fast_group_ok(int H);
 bool lowrank_seg_fast_ok(const LowRankParams& p);
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
 hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
-// 16-bit fast dx of the backward (same conditions, on dy and dx); it plans its own ranges.
-bool lowrank_bwd_dx_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);
-hipError_t launch_lowrank_bwd_dx_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
-// 16-bit fast g / dU / db partial sums (same conditions as the fast dx, on x too), over the
-// planned token ranges (Ltok, nTr) and 64-channel slices; one partial per token range and
-// group column (a group's H channels summed inside the workgroup).
-hipError_t launch_lowrank_bwd_gdu_fast(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
-// The same two computations in one kernel (8 waves: dx and g / dU / db roles sharing the
-// staged dy and z), over the planned token ranges and 64-channel slices.
+// Shapes and layouts the 16-bit fast backward serves (the forward's conditions, on x, dy,
+// z and dx).
+bool lowrank_bwd_fast_shape_ok(const LowRankParams& p, int W, dynconv_dtype dt);
+// The 16-bit fast backward's dx and g / dU / db partial sums in one kernel (8 waves: dx and
+// g / dU / db roles sharing the staged dy and z), over the planned token ranges (Ltok, nTr)
+// and 64-channel slices; one partial per token range and group column (a group's H
+// channels summed inside the workgroup).
 hipError_t launch_lowrank_bwd_fused(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
 // Whether the backward runs on the fast kernels (dx, then g / dU / db): they write
 // B * nTr partials per filter column, the general kernel B * nTr * H.
