@@ -1317,9 +1317,12 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
 // ---------------------------------------------------------------------------------
 // dz, bf16 interior blocks: the same computation as lowrank_dz_body, staged by LDS DMA
 // (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base + 16 *
-// lane, no registers involved) into a ring of NST stages, two chunks ahead of the one
+// lane, no registers involved) into a ring of NST stages, NST - 1 chunks ahead of the one
 // being computed. Each wave waits for its own transfers (vmcnt) and a barrier publishes
-// the stage; nothing else needs the loads, so no other wait is tied to them.
+// the stage; nothing else needs the loads, so no other wait is tied to them. Two stages
+// (one chunk ahead) leave room for 3 workgroups per CU at H = 1 (R = 64: 51 KiB each);
+// measured against three stages: low-rank backward 213.7 -> 208.2 us at B8 T4096 D2048
+// W4 R64, head-wise H = 4 194.3 -> 191.1 us.
 // A lane owns GL filter groups (GL = 8 for HG <= 4, 32 / HG for HG = 8, 16), a chunk the
 // 4 GL groups of the 4 lane groups: 32 channels per-channel, 32 * HG channels when HG
 // consecutive channels share a filter (HG = 2, 4), 128 channels for HG = 8, 16. The filter
@@ -1354,6 +1357,9 @@ struct LdsPlace {
   }
 };
 
+#ifndef LRDZ_NST
+#define LRDZ_NST 2
+#endif
 template <int W, int KS, int HG>
 struct LrDzDma {
   static_assert(HG == 1 || HG == 2 || HG == 4 || HG == 8 || HG == 16, "group size of the DMA dz path");
@@ -1374,7 +1380,7 @@ struct LrDzDma {
   static constexpr int X_OFF = NI_U * 64 * 16;   // byte offsets inside a stage
   static constexpr int D_OFF = X_OFF + NI_X * 64 * 16;
   static constexpr int STAGE = D_OFF + NI_D * 64 * 16;
-  static constexpr int NST = 3;
+  static constexpr int NST = LRDZ_NST;  // stages of the ring (2: one chunk ahead, 3: two)
   static constexpr int BYTES = NST * STAGE;
   static_assert(XCPR == 4 * RUNS && UC % 8 == 0, "dz DMA tiling");
   using UPlace = LdsPlace<UCPR>;
@@ -1501,11 +1507,16 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   issue(0, 0);
-  issue(1, 1);
+  if constexpr (D::NST == 3) issue(1, 1);
   for (int ci = 0; ci < nchunk; ++ci) {
-    // this wave's transfers of stage ci were followed by at least NIW_MIN newer ones
-    vm_wait_barrier<NMIN>();
-    issue((ci + 2) % D::NST, ci + 2);
+    if constexpr (D::NST == 3) {
+      // this wave's transfers of stage ci were followed by at least NMIN newer ones
+      vm_wait_barrier<NMIN>();
+      issue((ci + 2) % D::NST, ci + 2);
+    } else {
+      vm_wait_barrier<0>();
+      issue((ci + 1) % D::NST, ci + 1);
+    }
     const unsigned char* stage = smem + (ci % D::NST) * D::STAGE;
     // words of the lane's dy run and x runs (taps 0 .. W-1); channel j of the lane is
     // word (j % 8) / 2 of run j / 8

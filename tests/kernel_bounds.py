@@ -363,7 +363,10 @@ def lowrank_bwd_fused(B, T, D, W, H, R, ZB, xs1, zs1, dys1, os1, seg=False, has_
 # k_lowrank_dz_dma: one workgroup per 64-token block inside T, chunks of CH filter groups
 # ---------------------------------------------------------------------------------------
 
-def dz_dma_shape(W, KS, HG):
+DZ_STAGES = 2  # the DMA dz kernel's ring (LRDZ_NST)
+
+
+def dz_dma_shape(W, KS, HG, stages=DZ_STAGES):
     GL = 8 if HG <= 4 else 32 // HG
     CH = 4 * GL
     CHC, UC = CH * HG, CH * W
@@ -373,7 +376,7 @@ def dz_dma_shape(W, KS, HG):
     UCH, XCH, DCH = RP * UCPR, XR * XCPR, STEP * XCPR
     ni = lambda n: (n + 63) // 64  # noqa: E731
     stage = (ni(UCH) + ni(XCH) + ni(DCH)) * 64 * 16
-    ok = (GL * W) % 8 == 0 and 3 * stage <= 150 * 1024
+    ok = (GL * W) % 8 == 0 and stages * stage <= 150 * 1024
     return dict(GL=GL, CH=CH, CHC=CHC, UC=UC, UCPR=UCPR, XCPR=XCPR, XR=XR, UCH=UCH, XCH=XCH, DCH=DCH, ok=ok)
 
 
@@ -396,9 +399,9 @@ def dz_dma(B, T, D, W, H, R, xs1, dys1, ldu):
     for b in range(B):
         for tb in range(T // STEP):
             tb0 = tb * STEP
-            # issue(ci) for ci = 0 .. nchunk + 1, clamped to the last chunk; the chunk
-            # positions within a row are a permutation of 0 .. CPR - 1
-            for ci in sorted({min(i, nchunk - 1) for i in range(nchunk + 2)}):
+            # issue(ci) for ci = 0 .. nchunk - 1 + (stages - 1), clamped to the last chunk;
+            # the chunk positions within a row are a permutation of 0 .. CPR - 1
+            for ci in sorted({min(i, nchunk - 1) for i in range(nchunk + DZ_STAGES - 1)}):
                 acc.add("U", 0, r[~uz], ci * S["UC"] + 8 * pc[~uz], 8)
                 acc.zero += int(uz.sum())
                 xr = np.maximum(xrow, HALO - tb0)  # rows before token 0 read token 0
