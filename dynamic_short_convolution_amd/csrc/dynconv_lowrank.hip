@@ -19,7 +19,8 @@ LowRankPlan plan_lowrank(int64_t B, int64_t T, int64_t D, int W, int H, int R, b
   // The choice uses only what the workspace query knows; if alignment then rules the fast
   // kernels out, the main kernel runs with these token ranges instead.
   const int ksr = (R + 31) / 32;
-  const bool lean = bwd && (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(H) && W <= 4 &&
+  const bool lean = bwd && (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(H) &&
+                    (W <= 4 || (W == 5 && ksr <= 2)) &&
                     R % 2 == 0 && ksr != 3 && D % 64 == 0;
   const int64_t target = !bwd ? 1024 : lean ? 512 : 2048;
   const int64_t slices = lean ? D / 64 : pl.nCs;  // the fast kernel's 64-channel slices

@@ -189,6 +189,65 @@ struct FwdFast {
   static constexpr int kSteady = XD + 1;  // from this step on the count no longer changes
 };
 
+// Matrix-core tiles that generate a wave's filters: tile c4 (0..3) holds taps 0..3 of the
+// lane's channel c4 and, for W > 4, tile 4 + c4 its taps 4..7, so a lane receives every
+// tap of its 4 channels.
+template <int W>
+constexpr int gen_tiles() {
+  return W > 4 ? 8 : 4;
+}
+
+// A operands of the generation (U^T rows: the MFMA row n of tile mt is channel
+// cw + 4 (n / 4) + mt % 4, tap 4 (mt / 4) + n % 4; ranks 32 ks + 8 q + e) and the bias as
+// the accumulators' initial values (lane (n, q): channel cw + 4 q + mt % 4, taps
+// 4 (mt / 4) + i). Loads are unconditional (a clamped tap and rank, U standing in for a
+// missing bias) and the unused values are zeroed afterwards, so nothing waits on a branch.
+template <typename ET, int W, int KS>
+__device__ __forceinline__ void generation_operands(const LowRankParams& p, int cw, int n, int q,
+                                                    u16x8_t (&afr)[gen_tiles<W>()][KS],
+                                                    f32x4_t (&binit)[gen_tiles<W>()]) {
+  const uint16_t* U = static_cast<const uint16_t*>(p.U);
+  const bool has_bias = p.bias != nullptr;
+  const uint16_t* bsrc = has_bias ? static_cast<const uint16_t*>(p.bias) : U;
+  const int hsh = __builtin_ctz(unsigned(p.H));  // channel c takes group c / H's columns
+#pragma unroll
+  for (int mt = 0; mt < gen_tiles<W>(); ++mt) {
+    const int c4 = mt & 3, half = mt >> 2;
+    const int tap = 4 * half + (n & 3);
+    const int ltap = tap < W ? tap : W - 1;
+    const int ch = cw + 4 * (n >> 2) + c4;
+    const int64_t col = int64_t(ch >> hsh) * W + ltap;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // ranks from R up to 32 KS are zero (the row read is clamped inside U)
+        const int r = 32 * ks + 8 * q + e;
+        const uint16_t v = U[int64_t(min(r, p.R - 1)) * p.ldu + col];
+        afr[mt][ks][e] = (tap < W && r < p.R) ? v : uint16_t(0);
+      }
+    const int chq = cw + 4 * q + c4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tq = 4 * half + i;
+      const uint16_t v = bsrc[(has_bias ? int64_t(chq >> hsh) * W : 0) + (tq < W ? tq : W - 1)];
+      binit[mt][i] = (tq < W && has_bias) ? Cvt<ET>::of_bits(v) : 0.f;
+    }
+  }
+}
+
+// Filter tap k of the lane's channel c4 from the generation results of one token group.
+template <int W>
+__device__ __forceinline__ float tap_of(const f32x4_t (&a)[gen_tiles<W>()], int c4, int k) {
+  return k < 4 ? a[c4][k] : a[4 + c4][k - 4];
+}
+
+// Rank tiles of the filter-gradient role's partial sums staged in LDS at a time (two LDS
+// barriers each): up to 4, 2 when W > 4 (rows of 64 W + 1 floats).
+constexpr int gdu_tiles_per_chunk(int W, int KS) {
+  return (2 * KS < 4 ? 2 * KS : 4) / (W > 4 && 2 * KS >= 4 ? 2 : 1);
+}
+
 template <class F, int S>
 __device__ __forceinline__ void step_wait(int s) {
   if constexpr (S >= F::kSteady) {
@@ -212,6 +271,8 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   constexpr int HR = W - 1;       // rows before a token that its filter reaches
   constexpr int MLO = -HR;        // x rows 4n + m, m = MLO .. 3, feed the lane's 4 tokens
   constexpr int NM = 4 - MLO;
+  constexpr int NGT = gen_tiles<W>();
+  static_assert(HR <= 4, "x rows 4n + m with m >= -4 sit in the lane's row group or the one before");
   __shared__ __align__(16) unsigned char smem[F::BYTES];
 
   const int tid = threadIdx.x;
@@ -303,38 +364,9 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   };
 
   // ---- A operands (U^T rows in the lane order above) and the bias, once ----
-  // Loads are unconditional (a clamped tap, U standing in for a missing bias) and the
-  // unused values are zeroed afterwards, so nothing waits on a branch here.
-  u16x8_t afr[4][KS];
-  f32x4_t binit[4];
-  {
-    const uint16_t* U = static_cast<const uint16_t*>(p.U);
-    const bool has_bias = p.bias != nullptr;
-    const uint16_t* bsrc = has_bias ? static_cast<const uint16_t*>(p.bias) : U;
-    const int tap = n & 3;
-    const int ltap = tap < W ? tap : W - 1;
-    const int hsh = __builtin_ctz(unsigned(p.H));  // channel c takes group c / H's columns
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int ch = cw + 4 * (n >> 2) + mt;
-      const int64_t col = int64_t(ch >> hsh) * W + ltap;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // ranks from R up to 32 KS are zero (the row read is clamped inside U)
-          const int r = 32 * ks + 8 * q + e;
-          const uint16_t v = U[int64_t(min(r, p.R - 1)) * p.ldu + col];
-          afr[mt][ks][e] = (tap < W && r < p.R) ? v : uint16_t(0);
-        }
-      const int chq = cw + 4 * q + mt;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t v = bsrc[(has_bias ? int64_t(chq >> hsh) * W : 0) + (i < W ? i : W - 1)];
-        binit[mt][i] = (i < W && has_bias) ? Cvt<ET>::of_bits(v) : 0.f;
-      }
-    }
-  }
+  u16x8_t afr[NGT][KS];
+  f32x4_t binit[NGT];
+  generation_operands<ET, W, KS>(p, cw, n, q, afr, binit);
 
   // ---- the W-1 rows before the range: the last rows of ring stage XN - 1 ----
   if constexpr (HR > 0) {
@@ -425,23 +457,23 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
     const unsigned char* zs = smem + Z_OFF + uz * ZSTAGE;
     unsigned char* yt = smem + Y_OFF + (s & 1) * XSTAGE + ytw;
     // filters of token group j (MFMA), issued one group ahead of the convolution
-    auto gen = [&](int j, f32x4_t (&acc)[4]) {
+    auto gen = [&](int j, f32x4_t (&acc)[NGT]) {
       u16x8_t bfr[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8_t*>(zs + zr[ks] + j * ZROW);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < NGT; ++mt) {
         acc[mt] = mma32<ET>(afr[mt][0], bfr[0], binit[mt]);
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32<ET>(afr[mt][ks], bfr[ks], acc[mt]);
       }
     };
-    f32x4_t acc[2][4];
+    f32x4_t acc[2][NGT];
     gen(0, acc[0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j + 1 < 4) gen(j + 1, acc[(j + 1) & 1]);
-      const f32x4_t(&a)[4] = acc[j & 1];
+      const f32x4_t(&a)[NGT] = acc[j & 1];
       float yv[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -449,7 +481,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
         float y = fmaf(a[mt][0], xt, xt);
 #pragma unroll
         for (int k = 1; k < W; ++k) {
-          const float ak = (!SG || idv[j + 4 - k] == idv[j + 4]) ? a[mt][k] : 0.f;
+          const float ak = (!SG || idv[j + 4 - k] == idv[j + 4]) ? tap_of<W>(a, mt, k) : 0.f;
           y = fmaf(ak, xv[j - k - MLO][mt], y);
         }
         yv[mt] = y;
@@ -524,6 +556,13 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   constexpr int XCPR = FL::CPR, XROW = FL::ROW, XSTAGE = FL::STAGE;
   constexpr int ZCPR = FL::ZCPR, ZROW = FL::ZROW;
   constexpr int NS = 2;  // dx stores per wave and step (16 bytes per lane)
+  constexpr int NGT = gen_tiles<W>();
+  // Rows of delay: a token's dx needs the terms of the next W - 1 tokens, so a lane's first
+  // E tokens are complete from its own terms, the others wait for the next lane's (lane 15:
+  // for the next step's lane 0). The step's tile holds tokens t0 - DXH .. t0 + 63 - DXH.
+  constexpr int DXH = W > 4 ? 4 : 3;
+  constexpr int E = 4 - DXH;
+  static_assert(W <= 5, "terms reach the previous lane's tokens only");
 
   const int lane = tid & 63;
   const int q = lane >> 4;
@@ -540,36 +579,9 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   const int cw = c_base + 16 * wv;
 
   // ---- A operands and bias, as in the forward ----
-  u16x8_t afr[4][KS];
-  f32x4_t binit[4];
-  {
-    const uint16_t* U = static_cast<const uint16_t*>(p.U);
-    const bool has_bias = p.bias != nullptr;
-    const uint16_t* bsrc = has_bias ? static_cast<const uint16_t*>(p.bias) : U;
-    const int tap = n & 3;
-    const int ltap = tap < W ? tap : W - 1;
-    const int hsh = __builtin_ctz(unsigned(p.H));  // channel c takes group c / H's columns
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int ch = cw + 4 * (n >> 2) + mt;
-      const int64_t col = int64_t(ch >> hsh) * W + ltap;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // ranks from R up to 32 KS are zero (the row read is clamped inside U)
-          const int r = 32 * ks + 8 * q + e;
-          const uint16_t v = U[int64_t(min(r, p.R - 1)) * p.ldu + col];
-          afr[mt][ks][e] = (tap < W && r < p.R) ? v : uint16_t(0);
-        }
-      const int chq = cw + 4 * q + mt;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t v = bsrc[(has_bias ? int64_t(chq >> hsh) * W : 0) + (i < W ? i : W - 1)];
-        binit[mt][i] = (i < W && has_bias) ? Cvt<ET>::of_bits(v) : 0.f;
-      }
-    }
-  }
+  u16x8_t afr[NGT][KS];
+  f32x4_t binit[NGT];
+  generation_operands<ET, W, KS>(p, cw, n, q, afr, binit);
 
   // ---- per-lane LDS offsets ----
   const int xc = 2 * wv + (q >> 1);  // logical 16-byte chunk of the lane's 4 channels
@@ -592,7 +604,7 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   int trow[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = (n == 15 && j > 0) ? j - 1 : 4 * n + j + 3;
+    const int r = (n == 15 && j >= E) ? j - E : 4 * n + j + DXH;
     trow[j] = r * XROW + ((xc + (r >> 2)) & (XCPR - 1)) * 16 + 8 * (q & 1);
   }
   __amdgpu_buffer_rsrc_t dxr = __builtin_amdgcn_make_buffer_rsrc(
@@ -606,24 +618,24 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
     const int c = (pc - (r >> 2)) & (XCPR - 1);
     ttr[i] = idx * 16;
     trr[i] = r;
-    tgo[i] = int(((r - 3) * p.os1 + c_base + 8 * c) * 2);  // tile row r is token t0 - 3 + r
+    tgo[i] = int(((r - DXH) * p.os1 + c_base + 8 * c) * 2);  // tile row r is token t0 - DXH + r
   }
-  // Stores tile `buf` of step s (tokens t0 - 3 ..): the first step's rows 0..2 belong to
-  // the previous range and the tail's rows 3.. to the next; their offsets are pushed out
-  // of the buffer so the hardware drops them.
+  // Stores tile `buf` of step s (tokens t0 - DXH ..): the first step's rows 0 .. DXH - 1
+  // belong to the previous range and the tail's rows DXH .. to the next; their offsets are
+  // pushed out of the buffer so the hardware drops them.
   auto tflush = [&](int buf, int s, int t0) {
     const unsigned char* tt = smem + FL::T_OFF + buf * XSTAGE;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(tt + ttr[i]);
-      const bool keep = (s > 0 || trr[i] >= 3) && (s < nsteps || trr[i] < 3);
+      const bool keep = (s > 0 || trr[i] >= DXH) && (s < nsteps || trr[i] < DXH);
       __builtin_amdgcn_raw_buffer_store_b128(v, dxr, keep ? tgo[i] + t0 * dstep : int(0x80000000u), 0, 0);
     }
   };
 
-  float pend[3][4];  // lane 15: tokens 61..63 of the previous step, without lane 0's terms
+  float pend[DXH][4];  // lane 15: tokens 64 - DXH .. 63 of the previous step, without lane 0's terms
 #pragma unroll
-  for (int m = 0; m < 3; ++m)
+  for (int m = 0; m < DXH; ++m)
 #pragma unroll
     for (int c = 0; c < 4; ++c) pend[m][c] = 0.f;
 
@@ -666,19 +678,19 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
 #pragma unroll
       for (int i = 0; i < 8; ++i) idv[i] = ids[i];
     }
-    auto gen = [&](int j, f32x4_t (&acc)[4]) {
+    auto gen = [&](int j, f32x4_t (&acc)[NGT]) {
       u16x8_t bfr[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8_t*>(zs + z_at(j, ks));
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < NGT; ++mt) {
         acc[mt] = mma32<ET>(afr[mt][0], bfr[0], binit[mt]);
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32<ET>(afr[mt][ks], bfr[ks], acc[mt]);
       }
     };
     // own[j]: dx of the lane's token j from its own terms; out[m]: terms for the previous
-    // lane's token m (1..3)
+    // lane's token m (E .. 3)
     float own[4][4], out[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -687,19 +699,19 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
         own[j][c] = dyv[j][c];
         out[j][c] = 0.f;
       }
-    f32x4_t acc[2][4];
+    f32x4_t acc[2][NGT];
     gen(0, acc[0]);
 #pragma unroll
     for (int jp = 0; jp < 4; ++jp) {
       if (jp + 1 < 4) gen(jp + 1, acc[(jp + 1) & 1]);
-      const f32x4_t(&a)[4] = acc[jp & 1];
+      const f32x4_t(&a)[NGT] = acc[jp & 1];
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         const int j = jp - k;
         const bool keep = !SG || k == 0 || idv[4 + jp - k] == idv[4 + jp];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float ak = keep ? a[c][k] : 0.f;
+          const float ak = keep ? tap_of<W>(a, c, k) : 0.f;
           if (j >= 0) {
             own[j][c] = fmaf(ak, dyv[jp][c], own[j][c]);
           } else {
@@ -711,15 +723,17 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
     // the next lane's outgoing sums (lane 15: lane 0's, for the previous step's tokens)
     float dxv[4][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dxv[0][c] = own[0][c];
+    for (int m = 0; m < E; ++m)
 #pragma unroll
-    for (int m = 1; m < 4; ++m)
+      for (int c = 0; c < 4; ++c) dxv[m][c] = own[m][c];
+#pragma unroll
+    for (int m = E; m < 4; ++m)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float in = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(out[m][c]), 0x12F, 0xf, 0xf, false));
-        const float base = n == 15 ? pend[m - 1][c] : own[m][c];
+        const float base = n == 15 ? pend[m - E][c] : own[m][c];
         dxv[m][c] = base + in;
-        pend[m - 1][c] = own[m][c];
+        pend[m - E][c] = own[m][c];
       }
     unsigned char* tt = smem + FL::T_OFF + u * XSTAGE;
 #pragma unroll
@@ -730,7 +744,7 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   tflush(nsteps & 1, nsteps, t_first + nsteps * kStep);
   {
     // the filter-gradient role's epilogue: two barriers per chunk of its partial sums
-    constexpr int RT = 2 * KS, TPC = RT < 4 ? RT : 4;
+    constexpr int RT = 2 * KS, TPC = gdu_tiles_per_chunk(W, KS);
 #pragma unroll
     for (int c = 0; c < 2 * (RT / TPC); ++c) __syncthreads();
   }
@@ -1042,7 +1056,7 @@ __device__ __forceinline__ void lowrank_gdu_role(const LowRankParams& p, unsigne
   const int cw = c_base + 16 * wv;
   constexpr int COLS = 64 * W;
   constexpr int PITCH = COLS + 1;
-  constexpr int TPC = RT < 4 ? RT : 4;  // rank tiles per chunk
+  constexpr int TPC = gdu_tiles_per_chunk(W, KS);  // rank tiles per chunk
   static_assert(16 * TPC * PITCH * 4 <= F::BYTES, "staging fits the stages");
   static_assert(16 * TPC * PITCH * 4 <= F::T_OFF, "the staging leaves the dx tiles alone");
   __syncthreads();  // the dx role's last tile is complete before its final stores
@@ -1126,6 +1140,10 @@ __global__ __launch_bounds__(512) void k_lowrank_bwd_fast(const LowRankParams p)
   }
 }
 
+// W = 5 takes a second set of generation tiles (taps 4..7), whose registers fit up to 64
+// ranks: at 128 ranks the fused backward would spill hundreds of registers.
+constexpr bool fast_width_ok(int w, int ks) { return w >= 1 && (w <= 4 || (w == 5 && ks <= 2)); }
+
 // A rank of 32 KS is served when its z transfers split evenly over the waves.
 constexpr bool fwd_fast_rank_ok(int ks) {
   return (ks == 1 || ks == 2 || ks == 4) && (kStep * 4 * ks) % (64 * LRF_NWV) == 0;
@@ -1140,7 +1158,7 @@ constexpr int fwd_fast_resident(int lds_bytes) {
 
 template <typename ET, int W, int KS>
 hipError_t fwd_fast_try(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  if constexpr (fwd_fast_rank_ok(KS)) {
+  if constexpr (fwd_fast_rank_ok(KS) && fast_width_ok(W, KS)) {
     return fwd_fast_inst<ET, W, KS>(p, blocks, s);
   } else {
     return hipErrorInvalidValue;
@@ -1184,7 +1202,7 @@ bool lowrank_fast_rank_ok(const LowRankParams& p) {
 
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   const int ks = (p.R + 31) / 32;
-  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 &&
+  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && fast_width_ok(W, ks) &&
          lowrank_fast_rank_ok(p) && fwd_fast_rank_ok(ks) &&
          p.D % (16 * LRF_NWV) == 0 && p.act16 != 0 &&
          (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) && int64_t(kStep) * p.xs1 < (int64_t(1) << 30) &&
@@ -1229,6 +1247,7 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype 
       case 2: return fwd_fast_ks<ET, 2>(q, pl.blocks, s);
       case 3: return fwd_fast_ks<ET, 3>(q, pl.blocks, s);
       case 4: return fwd_fast_ks<ET, 4>(q, pl.blocks, s);
+      case 5: return fwd_fast_ks<ET, 5>(q, pl.blocks, s);
       default: return hipErrorInvalidValue;
     }
   };
@@ -1236,8 +1255,8 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype 
 }
 
 bool lowrank_bwd_fast_shape_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
-  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && W >= 1 && W <= 4 &&
-         lowrank_fast_rank_ok(p) && p.D % 64 == 0 && p.act16 != 0 &&
+  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) &&
+         fast_width_ok(W, (p.R + 31) / 32) && lowrank_fast_rank_ok(p) && p.D % 64 == 0 && p.act16 != 0 &&
          (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) &&
          int64_t(kStep) * p.dys1 < (int64_t(1) << 30) && int64_t(kStep) * p.zs1 < (int64_t(1) << 30) &&
          int64_t(kStep) * p.xs1 < (int64_t(1) << 30);
@@ -1263,7 +1282,12 @@ hipError_t bwd_fused_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   switch ((p.R + 31) / 32) {
     case 1: return z16 ? bwd_fused_zb<ET, W, 1, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 1, 4>(p, blocks, s);
     case 2: return z16 ? bwd_fused_zb<ET, W, 2, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 2, 4>(p, blocks, s);
-    case 4: return z16 ? bwd_fused_zb<ET, W, 4, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 4, 4>(p, blocks, s);
+    case 4:
+      if constexpr (fast_width_ok(W, 4)) {
+        return z16 ? bwd_fused_zb<ET, W, 4, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 4, 4>(p, blocks, s);
+      } else {
+        return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
 }
@@ -1282,6 +1306,7 @@ hipError_t launch_lowrank_bwd_fused(const LowRankParams& p, int W, dynconv_dtype
       case 2: return bwd_fused_ks<ET, 2>(q, blocks, s);
       case 3: return bwd_fused_ks<ET, 3>(q, blocks, s);
       case 4: return bwd_fused_ks<ET, 4>(q, blocks, s);
+      case 5: return bwd_fused_ks<ET, 5>(q, blocks, s);
       default: return hipErrorInvalidValue;
     }
   };

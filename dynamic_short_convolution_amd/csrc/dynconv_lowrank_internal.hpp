@@ -78,10 +78,10 @@ dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& pla
 // Group sizes the fast bf16 kernels serve: H in {1, 2, 4, 8, 16}, so that a 64-channel
 // slice holds whole groups (each channel loads its group's columns of U and of the bias).
 bool lowrank_fast_group_ok(int H);
-// 16-bit (bf16, float16) fast forward (LDS DMA pipeline; W <= 4, R zero-padded to 32, 64 or
-// 128 ranks (R <= 64 or R > 96) with 16-byte z pieces (aligned rows, R % 8 == 0) or 4-byte
-// ones (R even), those H, 16-byte aligned activation rows, D a multiple of 64). It plans
-// its own token ranges.
+// 16-bit (bf16, float16) fast forward (LDS DMA pipeline; W <= 4, or W = 5 up to 64 ranks;
+// R zero-padded to 32, 64 or 128 ranks (R <= 64 or R > 96) with 16-byte z pieces (aligned
+// rows, R % 8 == 0) or 4-byte ones (R even), those H, 16-byte aligned activation rows, D a
+// multiple of 64). It plans its own token ranges.
 // Packed sequences on the fast forward: contiguous, 16-byte aligned id rows, T % 4 == 0.
 bool lowrank_seg_fast_ok(const LowRankParams& p);
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt);

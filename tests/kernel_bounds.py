@@ -212,8 +212,8 @@ def _seg_loads(acc, b, t0, T):
 
 
 def _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias):
-    """U^T rows and bias of the 64 channels: rank rows clamped to R - 1, taps to W - 1; U
-    stands in for a missing bias (element 0 .. W - 1)."""
+    """U^T rows and bias of the 64 channels: rank rows clamped to R - 1, taps (0..3, and
+    4..7 when W > 4) clamped to W - 1; U stands in for a missing bias (element 0 .. W - 1)."""
     hsh = _log2(H)
     ch = c_base + np.arange(64)
     r = np.minimum(np.arange(32 * KS), R - 1)
@@ -241,9 +241,13 @@ def plan_fwd_fast(B, T, D, KS):
     return nCs, L, (T + L - 1) // L
 
 
+def fast_width_ok(W, KS):
+    return 1 <= W <= 4 or (W == 5 and KS <= 2)
+
+
 def fast_fwd_ok(T, D, W, H, R, xs1, zs1, os1):
     KS = (R + 31) // 32
-    return (KS in (1, 2, 4) and R % 2 == 0 and 1 <= W <= 4 and H in (1, 2, 4, 8, 16) and D % 64 == 0
+    return (KS in (1, 2, 4) and R % 2 == 0 and fast_width_ok(W, KS) and H in (1, 2, 4, 8, 16) and D % 64 == 0
             and (T + STEP) * os1 * 2 < I32 and STEP * xs1 < (1 << 30) and STEP * zs1 < (1 << 30))
 
 
@@ -304,7 +308,7 @@ def plan_lowrank_bwd(B, T, D, W, H, R, lean):
 
 def fast_bwd_ok(T, D, W, H, R, xs1, zs1, dys1, os1):
     KS = (R + 31) // 32
-    return (KS in (1, 2, 4) and R % 2 == 0 and 1 <= W <= 4 and H in (1, 2, 4, 8, 16) and D % 64 == 0
+    return (KS in (1, 2, 4) and R % 2 == 0 and fast_width_ok(W, KS) and H in (1, 2, 4, 8, 16) and D % 64 == 0
             and (T + STEP) * os1 * 2 < I32 and STEP * dys1 < (1 << 30) and STEP * zs1 < (1 << 30)
             and STEP * xs1 < (1 << 30))
 
@@ -342,15 +346,16 @@ def lowrank_bwd_fused(B, T, D, W, H, R, ZB, xs1, zs1, dys1, os1, seg=False, has_
         acc.add("part_dU", 0, rng * R + np.arange(R)[:, None], (c_base >> hsh) * W + np.arange(0, cols, 4)[None, :], 4)
         if want_db:
             acc.add("part_db", 0, rng, (((c_base + np.arange(64)) >> hsh) * W)[:, None] + np.arange(W)[None, :], 1)
-        # dx role (waves 0..3): tile rows r of steps 0 .. nsteps are tokens t0 - 3 + r; the
-        # first step keeps rows >= 3, the tail rows < 3, the rest are pushed out (offset
-        # 0x80000000, past every extent)
+        # dx role (waves 0..3): tile rows r of steps 0 .. nsteps are tokens t0 - DXH + r
+        # (DXH = 3 rows of delay, 4 at W = 5); the first step keeps rows >= DXH, the tail
+        # rows < DXH, the rest are pushed out (offset 0x80000000, past every extent)
         _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias)
+        DXH = 4 if W > 4 else 3
         for s in range(nsteps + 1):
             t0 = t_first + s * STEP
             r = np.arange(STEP)
-            keep = ((s > 0) | (r >= 3)) & ((s < nsteps) | (r < 3))
-            t = t0 - 3 + r[keep]
+            keep = ((s > 0) | (r >= DXH)) & ((s < nsteps) | (r < DXH))
+            t = t0 - DXH + r[keep]
             inb = t < T
             acc.add("dx", b, t[inb][:, None], c_base + 8 * np.arange(8)[None, :], 8)
             acc.dropped += int((~inb).sum()) * 8

@@ -182,8 +182,8 @@ def test_full_lowrank_r64_bwd(dtype):
 
 
 # ---------------------------------------------------------------------------------
-# The 16-bit fast paths (W <= 4, R in {32, 64, 128}, D a multiple of 64, 16-byte aligned
-# rows): token ranges of whole 64-token steps, an x ring in LDS that carries the W-1 rows
+# The 16-bit fast paths (W <= 4 at R up to 128, W = 5 up to 64 ranks; D a multiple of 64,
+# 16-byte aligned rows): token ranges of whole 64-token steps, an x ring in LDS that carries the W-1 rows
 # before each step (forward), dx completed across lanes, ranges and a tail step
 # (backward), buffer stores that drop rows past T.
 # ---------------------------------------------------------------------------------
@@ -191,7 +191,7 @@ def test_full_lowrank_r64_bwd(dtype):
 # z rows of 16-byte pieces where they are 16-byte aligned and R % 8 == 0 (8, 16, 40), of
 # 4-byte pieces otherwise (2, 20, 26, 42, 52, 100: the pages' ranks among them).
 FAST = []
-for W in (1, 2, 3, 4):
+for W in (1, 2, 3, 4, 5):
     for R in (2, 8, 16, 20, 26, 32, 40, 42, 52, 64, 100, 128):
         for (B, T, D) in ((1, 1, 64), (2, 65, 128), (3, 200, 192)):
             FAST.append((W, R, B, T, D))
@@ -210,10 +210,11 @@ def test_fast_no_bias(W, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_fast_fwd_multistep_ranges(dtype):
+@pytest.mark.parametrize("W", [4, 5])
+def test_fast_fwd_multistep_ranges(dtype, W):
     """Token ranges of several 64-token steps (the LDS ring wraps), a partial last step,
     and the rows before each range carried from memory; every element."""
-    B, T, D, W, R = 2, 3000, 2048, 4, 64
+    B, T, D, R = 2, 3000, 2048, 64
     x, z, U, b, _ = _inputs(B, T, D, W, R, dtype, 31)
     y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W)
     assert_close("y", y, lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W), y.dtype)
@@ -236,10 +237,12 @@ def test_fast_fwd_strided_views():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_fast_bwd_multistep_ranges(dtype):
+@pytest.mark.parametrize("W", [4, 5])
+def test_fast_bwd_multistep_ranges(dtype, W):
     """The backward over token ranges of several steps: the rows completed by the tail step
-    of one range and skipped by the first step of the next; every element of dx, dz, dU, db."""
-    B, T, D, W, R = 2, 3000, 2048, 4, 64
+    of one range and skipped by the first step of the next (three rows of delay up to W = 4,
+    four at W = 5); every element of dx, dz, dU, db."""
+    B, T, D, R = 2, 3000, 2048, 64
     x, z, U, b, dy = _inputs(B, T, D, W, R, dtype, 32)
     got = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W)
     check_lowrank_full_bwd(x, z, U, b, dy, W, {"bf16": torch.bfloat16, "f16": torch.float16}[dtype], got)
@@ -252,7 +255,7 @@ def test_fast_bwd_multistep_ranges(dtype):
 HEADWISE = []
 for dtype in ("f32", "bf16", "f16"):
     for H in (2, 4, 16):
-        for W, R in ((1, 16), (3, 40), (4, 64), (5, 128)):
+        for W, R in ((1, 16), (3, 40), (4, 64), (5, 52), (5, 128)):
             HEADWISE.append((dtype, H, W, R))
 
 

@@ -211,12 +211,14 @@ def test_full_packed_lowrank():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("W", [4, 5])
 @pytest.mark.parametrize("R", [20, 64])
-def test_packed_lowrank_fast_padded_rank(R):
+def test_packed_lowrank_fast_padded_rank(R, W):
     """Packed sequences on the fast low-rank kernels with a rank that is zero-padded (20:
-    4-byte z pieces) and one that is not."""
-    B, T, D, W = 2, 640, 256, 4
-    seed = 400 + R
+    4-byte z pieces) and one that is not, at W = 4 and W = 5 (a fifth tap reaching the
+    previous lane's first token)."""
+    B, T, D = 2, 640, 256
+    seed = 400 + R + 13 * W
     x = synth.draw((B, T, D), 1.0, seed, "x", "bf16")
     dy = synth.draw((B, T, D), 1.0, seed, "dy", "bf16")
     z = synth.draw((B, T, R), 1.0, seed, "z", "bf16")

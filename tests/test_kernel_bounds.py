@@ -68,8 +68,8 @@ FAST_RANKS = [2, 20, 26, 64, 100, 128]
 
 
 def _fast_cases():
-    for (B, T, D), W, H, R in itertools.product(FAST_SHAPES, [1, 2, 3, 4], [1, 4, 16], FAST_RANKS):
-        if D % H:
+    for (B, T, D), W, H, R in itertools.product(FAST_SHAPES, [1, 2, 3, 4, 5], [1, 4, 16], FAST_RANKS):
+        if D % H or not kb.fast_width_ok(W, (R + 31) // 32):
             continue
         for ZB in ([16, 4] if R % 8 == 0 else [4]):
             yield B, T, D, W, H, R, ZB
@@ -125,7 +125,7 @@ def test_fast_case_list_is_wide():
     rs = {c[5] for c in FAST_PICK}
     zbs = {c[6] for c in FAST_PICK}
     shapes = {c[:3] for c in FAST_PICK}
-    assert ws == {1, 2, 3, 4} and hs == {1, 4, 16} and rs == set(FAST_RANKS) and zbs == {4, 16}
+    assert ws == {1, 2, 3, 4, 5} and hs == {1, 4, 16} and rs == set(FAST_RANKS) and zbs == {4, 16}
     assert shapes == set(FAST_SHAPES)
 
 
