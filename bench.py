@@ -238,6 +238,8 @@ ROWS = (
     "lowrank_r20_bwd",
     "lowrank_r52_fwd",
     "lowrank_r52_bwd",
+    "lowrank_w5_r64_fwd",
+    "lowrank_w5_r64_bwd",
     "gemm_conv_qkv_fwd",
     "gemm_lowrank_qkv_fwd",
     "reference_unfused_gemm_conv_qkv_fwd",
@@ -339,10 +341,12 @@ def make_row(name, device):
     if name.startswith("lowrank"):
         # lowrank_h4_*: head-wise generation, U of R x (D/4)*W; *_f16_*: float16 storage;
         # lowrank_rN_*: rank N (the pages' models use 16..52; 20 and 52 are zero-padded on
-        # the fast kernels, their contiguous z rows staged in 4-byte pieces)
+        # the fast kernels, their contiguous z rows staged in 4-byte pieces); lowrank_w5_*:
+        # five taps (the widest low-rank filter of the pages' ablation that the ABI takes)
         import re
 
-        B, T, D, W = 8, 4096, 2048, 4
+        B, T, D = 8, 4096, 2048
+        W = int(re.search(r"_w(\d+)_", name).group(1)) if "_w" in name else 4
         R = int(re.search(r"_r(\d+)", name).group(1))
         H = 4 if name.startswith("lowrank_h4") else 1
         dt = torch.float16 if "_f16_" in name else torch.bfloat16
