@@ -342,3 +342,21 @@ def test_full_lowrank_pages_ranks(R):
         assert_close(f"y[{s_}]", y[s_ : s_ + 1], ref, torch.bfloat16)
     got = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W)
     check_lowrank_full_bwd(x, z, U, b, dy, W, torch.bfloat16, got)
+
+
+@pytest.mark.parametrize("W", [4, 5])
+def test_fast_long_sequence(W):
+    """One sequence of 2^17 + 37 tokens on the fast kernels (token ranges of many steps,
+    indices past 2^16, a ragged last step): every element of y, dx, dz, dU, db."""
+    B, T, D, R = 1, (1 << 17) + 37, 64, 64
+    x, z, U, b, dy = _inputs(B, T, D, W, R, "bf16", 91 + W)
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W).cpu()
+    assert_close("y", y, lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W), torch.bfloat16)
+    got = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W)
+    check_lowrank_full_bwd(x, z, U, b, dy, W, torch.bfloat16, got)
+
+
+def test_many_sequences_lowrank():
+    """1024 sequences of 37 tokens (each shorter than one 64-token step) on the fast
+    kernels."""
+    _check(1024, 37, 64, 4, 64, "bf16", seed=1024)

@@ -299,3 +299,18 @@ def test_static_dw_reduce_paths(D, offset):
     assert_close("dw_static", dw, rdw, torch.float32, rtol=1e-5, atol=1e-5)
     if offset:
         assert torch.isnan(buf[:offset]).all()
+
+
+@pytest.mark.parametrize("H,static", [(1, False), (4, False), (1, True)])
+def test_long_sequence(H, static):
+    """One sequence of 2^17 + 37 tokens: token indices past 2^16, many time chunks, a
+    ragged last chunk; every element."""
+    _check_case(1, (1 << 17) + 37, 128, 4, H, "bf16", static, seed=171 + H)
+
+
+@pytest.mark.parametrize("B,T,D", [(1024, 37, 64), (1, 17, 16384)])
+def test_many_sequences_and_wide_rows(B, T, D):
+    """Grids large along the batch (1024 sequences of 37 tokens) and along the channels
+    (one 16384-channel row per token): per-channel, head-wise and static."""
+    for H, static in ((1, False), (16, False), (1, True)):
+        _check_case(B, T, D, 4, H, "bf16", static, seed=B + D + H)
