@@ -107,6 +107,7 @@ __device__ __forceinline__ ZPiece z_piece(int idx, int R, int (*rot)(int)) {
   return ZPiece{row, gb, gb / 2 < R};
 }
 __device__ __forceinline__ int rot_quarter(int row) { return row >> 2; }
+__device__ __forceinline__ int rot_double(int row) { return 2 * row; }
 // Stages shared by both roles of the fused backward: the four rows of a transposing read
 // (8q + e, e = 0..3) land on distinct chunk positions as with 2 row, and the 16 rows
 // 4n + j that the dx role reads at once spread over 8 positions.
@@ -515,7 +516,7 @@ hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) 
 }
 
 // ---------------------------------------------------------------------------------
-// Backward dx (the dx role of k_lowrank_bwd_fast):
+// Backward dx, k_lowrank_bwd_dx_fast:
 //   dx_s = dy_s + sum_k w_k(s + k) dy_{s+k}    (the adjoint of eq. 2 + eq. 3)
 // Same workgroup shape, staging and filter generation as the forward, with dy in place
 // of x (dx needs no x). Lane (n, q) holds the filters of tokens 4n .. 4n+3 of the step
@@ -529,6 +530,25 @@ hipError_t fwd_fast_inst(const LowRankParams& p, int64_t blocks, hipStream_t s) 
 // three rows, and the first step's first three rows belong to the previous range.
 // dy rows at or past T are zeroed, so the tail contributes nothing past the sequence.
 // ---------------------------------------------------------------------------------
+template <int KS, int SG = 0, int ZB = 16>
+struct BwdDxFast {
+  static constexpr int NWV = 4;
+  // SG: packed sequences; the ids of tokens t0 - 4 .. t0 + 63 ride with each step's dy
+  // (one more transfer per wave, issued first)
+  static constexpr int SCH = 17, SPW = 5, SSTAGE = NWV * SPW * 16;
+  static constexpr int CPB = 64;
+  static constexpr int XCPR = 8, XROW = 128;
+  static constexpr int XSTAGE = kStep * XROW;        // dy stage, dx tile
+  static constexpr int ZCPR = 4 * KS;
+  static constexpr int ZROW = 16 * ZCPR;
+  static constexpr int ZSTAGE = kStep * ZROW;
+  static constexpr int Z_OFF = 2 * XSTAGE;            // two dy stages
+  static constexpr int T_OFF = Z_OFF + 2 * ZSTAGE;    // two z stages, then two dx tiles
+  static constexpr int S_OFF = T_OFF + 2 * XSTAGE;    // then two id stages (SG)
+  static constexpr int BYTES = S_OFF + (SG ? 2 * SSTAGE : 0);
+  static constexpr int DI = 2, ZI = kStep * ZROW / (64 * ZB) / NWV, ND = DI + ZI, NS = 2;
+};
+
 // Layout of the fused backward (k_lowrank_bwd_fast, 8 waves): x in a ring of 4 steps, dy,
 // z (and the ids of packed sequences) in 3 stages each, loaded two steps ahead by the
 // filter-gradient role, then the dx role's two output tiles.
@@ -547,15 +567,17 @@ struct BwdFused {
   static constexpr int XI = 2, DI = 2, ZI = kStep * ZROW / (64 * ZB) / 4, ND = XI + DI + ZI + SG;
 };
 
-// The dx computation: waves 0..3 of the fused backward, reading dy, z and ids from the
-// stages of layout FL that the other role fills, writing its tiles at FL::T_OFF, and running
-// one barrier per step (the range's steps and the tail step) plus the epilogue's.
-template <typename ET, int W, int KS, int SG, int ZB, class FL>
+// The dx computation. Standalone (FUSED false): its own kernel, staging dy and z itself.
+// FUSED: waves 0..3 of the fused backward, reading dy, z and ids from the stages of layout
+// FL that the other role fills, writing its tiles at FL::T_OFF, and running one barrier per
+// step (the range's steps and the tail step) plus the epilogue's.
+template <typename ET, int W, int KS, int SG, int ZB, bool FUSED, class FL>
 __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned char* smem, int tid,
                                                 uint32_t lb) {
-  constexpr int XCPR = FL::CPR, XROW = FL::ROW, XSTAGE = FL::STAGE;
-  constexpr int ZCPR = FL::ZCPR, ZROW = FL::ZROW;
-  constexpr int NS = 2;  // dx stores per wave and step (16 bytes per lane)
+  using F = BwdDxFast<KS, SG, ZB>;
+  constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
+  constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF;
+  constexpr int T_OFF = FUSED ? FL::T_OFF : F::T_OFF;
   constexpr int NGT = gen_tiles<W>();
   // Rows of delay: a token's dx needs the terms of the next W - 1 tokens, so a lane's first
   // E tokens are complete from its own terms, the others wait for the next lane's (lane 15:
@@ -572,33 +594,120 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   lb /= uint32_t(p.nCsL);
   const int tr = int(lb % uint32_t(p.nTr));
   const int b = int(lb / uint32_t(p.nTr));
-  const int c_base = cs * 64;
+  const int c_base = cs * F::CPB;
   const int t_first = tr * p.Ltok;
   const int t_end = min(p.T, t_first + p.Ltok);
   const int nsteps = (t_end - t_first + kStep - 1) / kStep;
+  const char* dyc = reinterpret_cast<const char*>(static_cast<const ET*>(p.dy) + b * p.dys0 + c_base);
+  const char* zc = reinterpret_cast<const char*>(static_cast<const ET*>(p.z) + b * p.zs0);
   const int cw = c_base + 16 * wv;
+
+  // ---- LDS DMA of a step's dy and z rows (rows past T - 1 read row T - 1) ----
+  uint32_t doff[F::DI], zoff[F::ZI];
+  int drl[F::DI], zrl[F::ZI];
+  bool zval[F::ZI];
+#pragma unroll
+  for (int i = 0; i < F::DI; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int rl = idx / XCPR, pc = idx % XCPR;
+    const int c = (pc - (rl >> 2)) & (XCPR - 1);
+    drl[i] = rl;
+    doff[i] = uint32_t(rl * int(p.dys1) + 8 * c) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < F::ZI; ++i) {
+    const ZPiece zp = z_piece<ZB, ZROW>((wv + 4 * i) * 64 + lane, p.R, rot_quarter);
+    zrl[i] = zp.row;
+    zval[i] = zp.valid;
+    zoff[i] = uint32_t(zp.row * int(p.zs1)) * 2u + uint32_t(zp.byte);
+  }
+  const char* zero = reinterpret_cast<const char*>(g_lr_zero16);
+  // segment ids (SG): chunk sc = 5 wv + lane holds the ids of tokens t0 - 4 + 4 sc .. + 3
+  const int sc = F::SPW * wv + lane;
+  const bool sact = SG && lane < F::SPW && sc < F::SCH;
+  const char* sgc = SG ? reinterpret_cast<const char*>(p.seg + b * p.ss0) : nullptr;
+  auto issue = [&](int st, int t0) {
+    unsigned char* ds = smem + st * XSTAGE;
+    unsigned char* zs = smem + Z_OFF + st * ZSTAGE;
+    if constexpr (SG) {
+      if (sact) {
+        const int tk = min(max(t0 - 4 + 4 * sc, 0), p.T - 4);
+        dma16(sgc + int64_t(tk) * 4, smem + F::S_OFF + st * F::SSTAGE + wv * F::SPW * 16);
+      }
+    }
+    if (t0 + kStep <= p.T) {
+      const char* dg = dyc + int64_t(t0) * p.dys1 * 2;
+      const char* zg = zc + int64_t(t0) * p.zs1 * 2;
+#pragma unroll
+      for (int i = 0; i < F::DI; ++i) dma16(dg + doff[i], ds + (wv + 4 * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < F::ZI; ++i) dmaz<ZB>(zval[i] ? zg + zoff[i] : zero, zs + (wv + 4 * i) * (64 * ZB));
+    } else {
+#pragma unroll
+      for (int i = 0; i < F::DI; ++i) {
+        const int t = min(t0 + drl[i], p.T - 1);
+        dma16(dyc + (int64_t(t) - drl[i]) * p.dys1 * 2 + doff[i], ds + (wv + 4 * i) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < F::ZI; ++i) {
+        const int t = min(t0 + zrl[i], p.T - 1);
+        dmaz<ZB>(zval[i] ? zc + (int64_t(t) - zrl[i]) * p.zs1 * 2 + zoff[i] : zero, zs + (wv + 4 * i) * (64 * ZB));
+      }
+    }
+  };
 
   // ---- A operands and bias, as in the forward ----
   u16x8_t afr[NGT][KS];
   f32x4_t binit[NGT];
   generation_operands<ET, W, KS>(p, cw, n, q, afr, binit);
+  if constexpr (!FUSED) issue(0, t_first);
 
   // ---- per-lane LDS offsets ----
   const int xc = 2 * wv + (q >> 1);  // logical 16-byte chunk of the lane's 4 channels
-  // dy row 4n + j and the chunk 4 ks + q of z row 4n + j inside a step's stage (rows
-  // rotated by rot_fused)
+  const int drd = 4 * n * XROW + ((xc + n) & (XCPR - 1)) * 16 + 8 * (q & 1);  // dy row 4n (+ j * XROW)
+  int zr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) zr[ks] = 4 * n * ZROW + ((4 * ks + q + n) % ZCPR) * 16;
+  // dy row 4n + j and the chunk 4 ks + q of z row 4n + j inside a step's stage: rotation
+  // row / 4 in the kernel's own stages, the shared one in the fused kernel's
   auto dy_at = [&](int j) -> int {
-    const int r = 4 * n + j;
-    return r * XROW + ((xc + rot_fused(r)) & (XCPR - 1)) * 16 + 8 * (q & 1);
-  };
-  auto z_at = [&](int j, int ks) -> int {
-    const int r = 4 * n + j;
-    return r * ZROW + ((4 * ks + q + rot_fused(r)) % ZCPR) * 16;
+    if constexpr (FUSED) {
+      const int r = 4 * n + j;
+      return r * XROW + ((xc + rot_fused(r)) & (XCPR - 1)) * 16 + 8 * (q & 1);
+    } else {
+      return drd + j * XROW;
+    }
   };
   // byte offsets of step s's dy, z and id stages
-  auto dy_stage = [&](int s) -> int { return FL::D_OFF + (s % FL::SN) * FL::STAGE; };
-  auto z_stage = [&](int s) -> int { return FL::Z_OFF + (s % FL::SN) * FL::ZSTAGE; };
-  auto id_stage = [&](int s) -> int { return FL::S_OFF + (s % FL::SN) * FL::SSTAGE; };
+  auto dy_stage = [&](int s) -> int {
+    if constexpr (FUSED) {
+      return FL::D_OFF + (s % FL::SN) * FL::STAGE;
+    } else {
+      return (s & 1) * XSTAGE;
+    }
+  };
+  auto z_stage = [&](int s) -> int {
+    if constexpr (FUSED) {
+      return FL::Z_OFF + (s % FL::SN) * FL::ZSTAGE;
+    } else {
+      return Z_OFF + (s & 1) * ZSTAGE;
+    }
+  };
+  auto id_stage = [&](int s) -> int {
+    if constexpr (FUSED) {
+      return FL::S_OFF + (s % FL::SN) * FL::SSTAGE;
+    } else {
+      return F::S_OFF + (s & 1) * F::SSTAGE;
+    }
+  };
+  auto z_at = [&](int j, int ks) -> int {
+    if constexpr (FUSED) {
+      const int r = 4 * n + j;
+      return r * ZROW + ((4 * ks + q + rot_fused(r)) % ZCPR) * 16;
+    } else {
+      return zr[ks] + j * ZROW;
+    }
+  };
   // dx tile row of the lane's output j: token 4n + j sits in row 4n + j + 3; lane 15's
   // outputs 1..3 are the previous step's tokens 61..63, rows 0..2
   int trow[4];
@@ -610,9 +719,9 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   __amdgpu_buffer_rsrc_t dxr = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<ET*>(p.out) + b * p.os0, 0, int((int64_t(p.T - 1) * p.os1 + p.D) * 2), kBufWord3);
   const int dstep = int(p.os1 * 2);
-  int ttr[NS], tgo[NS], trr[NS];
+  int ttr[F::NS], tgo[F::NS], trr[F::NS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
+  for (int i = 0; i < F::NS; ++i) {
     const int idx = (wv + 4 * i) * 64 + lane;
     const int r = idx / XCPR, pc = idx % XCPR;
     const int c = (pc - (r >> 2)) & (XCPR - 1);
@@ -624,9 +733,9 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   // belong to the previous range and the tail's rows DXH .. to the next; their offsets are
   // pushed out of the buffer so the hardware drops them.
   auto tflush = [&](int buf, int s, int t0) {
-    const unsigned char* tt = smem + FL::T_OFF + buf * XSTAGE;
+    const unsigned char* tt = smem + T_OFF + buf * XSTAGE;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = 0; i < F::NS; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(tt + ttr[i]);
       const bool keep = (s > 0 || trr[i] >= DXH) && (s < nsteps || trr[i] < DXH);
       __builtin_amdgcn_raw_buffer_store_b128(v, dxr, keep ? tgo[i] + t0 * dstep : int(0x80000000u), 0, 0);
@@ -643,9 +752,12 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
     const int t0 = t_first + s * kStep;
     const int u = s & 1;
     if (s >= 2) {
-      vm_wait_barrier<NS>();  // the stores of step s - 2 are done: their tile is free
+      vm_wait_barrier<F::NS>();
     } else {
       vm_wait_barrier<0>();
+    }
+    if constexpr (!FUSED) {
+      if (s < nsteps) issue(u ^ 1, t0 + kStep);
     }
     if (s > 0) tflush(u ^ 1, s - 1, t0 - kStep);
     // dy of the lane's tokens 4n .. 4n+3, 4 channels; zero at or past T
@@ -735,14 +847,14 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
         dxv[m][c] = base + in;
         pend[m - E][c] = own[m][c];
       }
-    unsigned char* tt = smem + FL::T_OFF + u * XSTAGE;
+    unsigned char* tt = smem + T_OFF + u * XSTAGE;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x2*>(tt + trow[j]) = u32x2{Cvt<ET>::pack2(dxv[j][0], dxv[j][1]), Cvt<ET>::pack2(dxv[j][2], dxv[j][3])};
   }
   __syncthreads();
   tflush(nsteps & 1, nsteps, t_first + nsteps * kStep);
-  {
+  if constexpr (FUSED) {
     // the filter-gradient role's epilogue: two barriers per chunk of its partial sums
     constexpr int RT = 2 * KS, TPC = gdu_tiles_per_chunk(W, KS);
 #pragma unroll
@@ -751,6 +863,12 @@ __device__ __forceinline__ void lowrank_dx_role(const LowRankParams& p, unsigned
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
+template <typename ET, int W, int KS, int SG, int ZB>
+__global__ __launch_bounds__(256) void k_lowrank_bwd_dx_fast(const LowRankParams p) {
+  using F = BwdDxFast<KS, SG, ZB>;
+  __shared__ __align__(16) unsigned char smem[F::BYTES];
+  lowrank_dx_role<ET, W, KS, SG, ZB, false, F>(p, smem, threadIdx.x, xcd_logical_block(blockIdx.x, gridDim.x));
+}
 
 
 // Transposing LDS reads (ds_read_b64_tr_b16) of N 8-byte rows at 32-bit LDS byte offsets,
@@ -796,8 +914,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // ---------------------------------------------------------------------------------
-// Backward filter gradient (the filter-gradient role of k_lowrank_bwd_fast): per token
-// range and 64-channel slice,
+// Backward filter gradient, k_lowrank_bwd_gdu_fast: per token range and 64-channel slice,
 // float32 partial sums of
 //   dU[r][g W + k] = sum_t z_t[r] g_t[g W + k],  db[g W + k] = sum_t g_t[g W + k],
 //   g_t[c W + k] = dy_t[c] x_{t-k}[c]
@@ -809,21 +926,42 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // choice of registers) give g in the A layout directly, and the z columns give B. So g
 // never goes to LDS. x sits in a ring of 4 steps (its rows before a step are the previous
 // step's), dy and z in 3 stages each, all filled by LDS DMA two steps ahead; a row's
-// 16-byte chunks are rotated by rot_fused(row) so that the 4 rows of a transposing read hit
+// 16-byte chunks are rotated by 2 row so that the 4 rows of a transposing read hit
 // distinct banks.
 // ---------------------------------------------------------------------------------
-// The g / dU / db partial sums: waves 4..7 of the fused backward with layout F (BwdFused).
-// They also stage dy and z for the tail step (s == nsteps) that the dx role needs, stay in
-// step with it (one barrier per step, the tail included) and meet its epilogue barriers.
-template <typename ET, int W, int KS, int SG, int ZB, class F>
+template <int KS, int SG_ = 0, int ZB = 16>
+struct BwdGduFast {
+  static constexpr int CPR = 8, ROW = 128, STAGE = kStep * ROW;  // x, dy: 64 channels
+  static constexpr int ZCPR = 4 * KS, ZROW = 16 * ZCPR, ZSTAGE = kStep * ZROW;
+  // SG: packed sequences. The ids of tokens t0 - 4 .. t0 + 63 ride with each step (one
+  // more transfer per wave, issued first). The stages then load one step ahead instead of
+  // two (two dy / z stages, 16 KiB less), which keeps two workgroups per CU at R = 64 with
+  // the id stages (80 KiB each without them).
+  static constexpr int SG = SG_;
+  static constexpr int DIST = SG ? 1 : 2;   // steps loaded ahead
+  static constexpr int XN = 4;   // x ring: the step, the previous one, two in flight
+  static constexpr int SN = DIST + 1;       // dy and z stages: the step and those in flight
+  static constexpr int SCH = 17, SPW = 5, SSTAGE = 4 * SPW * 16;
+  static constexpr int D_OFF = XN * STAGE;
+  static constexpr int Z_OFF = D_OFF + SN * STAGE;
+  static constexpr int S_OFF = Z_OFF + SN * ZSTAGE;
+  static constexpr int BYTES = S_OFF + (SG ? SN * SSTAGE : 0);
+  static constexpr int XI = 2, DI = 2, ZI = kStep * ZROW / (64 * ZB) / 4, ND = XI + DI + ZI + SG;
+};
+
+// The g / dU / db partial sums. Standalone (FUSED false): its own kernel with layout
+// BwdGduFast. FUSED: waves 4..7 of the fused backward with layout BwdFused, which also
+// stage dy and z for the tail step (s == nsteps) that the dx role needs, stay in step with
+// it (one barrier per step, the tail included) and meet its epilogue barriers.
+template <typename ET, int W, int KS, int SG, int ZB, bool FUSED, class F>
 __device__ __forceinline__ void lowrank_gdu_role(const LowRankParams& p, unsigned char* smem, int tid,
                                                  uint32_t lb) {
   constexpr int CPR = F::CPR, ROW = F::ROW, STAGE = F::STAGE, XN = F::XN;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, D_OFF = F::D_OFF, Z_OFF = F::Z_OFF;
   constexpr int RT = 2 * KS;  // 16-rank tiles
   constexpr int HR = W - 1;
-  constexpr int TAIL = 1;  // the dx role's tail step
-  auto rot = [](int row) { return rot_fused(row); };
+  constexpr int TAIL = FUSED ? 1 : 0;  // the dx role's tail step
+  auto rot = [](int row) { return FUSED ? rot_fused(row) : rot_double(row); };
 
   const int lane = tid & 63;
   const int q = lane >> 4;
@@ -856,7 +994,7 @@ __device__ __forceinline__ void lowrank_gdu_role(const LowRankParams& p, unsigne
   }
 #pragma unroll
   for (int i = 0; i < F::ZI; ++i) {
-    const ZPiece zp = z_piece<ZB, ZROW>((wv + 4 * i) * 64 + lane, p.R, rot_fused);
+    const ZPiece zp = z_piece<ZB, ZROW>((wv + 4 * i) * 64 + lane, p.R, FUSED ? rot_fused : rot_double);
     zrl[i] = zp.row;
     zval[i] = zp.valid;
     zoff[i] = uint32_t(zp.row * int(p.zs1)) * 2u + uint32_t(zp.byte);
@@ -952,7 +1090,7 @@ __device__ __forceinline__ void lowrank_gdu_role(const LowRankParams& p, unsigne
       vm_wait_barrier<0>();
     }
     if (s + F::DIST < nsteps + TAIL) issue(s + F::DIST, t0 + F::DIST * kStep);
-    if (s == nsteps) continue;  // the tail step's rows are the dx role's alone
+    if (FUSED && s == nsteps) continue;  // the tail step's rows are the dx role's alone
     const int ux = s % XN;
     const uint32_t dsa = lds0 + D_OFF + (s % F::SN) * STAGE;
     const uint32_t zsa = lds0 + Z_OFF + (s % F::SN) * ZSTAGE;
@@ -1058,8 +1196,10 @@ __device__ __forceinline__ void lowrank_gdu_role(const LowRankParams& p, unsigne
   constexpr int PITCH = COLS + 1;
   constexpr int TPC = gdu_tiles_per_chunk(W, KS);  // rank tiles per chunk
   static_assert(16 * TPC * PITCH * 4 <= F::BYTES, "staging fits the stages");
-  static_assert(16 * TPC * PITCH * 4 <= F::T_OFF, "the staging leaves the dx tiles alone");
-  __syncthreads();  // the dx role's last tile is complete before its final stores
+  if constexpr (FUSED) {
+    static_assert(16 * TPC * PITCH * 4 <= F::T_OFF, "the staging leaves the dx tiles alone");
+    __syncthreads();  // the dx role's last tile is complete before its final stores
+  }
   // Head-wise generation (H consecutive channels share a group's columns, H <= 16): the H
   // channels of a group are summed here, in channel order, so that one partial per
   // (sequence, token range) and group column is written.
@@ -1118,6 +1258,13 @@ __device__ __forceinline__ void lowrank_gdu_role(const LowRankParams& p, unsigne
   }
 }
 
+template <typename ET, int W, int KS, int SG, int ZB>
+__global__ __launch_bounds__(256) void k_lowrank_bwd_gdu_fast(const LowRankParams p) {
+  using F = BwdGduFast<KS, SG, ZB>;
+  __shared__ __align__(16) unsigned char smem[F::BYTES];
+  lowrank_gdu_role<ET, W, KS, SG, ZB, false, F>(p, smem, threadIdx.x, xcd_logical_block(blockIdx.x, gridDim.x));
+}
+
 // ---------------------------------------------------------------------------------
 // Fused backward, k_lowrank_bwd_fast: dx and the g / dU / db partial sums in one pass over
 // x, dy and z. A workgroup of 8 waves owns one (sequence, token range, 64-channel slice):
@@ -1134,9 +1281,9 @@ __global__ __launch_bounds__(512) void k_lowrank_bwd_fast(const LowRankParams p)
   __shared__ __align__(16) unsigned char smem[FL::BYTES];
   const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   if (__builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 8) == 0) {
-    lowrank_dx_role<ET, W, KS, SG, ZB, FL>(p, smem, int(threadIdx.x) & 255, lb);
+    lowrank_dx_role<ET, W, KS, SG, ZB, true, FL>(p, smem, int(threadIdx.x) & 255, lb);
   } else {
-    lowrank_gdu_role<ET, W, KS, SG, ZB, FL>(p, smem, int(threadIdx.x) & 255, lb);
+    lowrank_gdu_role<ET, W, KS, SG, ZB, true, FL>(p, smem, int(threadIdx.x) & 255, lb);
   }
 }
 
@@ -1254,6 +1401,31 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype 
   return dt == DYNCONV_F16 ? by_w(f16_t{}) : by_w(bf16_t{});
 }
 
+namespace {
+
+// The standalone dx and g / dU / db kernels serve 128 ranks (the fused kernel's 8 waves
+// would spill there).
+template <typename ET, int W, int KS, int ZB>
+hipError_t bwd_dx_zb(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 1, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_lowrank_bwd_dx_fast<ET, W, KS, 0, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename ET, int W>
+hipError_t bwd_dx_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  if constexpr (W <= 4) {
+    if ((p.R + 31) / 32 == 4)
+      return z_pieces16(p) ? bwd_dx_zb<ET, W, 4, 16>(p, blocks, s) : bwd_dx_zb<ET, W, 4, 4>(p, blocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
 bool lowrank_bwd_fast_shape_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) &&
          fast_width_ok(W, (p.R + 31) / 32) && lowrank_fast_rank_ok(p) && p.D % 64 == 0 && p.act16 != 0 &&
@@ -1262,8 +1434,25 @@ bool lowrank_bwd_fast_shape_ok(const LowRankParams& p, int W, dynconv_dtype dt) 
          int64_t(kStep) * p.xs1 < (int64_t(1) << 30);
 }
 
-bool lowrank_bwd_fast(const LowRankParams& p, int W, dynconv_dtype dt) {
-  return (p.seg == nullptr || lowrank_seg_fast_ok(p)) && lowrank_bwd_fast_shape_ok(p, W, dt);
+namespace {
+
+template <typename ET, int W, int KS, int ZB>
+hipError_t bwd_gdu_zb(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  if (p.seg != nullptr) {
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 1, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_lowrank_bwd_gdu_fast<ET, W, KS, 0, ZB>), dim3(unsigned(blocks)), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename ET, int W>
+hipError_t bwd_gdu_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
+  if constexpr (W <= 4) {
+    if ((p.R + 31) / 32 == 4)
+      return z_pieces16(p) ? bwd_gdu_zb<ET, W, 4, 16>(p, blocks, s) : bwd_gdu_zb<ET, W, 4, 4>(p, blocks, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename ET, int W, int KS, int ZB>
@@ -1282,31 +1471,59 @@ hipError_t bwd_fused_ks(const LowRankParams& p, int64_t blocks, hipStream_t s) {
   switch ((p.R + 31) / 32) {
     case 1: return z16 ? bwd_fused_zb<ET, W, 1, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 1, 4>(p, blocks, s);
     case 2: return z16 ? bwd_fused_zb<ET, W, 2, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 2, 4>(p, blocks, s);
-    case 4:
-      if constexpr (fast_width_ok(W, 4)) {
-        return z16 ? bwd_fused_zb<ET, W, 4, 16>(p, blocks, s) : bwd_fused_zb<ET, W, 4, 4>(p, blocks, s);
-      } else {
-        return hipErrorInvalidValue;
-      }
     default: return hipErrorInvalidValue;
   }
 }
 
+// dx by k_lowrank_bwd_dx_fast over its own token ranges (about 512 workgroups of 4 waves),
+// then the g / dU / db partial sums by k_lowrank_bwd_gdu_fast over the planned ranges.
+template <typename ET, int W>
+hipError_t bwd_split(const LowRankParams& p, hipStream_t s) {
+  const int nCs = p.D / 64;
+  int64_t per_seq = (512 + int64_t(p.B) * nCs - 1) / (int64_t(p.B) * nCs);
+  const int64_t max_ranges = (p.T + kStep - 1) / kStep;
+  if (per_seq > max_ranges) per_seq = max_ranges;
+  if (per_seq < 1) per_seq = 1;
+  int64_t L = (p.T + per_seq - 1) / per_seq;
+  L = (L + kStep - 1) / kStep * kStep;
+  LowRankParams q = p;
+  q.cs0 = 0;
+  q.nCsL = nCs;
+  q.nCs = nCs;
+  q.Ltok = int(L);
+  q.nTr = int((p.T + L - 1) / L);
+  hipError_t e = bwd_dx_ks<ET, W>(q, int64_t(p.B) * q.nTr * nCs, s);
+  if (e != hipSuccess) return e;
+  LowRankParams r = p;
+  r.cs0 = 0;
+  r.nCsL = nCs;
+  return bwd_gdu_ks<ET, W>(r, int64_t(p.B) * p.nTr * nCs, s);
+}
+
+}  // namespace
+
+bool lowrank_bwd_fast(const LowRankParams& p, int W, dynconv_dtype dt) {
+  return (p.seg == nullptr || lowrank_seg_fast_ok(p)) && lowrank_bwd_fast_shape_ok(p, W, dt);
+}
+
 hipError_t launch_lowrank_bwd_fused(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t s) {
-  // one workgroup of 8 waves per (sequence, planned token range, 64-channel slice)
+  // up to 64 ranks: one workgroup of 8 waves per (sequence, planned token range, 64-channel
+  // slice) running both roles; 128 ranks: the two roles as kernels of their own (4-wave
+  // workgroups, whose registers hold the g / dU / db role's 128 accumulators per lane)
   LowRankParams q = p;
   q.cs0 = 0;
   q.nCsL = p.D / 64;
   q.nCs = q.nCsL;
   const int64_t blocks = int64_t(p.B) * p.nTr * q.nCsL;
+  const bool split = (p.R + 31) / 32 == 4;
   auto by_w = [&](auto tag) -> hipError_t {
     using ET = decltype(tag);
     switch (W) {
-      case 1: return bwd_fused_ks<ET, 1>(q, blocks, s);
-      case 2: return bwd_fused_ks<ET, 2>(q, blocks, s);
-      case 3: return bwd_fused_ks<ET, 3>(q, blocks, s);
-      case 4: return bwd_fused_ks<ET, 4>(q, blocks, s);
-      case 5: return bwd_fused_ks<ET, 5>(q, blocks, s);
+      case 1: return split ? bwd_split<ET, 1>(p, s) : bwd_fused_ks<ET, 1>(q, blocks, s);
+      case 2: return split ? bwd_split<ET, 2>(p, s) : bwd_fused_ks<ET, 2>(q, blocks, s);
+      case 3: return split ? bwd_split<ET, 3>(p, s) : bwd_fused_ks<ET, 3>(q, blocks, s);
+      case 4: return split ? bwd_split<ET, 4>(p, s) : bwd_fused_ks<ET, 4>(q, blocks, s);
+      case 5: return split ? hipErrorInvalidValue : bwd_fused_ks<ET, 5>(q, blocks, s);
       default: return hipErrorInvalidValue;
     }
   };

@@ -89,10 +89,10 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype 
 // Shapes and layouts the 16-bit fast backward serves (the forward's conditions, on x, dy,
 // z and dx).
 bool lowrank_bwd_fast_shape_ok(const LowRankParams& p, int W, dynconv_dtype dt);
-// The 16-bit fast backward's dx and g / dU / db partial sums in one kernel (8 waves: dx and
-// g / dU / db roles sharing the staged dy and z), over the planned token ranges (Ltok, nTr)
-// and 64-channel slices; one partial per token range and group column (a group's H
-// channels summed inside the workgroup).
+// The 16-bit fast backward's dx and g / dU / db partial sums over the planned token ranges
+// (Ltok, nTr) and 64-channel slices; one partial per token range and group column (a
+// group's H channels summed inside the workgroup). Up to 64 ranks one kernel of 8 waves
+// runs both (the roles share the staged dy and z); at 128 ranks two kernels of 4 waves.
 hipError_t launch_lowrank_bwd_fused(const LowRankParams& p, int W, dynconv_dtype dt, hipStream_t stream);
 // Whether the backward runs on the fast kernels (dx, then g / dU / db): they write
 // B * nTr partials per filter column, the general kernel B * nTr * H.

@@ -314,8 +314,13 @@ def fast_bwd_ok(T, D, W, H, R, xs1, zs1, dys1, os1):
 
 
 def lowrank_bwd_fused(B, T, D, W, H, R, ZB, xs1, zs1, dys1, os1, seg=False, has_bias=True, want_db=True):
+    """The fast backward: up to 64 ranks k_lowrank_bwd_fast (both roles, the gradient role
+    staging steps 0 .. nsteps for both); at 128 ranks k_lowrank_bwd_dx_fast over its own
+    token ranges (about 512 workgroups; it stages dy and z itself, steps 0 .. nsteps) and
+    k_lowrank_bwd_gdu_fast over the planned ranges (steps 0 .. nsteps - 1)."""
     assert fast_bwd_ok(T, D, W, H, R, xs1, zs1, dys1, os1) and (ZB == 4 or R % 8 == 0)
     _, L, nTr, _, KS = plan_lowrank_bwd(B, T, D, W, H, R, lean=True)
+    split = KS == 4
     slices = D // 64
     acc = Accesses()
     HR = W - 1
@@ -329,8 +334,9 @@ def lowrank_bwd_fused(B, T, D, W, H, R, ZB, xs1, zs1, dys1, os1, seg=False, has_
         c_base, t_first = cs * 64, tr * L
         t_end = min(T, t_first + L)
         nsteps = (t_end - t_first + STEP - 1) // STEP
-        # filter-gradient role (waves 4..7): stages of steps 0 .. nsteps (dx's tail step too)
-        for s in range(nsteps + 1):
+        # filter-gradient role (waves 4..7): stages of steps 0 .. nsteps (dx's tail step too);
+        # the standalone gradient kernel stops before the tail step
+        for s in range(nsteps + (0 if split else 1)):
             t0 = t_first + s * STEP
             rows = step_rows(t0, rl, T)
             acc.add("x", b, rows, c_base + 8 * c, 8)
@@ -346,22 +352,51 @@ def lowrank_bwd_fused(B, T, D, W, H, R, ZB, xs1, zs1, dys1, os1, seg=False, has_
         acc.add("part_dU", 0, rng * R + np.arange(R)[:, None], (c_base >> hsh) * W + np.arange(0, cols, 4)[None, :], 4)
         if want_db:
             acc.add("part_db", 0, rng, (((c_base + np.arange(64)) >> hsh) * W)[:, None] + np.arange(W)[None, :], 1)
-        # dx role (waves 0..3): tile rows r of steps 0 .. nsteps are tokens t0 - DXH + r
-        # (DXH = 3 rows of delay, 4 at W = 5); the first step keeps rows >= DXH, the tail
-        # rows < DXH, the rest are pushed out (offset 0x80000000, past every extent)
-        _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias)
-        DXH = 4 if W > 4 else 3
-        for s in range(nsteps + 1):
-            t0 = t_first + s * STEP
-            r = np.arange(STEP)
-            keep = ((s > 0) | (r >= DXH)) & ((s < nsteps) | (r < DXH))
-            t = t0 - DXH + r[keep]
-            inb = t < T
-            acc.add("dx", b, t[inb][:, None], c_base + 8 * np.arange(8)[None, :], 8)
-            acc.dropped += int((~inb).sum()) * 8
-            acc.int32("dx store offset", (t * os1 + c_base + 56) * 2)
+        if not split:
+            _dx_role(acc, b, c_base, t_first, t_end, T, D, W, H, R, KS, os1, has_bias)
+    if split:
+        # the standalone dx kernel: its own ranges, dy and z staged for steps 0 .. nsteps
+        nCs = D // 64
+        per_seq = max(1, min((512 + B * nCs - 1) // (B * nCs), (T + STEP - 1) // STEP))
+        Ld = (T + per_seq - 1) // per_seq
+        Ld = (Ld + STEP - 1) // STEP * STEP
+        nTd = (T + Ld - 1) // Ld
+        zrow_q, zel_q, zval_q = z_pieces(ZB, KS, R, rot_quarter)
+        rlq, cq = _x_chunks(rot_quarter)
+        for lb in range(B * nTd * nCs):
+            cs, tr, b = lb % nCs, (lb // nCs) % nTd, lb // (nCs * nTd)
+            c_base, t_first = cs * 64, tr * Ld
+            t_end = min(T, t_first + Ld)
+            nsteps = (t_end - t_first + STEP - 1) // STEP
+            for s in range(nsteps + 1):
+                t0 = t_first + s * STEP
+                acc.add("dy", b, step_rows(t0, rlq, T), c_base + 8 * cq, 8)
+                acc.add("z", b, step_rows(t0, zrow_q[zval_q], T), zel_q[zval_q], ZB // 2)
+                acc.zero += int((~zval_q).sum())
+                if seg:
+                    _seg_loads(acc, b, t0, T)
+            _dx_role(acc, b, c_base, t_first, t_end, T, D, W, H, R, KS, os1, has_bias)
     acc.int32("dx buffer extent", ((T - 1) * os1 + D) * 2)
     return acc, nTr
+
+
+def _dx_role(acc, b, c_base, t_first, t_end, T, D, W, H, R, KS, os1, has_bias):
+    """dx stores of one (sequence, token range, 64-channel slice): tile rows r of steps
+    0 .. nsteps are tokens t0 - DXH + r (DXH = 3 rows of delay, 4 at W = 5); the first step
+    keeps rows >= DXH, the tail rows < DXH, the rest are pushed out (offset 0x80000000,
+    past every extent)."""
+    nsteps = (t_end - t_first + STEP - 1) // STEP
+    _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias)
+    DXH = 4 if W > 4 else 3
+    for s in range(nsteps + 1):
+        t0 = t_first + s * STEP
+        r = np.arange(STEP)
+        keep = ((s > 0) | (r >= DXH)) & ((s < nsteps) | (r < DXH))
+        t = t0 - DXH + r[keep]
+        inb = t < T
+        acc.add("dx", b, t[inb][:, None], c_base + 8 * np.arange(8)[None, :], 8)
+        acc.dropped += int((~inb).sum()) * 8
+        acc.int32("dx store offset", (t * os1 + c_base + 56) * 2)
 
 
 # ---------------------------------------------------------------------------------------
