@@ -210,6 +210,8 @@ ROWS = (
     "headwise_h4_bwd",
     "headwise_h16_fwd",
     "headwise_h16_bwd",
+    "headwise_h12_fwd",
+    "headwise_h12_bwd",
     "static_w3_fwd",
     "static_w3_bwd",
     "static_w4_fwd",
@@ -372,7 +374,9 @@ def make_row(name, device):
     else:
         B, T, D = 8, 4096, 2048
         W = int(name.split("_")[1][1:]) if name.startswith("static") else 8 if name.startswith("perchannel_w8") else 4
-        H = {"perchannel_h1": 1, "headwise_h4": 4, "headwise_h16": 16}.get(name.rsplit("_", 1)[0], 1)
+        H = int(name.split("_")[1][1:]) if name.startswith("headwise") else 1
+        if D % H:
+            D = 3072  # groups whose size is not a power of two (H = 12: 256 groups)
     static = name.startswith("static")
     x = gen((B, T, D), 1.0, 2, "x", device)
     w = gen((D // H, W) if static else (B, T, D // H, W), (1.0 / W) ** 0.5, 2, "w", device)

@@ -52,7 +52,6 @@ dynconv_status check_common(int64_t B, int64_t T, int64_t D, int32_t W, int32_t 
   if (W < 1 || H < 1) return DYNCONV_ERR_INVALID_ARG;
   if (W > kMaxW) return DYNCONV_ERR_UNSUPPORTED;
   if (D > 0 && D % H != 0) return DYNCONV_ERR_INVALID_ARG;
-  if (H > 1 && !is_pow2(H)) return DYNCONV_ERR_UNSUPPORTED;
   if (B > INT32_MAX || T > INT32_MAX || D > INT32_MAX) return DYNCONV_ERR_UNSUPPORTED;
   // Token indices, and a token plus a step of lookahead, stay in int; so do the filter
   // column counts (D/H)*W.
@@ -72,12 +71,11 @@ int act_alignment(const Act* a, int n, int eb) {
 }
 
 // The lane layout of the streaming kernels puts VEC channels on a lane and H / VEC lanes
-// on a group; bf16 lanes hold at least a channel pair, so D must be even.
+// on a group (group_vec), at most a wave; activation rows are whole 32-bit words, so with
+// 16-bit elements D must be even.
 dynconv_status check_stream_layout(int64_t D, int32_t H, int eb, int act_align) {
   if (act_align == 0 || D % (4 / eb) != 0) return DYNCONV_ERR_UNSUPPORTED;
-  const int vmax = act_align / eb;
-  const int vec = H == 1 ? 4 / eb : (H < vmax ? H : vmax);
-  if (H / vec > kWaveSize) return DYNCONV_ERR_UNSUPPORTED;
+  if (H > 1 && H / group_vec(H, eb, act_align) > kWaveSize) return DYNCONV_ERR_UNSUPPORTED;
   return DYNCONV_OK;
 }
 
@@ -186,6 +184,8 @@ dynconv_status fwd_impl(const void* x, const int64_t* xs, const void* w, const i
   p.D = int32_t(D);
   p.H = H;
   p.G = int32_t(D / H);
+  p.lpg = plan.lpg;
+  p.lpw = plan.lpw;
   p.L = plan.L;
   p.nTw = plan.nTw;
   p.nDw = plan.nDw;
@@ -245,6 +245,8 @@ size_t bwd_workspace(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, bool
   const int eb = elem_bytes(dtype);
   size_t best = 0;
   for (int align : {4, 8, 16}) {
+    // only the lane layouts a call can take (a group wider than a wave has no plan)
+    if (check_stream_layout(D, H, eb, align) != DYNCONV_OK) continue;
     const StreamPlan pl = plan_stream(B, T, D, W, H, eb, align, true, is_static);
     const size_t need = bwd_partial_floats(pl, B, D, W, H, is_static, dcbias) * sizeof(float);
     if (need > best) best = need;
@@ -402,6 +404,8 @@ dynconv_status bwd_impl(const void* x, const int64_t* xs, const void* w, const i
   p.D = int32_t(D);
   p.H = H;
   p.G = int32_t(D / H);
+  p.lpg = plan.lpg;
+  p.lpw = plan.lpw;
   p.L = plan.L;
   p.nTw = plan.nTw;
   p.nDw = plan.nDw;
@@ -834,7 +838,7 @@ dynconv_status check_gemm(const void* A, const int64_t* as, const void* Wp, int6
   if (A == nullptr || as == nullptr || Wp == nullptr || y == nullptr || ys == nullptr) return DYNCONV_ERR_INVALID_ARG;
   if (ldw < K) return DYNCONV_ERR_INVALID_ARG;
   if (dtype == DYNCONV_F32) return DYNCONV_ERR_UNSUPPORTED;  // matrix cores on 16-bit operands
-  if (W > 5 || H > 16) return DYNCONV_ERR_UNSUPPORTED;
+  if (W > 5 || H > 16 || !is_pow2(H)) return DYNCONV_ERR_UNSUPPORTED;  // whole groups in a 128-column tile
   if (as[2] != 1 || ys[2] != 1) return DYNCONV_ERR_UNSUPPORTED;
   if (as[0] < 0 || as[1] < 0 || ys[0] < 0 || ys[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
   if (K == 0 || K % kGemmK != 0) return DYNCONV_ERR_UNSUPPORTED;

@@ -22,8 +22,21 @@ constexpr int kBlockThreads = 256;  // 4 waves per workgroup
 // sweeps a run of tokens, keeping the W-1 token halo in registers.
 enum class StreamMode {
   PerChannel,  // H == 1: lane loads the VEC*W contiguous taps of its channels
-  Group,       // H > 1, VEC = min(H, 16 / element size): the lane's channels share one filter
+  Group,       // H > 1: the lane's VEC channels share one filter (group_vec below)
 };
+
+// Channels per lane of the head-wise (H > 1) streaming kernels: the largest power of two
+// that divides H and fits the widest lane vector the activations allow (`act_align` bytes),
+// so that a lane never straddles two groups. A group then spans H / VEC consecutive lanes.
+constexpr int group_vec(int H, int elem_bytes, int act_align) {
+  int v = act_align / elem_bytes;
+  while (v > 1 && H % v != 0) v /= 2;
+  return v;
+}
+
+// Lanes of a wave in use: whole groups only, so that no group straddles two waves (all 64
+// when the group's lanes divide 64, e.g. 63 for groups of 3 lanes, 60 for groups of 12).
+constexpr int lanes_in_use(int lanes_per_group) { return (kWaveSize / lanes_per_group) * lanes_per_group; }
 
 // Parameters of the streaming (materialised / static filter) kernels, passed by value.
 struct StreamParams {
@@ -43,6 +56,8 @@ struct StreamParams {
   int64_t os0, os1;
   int64_t dws0, dws1;
   int32_t B, T, D, H, G;
+  int32_t lpg;       // lanes per group (1 for the per-channel form)
+  int32_t lpw;       // lanes of a wave in use (backward: a multiple of lpg; forward: 64)
   int32_t L;         // tokens per wave time chunk
   int32_t nTw;       // time chunks per sequence
   int32_t nDw;       // channel slices (one wave wide) across D
@@ -52,13 +67,16 @@ struct StreamParams {
 
 struct StreamPlan {
   int vec;      // channels per lane
+  int lpg;      // lanes per group
+  int lpw;      // lanes of a wave in use
   StreamMode mode;
   int L, nTw, nDw, WD, WT, nDb, nTb;
   int64_t blocks;
 };
 
 // Chooses the lane vector width and the time chunking. `act_align` (4, 8 or 16) is the
-// widest lane vector, in bytes, that every activation-shaped tensor allows.
+// widest lane vector, in bytes, that every activation-shaped tensor allows; the layout must
+// be one the C ABI admits (a group of at most a wave's lanes).
 StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int W, int H, int elem_bytes, int act_align, bool bwd,
                        bool is_static);
 

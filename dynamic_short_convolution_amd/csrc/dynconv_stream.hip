@@ -142,13 +142,17 @@ StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int W, int H, int elem_b
     // forward, 100.5 vs 91.6 us backward at B8 T4096 D2048 W3)
     pl.mode = StreamMode::PerChannel;
     pl.vec = 4 / elem_bytes;
+    pl.lpg = 1;
   } else {
-    // a lane holds min(H, widest aligned vector) channels of one group
     pl.mode = StreamMode::Group;
-    const int vmax = act_align / elem_bytes;
-    pl.vec = H < vmax ? H : vmax;
+    pl.vec = group_vec(H, elem_bytes, act_align);
+    pl.lpg = H / pl.vec;
   }
-  const int64_t span = int64_t(kWaveSize) * pl.vec;
+  // The forward reduces nothing over a group: every lane in use, slices of whole cache lines
+  // (H = 12 at B8 T4096 D3072: 111.9 -> 87.9 us). The backward keeps each group inside a wave
+  // (aligning its slices to 128 or 64 bytes at the cost of more idle lanes measured no gain).
+  pl.lpw = bwd ? lanes_in_use(pl.lpg) : kWaveSize;
+  const int64_t span = int64_t(pl.lpw) * pl.vec;
   pl.nDw = int((D + span - 1) / span);
   pl.WD = pl.nDw >= 4 ? 4 : (pl.nDw >= 2 ? 2 : 1);
   pl.WT = 4 / pl.WD;

@@ -143,6 +143,16 @@ __device__ __forceinline__ void store_elems(ET* p, const float (&v)[N]) {
   }
 }
 
+// The lane's VEC channels of one activation row: 32-bit words, or one 16-bit element for
+// a lane of a single channel (head-wise groups of odd H in 16-bit storage).
+template <typename ET, int VEC>
+using ActRaw = typename std::conditional<(VEC * sizeof(ET)) % 4 == 0, Words<ET, VEC>, Halves<ET, VEC>>::type;
+
+template <bool NT, typename ET, int VEC>
+__device__ __forceinline__ void store_act(ET* p, const float (&v)[VEC]) {
+  store_elems<NT, (VEC * sizeof(ET)) % 4 == 0, ET, VEC>(p, v);
+}
+
 // Raw taps of one token for one lane: the VEC*W taps of its channels (H = 1) or the W
 // taps of its group (H > 1). Groups of whole 32-bit words are 4-byte aligned (the C ABI
 // checks it), odd bf16 groups are read as 16-bit halves.
@@ -194,11 +204,12 @@ __device__ __forceinline__ WaveTile wave_tile(const StreamParams& p, int vec) {
   }
   const int dsl = db * p.WD + (wv % p.WD);
   const int tch = tb * p.WT + (wv / p.WD);
-  wt.c0 = (dsl * kWaveSize + lane) * vec;
+  // a wave's slice is lpw lanes of vec channels (lanes past lpw idle, see lanes_in_use)
+  wt.c0 = (dsl * p.lpw + lane) * vec;
   wt.t0 = tch * p.L;
   wt.t1 = min(p.T, wt.t0 + p.L);
   wt.chunk = wt.b * p.nTw + tch;
-  wt.valid = dsl < p.nDw && tch < p.nTw && wt.c0 < p.D;
+  wt.valid = dsl < p.nDw && tch < p.nTw && lane < p.lpw && wt.c0 < p.D;
   return wt;
 }
 
@@ -255,7 +266,7 @@ constexpr int fwd_max_waves_per_simd(bool perch, bool is_static) { return perch 
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool SEG>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(
     1, fwd_max_waves_per_simd(PERCH, STATIC)))) void k_stream_fwd(const StreamParams p) {
-  using XR = Words<ET, VEC>;
+  using XR = ActRaw<ET, VEC>;
   using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
   constexpr int NC = PERCH ? VEC : 1;
   constexpr int LB = VEC * int(sizeof(ET)) + (STATIC ? 0 : TapsRaw<ET, W, VEC, PERCH>::bytes);
@@ -332,7 +343,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(
       }
       yv[v] = acc;
     }
-    store_words<NT, ET, VEC>(yb + t * p.os1, yv);
+    store_act<NT, ET, VEC>(yb + t * p.os1, yv);
   };
 
   int t = wt.t0;
@@ -365,8 +376,19 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(
 //   dx_s = dy_s + sum_k w_k^(s+k) dy_{s+k}
 //   dw_t[g,k] = sum_{d in g} dy_t[d] x_{t-k}[d]
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ float group_sum(float v, int lanes) {
-  for (int m = 1; m < lanes; m <<= 1) v += __shfl_xor(v, m, kWaveSize);
+// Sum of v over the `lanes` consecutive lanes of a group; `pos` is the lane's place in it.
+// A group never straddles a wave (lanes_in_use). Groups of 2^n lanes use a butterfly (every
+// lane gets the sum); other sizes a suffix scan whose first lane (pos 0) ends with the sum:
+// after the round with offset o, lane pos holds the sum over pos .. min(pos + 2o, lanes) - 1.
+__device__ __forceinline__ float group_sum(float v, int lanes, int pos) {
+  if ((lanes & (lanes - 1)) == 0) {
+    for (int m = 1; m < lanes; m <<= 1) v += __shfl_xor(v, m, kWaveSize);
+  } else {
+    for (int o = 1; o < lanes; o <<= 1) {
+      const float u = __shfl_down(v, o, kWaveSize);
+      if (pos + o < lanes) v += u;
+    }
+  }
   return v;
 }
 
@@ -377,7 +399,7 @@ __device__ __forceinline__ float group_sum(float v, int lanes) {
 // that the sweep without it carries no extra work).
 template <typename ET, int W, int VEC, bool PERCH, bool STATIC, bool ALL, bool SEG, bool CB>
 __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams p) {
-  using XR = Words<ET, VEC>;
+  using XR = ActRaw<ET, VEC>;
   using TR = typename TapsRaw<ET, W, VEC, PERCH>::type;
   constexpr int WM = W > 1 ? W - 1 : 1;
   constexpr int NC = PERCH ? VEC : 1;
@@ -396,8 +418,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
   // (H divides D and groups are lane-aligned), so invalid lanes can leave now.
   if (!wt.valid) return;
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int lanes_per_group = PERCH ? 1 : p.H / VEC;
-  const bool group_lead = PERCH || (lane % lanes_per_group) == 0;
+  const int lanes_per_group = PERCH ? 1 : p.lpg;
+  const int group_pos = PERCH ? 0 : lane % lanes_per_group;
+  const bool group_lead = group_pos == 0;
   const int g = PERCH ? wt.c0 : wt.c0 / p.H;
   const bool want_dx = ALL || p.out != nullptr;
   const bool want_dw = ALL || (STATIC ? (p.partial != nullptr) : (p.dw != nullptr));
@@ -498,7 +521,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
           for (int k = 0; k < W; ++k) sdw[0][k] += s[k];
         } else {
 #pragma unroll
-          for (int k = 0; k < W; ++k) s[k] = group_sum(s[k], lanes_per_group);
+          for (int k = 0; k < W; ++k) s[k] = group_sum(s[k], lanes_per_group, group_pos);
           if (group_lead) store_elems<NT, TapsRaw<ET, W, VEC, PERCH>::group_words, ET, W>(dwb + t * p.dws1, s);
         }
       }
@@ -520,9 +543,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       const int s = t - (W - 1);
       if (s >= wt.t0 && s < wt.t1) {
         if constexpr (W == 1) {
-          store_words<NT, ET, VEC>(dxb + s * p.os1, nacc);
+          store_act<NT, ET, VEC>(dxb + s * p.os1, nacc);
         } else {
-          store_words<NT, ET, VEC>(dxb + s * p.os1, acc[W - 2]);
+          store_act<NT, ET, VEC>(dxb + s * p.os1, acc[W - 2]);
         }
       }
 #pragma unroll
@@ -657,7 +680,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       } else {
         float s[W];
 #pragma unroll
-        for (int k = 0; k < W; ++k) s[k] = group_sum(sdw[0][k], lanes_per_group);
+        for (int k = 0; k < W; ++k) s[k] = group_sum(sdw[0][k], lanes_per_group, group_pos);
         if (group_lead) {
 #pragma unroll
           for (int k = 0; k < W; ++k) part[int64_t(g) * W + k] = s[k];
@@ -718,6 +741,10 @@ hipError_t dispatch_mode(const StreamParams& p, const StreamPlan& plan, bool st,
   if (plan.mode == StreamMode::PerChannel) return dispatch_static<BWD, ET, W, k4, true>(p, plan, st, s);
   if (plan.vec == 4 * k4) return dispatch_static<BWD, ET, W, 4 * k4, false>(p, plan, st, s);
   if (plan.vec == 2 * k4) return dispatch_static<BWD, ET, W, 2 * k4, false>(p, plan, st, s);
+  if constexpr (k4 == 2) {
+    // one 16-bit channel per lane: groups of odd H
+    if (plan.vec == 1) return dispatch_static<BWD, ET, W, 1, false>(p, plan, st, s);
+  }
   return dispatch_static<BWD, ET, W, k4, false>(p, plan, st, s);
 }
 

@@ -19,9 +19,12 @@ Kernels (dynamic_short_convolution_amd/csrc):
   k_lowrank_fwd          general low-rank forward (16-token tiles, register staging)
   k_lowrank_bwd          general low-rank backward (64-token steps; FAST and masked
                          loads, including the surplus threads' "safe" chunk)
+  k_stream_fwd/_bwd      materialised and static filters: a wave sweeps a run of tokens
+                         over lpw lanes of VEC channels (head-wise groups of H / VEC lanes)
 """
 from __future__ import annotations
 
+import math
 from collections import defaultdict
 
 import numpy as np
@@ -647,3 +650,198 @@ def lowrank_bwd_general(B, T, D, W, H, R, eb, fast, seg=False, has_bias=True, wa
                     if has_bias:
                         acc.add("bias", 0, 0, cols, W)
     return acc, nTr
+
+
+# ---------------------------------------------------------------------------------------
+# k_stream_fwd / k_stream_bwd (plan_stream, wave_tile and the per-lane loads and stores)
+# ---------------------------------------------------------------------------------------
+STREAM_WAVES = dict(fwd=8, fwd_group=12, fwd_wide=4, bwd=16, bwd_group=12, bwd_static=8, bwd_wide=8)
+
+
+def group_vec(H, eb, align):
+    """Channels per lane of a head-wise group: the largest power of two dividing H that
+    fits the lane vector (align bytes)."""
+    v = align // eb
+    while v > 1 and H % v:
+        v //= 2
+    return v
+
+
+def stream_layout_ok(D, H, eb, align):
+    """The ABI's check of the lane layout (check_stream_layout)."""
+    if D % (4 // eb):
+        return False
+    return H == 1 or H // group_vec(H, eb, align) <= 64
+
+
+def plan_stream(B, T, D, W, H, eb, align, bwd, static):
+    if H == 1:
+        vec, lpg = 4 // eb, 1
+    else:
+        vec = group_vec(H, eb, align)
+        lpg = H // vec
+    lpw = (64 // lpg) * lpg if bwd else 64
+    span = lpw * vec
+    nDw = (D + span - 1) // span
+    WD = 4 if nDw >= 4 else (2 if nDw >= 2 else 1)
+    WT = 4 // WD
+    nDb = (nDw + WD - 1) // WD
+    wide = H == 1 and not static and W >= 7
+    if not bwd:
+        waves = STREAM_WAVES["fwd_wide"] if wide else (
+            STREAM_WAVES["fwd_group"] if H > 1 and not static else STREAM_WAVES["fwd"])
+    else:
+        waves = STREAM_WAVES["bwd_static"] if static else (
+            STREAM_WAVES["bwd_group"] if H > 1 else (STREAM_WAVES["bwd_wide"] if wide else STREAM_WAVES["bwd"]))
+    target = 256.0 * waves / 4
+    min_len = 64 if (bwd and static) else 16
+    max_chunks = 1 if T <= min_len else (T + min_len - 1) // min_len
+    per_seq = target * WT / (B * nDb)
+    lo, hi = int(per_seq / 4), int(per_seq * 4) + 1
+    lo = max(lo, 1)
+    hi = min(hi, max_chunks)
+    lo = min(lo, hi)
+    best, bestL = -1e30, T
+    for c in range(lo, hi + 1):
+        L = (T + c - 1) // c
+        L = (L + 3) // 4 * 4
+        nTw = (T + L - 1) // L
+        blocks = B * nDb * ((nTw + WT - 1) // WT)
+        per_cu = (blocks + 255) // 256
+        score = blocks / (256 * per_cu) - 0.25 * abs(math.log(blocks / target))
+        if score > best + 1e-12:
+            best, bestL = score, L
+    nTw = (T + bestL - 1) // bestL
+    nTb = (nTw + WT - 1) // WT
+    return dict(vec=vec, lpg=lpg, lpw=lpw, nDw=nDw, WD=WD, WT=WT, nDb=nDb, L=bestL, nTw=nTw, nTb=nTb,
+                blocks=B * nDb * nTb)
+
+
+def _stream_waves(pl, B, T, D, channel_fastest, xcd):
+    """(b, c0 per lane, valid per lane, t0, t1, chunk) of every wave of the launch."""
+    lane = np.arange(64)
+    n = pl["blocks"]
+    for bid in range(n):
+        lb = int(xcd_logical_block(bid, n)) if xcd else bid
+        if channel_fastest:
+            db = lb % pl["nDb"]
+            lb //= pl["nDb"]
+            tb = lb % pl["nTb"]
+            b = lb // pl["nTb"]
+        else:
+            tb = lb % pl["nTb"]
+            lb //= pl["nTb"]
+            db = lb % pl["nDb"]
+            b = lb // pl["nDb"]
+        for wv in range(4):
+            dsl = db * pl["WD"] + wv % pl["WD"]
+            tch = tb * pl["WT"] + wv // pl["WD"]
+            c0 = (dsl * pl["lpw"] + lane) * pl["vec"]
+            valid = (dsl < pl["nDw"]) & (tch < pl["nTw"]) & (lane < pl["lpw"]) & (c0 < D)
+            t0 = tch * pl["L"]
+            yield b, c0, valid, t0, min(T, t0 + pl["L"]), b * pl["nTw"] + tch
+
+
+def _check_groups(c0, valid, pl, H):
+    """The group reductions read the H / VEC consecutive lanes from each group's first one
+    (pos = lane % lpg): all of them valid and of that group."""
+    lpg = pl["lpg"]
+    g = c0 // H
+    for lane in np.nonzero(valid)[0]:
+        lead = lane - lane % lpg
+        assert lead + lpg <= pl["lpw"], f"group at lane {lead} straddles the lanes in use"
+        assert valid[lead:lead + lpg].all(), f"group at lane {lead} partly invalid"
+        assert (g[lead:lead + lpg] == g[lane]).all(), f"lane {lane} is not in the group of lane {lead}"
+        assert c0[lead] % H == 0, f"group at lane {lead} does not start a filter group"
+
+
+def stream_fwd(B, T, D, W, H, eb, align, static=False, seg=False, cbias=False):
+    pl = plan_stream(B, T, D, W, H, eb, align, False, static)
+    vec = pl["vec"]
+    perch = H == 1
+    nw = vec * W if perch else W
+    acc = Accesses()
+    for b, c0, valid, t0, t1, _ in _stream_waves(pl, B, T, D, static, False):
+        c0 = c0[valid]
+        if c0.size == 0:
+            continue
+        gcol = (c0 if perch else c0 // H) * W
+        for k in range(1, W):
+            if t0 - k >= 0:
+                acc.add("x", b, t0 - k, c0, vec)
+                if seg:
+                    acc.add("seg", b, t0 - k, 0, 1)
+        if static:
+            acc.add("w", 0, 0, gcol, nw)
+        if cbias:
+            acc.add("cbias", 0, 0, c0, vec)
+        t = np.arange(t0, t1)[:, None]
+        acc.add("x", b, t, c0[None, :], vec)
+        acc.add("y", b, t, c0[None, :], vec)
+        if not static:
+            acc.add("w", b, t, gcol[None, :], nw)
+        if seg:
+            acc.add("seg", b, t, 0, 1)
+    return acc, pl
+
+
+def stream_bwd(B, T, D, W, H, eb, align, static=False, want_dx=True, want_dw=True, seg=False, cb=False):
+    pl = plan_stream(B, T, D, W, H, eb, align, True, static)
+    vec = pl["vec"]
+    perch = H == 1
+    nw = vec * W if perch else W
+    acc = Accesses()
+    for b, c0_all, valid, t0, t1, chunk in _stream_waves(pl, B, T, D, static, True):
+        if not perch:
+            _check_groups(c0_all, valid, pl, H)
+        lane = np.arange(64)[valid]
+        c0 = c0_all[valid]
+        if c0.size == 0:
+            continue
+        lead = lane % pl["lpg"] == 0
+        gcol = (c0 if perch else c0 // H) * W
+        if want_dw:
+            for k in range(1, W):
+                if t0 - k >= 0:
+                    acc.add("x", b, t0 - k, c0, vec)
+        if seg:
+            for k in range(1, W):
+                if t0 - k >= 0:
+                    acc.add("seg", b, t0 - k, 0, 1)
+        if static:
+            acc.add("w", 0, 0, gcol, nw)
+        if want_dx:
+            for e in range(W - 1):
+                tt = t1 + e
+                if tt < T:
+                    acc.add("dy", b, tt, c0, vec)
+                    if seg:
+                        acc.add("seg", b, tt, 0, 1)
+                    if not static:
+                        acc.add("w", b, tt, gcol, nw)
+        t = np.arange(t0, t1)[:, None]
+        acc.add("dy", b, t, c0[None, :], vec)
+        if seg:
+            acc.add("seg", b, t, 0, 1)
+        if want_dw:
+            acc.add("x", b, t, c0[None, :], vec)
+        if not static and want_dx:
+            acc.add("w", b, t, gcol[None, :], nw)
+        if want_dx:
+            # steps t0 .. t1 + W - 2 (the last W - 1 on the future halo) store row s = t - (W - 1)
+            s_ = np.arange(t0, t1 + W - 1) - (W - 1)
+            s_ = s_[(s_ >= t0) & (s_ < t1)][:, None]
+            acc.add("dx", b, s_, c0[None, :], vec)
+        if want_dw and not static:
+            if perch:
+                acc.add("dw", b, t, gcol[None, :], nw)
+            else:
+                acc.add("dw", b, t, gcol[lead][None, :], W)
+        if cb:
+            acc.add("cb_partial", 0, chunk, c0, vec)
+        if static and want_dw:
+            if perch:
+                acc.add("partial", 0, chunk, gcol, nw)
+            else:
+                acc.add("partial", 0, chunk, gcol[lead], W)
+    return acc, pl

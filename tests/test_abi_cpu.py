@@ -68,7 +68,10 @@ def fwd(lib, x=X, xs=(800, 200, 1), w=W_, ws=(800 * 4, 200 * 4, 4, 1), y=Y, ys=(
         (dict(W=9), UNSUP),
         (dict(H=0), INVALID),
         (dict(D=200, H=3), INVALID),  # 3 does not divide 200
-        (dict(D=198, H=3, xs=(792, 198, 1), ys=(792, 198, 1), ws=(264 * 4, 66 * 4, 4, 1)), UNSUP),  # not a power of 2
+        # odd H: one bf16 channel per lane, a group of 99 lanes would straddle waves
+        (dict(D=198, H=99, xs=(792, 198, 1), ys=(792, 198, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
+        # H = 3 * 128 with 8-byte rows: 4 channels per lane, 96 lanes per group
+        (dict(D=768, H=384, xs=(4 * 768 + 4, 768, 1), ys=(4 * 768 + 4, 768, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
         (dict(x=P(0)), INVALID),
         (dict(y=P(0)), INVALID),
         (dict(w=P(0)), INVALID),
@@ -113,6 +116,12 @@ def test_workspace_queries(lib):
     assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 3, 1, 1, BF16) % 4 == 0
     assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 9, 1, 1, BF16) == 0  # invalid W
     assert lib.dynconv_bwd_workspace_size(8, 4096, 2048, 8, 1, 1, BF16) > 0
+    # groups that only the widest lane vectors serve (512 bf16 channels: 64 lanes of 8), or
+    # none (odd 99: 99 lanes), and groups whose size is not a power of two
+    for H, dt in ((512, BF16), (256, F32), (384, BF16), (96, F32), (3, BF16), (63, F32), (99, BF16)):
+        n = lib.dynconv_bwd_ex_workspace_size(2, 50, 16 * H, 3, H, 1, 1, dt)
+        assert n > 0 or H == 99
+        assert n % 4 == 0
     assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 6, 1, 64, BF16) == 0  # low-rank: W <= 5
     n = lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 64, BF16)
     assert n >= 64 * 2048 * 4 * 4  # at least one float32 dU partial
@@ -432,6 +441,7 @@ def test_gemm_validation(lib):
     assert g(W_=6, ws=(T * N * 6, N * 6, 6, 1)) == UNSUP
     assert g(H=32, ws=(T * 8 * W, 8 * W, W, 1)) == UNSUP
     assert g(H=3) == INVALID  # H must divide N
+    assert g(N_=384, H=6, ws=(T * 64 * W, 64 * W, W, 1), ys=(T * 384, 384, 1)) == UNSUP  # whole groups per 128 columns
     assert g(K_=96, as_=(T * 96, 96, 1), ldw=96) == UNSUP  # K % 64
     assert g(N_=192, ws=(T * 192 * W, 192 * W, W, 1)) == UNSUP  # N % 128
     assert g(A_=P(0x100008)) == UNSUP  # 16-byte rows of A

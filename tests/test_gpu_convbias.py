@@ -55,13 +55,13 @@ def _case(B, T, D, W, H, dtype, static, seed, packed=False, need_dx=True, need_d
 CASES = []
 for dtype in ("f32", "bf16", "f16"):
     for W in (1, 3, 4, 8):
-        for H, static in ((1, False), (4, False), (16, False), (1, True), (4, True)):
+        for H, static in ((1, False), (4, False), (16, False), (1, True), (4, True), (6, False), (3, True)):
             CASES.append((dtype, W, H, static))
 
 
 @pytest.mark.parametrize("dtype,W,H,static", CASES)
 def test_conv_bias_parity(dtype, W, H, static):
-    D = 136 if H == 1 else 256
+    D = 136 if H == 1 else (264 if H % 3 == 0 else 256)
     _case(2, 300, D, W, H, dtype, static, seed=40 + W + H + int(static))
 
 

@@ -35,6 +35,10 @@ for dtype in ("f32", "bf16", "f16"):
         for H, static in ((1, False), (4, False), (1, True)):
             for T0 in (0, 2, 7):
                 CASES.append((dtype, W, H, static, T0))
+    # groups whose size is not a power of two
+    for W in (3, 4, 8):
+        for H, static in ((6, False), (3, True), (9, False)):
+            CASES.append((dtype, W, H, static, 2))
 
 
 @pytest.mark.parametrize("dtype,W,H,static,T0", CASES)
@@ -75,7 +79,7 @@ def test_lowrank_decode_matches_full_sequence(dtype, W, R, T0):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("H,W,R", [(4, 4, 64), (2, 3, 20), (16, 5, 32)])
+@pytest.mark.parametrize("H,W,R", [(4, 4, 64), (2, 3, 20), (16, 5, 32), (3, 4, 64), (6, 3, 20), (12, 5, 40)])
 def test_headwise_lowrank_decode(dtype, H, W, R):
     """U of R x (D/H)*W: the H channels of a group share the generated filter."""
     B, Ttot, D = 5, 8, 96

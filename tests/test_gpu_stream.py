@@ -94,6 +94,35 @@ def test_large_head_sizes(dtype, H):
     _check_case(1, 50, 1024, 3, H, dtype, True, seed=H + 1)
 
 
+# Head-wise groups whose size is not a power of two (the head-wise parameterisation takes
+# any H that divides D): odd H (one 16-bit channel per lane), H = 3 * 2^n and 5 * 2^n;
+# groups of 3, 5, 12, 48 and 63 lanes reduce with the suffix scan, and the lanes of a wave
+# past the last whole group stay idle.
+ODD_H = [
+    # dtype, W, H, D
+    ("bf16", 4, 3, 198),
+    ("f16", 3, 5, 390),
+    ("f32", 4, 3, 198),
+    ("f32", 2, 63, 126),
+    ("bf16", 1, 6, 1152),
+    ("bf16", 4, 6, 1152),
+    ("f32", 5, 6, 1152),
+    ("bf16", 4, 12, 1536),
+    ("f16", 8, 24, 768),
+    ("bf16", 3, 96, 2304),
+    ("f32", 4, 96, 2304),
+    ("bf16", 4, 384, 1536),
+    ("bf16", 2, 10, 640),
+    ("bf16", 4, 63, 126),
+]
+
+
+@pytest.mark.parametrize("dtype,W,H,D", ODD_H)
+@pytest.mark.parametrize("static", [False, True])
+def test_non_power_of_two_groups(dtype, W, H, D, static):
+    _check_case(2, 333, D, W, H, dtype, static, seed=H + W + int(static))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T", [1, 2, 4, 5])
 def test_short_sequences(dtype, T):
@@ -141,11 +170,12 @@ def test_zero_filters_identity_bitwise():
     assert torch.equal(dx, dy)
 
 
-@pytest.mark.parametrize("H,static", [(1, False), (16, False), (1, True)])
-def test_every_output_written_and_guards_untouched(H, static):
+@pytest.mark.parametrize("H,static,D", [(1, False, 1024), (16, False, 1024), (1, True, 1024), (6, False, 1152),
+                                          (3, True, 1152), (96, False, 1152)])
+def test_every_output_written_and_guards_untouched(H, static, D):
     """Outputs start as NaN inside guard bands of rows and columns; afterwards every
     element is finite and the guards are still NaN (bitwise)."""
-    B, T, D, W = 2, 130, 1024, 4
+    B, T, W = 2, 130, 4
     x, w, dy = _inputs(B, T, D, W, H, "bf16", static, 9)
     xg, wg, dyg = x.cuda(), w.cuda(), dy.cuda()
     G = 3
@@ -179,9 +209,10 @@ def test_every_output_written_and_guards_untouched(H, static):
         assert_close("dw(strided)", dw, rdw, torch.bfloat16)
 
 
-@pytest.mark.parametrize("H,static", [(1, False), (4, False), (16, False), (1, True), (16, True)])
+@pytest.mark.parametrize("H,static", [(1, False), (4, False), (16, False), (1, True), (16, True), (12, False),
+                                      (3, True)])
 def test_run_to_run_deterministic(H, static):
-    x, w, dy = _inputs(2, 300, 1024, 4, H, "bf16", static, 11)
+    x, w, dy = _inputs(2, 300, 1152 if H % 3 == 0 else 1024, 4, H, "bf16", static, 11)
     xg, wg, dyg = x.cuda(), w.cuda(), dy.cuda()
     outs = []
     for _ in range(3):

@@ -57,11 +57,14 @@ for dtype in ("f32", "bf16", "f16"):
     for W in (1, 2, 3, 4, 5, 6, 8):
         for H, static in ((1, False), (4, False), (16, False), (1, True), (4, True)):
             STREAM.append((dtype, W, H, static))
+    for W in (3, 4):
+        for H, static in ((6, False), (3, True), (12, False)):
+            STREAM.append((dtype, W, H, static))
 
 
 @pytest.mark.parametrize("dtype,W,H,static", STREAM)
 def test_packed_stream_parity(dtype, W, H, static):
-    D = 136 if H == 1 else 256
+    D = 136 if H == 1 else (264 if H % 3 == 0 else 256)
     _stream_case(2, 300, D, W, H, dtype, static, seed=300 + 10 * W + H + int(static))
 
 
@@ -112,7 +115,8 @@ LOWRANK = [("bf16", 4, 64, 128, 1), ("bf16", 2, 32, 128, 1), ("bf16", 3, 64, 192
            ("f32", 1, 16, 64, 1), ("f32", 3, 64, 136, 1), ("f32", 4, 128, 64, 1), ("bf16", 4, 64, 128, 4),
            ("f32", 3, 32, 64, 8), ("f16", 4, 64, 128, 1), ("f16", 3, 40, 96, 2), ("bf16", 4, 64, 512, 4),
            ("bf16", 3, 32, 320, 2), ("bf16", 5, 64, 192, 2),
-           ("bf16", 4, 64, 1024, 8), ("bf16", 4, 64, 1024, 16), ("bf16", 2, 32, 512, 8)]
+           ("bf16", 4, 64, 1024, 8), ("bf16", 4, 64, 1024, 16), ("bf16", 2, 32, 512, 8),
+           ("bf16", 4, 64, 192, 6), ("f32", 3, 20, 96, 3), ("f16", 5, 40, 240, 12)]
 
 
 @pytest.mark.parametrize("dtype,W,R,D,H", LOWRANK)

@@ -172,6 +172,8 @@ GEN = [
     (2, 17, 40, 2),
     (1, 100, 130, 1),
     (1, 300, 96, 4),
+    (2, 45, 36, 3),
+    (1, 70, 120, 12),
 ]
 
 
@@ -197,6 +199,8 @@ GEN_BWD = [
     (1, 65, 48, 4),
     (1, 150, 96, 1),
     (2, 300, 64, 2),
+    (1, 70, 96, 6),
+    (2, 33, 60, 5),
 ]
 
 
@@ -207,13 +211,98 @@ GEN_BWD = [
 def test_lowrank_bwd_general_bounds(B, T, D, H, W, R, eb):
     fast = R % 32 == 0
     acc, nTr = kb.lowrank_bwd_general(B, T, D, W, H, R, eb, fast, seg=T % 2 == 1, has_bias=W % 2 == 0,
-                                      want_db=R != 64, lean=(eb == 2 and W <= 4 and D % 64 == 0))
+                                      want_db=R != 64,
+                                      lean=(eb == 2 and W <= 4 and D % 64 == 0 and H in (1, 2, 4, 8, 16)))
     J = (D // H) * W
     nR = B * nTr
     acc.check({"x": (B, T, D), "dy": (B, T, D), "z": (B, T, R), "U": (1, R, J), "bias": (1, 1, J),
                "dx": (B, T, D), "seg": (B, T, 1), "part_dU": (1, nR * H * R, J), "part_db": (1, nR * H, J)})
     _full(acc, "dx", B, T, D)
     _full(acc, "part_dU", 1, nR * H * R, J)
+
+
+# ---------------------------------------------------------------------------------------
+# streaming kernels (materialised and static filters), every group size the ABI admits
+# ---------------------------------------------------------------------------------------
+STREAM = [
+    # B, T, D, H
+    (1, 1, 2, 1),
+    (2, 37, 200, 1),
+    (1, 300, 768, 1),
+    (2, 50, 96, 2),
+    (1, 129, 1024, 16),
+    (3, 40, 198, 3),
+    (1, 70, 390, 5),
+    (2, 33, 1152, 6),
+    (1, 90, 1536, 12),
+    (1, 20, 2304, 96),
+    (1, 17, 1536, 384),
+    (2, 25, 126, 63),
+]
+
+
+def _stream_cases():
+    for (B, T, D, H), eb, align in itertools.product(STREAM, (2, 4), (4, 8, 16)):
+        if (D * eb) % align == 0 and kb.stream_layout_ok(D, H, eb, align):
+            yield B, T, D, H, eb, align
+
+
+STREAM_CASES = list(_stream_cases())
+
+
+@pytest.mark.parametrize("B,T,D,H,eb,align", STREAM_CASES)
+@pytest.mark.parametrize("W", [1, 3, 4, 8])
+@pytest.mark.parametrize("static", [False, True])
+def test_stream_fwd_bounds(B, T, D, H, eb, align, W, static):
+    acc, _ = kb.stream_fwd(B, T, D, W, H, eb, align, static=static, seg=T % 2 == 1, cbias=W % 2 == 0)
+    G = D // H
+    wext = (1, 1, G * W) if static else (B, T, G * W)
+    acc.check({"x": (B, T, D), "y": (B, T, D), "w": wext, "seg": (B, T, 1), "cbias": (1, 1, D)})
+    _full(acc, "y", B, T, D)
+
+
+@pytest.mark.parametrize("B,T,D,H,eb,align", STREAM_CASES)
+@pytest.mark.parametrize("W", [1, 3, 4, 8])
+@pytest.mark.parametrize("static", [False, True])
+@pytest.mark.parametrize("want", ["dx", "dw", "both"])
+def test_stream_bwd_bounds(B, T, D, H, eb, align, W, static, want):
+    want_dx, want_dw = want in ("dx", "both"), want in ("dw", "both")
+    cb = T % 2 == 0
+    acc, pl = kb.stream_bwd(B, T, D, W, H, eb, align, static=static, want_dx=want_dx, want_dw=want_dw,
+                            seg=W % 2 == 1, cb=cb)
+    G = D // H
+    nch = B * pl["nTw"]
+    wext = (1, 1, G * W) if static else (B, T, G * W)
+    acc.check({"x": (B, T, D), "dy": (B, T, D), "dx": (B, T, D), "w": wext, "dw": (B, T, G * W),
+               "seg": (B, T, 1), "cb_partial": (1, nch, D), "partial": (1, nch, G * W)})
+    if want_dx:
+        _full(acc, "dx", B, T, D)
+    if want_dw:
+        _full(acc, "partial" if static else "dw", *((1, nch, G * W) if static else (B, T, G * W)))
+    if cb:
+        _full(acc, "cb_partial", 1, nch, D)
+
+
+def test_stream_cases_cover_odd_and_mixed_groups():
+    """The sweep reaches groups of 3, 5, 12 (H = 96 at 8 channels per lane) and 63 lanes,
+    so the suffix-scan reduction and the idle lanes past lanes_in_use are exercised."""
+    lpgs = {kb.plan_stream(B, T, D, 4, H, eb, al, True, False)["lpg"] for B, T, D, H, eb, al in STREAM_CASES}
+    assert {3, 5, 12, 63} <= lpgs
+    assert any(kb.plan_stream(B, T, D, 4, H, eb, al, True, False)["vec"] == 1 and eb == 2
+               for B, T, D, H, eb, al in STREAM_CASES)
+
+
+def test_stream_group_check_catches_a_straddling_group():
+    """A wave slice of all 64 lanes with groups of 3 lanes would split a group between two
+    waves: the group check must see it."""
+    B, T, D, H, eb, align = 1, 8, 198, 3, 2, 4
+    pl = kb.plan_stream(B, T, D, 4, H, eb, align, True, False)
+    bad = dict(pl, lpw=64, nDw=(D + 63) // 64)
+    lane = np.arange(64)
+    c0 = lane * bad["vec"] + 64 * bad["vec"]  # the second slice
+    valid = c0 < D
+    with pytest.raises(AssertionError):
+        kb._check_groups(c0, valid, bad, H)
 
 
 # ---------------------------------------------------------------------------------------
