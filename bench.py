@@ -228,6 +228,8 @@ ROWS = (
     "perchannel_w8_bwd",
     "convbias_perchannel_h1_fwd",
     "convbias_perchannel_h1_bwd",
+    "convbias_lowrank_r64_fwd",
+    "convbias_lowrank_r64_bwd",
     "packed_perchannel_h1_fwd",
     "packed_perchannel_h1_bwd",
     "packed_lowrank_r64_fwd",
@@ -361,14 +363,19 @@ def make_row(name, device):
                    B, T)
         seq = segs(B, T)
         sb = 4 * B * T if packed else 0
+        cb = gen((D,), 0.5, 4, "c", device).to(dt) if cbias else None
+        if cbias:
+            desc += " + convolution bias"
         if name.endswith("fwd"):
             y = torch.empty_like(x)
-            return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, H, out=y, seq_idx=seq)), \
-                lowrank_bytes(B, T, D, W, R, H=H) + sb, lowrank_flops(B, T, D, W, R, H=H), desc
+            return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, H, out=y, seq_idx=seq, conv_bias=cb)), \
+                lowrank_bytes(B, T, D, W, R, H=H) + sb + (2 * D if cbias else 0), lowrank_flops(B, T, D, W, R, H=H), desc
         dy = gen((B, T, D), 1.0, 4, "dy", device).to(dt)
-        ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dt), dtype=torch.uint8, device=device)
-        return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, H, workspace=ws, seq_idx=seq)), \
-            lowrank_bytes(B, T, D, W, R, fwd=False, H=H) + sb, lowrank_flops(B, T, D, W, R, fwd=False, H=H), desc
+        ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dt, want_dconv_bias=cbias),
+                         dtype=torch.uint8, device=device)
+        return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, H, workspace=ws, seq_idx=seq, want_dconv_bias=cbias)), \
+            lowrank_bytes(B, T, D, W, R, fwd=False, H=H) + sb + (4 * D if cbias else 0), \
+            lowrank_flops(B, T, D, W, R, fwd=False, H=H), desc
     if name.startswith("qkv"):
         B, T, D, W, H = 4, 8192, 3072, 4, 1
     else:

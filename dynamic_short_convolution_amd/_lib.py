@@ -46,6 +46,10 @@ EXPORTS = (
     "dynconv_bwd_ex_noalloc",
     "dynconv_gemm_fwd",
     "dynconv_gemm_lowrank_fwd",
+    "dynconv_lowrank_fwd_ex",
+    "dynconv_lowrank_bwd_ex",
+    "dynconv_lowrank_bwd_ex_workspace_size",
+    "dynconv_lowrank_decode_step_ex",
 )
 
 # Bytes of the per-GPU scratch array of dynconv_bwd_ex_noalloc (DYNCONV_NOALLOC_SCRATCH_BYTES).
@@ -119,6 +123,19 @@ _SIGNATURES["dynconv_gemm_lowrank_fwd"] = (
 # the workspace pointer and size of dynconv_bwd_ex dropped
 _SIGNATURES["dynconv_bwd_ex_noalloc"] = (
     _SIGNATURES["dynconv_bwd_ex"][0][:-3] + [_vp], ctypes.c_int)
+# low-rank with a convolution bias: (seq_idx, ss, conv_bias) after the bias; bwd: (seq_idx, ss)
+# after the bias and dconv_bias after db; decoding: conv_bias after the bias
+_SIGNATURES["dynconv_lowrank_fwd_ex"] = (
+    _SIGNATURES["dynconv_lowrank_fwd"][0][:7] + [_vp, _i64p, _vp] + _SIGNATURES["dynconv_lowrank_fwd"][0][7:],
+    ctypes.c_int)
+_SIGNATURES["dynconv_lowrank_bwd_ex"] = (
+    _SIGNATURES["dynconv_lowrank_bwd"][0][:7] + [_vp, _i64p] + _SIGNATURES["dynconv_lowrank_bwd"][0][7:15] + [_vp]
+    + _SIGNATURES["dynconv_lowrank_bwd"][0][15:], ctypes.c_int)
+_SIGNATURES["dynconv_lowrank_bwd_ex_workspace_size"] = ([_i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_int,
+                                                         ctypes.c_int], _sz)
+_SIGNATURES["dynconv_lowrank_decode_step_ex"] = (
+    _SIGNATURES["dynconv_lowrank_decode_step"][0][:7] + [_vp] + _SIGNATURES["dynconv_lowrank_decode_step"][0][7:],
+    ctypes.c_int)
 _SIGNATURES["dynconv_cache_fill_varlen"] = (
     _SIGNATURES["dynconv_cache_fill"][0][:2] + [_vp, _i64p] + _SIGNATURES["dynconv_cache_fill"][0][2:], ctypes.c_int)
 

@@ -526,15 +526,28 @@ extern "C" {
 
 namespace {
 
+// Workspace of the low-rank backward: the partial sums of dU and db, then (with a
+// convolution-bias gradient) the column-sum partials of dy, 256-byte aligned.
+constexpr size_t kCbAlign = 256;
+size_t lowrank_cb_offset(const LowRankPlan& plan) { return (plan.ws_total + kCbAlign - 1) / kCbAlign * kCbAlign; }
+size_t lowrank_bwd_workspace(const LowRankPlan& plan, int64_t B, int64_t T, int64_t D, bool dcbias) {
+  if (!dcbias) return plan.ws_total;
+  return lowrank_cb_offset(plan) + size_t(B) * size_t(colsum_chunks(B, T, D)) * size_t(D) * sizeof(float);
+}
+
 dynconv_status lowrank_fwd_impl(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
-                                int64_t ldu, const void* bias, const int32_t* seg, const int64_t* ss, void* y,
-                                const int64_t* ys, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
-                                dynconv_dtype dtype, void* stream) {
+                                int64_t ldu, const void* bias, const int32_t* seg, const int64_t* ss,
+                                const void* conv_bias, void* y, const int64_t* ys, int64_t B, int64_t T, int64_t D,
+                                int32_t W, int32_t H, int32_t R, dynconv_dtype dtype, void* stream) {
   dynconv_status st = check_lowrank(x, xs, z, zs, U, ldu, B, T, D, W, H, R, dtype);
   if (st != DYNCONV_OK) return st;
   if ((st = check_act(y, ys, true)) != DYNCONV_OK) return st;
   if (ys[1] >= kLowrankMaxRowStride) return DYNCONV_ERR_UNSUPPORTED;
   if (y == x || y == z || y == U || (bias != nullptr && y == bias)) return DYNCONV_ERR_INVALID_ARG;
+  if (conv_bias != nullptr) {
+    if (conv_bias == y) return DYNCONV_ERR_INVALID_ARG;
+    if (!aligned(conv_bias, 4)) return DYNCONV_ERR_UNSUPPORTED;
+  }
   if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
   const int eb = elem_bytes(dtype);
   const Act acts[2] = {{x, xs}, {y, ys}};
@@ -547,6 +560,7 @@ dynconv_status lowrank_fwd_impl(const void* x, const int64_t* xs, const void* z,
   p.out = y;
   p.os0 = ys[0];
   p.os1 = ys[1];
+  p.cbias = conv_bias;
   if (seg != nullptr) {
     p.seg = seg;
     p.ss0 = ss[0];
@@ -562,7 +576,8 @@ extern "C" {
 dynconv_status dynconv_lowrank_fwd(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
                                    int64_t ldu, const void* bias, void* y, const int64_t* ys, int64_t B, int64_t T,
                                    int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype, void* stream) {
-  return lowrank_fwd_impl(x, xs, z, zs, U, ldu, bias, nullptr, nullptr, y, ys, B, T, D, W, H, R, dtype, stream);
+  return lowrank_fwd_impl(x, xs, z, zs, U, ldu, bias, nullptr, nullptr, nullptr, y, ys, B, T, D, W, H, R, dtype,
+                          stream);
 }
 
 dynconv_status dynconv_lowrank_fwd_varlen(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
@@ -572,14 +587,32 @@ dynconv_status dynconv_lowrank_fwd_varlen(const void* x, const int64_t* xs, cons
                                           void* stream) {
   const dynconv_status st = check_seg(seq_idx, ss);
   if (st != DYNCONV_OK) return st;
-  return lowrank_fwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, y, ys, B, T, D, W, H, R, dtype, stream);
+  return lowrank_fwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, nullptr, y, ys, B, T, D, W, H, R, dtype, stream);
+}
+
+dynconv_status dynconv_lowrank_fwd_ex(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                      const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                      const int64_t* ss, const void* conv_bias, void* y, const int64_t* ys, int64_t B,
+                                      int64_t T, int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                      void* stream) {
+  if (seq_idx != nullptr) {
+    const dynconv_status st = check_seg(seq_idx, ss);
+    if (st != DYNCONV_OK) return st;
+  }
+  return lowrank_fwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, conv_bias, y, ys, B, T, D, W, H, R, dtype,
+                          stream);
 }
 
 size_t dynconv_lowrank_bwd_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
                                           dynconv_dtype dtype) {
+  return dynconv_lowrank_bwd_ex_workspace_size(B, T, D, W, H, R, 0, dtype);
+}
+
+size_t dynconv_lowrank_bwd_ex_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                             int want_dconv_bias, dynconv_dtype dtype) {
   if (check_common(B, T, D, W, H, dtype) != DYNCONV_OK || R < 1 || R > 128 || W > kMaxLowrankW) return 0;
   if (B == 0 || T == 0 || D == 0) return 0;
-  return plan_lowrank(B, T, D, W, H, R, true, dtype).ws_total;
+  return lowrank_bwd_workspace(plan_lowrank(B, T, D, W, H, R, true, dtype), B, T, D, want_dconv_bias != 0);
 }
 
 }  // extern "C"
@@ -589,8 +622,8 @@ namespace {
 dynconv_status lowrank_bwd_impl(const void* x, const int64_t* xs, const void* z, const int64_t* zs, const void* U,
                                 int64_t ldu, const void* bias, const int32_t* seg, const int64_t* ss, const void* dy,
                                 const int64_t* dys, void* dx, const int64_t* dxs, void* dz, const int64_t* dzs,
-                                float* dU, float* db, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
-                                int32_t R, dynconv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                float* dU, float* db, float* dcb, int64_t B, int64_t T, int64_t D, int32_t W,
+                                int32_t H, int32_t R, dynconv_dtype dtype, void* workspace, size_t workspace_bytes,
                                 void* stream) {
   dynconv_status st = check_lowrank(x, xs, z, zs, U, ldu, B, T, D, W, H, R, dtype);
   if (st != DYNCONV_OK) return st;
@@ -600,21 +633,24 @@ dynconv_status lowrank_bwd_impl(const void* x, const int64_t* xs, const void* z,
   if (dzs[2] != 1 || dzs[0] < 0 || dzs[1] < 0) return DYNCONV_ERR_UNSUPPORTED;
   if (dys[1] >= kLowrankMaxRowStride || dxs[1] >= kLowrankMaxRowStride) return DYNCONV_ERR_UNSUPPORTED;
   const void* ins[5] = {x, z, U, bias, dy};
-  const void* outs[4] = {dx, dz, dU, db};
+  const void* outs[5] = {dx, dz, dU, db, dcb};
   for (const void* o : outs) {
     if (o == nullptr) continue;
     for (const void* in : ins)
       if (in != nullptr && o == in) return DYNCONV_ERR_INVALID_ARG;
   }
-  if (dx == dz || dx == dU || dz == dU || (db != nullptr && (db == dx || db == dz || db == dU)))
-    return DYNCONV_ERR_INVALID_ARG;
-  if (!aligned(dU, 4) || (db != nullptr && !aligned(db, 4))) return DYNCONV_ERR_UNSUPPORTED;
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (outs[i] != nullptr && outs[i] == outs[j]) return DYNCONV_ERR_INVALID_ARG;
+  if (!aligned(dU, 4) || (db != nullptr && !aligned(db, 4)) || (dcb != nullptr && !aligned(dcb, 4)))
+    return DYNCONV_ERR_UNSUPPORTED;
   if (B == 0 || T == 0 || D == 0) return DYNCONV_OK;
   const int eb = elem_bytes(dtype);
   const Act acts[3] = {{x, xs}, {dy, dys}, {dx, dxs}};
   if (!act_align_ok(acts, 3, eb, 4)) return DYNCONV_ERR_UNSUPPORTED;
   const LowRankPlan plan = plan_lowrank(B, T, D, W, H, R, true, dtype);
-  if (workspace == nullptr || workspace_bytes < plan.ws_total) return DYNCONV_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < lowrank_bwd_workspace(plan, B, T, D, dcb != nullptr))
+    return DYNCONV_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return DYNCONV_ERR_UNSUPPORTED;
   LowRankParams p = lowrank_params(x, xs, z, zs, U, ldu, bias, B, T, D, W, H, R, plan);
   p.act16 = act_align_ok(acts, 3, eb, 16) ? 1 : 0;
@@ -638,7 +674,13 @@ dynconv_status lowrank_bwd_impl(const void* x, const int64_t* xs, const void* z,
     p.ss0 = ss[0];
     p.ss1 = ss[1];
   }
-  return launch_lowrank_bwd(p, plan, W, dtype, dU, db, static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dcb != nullptr) {
+    // the bias gradient, sum of dy over every token (packed sequences included)
+    float* part = reinterpret_cast<float*>(wsb + lowrank_cb_offset(plan));
+    if ((st = launch_column_sums(dy, dys[0], dys[1], B, T, D, dtype, part, dcb, hs)) != DYNCONV_OK) return st;
+  }
+  return launch_lowrank_bwd(p, plan, W, dtype, dU, db, hs);
 }
 
 }  // namespace
@@ -650,8 +692,8 @@ dynconv_status dynconv_lowrank_bwd(const void* x, const int64_t* xs, const void*
                                    const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db, int64_t B,
                                    int64_t T, int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  return lowrank_bwd_impl(x, xs, z, zs, U, ldu, bias, nullptr, nullptr, dy, dys, dx, dxs, dz, dzs, dU, db, B, T, D,
-                          W, H, R, dtype, workspace, workspace_bytes, stream);
+  return lowrank_bwd_impl(x, xs, z, zs, U, ldu, bias, nullptr, nullptr, dy, dys, dx, dxs, dz, dzs, dU, db, nullptr, B,
+                          T, D, W, H, R, dtype, workspace, workspace_bytes, stream);
 }
 
 dynconv_status dynconv_lowrank_bwd_varlen(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
@@ -663,8 +705,23 @@ dynconv_status dynconv_lowrank_bwd_varlen(const void* x, const int64_t* xs, cons
                                           void* stream) {
   const dynconv_status st = check_seg(seq_idx, ss);
   if (st != DYNCONV_OK) return st;
-  return lowrank_bwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, dy, dys, dx, dxs, dz, dzs, dU, db, B, T, D, W, H,
-                          R, dtype, workspace, workspace_bytes, stream);
+  return lowrank_bwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, dy, dys, dx, dxs, dz, dzs, dU, db, nullptr, B, T,
+                          D, W, H, R, dtype, workspace, workspace_bytes, stream);
+}
+
+dynconv_status dynconv_lowrank_bwd_ex(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                      const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                      const int64_t* ss, const void* dy, const int64_t* dys, void* dx,
+                                      const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db,
+                                      float* dconv_bias, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                                      int32_t R, dynconv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (seq_idx != nullptr) {
+    const dynconv_status st = check_seg(seq_idx, ss);
+    if (st != DYNCONV_OK) return st;
+  }
+  return lowrank_bwd_impl(x, xs, z, zs, U, ldu, bias, seq_idx, ss, dy, dys, dx, dxs, dz, dzs, dU, db, dconv_bias, B, T,
+                          D, W, H, R, dtype, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------
@@ -796,6 +853,15 @@ dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, con
                                            const int64_t* cs, void* y, const int64_t* ys, int64_t t, int64_t B,
                                            int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
                                            void* stream) {
+  return dynconv_lowrank_decode_step_ex(x, xs, z, zs, U, ldu, bias, nullptr, cache, cs, y, ys, t, B, D, W, H, R, dtype,
+                                        stream);
+}
+
+dynconv_status dynconv_lowrank_decode_step_ex(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                              const void* U, int64_t ldu, const void* bias, const void* conv_bias,
+                                              void* cache, const int64_t* cs, void* y, const int64_t* ys, int64_t t,
+                                              int64_t B, int64_t D, int32_t W, int32_t H, int32_t R,
+                                              dynconv_dtype dtype, void* stream) {
   dynconv_status st = check_common(B, 1, D, W, H, dtype);
   if (st != DYNCONV_OK) return st;
   const int eb = elem_bytes(dtype);
@@ -811,8 +877,13 @@ dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, con
   if (y == x || y == z || y == U || (bias != nullptr && y == bias) ||
       (W > 1 && (y == cache || cache == x || cache == z || cache == U)))
     return DYNCONV_ERR_INVALID_ARG;
+  if (conv_bias != nullptr) {
+    if (conv_bias == y || conv_bias == cache) return DYNCONV_ERR_INVALID_ARG;
+    if (!aligned(conv_bias, eb)) return DYNCONV_ERR_UNSUPPORTED;
+  }
   if (B == 0 || D == 0) return DYNCONV_OK;
   DecodeParams p = decode_params(x, xs, cache, cs, y, ys, t, B, D, W, H);
+  p.cbias = conv_bias;
   p.z = z;
   p.zs0 = zs[0];
   p.U = U;

@@ -240,6 +240,8 @@ __global__ __launch_bounds__(64) void k_lowrank_decode_step(const DecodeParams p
     for (int k = 0; k < W; ++k) bias[k] = RT(0);
   }
 
+  const float cb = p.cbias != nullptr ? ldf<ET>(p.cbias, ca) : 0.f;  // optional convolution bias
+
   // Every load is in flight before the first wait.
   __builtin_amdgcn_sched_barrier(0);
 
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(64) void k_lowrank_decode_step(const DecodeParams p
 #pragma unroll
     for (int s = 0; s < NK; ++s) acc = M::mma(a[s], bt[s][k], acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = k == 0 ? fmaf(acc[i], xv[i], xv[i]) : fmaf(acc[i], cv[i][k], y[i]);
+    for (int i = 0; i < 4; ++i) y[i] = k == 0 ? fmaf(acc[i], xv[i], xv[i] + cb) : fmaf(acc[i], cv[i][k], y[i]);
   }
   if (c0 + l >= p.D) return;
 #pragma unroll

@@ -101,6 +101,14 @@ dynconv_status launch_reduce_partials(const float* partial, int64_t nchunk, int6
 dynconv_status launch_reduce_partials2(const float* part0, int64_t n0, float* out0, const float* part1, int64_t n1,
                                        float* out1, int64_t nchunk, hipStream_t stream);
 
+// Column sums of an activation-shaped tensor a [B,T,D] (strides s0, s1; 4-byte aligned rows):
+// out[d] = sum over (b, t) of a[b,t,d], the gradient of a convolution bias. Float32 partial
+// sums per (sequence, chunk of tokens) go to part [B * colsum_chunks(B, T, D)][D], then the
+// fixed-order reduce, so results are run-to-run identical.
+int64_t colsum_chunks(int64_t B, int64_t T, int64_t D);
+dynconv_status launch_column_sums(const void* a, int64_t s0, int64_t s1, int64_t B, int64_t T, int64_t D,
+                                  dynconv_dtype dt, float* part, float* out, hipStream_t stream);
+
 // Records a HIP failure for dynconv_last_hip_error(); returns DYNCONV_ERR_HIP.
 dynconv_status record_hip_error(hipError_t e);
 

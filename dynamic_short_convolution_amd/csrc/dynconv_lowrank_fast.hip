@@ -401,6 +401,17 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) zr[ks] = 4 * n * ZROW + ((4 * ks + q + n) % ZCPR) * 16;
   const int ytw = xhi;  // y tile: the lane writes row 4n + j (+ j * XROW), same rotation as x
+  // optional convolution bias of the lane's 4 channels c_base + 8 xc + 4 (q & 1) + mt
+  float cb[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.cbias != nullptr) {  // 4-byte aligned (C ABI)
+    const uint32_t* v =
+        reinterpret_cast<const uint32_t*>(static_cast<const ET*>(p.cbias) + c_base + 8 * xc + 4 * (q & 1));
+    const uint32_t v0 = v[0], v1 = v[1];
+    cb[0] = Cvt<ET>::lo(v0);
+    cb[1] = Cvt<ET>::hi(v0);
+    cb[2] = Cvt<ET>::lo(v1);
+    cb[3] = Cvt<ET>::hi(v1);
+  }
 
   // y: buffer resource spanning this sequence's rows 0 .. T-1 (stores past it are dropped)
   __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const float xt = xv[j - MLO][mt];
-        float y = fmaf(a[mt][0], xt, xt);
+        float y = fmaf(a[mt][0], xt, xt + cb[mt]);
 #pragma unroll
         for (int k = 1; k < W; ++k) {
           const float ak = (!SG || idv[j + 4 - k] == idv[j + 4]) ? tap_of<W>(a, mt, k) : 0.f;

@@ -15,6 +15,7 @@ struct LowRankParams {
   const void* z;
   const void* U;
   const void* bias;  // may be null
+  const void* cbias; // forward: optional convolution bias [D] (dtype), added to y; may be null
   const void* dy;
   void* out;   // y (forward) or dx (backward)
   void* dz;

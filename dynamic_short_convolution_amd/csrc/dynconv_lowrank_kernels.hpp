@@ -474,6 +474,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
   __syncthreads();
 
   const int lane_c = (q / LPC) * MT;  // first channel of this lane's run, within the wave
+  // optional convolution bias of the lane's channels (zero without one, or past D)
+  float cbv[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int ch = cw0 + lane_c + mt;
+    cbv[mt] = (p.cbias != nullptr && ch < p.D) ? Raw<ET>::to_float(Raw<ET>::from_mem(static_cast<const ET*>(p.cbias), ch))
+                                                : 0.f;
+  }
   for (int t0 = t_first; t0 < t_end; t0 += TT) {
     const bool more = t0 + TT < t_end;
     if (more) prefetch(zpre_s[0], xpre_s[0], t0 + TT);
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
     if ((q % LPC) == 0 && t < t_end && cg < p.D) {
       float yv[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) yv[mt] = xcur[mt] + sum[mt];
+      for (int mt = 0; mt < MT; ++mt) yv[mt] = xcur[mt] + sum[mt] + cbv[mt];
       global_store_run<ET, MT>(y + int64_t(t) * p.os1 + cg, yv, act16, p.D - cg);
     }
     __syncthreads();

@@ -126,6 +126,46 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce_partials4x2(const floa
   }
 }
 
+// Partial column sums: workgroup (chunk, db) sums 256 lanes x one 32-bit word of channels
+// over the chunk's tokens (8 rows of loads in flight per lane).
+template <typename ET>
+__global__ __launch_bounds__(kBlockThreads) void k_column_partials(const ET* __restrict__ a, int64_t s0, int64_t s1,
+                                                                   int T, int D, int L, int nchunk, int nDb,
+                                                                   float* __restrict__ part) {
+  constexpr int V = 4 / int(sizeof(ET));  // channels per lane
+  const int db = int(blockIdx.x % unsigned(nDb));
+  const int chunk = int(blockIdx.x / unsigned(nDb));  // b * nchunk + token chunk
+  const int b = chunk / nchunk, tc = chunk % nchunk;
+  const int c = (db * kBlockThreads + int(threadIdx.x)) * V;
+  if (c >= D) return;
+  const int t0 = tc * L, t1 = min(T, t0 + L);
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(a + b * s0 + c);
+  const int64_t row = s1 * int64_t(sizeof(ET)) / 4;  // words per row
+  float s[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) s[v] = 0.f;
+  auto add = [&](uint32_t w) {
+    if constexpr (V == 2) {
+      s[0] += Cvt<ET>::lo(w);
+      s[1] += Cvt<ET>::hi(w);
+    } else {
+      s[0] += __uint_as_float(w);
+    }
+  };
+  int t = t0;
+  for (; t + 8 <= t1; t += 8) {
+    uint32_t w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = p[(t + u) * row];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(w[u]);
+  }
+  for (; t < t1; ++t) add(p[t * row]);
+  float* o = part + int64_t(chunk) * D + c;
+#pragma unroll
+  for (int v = 0; v < V; ++v) o[v] = s[v];
+}
+
 bool reduce4_ok(const float* part, int64_t n, const float* out) {
   return n % 4 == 0 && reinterpret_cast<uintptr_t>(part) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
 }
@@ -267,6 +307,36 @@ dynconv_status launch_reduce_partials2(const float* part0, int64_t n0, float* ou
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DYNCONV_OK : record_hip_error(e);
+}
+
+// About 2048 workgroups (of 256 channels each at one channel per lane), chunks of at least
+// 64 tokens.
+int64_t colsum_chunks(int64_t B, int64_t T, int64_t D) {
+  const int64_t per_seq = (2048 + B * ((D + 255) / 256) - 1) / (B * ((D + 255) / 256));
+  const int64_t most = (T + 63) / 64;
+  return per_seq < 1 ? 1 : (per_seq > most ? (most < 1 ? 1 : most) : per_seq);
+}
+
+dynconv_status launch_column_sums(const void* a, int64_t s0, int64_t s1, int64_t B, int64_t T, int64_t D,
+                                  dynconv_dtype dt, float* part, float* out, hipStream_t stream) {
+  const int64_t nchunk = colsum_chunks(B, T, D);
+  const int64_t L = (T + nchunk - 1) / nchunk;
+  const int V = dt == DYNCONV_F32 ? 1 : 2;
+  const int64_t nDb = (D + int64_t(kBlockThreads) * V - 1) / (int64_t(kBlockThreads) * V);
+  const dim3 grid(unsigned(B * nchunk * nDb));
+  if (dt == DYNCONV_BF16) {
+    hipLaunchKernelGGL(k_column_partials<bf16_t>, grid, dim3(kBlockThreads), 0, stream, static_cast<const bf16_t*>(a),
+                       s0, s1, int(T), int(D), int(L), int(nchunk), int(nDb), part);
+  } else if (dt == DYNCONV_F16) {
+    hipLaunchKernelGGL(k_column_partials<f16_t>, grid, dim3(kBlockThreads), 0, stream, static_cast<const f16_t*>(a),
+                       s0, s1, int(T), int(D), int(L), int(nchunk), int(nDb), part);
+  } else {
+    hipLaunchKernelGGL(k_column_partials<float>, grid, dim3(kBlockThreads), 0, stream, static_cast<const float*>(a),
+                       s0, s1, int(T), int(D), int(L), int(nchunk), int(nDb), part);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return record_hip_error(e);
+  return launch_reduce_partials(part, B * nchunk, D, out, stream);
 }
 
 }  // namespace dynconv

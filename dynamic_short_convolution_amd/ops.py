@@ -216,19 +216,24 @@ def _check_lowrank_operands(x, z, U, bias, J: int):
             raise TypeError(f"{name} is {t.dtype} but x is {x.dtype}")
 
 
-def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None, seq_idx=None):
-    """y = x + conv(x) with filters z U + bias generated on the GPU (never stored); with
-    seq_idx (int32 [B, T]) no tap crosses into another segment."""
+def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None, seq_idx=None, conv_bias=None):
+    """y = x + conv(x) with filters z U + bias generated on the GPU (never stored), plus
+    conv_bias [D] on every token if given; with seq_idx (int32 [B, T]) no tap crosses into
+    another segment."""
     B, T, D = _check_act3(x)
     R = z.shape[-1]
     _check_lowrank_operands(x, z, U, bias, _groups(D, H) * W)
+    conv_bias = _conv_bias_arg(conv_bias, x)
     _expect("out", out, (B, T, D), x.dtype)
     y = torch.empty_like(x) if out is None else out
-    dev = _require_device(x, z, U, bias, y, seq_idx)
+    dev = _require_device(x, z, U, bias, y, seq_idx, conv_bias)
     lib = _lib.load()
     head = (_ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias))
     tail = (_ptr(y), _lib.strides(y.stride()), B, T, D, W, H, R, _dtype_code(x), _stream(dev))
-    if seq_idx is None:
+    if conv_bias is not None:
+        seg = _seg_args(seq_idx, B, T) if seq_idx is not None else (None, None)
+        st = lib.dynconv_lowrank_fwd_ex(*head, *seg, _ptr(conv_bias), *tail)
+    elif seq_idx is None:
         st = lib.dynconv_lowrank_fwd(*head, *tail)
     else:
         st = lib.dynconv_lowrank_fwd_varlen(*head, *_seg_args(seq_idx, B, T), *tail)
@@ -236,15 +241,18 @@ def dynconv_lowrank_fwd(x, z, U, bias, W: int, H: int = 1, out=None, seq_idx=Non
     return y
 
 
-def dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dtype) -> int:
-    return int(_lib.load().dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, _DTYPE[dtype]))
+def dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dtype, want_dconv_bias: bool = False) -> int:
+    return int(_lib.load().dynconv_lowrank_bwd_ex_workspace_size(B, T, D, W, H, R, int(bool(want_dconv_bias)),
+                                                                 _DTYPE[dtype]))
 
 
 def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = True, workspace=None,
-                        seq_idx=None):
-    """(dx, dz, dU, db) of <dy, dynconv_lowrank_fwd(...)>; dU and db are float32. A caller's
-    workspace must be a contiguous tensor on x's device of at least
-    dynconv_lowrank_bwd_workspace_size(...) bytes (the library checks the size)."""
+                        seq_idx=None, want_dconv_bias: bool = False):
+    """(dx, dz, dU, db) of <dy, dynconv_lowrank_fwd(...)>; dU and db are float32. With
+    want_dconv_bias, (dx, dz, dU, db, dconv_bias): the float32 [D] gradient of a convolution
+    bias (the sum of dy over every token). A caller's workspace must be a contiguous tensor
+    on x's device of at least dynconv_lowrank_bwd_workspace_size(..., want_dconv_bias)
+    bytes (the library checks the size)."""
     B, T, D = _check_act3(x)
     R = z.shape[-1]
     J = _groups(D, H) * W
@@ -257,9 +265,10 @@ def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = T
     dz = torch.empty_like(z)
     dU = torch.empty((R, J), dtype=torch.float32, device=x.device)
     db = torch.empty((J,), dtype=torch.float32, device=x.device) if need_db else None
+    dcb = torch.empty((D,), dtype=torch.float32, device=x.device) if want_dconv_bias else None
     lib = _lib.load()
     if workspace is None:
-        ws_bytes = dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, x.dtype)
+        ws_bytes = dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, x.dtype, want_dconv_bias)
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
@@ -268,6 +277,11 @@ def dynconv_lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, need_db: bool = T
         _ptr(dy), _lib.strides(dy.stride()), _ptr(dx), _lib.strides(dx.stride()), _ptr(dz), _lib.strides(dz.stride()),
         _ptr(dU), _ptr(db), B, T, D, W, H, R, _dtype_code(x), _ptr(workspace), ws_bytes, _stream(dev),
     )
+    if want_dconv_bias:
+        seg = _seg_args(seq_idx, B, T) if seq_idx is not None else (None, None)
+        st = lib.dynconv_lowrank_bwd_ex(*head, *seg, *tail[:8], _ptr(dcb), *tail[8:])
+        _lib.check("dynconv_lowrank_bwd", st)
+        return dx, dz, dU, db, dcb
     if seq_idx is None:
         st = lib.dynconv_lowrank_bwd(*head, *tail)
     else:
@@ -386,9 +400,9 @@ def dynconv_decode_step(x, w, cache, t: int, H: int = 1, out=None, conv_bias=Non
     return y
 
 
-def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None, H: int = 1):
-    """y [B,D] of token t with filters z [B,R] U + bias generated on the GPU (U: [R, (D/H)*W]);
-    the cache is updated in place."""
+def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None, H: int = 1, conv_bias=None):
+    """y [B,D] of token t with filters z [B,R] U + bias generated on the GPU (U: [R, (D/H)*W]),
+    plus conv_bias [D] if given; the cache is updated in place."""
     if x.dim() != 2:
         raise ValueError(f"x must be [B, D]; got shape {list(x.shape)}")
     B, D = x.shape
@@ -399,10 +413,12 @@ def dynconv_lowrank_decode_step(x, z, U, bias, cache, t: int, W: int, out=None, 
         raise ValueError("a cache [B, W-1, D] is required for W > 1")
     _expect("out", out, (B, D), x.dtype)
     y = torch.empty_like(x) if out is None else out
-    dev = _require_device(x, z, U, bias, y, cache)
+    conv_bias = _conv_bias_arg(conv_bias, x)
+    dev = _require_device(x, z, U, bias, y, cache, conv_bias)
     cs = _lib.strides(cache.stride()) if cache is not None else None
-    st = _lib.load().dynconv_lowrank_decode_step(
+    st = _lib.load().dynconv_lowrank_decode_step_ex(
         _ptr(x), _lib.strides(x.stride()), _ptr(z), _lib.strides(z.stride()), _ptr(U), U.stride(0), _ptr(bias),
-        _ptr(cache), cs, _ptr(y), _lib.strides(y.stride()), int(t), B, D, W, H, R, _dtype_code(x), _stream(dev))
+        _ptr(conv_bias), _ptr(cache), cs, _ptr(y), _lib.strides(y.stride()), int(t), B, D, W, H, R, _dtype_code(x),
+        _stream(dev))
     _lib.check("dynconv_lowrank_decode_step", st)
     return y

@@ -236,7 +236,8 @@ dynconv_status dynconv_lowrank_bwd_varlen(const void* x, const int64_t* xs, cons
  *   dconv_bias  [D] float32, overwritten with sum over (b, t) of dy (NULL to skip)
  * The backward's workspace then holds float32 partial sums of dy per (sequence, time
  * chunk) after those of a static filter: size it with dynconv_bwd_ex_workspace_size.
- * Materialised, static and head-wise forms; the decoding step adds c to its output.
+ * Materialised, static and head-wise forms (the low-rank form: dynconv_lowrank_*_ex below);
+ * the decoding step adds c to its output.
  */
 dynconv_status dynconv_fwd_ex(const void* x, const int64_t* xs, const void* w, const int64_t* ws,
                               const int32_t* seq_idx, const int64_t* ss, const void* conv_bias, void* y,
@@ -256,6 +257,42 @@ dynconv_status dynconv_decode_step_ex(const void* x, const int64_t* xs, const vo
                                       const void* conv_bias, void* cache, const int64_t* cs, void* y,
                                       const int64_t* ys, int64_t t, int64_t B, int64_t D, int32_t W, int32_t H,
                                       dynconv_dtype dtype, void* stream);
+
+/*
+ * The same optional convolution bias on the low-rank form (y = x + conv(x) + c with the
+ * generated filters), together with optional segment ids (seq_idx == NULL: one document
+ * per row, ss ignored); every other argument is as in dynconv_lowrank_{fwd,bwd} and
+ * dynconv_lowrank_decode_step.
+ *   conv_bias   [D] of `dtype`, contiguous, 4-byte aligned (decoding step: element
+ *               aligned), or NULL
+ *   dconv_bias  [D] float32, 4-byte aligned, overwritten with sum over (b, t) of dy (NULL
+ *               to skip); its float32 partial sums per (sequence, chunk of tokens) take
+ *               workspace after those of dU and db: size the workspace with
+ *               dynconv_lowrank_bwd_ex_workspace_size(..., want_dconv_bias = 1, ...).
+ * The bias gradient reads dy once more (one extra pass over B*T*D elements).
+ */
+dynconv_status dynconv_lowrank_fwd_ex(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                      const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                      const int64_t* ss, const void* conv_bias, void* y, const int64_t* ys, int64_t B,
+                                      int64_t T, int64_t D, int32_t W, int32_t H, int32_t R, dynconv_dtype dtype,
+                                      void* stream);
+
+size_t dynconv_lowrank_bwd_ex_workspace_size(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int32_t R,
+                                             int want_dconv_bias, dynconv_dtype dtype);
+
+dynconv_status dynconv_lowrank_bwd_ex(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                      const void* U, int64_t ldu, const void* bias, const int32_t* seq_idx,
+                                      const int64_t* ss, const void* dy, const int64_t* dys, void* dx,
+                                      const int64_t* dxs, void* dz, const int64_t* dzs, float* dU, float* db,
+                                      float* dconv_bias, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                                      int32_t R, dynconv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+dynconv_status dynconv_lowrank_decode_step_ex(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
+                                              const void* U, int64_t ldu, const void* bias, const void* conv_bias,
+                                              void* cache, const int64_t* cs, void* y, const int64_t* ys, int64_t t,
+                                              int64_t B, int64_t D, int32_t W, int32_t H, int32_t R,
+                                              dynconv_dtype dtype, void* stream);
 
 /*
  * The convolution in the epilogue of the producing projection (the reading note's

@@ -173,9 +173,11 @@ def lowrank_filters(z, U, bias, W: int) -> np.ndarray:
     return wf.reshape(B, T, J // W, W)
 
 
-def lowrank_fwd(x, z, U, bias, W: int, H: int = 1, seq_idx=None) -> np.ndarray:
-    """Low-rank form: filters z U + b (never stored by the kernel), then eq. 2 + eq. 3."""
-    return conv_fwd(x, lowrank_filters(z, U, bias, W), H, seq_idx)
+def lowrank_fwd(x, z, U, bias, W: int, H: int = 1, seq_idx=None, conv_bias=None) -> np.ndarray:
+    """Low-rank form: filters z U + b (never stored by the kernel), then eq. 2 + eq. 3, plus
+    the optional convolution bias c (its gradient is conv_bias_grad(dy), whatever the
+    filters)."""
+    return conv_fwd(x, lowrank_filters(z, U, bias, W), H, seq_idx, conv_bias)
 
 
 def lowrank_bwd(x, z, U, bias, dy, W: int, H: int = 1, seq_idx=None):

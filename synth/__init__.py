@@ -29,6 +29,7 @@ TENSOR_STREAM = {
     "w_static": 6,
     "probe": 7,
     "seg": 8,
+    "c": 9,  # convolution bias (the low-rank tests, whose "b" is the generator bias)
 }
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}

@@ -150,6 +150,47 @@ def test_lowrank_validation(lib):
     assert st == WORKSPACE
 
 
+def test_lowrank_conv_bias_validation(lib):
+    """dynconv_lowrank_{fwd,bwd,decode_step}_ex: the bias may not alias the output, needs
+    4-byte alignment (element alignment when decoding), and the bias gradient needs its own
+    workspace (the partial sums of dy after those of dU and db) and a distinct output."""
+    CB, DCB = P(0xB00000), P(0xB10000)
+
+    def fwd_(cb=CB, y=Y, seq=None):
+        return lib.dynconv_lowrank_fwd_ex(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, seq, S(4, 1) if seq else
+                                          None, cb, y, S(800, 200, 1), 2, 4, 200, 4, 1, 64, BF16, None)
+
+    assert fwd_(cb=Y) == INVALID
+    assert fwd_(cb=P(0xB00002)) == UNSUP  # 2-byte aligned
+    assert fwd_(seq=P(0xB20002)) == UNSUP  # segment ids are int32: 4-byte aligned
+
+    base = lib.dynconv_lowrank_bwd_workspace_size(2, 4, 200, 4, 1, 64, BF16)
+    need = lib.dynconv_lowrank_bwd_ex_workspace_size(2, 4, 200, 4, 1, 64, 1, BF16)
+    assert lib.dynconv_lowrank_bwd_ex_workspace_size(2, 4, 200, 4, 1, 64, 0, BF16) == base
+    assert need >= base + 2 * 200 * 4  # at least one float32 partial per sequence and channel
+    big = lib.dynconv_lowrank_bwd_ex_workspace_size(8, 4096, 2048, 4, 1, 64, 1, BF16)
+    assert big % 4 == 0 and big > lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 64, BF16)
+
+    def bwd_(dcb=DCB, wsb=need, db=None):
+        return lib.dynconv_lowrank_bwd_ex(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, None, None, DY,
+                                          S(800, 200, 1), DX, S(800, 200, 1), P(0x990000), S(256, 64, 1), P(0x9a0000),
+                                          db, dcb, 2, 4, 200, 4, 1, 64, BF16, P(0x9b0000), wsb, None)
+
+    assert bwd_(wsb=need - 1) == WORKSPACE
+    assert bwd_(dcb=DX) == INVALID  # aliases dx
+    assert bwd_(dcb=DY) == INVALID  # aliases an input
+    assert bwd_(dcb=P(0x9a0000)) == INVALID  # aliases dU
+    assert bwd_(dcb=P(0xB10002)) == UNSUP  # float32 output 2-byte aligned
+
+    def dec_(cb=CB, y=P(0xC00000)):
+        return lib.dynconv_lowrank_decode_step_ex(X, S(200, 1), Z, S(64, 1), U, 800, None, cb, P(0xA00000),
+                                                  S(600, 200, 1), y, S(200, 1), 5, 2, 200, 4, 1, 64, BF16, None)
+
+    assert dec_(cb=P(0xC00000)) == INVALID
+    assert dec_(cb=P(0xA00000)) == INVALID  # aliases the cache
+    assert dec_(cb=P(0xB00001)) == UNSUP  # not element aligned
+
+
 def test_lowrank_row_stride_bound(lib):
     """Row strides of 2^24 elements or more are refused before any launch: the low-rank
     kernels form the offsets of up to 128 rows in 32-bit arithmetic."""

@@ -1,5 +1,6 @@
 """GPU parity of the optional convolution bias (dynconv_fwd_ex / dynconv_bwd_ex /
-dynconv_decode_step_ex) against the float64 oracle.
+dynconv_decode_step_ex, and dynconv_lowrank_{fwd,bwd,decode_step}_ex) against the float64
+oracle.
 
 The bias is the per-channel vector of the convolution technical report's Conv1D module,
 added to every output token; its gradient is the sum of dy over every token (float32,
@@ -11,8 +12,9 @@ import pytest
 import torch
 
 import synth
-from dynamic_short_convolution_amd import dynconv_bwd, dynconv_cache_fill, dynconv_decode_step, dynconv_fwd
-from oracle import conv_bias_grad, conv_bwd, conv_fwd
+from dynamic_short_convolution_amd import (dynconv_bwd, dynconv_cache_fill, dynconv_decode_step, dynconv_fwd,
+                                           dynconv_lowrank_bwd, dynconv_lowrank_decode_step, dynconv_lowrank_fwd)
+from oracle import conv_bias_grad, conv_bwd, conv_fwd, lowrank_fwd
 from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
@@ -106,4 +108,74 @@ def test_conv_bias_decode(dtype, W, H, static):
     cache = dynconv_cache_fill(xg[:, :T0], W)
     for t in range(T0, Ttot):
         yt = dynconv_decode_step(xg[:, t], wg if static else wg[:, t], cache, t, H, conv_bias=cg)
+        assert_close(f"y[{t}]", yt, ref[:, t], DT[dtype])
+
+
+# ------------------------------------------------------------------------------------
+# the low-rank form: the bias joins the generated filters' output; its gradient is one
+# more pass over dy, and the other gradients are those of the call without it, bit for bit
+# ------------------------------------------------------------------------------------
+LOWRANK = [
+    # dtype, B, T, D, W, H, R, packed: the fast kernels (bf16 / f16, D % 64, even R) and the
+    # general ones (float32, W = 5 above 64 ranks, odd R, groups of 6)
+    ("bf16", 2, 300, 128, 4, 1, 64, False),
+    ("f16", 2, 300, 128, 5, 1, 32, False),
+    ("bf16", 2, 300, 256, 4, 4, 20, True),
+    ("f32", 2, 300, 96, 3, 1, 16, False),
+    ("bf16", 2, 150, 96, 5, 1, 100, False),
+    ("bf16", 1, 77, 72, 2, 6, 7, True),
+]
+
+
+@pytest.mark.parametrize("dtype,B,T,D,W,H,R,packed", LOWRANK)
+def test_lowrank_conv_bias(dtype, B, T, D, W, H, R, packed):
+    seed = 800 + W + R + H
+    td = DT[dtype]
+    G = D // H
+    x = synth.draw((B, T, D), 1.0, seed, "x", dtype)
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", dtype)
+    z = synth.draw((B, T, R), 1.0, seed, "z", dtype)
+    U = synth.draw((R, G * W), 0.3 / R**0.5, seed, "U", dtype)
+    b = synth.draw((G * W,), 0.3, seed, "b", dtype)
+    c = synth.draw((D,), 0.5, seed, "c", dtype)
+    seq = synth.segments(B, T, 40.0, seed) if packed else None
+    xg, zg, Ug, bg, cg, dyg = x.cuda(), z.cuda(), U.cuda(), b.cuda(), c.cuda(), dy.cuda()
+    sg = seq.cuda() if packed else None
+    y = dynconv_lowrank_fwd(xg, zg, Ug, bg, W, H, seq_idx=sg, conv_bias=cg)
+    s64 = seq.numpy() if packed else None
+    assert_close("y", y, lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W, H, s64, to64(c)), td)
+    with_cb = dynconv_lowrank_bwd(xg, zg, Ug, bg, dyg, W, H, seq_idx=sg, want_dconv_bias=True)
+    without = dynconv_lowrank_bwd(xg, zg, Ug, bg, dyg, W, H, seq_idx=sg)
+    torch.cuda.synchronize()
+    for name, a_, b_ in zip(("dx", "dz", "dU", "db"), with_cb[:4], without):
+        assert torch.equal(a_, b_), name
+    assert_close("dconv_bias", with_cb[4], conv_bias_grad(to64(dy)), torch.float32, rtol=1e-5, atol=1e-5)
+
+
+def test_lowrank_conv_bias_many_chunks():
+    """Long sequences: the column sums take many chunks per sequence."""
+    B, T, D, W, R = 3, 3000, 192, 4, 32
+    x = synth.draw((B, T, D), 1.0, 5, "x", "bf16").cuda()
+    dy = synth.draw((B, T, D), 1.0, 5, "dy", "bf16")
+    z = synth.draw((B, T, R), 1.0, 5, "z", "bf16").cuda()
+    U = synth.draw((R, D * W), 0.05, 5, "U", "bf16").cuda()
+    out = dynconv_lowrank_bwd(x, z, U, None, dy.cuda(), W, want_dconv_bias=True)
+    assert_close("dconv_bias", out[4], conv_bias_grad(to64(dy)), torch.float32, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W,H,R", [(4, 1, 64), (3, 4, 20), (5, 3, 40)])
+def test_lowrank_conv_bias_decode(dtype, W, H, R):
+    B, Ttot, D, T0 = 5, 8, 96, 3
+    seed = 70 + W + R
+    x = synth.draw((B, Ttot, D), 1.0, seed, "x", dtype)
+    z = synth.draw((B, Ttot, R), 1.0, seed, "z", dtype)
+    U = synth.draw((R, (D // H) * W), 0.3 / R**0.5, seed, "U", dtype)
+    b = synth.draw(((D // H) * W,), 0.3, seed, "b", dtype)
+    c = synth.draw((D,), 0.5, seed, "c", dtype)
+    ref = lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W, H, None, to64(c))
+    xg, zg, Ug, bg, cg = x.cuda(), z.cuda(), U.cuda(), b.cuda(), c.cuda()
+    cache = dynconv_cache_fill(xg[:, :T0], W)
+    for t in range(T0, Ttot):
+        yt = dynconv_lowrank_decode_step(xg[:, t], zg[:, t], Ug, bg, cache, t, W, H=H, conv_bias=cg)
         assert_close(f"y[{t}]", yt, ref[:, t], DT[dtype])

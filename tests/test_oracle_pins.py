@@ -742,6 +742,20 @@ def test_pins_reject_conv_bias_mutants():
     assert not pin_conv_bias(conv_fwd, _mut_bias_grad_mean, 93)
 
 
+def _lowrank_as_conv(x, w, H=1, seq_idx=None, conv_bias=None):
+    """The low-rank form with U = I (R = (D/H) W, no generator bias): z U reproduces any
+    filter tensor, so the convolution-bias pin applies to the low-rank forward as is."""
+    B, T, G, W = np.shape(w)
+    return lowrank_fwd(x, np.reshape(w, (B, T, G * W)), np.eye(G * W), None, W, H, seq_idx, conv_bias)
+
+
+def test_lowrank_conv_bias():
+    assert pin_conv_bias(_lowrank_as_conv, conv_bias_grad, 94)
+    assert not pin_conv_bias(
+        lambda x, w, H=1, s=None, c=None: _lowrank_as_conv(x, w, H, s, None if c is None else 2 * c),
+        conv_bias_grad, 95)  # a bias counted twice
+
+
 # ----------------------------------------------------------------------------------
 # The convolution on a projection's output (the epilogue fusion of the end-to-end
 # throughput section): X = A W_p^T, then eq. 2 + eq. 3 on X.
