@@ -148,4 +148,6 @@ def workloads() -> dict:
         "headwise_h4": Workload("headwise_h4", 8, 4096, 2048, 4, 4, seed=5),
         "headwise_h16_bwd": Workload("headwise_h16_bwd", 8, 4096, 2048, 4, 16, seed=5),
         "lowrank_r64_bwd": Workload("lowrank_r64_bwd", 8, 4096, 2048, 4, 1, R=64, seed=5),
+        # Head-wise groups whose size is not a power of two: 12 channels per filter, D = 3072.
+        "headwise_h12": Workload("headwise_h12", 8, 4096, 3072, 4, 12, seed=6),
     }

@@ -313,6 +313,11 @@ def test_full_headwise_h16_bwd():
     _full_check(synth.workloads()["headwise_h16_bwd"], do_fwd=False)
 
 
+def test_full_headwise_h12_fwd_bwd():
+    # groups of 3 lanes (4 channels each), 63 lanes of a backward wave in use
+    _full_check(synth.workloads()["headwise_h12"])
+
+
 # The fixed-order reduce of the static backward's per-chunk partials has a 16-byte path
 # (row length n = D/H * W a multiple of 4, aligned pointers) and a 4-byte one; both sum
 # each column in the same order. n = 594 and a dw output one float off a 16-byte boundary
