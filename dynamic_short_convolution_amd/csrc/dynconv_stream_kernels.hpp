@@ -376,20 +376,60 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(
 //   dx_s = dy_s + sum_k w_k^(s+k) dy_{s+k}
 //   dw_t[g,k] = sum_{d in g} dy_t[d] x_{t-k}[d]
 // ---------------------------------------------------------------------------------
-// Sum of v over the `lanes` consecutive lanes of a group; `pos` is the lane's place in it.
-// A group never straddles a wave (lanes_in_use). Groups of 2^n lanes use a butterfly (every
-// lane gets the sum); other sizes a suffix scan whose first lane (pos 0) ends with the sum:
-// after the round with offset o, lane pos holds the sum over pos .. min(pos + 2o, lanes) - 1.
-__device__ __forceinline__ float group_sum(float v, int lanes, int pos) {
+// Sums of the N values v[k] over the `lanes` consecutive lanes of a group; `pos` is the
+// lane's place in it. A group never straddles a wave (lanes_in_use). Groups of 2^n lanes
+// use a butterfly, every lane ending with the sums: after the rounds below 2^r each lane
+// holds its aligned 2^r-lane sum, so any partner in the other half of the aligned 2^(r+1)
+// lanes completes the next one. Within 16 lanes the partners are DPP operand modifiers
+// (lane ^ 1, lane ^ 2, the mirror within 8, the mirror within 16: no LDS traffic); wider
+// rounds use ds_bpermute. Other group sizes use a suffix scan whose first lane (pos 0) ends
+// with the sums: after the round with offset o, lane pos holds the sum over pos ..
+// min(pos + 2o, lanes) - 1 (DPP shifts of the whole wave measured slower than ds_bpermute
+// there). Each round moves all N values at once, so their exchanges are in flight together
+// and one-lane groups pay a single branch. Backward at B8 T4096 W4 against one value per
+// call with ds_bpermute rounds: H = 128 99.9 -> 78.6 us, H = 32 87.8 -> 81.9, H = 16 86.6 ->
+// 86.4 (D = 2048); H = 12 226 -> 184, H = 96 181 -> 142 (D = 3072).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1, 0, 3, 2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2, 3, 0, 1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane 15 - i within 16 lanes
+
+template <int N>
+__device__ __forceinline__ void group_sums(float (&v)[N], int lanes, int pos) {
+  if (lanes == 1) return;
   if ((lanes & (lanes - 1)) == 0) {
-    for (int m = 1; m < lanes; m <<= 1) v += __shfl_xor(v, m, kWaveSize);
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += dpp_mov<kDppQuadSwap1>(v[k]);
+    if (lanes > 2) {
+#pragma unroll
+      for (int k = 0; k < N; ++k) v[k] += dpp_mov<kDppQuadSwap2>(v[k]);
+      if (lanes > 4) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += dpp_mov<kDppHalfMirror>(v[k]);
+        if (lanes > 8) {
+#pragma unroll
+          for (int k = 0; k < N; ++k) v[k] += dpp_mov<kDppMirror>(v[k]);
+          for (int m = 16; m < lanes; m <<= 1) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) v[k] += __shfl_xor(v[k], m, kWaveSize);
+          }
+        }
+      }
+    }
   } else {
     for (int o = 1; o < lanes; o <<= 1) {
-      const float u = __shfl_down(v, o, kWaveSize);
-      if (pos + o < lanes) v += u;
+      const bool in = pos + o < lanes;
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        const float u = __shfl_down(v[k], o, kWaveSize);
+        if (in) v[k] += u;
+      }
     }
   }
-  return v;
 }
 
 // ALL: both dx and dw are wanted, known at compile time (static filters only: their
@@ -520,8 +560,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
 #pragma unroll
           for (int k = 0; k < W; ++k) sdw[0][k] += s[k];
         } else {
-#pragma unroll
-          for (int k = 0; k < W; ++k) s[k] = group_sum(s[k], lanes_per_group, group_pos);
+          group_sums<W>(s, lanes_per_group, group_pos);
           if (group_lead) store_elems<NT, TapsRaw<ET, W, VEC, PERCH>::group_words, ET, W>(dwb + t * p.dws1, s);
         }
       }
@@ -680,7 +719,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_stream_bwd(const StreamParams
       } else {
         float s[W];
 #pragma unroll
-        for (int k = 0; k < W; ++k) s[k] = group_sum(sdw[0][k], lanes_per_group, group_pos);
+        for (int k = 0; k < W; ++k) s[k] = sdw[0][k];
+        group_sums<W>(s, lanes_per_group, group_pos);
         if (group_lead) {
 #pragma unroll
           for (int k = 0; k < W; ++k) part[int64_t(g) * W + k] = s[k];
