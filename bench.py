@@ -14,7 +14,9 @@ the Infinity Cache flushed between launches; and the float64 CPU oracle on a bou
 sample (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
-Prints ONE JSON line.
+Prints ONE JSON line. `--rows a,b,...` times only the named rows (the same timing, no
+headline, no CPU baseline): names from ROWS, or head-wise rows headwise_h<N>_{fwd,bwd} for
+any group size N (at D = 3072 when N does not divide 2048).
 """
 from __future__ import annotations
 
@@ -47,6 +49,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the per-form measurements")
+    ap.add_argument("--rows", default=None, help="comma-separated rows to time alone (prints only them)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--only", default=None,
                     help="run only this row's kernel in a loop (for profiler runs): one of ROWS, or 'copy'; "
@@ -405,12 +408,12 @@ def make_row(name, device):
         stream_bytes(B, T, D, W, H, static=static, fwd=False) + sb + (4 * D if cbias else 0), None, desc
 
 
-def run_rows(args, device):
+def time_rows(args, device, names, flush):
+    """Each named row timed on its own (median of args.reps launches, flush between)."""
     import torch
 
-    flush = Flusher(device)
     out = {}
-    for name in ROWS:
+    for name in names:
         fn, nbytes, flops, desc = make_row(name, device)
         med, mean = time_launches(fn, args.reps, flush)
         r = dict(config=desc, median_us=round(med * 1e3, 2), mean_us=round(mean * 1e3, 2), bytes=nbytes,
@@ -425,6 +428,12 @@ def run_rows(args, device):
         log(f"{name}: {r['median_us']} us, {r['gbs']} GB/s")
         del fn
         torch.cuda.empty_cache()
+    return out
+
+
+def run_rows(args, device):
+    flush = Flusher(device)
+    out = time_rows(args, device, ROWS, flush)
     # context, not the library: the runtime's own streaming kernels, timed the same way, as
     # the rates plain kernels reach on this part at three read/write mixes (a practical
     # ceiling next to the 8 TB/s peak)
@@ -646,7 +655,7 @@ def main():
               f"multi-GPU component (got --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     cpu = None
-    if not args.only and not args.no_cpu_baseline:
+    if not args.only and not args.rows and not args.no_cpu_baseline:
         # before any GPU call: its P-core setting forks worker processes
         log("cpu baseline: float64 oracle on a sample (1 core, then P cores)")
         cpu = run_cpu_baseline()
@@ -661,6 +670,9 @@ def main():
     _lib.load()
     if args.only:
         run_only(args, device)
+        return
+    if args.rows:
+        print(json.dumps({"rows": time_rows(args, device, args.rows.split(","), Flusher(device))}))
         return
 
     log("headline: generating inputs")
