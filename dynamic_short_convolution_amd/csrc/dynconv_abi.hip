@@ -75,7 +75,8 @@ int act_alignment(const Act* a, int n, int eb) {
 // 16-bit elements D must be even.
 dynconv_status check_stream_layout(int64_t D, int32_t H, int eb, int act_align) {
   if (act_align == 0 || D % (4 / eb) != 0) return DYNCONV_ERR_UNSUPPORTED;
-  if (H > 1 && H / group_vec(H, eb, act_align) > kWaveSize) return DYNCONV_ERR_UNSUPPORTED;
+  // the backward's layout has the most lanes per group
+  if (H > 1 && H / group_vec(H, eb, act_align, true) > kWaveSize) return DYNCONV_ERR_UNSUPPORTED;
   return DYNCONV_OK;
 }
 

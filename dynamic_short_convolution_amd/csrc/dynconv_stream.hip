@@ -185,7 +185,7 @@ StreamPlan plan_stream(int64_t B, int64_t T, int64_t D, int W, int H, int elem_b
     pl.lpg = 1;
   } else {
     pl.mode = StreamMode::Group;
-    pl.vec = group_vec(H, elem_bytes, act_align);
+    pl.vec = group_vec(H, elem_bytes, act_align, bwd);
     pl.lpg = H / pl.vec;
   }
   // The forward reduces nothing over a group: every lane in use, slices of whole cache lines

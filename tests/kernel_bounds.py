@@ -658,27 +658,29 @@ def lowrank_bwd_general(B, T, D, W, H, R, eb, fast, seg=False, has_bias=True, wa
 STREAM_WAVES = dict(fwd=8, fwd_group=12, fwd_wide=4, bwd=16, bwd_group=12, bwd_static=8, bwd_wide=8)
 
 
-def group_vec(H, eb, align):
-    """Channels per lane of a head-wise group: the largest power of two dividing H that
-    fits the lane vector (align bytes)."""
+def group_vec(H, eb, align, bwd):
+    """Channels per lane of a head-wise group: the largest power of two dividing H that fits
+    the lane vector (align bytes), or 6 for 16-bit groups of 3 * 2^k channels (k >= 1) in
+    the backward, and in the forward when the power of two is below 6."""
     v = align // eb
     while v > 1 and H % v:
         v //= 2
-    return v
+    three = H % 6 == 0 and (H // 3) & (H // 3 - 1) == 0
+    return 6 if (three and eb == 2 and (bwd or v < 6)) else v
 
 
 def stream_layout_ok(D, H, eb, align):
     """The ABI's check of the lane layout (check_stream_layout)."""
     if D % (4 // eb):
         return False
-    return H == 1 or H // group_vec(H, eb, align) <= 64
+    return H == 1 or H // group_vec(H, eb, align, True) <= 64
 
 
 def plan_stream(B, T, D, W, H, eb, align, bwd, static):
     if H == 1:
         vec, lpg = 4 // eb, 1
     else:
-        vec = group_vec(H, eb, align)
+        vec = group_vec(H, eb, align, bwd)
         lpg = H // vec
     lpw = (64 // lpg) * lpg if bwd else 64
     span = lpw * vec

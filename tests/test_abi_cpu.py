@@ -70,8 +70,10 @@ def fwd(lib, x=X, xs=(800, 200, 1), w=W_, ws=(800 * 4, 200 * 4, 4, 1), y=Y, ys=(
         (dict(D=200, H=3), INVALID),  # 3 does not divide 200
         # odd H: one bf16 channel per lane, a group of 99 lanes would straddle waves
         (dict(D=198, H=99, xs=(792, 198, 1), ys=(792, 198, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
-        # H = 3 * 128 with 8-byte rows: 4 channels per lane, 96 lanes per group
-        (dict(D=768, H=384, xs=(4 * 768 + 4, 768, 1), ys=(4 * 768 + 4, 768, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
+        # H = 3 * 512: 12 channels per lane, 128 lanes per group
+        (dict(D=3072, H=1536, xs=(4 * 3072, 3072, 1), ys=(4 * 3072, 3072, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
+        # H = 5 * 128 with 8-byte rows: 4 channels per lane, 160 lanes per group
+        (dict(D=1280, H=640, xs=(4 * 1280 + 4, 1280, 1), ys=(4 * 1280 + 4, 1280, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
         (dict(x=P(0)), INVALID),
         (dict(y=P(0)), INVALID),
         (dict(w=P(0)), INVALID),

@@ -95,9 +95,10 @@ def test_large_head_sizes(dtype, H):
 
 
 # Head-wise groups whose size is not a power of two (the head-wise parameterisation takes
-# any H that divides D): odd H (one 16-bit channel per lane), H = 3 * 2^n and 5 * 2^n;
-# groups of 3, 5, 12, 48 and 63 lanes reduce with the suffix scan, and the lanes of a wave
-# past the last whole group stay idle.
+# any H that divides D): odd H (one 16-bit channel per lane) and groups of 5 * 2^k, 63
+# channels reduce with the suffix scan over 3, 5, 10 or 63 lanes, the lanes of a wave past
+# the last whole group idle; 16-bit groups of 3 * 2^k channels (k >= 1) take 6 channels per
+# lane and a power-of-two number of lanes (the butterfly); float32 ones take the scan.
 ODD_H = [
     # dtype, W, H, D
     ("bf16", 4, 3, 198),
@@ -114,6 +115,12 @@ ODD_H = [
     ("bf16", 4, 384, 1536),
     ("bf16", 2, 10, 640),
     ("bf16", 4, 63, 126),
+    # more groups of 3 * 2^k channels: wide filters, the widest group (64 lanes of 6)
+    ("bf16", 8, 12, 1536),
+    ("f16", 6, 96, 2304),
+    ("f32", 4, 12, 1536),
+    ("f32", 3, 192, 1536),
+    ("bf16", 5, 384, 1536),
 ]
 
 

@@ -284,12 +284,13 @@ def test_stream_bwd_bounds(B, T, D, H, eb, align, W, static, want):
 
 
 def test_stream_cases_cover_odd_and_mixed_groups():
-    """The sweep reaches groups of 3, 5, 12 (H = 96 at 8 channels per lane) and 63 lanes,
-    so the suffix-scan reduction and the idle lanes past lanes_in_use are exercised."""
-    lpgs = {kb.plan_stream(B, T, D, 4, H, eb, al, True, False)["lpg"] for B, T, D, H, eb, al in STREAM_CASES}
-    assert {3, 5, 12, 63} <= lpgs
-    assert any(kb.plan_stream(B, T, D, 4, H, eb, al, True, False)["vec"] == 1 and eb == 2
-               for B, T, D, H, eb, al in STREAM_CASES)
+    """The sweep reaches groups of 3, 5 and 63 lanes (suffix scan, idle lanes past
+    lanes_in_use), one 16-bit channel per lane, and 6 channels per lane for 16-bit groups of
+    3 * 2^k channels (power-of-two lanes per group)."""
+    plans = [kb.plan_stream(B, T, D, 4, H, eb, al, True, False) for B, T, D, H, eb, al in STREAM_CASES]
+    assert {3, 5, 63} <= {p["lpg"] for p in plans}
+    assert {1, 6} <= {p["vec"] for p in plans}
+    assert any(p["vec"] == 6 and p["lpg"] > 1 for p in plans)
 
 
 def test_stream_group_check_catches_a_straddling_group():
