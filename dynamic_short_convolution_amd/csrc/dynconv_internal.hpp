@@ -28,18 +28,24 @@ enum class StreamMode {
 // Channels per lane of the head-wise (H > 1) streaming kernels, so that a lane never
 // straddles two groups and a group spans H / VEC consecutive lanes: the largest power of
 // two that divides H and fits the widest lane vector the activations allow (`act_align`
-// bytes), except for groups of 3 * 2^k channels (k >= 1) in 16-bit storage, which take 6
-// channels (12 bytes) per lane in the backward, so that H / VEC is a power of two and the
-// group's dw sums take the butterfly, and in the forward when the power of two would give
-// a lane fewer than 12 bytes. Measured at B8 T4096 D3072 W4 bf16 against the power-of-two
-// layout (3 lanes per group and the scan): backward H = 6 260 -> 149 us, H = 12 184 -> 129,
-// H = 24 139 -> 122, H = 96 142 -> 117; forward H = 6 100 -> 92, H = 12 88 -> 81 (lanes of
-// 12 channels, 24 bytes, were slower in both directions).
+// bytes), except for groups of m * 2^k channels with m = 3 or 5 (k >= 1) in 16-bit storage,
+// which take 2m channels (12 or 20 bytes) per lane in the backward, so that H / VEC is a
+// power of two and the group's dw sums take the butterfly; the forward, which sums
+// nothing, takes 6 channels for m = 3 where the power of two is narrower. Measured at B8
+// T4096 W4 bf16 against the power-of-two layout (groups of 3 or 5 lanes and the scan):
+// backward H = 6 260 -> 149 us, H = 12 184 -> 129, H = 24 139 -> 122, H = 96 142 -> 117
+// (D = 3072), H = 10 234 -> 136 (D = 2560); forward H = 6 100 -> 92, H = 12 88 -> 81. Lanes of
+// 20 or 24 bytes (5 or 6 words: two load instructions per row, each spanning the wave's
+// row with gaps) were slower in the forward than the power of two, even 4-byte lanes.
 constexpr int group_vec(int H, int elem_bytes, int act_align, bool bwd) {
   int v = act_align / elem_bytes;
   while (v > 1 && H % v != 0) v /= 2;
-  const bool three = H % 6 == 0 && ((H / 3) & (H / 3 - 1)) == 0;
-  if (three && elem_bytes == 2 && (bwd || v < 6)) return 6;
+  int m = H;  // the odd part of H
+  while (m % 2 == 0) m /= 2;
+  if (elem_bytes == 2 && (m == 3 || m == 5) && H % (2 * m) == 0) {
+    if (bwd) return 2 * m;
+    if (m == 3 && v < 6) return 6;
+  }
   return v;
 }
 

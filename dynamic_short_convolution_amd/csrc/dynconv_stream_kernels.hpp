@@ -786,8 +786,9 @@ hipError_t dispatch_mode(const StreamParams& p, const StreamPlan& plan, bool st,
     if (plan.vec == 1) return dispatch_static<BWD, ET, W, 1, false>(p, plan, st, s);
   }
   if constexpr (k4 == 2) {
-    // 16-bit groups of 3 * 2^k channels (group_vec)
+    // 16-bit groups of 3 * 2^k and 5 * 2^k channels (group_vec)
     if (plan.vec == 6) return dispatch_static<BWD, ET, W, 6, false>(p, plan, st, s);
+    if (plan.vec == 10) return dispatch_static<BWD, ET, W, 10, false>(p, plan, st, s);
   }
   return dispatch_static<BWD, ET, W, k4, false>(p, plan, st, s);
 }

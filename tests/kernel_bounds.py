@@ -660,13 +660,20 @@ STREAM_WAVES = dict(fwd=8, fwd_group=12, fwd_wide=4, bwd=16, bwd_group=12, bwd_s
 
 def group_vec(H, eb, align, bwd):
     """Channels per lane of a head-wise group: the largest power of two dividing H that fits
-    the lane vector (align bytes), or 6 for 16-bit groups of 3 * 2^k channels (k >= 1) in
-    the backward, and in the forward when the power of two is below 6."""
+    the lane vector (align bytes), or 2m for 16-bit groups of m * 2^k channels (m = 3 or 5,
+    k >= 1) in the backward, and 6 in the forward for m = 3 when the power of two is below 6."""
     v = align // eb
     while v > 1 and H % v:
         v //= 2
-    three = H % 6 == 0 and (H // 3) & (H // 3 - 1) == 0
-    return 6 if (three and eb == 2 and (bwd or v < 6)) else v
+    m = H
+    while m % 2 == 0:
+        m //= 2
+    if eb == 2 and m in (3, 5) and H % (2 * m) == 0:
+        if bwd:
+            return 2 * m
+        if m == 3 and v < 6:
+            return 6
+    return v
 
 
 def stream_layout_ok(D, H, eb, align):

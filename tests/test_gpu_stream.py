@@ -95,10 +95,10 @@ def test_large_head_sizes(dtype, H):
 
 
 # Head-wise groups whose size is not a power of two (the head-wise parameterisation takes
-# any H that divides D): odd H (one 16-bit channel per lane) and groups of 5 * 2^k, 63
-# channels reduce with the suffix scan over 3, 5, 10 or 63 lanes, the lanes of a wave past
-# the last whole group idle; 16-bit groups of 3 * 2^k channels (k >= 1) take 6 channels per
-# lane and a power-of-two number of lanes (the butterfly); float32 ones take the scan.
+# any H that divides D): odd H (one 16-bit channel per lane), 63 channels and float32 groups
+# of 3 * 2^k or 5 * 2^k channels reduce with the suffix scan (groups of 3, 5 or 63 lanes, the
+# lanes of a wave past the last whole group idle); 16-bit groups of 3 * 2^k and 5 * 2^k
+# channels (k >= 1) take 6 or 10 channels per lane and a power-of-two number of lanes.
 ODD_H = [
     # dtype, W, H, D
     ("bf16", 4, 3, 198),
@@ -121,6 +121,12 @@ ODD_H = [
     ("f32", 4, 12, 1536),
     ("f32", 3, 192, 1536),
     ("bf16", 5, 384, 1536),
+    # 16-bit groups of 5 * 2^k channels: 10 channels per lane
+    ("bf16", 4, 10, 1280),
+    ("f16", 3, 20, 1280),
+    ("bf16", 8, 80, 2560),
+    ("bf16", 2, 640, 1280),
+    ("f32", 4, 80, 1280),
 ]
 
 

@@ -238,6 +238,9 @@ STREAM = [
     (1, 20, 2304, 96),
     (1, 17, 1536, 384),
     (2, 25, 126, 63),
+    (1, 40, 1280, 10),
+    (2, 30, 2560, 80),
+    (1, 20, 2560, 640),
 ]
 
 
@@ -285,12 +288,12 @@ def test_stream_bwd_bounds(B, T, D, H, eb, align, W, static, want):
 
 def test_stream_cases_cover_odd_and_mixed_groups():
     """The sweep reaches groups of 3, 5 and 63 lanes (suffix scan, idle lanes past
-    lanes_in_use), one 16-bit channel per lane, and 6 channels per lane for 16-bit groups of
-    3 * 2^k channels (power-of-two lanes per group)."""
+    lanes_in_use), one 16-bit channel per lane, and 6 or 10 channels per lane for 16-bit
+    groups of 3 * 2^k and 5 * 2^k channels (power-of-two lanes per group)."""
     plans = [kb.plan_stream(B, T, D, 4, H, eb, al, True, False) for B, T, D, H, eb, al in STREAM_CASES]
     assert {3, 5, 63} <= {p["lpg"] for p in plans}
-    assert {1, 6} <= {p["vec"] for p in plans}
-    assert any(p["vec"] == 6 and p["lpg"] > 1 for p in plans)
+    assert {1, 6, 10} <= {p["vec"] for p in plans}
+    assert any(p["vec"] == 6 and p["lpg"] > 1 for p in plans) and any(p["vec"] == 10 and p["lpg"] > 1 for p in plans)
 
 
 def test_stream_group_check_catches_a_straddling_group():
