@@ -72,8 +72,11 @@ def fwd(lib, x=X, xs=(800, 200, 1), w=W_, ws=(800 * 4, 200 * 4, 4, 1), y=Y, ys=(
         (dict(D=198, H=99, xs=(792, 198, 1), ys=(792, 198, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
         # H = 3 * 512: 12 channels per lane, 128 lanes per group
         (dict(D=3072, H=1536, xs=(4 * 3072, 3072, 1), ys=(4 * 3072, 3072, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
-        # H = 5 * 128 with 8-byte rows: 4 channels per lane, 160 lanes per group
-        (dict(D=1280, H=640, xs=(4 * 1280 + 4, 1280, 1), ys=(4 * 1280 + 4, 1280, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
+        # H = 5 * 256: 10 channels per lane, 128 lanes per group
+        (dict(D=2560, H=1280, xs=(4 * 2560, 2560, 1), ys=(4 * 2560, 2560, 1), ws=(8 * 4, 2 * 4, 4, 1)), UNSUP),
+        # float32 H = 5 * 64 with 8-byte rows: 2 channels per lane, 160 lanes per group
+        (dict(D=640, H=320, xs=(4 * 640 + 2, 640, 1), ys=(4 * 640 + 2, 640, 1), ws=(8 * 4, 2 * 4, 4, 1), dt=0),
+         UNSUP),
         (dict(x=P(0)), INVALID),
         (dict(y=P(0)), INVALID),
         (dict(w=P(0)), INVALID),
