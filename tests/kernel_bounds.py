@@ -21,6 +21,7 @@ Kernels (dynamic_short_convolution_amd/csrc):
                          loads, including the surplus threads' "safe" chunk)
   k_stream_fwd/_bwd      materialised and static filters: a wave sweeps a run of tokens
                          over lpw lanes of VEC channels (head-wise groups of H / VEC lanes)
+  k_column_partials      column sums of dy (the low-rank form's convolution-bias gradient)
 """
 from __future__ import annotations
 
@@ -854,3 +855,33 @@ def stream_bwd(B, T, D, W, H, eb, align, static=False, want_dx=True, want_dw=Tru
             else:
                 acc.add("partial", 0, chunk, gcol[lead], W)
     return acc, pl
+
+
+# ---------------------------------------------------------------------------------------
+# k_column_partials (launch_column_sums): 256 lanes of one 32-bit word of channels per
+# workgroup, a chunk of tokens each, partial sums per (sequence, chunk)
+# ---------------------------------------------------------------------------------------
+
+def colsum_chunks(B, T, D):
+    per_seq = (2048 + B * ((D + 255) // 256) - 1) // (B * ((D + 255) // 256))
+    most = (T + 63) // 64
+    return 1 if per_seq < 1 else (max(most, 1) if per_seq > most else per_seq)
+
+
+def column_partials(B, T, D, eb):
+    nchunk = colsum_chunks(B, T, D)
+    L = (T + nchunk - 1) // nchunk
+    V = 4 // eb
+    nDb = (D + 256 * V - 1) // (256 * V)
+    acc = Accesses()
+    lane = np.arange(256)
+    for bid in range(B * nchunk * nDb):
+        db, chunk = bid % nDb, bid // nDb
+        b, tc = chunk // nchunk, chunk % nchunk
+        c = (db * 256 + lane) * V
+        c = c[c < D]
+        t0, t1 = tc * L, min(T, tc * L + L)
+        if t1 > t0:
+            acc.add("dy", b, np.arange(t0, t1)[:, None], c[None, :], V)
+        acc.add("part", 0, chunk, c, V)
+    return acc, nchunk

@@ -310,6 +310,19 @@ def test_stream_group_check_catches_a_straddling_group():
 
 
 # ---------------------------------------------------------------------------------------
+# column sums of dy (the low-rank form's convolution-bias gradient)
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,D", [(1, 1, 2), (2, 5, 200), (1, 300, 1024), (8, 4096, 2048), (3, 3000, 192),
+                                   (1000, 37, 64)])
+@pytest.mark.parametrize("eb", [2, 4])
+def test_column_partials_bounds(B, T, D, eb):
+    acc, nchunk = kb.column_partials(B, T, D, eb)
+    acc.check({"dy": (B, T, D), "part": (1, B * nchunk, D)})
+    _full(acc, "dy", B, T, D)
+    _full(acc, "part", 1, B * nchunk, D)
+
+
+# ---------------------------------------------------------------------------------------
 # 32-bit offsets at the largest row strides the ABI admits
 # ---------------------------------------------------------------------------------------
 BIG = kb.MAX_ROW_STRIDE - 64  # a multiple of 16 bytes for every dtype
