@@ -436,6 +436,13 @@ def test_bindings_reject_mismatched_shapes_and_dtypes():
         dynconv_decode_step(x[:, 0], w1[:, 0], None, 0)
     with pytest.raises(ValueError, match="z must be"):
         dynconv_lowrank_decode_step(x[:, 0], z, U, b, torch.zeros((B, W - 1, D), dtype=bf), 0, W)
+    with pytest.raises(ValueError, match="conv_bias must be"):
+        dynconv_lowrank_fwd(x, z, U, b, W, conv_bias=torch.zeros((D // 2,), dtype=bf))
+    with pytest.raises(ValueError, match="conv_bias must be"):
+        dynconv_lowrank_fwd(x, z, U, b, W, conv_bias=torch.zeros((D,), dtype=torch.float32))
+    with pytest.raises(ValueError, match="conv_bias must be"):
+        dynconv_lowrank_decode_step(x[:, 0], z[:, 0], U, b, torch.zeros((B, W - 1, D), dtype=bf), 0, W,
+                                    conv_bias=torch.zeros((2 * D,), dtype=bf)[::2])
 
 
 def test_noalloc_validation(lib):
