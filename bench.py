@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak, published
+MFMA_F32_PEAK_TFLOPS = 157.3  # dense float32 matrix-core peak
 METRIC = "dyn-conv fwd+bwd achieved HBM GB/s (% of peak), B8·T4096·D2048·W4"
 HEADLINE = dict(B=8, T=4096, D=2048, W=4, H=1)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -247,6 +248,8 @@ ROWS = (
     "lowrank_r52_bwd",
     "lowrank_w5_r64_fwd",
     "lowrank_w5_r64_bwd",
+    "lowrank_r64_f32_fwd",
+    "lowrank_r64_f32_bwd",
     "gemm_conv_qkv_fwd",
     "gemm_lowrank_qkv_fwd",
     "reference_unfused_gemm_conv_qkv_fwd",
@@ -356,14 +359,15 @@ def make_row(name, device):
         W = int(re.search(r"_w(\d+)_", name).group(1)) if "_w" in name else 4
         R = int(re.search(r"_r(\d+)", name).group(1))
         H = 4 if name.startswith("lowrank_h4") else 1
-        dt = torch.float16 if "_f16_" in name else torch.bfloat16
+        dt = torch.float16 if "_f16_" in name else torch.float32 if "_f32_" in name else torch.bfloat16
         J = (D // H) * W
         x = gen((B, T, D), 1.0, 4, "x", device).to(dt)
         z = gen((B, T, R), 1.0, 4, "z", device).to(dt)
         U = gen((R, J), 0.1 / R**0.5, 4, "U", device).to(dt)
         b = gen((J,), 0.1**0.5, 4, "b", device).to(dt)
-        desc = tag(f"B{B} T{T} D{D} W{W} R{R}{f' H{H}' if H > 1 else ''} {'f16' if dt == torch.float16 else 'bf16'}",
-                   B, T)
+        dname = {torch.float16: "f16", torch.float32: "f32"}.get(dt, "bf16")
+        eb = 4 if dt == torch.float32 else 2
+        desc = tag(f"B{B} T{T} D{D} W{W} R{R}{f' H{H}' if H > 1 else ''} {dname}", B, T)
         seq = segs(B, T)
         sb = 4 * B * T if packed else 0
         cb = gen((D,), 0.5, 4, "c", device).to(dt) if cbias else None
@@ -372,12 +376,12 @@ def make_row(name, device):
         if name.endswith("fwd"):
             y = torch.empty_like(x)
             return (lambda: dynconv_lowrank_fwd(x, z, U, b, W, H, out=y, seq_idx=seq, conv_bias=cb)), \
-                lowrank_bytes(B, T, D, W, R, H=H) + sb + (2 * D if cbias else 0), lowrank_flops(B, T, D, W, R, H=H), desc
+                lowrank_bytes(B, T, D, W, R, eb=eb, H=H) + sb + (2 * D if cbias else 0), lowrank_flops(B, T, D, W, R, H=H), desc
         dy = gen((B, T, D), 1.0, 4, "dy", device).to(dt)
         ws = torch.empty(dynconv_lowrank_bwd_workspace_size(B, T, D, W, H, R, dt, want_dconv_bias=cbias),
                          dtype=torch.uint8, device=device)
         return (lambda: dynconv_lowrank_bwd(x, z, U, b, dy, W, H, workspace=ws, seq_idx=seq, want_dconv_bias=cbias)), \
-            lowrank_bytes(B, T, D, W, R, fwd=False, H=H) + sb + (4 * D if cbias else 0), \
+            lowrank_bytes(B, T, D, W, R, eb=eb, fwd=False, H=H) + sb + (4 * D if cbias else 0), \
             lowrank_flops(B, T, D, W, R, fwd=False, H=H), desc
     if name.startswith("qkv"):
         B, T, D, W, H = 4, 8192, 3072, 4, 1
@@ -425,7 +429,10 @@ def time_rows(args, device, names, flush):
             tf = flops / (med * 1e-3) / 1e12
             r["flops"] = flops
             r["tflops"] = round(tf, 1)
-            r["pct_mfma_bf16_peak"] = round(100.0 * tf / MFMA_BF16_PEAK_TFLOPS, 1)
+            if "_f32_" in name:  # float32 operands run on the float32 matrix cores
+                r["pct_mfma_f32_peak"] = round(100.0 * tf / MFMA_F32_PEAK_TFLOPS, 1)
+            else:
+                r["pct_mfma_bf16_peak"] = round(100.0 * tf / MFMA_BF16_PEAK_TFLOPS, 1)
         out[name] = r
         log(f"{name}: {r['median_us']} us, {r['gbs']} GB/s")
         del fn
