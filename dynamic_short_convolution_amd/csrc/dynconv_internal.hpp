@@ -37,6 +37,9 @@ enum class StreamMode {
 // (D = 3072), H = 10 234 -> 136 (D = 2560); forward H = 6 100 -> 92, H = 12 88 -> 81. Lanes of
 // 20 or 24 bytes (5 or 6 words: two load instructions per row, each spanning the wave's
 // row with gaps) were slower in the forward than the power of two, even 4-byte lanes.
+// Groups of exactly 3 or 5 channels in 16-bit storage take one whole group per lane (16-bit
+// loads) instead of one channel per lane and the scan: H = 3 forward / backward 169 / 430
+// -> 144 / 271 us (D = 3072), H = 5 152 / 420 -> 105 / 163 us (D = 2560).
 constexpr int group_vec(int H, int elem_bytes, int act_align, bool bwd) {
   int v = act_align / elem_bytes;
   while (v > 1 && H % v != 0) v /= 2;
@@ -46,6 +49,7 @@ constexpr int group_vec(int H, int elem_bytes, int act_align, bool bwd) {
     if (bwd) return 2 * m;
     if (m == 3 && v < 6) return 6;
   }
+  if (elem_bytes == 2 && (m == 3 || m == 5) && H == m) return m;  // one group per lane (16-bit loads)
   return v;
 }
 

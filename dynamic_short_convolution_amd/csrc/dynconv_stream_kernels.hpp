@@ -789,6 +789,9 @@ hipError_t dispatch_mode(const StreamParams& p, const StreamPlan& plan, bool st,
     // 16-bit groups of 3 * 2^k and 5 * 2^k channels (group_vec)
     if (plan.vec == 6) return dispatch_static<BWD, ET, W, 6, false>(p, plan, st, s);
     if (plan.vec == 10) return dispatch_static<BWD, ET, W, 10, false>(p, plan, st, s);
+    // odd groups of 3 or 5 channels, one group per lane
+    if (plan.vec == 3) return dispatch_static<BWD, ET, W, 3, false>(p, plan, st, s);
+    if (plan.vec == 5) return dispatch_static<BWD, ET, W, 5, false>(p, plan, st, s);
   }
   return dispatch_static<BWD, ET, W, k4, false>(p, plan, st, s);
 }

@@ -35,13 +35,13 @@
  * - Validation happens before any HIP call; invalid input returns a status, never aborts.
  *   B == 0 or T == 0 or D == 0 is a no-op returning DYNCONV_OK.
  * - Supported parameters: 1 <= W <= 8 (low-rank form: W <= 5); H any divisor of D, with
- *   H / VEC <= 64 for the materialised and static forms, where VEC (channels per lane) is 2m
- *   for 16-bit storage when H = m * 2^k with m = 3 or 5 and k >= 1, and otherwise the largest
- *   power of two that divides H and is at most the widest lane vector allowed by the
- *   alignment below / element size (so with 16-byte aligned activations: powers of two up
- *   to 512 in 16-bit storage and 256 in float32; H = 3 * 2^k up to 384 and H = 5 * 2^k up to
- *   640 in 16-bit storage, 192 and 160 in float32; odd H up to 64); low-rank form:
- *   1 <= R <= 128.
+ *   H / VEC <= 64 for the materialised and static forms, where VEC (channels per lane) is,
+ *   in 16-bit storage, 2m when H = m * 2^k with m = 3 or 5 and k >= 1 and H itself when H is
+ *   3 or 5, and otherwise the largest power of two that divides H and is at most the widest
+ *   lane vector allowed by the alignment below / element size (so with 16-byte aligned
+ *   activations: powers of two up to 512 in 16-bit storage and 256 in float32; H = 3 * 2^k up
+ *   to 384 and H = 5 * 2^k up to 640 in 16-bit storage, 192 and 160 in float32; other odd H
+ *   up to 63); low-rank form: 1 <= R <= 128.
  * - Alignment: base pointers of activation-shaped tensors and their s[0], s[1] (in bytes)
  *   must be multiples of 4 bytes (bf16: D even); wider lane vectors (8 or 16 bytes) are
  *   used when every activation-shaped tensor of the call allows them. Filters: base and

@@ -674,6 +674,8 @@ def group_vec(H, eb, align, bwd):
             return 2 * m
         if m == 3 and v < 6:
             return 6
+    if eb == 2 and m in (3, 5) and H == m:
+        return m
     return v
 
 

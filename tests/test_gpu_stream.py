@@ -95,10 +95,11 @@ def test_large_head_sizes(dtype, H):
 
 
 # Head-wise groups whose size is not a power of two (the head-wise parameterisation takes
-# any H that divides D): odd H (one 16-bit channel per lane), 63 channels and float32 groups
-# of 3 * 2^k or 5 * 2^k channels reduce with the suffix scan (groups of 3, 5 or 63 lanes, the
-# lanes of a wave past the last whole group idle); 16-bit groups of 3 * 2^k and 5 * 2^k
-# channels (k >= 1) take 6 or 10 channels per lane and a power-of-two number of lanes.
+# any H that divides D): odd H other than 3 and 5 in 16-bit storage (one channel per lane),
+# 63 channels and float32 groups of 3 * 2^k or 5 * 2^k channels reduce with the suffix scan
+# (the lanes of a wave past the last whole group idle); 16-bit groups of 3 * 2^k and 5 * 2^k
+# channels take 6 or 10 channels per lane and a power-of-two number of lanes, and the 16-bit
+# backward puts a whole group of 3 or 5 channels on a lane.
 ODD_H = [
     # dtype, W, H, D
     ("bf16", 4, 3, 198),
@@ -121,6 +122,11 @@ ODD_H = [
     ("f32", 4, 12, 1536),
     ("f32", 3, 192, 1536),
     ("bf16", 5, 384, 1536),
+    # odd groups: 3 or 5 channels per lane in the 16-bit backward, 7 with the scan
+    ("f16", 8, 3, 198),
+    ("bf16", 5, 5, 390),
+    ("bf16", 4, 7, 196),
+    ("f16", 2, 7, 196),
     # 16-bit groups of 5 * 2^k channels: 10 channels per lane
     ("bf16", 4, 10, 1280),
     ("f16", 3, 20, 1280),

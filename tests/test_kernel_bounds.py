@@ -297,10 +297,11 @@ def test_stream_cases_cover_odd_and_mixed_groups():
 
 
 def test_stream_group_check_catches_a_straddling_group():
-    """A wave slice of all 64 lanes with groups of 3 lanes would split a group between two
+    """A wave slice of all 64 lanes with groups of 7 lanes would split a group between two
     waves: the group check must see it."""
-    B, T, D, H, eb, align = 1, 8, 198, 3, 2, 4
+    B, T, D, H, eb, align = 1, 8, 196, 7, 2, 4
     pl = kb.plan_stream(B, T, D, 4, H, eb, align, True, False)
+    assert pl["lpg"] == 7 and pl["lpw"] == 63
     bad = dict(pl, lpw=64, nDw=(D + 63) // 64)
     lane = np.arange(64)
     c0 = lane * bad["vec"] + 64 * bad["vec"]  # the second slice
