@@ -16,7 +16,7 @@ sample (cpu_baseline).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
 Prints ONE JSON line. `--rows a,b,...` times only the named rows (the same timing, no
 headline, no CPU baseline): names from ROWS, or head-wise rows headwise_h<N>_{fwd,bwd} for
-any group size N that divides 2048, 3072 or 2560 (D is the first of those it divides).
+any group size N that divides 2048, 3072, 2560 or 3584 (D is the first of those it divides).
 """
 from __future__ import annotations
 
@@ -389,10 +389,10 @@ def make_row(name, device):
         B, T, D = 8, 4096, 2048
         W = int(name.split("_")[1][1:]) if name.startswith("static") else 8 if name.startswith("perchannel_w8") else 4
         H = int(name.split("_")[1][1:]) if name.startswith("headwise") else 1
-        if D % H:  # groups whose size is not a power of two: D = 3072 (H = 12: 256 groups) or 2560
-            D = next((d for d in (3072, 2560) if d % H == 0), None)
+        if D % H:  # groups whose size is not a power of two: D = 3072 (H = 12: 256 groups), 2560, 3584
+            D = next((d for d in (3072, 2560, 3584) if d % H == 0), None)
             if D is None:
-                raise ValueError(f"{name}: no row width here for groups of {H} channels (2048, 3072 or 2560)")
+                raise ValueError(f"{name}: no row width here for groups of {H} channels (2048, 3072, 2560, 3584)")
     static = name.startswith("static")
     x = gen((B, T, D), 1.0, 2, "x", device)
     w = gen((D // H, W) if static else (B, T, D // H, W), (1.0 / W) ** 0.5, 2, "w", device)
