@@ -248,6 +248,10 @@ ROWS = (
     "lowrank_r52_bwd",
     "lowrank_w5_r64_fwd",
     "lowrank_w5_r64_bwd",
+    "lowrank_w6_r64_fwd",
+    "lowrank_w6_r64_bwd",
+    "lowrank_w8_r64_fwd",
+    "lowrank_w8_r64_bwd",
     "lowrank_r64_f32_fwd",
     "lowrank_r64_f32_bwd",
     "gemm_conv_qkv_fwd",
@@ -351,8 +355,9 @@ def make_row(name, device):
     if name.startswith("lowrank"):
         # lowrank_h4_*: head-wise generation, U of R x (D/4)*W; *_f16_*: float16 storage;
         # lowrank_rN_*: rank N (the pages' models use 16..52; 20 and 52 are zero-padded on
-        # the fast kernels, their contiguous z rows staged in 4-byte pieces); lowrank_w5_*:
-        # five taps (the widest low-rank filter of the pages' ablation that the ABI takes)
+        # the fast kernels, their contiguous z rows staged in 4-byte pieces); lowrank_wN_*:
+        # N taps (5 on the fast kernels; 6, the widest of the pages' ablation, and 8 on the
+        # general ones)
         import re
 
         B, T, D = 8, 4096, 2048

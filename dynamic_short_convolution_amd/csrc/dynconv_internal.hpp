@@ -11,7 +11,7 @@ namespace dynconv {
 
 constexpr int kWaveSize = 64;
 constexpr int kMaxW = 8;         // widest filter (materialised, static and head-wise forms, decoding)
-constexpr int kMaxLowrankW = 5;  // widest filter of the low-rank form (its kernels keep a 4-token halo)
+constexpr int kMaxLowrankW = 8;  // widest filter of the low-rank form (W > 5: the general kernels)
 // Row strides (x, z, dy, y / dx) and U's row stride of the low-rank form stay below this many
 // elements: its kernels form the offsets of up to 128 rows (a step of 64 tokens with its halo,
 // or the rank rows of U) in 32-bit arithmetic.

@@ -47,8 +47,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TT = kLowrankTT;  // tokens per tile (the N, or K, extent of one MFMA)
-constexpr int HALO = 4;   // W - 1 for the widest filter (W = 5)
-constexpr int RING = TT + HALO;
+// Rows staged before a token range or step: the W - 1 earlier tokens a filter reaches (at
+// least 4, so that the tilings of W <= 5 stay as they are).
+constexpr int lr_halo(int W) { return W <= 5 ? 4 : W - 1; }
 
 // Raw storage of an element in LDS / fragments: bf16 bits or float32.
 template <typename ET>
@@ -170,6 +171,7 @@ __device__ __forceinline__ LrBlock lr_block(const LowRankParams& p) {
 }
 
 // Slot of token t in the x ring of one workgroup (tokens t_first - HALO .. kept).
+template <int HALO, int RING>
 __device__ __forceinline__ int ring_slot(int t, int t_first) { return (t - t_first + HALO) % RING; }
 
 // ---------------------------------------------------------------------------------
@@ -354,6 +356,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
   constexpr int XCH = (TT * DC / CE + kBlockThreads - 1) / kBlockThreads;  // x chunks per thread
   constexpr int ZCH = (TT * RP / CE + kBlockThreads - 1) / kBlockThreads;  // z chunks per thread
   static_assert(DC % CE == 0 && RP % CE == 0, "tiles hold whole 16-byte chunks");
+  constexpr int HALO = lr_halo(W);
+  constexpr int RING = TT + HALO;
   __shared__ __align__(16) RT zl[TT * ZP];
   __shared__ __align__(16) ET xl[RING * XP];
   __shared__ int sl[RING];  // segment ids of the ring's tokens (packed sequences)
@@ -450,10 +454,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
       const int ck = tid + i * kBlockThreads;
       if (ck < TT * DC / CE) {
         const int row = ck / (DC / CE);
-        *reinterpret_cast<u32x4*>(&xl[ring_slot(t0 + row, t_first) * XP + (ck % (DC / CE)) * CE]) = xpre[i];
+        *reinterpret_cast<u32x4*>(&xl[ring_slot<HALO, RING>(t0 + row, t_first) * XP + (ck % (DC / CE)) * CE]) = xpre[i];
       }
     }
-    if (segs && tid < TT) sl[ring_slot(t0 + tid, t_first)] = spre;
+    if (segs && tid < TT) sl[ring_slot<HALO, RING>(t0 + tid, t_first)] = spre;
   };
 
   // halo: the HALO tokens before the range
@@ -463,11 +467,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
     const int t = t_first - HALO + row;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (t >= 0) v = load_chunk<ET>(x + int64_t(t) * p.xs1 + c_base, c, p.D - c_base, act16);
-    *reinterpret_cast<u32x4*>(&xl[ring_slot(t, t_first) * XP + c]) = v;
+    *reinterpret_cast<u32x4*>(&xl[ring_slot<HALO, RING>(t, t_first) * XP + c]) = v;
   }
   if (segs && tid < HALO) {
     const int t = t_first - HALO + tid;
-    sl[ring_slot(t, t_first)] = t >= 0 ? sgp[int64_t(t) * p.ss1] : INT32_MIN;
+    sl[ring_slot<HALO, RING>(t, t_first)] = t >= 0 ? sgp[int64_t(t) * p.ss1] : INT32_MIN;
   }
   prefetch(zpre_s[0], xpre_s[0], t_first);
   commit(zpre_s[0], xpre_s[0], t_first);
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
     }
     // conv + residual for token t0 + n, channels cw0 + lane_c .. + MT - 1
     const int t = t0 + n;
-    const int sc = segs ? sl[ring_slot(t, t_first)] : 0;
+    const int sc = segs ? sl[ring_slot<HALO, RING>(t, t_first)] : 0;
     float sum[MT], xcur[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -515,9 +519,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_lowrank_fwd(const LowRankPara
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tap = 4 * (q % LPC) + i;
-      if (tap < W && (!segs || sl[ring_slot(t - tap, t_first)] == sc)) {
+      if (tap < W && (!segs || sl[ring_slot<HALO, RING>(t - tap, t_first)] == sc)) {
         float xv[MT];
-        lds_read_run<ET, MT>(&xl[ring_slot(t - tap, t_first) * XP + wv * CPW + lane_c], xv);
+        lds_read_run<ET, MT>(&xl[ring_slot<HALO, RING>(t - tap, t_first) * XP + wv * CPW + lane_c], xv);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           sum[mt] = fmaf(acc[mt][i], xv[mt], sum[mt]);
@@ -598,6 +602,9 @@ __device__ __forceinline__ u32x4 stage16(const ET* base, int off, bool ok, int l
 __device__ __forceinline__ u32x4 keep_if(const u32x4& v, uint32_t okmask, int bit) {
   return ((okmask >> bit) & 1u) ? v : u32x4{0u, 0u, 0u, 0u};
 }
+__device__ __forceinline__ u32x4 keep_if(const u32x4& v, uint64_t okmask, int bit) {
+  return ((okmask >> bit) & 1u) ? v : u32x4{0u, 0u, 0u, 0u};
+}
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -645,6 +652,7 @@ struct LrBwdShape {
   static constexpr int RP = 32 * KS;
   static constexpr int CE = 16 / EB;
   static constexpr int S = kLowrankBwdStep;  // tokens per pipeline step
+  static constexpr int HALO = lr_halo(W);
   static constexpr int XR = S + HALO;        // rows of a step's x / dy tile
   static constexpr int ZP = RP + CE;         // z row pitch (elements)
   static constexpr int XP = DC + CE;
@@ -673,7 +681,7 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
   using R_ = Raw<ET>;
   constexpr int EB = Sh::EB, MT = Sh::MT, WP = Sh::WP, LPC = Sh::LPC, CPW = Sh::CPW, DC = Sh::DC;
   constexpr int RP = Sh::RP, CE = Sh::CE, S = Sh::S, XR = Sh::XR, ZP = Sh::ZP, XP = Sh::XP;
-  constexpr int GC = Sh::GC, GP = Sh::GP, ZB = Sh::ZB;
+  constexpr int GC = Sh::GC, GP = Sh::GP, ZB = Sh::ZB, HALO = Sh::HALO;
   constexpr int NSUB = S / TT;
   constexpr int RTN = RP / 16;        // r tiles of dU
   constexpr int JTN = GC / 16;        // column tiles of dU
@@ -943,10 +951,15 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
             if constexpr (W > 2) acc += shift_lanes<(W > 2 ? W - 3 : 0)>(P[mt][2], Pprev[mt][2]);
             if constexpr (W > 3) acc += shift_lanes<(W > 3 ? W - 4 : 0)>(P[mt][3], Pprev[mt][3]);
           } else {
-            // even groups hold taps 0..3 (later by 4..1 tokens), odd groups tap 4 (same token)
-            const float even = shift_lanes<4>(P[mt][0], Pprev[mt][0]) + shift_lanes<3>(P[mt][1], Pprev[mt][1]) +
-                               shift_lanes<2>(P[mt][2], Pprev[mt][2]) + shift_lanes<1>(P[mt][3], Pprev[mt][3]);
-            const float mine = (q & 1) ? P[mt][0] : even;
+            // even groups hold taps 0..3 (from W-1..W-4 tokens back), odd groups taps
+            // 4..W-1 (from W-5..0 tokens back)
+            const float even = shift_lanes<W - 1>(P[mt][0], Pprev[mt][0]) + shift_lanes<W - 2>(P[mt][1], Pprev[mt][1]) +
+                               shift_lanes<W - 3>(P[mt][2], Pprev[mt][2]) + shift_lanes<W - 4>(P[mt][3], Pprev[mt][3]);
+            float odd = shift_lanes<(W > 4 ? W - 5 : 0)>(P[mt][0], Pprev[mt][0]);
+            if constexpr (W > 5) odd += shift_lanes<(W > 5 ? W - 6 : 0)>(P[mt][1], Pprev[mt][1]);
+            if constexpr (W > 6) odd += shift_lanes<(W > 6 ? W - 7 : 0)>(P[mt][2], Pprev[mt][2]);
+            if constexpr (W > 7) odd += shift_lanes<(W > 7 ? W - 8 : 0)>(P[mt][3], Pprev[mt][3]);
+            const float mine = (q & 1) ? odd : even;
             acc = mine + __shfl_xor(mine, 16, 64);
           }
           dxs[mt] = acc;
@@ -976,8 +989,8 @@ __device__ __forceinline__ void lowrank_bwd_body(const LowRankParams& p, LrBwdSm
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tap = 4 * (q % LPC) + i;
-          // odd lane groups of a W = 5 filter hold tap 4 only: read a valid row (tap 0)
-          // for the others and zero the result
+          // padded taps (tap >= W) of the odd lane groups read a valid row (tap 0) and
+          // zero the result
           const int rtap = tap < W ? tap : 0;
           float xr[MT] = {};
           if (LPC == 2 || tap < W) lds_read_run<ET, MT>(xt + (sub * TT - rtap) * XP, xr);
@@ -1094,6 +1107,7 @@ struct LrDzShape {
   static constexpr int CE = 16 / EB;
   static constexpr int UP = UC + CE;         // U row pitch (elements)
   static constexpr int TB = kLowrankDzTokens;
+  static constexpr int HALO = lr_halo(W);
   static constexpr int XR = TB + HALO;
   static constexpr int XP = CH + CE;
   static constexpr int STAGE = (RP * UP + XR * XP + TB * XP) * EB;
@@ -1113,7 +1127,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
   using Sh = LrDzShape<ET, W, KS>;
   using RT = typename Raw<ET>::type;
   constexpr int EB = Sh::EB, RP = Sh::RP, CH = Sh::CH, UC = Sh::UC, CE = Sh::CE, UP = Sh::UP;
-  constexpr int TB = Sh::TB, XR = Sh::XR, XP = Sh::XP, NBUF = Sh::NBUF;
+  constexpr int TB = Sh::TB, XR = Sh::XR, XP = Sh::XP, NBUF = Sh::NBUF, HALO = Sh::HALO;
   constexpr int RTN = RP / 16;
   constexpr int CR = CH / 4;          // channels of a lane group
   constexpr int RUN = CR * W;         // columns of a lane group
@@ -1145,16 +1159,18 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
   const ET* dysafe = static_cast<const ET*>(p.dy);
   const int nchunk = (p.D + CH - 1) / CH;
 
+  // bit i: u[i]; bit US + i: a[i] (64 bits for float32 U at W >= 7 with 128 ranks)
+  using Mask = typename std::conditional<(US + AS <= 32), uint32_t, uint64_t>::type;
   struct Stage {
     u32x4 u[US], a[AS];
-    uint32_t ok;  // bit i: u[i]; bit US + i: a[i]
+    Mask ok;
   };
-  static_assert(US + AS <= 32, "valid bits");
+  static_assert(US + AS <= 64, "valid bits");
   auto prefetch = [&](Stage& st, int c0) {
     const int climit = p.D - c0;
     const int jlimit = climit * W;  // filter columns (channel, tap) of the chunk inside D
     const ET* ub = U + int64_t(c0) * W;
-    uint32_t okm = 0;
+    Mask okm = 0;
 #pragma unroll
     for (int i = 0; i < US; ++i) {
       const int ck = tid + i * kBlockThreads;
@@ -1166,7 +1182,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
         // head-wise: column (c0 + cc) / H * W + k of U for the chunk's column cc * W + k
         st.u[i] = ok ? load_group_cols<ET>(U + int64_t(r) * p.ldu, c0, c, jlimit - c, W, p.H) : u32x4{0u, 0u, 0u, 0u};
       }
-      okm |= uint32_t(ok) << i;
+      okm |= Mask(ok) << i;
     }
 #pragma unroll
     for (int i = 0; i < AS; ++i) {
@@ -1179,7 +1195,7 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
       const bool ok = (isx || k2 < DCH) && t >= 0 && t < p.T && c < climit;
       st.a[i] = stage16<false, ET>(isx ? x + c0 : dy + c0, row * int(isx ? p.xs1 : p.dys1) + c, ok, climit - c,
                                   isx ? xsafe : dysafe);
-      okm |= uint32_t(ok) << (US + i);
+      okm |= Mask(ok) << (US + i);
     }
     st.ok = okm;
   };
@@ -1371,6 +1387,7 @@ struct LdsPlace {
 template <int W, int KS, int HG>
 struct LrDzDma {
   static_assert(HG == 1 || HG == 2 || HG == 4 || HG == 8 || HG == 16, "group size of the DMA dz path");
+  static constexpr int HALO = lr_halo(W);
   static constexpr int RP = 32 * KS;
   static constexpr int GL = HG <= 4 ? 8 : 32 / HG;  // filter groups of a lane
   static constexpr int RUNS = GL * HG / 8;          // 16-byte runs of a lane's row
@@ -1414,7 +1431,7 @@ __device__ __forceinline__ void vm_wait_barrier() {
 template <typename ET, int W, int KS, int HG>
 __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned char* smem, int b, int tb0) {
   using D = LrDzDma<W, KS, HG>;
-  constexpr int RP = D::RP, CH = D::CH, UC = D::UC, UCPR = D::UCPR, XCPR = D::XCPR;
+  constexpr int RP = D::RP, CH = D::CH, UC = D::UC, UCPR = D::UCPR, XCPR = D::XCPR, HALO = D::HALO;
   constexpr int RTN = RP / 16;
   constexpr int GL = D::GL, RUNS = D::RUNS;
   constexpr int KST = GL * W / 8;  // K steps per chunk: the lane's GL * W columns / 8
@@ -1596,7 +1613,8 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 // stages fit.
 template <typename ET, int W, int KS, int HG>
 constexpr bool lowrank_dz_dma_ok() {
-  return (std::is_same<ET, bf16_t>::value || std::is_same<ET, f16_t>::value) && LrDzDma<W, KS, HG>::SHAPE_OK && LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
+  return (std::is_same<ET, bf16_t>::value || std::is_same<ET, f16_t>::value) && W <= 5 && LrDzDma<W, KS, HG>::SHAPE_OK &&
+         LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
 }
 
 // The register-staged path: any storage type, ragged token blocks, unaligned rows, any
@@ -1723,6 +1741,9 @@ hipError_t lr_dispatch_w(const LowRankParams& p, const LowRankPlan& pl, int W, h
     case 3: return lr_dispatch_ks<BWD, ET, 3>(p, pl, s);
     case 4: return lr_dispatch_ks<BWD, ET, 4>(p, pl, s);
     case 5: return lr_dispatch_ks<BWD, ET, 5>(p, pl, s);
+    case 6: return lr_dispatch_ks<BWD, ET, 6>(p, pl, s);
+    case 7: return lr_dispatch_ks<BWD, ET, 7>(p, pl, s);
+    case 8: return lr_dispatch_ks<BWD, ET, 8>(p, pl, s);
     default: return hipErrorInvalidValue;
   }
 }

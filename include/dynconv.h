@@ -34,7 +34,7 @@
  *   The fast low-rank kernels serve bfloat16 and float16; float32 takes the general ones.
  * - Validation happens before any HIP call; invalid input returns a status, never aborts.
  *   B == 0 or T == 0 or D == 0 is a no-op returning DYNCONV_OK.
- * - Supported parameters: 1 <= W <= 8 (low-rank form: W <= 5); H any divisor of D, with
+ * - Supported parameters: 1 <= W <= 8; H any divisor of D, with
  *   H / VEC <= 64 for the materialised and static forms, where VEC (channels per lane) is,
  *   in 16-bit storage, 2m when H = m * 2^k with m = 3 or 5 and k >= 1 and H itself when H is
  *   3 or 5, and otherwise the largest power of two that divides H and is at most the widest
@@ -186,7 +186,7 @@ dynconv_status dynconv_decode_step(const void* x, const int64_t* xs, const void*
  * Low-rank decoding step: the filters of the new token, w[b,g,k] = sum_r z[b,r] U[r, g*W+k]
  * + bias[g*W+k], are formed on the GPU (float32) and applied as in dynconv_decode_step.
  *   z  [B, R] with strides zs[0..1] (zs[1] == 1); U, ldu, bias as in dynconv_lowrank_fwd.
- * 1 <= R <= 128, W <= 5.
+ * 1 <= R <= 128, W <= 8.
  */
 dynconv_status dynconv_lowrank_decode_step(const void* x, const int64_t* xs, const void* z, const int64_t* zs,
                                            const void* U, int64_t ldu, const void* bias, void* cache,

@@ -32,7 +32,13 @@ import numpy as np
 
 STEP = 64  # tokens per pipeline step (fast kernels, general backward, dz blocks)
 TT = 16  # tokens per tile of the general forward
-HALO = 4  # rows before a range that the general kernels stage (W - 1 for W = 5)
+
+
+def lr_halo(W):
+    """Rows before a range that the general low-rank kernels stage (lr_halo)."""
+    return 4 if W <= 5 else W - 1
+
+
 I32 = 1 << 31
 U32 = 1 << 32
 MAX_ROW_STRIDE = 1 << 24  # the ABI's bound on the low-rank form's row strides
@@ -416,18 +422,19 @@ def dz_dma_shape(W, KS, HG, stages=DZ_STAGES):
     CHC, UC = CH * HG, CH * W
     RP = 32 * KS
     UCPR, XCPR = UC // 8, CHC // 8
-    XR = STEP + HALO
+    XR = STEP + lr_halo(W)
     UCH, XCH, DCH = RP * UCPR, XR * XCPR, STEP * XCPR
     ni = lambda n: (n + 63) // 64  # noqa: E731
     stage = (ni(UCH) + ni(XCH) + ni(DCH)) * 64 * 16
-    ok = (GL * W) % 8 == 0 and stages * stage <= 150 * 1024
+    ok = W <= 5 and (GL * W) % 8 == 0 and stages * stage <= 150 * 1024
     return dict(GL=GL, CH=CH, CHC=CHC, UC=UC, UCPR=UCPR, XCPR=XCPR, XR=XR, UCH=UCH, XCH=XCH, DCH=DCH, ok=ok)
 
 
 def dz_dma(B, T, D, W, H, R, xs1, dys1, ldu):
     KS = (R + 31) // 32
     S = dz_dma_shape(W, KS, H)
-    assert S["ok"] and D % S["CHC"] == 0
+    assert S["ok"] and D % S["CHC"] == 0 and W <= 5
+    HALO = lr_halo(W)
     nchunk = D // S["CHC"]
     acc = Accesses()
     pidx = np.arange(S["UCH"])
@@ -485,6 +492,7 @@ def lowrank_fwd_general(B, T, D, W, H, R, eb, act16, z16, seg=False, has_bias=Tr
     RP = 32 * KS
     WP = 8 if W > 4 else 4
     CPW = MT * 4 // (WP // 4)
+    HALO = lr_halo(W)
     acc = Accesses()
     zck = np.arange(TT * RP // CE)
     zrow, zc = zck // (RP // CE), (zck % (RP // CE)) * CE
@@ -551,6 +559,7 @@ def lowrank_bwd_general(B, T, D, W, H, R, eb, fast, seg=False, has_bias=True, wa
     ZCH, XCH = S * RP // CE, S * DC // CE
     NT = 256
     ZS, XS = (ZCH + NT - 1) // NT, (XCH + NT - 1) // NT
+    HALO = lr_halo(W)
     HCH = HALO * DC // CE
     assert not fast or R % 32 == 0
     acc = Accesses()

@@ -127,7 +127,8 @@ def test_workspace_queries(lib):
         n = lib.dynconv_bwd_ex_workspace_size(2, 50, 16 * H, 3, H, 1, 1, dt)
         assert n > 0 or H == 99
         assert n % 4 == 0
-    assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 6, 1, 64, BF16) == 0  # low-rank: W <= 5
+    assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 9, 1, 64, BF16) == 0  # low-rank: W <= 8
+    assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 8, 1, 64, BF16) > 0
     n = lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 64, BF16)
     assert n >= 64 * 2048 * 4 * 4  # at least one float32 dU partial
     assert lib.dynconv_lowrank_bwd_workspace_size(8, 4096, 2048, 4, 1, 0, BF16) == 0
@@ -147,7 +148,7 @@ def test_lowrank_validation(lib):
     assert lr_fwd(lib, ldu=100) == INVALID  # row shorter than (D/H)*W
     assert lr_fwd(lib, H=3) == INVALID  # 3 does not divide D = 200
     assert lr_fwd(lib, H=2, ldu=399) == INVALID  # head-wise: rows hold (D/H)*W = 400 columns
-    assert lr_fwd(lib, W=6, ldu=1200) == UNSUP  # the low-rank kernels take W <= 5
+    assert lr_fwd(lib, W=9, ldu=1800) == UNSUP  # the low-rank kernels take W <= 8
     need = lib.dynconv_lowrank_bwd_workspace_size(2, 4, 200, 4, 1, 64, BF16)
     st = lib.dynconv_lowrank_bwd(X, S(800, 200, 1), Z, S(256, 64, 1), U, 800, None, DY, S(800, 200, 1), DX,
                                  S(800, 200, 1), P(0x990000), S(256, 64, 1), P(0x9a0000), None, 2, 4, 200, 4, 1, 64,

@@ -117,13 +117,15 @@ def test_conv_bias_decode(dtype, W, H, static):
 # ------------------------------------------------------------------------------------
 LOWRANK = [
     # dtype, B, T, D, W, H, R, packed: the fast kernels (bf16 / f16, D % 64, even R) and the
-    # general ones (float32, W = 5 above 64 ranks, odd R, groups of 6)
+    # general ones (float32, W = 5 above 64 ranks, W = 6..8, odd R, groups of 6)
     ("bf16", 2, 300, 128, 4, 1, 64, False),
     ("f16", 2, 300, 128, 5, 1, 32, False),
     ("bf16", 2, 300, 256, 4, 4, 20, True),
     ("f32", 2, 300, 96, 3, 1, 16, False),
     ("bf16", 2, 150, 96, 5, 1, 100, False),
     ("bf16", 1, 77, 72, 2, 6, 7, True),
+    ("bf16", 2, 150, 128, 8, 1, 64, True),
+    ("f32", 2, 100, 96, 6, 2, 20, False),
 ]
 
 

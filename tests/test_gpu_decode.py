@@ -59,7 +59,8 @@ def test_decode_matches_full_sequence(dtype, W, H, static, T0):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("W,R,T0", [(1, 16, 3), (2, 40, 1), (3, 20, 0), (4, 64, 5), (4, 96, 0), (5, 128, 2)])
+@pytest.mark.parametrize("W,R,T0", [(1, 16, 3), (2, 40, 1), (3, 20, 0), (4, 64, 5), (4, 96, 0), (5, 128, 2), (6, 32, 2),
+                                     (7, 64, 0), (8, 128, 3)])
 def test_lowrank_decode_matches_full_sequence(dtype, W, R, T0):
     B, Ttot, D = 19, 10, 136  # two groups of sequences, a partial group of channels
     seed = 900 + W + R + T0

@@ -72,6 +72,9 @@ for dtype in ("f32", "bf16", "f16"):
     for W in (1, 2, 3, 4, 5):
         for R in (1, 20, 33, 64, 128):
             SMALL.append((dtype, W, R))
+    # the widest filters (W = 6..8, the pages' ablation reaches W = 6) take the general kernels
+    for W, R in ((6, 20), (6, 64), (7, 33), (7, 128), (8, 1), (8, 64), (8, 128)):
+        SMALL.append((dtype, W, R))
 
 
 @pytest.mark.parametrize("dtype,W,R", SMALL)
@@ -261,7 +264,8 @@ for dtype in ("f32", "bf16", "f16"):
 
 # groups whose size is not a power of two take the general kernels
 HEADWISE += [(dtype, H, W, R) for dtype in ("f32", "bf16", "f16") for H, W, R in ((3, 4, 64), (6, 3, 40), (12, 5, 52),
-                                                                                   (24, 2, 128))]
+                                                                                   (24, 2, 128), (4, 6, 64),
+                                                                                   (2, 8, 128), (3, 7, 40))]
 
 
 @pytest.mark.parametrize("dtype,H,W,R", HEADWISE)

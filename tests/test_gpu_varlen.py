@@ -116,7 +116,8 @@ LOWRANK = [("bf16", 4, 64, 128, 1), ("bf16", 2, 32, 128, 1), ("bf16", 3, 64, 192
            ("f32", 3, 32, 64, 8), ("f16", 4, 64, 128, 1), ("f16", 3, 40, 96, 2), ("bf16", 4, 64, 512, 4),
            ("bf16", 3, 32, 320, 2), ("bf16", 5, 64, 192, 2),
            ("bf16", 4, 64, 1024, 8), ("bf16", 4, 64, 1024, 16), ("bf16", 2, 32, 512, 8),
-           ("bf16", 4, 64, 192, 6), ("f32", 3, 20, 96, 3), ("f16", 5, 40, 240, 12)]
+           ("bf16", 4, 64, 192, 6), ("f32", 3, 20, 96, 3), ("f16", 5, 40, 240, 12),
+           ("bf16", 6, 64, 128, 1), ("f32", 8, 32, 96, 2), ("f16", 7, 100, 72, 1)]
 
 
 @pytest.mark.parametrize("dtype,W,R,D,H", LOWRANK)

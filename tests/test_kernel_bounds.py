@@ -178,7 +178,7 @@ GEN = [
 
 
 @pytest.mark.parametrize("B,T,D,H", GEN)
-@pytest.mark.parametrize("W", [1, 3, 4, 5])
+@pytest.mark.parametrize("W", [1, 3, 4, 5, 7, 8])
 @pytest.mark.parametrize("R", [1, 3, 20, 64, 100])
 @pytest.mark.parametrize("eb", [2, 4])
 def test_lowrank_fwd_general_bounds(B, T, D, H, W, R, eb):
@@ -205,7 +205,7 @@ GEN_BWD = [
 
 
 @pytest.mark.parametrize("B,T,D,H", GEN_BWD)
-@pytest.mark.parametrize("W", [1, 2, 4, 5])
+@pytest.mark.parametrize("W", [1, 2, 4, 5, 6, 8])
 @pytest.mark.parametrize("R", [3, 32, 64, 100, 128])
 @pytest.mark.parametrize("eb", [2, 4])
 def test_lowrank_bwd_general_bounds(B, T, D, H, W, R, eb):
