@@ -1361,22 +1361,25 @@ __device__ __forceinline__ void lowrank_dz_body(const LowRankParams& p, LrDzSmem
 // LdsPlace<CPR> maps logical chunk c of row r to a slot:
 //   CPR == 16 (256-byte rows: U at W = 4, x / dy at H = 4): rotate by
 //     r % 4 + 8 * ((r / 4) % 2), which puts the 16 reads of a pass on distinct slots;
-//   CPR % 8 == 4 (rows of 64, 192, 320 bytes): rotate by r / 2 (conflict-free for 64-byte
-//     rows, x / dy at H = 1);
-//   CPR == 8 (128-byte rows): rotate by r.
+//   CPR % 8 == 4 (rows of 64, 192, 320, 448 bytes) and CPR == 24 (U at W = 6): rotate by
+//     r / 2 (conflict-free for 64-byte rows, x / dy at H = 1; two-way for the others);
+//   CPR == 8 and CPR == 32 (128- and 512-byte rows, U at W = 2 and W = 8): rotate by r
+//     (r < 16: the 8 rows of a pass take 8 consecutive slots, the two chunks 8 apart).
 // U rows use r % 16 (the row within a 16-row tile), so every tile has the same slots.
 // ---------------------------------------------------------------------------------
+constexpr bool lds_place_ok(int cpr) { return cpr % 8 == 4 || cpr == 8 || cpr == 16 || cpr == 24 || cpr == 32; }
+
 template <int CPR>
 struct LdsPlace {
-  static_assert(CPR % 8 == 4 || CPR == 8 || CPR == 16, "LDS row length of the dz kernel");
+  static_assert(lds_place_ok(CPR), "LDS row length of the dz kernel");
   static __device__ __forceinline__ int slot(int r, int c) {
     if constexpr (CPR == 16) return (c + r % 4 + 8 * ((r / 4) % 2)) % 16;
-    else if constexpr (CPR == 8) return (c + r) % 8;
+    else if constexpr (CPR == 8 || CPR == 32) return (c + r) % CPR;
     else return (c + r / 2) % CPR;
   }
   static __device__ __forceinline__ int chunk(int r, int p) {  // inverse of slot for row r
     if constexpr (CPR == 16) return (p - r % 4 - 8 * ((r / 4) % 2) + 16) % 16;
-    else if constexpr (CPR == 8) return ((p - r % 8) % 8 + 8) % 8;
+    else if constexpr (CPR == 8 || CPR == 32) return ((p - r % CPR) % CPR + CPR) % CPR;
     else return ((p - (r / 2) % CPR) % CPR + CPR) % CPR;
   }
 };
@@ -1391,7 +1394,6 @@ struct LrDzDma {
   static constexpr int RP = 32 * KS;
   static constexpr int GL = HG <= 4 ? 8 : 32 / HG;  // filter groups of a lane
   static constexpr int RUNS = GL * HG / 8;          // 16-byte runs of a lane's row
-  static constexpr bool SHAPE_OK = (GL * W) % 8 == 0;
   static constexpr int CH = 4 * GL;            // filter groups of a chunk
   static constexpr int CHC = CH * HG;          // channels of a chunk
   static constexpr int UC = CH * W;            // filter columns of a chunk
@@ -1399,6 +1401,7 @@ struct LrDzDma {
   static constexpr int TB = kLowrankDzTokens;
   static constexpr int XR = TB + HALO;
   static constexpr int XCPR = CHC / 8;         // 16-byte chunks of an x / dy row
+  static constexpr bool SHAPE_OK = (GL * W) % 8 == 0 && lds_place_ok(UCPR) && lds_place_ok(XCPR);
   static constexpr int UCH = RP * UCPR, XCH = XR * XCPR, DCH = TB * XCPR;
   static constexpr int NI_U = (UCH + 63) / 64, NI_X = (XCH + 63) / 64, NI_D = (DCH + 63) / 64;
   static constexpr int NI = NI_U + NI_X + NI_D;  // wave-wide transfers per stage
@@ -1613,7 +1616,7 @@ __device__ __forceinline__ void lowrank_dz_dma(const LowRankParams& p, unsigned 
 // stages fit.
 template <typename ET, int W, int KS, int HG>
 constexpr bool lowrank_dz_dma_ok() {
-  return (std::is_same<ET, bf16_t>::value || std::is_same<ET, f16_t>::value) && W <= 5 && LrDzDma<W, KS, HG>::SHAPE_OK &&
+  return (std::is_same<ET, bf16_t>::value || std::is_same<ET, f16_t>::value) && LrDzDma<W, KS, HG>::SHAPE_OK &&
          LrDzDma<W, KS, HG>::BYTES <= 150 * 1024;
 }
 

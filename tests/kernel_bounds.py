@@ -426,14 +426,15 @@ def dz_dma_shape(W, KS, HG, stages=DZ_STAGES):
     UCH, XCH, DCH = RP * UCPR, XR * XCPR, STEP * XCPR
     ni = lambda n: (n + 63) // 64  # noqa: E731
     stage = (ni(UCH) + ni(XCH) + ni(DCH)) * 64 * 16
-    ok = W <= 5 and (GL * W) % 8 == 0 and stages * stage <= 150 * 1024
+    place_ok = lambda cpr: cpr % 8 == 4 or cpr in (8, 16, 24, 32)  # noqa: E731 (lds_place_ok)
+    ok = (GL * W) % 8 == 0 and place_ok(UCPR) and place_ok(XCPR) and stages * stage <= 150 * 1024
     return dict(GL=GL, CH=CH, CHC=CHC, UC=UC, UCPR=UCPR, XCPR=XCPR, XR=XR, UCH=UCH, XCH=XCH, DCH=DCH, ok=ok)
 
 
 def dz_dma(B, T, D, W, H, R, xs1, dys1, ldu):
     KS = (R + 31) // 32
     S = dz_dma_shape(W, KS, H)
-    assert S["ok"] and D % S["CHC"] == 0 and W <= 5
+    assert S["ok"] and D % S["CHC"] == 0
     HALO = lr_halo(W)
     nchunk = D // S["CHC"]
     acc = Accesses()

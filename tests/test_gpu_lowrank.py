@@ -303,6 +303,9 @@ def test_headwise_lowrank_parity(dtype, H, W, R):
 # (register path); the other W, R and H take the general kernels
 HEADWISE_DMA = [(H, W, R) for H in (2, 4, 8, 16) for W in (1, 2, 3, 4, 5) for R in (32, 64, 96, 128)]
 HEADWISE_DMA += [(H, W, R) for H in (4, 16) for W in (2, 4) for R in (20, 52)]
+# the widest filters: dz on the DMA path where its stages fit (U rows of 24, 28 or 32
+# 16-byte chunks per-channel), the rest of the backward and the forward on the general kernels
+HEADWISE_DMA += [(H, W, R) for H in (1, 2, 4, 8, 16) for W in (6, 7, 8) for R in (32, 64, 128)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
