@@ -135,15 +135,18 @@ __device__ __forceinline__ f32x4_t mma32(const u16x8_t& a, const u16x8_t& b, f32
   }
 }
 
-template <int KS, int NWV_, int XN_, int XD_, int ZN_, int ZD_, int SG_ = 0, int ZB_ = 16>
+template <int KS, int NWV_, int XN_, int XD_, int ZN_, int ZD_, int SG_ = 0, int ZB_ = 16, int IH_ = 4>
 struct FwdFast {
   static constexpr int NWV = NWV_, XN = XN_, XD = XD_, ZN = ZN_, ZD = ZD_;
   static constexpr int ZB = ZB_;  // bytes of a z piece per lane and transfer
-  // SG: packed sequences. Each step also stages the segment ids of tokens t0 - 4 .. t0 + 63
-  // (17 chunks of 16 bytes, 5 per wave: every wave issues exactly one more transfer, right
-  // before its x transfers, so it is complete whenever x is).
+  // SG: packed sequences. Each step also stages the segment ids of tokens t0 - IH .. t0 + 63
+  // (IH = 4, or 8 for filters of more than 5 taps: 17 or 18 chunks of 16 bytes, 5 per wave:
+  // every wave issues exactly one more transfer, right before its x transfers, so it is
+  // complete whenever x is).
   static constexpr int SG = SG_;
-  static constexpr int SCH = 17, SPW = 5, SSTAGE = NWV_ * SPW * 16;
+  static constexpr int IH = IH_;
+  static_assert(IH == 4 || IH == 8, "id rows before the step: one or two row groups");
+  static constexpr int SCH = (kStep + IH) / 4, SPW = 5, SSTAGE = NWV_ * SPW * 16;
   static constexpr int NT = 64 * NWV;                // threads
   static constexpr int CPB = 16 * NWV;               // channels per workgroup
   static constexpr int XCPR = CPB / 8;               // 16-byte chunks of an x (or y) row
@@ -162,7 +165,7 @@ struct FwdFast {
   static_assert((kStep * ZROW) % (64 * ZB * NWV) == 0, "z transfers split evenly over the waves");
   static_assert(XD >= 1 && XD <= XN - 2 && ZD >= 1 && ZD <= ZN - 1 && ZD <= XD, "pipeline depths");
   static_assert((XCPR & (XCPR - 1)) == 0 && 16 % XCPR == 0, "x row rotation");
-  static_assert(!SG || NWV * SPW >= SCH, "id chunks spread over the waves");
+  static_assert(!SG || (NWV * SPW >= SCH && (NWV - 1) * SPW < SCH), "id chunks: at least one in every wave");
   static constexpr int XG = XI + SG;  // operations of the x group (ids first)
 
   // Issue order of one wave's vector memory operations: a prologue x(0), z(0), x(1),
@@ -264,7 +267,7 @@ __device__ __forceinline__ void step_wait(int s) {
 
 template <typename ET, int W, int KS, int SG, int ZB>
 __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRankParams p) {
-  using F = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD, SG, ZB>;
+  using F = FwdFast<KS, LRF_NWV, LRF_XN, LRF_XD, LRF_ZN, LRF_ZD, SG, ZB, (W > 5 ? 8 : 4)>;
   constexpr int NWV = F::NWV, XN = F::XN, XD = F::XD, ZN = F::ZN, ZD = F::ZD, CPB = F::CPB;
   constexpr int XCPR = F::XCPR, XROW = F::XROW, XSTAGE = F::XSTAGE;
   constexpr int ZCPR = F::ZCPR, ZROW = F::ZROW, ZSTAGE = F::ZSTAGE, Z_OFF = F::Z_OFF, Y_OFF = F::Y_OFF;
@@ -273,7 +276,8 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   constexpr int MLO = -HR;        // x rows 4n + m, m = MLO .. 3, feed the lane's 4 tokens
   constexpr int NM = 4 - MLO;
   constexpr int NGT = gen_tiles<W>();
-  static_assert(HR <= 4, "x rows 4n + m with m >= -4 sit in the lane's row group or the one before");
+  constexpr int IH = F::IH;       // id rows before the lane's first token
+  static_assert(HR <= 7 && HR <= IH, "x rows 4n + m with m >= -8: the lane's row group or one of the two before");
   __shared__ __align__(16) unsigned char smem[F::BYTES];
 
   const int tid = threadIdx.x;
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
       }
     }
   };
-  // segment ids (SG): chunk sc = 5 wv + lane holds the ids of tokens t0 - 4 + 4 sc .. + 3
+  // segment ids (SG): chunk sc = 5 wv + lane holds the ids of tokens t0 - IH + 4 sc .. + 3
   // (clamped into 0 .. T - 1: before t = 0 the x rows are zero, past T nothing is stored)
   const int sc = F::SPW * wv + lane;
   const bool sact = SG && lane < F::SPW && sc < F::SCH;
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
   auto issue_s = [&](int st, int t0) {
     if constexpr (SG) {
       if (sact) {
-        const int tk = min(max(t0 - 4 + 4 * sc, 0), p.T - 4);
+        const int tk = min(max(t0 - IH + 4 * sc, 0), p.T - 4);
         dma16(sgc + int64_t(tk) * 4, smem + F::S_OFF + st * F::SSTAGE + wv * F::SPW * 16);
       }
     }
@@ -391,12 +395,16 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
 
   // ---- per-lane LDS offsets ----
   // x row 4n + m of ring stage u sits at u * XSTAGE + (4n + m) * XROW (rows before the
-  // stage, m < 0, are the previous stage's last rows; from stage 0 they wrap to the ring's
-  // end), chunk rotated by (row / 4): n - 1 for m < 0, n for m >= 0.
+  // stage, 4n + m < 0, are the previous stage's last rows; from stage 0 they wrap to the
+  // ring's end), chunk rotated by (row / 4): n - 2 for m < -4, n - 1 for m < 0, n for m >= 0
+  // (the rotation is taken modulo XCPR, which divides the 16 row groups of a stage, so a
+  // wrapped row keeps it).
   const int xc = 2 * wv + (q >> 1);  // logical 16-byte chunk of the lane's 4 channels
-  const int xlo = 4 * n * XROW + ((xc + n - 1) & (XCPR - 1)) * 16 + 8 * (q & 1);  // + m * XROW, m < 0
-  const int xhi = 4 * n * XROW + ((xc + n) & (XCPR - 1)) * 16 + 8 * (q & 1);      // + m * XROW, m >= 0
+  const int xlo2 = 4 * n * XROW + ((xc + n - 2) & (XCPR - 1)) * 16 + 8 * (q & 1);  // + m * XROW, m < -4
+  const int xlo = 4 * n * XROW + ((xc + n - 1) & (XCPR - 1)) * 16 + 8 * (q & 1);   // + m * XROW, -4 <= m < 0
+  const int xhi = 4 * n * XROW + ((xc + n) & (XCPR - 1)) * 16 + 8 * (q & 1);       // + m * XROW, m >= 0
   const int xwrap = n == 0 ? XN * XSTAGE : 0;
+  const int xwrap2 = n <= 1 ? XN * XSTAGE : 0;
   int zr[KS];  // + j * ZROW for token group j
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) zr[ks] = 4 * n * ZROW + ((4 * ks + q + n) % ZCPR) * 16;
@@ -445,22 +453,23 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
     issue_x((s + XD) % XN, t0 + XD * kStep);
     issue_z((s + ZD) % ZN, t0 + ZD * kStep);
     if (s > 0) yflush((s - 1) & 1, t0 - kStep);
-    // ids of rows 4n - 4 .. 4n + 3 (tap k of the lane's token 4n + j: kept when the id of
+    // ids of rows 4n - IH .. 4n + 3 (tap k of the lane's token 4n + j: kept when the id of
     // row 4n + j - k equals that of row 4n + j)
-    int idv[8] = {};
+    int idv[IH + 4] = {};
     if constexpr (SG) {
       const int* ids = reinterpret_cast<const int*>(smem + F::S_OFF + ux * F::SSTAGE) + 4 * n;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) idv[i] = ids[i];
+      for (int i = 0; i < IH + 4; ++i) idv[i] = ids[i];
     }
     // x rows 4n + MLO .. 4n + 3 of the lane's channels, as float32
     const unsigned char* xst = smem + ux * XSTAGE;
     const int lo = xlo + (ux == 0 ? xwrap : 0);
+    const int lo2 = xlo2 + (ux == 0 ? xwrap2 : 0);
     float xv[NM][4];
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi) {
       const int m = MLO + mi;
-      const u32x2 v = *reinterpret_cast<const u32x2*>(xst + (m < 0 ? lo : xhi) + m * XROW);
+      const u32x2 v = *reinterpret_cast<const u32x2*>(xst + (m < -4 ? lo2 : m < 0 ? lo : xhi) + m * XROW);
       xv[mi][0] = Cvt<ET>::lo(v[0]);
       xv[mi][1] = Cvt<ET>::hi(v[0]);
       xv[mi][2] = Cvt<ET>::lo(v[1]);
@@ -493,7 +502,7 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
         float y = fmaf(a[mt][0], xt, xt + cb[mt]);
 #pragma unroll
         for (int k = 1; k < W; ++k) {
-          const float ak = (!SG || idv[j + 4 - k] == idv[j + 4]) ? tap_of<W>(a, mt, k) : 0.f;
+          const float ak = (!SG || idv[j + IH - k] == idv[j + IH]) ? tap_of<W>(a, mt, k) : 0.f;
           y = fmaf(ak, xv[j - k - MLO][mt], y);
         }
         yv[mt] = y;
@@ -1301,6 +1310,8 @@ __global__ __launch_bounds__(512) void k_lowrank_bwd_fast(const LowRankParams p)
 // W = 5 takes a second set of generation tiles (taps 4..7), whose registers fit up to 64
 // ranks: at 128 ranks the fused backward would spill hundreds of registers.
 constexpr bool fast_width_ok(int w, int ks) { return w >= 1 && (w <= 4 || (w == 5 && ks <= 2)); }
+// The forward reaches up to two row groups back: up to eight taps.
+constexpr bool fwd_fast_width_ok(int w, int ks) { return w >= 1 && (w <= 4 || (w <= 8 && ks <= 2)); }
 
 // A rank of 32 KS is served when its z transfers split evenly over the waves.
 constexpr bool fwd_fast_rank_ok(int ks) {
@@ -1316,7 +1327,7 @@ constexpr int fwd_fast_resident(int lds_bytes) {
 
 template <typename ET, int W, int KS>
 hipError_t fwd_fast_try(const LowRankParams& p, int64_t blocks, hipStream_t s) {
-  if constexpr (fwd_fast_rank_ok(KS) && fast_width_ok(W, KS)) {
+  if constexpr (fwd_fast_rank_ok(KS) && fwd_fast_width_ok(W, KS)) {
     return fwd_fast_inst<ET, W, KS>(p, blocks, s);
   } else {
     return hipErrorInvalidValue;
@@ -1360,7 +1371,7 @@ bool lowrank_fast_rank_ok(const LowRankParams& p) {
 
 bool lowrank_fwd_fast_ok(const LowRankParams& p, int W, dynconv_dtype dt) {
   const int ks = (p.R + 31) / 32;
-  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && fast_width_ok(W, ks) &&
+  return (dt == DYNCONV_BF16 || dt == DYNCONV_F16) && lowrank_fast_group_ok(p.H) && fwd_fast_width_ok(W, ks) &&
          lowrank_fast_rank_ok(p) && fwd_fast_rank_ok(ks) &&
          p.D % (16 * LRF_NWV) == 0 && p.act16 != 0 &&
          (int64_t(p.T) + kStep) * p.os1 * 2 < (int64_t(1) << 31) && int64_t(kStep) * p.xs1 < (int64_t(1) << 30) &&
@@ -1406,6 +1417,9 @@ hipError_t launch_lowrank_fwd_fast(const LowRankParams& p, int W, dynconv_dtype 
       case 3: return fwd_fast_ks<ET, 3>(q, pl.blocks, s);
       case 4: return fwd_fast_ks<ET, 4>(q, pl.blocks, s);
       case 5: return fwd_fast_ks<ET, 5>(q, pl.blocks, s);
+      case 6: return fwd_fast_ks<ET, 6>(q, pl.blocks, s);
+      case 7: return fwd_fast_ks<ET, 7>(q, pl.blocks, s);
+      case 8: return fwd_fast_ks<ET, 8>(q, pl.blocks, s);
       default: return hipErrorInvalidValue;
     }
   };

@@ -214,9 +214,9 @@ def _x_chunks(rot):
     return rl, (pc - rot(rl)) & 7
 
 
-def _seg_loads(acc, b, t0, T):
-    sc = np.arange(17)  # id chunk sc: tokens t0 - 4 + 4 sc .. + 3, clamped into 0 .. T - 4
-    tk = np.minimum(np.maximum(t0 - 4 + 4 * sc, 0), T - 4)
+def _seg_loads(acc, b, t0, T, ih=4):
+    sc = np.arange((STEP + ih) // 4)  # id chunk sc: tokens t0 - ih + 4 sc .. + 3, clamped into 0 .. T - 4
+    tk = np.minimum(np.maximum(t0 - ih + 4 * sc, 0), T - 4)
     acc.add("seg", b, tk, 0, 1)
     acc.add("seg", b, tk + 3, 0, 1)
 
@@ -255,9 +255,14 @@ def fast_width_ok(W, KS):
     return 1 <= W <= 4 or (W == 5 and KS <= 2)
 
 
+def fwd_fast_width_ok(W, KS):
+    """The forward reaches two row groups back: up to eight taps."""
+    return 1 <= W <= 4 or (W <= 8 and KS <= 2)
+
+
 def fast_fwd_ok(T, D, W, H, R, xs1, zs1, os1):
     KS = (R + 31) // 32
-    return (KS in (1, 2, 4) and R % 2 == 0 and fast_width_ok(W, KS) and H in (1, 2, 4, 8, 16) and D % 64 == 0
+    return (KS in (1, 2, 4) and R % 2 == 0 and fwd_fast_width_ok(W, KS) and H in (1, 2, 4, 8, 16) and D % 64 == 0
             and (T + STEP) * os1 * 2 < I32 and STEP * xs1 < (1 << 30) and STEP * zs1 < (1 << 30))
 
 
@@ -285,7 +290,7 @@ def lowrank_fwd_fast(B, T, D, W, H, R, ZB, xs1, zs1, os1, seg=False, has_bias=Tr
             acc.add("z", b, step_rows(t0, zrow[zval], T), zel[zval], ZB // 2)
             acc.zero += int((~zval).sum())
             if seg:
-                _seg_loads(acc, b, t0, T)
+                _seg_loads(acc, b, t0, T, ih=8 if W > 5 else 4)
         if HR > 0 and t_first > 0:
             acc.add("x", b, t_first - HR + np.arange(HR)[:, None], c_base + 8 * np.arange(8)[None, :], 8)
         _fast_generation_operands(acc, c_base, H, W, R, KS, has_bias)

@@ -103,6 +103,24 @@ def test_fused_equals_materialised_path():
     assert_close("fused vs materialised", y_fused, to64(y_mat), torch.float32)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("W", [6, 7, 8])
+@pytest.mark.parametrize("R", [20, 64])
+@pytest.mark.parametrize("packed", [False, True])
+def test_wide_filters_fast_forward(dtype, W, R, packed):
+    """Six to eight taps on the fast forward (16-bit, D % 64 == 0, up to 64 ranks): the taps
+    reach two 4-token row groups back, across step boundaries, into the rows before a
+    range, and (packed) across documents of 1 to 3 tokens at the start of each row."""
+    B, T, D = 2, 388, 192
+    seed = 1100 + 10 * W + R + int(packed)
+    td = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    x, z, U, b, _ = _inputs(B, T, D, W, R, dtype, seed)
+    seq = synth.segments(B, T, 24.0, seed, first=(1, 2, 3)) if packed else None
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W, seq_idx=seq.cuda() if packed else None)
+    ref = lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W, 1, seq.numpy() if packed else None)
+    assert_close("y", y, ref, td)
+
+
 def test_deterministic():
     B, T, D, W, R = 2, 400, 256, 4, 64
     x, z, U, b, dy = (t.cuda() if t is not None else None for t in _inputs(B, T, D, W, R, "bf16", 22))

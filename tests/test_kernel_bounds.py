@@ -67,9 +67,9 @@ FAST_SHAPES = [
 FAST_RANKS = [2, 20, 26, 64, 100, 128]
 
 
-def _fast_cases():
-    for (B, T, D), W, H, R in itertools.product(FAST_SHAPES, [1, 2, 3, 4, 5], [1, 4, 16], FAST_RANKS):
-        if D % H or not kb.fast_width_ok(W, (R + 31) // 32):
+def _fast_cases(widths=(1, 2, 3, 4, 5), ok=kb.fast_width_ok):
+    for (B, T, D), W, H, R in itertools.product(FAST_SHAPES, widths, [1, 4, 16], FAST_RANKS):
+        if D % H or not ok(W, (R + 31) // 32):
             continue
         for ZB in ([16, 4] if R % 8 == 0 else [4]):
             yield B, T, D, W, H, R, ZB
@@ -78,6 +78,8 @@ def _fast_cases():
 FAST_CASES = list(_fast_cases())
 # a deterministic subset keeps the CPU suite short; every shape, W, H, R and ZB appears
 FAST_PICK = FAST_CASES[::7]
+# the forward alone also takes six to eight taps (up to 64 ranks)
+FAST_FWD_WIDE = list(_fast_cases((6, 7, 8), kb.fwd_fast_width_ok))[::5]
 
 
 def _layout(D, R, ZB, strided):
@@ -89,7 +91,7 @@ def _layout(D, R, ZB, strided):
     return D + 64, (R + zpad + (zpad - 1)) // zpad * zpad, D + 8, D + 128
 
 
-@pytest.mark.parametrize("B,T,D,W,H,R,ZB", FAST_PICK)
+@pytest.mark.parametrize("B,T,D,W,H,R,ZB", FAST_PICK + FAST_FWD_WIDE)
 @pytest.mark.parametrize("strided", [False, True])
 def test_lowrank_fwd_fast_bounds(B, T, D, W, H, R, ZB, strided):
     xs1, zs1, dys1, os1 = _layout(D, R, ZB, strided)
