@@ -166,7 +166,7 @@ def test_lowrank_conv_bias_many_chunks():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("W,H,R", [(4, 1, 64), (3, 4, 20), (5, 3, 40)])
+@pytest.mark.parametrize("W,H,R", [(4, 1, 64), (3, 4, 20), (5, 3, 40), (8, 2, 32), (7, 1, 100)])
 def test_lowrank_conv_bias_decode(dtype, W, H, R):
     B, Ttot, D, T0 = 5, 8, 96, 3
     seed = 70 + W + R
