@@ -353,6 +353,27 @@ def test_headwise_lowrank_fast_kernels(H, W, R, dtype):
     assert_close("db", db, rdb, td, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("W", [6, 8])
+def test_full_lowrank_wide_filters(W):
+    """Six taps (the widest of the pages' ablation) and eight at B8 T4096 D2048 R64, the
+    bench rows' launch: the fast forward (taps two row groups back), the general backward
+    and the DMA dz kernel (U rows of 24 and 32 chunks); every element of y, dx, dz, dU, db."""
+    B, T, D, R = 8, 4096, 2048, 64
+    seed = 320 + W
+    x = synth.draw((B, T, D), 1.0, seed, "x", "bf16")
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", "bf16")
+    z = synth.draw((B, T, R), 1.0, seed, "z", "bf16")
+    U = synth.draw((R, D * W), 0.1 / R**0.5, seed, "U", "bf16")
+    b = synth.draw((D * W,), 0.1**0.5, seed, "b", "bf16")
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W).cpu()
+    U64, b64 = to64(U), to64(b)
+    for s_ in range(B):
+        ref = lowrank_fwd(to64(x[s_ : s_ + 1]), to64(z[s_ : s_ + 1]), U64, b64, W)
+        assert_close(f"y[{s_}]", y[s_ : s_ + 1], ref, torch.bfloat16)
+    got = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W)
+    check_lowrank_full_bwd(x, z, U, b, dy, W, torch.bfloat16, got)
+
+
 @pytest.mark.parametrize("R", [20, 52])
 def test_full_lowrank_pages_ranks(R):
     """The pages' ranks at B8 T4096 D2048 W4 on the fast kernels (contiguous z: rows of
