@@ -121,6 +121,21 @@ def test_wide_filters_fast_forward(dtype, W, R, packed):
     assert_close("y", y, ref, td)
 
 
+@pytest.mark.parametrize("T", [1, 4, 7, 64, 65, 132])
+@pytest.mark.parametrize("packed", [False, True])
+def test_wide_filters_fast_forward_short(T, packed):
+    """Eight taps on the fast forward at lengths shorter than the filter, one step, one step
+    plus a token, and two steps plus four tokens (packed rows with T % 4 != 0 take the
+    general kernels)."""
+    B, D, W, R = 3, 128, 8, 32
+    seed = 1200 + T + int(packed)
+    x, z, U, b, _ = _inputs(B, T, D, W, R, "bf16", seed)
+    seq = synth.segments(B, T, 3.0, seed, first=(1, 2)) if packed else None
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W, seq_idx=seq.cuda() if packed else None)
+    ref = lowrank_fwd(to64(x), to64(z), to64(U), to64(b), W, 1, seq.numpy() if packed else None)
+    assert_close("y", y, ref, torch.bfloat16)
+
+
 def test_deterministic():
     B, T, D, W, R = 2, 400, 256, 4, 64
     x, z, U, b, dy = (t.cuda() if t is not None else None for t in _inputs(B, T, D, W, R, "bf16", 22))
