@@ -1308,7 +1308,8 @@ __global__ __launch_bounds__(512) void k_lowrank_bwd_fast(const LowRankParams p)
 }
 
 // W = 5 takes a second set of generation tiles (taps 4..7), whose registers fit up to 64
-// ranks: at 128 ranks the fused backward would spill hundreds of registers.
+// ranks: at 128 ranks the fused backward would spill hundreds of registers. The backward's
+// dx terms reach one lane back (W <= 5).
 constexpr bool fast_width_ok(int w, int ks) { return w >= 1 && (w <= 4 || (w == 5 && ks <= 2)); }
 // The forward reaches up to two row groups back: up to eight taps.
 constexpr bool fwd_fast_width_ok(int w, int ks) { return w >= 1 && (w <= 4 || (w <= 8 && ks <= 2)); }

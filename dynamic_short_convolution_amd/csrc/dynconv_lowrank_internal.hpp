@@ -43,7 +43,7 @@ struct LowRankParams {
 
 // Low-rank forward tiling, shared by the planner and the kernel: each wave generates MT
 // 16-row MFMA tiles of filter columns; a filter of W <= 4 taps takes 4 rows (one lane
-// group), W = 5 takes 8 rows (two lane groups). A workgroup of 4 waves covers
+// group), W = 5..8 take 8 rows (two lane groups). A workgroup of 4 waves covers
 // 4 * MT * 16 / rows_per_channel channels.
 #ifndef LOWRANK_FWD_MT
 #define LOWRANK_FWD_MT 8
@@ -79,7 +79,7 @@ dynconv_status launch_lowrank_fwd(const LowRankParams& p, const LowRankPlan& pla
 // Group sizes the fast bf16 kernels serve: H in {1, 2, 4, 8, 16}, so that a 64-channel
 // slice holds whole groups (each channel loads its group's columns of U and of the bias).
 bool lowrank_fast_group_ok(int H);
-// 16-bit (bf16, float16) fast forward (LDS DMA pipeline; W <= 4, or W = 5 up to 64 ranks;
+// 16-bit (bf16, float16) fast forward (LDS DMA pipeline; W <= 4, or W = 5..8 up to 64 ranks;
 // R zero-padded to 32, 64 or 128 ranks (R <= 64 or R > 96) with 16-byte z pieces (aligned
 // rows, R % 8 == 0) or 4-byte ones (R even), those H, 16-byte aligned activation rows, D a
 // multiple of 64). It plans its own token ranges.

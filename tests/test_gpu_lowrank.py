@@ -218,7 +218,8 @@ def test_full_lowrank_r64_bwd(dtype):
 
 
 # ---------------------------------------------------------------------------------
-# The 16-bit fast paths (W <= 4 at R up to 128, W = 5 up to 64 ranks; D a multiple of 64,
+# The 16-bit fast paths (W <= 4 at R up to 128, W = 5 up to 64 ranks, and the forward alone
+# W = 6..8 up to 64 ranks; D a multiple of 64,
 # 16-byte aligned rows): token ranges of whole 64-token steps, an x ring in LDS that carries the W-1 rows
 # before each step (forward), dx completed across lanes, ranges and a tail step
 # (backward), buffer stores that drop rows past T.
