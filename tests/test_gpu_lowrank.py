@@ -14,7 +14,7 @@ import torch
 
 import synth
 from dynamic_short_convolution_amd import dynconv_fwd, dynconv_lowrank_bwd, dynconv_lowrank_fwd
-from oracle import conv_bwd, lowrank_bwd, lowrank_filters, lowrank_fwd
+from oracle import conv_bias_grad, conv_bwd, lowrank_bwd, lowrank_filters, lowrank_fwd
 from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
@@ -163,7 +163,7 @@ def rounded(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to(dtype).to(torch.float64).numpy()
 
 
-def check_lowrank_full_bwd(x, z, U, b, dy, W, dtype, got, seq_idx=None):
+def check_lowrank_full_bwd(x, z, U, b, dy, W, dtype, got, seq_idx=None, H=1):
     """Every element of a full-size low-rank backward, one sequence at a time.
 
     dx and db: against the oracle with the usual bounds. dz and dU: the normwise gate
@@ -171,7 +171,9 @@ def check_lowrank_full_bwd(x, z, U, b, dy, W, dtype, got, seq_idx=None):
     to the storage type (the kernels round g = dy x_{t-k} to 16 bits as the operand of
     the matrix-core products dz = g U^T and dU = z^T g; the rounding noise of 32768 tokens
     would otherwise hide a dropped or doubled token): float32 accumulation, at most 128
-    roundings of a running sum per output element, gives 2^-17 sum |terms|.
+    roundings of a running sum per output element, gives 2^-17 sum |terms|. Head-wise
+    (H > 1): dz takes each group's g summed over its H channels in float32 and then
+    rounded; dU takes every channel's g rounded, its H channels summed afterwards.
     """
     dx, dz, dU, db = (t.cpu() for t in got)
     B, T, D = x.shape
@@ -186,12 +188,19 @@ def check_lowrank_full_bwd(x, z, U, b, dy, W, dtype, got, seq_idx=None):
     for s_ in range(B):
         x64, z64, dy64 = to64(x[s_ : s_ + 1]), to64(z[s_ : s_ + 1]), to64(dy[s_ : s_ + 1])
         sq = seq_idx[s_ : s_ + 1] if seq_idx is not None else None
-        rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, 1, sq)
+        rdx, rdz, rdU, rdb = lowrank_bwd(x64, z64, U64, b64, dy64, W, H, sq)
         assert_close(f"dx[{s_}]", dx[s_ : s_ + 1], rdx, dtype)
         # the oracle's per-token filter gradient g (independent of the filters) and its rounding
-        _, g = conv_bwd(x64, np.zeros((1, T, D, W)), dy64, 1, sq)
+        _, g = conv_bwd(x64, np.zeros((1, T, D // H, W)), dy64, H, sq)
         g = g.reshape(T, J)
         gr = rounded(g, dtype)
+        if H > 1:
+            _, gc = conv_bwd(x64, np.zeros((1, T, D, W)), dy64, 1, sq)
+            gr_dU = rounded(gc.reshape(T, D * W), dtype).reshape(T, D // H, H, W).sum(axis=2).reshape(T, J)
+            gabs_dU = np.abs(rounded(gc.reshape(T, D * W), dtype)).reshape(T, D // H, H, W).sum(axis=2).reshape(T, J)
+            del gc
+        else:
+            gr_dU, gabs_dU = gr, np.abs(gr)
         zf = z64.reshape(T, R)
         dz_rnd = (gr @ U64.T).reshape(1, T, R)
         err = float(np.max(np.abs(to64(dz[s_ : s_ + 1]) - rdz)) / np.max(np.abs(rdz)))
@@ -199,8 +208,8 @@ def check_lowrank_full_bwd(x, z, U, b, dy, W, dtype, got, seq_idx=None):
         assert_close(f"dz[{s_}] vs rounded g", dz[s_ : s_ + 1], dz_rnd, dtype,
                      extra=2.0**-17 * (np.abs(gr) @ np.abs(U64).T).reshape(1, T, R))
         dU_ref += rdU
-        dU_rnd += zf.T @ gr
-        dU_abs += np.abs(zf).T @ np.abs(gr)
+        dU_rnd += zf.T @ gr_dU
+        dU_abs += np.abs(zf).T @ gabs_dU
         db_ref += rdb
     err = float(np.max(np.abs(to64(dU) - dU_ref)) / np.max(np.abs(dU_ref)))
     assert err <= {torch.bfloat16: 2e-2, torch.float16: 2.5e-3}[dtype], f"dU normwise {err}"
@@ -390,7 +399,70 @@ def test_full_lowrank_wide_filters(W):
     check_lowrank_full_bwd(x, z, U, b, dy, W, torch.bfloat16, got)
 
 
-@pytest.mark.parametrize("R", [20, 52])
+def _full_lowrank(W, R, H, seed, dtype=torch.bfloat16):
+    """Every element of y, dx, dz, dU and db at B8 T4096 D2048 (U of R x (D/H)*W)."""
+    B, T, D = 8, 4096, 2048
+    dn = {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
+    x = synth.draw((B, T, D), 1.0, seed, "x", dn)
+    dy = synth.draw((B, T, D), 1.0, seed, "dy", dn)
+    z = synth.draw((B, T, R), 1.0, seed, "z", dn)
+    U = synth.draw((R, (D // H) * W), 0.1 / R**0.5, seed, "U", dn)
+    b = synth.draw(((D // H) * W,), 0.1**0.5, seed, "b", dn)
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W, H).cpu()
+    U64, b64 = to64(U), to64(b)
+    for s_ in range(B):
+        ref = lowrank_fwd(to64(x[s_ : s_ + 1]), to64(z[s_ : s_ + 1]), U64, b64, W, H)
+        assert_close(f"y[{s_}]", y[s_ : s_ + 1], ref, dtype)
+    got = dynconv_lowrank_bwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), dy.cuda(), W, H)
+    check_lowrank_full_bwd(x, z, U, b, dy, W, dtype, got, H=H)
+
+
+def test_full_lowrank_w5_r64():
+    """Five taps at 64 ranks on the fast kernels (the second generation tile set)."""
+    _full_lowrank(5, 64, 1, 330)
+
+
+def test_full_lowrank_h4_r64():
+    """Head-wise generation, groups of 4 channels, on the fast kernels and the DMA dz."""
+    _full_lowrank(4, 64, 4, 331)
+
+
+def test_full_lowrank_r64_f32_fwd():
+    """The float32 row (general kernels on the float32 matrix cores): every element of y."""
+    B, T, D, W, R = 8, 4096, 2048, 4, 64
+    seed = 332
+    x = synth.draw((B, T, D), 1.0, seed, "x", "f32")
+    z = synth.draw((B, T, R), 1.0, seed, "z", "f32")
+    U = synth.draw((R, D * W), 0.1 / R**0.5, seed, "U", "f32")
+    b = synth.draw((D * W,), 0.1**0.5, seed, "b", "f32")
+    y = dynconv_lowrank_fwd(x.cuda(), z.cuda(), U.cuda(), b.cuda(), W).cpu()
+    U64, b64 = to64(U), to64(b)
+    for s_ in range(B):
+        ref = lowrank_fwd(to64(x[s_ : s_ + 1]), to64(z[s_ : s_ + 1]), U64, b64, W)
+        assert_close(f"y[{s_}]", y[s_ : s_ + 1], ref, torch.float32)
+
+
+def test_full_lowrank_conv_bias():
+    """The low-rank bias row at B8 T4096 D2048 W4 R64: y against the oracle with the bias,
+    the bias gradient against the column sum of dy, and dx, dz, dU, db bit for bit those of
+    the call without it."""
+    wl = synth.workloads()["lowrank_r64_bwd"]
+    x, z, U, b, dy = (t.cuda() for t in (wl.x(), wl.z(), wl.U(), wl.b(), wl.dy()))
+    c = synth.draw((wl.D,), 0.5, wl.seed, "c", "bf16")
+    y = dynconv_lowrank_fwd(x, z, U, b, wl.W, conv_bias=c.cuda()).cpu()
+    with_cb = dynconv_lowrank_bwd(x, z, U, b, dy, wl.W, want_dconv_bias=True)
+    without = dynconv_lowrank_bwd(x, z, U, b, dy, wl.W)
+    for name, a_, b_ in zip(("dx", "dz", "dU", "db"), with_cb[:4], without):
+        assert torch.equal(a_, b_), name
+    U64, b64, c64 = to64(U.cpu()), to64(b.cpu()), to64(c)
+    xc, zc, dyc = x.cpu(), z.cpu(), dy.cpu()
+    for s_ in range(wl.B):
+        ref = lowrank_fwd(to64(xc[s_ : s_ + 1]), to64(zc[s_ : s_ + 1]), U64, b64, wl.W, 1, None, c64)
+        assert_close(f"y[{s_}]", y[s_ : s_ + 1], ref, torch.bfloat16)
+    assert_close("dconv_bias", with_cb[4], conv_bias_grad(to64(dyc)), torch.float32, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("R", [16, 20, 52])
 def test_full_lowrank_pages_ranks(R):
     """The pages' ranks at B8 T4096 D2048 W4 on the fast kernels (contiguous z: rows of
     40 or 104 bytes, staged in 4-byte pieces, ranks zero-padded to 32 or 64): every

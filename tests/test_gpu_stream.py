@@ -11,7 +11,7 @@ import torch
 
 import synth
 from dynamic_short_convolution_amd import dynconv_bwd, dynconv_fwd
-from oracle import conv_bwd, conv_fwd
+from oracle import conv_bias_grad, conv_bwd, conv_fwd
 from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
@@ -335,6 +335,40 @@ def test_full_headwise_h16_bwd():
 def test_full_headwise_h12_fwd_bwd():
     # groups of 3 lanes (4 channels each), 63 lanes of a backward wave in use
     _full_check(synth.workloads()["headwise_h12"])
+
+
+def test_full_headwise_h4_fwd():
+    _full_check(synth.workloads()["headwise_h4"], do_bwd=False)
+
+
+def test_full_static_w4_fwd_bwd():
+    _full_check(synth.Workload("static_w4", 8, 4096, 2048, 4, 1, static=True, seed=7, w_var=0.25))
+
+
+def test_full_perchannel_w8_fwd_bwd():
+    # the widest filter: plain stores in the backward, 8 taps per lane window
+    _full_check(synth.Workload("perchannel_w8", 8, 4096, 2048, 8, 1, seed=8))
+
+
+def test_full_perchannel_conv_bias():
+    """The per-channel bias row at B8 T4096 D2048 W4: y with the bias, dx and dw as without
+    it, and the bias gradient (a column sum of dy over all 32768 tokens)."""
+    wl = synth.Workload("convbias_perchannel_h1", 8, 4096, 2048, 4, 1, seed=9)
+    x, w, dy = wl.x(), wl.w(), wl.dy()
+    c = synth.draw((wl.D,), 0.5, wl.seed, "c", "bf16")
+    xg, wg, dyg, cg = x.cuda(), w.cuda(), dy.cuda(), c.cuda()
+    y = dynconv_fwd(xg, wg, 1, conv_bias=cg).cpu()
+    dx, dw, dcb = (t.cpu() for t in dynconv_bwd(xg, wg, dyg, 1, want_dconv_bias=True))
+    del xg, wg, dyg
+    torch.cuda.empty_cache()
+    c64 = to64(c)
+    for b in range(wl.B):
+        x64, w64 = to64(x[b : b + 1]), to64(w[b : b + 1])
+        assert_close(f"y[{b}]", y[b : b + 1], conv_fwd(x64, w64, 1, None, c64), torch.bfloat16)
+        rdx, rdw = conv_bwd(x64, w64, to64(dy[b : b + 1]), 1)
+        assert_close(f"dx[{b}]", dx[b : b + 1], rdx, torch.bfloat16)
+        assert_close(f"dw[{b}]", dw[b : b + 1], rdw, torch.bfloat16)
+    assert_close("dconv_bias", dcb, conv_bias_grad(to64(dy)), torch.float32, rtol=1e-5, atol=1e-5)
 
 
 # The fixed-order reduce of the static backward's per-chunk partials has a 16-byte path
