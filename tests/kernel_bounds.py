@@ -469,6 +469,70 @@ def dz_dma(B, T, D, W, H, R, xs1, dys1, ldu):
 
 
 # ---------------------------------------------------------------------------------------
+# k_lowrank_dz: register-staged dz (any storage type, ragged token blocks and D, any H)
+# ---------------------------------------------------------------------------------------
+DZ_CHUNK = 32  # channels per chunk (kLowrankDzChunk)
+
+
+def lowrank_dz_register(B, T, D, W, H, R, eb, xs1, dys1, ldu, tbb0=0, nTbL=None, seg=False):
+    """One workgroup per (sequence, 64-token block tbb0 ..): every chunk of CH channels stages
+    the chunk's U columns (all ranks; head-wise: each channel's group columns, element by
+    element), the x rows from HALO tokens before the block and the dy rows, each 16-byte
+    piece clipped to the chunk's end in D and to rows 0 .. T-1; prefetches run two chunks
+    past the last one and load nothing there."""
+    KS = (R + 31) // 32
+    CE = 16 // eb
+    CH, TB, HALO, RP = DZ_CHUNK, STEP, lr_halo(W), 32 * KS
+    UC = CH * W
+    XR = TB + HALO
+    UCH, XCH, DCH = RP * UC // CE, XR * CH // CE, TB * CH // CE
+    US, AS = (UCH + 255) // 256, (XCH + DCH + 255) // 256
+    nblk = (T + TB - 1) // TB
+    nTbL = nblk - tbb0 if nTbL is None else nTbL
+    nchunk = (D + CH - 1) // CH
+    acc = Accesses()
+    ck = np.arange(US * 256)
+    ur, uc = ck // (UC // CE), (ck % (UC // CE)) * CE
+    ak = np.arange(AS * 256)
+    isx = ak < XCH
+    k2 = np.where(isx, ak, ak - XCH)
+    arow, ac = k2 // (CH // CE), (k2 % (CH // CE)) * CE
+    acc.int32("U offset r*int(ldu) + c", ur[(ck < UCH) & (ur < R)] * ldu + UC)
+    acc.int32("x offset row*int(xs1) + c", arow[isx] * xs1 + CH)
+    acc.int32("dy offset row*int(dys1) + c", arow[~isx & (k2 < DCH)] * dys1 + CH)
+    e = np.arange(CE)
+    for b in range(B):
+        for tb in range(tbb0, tbb0 + nTbL):
+            tb0 = tb * TB
+            for c0 in range(0, (nchunk + 2) * CH, CH):
+                climit, jlimit = D - c0, (D - c0) * W
+                ok = (ck < UCH) & (ur < R) & (uc < jlimit)
+                if H == 1:
+                    acc.add("U", 0, ur[ok], c0 * W + uc[ok], np.minimum(CE, jlimit - uc[ok]))
+                else:
+                    # element e reads column c + min(e, limit - 1) of the chunk
+                    lim = jlimit - uc[ok]
+                    jj = uc[ok][:, None] + np.minimum(e[None, :], lim[:, None] - 1)
+                    col = ((c0 + jj // W) // H) * W + jj % W
+                    acc.add("U", 0, np.broadcast_to(ur[ok][:, None], col.shape), col, 1)
+                t = np.where(isx, tb0 - HALO + arow, tb0 + arow)
+                okx = (isx | (k2 < DCH)) & (t >= 0) & (t < T) & (ac < climit)
+                w = np.minimum(CE, climit - ac)
+                acc.add("x", b, t[okx & isx], c0 + ac[okx & isx], w[okx & isx])
+                acc.add("dy", b, t[okx & ~isx], c0 + ac[okx & ~isx], w[okx & ~isx])
+            nt = np.arange(TB)
+            if seg:
+                tt = np.minimum(tb0 + nt, T - 1)
+                acc.add("seg", b, tt, 0, 1)
+                for k in range(1, W):
+                    acc.add("seg", b, (tt - k)[tt - k >= 0], 0, 1)
+            t = tb0 + nt
+            t = t[t < T]
+            acc.add("dz", b, t[:, None], np.arange(R)[None, :], 1)
+    return acc
+
+
+# ---------------------------------------------------------------------------------------
 # general low-rank kernels (register-staged 16-byte chunks; any dtype, ragged D)
 # ---------------------------------------------------------------------------------------
 

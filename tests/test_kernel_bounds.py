@@ -166,6 +166,43 @@ def test_dz_cases_cover_every_group_size_and_width():
 
 
 # ---------------------------------------------------------------------------------------
+# register-path dz (every dtype, ragged T and D, any H; the blocks the DMA path leaves)
+# ---------------------------------------------------------------------------------------
+DZ_REG = [
+    # B, T, D, H
+    (1, 1, 8, 1),
+    (2, 65, 40, 2),
+    (1, 130, 96, 3),
+    (1, 200, 72, 12),
+    (2, 64, 256, 16),
+]
+
+
+@pytest.mark.parametrize("B,T,D,H", DZ_REG)
+@pytest.mark.parametrize("W", [1, 3, 4, 5, 7, 8])
+@pytest.mark.parametrize("R", [1, 20, 64, 100, 128])
+@pytest.mark.parametrize("eb", [2, 4])
+def test_lowrank_dz_register_bounds(B, T, D, H, W, R, eb):
+    J = (D // H) * W
+    strided = (T + W + R) % 2 == 1
+    xs1, dys1, ldu = (D + 24, D + 8, J + 5) if strided else (D, D, J)
+    acc = kb.lowrank_dz_register(B, T, D, W, H, R, eb, xs1, dys1, ldu, seg=T % 2 == 1)
+    acc.check({"x": (B, T, D), "dy": (B, T, D), "U": (1, R, J), "dz": (B, T, R), "seg": (B, T, 1)})
+    _full(acc, "dz", B, T, R)
+    _full(acc, "x", B, T, D)
+    _full(acc, "dy", B, T, D)
+
+
+def test_lowrank_dz_register_tail_blocks():
+    """The blocks after the DMA path's whole ones (tbb0 > 0): only the tail's tokens of dz."""
+    B, T, D, W, H, R = 2, 200, 64, 4, 1, 64
+    acc = kb.lowrank_dz_register(B, T, D, W, H, R, 2, D, D, D * W, tbb0=3, nTbL=1)
+    acc.check({"x": (B, T, D), "dy": (B, T, D), "U": (1, R, D * W), "dz": (B, T, R)})
+    cov = acc.cover("dz", B, T, R)
+    assert cov[:, 192:].all() and not cov[:, :192].any()
+
+
+# ---------------------------------------------------------------------------------------
 # general kernels
 # ---------------------------------------------------------------------------------------
 GEN = [
