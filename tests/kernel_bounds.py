@@ -469,6 +469,99 @@ def dz_dma(B, T, D, W, H, R, xs1, dys1, ldu):
 
 
 # ---------------------------------------------------------------------------------------
+# decoding: k_cache_fill, k_decode_step, k_lowrank_decode_step
+# ---------------------------------------------------------------------------------------
+
+def cache_fill(B, t, D, W, seg=False):
+    """One thread per (sequence, cache slot, channel): slot m holds token s, the one of
+    t - (W-1) .. t-1 with s = m (mod W-1); tokens before 0 (and, packed, of another
+    document than token t-1) store zero without a load."""
+    S = W - 1
+    acc = Accesses()
+    if S == 0:
+        return acc
+    idx = np.arange(B * S * D)
+    d, m, b = idx % D, (idx // D) % S, idx // (D * S)
+    s0 = t - S
+    s_ = s0 + ((m - s0) % S + S) % S
+    keep = s_ >= 0
+    if seg:
+        acc.add("seg", b[keep], s_[keep], 0, 1)
+        acc.add("seg", b[keep], t - 1, 0, 1)
+    acc.add("x", b[keep], s_[keep], d[keep], 1)
+    acc.add("cache", b, m, d, 1)
+    return acc
+
+
+def decode_step(B, D, W, H, t, static=False, cbias=False):
+    """One thread per (sequence, channel): the W taps of its group, x_t, the W-1 cached
+    inputs and the optional bias; stores y and the cache slot of token t."""
+    S = W - 1
+    acc = Accesses()
+    idx = np.arange(B * D)
+    d, b = idx % D, idx // D
+    wb = 0 if static else b
+    acc.add("w", np.broadcast_to(np.asarray(wb), d.shape), 0, (d // H) * W, W)
+    acc.add("x", b, 0, d, 1)
+    if cbias:
+        acc.add("cbias", 0, 0, d, 1)
+    for kk in range(1, W):
+        acc.add("cache", b, ((t - kk) % S + S) % S, d, 1)
+    if S > 0:
+        acc.add("cache", b, t % S, d, 1)
+    acc.add("y", b, 0, d, 1)
+    return acc
+
+
+def lowrank_decode_step(B, D, W, H, R, t, vec, has_bias=True, cbias=False):
+    """Workgroups of 64 lanes over (16 channels, 16 sequences): lane (l, q) generates the
+    filters of channel c0 + l (clamped to D-1) for sequences b0 + 4q + i (clamped to B-1),
+    from z rows b0 + l (clamped) and U rows r < 32 NK (clamped to R-1); VEC: 16-byte z
+    pieces at rank min(32 s + 8 q, R - 8) (R % 8 == 0). Stores only for c0 + l < D and
+    sequences below B. Returns the accesses and the element offsets of the vector loads."""
+    S = W - 1
+    NK = (R + 31) // 32
+    acc = Accesses()
+    vec_offsets = []
+    for by in range((B + 15) // 16):
+        for bx in range((D + 15) // 16):
+            b0, c0 = by * 16, bx * 16
+            for lane in range(64):
+                l, q = lane & 15, lane >> 4
+                ca = min(c0 + l, D - 1)
+                bs = [min(b0 + 4 * q + i, B - 1) for i in range(4)]
+                acc.add("x", bs, 0, ca, 1)
+                for kk in range(1, W):
+                    acc.add("cache", bs, ((t - kk) % S + S) % S, ca, 1)
+                zb = min(b0 + l, B - 1)
+                for s_ in range(NK):
+                    k0 = 32 * s_ + 8 * q
+                    if vec:
+                        acc.add("z", zb, 0, min(k0, R - 8), 8)
+                        vec_offsets.append(("z", zb, min(k0, R - 8)))
+                    else:
+                        acc.add("z", zb, 0, [min(k0 + e, R - 1) for e in range(8)], 1)
+                    for e in range(8):
+                        r = min(32 * s_ + 8 * q + e, R - 1)
+                        acc.add("U", 0, r, (ca // H) * W, W)
+                        if vec and W in (2, 4):
+                            vec_offsets.append(("U", r, (ca // H) * W))
+                if has_bias:
+                    acc.add("bias", 0, 0, (ca // H) * W, W)
+                if cbias:
+                    acc.add("cbias", 0, 0, ca, 1)
+                if c0 + l < D:
+                    for i in range(4):
+                        b = b0 + 4 * q + i
+                        if b >= B:
+                            break
+                        acc.add("y", b, 0, ca, 1)
+                        if S > 0:
+                            acc.add("cache", b, t % S, ca, 1)
+    return acc, vec_offsets
+
+
+# ---------------------------------------------------------------------------------------
 # k_lowrank_dz: register-staged dz (any storage type, ragged token blocks and D, any H)
 # ---------------------------------------------------------------------------------------
 DZ_CHUNK = 32  # channels per chunk (kLowrankDzChunk)

@@ -166,6 +166,43 @@ def test_dz_cases_cover_every_group_size_and_width():
 
 
 # ---------------------------------------------------------------------------------------
+# decoding
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,D,H", [(1, 8, 1), (3, 72, 4), (5, 130, 5), (17, 96, 6)])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("t", [0, 1, 2, 7, 20])
+def test_decode_bounds(B, D, H, W, t):
+    S = max(W - 1, 1)
+    fill = kb.cache_fill(B, t, D, W, seg=t > 0)
+    fill.check({"x": (B, max(t, 1), D), "cache": (B, S, D), "seg": (B, max(t, 1), 1)})
+    if W > 1:
+        _full(fill, "cache", B, S, D)
+    for static in (False, True):
+        acc = kb.decode_step(B, D, W, H, t, static=static, cbias=True)
+        acc.check({"w": (1 if static else B, 1, (D // H) * W), "x": (B, 1, D), "cbias": (1, 1, D),
+                   "cache": (B, S, D), "y": (B, 1, D)})
+        _full(acc, "y", B, 1, D)
+
+
+@pytest.mark.parametrize("B,D,H", [(1, 8, 1), (19, 136, 1), (16, 64, 4), (33, 72, 3)])
+@pytest.mark.parametrize("W", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("R", [1, 8, 20, 64, 96, 128])
+@pytest.mark.parametrize("t", [0, 3])
+def test_lowrank_decode_bounds(B, D, H, W, R, t):
+    vec = R % 8 == 0
+    S = max(W - 1, 1)
+    J = (D // H) * W
+    acc, voffs = kb.lowrank_decode_step(B, D, W, H, R, t, vec, has_bias=R % 3 != 0, cbias=True)
+    acc.check({"x": (B, 1, D), "cache": (B, S, D), "z": (B, 1, R), "U": (1, R, J), "bias": (1, 1, J),
+               "cbias": (1, 1, D), "y": (B, 1, D)})
+    _full(acc, "y", B, 1, D)
+    # vector loads: z pieces of 8 ranks at multiples of 8 (16-byte aligned rows), U taps at
+    # multiples of W (rows ldu = J, a multiple of W)
+    for name, row, col in voffs:
+        assert col % (8 if name == "z" else W) == 0, (name, row, col)
+
+
+# ---------------------------------------------------------------------------------------
 # register-path dz (every dtype, ragged T and D, any H; the blocks the DMA path leaves)
 # ---------------------------------------------------------------------------------------
 DZ_REG = [
