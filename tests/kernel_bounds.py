@@ -469,6 +469,37 @@ def dz_dma(B, T, D, W, H, R, xs1, dys1, ldu):
 
 
 # ---------------------------------------------------------------------------------------
+# fixed-order reduce of float32 partials: k_reduce_partials (one column per thread, 8
+# groups of chunks) and k_reduce_partials4 / 4x2 (4 columns per thread, 16-byte loads,
+# G = 8 groups, or 32 from 64 chunks on)
+# ---------------------------------------------------------------------------------------
+
+def reduce_partials(nchunk, n, vec4):
+    acc = Accesses()
+    tid = np.arange(256)
+    if vec4:
+        assert n % 4 == 0
+        G = 32 if nchunk >= 64 else 8
+        C = 256 // G
+        col, grp = tid % C, tid // C
+        for blk in range((n + 4 * C - 1) // (4 * C)):
+            i = blk * 4 * C + 4 * col
+            for g, ii in zip(grp[i < n], i[i < n]):
+                acc.add("part", 0, np.arange(g, nchunk, G), ii, 4)
+            st = (grp == 0) & (i < n)
+            acc.add("out", 0, 0, i[st], 4)
+    else:
+        col, grp = tid % 32, tid // 32
+        for blk in range((n + 31) // 32):
+            i = blk * 32 + col
+            for g, ii in zip(grp[i < n], i[i < n]):
+                acc.add("part", 0, np.arange(g, nchunk, 8), ii, 1)
+            st = (grp == 0) & (i < n)
+            acc.add("out", 0, 0, i[st], 1)
+    return acc
+
+
+# ---------------------------------------------------------------------------------------
 # decoding: k_cache_fill, k_decode_step, k_lowrank_decode_step
 # ---------------------------------------------------------------------------------------
 

@@ -166,6 +166,20 @@ def test_dz_cases_cover_every_group_size_and_width():
 
 
 # ---------------------------------------------------------------------------------------
+# fixed-order reduce
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("nchunk", [1, 7, 8, 63, 64, 200])
+@pytest.mark.parametrize("n", [1, 3, 4, 31, 33, 600, 2052])
+def test_reduce_partials_bounds(nchunk, n):
+    for vec4 in ([False, True] if n % 4 == 0 else [False]):
+        acc = kb.reduce_partials(nchunk, n, vec4)
+        acc.check({"part": (1, nchunk, n), "out": (1, 1, n)})
+        _full(acc, "part", 1, nchunk, n)  # every partial summed ...
+        assert sum(int(w.sum()) for *_, w in acc.spans["part"]) == nchunk * n  # ... once
+        _full(acc, "out", 1, 1, n)
+
+
+# ---------------------------------------------------------------------------------------
 # decoding
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("B,D,H", [(1, 8, 1), (3, 72, 4), (5, 130, 5), (17, 96, 6)])
