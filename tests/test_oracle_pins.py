@@ -236,7 +236,7 @@ def test_finite_differences_conv(W, H, T, static):
     assert pin_fd_conv(conv_fwd, conv_bwd, 2, T, 4 * H if H > 1 else 4, W, H, static, seed=W * 31 + T)
 
 
-@pytest.mark.parametrize("W,H,R,T", [(4, 1, 3, 6), (2, 2, 2, 5), (5, 1, 1, 4), (3, 4, 5, 7)])
+@pytest.mark.parametrize("W,H,R,T", [(4, 1, 3, 6), (2, 2, 2, 5), (5, 1, 1, 4), (3, 4, 5, 7), (6, 2, 3, 7), (8, 1, 2, 10)])
 def test_finite_differences_lowrank(W, H, R, T):
     assert pin_fd_lowrank(lowrank_fwd, lowrank_bwd, 2, T, 8, W, H, R, seed=W * 17 + R)
 
@@ -627,14 +627,14 @@ def pin_packed_bwd(bwd, W, H, static, seed):
     return (not static) or np.allclose(dw, dw_sum, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("H,static", [(1, False), (2, False), (1, True), (4, True)])
 def test_packed_equals_separate_documents(W, H, static):
     assert pin_packed_fwd(conv_fwd, W, H, static, seed=40 + W)
     assert pin_packed_bwd(conv_bwd, W, H, static, seed=50 + W)
 
 
-@pytest.mark.parametrize("W", [2, 4, 5])
+@pytest.mark.parametrize("W", [2, 4, 5, 7])
 def test_packed_equals_separate_documents_lowrank(W):
     r = _rng(60 + W)
     B, T, D, R = 2, sum(PACKED_DOCS[0]), 6, 3
