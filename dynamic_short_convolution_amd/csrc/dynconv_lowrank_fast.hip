@@ -489,12 +489,20 @@ __global__ __launch_bounds__(64 * LRF_NWV) void k_lowrank_fwd_fast(const LowRank
         for (int ks = 1; ks < KS; ++ks) acc[mt] = mma32<ET>(afr[mt][ks], bfr[ks], acc[mt]);
       }
     };
-    f32x4_t acc[2][NGT];
-    gen(0, acc[0]);
+    // the filters of group j + 1 are generated while group j's are applied, except where
+    // the second accumulator set would not fit next to the rest (more than 5 taps at 64
+    // ranks: one set, two workgroups per CU instead of one)
+    constexpr bool AHEAD = W <= 5 || KS == 1;
+    f32x4_t acc[AHEAD ? 2 : 1][NGT];
+    if constexpr (AHEAD) gen(0, acc[0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j + 1 < 4) gen(j + 1, acc[(j + 1) & 1]);
-      const f32x4_t(&a)[NGT] = acc[j & 1];
+      if constexpr (AHEAD) {
+        if (j + 1 < 4) gen(j + 1, acc[(j + 1) & 1]);
+      } else {
+        gen(j, acc[0]);
+      }
+      const f32x4_t(&a)[NGT] = acc[AHEAD ? (j & 1) : 0];
       float yv[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
